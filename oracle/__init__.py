@@ -1,0 +1,138 @@
+"""Python face of the CPU oracle (``agq_oracle.c``), loaded through ctypes.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The GPU library
+never does.
+
+The oracle is single-threaded C in float64. It unpacks the codes,
+dequantizes ``w = scale*q + bias``, and takes dot products in increasing k.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "agq_oracle.c")
+LIB = os.path.join(HERE, "libagq_oracle.so")
+
+_CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-Wall", "-Wextra", "-Werror"]
+
+
+def build(src: str = SRC, out: str = LIB, strict: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, no FMA contraction, no fast-math)."""
+    flags = _CFLAGS if strict else [f for f in _CFLAGS if f != "-Werror"]
+    cmd = ["gcc", *flags, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle, building it first if missing or older than its source."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(LIB))
+    return _lib
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    lib.agqo_unpack.argtypes = [P, I64, I64, I, P]
+    lib.agqo_dequantize.argtypes = [P, P, P, I64, I64, I, I, P, P]
+    lib.agqo_qmv.argtypes = [P, I64, P, P, P, I64, I64, I, I, P, I64, P, P]
+    lib.agqo_gather_qmv.argtypes = [P, I64, P, P, P, I64, I64, I64, I, I, P, P, I64, P, I64, P, P]
+    for f in (lib.agqo_unpack, lib.agqo_dequantize, lib.agqo_qmv, lib.agqo_gather_qmv):
+        f.restype = I
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc):
+    if rc != 0:
+        raise OracleError(f"oracle returned {rc}")
+
+
+def unpack(w, K: int, bits: int, lib=None) -> np.ndarray:
+    """Packed uint32 ``[N, K*bits/32]`` -> codes uint8 ``[N, K]``."""
+    lib = lib or load()
+    w = _c(w, np.uint32)
+    w2 = w.reshape(-1, w.shape[-1])
+    q = np.empty((w2.shape[0], K), dtype=np.uint8)
+    _check(lib.agqo_unpack(_p(w2), w2.shape[0], K, bits, _p(q)))
+    return q.reshape(w.shape[:-1] + (K,))
+
+
+def dequantize(w, scales, biases, K: int, bits: int, group_size: int = 64, lib=None):
+    """-> (float64 ``[N, K]`` weights, count of values not exact in binary32)."""
+    lib = lib or load()
+    w = _c(w, np.uint32)
+    s = _c(scales, np.uint16)
+    b = _c(biases, np.uint16)
+    n = int(np.prod(w.shape[:-1]))
+    out = np.empty((n, K), dtype=np.float64)
+    bad = np.zeros(1, dtype=np.int64)
+    _check(lib.agqo_dequantize(_p(w), _p(s), _p(b), n, K, bits, group_size, _p(out), _p(bad)))
+    return out.reshape(w.shape[:-1] + (K,)), int(bad[0])
+
+
+def qmv(x, w, scales, biases, K: int, bits: int, group_size: int = 64, rows=None, lib=None):
+    """-> (y float64 ``[M, nrows]``, A float64 ``[M, nrows]``) with A = sum |x*w|."""
+    lib = lib or load()
+    x = _c(x, np.uint16).reshape(-1, K)
+    w = _c(w, np.uint32)
+    s = _c(scales, np.uint16)
+    b = _c(biases, np.uint16)
+    n = w.shape[0]
+    r = None if rows is None else _c(rows, np.int64)
+    nrows = n if r is None else r.shape[0]
+    y = np.empty((x.shape[0], nrows), dtype=np.float64)
+    a = np.empty_like(y)
+    _check(lib.agqo_qmv(_p(x), x.shape[0], _p(w), _p(s), _p(b), n, K, bits, group_size,
+                        _p(r), nrows, _p(y), _p(a)))
+    return y, a
+
+
+def gather_qmv(x, w, scales, biases, lhs, rhs, K: int, bits: int, group_size: int = 64,
+               rows=None, P: int | None = None, lib=None):
+    """Expert-gathered product. ``w`` is ``[E, N, K*bits/32]``; returns ``[P, nrows]`` y and A."""
+    lib = lib or load()
+    x = _c(x, np.uint16).reshape(-1, K)
+    w = _c(w, np.uint32)
+    s = _c(scales, np.uint16)
+    b = _c(biases, np.uint16)
+    e, n = w.shape[0], w.shape[1]
+    lh = None if lhs is None else _c(lhs, np.uint32)
+    rh = None if rhs is None else _c(rhs, np.uint32)
+    if P is None:
+        P = (lh if lh is not None else rh).shape[0]
+    r = None if rows is None else _c(rows, np.int64)
+    nrows = n if r is None else r.shape[0]
+    y = np.empty((P, nrows), dtype=np.float64)
+    a = np.empty_like(y)
+    _check(lib.agqo_gather_qmv(_p(x), x.shape[0], _p(w), _p(s), _p(b), e, n, K, bits, group_size,
+                               _p(lh), _p(rh), P, _p(r), nrows, _p(y), _p(a)))
+    return y, a

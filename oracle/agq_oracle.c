@@ -1,0 +1,184 @@
+/*
+ * CPU oracle for the affine group-quantized matrix-vector product.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library. The GPU library
+ * never links, includes or calls it, and it shares no code with the GPU library.
+ *
+ * It is plain, slow, single-threaded C in double precision. It takes the
+ * method's steps in order (unpack -> dequantize -> dot product), with no
+ * blocking, fusion or reordering.
+ *
+ * Sources:
+ *  - Operand formats: "MLX CUDA Cleanup Plan", Target Architecture §1. The
+ *    accelerated op multiplies BF16 activations by U32-packed affine-quantized
+ *    weights with BF16 scales and biases, in rank-2 and rank-3-plane
+ *    (per-expert) forms.
+ *  - Bit widths and group size: same page, Refactor Plan, Phase 3. BF16
+ *    inputs, 4-bit and 8-bit affine packed weights, group size 64.
+ *  - "gemma-4 decode carries ~44 ms/token model-specific fixed overhead on
+ *    GB10", Re-scope: the MLP projections are 8-bit, group size 64.
+ *  - The expert-gathered form is the gather_qmm path of "epic: CUDA (MLX
+ *    backend) prefill and decode acceleration program", Code-audit findings.
+ *
+ * The pages name the format ("affine") but print neither the affine map nor
+ * the bit order. Readings adopted:
+ *  - a weight is w = scale * q + bias, one (scale, bias) per 64 consecutive
+ *    input columns of a row;
+ *  - element k of a row sits in word k / (32/bits) at bit offset
+ *    bits * (k % (32/bits)), i.e. low-first;
+ *  - W is [N out, K in] and y[m, n] = sum_k x[m, k] * w[n, k].
+ *
+ * Every function here is pinned by the CPU test suite to known-answer words,
+ * closed forms, exact rational brute force and a float64 BLAS product.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+
+#define AGQO_OK 0
+#define AGQO_EARG (-1)
+#define AGQO_EINDEX (-2)
+
+/* A bfloat16 is the top half of an IEEE binary32, so the value is exact. */
+static double bf16_value(uint16_t h)
+{
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int check_format(int64_t K, int bits, int group_size)
+{
+    if (bits != 4 && bits != 8) return AGQO_EARG;
+    if (group_size <= 0 || K <= 0 || K % group_size != 0) return AGQO_EARG;
+    if (K % (32 / bits) != 0) return AGQO_EARG;
+    return AGQO_OK;
+}
+
+/* Step 1, unpack: the integer code of element k of one packed row. */
+static uint32_t code_at(const uint32_t *packed_row, int64_t k, int bits)
+{
+    int64_t per_word = 32 / bits;
+    uint32_t word = packed_row[k / per_word];
+    uint32_t shift = (uint32_t)(bits * (k % per_word));
+    uint32_t mask = (1u << bits) - 1u;
+    return (word >> shift) & mask;
+}
+
+/* Step 2, dequantize: w = scale * q + bias, in double (exact for bf16 scale/bias). */
+static double weight_at(const uint32_t *packed_row, const uint16_t *scale_row,
+                        const uint16_t *bias_row, int64_t k, int bits, int group_size)
+{
+    int64_t g = k / group_size;
+    double q = (double)code_at(packed_row, k, bits);
+    return bf16_value(scale_row[g]) * q + bf16_value(bias_row[g]);
+}
+
+/* Step 3, dot product of one activation row with one weight row, in increasing k.
+ * Also returns sum_k |x_k * w_k|, the scale of the rounding tolerance. */
+static void row_dot(const uint16_t *x_row, const uint32_t *packed_row,
+                    const uint16_t *scale_row, const uint16_t *bias_row,
+                    int64_t K, int bits, int group_size, double *y, double *a)
+{
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double term = bf16_value(x_row[k]) *
+                      weight_at(packed_row, scale_row, bias_row, k, bits, group_size);
+        acc += term;
+        mag += fabs(term);
+    }
+    *y = acc;
+    *a = mag;
+}
+
+/* Unpacked integer codes, q[n*K + k]. */
+int agqo_unpack(const uint32_t *w, int64_t N, int64_t K, int bits, uint8_t *q)
+{
+    if (!w || !q || N <= 0 || (bits != 4 && bits != 8) || K <= 0 || K % (32 / bits))
+        return AGQO_EARG;
+    int64_t words = K * bits / 32;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            q[n * K + k] = (uint8_t)code_at(w + n * words, k, bits);
+    return AGQO_OK;
+}
+
+/* Dequantized weights out[n*K + k] = scale*q + bias (double). Returns through
+ * *not_f32 how many values are not exactly representable in binary32. */
+int agqo_dequantize(const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                    int64_t N, int64_t K, int bits, int group_size,
+                    double *out, int64_t *not_f32)
+{
+    if (!w || !scales || !biases || !out || N <= 0) return AGQO_EARG;
+    if (check_format(K, bits, group_size)) return AGQO_EARG;
+    int64_t words = K * bits / 32, groups = K / group_size, bad = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            double v = weight_at(w + n * words, scales + n * groups, biases + n * groups,
+                                 k, bits, group_size);
+            out[n * K + k] = v;
+            if ((double)(float)v != v) ++bad;
+        }
+    }
+    if (not_f32) *not_f32 = bad;
+    return AGQO_OK;
+}
+
+/* y[m, i] = sum_k x[m, k] * w[n_i, k] for M activation rows and the weight rows
+ * n_i = rows[i] (or n_i = i when rows is NULL, nrows == N). Output layout
+ * [M, nrows]; a[] receives sum_k |x[m,k] * w[n_i,k]| in the same layout. */
+int agqo_qmv(const uint16_t *x, int64_t M,
+             const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+             int64_t N, int64_t K, int bits, int group_size,
+             const int64_t *rows, int64_t nrows, double *y, double *a)
+{
+    if (!x || !w || !scales || !biases || !y || !a || M <= 0 || N <= 0) return AGQO_EARG;
+    if (check_format(K, bits, group_size)) return AGQO_EARG;
+    if (!rows) nrows = N;
+    if (nrows <= 0) return AGQO_EARG;
+    int64_t words = K * bits / 32, groups = K / group_size;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t i = 0; i < nrows; ++i) {
+            int64_t n = rows ? rows[i] : i;
+            if (n < 0 || n >= N) return AGQO_EINDEX;
+            row_dot(x + m * K, w + n * words, scales + n * groups, biases + n * groups,
+                    K, bits, group_size, &y[m * nrows + i], &a[m * nrows + i]);
+        }
+    }
+    return AGQO_OK;
+}
+
+/* Expert-gathered product, one output row per (token, expert) pair p:
+ * y[p, i] = sum_k x[lhs[p], k] * w[rhs[p]][n_i, k]. W, scales and biases are
+ * stacked expert planes [E, N, .]. A NULL lhs (rhs) means lhs[p] = p (rhs[p] = p).
+ * Output layout [P, nrows]. */
+int agqo_gather_qmv(const uint16_t *x, int64_t R,
+                    const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                    int64_t E, int64_t N, int64_t K, int bits, int group_size,
+                    const uint32_t *lhs, const uint32_t *rhs, int64_t P,
+                    const int64_t *rows, int64_t nrows, double *y, double *a)
+{
+    if (!x || !w || !scales || !biases || !y || !a) return AGQO_EARG;
+    if (R <= 0 || E <= 0 || N <= 0 || P <= 0) return AGQO_EARG;
+    if (check_format(K, bits, group_size)) return AGQO_EARG;
+    if (!rows) nrows = N;
+    if (nrows <= 0) return AGQO_EARG;
+    int64_t words = K * bits / 32, groups = K / group_size;
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t r = lhs ? (int64_t)lhs[p] : p;
+        int64_t e = rhs ? (int64_t)rhs[p] : p;
+        if (r < 0 || r >= R || e < 0 || e >= E) return AGQO_EINDEX;
+        const uint32_t *we = w + e * N * words;
+        const uint16_t *se = scales + e * N * groups;
+        const uint16_t *be = biases + e * N * groups;
+        for (int64_t i = 0; i < nrows; ++i) {
+            int64_t n = rows ? rows[i] : i;
+            if (n < 0 || n >= N) return AGQO_EINDEX;
+            row_dot(x + r * K, we + n * words, se + n * groups, be + n * groups,
+                    K, bits, group_size, &y[p * nrows + i], &a[p * nrows + i]);
+        }
+    }
+    return AGQO_OK;
+}

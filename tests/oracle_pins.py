@@ -1,0 +1,214 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` takes a loaded oracle library and raises ``AssertionError`` on
+a mismatch. ``test_oracle_pins.py`` runs them against the real oracle.
+``test_oracle_mutants.py`` runs them against copies of the oracle with one
+planted mistake each, and requires every mutant to fail at least one pin.
+
+Anchors used:
+  * known-answer packed words (the low-first bit layout, written out by hand);
+  * the hand-worked closed forms in ``golden/worked_k64.json``;
+  * the producer-side quantizer (scale = (max-min)/(2^bits-1), bias = min):
+    quantizing the oracle's dequantized weights must give back the original
+    codes, scales and biases;
+  * exact rational brute force (``fractions.Fraction``) on tiny shapes, with
+    codes taken from before packing;
+  * a float64 BLAS product on a densely built weight matrix;
+  * an integer-valued special case, which must come out exact;
+  * the constant-code closed form sum_g (s_g*c + b_g) * sum_{k in g} x_k.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from seeded_inputs import bf16_bits, bf16_to_f32, pack_codes, quantize_rows, draw_quantized_weight
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_k64.json")
+U53 = 2.0 ** -53
+
+
+def _frac_bf16(h):
+    return Fraction(float(bf16_to_f32(np.array([h], dtype=np.uint16))[0]))
+
+
+def _random_problem(seed, M, N, K, bits, E=None):
+    g = np.random.default_rng(seed)
+    shape = (N, K) if E is None else (E, N, K)
+    codes = g.integers(0, 2 ** bits, size=shape, dtype=np.uint8)
+    gshape = shape[:-1] + (K // 64,)
+    scales = bf16_bits((0.01 + 0.02 * g.random(gshape)).astype(np.float32))
+    biases = bf16_bits((-0.05 + 0.03 * g.standard_normal(gshape)).astype(np.float32))
+    x = bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    return x, codes, scales, biases
+
+
+def _exact_row(xrow, qrow, srow, brow):
+    y = Fraction(0)
+    a = Fraction(0)
+    for k in range(len(qrow)):
+        w = _frac_bf16(srow[k // 64]) * int(qrow[k]) + _frac_bf16(brow[k // 64])
+        t = _frac_bf16(xrow[k]) * w
+        y += t
+        a += abs(t)
+    return y, a
+
+
+def pin_unpack_known_words(lib):
+    words4 = np.array([[0x76543210, 0xFEDCBA98, 0x00000000, 0x80000000,
+                        0xFFFFFFFF, 0x11111111, 0x01234567, 0x0000000F]], dtype=np.uint32)
+    want4 = ([0, 1, 2, 3, 4, 5, 6, 7] + [8, 9, 10, 11, 12, 13, 14, 15] + [0] * 8 +
+             [0] * 7 + [8] + [15] * 8 + [1] * 8 + [7, 6, 5, 4, 3, 2, 1, 0] + [15] + [0] * 7)
+    got4 = oracle.unpack(words4, 64, 4, lib=lib)
+    assert got4.tolist() == [want4], got4
+    words8 = np.array([[0x03020100, 0xFFFEFDFC, 0x80000000, 0xFFFFFFFF,
+                        0x000000FF, 0x7F00807F, 0x00000001, 0x01000000]], dtype=np.uint32)
+    want8 = ([0, 1, 2, 3] + [252, 253, 254, 255] + [0, 0, 0, 128] + [255] * 4 +
+             [255, 0, 0, 0] + [127, 128, 0, 127] + [1, 0, 0, 0] + [0, 0, 0, 1])
+    got8 = oracle.unpack(words8, 32, 8, lib=lib)
+    assert got8.tolist() == [want8], got8
+
+
+def pin_unpack_roundtrip(lib):
+    for bits in (4, 8):
+        q = np.random.default_rng(bits).integers(0, 2 ** bits, size=(5, 192), dtype=np.uint8)
+        got = oracle.unpack(pack_codes(q, bits), 192, bits, lib=lib)
+        assert np.array_equal(got, q)
+
+
+def pin_golden_worked(lib):
+    with open(GOLDEN) as f:
+        doc = json.load(f)
+    for case in doc["cases"]:
+        y, a = oracle.qmv(np.array(case["x_bf16"], dtype=np.uint16),
+                          np.array(case["w_u32"], dtype=np.uint32),
+                          np.array(case["scales_bf16"], dtype=np.uint16),
+                          np.array(case["biases_bf16"], dtype=np.uint16),
+                          case["K"], case["bits"], case["group_size"], lib=lib)
+        assert y.tolist() == case["y"], (case["bits"], y)
+        assert a.tolist() == case["A"], (case["bits"], a)
+
+
+def pin_dequant_quantizer_roundtrip(lib):
+    for bits in (4, 8):
+        d = draw_quantized_weight(99, bits, 64, 256, bits, keep_codes=True)
+        what, not_f32 = oracle.dequantize(d["w"], d["scales"], d["biases"], 256, bits, lib=lib)
+        assert not_f32 == 0
+        q2, s2, b2 = quantize_rows(what.astype(np.float32), bits)
+        # Groups whose codes span the full range re-quantize to themselves exactly:
+        # max - min = scale*(2^bits-1) and min = bias. (8-bit groups whose top code
+        # rounded to 2^bits-2 are excluded; they are a minority.)
+        qg = d["codes"].reshape(64, 4, 64)
+        full = (qg.min(-1) == 0) & (qg.max(-1) == 2 ** bits - 1)
+        assert full.mean() > 0.5
+        assert np.array_equal(s2[full], d["scales"][full])
+        assert np.array_equal(b2[full], d["biases"][full])
+        assert np.array_equal(q2.reshape(64, 4, 64)[full], qg[full])
+
+
+def pin_dot_exact_bruteforce(lib):
+    for bits in (4, 8):
+        for seed, (M, N, K) in enumerate([(2, 3, 64), (1, 2, 128), (3, 4, 192)]):
+            x, q, s, b = _random_problem(100 + seed + bits, M, N, K, bits)
+            y, a = oracle.qmv(x, pack_codes(q, bits), s, b, K, bits, lib=lib)
+            for m in range(M):
+                for n in range(N):
+                    ye, ae = _exact_row(x[m], q[n], s[n], b[n])
+                    bound = 2 * K * U53 * float(ae)
+                    assert abs(y[m, n] - float(ye)) <= bound, (bits, M, N, K, m, n)
+                    assert abs(a[m, n] - float(ae)) <= bound, (bits, M, N, K, m, n)
+
+
+def pin_numpy_blas(lib):
+    for bits in (4, 8):
+        x, q, s, b = _random_problem(7 + bits, 3, 96, 1024, bits)
+        y, a = oracle.qmv(x, pack_codes(q, bits), s, b, 1024, bits, lib=lib)
+        sf = np.repeat(bf16_to_f32(s).astype(np.float64), 64, axis=1)
+        bf = np.repeat(bf16_to_f32(b).astype(np.float64), 64, axis=1)
+        wd = sf * q.astype(np.float64) + bf
+        xd = bf16_to_f32(x).astype(np.float64)
+        yb = xd @ wd.T
+        ab = np.abs(xd) @ np.abs(wd).T
+        assert np.all(np.abs(y - yb) <= 1e-12 * ab)
+        assert np.allclose(a, ab, rtol=1e-12, atol=0)
+
+
+def pin_integer_special_case(lib):
+    g = np.random.default_rng(5)
+    N, K = 7, 320
+    q = g.integers(0, 256, size=(N, K), dtype=np.uint8)
+    xi = g.integers(-8, 9, size=(2, K))
+    x = bf16_bits(xi.astype(np.float32))
+    ones = np.full((N, K // 64), 0x3F80, dtype=np.uint16)
+    zeros = np.zeros((N, K // 64), dtype=np.uint16)
+    y, a = oracle.qmv(x, pack_codes(q, 8), ones, zeros, K, 8, lib=lib)
+    want = xi.astype(np.int64) @ q.astype(np.int64).T
+    assert np.array_equal(y, want.astype(np.float64))
+    assert np.array_equal(a, (np.abs(xi) @ q.astype(np.int64).T).astype(np.float64))
+
+
+def pin_constant_code_closed_form(lib):
+    for bits, c in ((4, 11), (8, 200)):
+        g = np.random.default_rng(bits)
+        N, K = 3, 256
+        q = np.full((N, K), c, dtype=np.uint8)
+        s = bf16_bits((0.01 + 0.02 * g.random((N, K // 64))).astype(np.float32))
+        b = bf16_bits((-0.1 * g.random((N, K // 64))).astype(np.float32))
+        x = bf16_bits(g.standard_normal((1, K)).astype(np.float32))
+        y, a = oracle.qmv(x, pack_codes(q, bits), s, b, K, bits, lib=lib)
+        for n in range(N):
+            want = Fraction(0)
+            for gi in range(K // 64):
+                xs = sum((_frac_bf16(x[0, k]) for k in range(64 * gi, 64 * gi + 64)), Fraction(0))
+                want += (_frac_bf16(s[n, gi]) * c + _frac_bf16(b[n, gi])) * xs
+            assert abs(y[0, n] - float(want)) <= 2 * K * U53 * a[0, n]
+    # a single group value everywhere: (s*c + b) * sum(x)
+    K = 128
+    x = bf16_bits(np.linspace(-1, 1, K).astype(np.float32))[None]
+    y, _ = oracle.qmv(x, pack_codes(np.full((1, K), 3, np.uint8), 4),
+                      np.full((1, 2), 0x3F00, np.uint16), np.full((1, 2), 0xBF80, np.uint16), K, 4, lib=lib)
+    assert y[0, 0] == 0.5 * float(bf16_to_f32(x).astype(np.float64).sum())
+
+
+def pin_gather_bruteforce(lib):
+    bits, E, N, K, R = 4, 3, 5, 128, 4
+    x, q, s, b = _random_problem(31, R, N, K, bits, E=E)
+    lhs = np.array([0, 0, 1, 2, 3, 3], dtype=np.uint32)
+    rhs = np.array([2, 0, 1, 1, 0, 2], dtype=np.uint32)
+    y, a = oracle.gather_qmv(x, pack_codes(q, bits), s, b, lhs, rhs, K, bits, lib=lib)
+    for p in range(len(lhs)):
+        for n in range(N):
+            ye, ae = _exact_row(x[lhs[p]], q[rhs[p], n], s[rhs[p], n], b[rhs[p], n])
+            assert abs(y[p, n] - float(ye)) <= 2 * K * U53 * float(ae), (p, n)
+    # NULL indices mean the identity map
+    w = pack_codes(q, bits)
+    y1, _ = oracle.gather_qmv(x[:3], w, s, b, None, np.array([2, 0, 1], np.uint32), K, bits, lib=lib)
+    y2, _ = oracle.gather_qmv(x[:3], w, s, b, np.arange(3, dtype=np.uint32), np.array([2, 0, 1], np.uint32),
+                              K, bits, lib=lib)
+    assert np.array_equal(y1, y2)
+    y3, _ = oracle.gather_qmv(x, w, s, b, np.array([3, 1, 0], np.uint32), None, K, bits, lib=lib)
+    y4, _ = oracle.gather_qmv(x, w, s, b, np.array([3, 1, 0], np.uint32), np.arange(3, dtype=np.uint32),
+                              K, bits, lib=lib)
+    assert np.array_equal(y3, y4)
+
+
+def pin_row_subset(lib):
+    x, q, s, b = _random_problem(3, 2, 9, 128, 8)
+    w = pack_codes(q, 8)
+    yf, af = oracle.qmv(x, w, s, b, 128, 8, lib=lib)
+    rows = np.array([8, 0, 4, 4], dtype=np.int64)
+    ys, as_ = oracle.qmv(x, w, s, b, 128, 8, rows=rows, lib=lib)
+    assert np.array_equal(ys, yf[:, rows]) and np.array_equal(as_, af[:, rows])
+    for bits in (4, 8):
+        x, q, s, b = _random_problem(40 + bits, 1, 6, 192, bits)
+        ye = [_exact_row(x[0], q[n], s[n], b[n])[0] for n in range(6)]
+        ys, as_ = oracle.qmv(x, pack_codes(q, bits), s, b, 192, bits, rows=np.array([5, 1]), lib=lib)
+        for i, n in enumerate([5, 1]):
+            assert abs(ys[0, i] - float(ye[n])) <= 2 * 192 * U53 * as_[0, i]
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,55 @@
+"""Planted-mistake check of the pins.
+
+Each mutant is the oracle's C source with one plausible mistake, compiled to a
+private library on the CPU. Every mutant must fail at least one pin. The
+original snippet must occur exactly once, which keeps this list in step with
+the source.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+MUTANTS = {
+    "high_first_unpack": ("uint32_t shift = (uint32_t)(bits * (k % per_word));",
+                          "uint32_t shift = (uint32_t)(bits * (per_word - 1 - k % per_word));"),
+    "wrong_word_index": ("uint32_t word = packed_row[k / per_word];",
+                         "uint32_t word = packed_row[k % per_word];"),
+    "short_mask": ("uint32_t mask = (1u << bits) - 1u;", "uint32_t mask = (1u << (bits - 1)) - 1u;"),
+    "dropped_bias": ("return bf16_value(scale_row[g]) * q + bf16_value(bias_row[g]);",
+                     "return bf16_value(scale_row[g]) * q;"),
+    "swapped_scale_bias": ("return bf16_value(scale_row[g]) * q + bf16_value(bias_row[g]);",
+                           "return bf16_value(bias_row[g]) * q + bf16_value(scale_row[g]);"),
+    "bias_sign": ("return bf16_value(scale_row[g]) * q + bf16_value(bias_row[g]);",
+                  "return bf16_value(scale_row[g]) * q - bf16_value(bias_row[g]);"),
+    "group_of_128": ("int64_t g = k / group_size;", "int64_t g = k / (2 * group_size);"),
+    "dropped_last_term": ("for (int64_t k = 0; k < K; ++k) {\n        double term",
+                          "for (int64_t k = 0; k < K - 1; ++k) {\n        double term"),
+    "signed_magnitude": ("mag += fabs(term);", "mag += term;"),
+    "bf16_shift": ("uint32_t u = ((uint32_t)h) << 16;", "uint32_t u = ((uint32_t)h) << 15;"),
+    "x_row_ignored": ("row_dot(x + m * K,", "row_dot(x,"),
+    "scale_row_offset": ("row_dot(x + m * K, w + n * words, scales + n * groups,",
+                         "row_dot(x + m * K, w + n * words, scales,"),
+    "expert_plane_ignored": ("const uint32_t *we = w + e * N * words;", "const uint32_t *we = w;"),
+    "lhs_ignored": ("int64_t r = lhs ? (int64_t)lhs[p] : p;", "int64_t r = p % R;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(oracle.SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"snippet for {name} not found exactly once"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle.load(oracle.build(str(path), str(tmp_path / f"lib{name}.so"), strict=False))
+    failed = []
+    for pin in PINS:
+        try:
+            pin(lib)
+        except (AssertionError, oracle.OracleError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
