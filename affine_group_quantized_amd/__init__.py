@@ -1,0 +1,244 @@
+"""Affine group-quantized matrix-vector products on AMD MI355X (gfx950).
+
+Python binding of ``libagq.so`` (ctypes). This module only marshals
+arguments. Every step of the computation runs in the library's HIP kernels,
+and torch supplies device memory and the current stream. If the library is
+not built, importing this module raises ``ImportError``; there is no
+fallback path.
+
+Operands follow the accelerator boundary of "MLX CUDA Cleanup Plan", Target
+Architecture §1: BF16 activations, U32-packed affine codes (4 or 8 bits,
+low-first in each word), and BF16 scales and biases per 64-column group.
+Weight n, column k dequantizes to ``scales[n, k//64] * q[n, k] + biases[n, k//64]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["qmv", "qmv_wide", "gather_qmv", "dequantize", "plan", "prepare_qmv", "AgqError", "LIB_PATH", "lib"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libagq.so")
+
+AGQ_OK, AGQ_EINVAL, AGQ_ENOTSUP, AGQ_EHIP = 0, 1, 2, 3
+
+
+class AgqError(RuntimeError):
+    """A non-OK status from libagq, carrying the library's message."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_STATUS = {AGQ_OK: "AGQ_OK", AGQ_EINVAL: "AGQ_EINVAL", AGQ_ENOTSUP: "AGQ_ENOTSUP", AGQ_EHIP: "AGQ_EHIP"}
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("bits", ctypes.c_int32), ("chunks_per_row", ctypes.c_int32), ("cpt", ctypes.c_int32),
+        ("mw", ctypes.c_int32), ("rows_per_iter", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
+        ("groups_per_block", ctypes.c_int32), ("threads_per_block", ctypes.c_int32),
+        ("rows_per_group", ctypes.c_int64), ("row_groups", ctypes.c_int64), ("blocks", ctypes.c_int64),
+    ]
+
+
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"libagq.so is not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.agq_version.restype = I
+    lib.agq_status_str.argtypes = [I]
+    lib.agq_status_str.restype = ctypes.c_char_p
+    lib.agq_last_error.restype = ctypes.c_char_p
+    lib.agq_qmv.argtypes = [P, P, P, P, P, I64, I64, I, I, P]
+    lib.agq_qmv_wide.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
+    lib.agq_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
+    lib.agq_dequantize.argtypes = [P, P, P, P, I64, I64, I, I, P]
+    lib.agq_plan_product.argtypes = [I64, I64, I64, I, I, I, I64, ctypes.POINTER(Plan)]
+    for f in (lib.agq_qmv, lib.agq_qmv_wide, lib.agq_gather_qmv, lib.agq_dequantize, lib.agq_plan_product):
+        f.restype = I
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != AGQ_OK:
+        raise AgqError(status, lib.agq_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtypes, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}; expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16 = (torch.bfloat16,)
+_U32 = (torch.int32, torch.uint32)
+
+
+def _weights(w, scales, biases, K, bits, group_size, device, planes):
+    _need(w, "w", _U32, device)
+    _need(scales, "scales", _BF16, device)
+    _need(biases, "biases", _BF16, device)
+    if bits not in (4, 8) or group_size <= 0 or K % group_size or (K * bits) % 32:
+        raise ValueError(f"bad format: K={K} bits={bits} group_size={group_size}")
+    lead = w.shape[:-1]
+    if w.dim() != planes + 1 or w.shape[-1] != K * bits // 32:
+        raise ValueError(f"w has shape {tuple(w.shape)}; expected {planes + 1} dims ending in {K * bits // 32}")
+    gshape = tuple(lead) + (K // group_size,)
+    if tuple(scales.shape) != gshape or tuple(biases.shape) != gshape:
+        raise ValueError(f"scales/biases must have shape {gshape}")
+    return lead
+
+
+def qmv(x, w, scales, biases, bits: int = 4, group_size: int = 64, out=None):
+    """Batch-1 product: ``x`` [K] (or [1, K]) bf16 -> ``y`` [N] (or [1, N]) bf16."""
+    device = x.device
+    _need(x, "x", _BF16, device)
+    K = x.shape[-1]
+    if x.numel() != K:
+        raise ValueError("qmv takes a single activation row; use qmv_wide for M > 1")
+    (N,) = _weights(w, scales, biases, K, bits, group_size, device, 1)
+    shape = tuple(x.shape[:-1]) + (N,)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    else:
+        _need(out, "out", _BF16, device)
+        if out.numel() != N:
+            raise ValueError("out has the wrong size")
+    with torch.cuda.device(device):
+        _check(lib.agq_qmv(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(out), N, K, bits, group_size,
+                           _stream(device)))
+    return out
+
+
+def prepare_qmv(x, w, scales, biases, out, bits: int = 4, group_size: int = 64, stream=None):
+    """Validate once and return a zero-argument callable that queues the product.
+
+    For hot loops (decode steps, benchmarks), each call is one C call with
+    cached pointers, so per-call host overhead stays well below the kernel
+    time. ``x`` is ``[K]`` or ``[M, K]`` (M <= 8), and ``out`` is the matching
+    ``[N]`` / ``[M, N]`` bf16 buffer. The tensors must outlive the callable.
+    Work is queued on ``stream``, or on the current stream at preparation time.
+    """
+    device = x.device
+    _need(x, "x", _BF16, device)
+    _need(out, "out", _BF16, device)
+    K = x.shape[-1]
+    M = x.numel() // K
+    (N,) = _weights(w, scales, biases, K, bits, group_size, device, 1)
+    if out.numel() != M * N:
+        raise ValueError("out has the wrong size")
+    st = ctypes.c_void_p((stream or torch.cuda.current_stream(device)).cuda_stream)
+    args = (_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(out))
+    fn = lib.agq_qmv_wide
+
+    def call():
+        status = fn(*args, M, N, K, bits, group_size, st)
+        if status:
+            _check(status)
+    return call
+
+
+def qmv_wide(x, w, scales, biases, bits: int = 4, group_size: int = 64, out=None):
+    """Small-batch product: ``x`` [M, K] bf16 (1 <= M <= 8) -> ``y`` [M, N] bf16."""
+    device = x.device
+    _need(x, "x", _BF16, device)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    (N,) = _weights(w, scales, biases, K, bits, group_size, device, 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    else:
+        _need(out, "out", _BF16, device)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    with torch.cuda.device(device):
+        _check(lib.agq_qmv_wide(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(out), M, N, K, bits,
+                                group_size, _stream(device)))
+    return out
+
+
+def gather_qmv(x, w, scales, biases, rhs_indices=None, lhs_indices=None, bits: int = 4, group_size: int = 64,
+               out=None, num_pairs: int | None = None):
+    """Expert-gathered product, one output row per (token, expert) pair.
+
+    ``x`` [R, K] bf16; ``w`` [E, N, K*bits/32]; ``scales``/``biases`` [E, N, K/64];
+    ``rhs_indices`` [P] expert per pair; ``lhs_indices`` [P] row of ``x`` per pair.
+    A missing index array is the identity. Returns ``y`` [P, N] bf16.
+    """
+    device = x.device
+    _need(x, "x", _BF16, device)
+    if x.dim() != 2:
+        raise ValueError("x must be [R, K]")
+    R, K = x.shape
+    E, N = _weights(w, scales, biases, K, bits, group_size, device, 2)
+    for name, t in (("lhs_indices", lhs_indices), ("rhs_indices", rhs_indices)):
+        if t is not None:
+            _need(t, name, _U32, device)
+            if t.dim() != 1:
+                raise ValueError(f"{name} must be 1-D")
+    if num_pairs is None:
+        idx = rhs_indices if rhs_indices is not None else lhs_indices
+        num_pairs = idx.shape[0] if idx is not None else R
+    P = int(num_pairs)
+    for t in (lhs_indices, rhs_indices):
+        if t is not None and t.shape[0] != P:
+            raise ValueError("index arrays must have P entries")
+    if out is None:
+        out = torch.empty((P, N), dtype=torch.bfloat16, device=device)
+    else:
+        _need(out, "out", _BF16, device)
+        if tuple(out.shape) != (P, N):
+            raise ValueError("out has the wrong shape")
+    with torch.cuda.device(device):
+        _check(lib.agq_gather_qmv(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(lhs_indices),
+                                  _ptr(rhs_indices), _ptr(out), P, R, E, N, K, bits, group_size, _stream(device)))
+    return out
+
+
+def dequantize(w, scales, biases, bits: int = 4, group_size: int = 64, out=None):
+    """Dequantized fp32 weights, shape ``w.shape[:-1] + (K,)``."""
+    device = w.device
+    K = w.shape[-1] * 32 // bits
+    lead = _weights(w, scales, biases, K, bits, group_size, device, w.dim() - 1)
+    rows = 1
+    for d in lead:
+        rows *= d
+    if out is None:
+        out = torch.empty(tuple(lead) + (K,), dtype=torch.float32, device=device)
+    else:
+        _need(out, "out", (torch.float32,), device)
+        if out.numel() != rows * K:
+            raise ValueError("out has the wrong size")
+    with torch.cuda.device(device):
+        _check(lib.agq_dequantize(_ptr(w), _ptr(scales), _ptr(biases), _ptr(out), rows, K, bits, group_size,
+                                  _stream(device)))
+    return out
+
+
+def plan(M: int, N: int, K: int, bits: int = 4, group_size: int = 64, num_cus: int = 256, experts: int = 0):
+    """The library's launch plan for a product of this shape (host only)."""
+    p = Plan()
+    _check(lib.agq_plan_product(M, N, K, bits, group_size, num_cus, experts, ctypes.byref(p)))
+    return {name: getattr(p, name) for name, _ in Plan._fields_}

@@ -1,0 +1,250 @@
+// C ABI of libagq: argument validation, launch planning and kernel launches.
+//
+// The boundary follows the accelerator interface of "MLX CUDA Cleanup Plan",
+// Target Architecture §2-§4 and Hard Constraints. Callers pass borrowed device
+// buffers. A call adds no host or device copies and no synchronization. It
+// falls back to no other path: a shape it does not implement returns
+// AGQ_ENOTSUP to the caller.
+//
+// Every argument check runs before the first HIP call.
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "agq.h"
+#include "plan.hpp"
+#include "qmv_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+agq_status fail(agq_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    std::atomic<int> state{0};  // 0 unknown, 1 ready
+    int cus = 0;
+    bool gfx950 = false;
+    char arch[64] = "";
+};
+
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Current device's compute-unit count; checks once per device that it is gfx950.
+agq_status current_device(int *cus) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(AGQ_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(AGQ_EHIP, "device ordinal %d out of range", dev);
+    DeviceInfo &d = g_dev[dev];
+    if (d.state.load(std::memory_order_acquire) == 0) {
+        std::lock_guard<std::mutex> lock(g_dev_mu);
+        if (d.state.load(std::memory_order_relaxed) == 0) {
+            hipDeviceProp_t prop;
+            e = hipGetDeviceProperties(&prop, dev);
+            if (e != hipSuccess)
+                return fail(AGQ_EHIP, "hipGetDeviceProperties(%d) failed: %s", dev, hipGetErrorString(e));
+            std::snprintf(d.arch, sizeof d.arch, "%s", prop.gcnArchName);
+            d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            d.cus = prop.multiProcessorCount;
+            d.state.store(1, std::memory_order_release);
+        }
+    }
+    if (!d.gfx950) return fail(AGQ_ENOTSUP, "device %d is %s; libagq is built for gfx950 only", dev, d.arch);
+    *cus = d.cus;
+    return AGQ_OK;
+}
+
+bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+constexpr int64_t kMaxN = int64_t(1) << 40;
+constexpr int64_t kMaxK = int64_t(1) << 30;
+
+// Format and operand checks shared by the products and dequantize.
+agq_status check_operands(const void *x, const void *w, const void *s, const void *b, const void *y, int64_t N,
+                          int64_t K, int bits, int group_size, bool need_x) {
+    if ((need_x && !x) || !w || !s || !b || !y) return fail(AGQ_EINVAL, "null tensor pointer");
+    if (N <= 0 || K <= 0) return fail(AGQ_EINVAL, "N and K must be positive (N=%lld, K=%lld)", (long long)N,
+                                      (long long)K);
+    if (N > kMaxN || K > kMaxK) return fail(AGQ_EINVAL, "N or K too large (N=%lld, K=%lld)", (long long)N,
+                                            (long long)K);
+    if (group_size <= 0) return fail(AGQ_EINVAL, "group_size must be positive (got %d)", group_size);
+    if (bits != 4 && bits != 8) return fail(AGQ_ENOTSUP, "bits=%d not supported (4 or 8)", bits);
+    if (group_size != 64) return fail(AGQ_ENOTSUP, "group_size=%d not supported (64)", group_size);
+    if (K % group_size != 0) return fail(AGQ_EINVAL, "K=%lld is not a multiple of group_size", (long long)K);
+    if ((need_x && misaligned(x, 16)) || misaligned(w, 16))
+        return fail(AGQ_EINVAL, "x and w must be 16-byte aligned");
+    if (misaligned(s, 2) || misaligned(b, 2) || misaligned(y, 2))
+        return fail(AGQ_EINVAL, "scales, biases and y must be 2-byte aligned");
+    return AGQ_OK;
+}
+
+agq::ProductArgs make_args(const void *x, const uint32_t *w, const void *s, const void *b, void *y, int64_t N,
+                           int64_t K, int bits, int M, const agq::Plan &p) {
+    agq::ProductArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = reinterpret_cast<const agq::u32x4 *>(w);
+    a.s = static_cast<const uint16_t *>(s);
+    a.b = static_cast<const uint16_t *>(b);
+    a.y = static_cast<uint16_t *>(y);
+    a.N = N;
+    a.RPG = p.RPG;
+    a.K = (int32_t)K;
+    a.C = (int32_t)(K * bits / 128);
+    a.G = (int32_t)(K / 64);
+    a.M = M;
+    a.S = p.S;
+    a.GPB = p.GPB;
+    return a;
+}
+
+agq_status launch(const void *sym, dim3 grid, dim3 block, void *arg, void *stream) {
+    void *args[] = {arg};
+    hipError_t e = hipLaunchKernel(sym, grid, block, args, 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(AGQ_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return AGQ_OK;
+}
+
+agq_status dense_product(const void *x, const uint32_t *w, const void *s, const void *b, void *y, int64_t M,
+                         int64_t N, int64_t K, int bits, int group_size, void *stream) {
+    agq_status st = check_operands(x, w, s, b, y, N, K, bits, group_size, true);
+    if (st != AGQ_OK) return st;
+    if (M <= 0) return fail(AGQ_EINVAL, "M must be positive (got %lld)", (long long)M);
+    if (M > 8) return fail(AGQ_ENOTSUP, "M=%lld > 8 is a quantized GEMM, not a matvec", (long long)M);
+    agq::Plan plan;
+    if (agq::make_plan(M, N, K, bits, 256, 0, &plan) != AGQ_OK)
+        return fail(AGQ_ENOTSUP, "K=%lld too large for M=%lld at %d bits", (long long)K, (long long)M, bits);
+    int cus = 0;
+    st = current_device(&cus);
+    if (st != AGQ_OK) return st;
+    agq::make_plan(M, N, K, bits, cus, 0, &plan);
+    const void *sym = agq::product_kernel(bits, plan.mw, plan.cpt, false);
+    if (!sym) return fail(AGQ_ENOTSUP, "no kernel for bits=%d M=%d cpt=%d", bits, plan.mw, plan.cpt);
+    agq::ProductArgs a = make_args(x, w, s, b, y, N, K, bits, (int)M, plan);
+    return launch(sym, dim3((unsigned)plan.blocks), dim3(plan.threads), &a, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int agq_version(void) { return 100; }
+
+const char *agq_status_str(agq_status status) {
+    switch (status) {
+        case AGQ_OK: return "AGQ_OK";
+        case AGQ_EINVAL: return "AGQ_EINVAL";
+        case AGQ_ENOTSUP: return "AGQ_ENOTSUP";
+        case AGQ_EHIP: return "AGQ_EHIP";
+    }
+    return "AGQ_UNKNOWN";
+}
+
+const char *agq_last_error(void) { return g_err; }
+
+agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases, void *y, int64_t N,
+                   int64_t K, int bits, int group_size, void *stream) {
+    return dense_product(x, w, scales, biases, y, 1, N, K, bits, group_size, stream);
+}
+
+agq_status agq_qmv_wide(const void *x, const uint32_t *w, const void *scales, const void *biases, void *y,
+                        int64_t M, int64_t N, int64_t K, int bits, int group_size, void *stream) {
+    return dense_product(x, w, scales, biases, y, M, N, K, bits, group_size, stream);
+}
+
+agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
+                          const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y, int64_t P, int64_t R,
+                          int64_t E, int64_t N, int64_t K, int bits, int group_size, void *stream) {
+    agq_status st = check_operands(x, w, scales, biases, y, N, K, bits, group_size, true);
+    if (st != AGQ_OK) return st;
+    if (P <= 0 || R <= 0 || E <= 0)
+        return fail(AGQ_EINVAL, "P, R and E must be positive (P=%lld, R=%lld, E=%lld)", (long long)P,
+                    (long long)R, (long long)E);
+    if (!lhs_indices && R != P) return fail(AGQ_EINVAL, "lhs_indices == NULL requires R == P");
+    if (!rhs_indices && E != P) return fail(AGQ_EINVAL, "rhs_indices == NULL requires E == P");
+    if (misaligned(lhs_indices, 4) || misaligned(rhs_indices, 4))
+        return fail(AGQ_EINVAL, "index arrays must be 4-byte aligned");
+    if (P > agq::kMaxPairs) return fail(AGQ_ENOTSUP, "P=%lld pairs exceeds %d", (long long)P, agq::kMaxPairs);
+    if (R > INT32_MAX) return fail(AGQ_EINVAL, "R too large");
+    if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
+    if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
+    agq::Plan plan;
+    if (agq::make_plan(8, N, K, bits, 256, E, &plan) != AGQ_OK)
+        return fail(AGQ_ENOTSUP, "K=%lld too large for the gather at %d bits", (long long)K, bits);
+    int cus = 0;
+    st = current_device(&cus);
+    if (st != AGQ_OK) return st;
+    agq::make_plan(8, N, K, bits, cus, E, &plan);
+    const void *sym = agq::product_kernel(bits, plan.mw, plan.cpt, true);
+    if (!sym) return fail(AGQ_ENOTSUP, "no gather kernel for bits=%d cpt=%d", bits, plan.cpt);
+    agq::ProductArgs a = make_args(x, w, scales, biases, y, N, K, bits, (int)P, plan);
+    a.lhs = lhs_indices;
+    a.rhs = rhs_indices;
+    a.R_x = (int32_t)R;
+    a.E = (int32_t)E;
+    return launch(sym, dim3((unsigned)plan.blocks, (unsigned)E), dim3(plan.threads), &a, stream);
+}
+
+agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *biases, float *out, int64_t rows,
+                          int64_t K, int bits, int group_size, void *stream) {
+    agq_status st = check_operands(nullptr, w, scales, biases, out, rows, K, bits, group_size, false);
+    if (st != AGQ_OK) return st;
+    if (misaligned(out, 16)) return fail(AGQ_EINVAL, "out must be 16-byte aligned");
+    int cus = 0;
+    st = current_device(&cus);
+    if (st != AGQ_OK) return st;
+    int64_t words_per_row = K * bits / 32;
+    int64_t words = rows * words_per_row;
+    int64_t blocks = (words + 255) / 256;
+    int64_t cap = (int64_t)cus * 32;
+    if (blocks > cap) blocks = cap;
+    const void *sym = agq::dequant_kernel_sym(bits);
+    void *args[] = {&w, &scales, &biases, &out, &words, &words_per_row, &K};
+    hipError_t e = hipLaunchKernel(sym, dim3((unsigned)blocks), dim3(256), args, 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(AGQ_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return AGQ_OK;
+}
+
+agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group_size, int num_cus, int64_t experts,
+                            agq_plan *out) {
+    if (!out) return fail(AGQ_EINVAL, "null plan pointer");
+    if (N <= 0 || K <= 0 || N > kMaxN || K > kMaxK || group_size <= 0 || experts < 0)
+        return fail(AGQ_EINVAL, "bad shape");
+    if (bits != 4 && bits != 8) return fail(AGQ_ENOTSUP, "bits=%d not supported", bits);
+    if (group_size != 64) return fail(AGQ_ENOTSUP, "group_size=%d not supported", group_size);
+    if (K % group_size) return fail(AGQ_EINVAL, "K not a multiple of group_size");
+    if (experts == 0 && (M <= 0)) return fail(AGQ_EINVAL, "M must be positive");
+    if (experts == 0 && M > 8) return fail(AGQ_ENOTSUP, "M > 8");
+    agq::Plan p;
+    if (agq::make_plan(experts ? 8 : M, N, K, bits, num_cus, experts, &p) != AGQ_OK)
+        return fail(AGQ_ENOTSUP, "K too large");
+    out->bits = p.bits;
+    out->chunks_per_row = p.C;
+    out->cpt = p.cpt;
+    out->mw = p.mw;
+    out->rows_per_iter = p.R;
+    out->waves_per_group = p.S;
+    out->groups_per_block = p.GPB;
+    out->threads_per_block = p.threads;
+    out->rows_per_group = p.RPG;
+    out->row_groups = p.TG;
+    out->blocks = p.blocks;
+    return AGQ_OK;
+}
+
+}  // extern "C"

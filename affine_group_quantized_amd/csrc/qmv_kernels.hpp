@@ -1,0 +1,35 @@
+// Kernel argument block and kernel lookup shared by the launcher and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace agq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Passed by value as the single kernel argument.
+struct ProductArgs {
+    const uint16_t *x;    // activation rows, bf16 [rows, K]
+    const u32x4 *w;       // packed codes in 16-byte chunks, [planes, N, C]
+    const uint16_t *s;    // bf16 scales [planes, N, G]
+    const uint16_t *b;    // bf16 biases [planes, N, G]
+    uint16_t *y;          // bf16 outputs [M or P, N]
+    const uint32_t *lhs;  // gather: x row per pair (NULL = identity)
+    const uint32_t *rhs;  // gather: expert per pair (NULL = identity)
+    int64_t N;            // weight rows per plane
+    int64_t RPG;          // weight rows per row group
+    int32_t K;            // columns
+    int32_t C;            // 16-byte chunks per weight row
+    int32_t G;            // 64-column groups per weight row
+    int32_t M;            // activation rows (dense) or pairs P (gather)
+    int32_t R_x;          // gather: rows of x
+    int32_t E;            // gather: expert planes
+    int32_t S;            // waves per row group (K split)
+    int32_t GPB;          // row groups per block
+};
+
+// Kernel symbol for (bits, activation rows per pass, chunks per lane), or NULL.
+const void *product_kernel(int bits, int mw, int cpt, bool gather);
+const void *dequant_kernel_sym(int bits);
+
+}  // namespace agq

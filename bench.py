@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the affine group-quantized matvec on one MI355X.
+
+Workload: the Llama-3-8B-shaped batch-1 decode GEMV set at 4 bits, group size
+64: qkv 6144x4096, o 4096x4096, gate_up 28672x4096, down 4096x14336 and
+lm_head 128256x4096. Inputs are seeded synthetic data (x ~ N(0,1) in bf16;
+W ~ N(0, 0.02) quantized per 64-column group). One step is one batch-1
+product through each of the five matrices.
+
+Every step reads its weights from one of ROT distinct copies, at least
+512 MiB in total, so the 256 MB Infinity Cache cannot serve repeated reads.
+Inputs are resident in HBM before timing starts.
+
+value: algorithmic bytes moved per step / measured time, in GB/s. Algorithmic
+bytes are N*K*bits/8 (codes) + 4*N*K/64 (bf16 scale and bias) + 2*K (x)
++ 2*N (y) per product.
+
+roofline: the kernel with the most time (the 4-bit, K=4096, batch-1
+instantiation, which runs qkv, o, gate_up and lm_head). HIP events around each
+of its launches inside the timed region give its average duration. Achieved
+GB/s is its algorithmic bytes per launch over that duration, against the
+8 TB/s HBM3E peak.
+
+cpu_baseline: the CPU oracle (single thread, float64) on a row sample of the
+same five matrices, sized to about --cpu-seconds of work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+ROTATION_BYTES = 512 * 1024 * 1024
+SHAPES = ["qkv", "o", "gate_up", "down", "lm_head"]
+
+
+def algo_bytes(N, K, bits, M=1):
+    return N * K * bits // 8 + 4 * N * K // 64 + 2 * M * K + 2 * M * N
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-shape", action="store_true", help="also time each matrix alone (to stderr)")
+    return ap.parse_args()
+
+
+def cpu_baseline(data, target_s):
+    """The oracle on an evenly spaced row sample of each matrix, ~target_s seconds in total."""
+    import numpy as np
+
+    import oracle
+    x = {"x4096": data["x4096"], "x14336": data["x14336"]}
+
+    def run(frac):
+        total_b, t0 = 0, time.perf_counter()
+        for name in SHAPES:
+            m = data[name]
+            n = max(1, int(m["N"] * frac))
+            rows = np.linspace(0, m["N"] - 1, n).astype(np.int64)
+            oracle.qmv(x[m["x"]], m["w"], m["scales"], m["biases"], m["K"], 4, rows=rows)
+            total_b += algo_bytes(n, m["K"], 4)
+        return total_b, time.perf_counter() - t0
+
+    b0, t0 = run(1 / 512)                      # calibration pass
+    frac = min(1.0, (1 / 512) * target_s / max(t0, 1e-3))
+    b, t = run(frac)
+    rows = sum(max(1, int(data[n]["N"] * frac)) for n in SHAPES)
+    return {
+        "value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{rows} evenly spaced weight rows ({frac:.4f} of each of the 5 matrices), batch 1, "
+                  f"{b / 1e6:.1f} MB algorithmic, {t:.1f} s single-threaded float64",
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this library has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import seeded_inputs as si
+    import affine_group_quantized_amd as agq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    data = si.workload(1)
+    print(f"[bench] generated workload in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def u32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to(dev)
+
+    step_bytes = sum(algo_bytes(data[n]["N"], data[n]["K"], 4) for n in SHAPES)
+    rot = max(2, math.ceil(ROTATION_BYTES / step_bytes))
+    xs = {"x4096": bf16(data["x4096"])[0], "x14336": bf16(data["x14336"])[0]}
+    mats = {}
+    for name in SHAPES:
+        m = data[name]
+        w0, s0, b0 = u32(m["w"]), bf16(m["scales"]), bf16(m["biases"])
+        copies = [(w0, s0, b0)] + [(w0.clone(), s0.clone(), b0.clone()) for _ in range(rot - 1)]
+        mats[name] = {"copies": copies, "x": xs[m["x"]], "N": m["N"], "K": m["K"],
+                      "y": torch.empty(m["N"], dtype=torch.bfloat16, device=dev)}
+    torch.cuda.synchronize()
+
+    plans = {n: agq.plan(1, mats[n]["N"], mats[n]["K"], 4) for n in SHAPES}
+    kern = lambda p: (p["cpt"], p["mw"], p["rows_per_iter"])  # noqa: E731  kernel instantiation key
+    # the dominant kernel: the instantiation with the most algorithmic bytes per step
+    by_kernel = {}
+    for n in SHAPES:
+        by_kernel.setdefault(kern(plans[n]), []).append(n)
+    dom_key = max(by_kernel, key=lambda k: sum(algo_bytes(mats[n]["N"], mats[n]["K"], 4) for n in by_kernel[k]))
+    dom = set(by_kernel[dom_key])
+    stream = torch.cuda.current_stream(dev)
+
+    calls = [{name: agq.prepare_qmv(mats[name]["x"], *mats[name]["copies"][r], mats[name]["y"], bits=4,
+                                    stream=stream) for name in SHAPES} for r in range(rot)]
+
+    def step(i, events=None):
+        c = calls[i % rot]
+        for name in SHAPES:
+            if events is not None and name in dom:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                c[name]()
+                e1.record(stream)
+                events.append((name, e0, e1))
+            else:
+                c[name]()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, events)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    value_gbps = step_bytes * args.steps / (total_ms * 1e-3) / 1e9
+
+    dom_ms = [e0.elapsed_time(e1) for _, e0, e1 in events]
+    dom_bytes = sum(algo_bytes(mats[n]["N"], mats[n]["K"], 4) for n in dom)
+    launches_per_step = len(dom)
+    avg_launch_s = (sum(dom_ms) / len(dom_ms)) * 1e-3
+    achieved = (dom_bytes / launches_per_step) / avg_launch_s / 1e9
+    per_shape_ms = {n: float(np.mean([t for (nn, _, _), t in zip(events, dom_ms) if nn == n])) for n in dom}
+
+    dom_name = "qmv_kernel<bits=4, cpt=%d, mw=%d, rows=%d>" % dom_key
+    result = {
+        "metric": "qmv achieved HBM GB/s (% of MI355X peak) + us/call, 4-bit gs64 decode shapes",
+        "value": round(value_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4 codes, bf16 in/out, fp32 accumulate",
+        "data": "synthetic (seeded; x ~ N(0,1) bf16, W ~ N(0,0.02) quantized 4-bit gs64)",
+        "config": {"workload": "Llama-3-8B-shaped decode GEMV set, batch 1, 4-bit gs64",
+                   "shapes": {n: [mats[n]["N"], mats[n]["K"]] for n in SHAPES},
+                   "bytes_per_step": step_bytes, "rotation_copies": rot,
+                   "pct_of_hbm_peak": round(100 * value_gbps / HBM_PEAK_GBPS, 2),
+                   "us_per_call_avg": round(ms_per_step * 1e3 / len(SHAPES), 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": dom_name, "launches_per_step": launches_per_step,
+                     "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                     "event_us_per_shape": {n: round(v * 1e3, 3) for n, v in per_shape_ms.items()}},
+    }
+
+    if args.per_shape:
+        for name in SHAPES:
+            m = mats[name]
+            ts = []
+            for i in range(max(20, 2 * rot)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                calls[i % rot][name]()
+                e1.record(stream)
+                ts.append((e0, e1))
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
+            gb = algo_bytes(m["N"], m["K"], 4) / (us * 1e-6) / 1e9
+            print(f"[bench] {name:8s} {m['N']}x{m['K']}: {us:8.2f} us/call  {gb:8.1f} GB/s  "
+                  f"{100 * gb / HBM_PEAK_GBPS:5.1f}% of peak", file=sys.stderr, flush=True)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * agq.h: C ABI of libagq, the affine group-quantized matrix-vector product
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes. An activation row x (BF16) multiplies a weight matrix W
+ * stored as U32-packed affine codes with BF16 per-group scales and biases.
+ * This is the operand triple named in "MLX CUDA Cleanup Plan", Target
+ * Architecture §1, with its rank-2 and rank-3-plane forms. Refactor Plan
+ * Phase 3 of that page fixes the formats: BF16 inputs, 4-bit or 8-bit codes,
+ * group size 64. For output row n:
+ *
+ *     y[m, n] = sum_k x[m, k] * (scale[n, k/64] * q[n, k] + bias[n, k/64])
+ *
+ * Code q[n, k] is stored low-first: it is bits [bits*(k % (32/bits)), +bits)
+ * of word k / (32/bits) of packed row n. W is [N out, K in]. Arithmetic is in
+ * fp32, and outputs are BF16, rounded to nearest even.
+ *
+ * The three product entry points map to the decode kernels those pages
+ * discuss:
+ *  - agq_qmv is the batch-1 matvec;
+ *  - agq_qmv_wide is the small-batch "qmv_wide" / multirow variant for
+ *    M*B > 1, named in "epic: CUDA (MLX backend) prefill and decode
+ *    acceleration program", Code-audit findings, and in the post-reboot
+ *    re-measurement pasted into mlxcel PR #727;
+ *  - agq_gather_qmv is the expert-gathered (MoE) form of the gather_qmm path
+ *    in the same epic.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major arrays. The
+ *    caller owns them; they must stay valid until the work queued on
+ *    `stream` completes. Outputs must not overlap inputs.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Each call queues
+ *    its kernels on that stream and returns at once. It never synchronizes,
+ *    allocates or copies. The current HIP device must be the one that holds
+ *    the buffers.
+ *  - BF16 tensors are passed as `const void *` and hold raw bfloat16 bit
+ *    patterns.
+ *  - Alignment: x and w 16 bytes; scales, biases and y 2 bytes; indices 4 bytes.
+ *  - Every argument check runs on the host before any HIP call, so a
+ *    rejected call touches no device state. AGQ_EINVAL means malformed
+ *    arguments. AGQ_ENOTSUP means well-formed but outside what this library
+ *    implements (including a current device other than gfx950); this is a
+ *    decline with no fallback path. AGQ_EHIP means the HIP runtime failed (no
+ *    device, or a launch error). agq_last_error() then holds a message for
+ *    the calling thread.
+ *  - Calls are reentrant and keep no state between calls besides a cached
+ *    per-device property record.
+ */
+#ifndef AGQ_H
+#define AGQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum agq_status {
+    AGQ_OK = 0,
+    AGQ_EINVAL = 1,
+    AGQ_ENOTSUP = 2,
+    AGQ_EHIP = 3
+} agq_status;
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int agq_version(void);
+
+/* Human-readable name of a status code. The string is static. */
+const char *agq_status_str(agq_status status);
+
+/* Detail message of the last non-OK status returned on this thread ("" if none). */
+const char *agq_last_error(void);
+
+/*
+ * Batch-1 matvec: y[n] = sum_k x[k] * w_hat[n, k].
+ *   x      [K] BF16
+ *   w      [N, K*bits/32] U32 packed codes
+ *   scales [N, K/group_size] BF16
+ *   biases [N, K/group_size] BF16
+ *   y      [N] BF16 (written)
+ * bits must be 4 or 8 and group_size 64 (else AGQ_ENOTSUP); K must be a
+ * positive multiple of group_size, and N positive (else AGQ_EINVAL). K above
+ * 131072 (4-bit) or 65536 (8-bit) is AGQ_ENOTSUP.
+ */
+agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
+                   void *y, int64_t N, int64_t K, int bits, int group_size, void *stream);
+
+/*
+ * Small-batch matvec ("qmv_wide"): y[m, n] = sum_k x[m, k] * w_hat[n, k] for
+ * 1 <= M <= 8 activation rows, streaming each weight byte once for all M rows.
+ *   x [M, K] BF16, y [M, N] BF16; w, scales and biases as in agq_qmv.
+ * M > 8 is AGQ_ENOTSUP; that is a quantized GEMM, not a matvec. The K limit
+ * shrinks with M: K <= 16384 * floor(8/M) for 4-bit and 8192 * floor(8/M)
+ * for 8-bit (larger K is AGQ_ENOTSUP).
+ */
+agq_status agq_qmv_wide(const void *x, const uint32_t *w, const void *scales, const void *biases,
+                        void *y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                        void *stream);
+
+/*
+ * Expert-gathered matvec for MoE decode. For each (token, expert) pair p:
+ *     y[p, n] = sum_k x[lhs[p], k] * w_hat[rhs[p]][n, k]
+ *   x       [R, K] BF16 activation rows
+ *   w       [E, N, K*bits/32] U32, stacked expert planes
+ *   scales  [E, N, K/group_size] BF16; biases the same
+ *   lhs_indices [P] uint32 row of x per pair. NULL means lhs[p] = p and requires R == P.
+ *   rhs_indices [P] uint32 expert per pair. NULL means rhs[p] = p and requires E == P.
+ *   y       [P, N] BF16 (written)
+ * Each expert plane that some pair uses is streamed from memory once for all
+ * of its pairs. Unused planes are never read. No router weighting and no sum
+ * over the top-k slots is applied. P may be at most 4096. Index values are
+ * device data and cannot be checked on the host. A pair whose lhs >= R or
+ * rhs >= E gets an all-NaN output row, and no memory outside the arrays is
+ * read. K limits are those of agq_qmv_wide at M = 8.
+ */
+agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
+                          const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y,
+                          int64_t P, int64_t R, int64_t E, int64_t N, int64_t K,
+                          int bits, int group_size, void *stream);
+
+/*
+ * Dequantize to fp32: out[n, k] = scale[n, k/64] * q[n, k] + bias[n, k/64],
+ * formed with one fused multiply-add, so each output is the exact value
+ * rounded once to binary32. The exact value is representable, and the result
+ * therefore exact, unless the bias exceeds the scale by more than about 2^15
+ * (BF16 scale and bias hold 8 significant bits each).
+ * `rows` covers stacked planes: pass E*N for a [E, N, .] tensor.
+ *   w [rows, K*bits/32] U32; scales/biases [rows, K/group_size] BF16; out [rows, K] fp32.
+ */
+agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *biases, float *out,
+                          int64_t rows, int64_t K, int bits, int group_size, void *stream);
+
+/*
+ * Launch plan (host-only introspection; no HIP call). It describes how the
+ * product kernels would tile a problem of this shape on a device with
+ * `num_cus` compute units. `experts` is 0 for agq_qmv / agq_qmv_wide and E
+ * for agq_gather_qmv (whose plan ignores M and sizes for 8 rows per pass).
+ */
+typedef struct agq_plan {
+    int32_t bits;            /* 4 or 8 */
+    int32_t chunks_per_row;  /* 16-byte chunks of packed codes per weight row */
+    int32_t cpt;             /* chunks per lane within a wave's K segment */
+    int32_t mw;              /* activation rows handled per pass */
+    int32_t rows_per_iter;   /* weight rows in flight per wave iteration */
+    int32_t waves_per_group; /* waves splitting K for one set of rows */
+    int32_t groups_per_block;
+    int32_t threads_per_block;
+    int64_t rows_per_group;
+    int64_t row_groups;
+    int64_t blocks;          /* grid size (per expert for gather) */
+} agq_plan;
+
+agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                            int num_cus, int64_t experts, agq_plan *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AGQ_H */

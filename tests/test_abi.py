@@ -1,0 +1,135 @@
+"""C-ABI tests that need no GPU: exported symbols, host-side validation, launch plans.
+
+Each validation case is malformed or unsupported, so the library rejects it
+before any HIP call; no fake pointer ever reaches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "agq.h")
+
+agq = pytest.importorskip("affine_group_quantized_amd")
+lib = agq.lib
+
+EINVAL, ENOTSUP = agq.AGQ_EINVAL, agq.AGQ_ENOTSUP
+A = ctypes.c_void_p(0x10000)      # 16-byte aligned stand-in address (never dereferenced)
+A2 = ctypes.c_void_p(0x10002)     # 2-byte aligned, not 16
+NUL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(agq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("agq_qmv", "agq_qmv_wide", "agq_gather_qmv", "agq_dequantize", "agq_status_str",
+                 "agq_last_error", "agq_version", "agq_plan_product"):
+        assert want in names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_library_exports_every_declared_symbol(name):
+    assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert lib.agq_status_str(0) == b"AGQ_OK"
+    assert lib.agq_status_str(1) == b"AGQ_EINVAL"
+    assert lib.agq_status_str(2) == b"AGQ_ENOTSUP"
+    assert lib.agq_status_str(3) == b"AGQ_EHIP"
+    assert lib.agq_version() >= 100
+
+
+def qmv(x=A, w=A, s=A, b=A, y=A, N=16, K=64, bits=4, gs=64):
+    return lib.agq_qmv(x, w, s, b, y, N, K, bits, gs, None)
+
+
+def wide(M=2, x=A, N=16, K=64, bits=4, gs=64):
+    return lib.agq_qmv_wide(x, A, A, A, A, M, N, K, bits, gs, None)
+
+
+def gather(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
+    return lib.agq_gather_qmv(x, A, A, A, lhs, rhs, A, P, R, E, N, K, bits, gs, None)
+
+
+@pytest.mark.parametrize("call,status", [
+    (lambda: qmv(x=NUL), EINVAL),
+    (lambda: qmv(w=NUL), EINVAL),
+    (lambda: qmv(y=NUL), EINVAL),
+    (lambda: qmv(N=0), EINVAL),
+    (lambda: qmv(K=0), EINVAL),
+    (lambda: qmv(N=-3), EINVAL),
+    (lambda: qmv(K=96), EINVAL),
+    (lambda: qmv(bits=3), ENOTSUP),
+    (lambda: qmv(bits=2), ENOTSUP),
+    (lambda: qmv(gs=32), ENOTSUP),
+    (lambda: qmv(gs=128, K=128), ENOTSUP),
+    (lambda: qmv(gs=0), EINVAL),
+    (lambda: qmv(x=A2), EINVAL),
+    (lambda: qmv(w=A2), EINVAL),
+    (lambda: qmv(s=ctypes.c_void_p(0x10001)), EINVAL),
+    (lambda: qmv(N=1 << 41), EINVAL),
+    (lambda: qmv(K=1 << 31), EINVAL),
+    (lambda: qmv(K=131072 + 64), ENOTSUP),
+    (lambda: qmv(K=65536 + 64, bits=8), ENOTSUP),
+    (lambda: wide(M=0), EINVAL),
+    (lambda: wide(M=-1), EINVAL),
+    (lambda: wide(M=9), ENOTSUP),
+    (lambda: wide(M=8, K=16384 + 64), ENOTSUP),
+    (lambda: wide(M=8, K=8192 + 64, bits=8), ENOTSUP),
+    (lambda: wide(M=2, K=65536 + 64), ENOTSUP),
+    (lambda: gather(P=0), EINVAL),
+    (lambda: gather(R=0), EINVAL),
+    (lambda: gather(E=0), EINVAL),
+    (lambda: gather(lhs=NUL, R=3), EINVAL),
+    (lambda: gather(rhs=NUL, E=3), EINVAL),
+    (lambda: gather(lhs=ctypes.c_void_p(0x10002)), EINVAL),
+    (lambda: gather(P=4097, R=4097, E=4), ENOTSUP),
+    (lambda: gather(E=70000), ENOTSUP),
+    (lambda: gather(K=16384 + 64), ENOTSUP),
+    (lambda: lib.agq_dequantize(A, A, A, ctypes.c_void_p(0x10004), 4, 64, 4, 64, None), EINVAL),
+    (lambda: lib.agq_dequantize(A, A, A, A, 4, 64, 5, 64, None), ENOTSUP),
+])
+def test_host_validation(call, status):
+    assert call() == status
+    assert lib.agq_last_error() != b""
+
+
+SHAPES = [  # (M, N, K, bits, experts)
+    (1, 4096, 4096, 4, 0), (1, 6144, 4096, 4, 0), (1, 28672, 4096, 4, 0), (1, 4096, 14336, 4, 0),
+    (1, 128256, 4096, 4, 0), (2, 14336, 4096, 4, 0), (4, 14336, 4096, 4, 0), (8, 14336, 4096, 4, 0),
+    (2, 4096, 14336, 4, 0), (4, 4096, 14336, 4, 0), (8, 4096, 14336, 4, 0),
+    (1, 4864, 896, 8, 0), (1, 896, 4864, 8, 0), (1, 1152, 896, 8, 0), (1, 151936, 896, 8, 0),
+    (8, 14336, 4096, 4, 8), (8, 4096, 14336, 4, 8),
+    (1, 1, 64, 4, 0), (3, 7, 192, 8, 0), (5, 33, 1088, 4, 0), (7, 100, 8192, 8, 0), (1, 5, 131072, 4, 0),
+    (8, 3, 16384, 4, 0), (2, 9, 4096, 4, 3), (1, 2, 64, 8, 1),
+]
+
+
+@pytest.mark.parametrize("M,N,K,bits,experts", SHAPES)
+@pytest.mark.parametrize("cus", [256, 304, 8])
+def test_plan_covers_the_problem(M, N, K, bits, experts, cus):
+    p = agq.plan(M, N, K, bits, 64, cus, experts)
+    C = K * bits // 128
+    assert p["chunks_per_row"] == C
+    assert 1 <= p["cpt"] <= 8 and p["cpt"] * p["mw"] <= 8
+    assert 1 <= p["waves_per_group"] <= 8
+    assert p["waves_per_group"] * p["cpt"] * 64 >= C                     # every chunk has a lane
+    assert (p["waves_per_group"] - 1) * p["cpt"] * 64 < C                 # no wave is idle
+    assert p["threads_per_block"] == 64 * p["waves_per_group"] * p["groups_per_block"] <= 512
+    assert p["rows_per_group"] % p["rows_per_iter"] == 0
+    assert p["row_groups"] * p["rows_per_group"] >= N                    # every row is covered
+    assert (p["row_groups"] - 1) * p["rows_per_group"] < N               # no group is empty
+    assert p["blocks"] * p["groups_per_block"] >= p["row_groups"]
+    assert p["rows_per_iter"] * p["mw"] <= 32
+    if experts:
+        assert p["mw"] == 8 and p["cpt"] == 1
+    else:
+        assert p["mw"] == M

@@ -1,0 +1,351 @@
+"""GPU parity: libagq through its C ABI against the CPU oracle, element by element.
+
+Tolerance: |y_gpu - y_ref| <= 2e-3 * sum_k |x_k * w_hat_k| per output element,
+with w_hat the dequantized weight. The adversarial closed-form cases, where
+|y| equals that sum, also allow half a bf16 ulp for the output rounding.
+Dequantization is compared bit for bit.
+
+Full-size workloads run in the launch configuration the benchmark uses. The
+oracle checks them on every row where it finishes in seconds, otherwise on a
+seeded sample of rows that includes the first and last rows and every
+row-group boundary.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from gpu_util import bf16_bits_host, bf16_dev, bf16_host, check_close, progress, u32_dev
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import affine_group_quantized_amd as agq  # noqa: E402  (loads libagq.so; fails loudly if missing)
+
+
+def dev_weight(d):
+    return u32_dev(d["w"]), bf16_dev(d["scales"]), bf16_dev(d["biases"])
+
+
+def sample_rows(N, plan, n_random=1024, seed=0):
+    """First/last rows, every row-group boundary, and a seeded random sample."""
+    rows = {0, N - 1}
+    rpg = plan["rows_per_group"]
+    for g in range(plan["row_groups"]):
+        for r in (g * rpg - 1, g * rpg, g * rpg + rpg - 1):
+            if 0 <= r < N:
+                rows.add(r)
+    rng = np.random.default_rng(seed)
+    rows.update(rng.integers(0, N, size=min(n_random, N)).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.fixture(scope="module")
+def wl():
+    cache = {}
+
+    def get(cfg):
+        if cfg not in cache:
+            progress(f"generating workload {cfg}")
+            cache[cfg] = si.workload(cfg)
+        return cache[cfg]
+    return get
+
+
+def run_qmv_case(name, x, d, K, bits, rows=None, M=None):
+    w, s, b = dev_weight(d)
+    xd = bf16_dev(x)
+    N = d["w"].shape[0]
+    progress(f"{name}: N={N} K={K} bits={bits} M={x.shape[0]}")
+    if x.shape[0] == 1 and M is None:
+        y = agq.qmv(xd[0], w, s, b, bits=bits)[None]
+    else:
+        y = agq.qmv_wide(xd, w, s, b, bits=bits)
+    torch.cuda.synchronize()
+    y_ref, A = oracle.qmv(x, d["w"], d["scales"], d["biases"], K, bits, rows=rows)
+    yg = y if rows is None else y[:, torch.as_tensor(rows, device=y.device)]
+    worst = check_close(yg, y_ref, A, name)
+    progress(f"{name}: ok, worst |err|/A = {worst:.3e}")
+    return y
+
+
+# ---------------------------------------------------------------- dequantize
+
+
+@pytest.mark.parametrize("bits,N,K", [(4, 4096, 4096), (8, 4864, 896), (8, 896, 4864), (4, 7, 64), (4, 33, 1088)])
+def test_dequantize_bit_exact(bits, N, K):
+    d = si.draw_quantized_weight(5, bits, N, K, bits)
+    w, s, b = dev_weight(d)
+    progress(f"dequantize bits={bits} N={N} K={K}")
+    out = agq.dequantize(w, s, b, bits=bits)
+    torch.cuda.synchronize()
+    ref, not_f32 = oracle.dequantize(d["w"], d["scales"], d["biases"], K, bits)
+    assert not_f32 == 0
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+
+
+def test_dequantize_expert_planes(wl):
+    d = si.draw_quantized_weight(6, 1, 3 * 96, 256, 4)
+    w = u32_dev(d["w"].reshape(3, 96, -1))
+    s = bf16_dev(d["scales"].reshape(3, 96, -1))
+    b = bf16_dev(d["biases"].reshape(3, 96, -1))
+    progress("dequantize planes [3,96,256]")
+    out = agq.dequantize(w, s, b, bits=4)
+    torch.cuda.synchronize()
+    ref, _ = oracle.dequantize(d["w"], d["scales"], d["biases"], 256, 4)
+    assert out.shape == (3, 96, 256)
+    assert np.array_equal(out.cpu().numpy().reshape(-1, 256), ref.astype(np.float32))
+
+
+# ---------------------------------------------------------------- workloads
+
+
+def test_workload0_qmv_4096(wl):
+    d = wl(0)
+    run_qmv_case("w0 qmv 4096x4096", d["x"], d["w"], 4096, 4)
+
+
+@pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down", "lm_head"])
+def test_workload1_llama_gemv_set(wl, name):
+    d = wl(1)
+    m = d[name]
+    rows = None
+    if m["N"] > 30000:
+        rows = sample_rows(m["N"], agq.plan(1, m["N"], m["K"], 4))
+    run_qmv_case(f"w1 {name}", d[m["x"]], m, m["K"], 4, rows=rows)
+
+
+@pytest.mark.parametrize("M", [2, 4, 8])
+@pytest.mark.parametrize("name", ["w_a", "w_b"])
+def test_workload2_qmv_wide(wl, name, M):
+    d = wl(2)
+    m = d[name]
+    rows = sample_rows(m["N"], agq.plan(M, m["N"], m["K"], 4), n_random=512)
+    run_qmv_case(f"w2 {name} M={M}", d[m["x"]][:M], m, m["K"], 4, rows=rows, M=M)
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down", "qkv", "lm_head"])
+def test_workload3_8bit(wl, name):
+    d = wl(3)
+    m = d[name]
+    rows = None if m["N"] < 10000 else sample_rows(m["N"], agq.plan(1, m["N"], m["K"], 8))
+    run_qmv_case(f"w3 {name}", d[m["x"]], m, m["K"], 8, rows=rows)
+
+
+@pytest.fixture(scope="module")
+def moe():
+    progress("generating workload 4 (MoE)")
+    return si.workload(4)
+
+
+@pytest.mark.parametrize("which", ["w1", "w2"])
+def test_workload4_gather(moe, which):
+    m = moe[which]
+    K, N, E = m["K"], m["N"], m["E"]
+    if which == "w1":
+        x, lhs = moe["x"], moe["lhs1"]
+    else:
+        x, lhs = moe["h"], None
+    rhs = moe["rhs"]
+    w = u32_dev(m["w"])
+    s = bf16_dev(m["scales"])
+    b = bf16_dev(m["biases"])
+    progress(f"w4 gather {which}: E={E} N={N} K={K} P={len(rhs)}")
+    y = agq.gather_qmv(bf16_dev(x), w, s, b, rhs_indices=u32_dev(rhs),
+                       lhs_indices=None if lhs is None else u32_dev(lhs), bits=4)
+    torch.cuda.synchronize()
+    rows = sample_rows(N, agq.plan(8, N, K, 4, experts=E), n_random=256)
+    y_ref, A = oracle.gather_qmv(x, m["w"], m["scales"], m["biases"], lhs, rhs, K, 4, rows=rows)
+    worst = check_close(y[:, torch.as_tensor(rows, device=y.device)], y_ref, A, f"w4 {which}")
+    progress(f"w4 gather {which}: ok, worst |err|/A = {worst:.3e}")
+
+
+# ---------------------------------------------------------------- shapes and edges
+
+
+@pytest.mark.parametrize("bits,M,N,K", [
+    (4, 1, 1, 64), (8, 1, 1, 64), (4, 1, 7, 192), (8, 3, 7, 192), (4, 1, 33, 4160), (8, 1, 33, 4160),
+    (4, 1, 1001, 896), (8, 1, 1001, 896), (4, 1, 300, 32768), (4, 1, 17, 131072), (8, 1, 9, 65536),
+    (4, 5, 129, 1088), (4, 6, 77, 8192), (4, 7, 64, 16384), (8, 7, 64, 8192), (4, 3, 513, 12288),
+    (8, 2, 257, 4864), (4, 8, 4099, 4096), (8, 8, 1000, 896), (4, 1, 4097, 4096), (8, 4, 3, 30720),
+])
+def test_shapes_and_ragged_tails(bits, M, N, K):
+    d = si.draw_quantized_weight(7, 100 * bits + M, N, K, bits)
+    x = si.draw_activations(7, 1000 + M, M, K)
+    run_qmv_case(f"shape M={M}", x, d, K, bits, M=None if M == 1 else M)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_constant_code_closed_form_adversarial(bits):
+    """|y| equals sum|x*w| here, so the bf16 output rounding alone can approach 4e-3*A."""
+    N, K = 64, 4096
+    g = np.random.default_rng(bits)
+    q = np.full((N, K), 2 ** bits - 1, np.uint8)
+    s = si.bf16_bits((0.01 + 0.01 * g.random((N, K // 64))).astype(np.float32))
+    b = si.bf16_bits((0.001 * g.random((N, K // 64))).astype(np.float32))
+    x = si.bf16_bits(np.abs(g.standard_normal((1, K))).astype(np.float32))
+    wq = si.pack_codes(q, bits)
+    progress(f"adversarial bits={bits}")
+    y = agq.qmv(bf16_dev(x)[0], u32_dev(wq), bf16_dev(s), bf16_dev(b), bits=bits)
+    torch.cuda.synchronize()
+    y_ref, A = oracle.qmv(x, wq, s, b, K, bits)
+    check_close(y[None], y_ref, A, "adversarial", extra_half_ulp=True)
+
+
+# ---------------------------------------------------------------- invariants
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_one_hot_columns_are_bitwise_weights(bits):
+    """x = e_k gives y[n] = bf16(w_hat[n, k]) exactly: one exact product per output."""
+    N, K = 515, 1024
+    d = si.draw_quantized_weight(8, bits, N, K, bits)
+    w, s, b = dev_weight(d)
+    ref, _ = oracle.dequantize(d["w"], d["scales"], d["biases"], K, bits)
+    want = si.bf16_bits(ref.astype(np.float32))
+    cols = list(range(0, 8)) + list(range(56, 72)) + [K - 9, K - 1] + list(np.random.default_rng(1).integers(0, K, 14))
+    for c0 in range(0, len(cols), 8):
+        cs = cols[c0:c0 + 8]
+        x = np.zeros((len(cs), K), np.uint16)
+        for i, c in enumerate(cs):
+            x[i, c] = 0x3F80
+        progress(f"one-hot bits={bits} cols={cs}")
+        y = agq.qmv_wide(bf16_dev(x), w, s, b, bits=bits)
+        torch.cuda.synchronize()
+        got = bf16_bits_host(y)
+        for i, c in enumerate(cs):
+            assert np.array_equal(got[i], want[:, c]), (bits, c)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_zero_x_gives_positive_zero(bits):
+    d = si.draw_quantized_weight(9, bits, 300, 2048, bits)
+    w, s, b = dev_weight(d)
+    progress(f"zero x bits={bits}")
+    y = agq.qmv(torch.zeros(2048, dtype=torch.bfloat16, device="cuda"), w, s, b, bits=bits)
+    torch.cuda.synchronize()
+    assert np.all(bf16_bits_host(y) == 0)
+
+
+@pytest.mark.parametrize("bits,M", [(4, 1), (8, 1), (4, 4), (4, 8)])
+def test_deterministic_and_power_of_two_scaling(bits, M):
+    N, K = 2000, 4096
+    d = si.draw_quantized_weight(10, bits, N, K, bits)
+    w, s, b = dev_weight(d)
+    x = si.draw_activations(10, 100 + M, M, K)
+    xd = bf16_dev(x)
+    progress(f"determinism bits={bits} M={M}")
+    f = (lambda t: agq.qmv(t[0], w, s, b, bits=bits)[None]) if M == 1 else (lambda t: agq.qmv_wide(t, w, s, b, bits=bits))
+    y1 = bf16_bits_host(f(xd))
+    y2 = bf16_bits_host(f(xd))
+    assert np.array_equal(y1, y2)
+    y4 = bf16_bits_host(f(xd * 4))        # exact: multiplying bf16 by 4 only shifts the exponent
+    assert np.array_equal(bf16_host(f(xd * 4)), 4 * bf16_host(f(xd)))
+    assert y4.shape == y1.shape
+
+
+def test_row_permutation_equivariance():
+    N, K = 1000, 4096
+    d = si.draw_quantized_weight(11, 4, N, K, 4)
+    x = bf16_dev(si.draw_activations(11, 1, 1, K))[0]
+    perm = np.random.default_rng(2).permutation(N)
+    w, s, b = dev_weight(d)
+    wp, sp, bp = dev_weight({k: v[perm] for k, v in d.items()})
+    progress("row permutation")
+    y = bf16_bits_host(agq.qmv(x, w, s, b))
+    yp = bf16_bits_host(agq.qmv(x, wp, sp, bp))
+    assert np.array_equal(yp, y[perm])
+
+
+def test_output_guard_region_untouched():
+    N, K = 1003, 4096
+    d = si.draw_quantized_weight(12, 4, N, K, 4)
+    w, s, b = dev_weight(d)
+    x = bf16_dev(si.draw_activations(12, 1, 3, K))
+    buf = torch.full((3 * N + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    sentinel = bf16_bits_host(buf[3 * N:]).copy()
+    progress("guard region")
+    agq.qmv_wide(x, w, s, b, out=buf[:3 * N].view(3, N))
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits_host(buf[3 * N:]), sentinel)
+
+
+def test_gather_matches_per_pair_qmv_and_identity_forms():
+    E, N, K, R = 4, 700, 4096, 5
+    planes = [si.draw_quantized_weight(13, e, N, K, 4) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(13, 99, R, K)
+    lhs = np.array([0, 1, 1, 4, 2, 3, 0, 4, 2], np.uint32)
+    rhs = np.array([3, 0, 2, 2, 2, 1, 0, 3, 2], np.uint32)
+    w, s, b = u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"])
+    xd = bf16_dev(x)
+    progress("gather vs per-pair qmv")
+    y = agq.gather_qmv(xd, w, s, b, rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs))
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, 4)
+    check_close(y, y_ref, A, "gather small")
+    for p in range(len(lhs)):
+        yp = agq.qmv(xd[lhs[p]], w[rhs[p]], s[rhs[p]], b[rhs[p]])
+        check_close(yp[None], y_ref[p:p + 1], A[p:p + 1], f"qmv pair {p}")
+    # NULL indices are the identity
+    y_id = agq.gather_qmv(xd[:4], w, s, b, rhs_indices=None, lhs_indices=None)
+    y_ex = agq.gather_qmv(xd[:4], w, s, b, rhs_indices=u32_dev(np.arange(4, dtype=np.uint32)),
+                          lhs_indices=u32_dev(np.arange(4, dtype=np.uint32)))
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits_host(y_id), bf16_bits_host(y_ex))
+
+
+def test_gather_many_pairs_one_expert_and_unused_experts():
+    """17 pairs on one expert (three passes of up to 8), other experts unused."""
+    E, N, K = 6, 300, 14336
+    planes = [si.draw_quantized_weight(14, e, N, K, 4) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(14, 99, 20, K)
+    lhs = np.arange(19, dtype=np.uint32) % 20
+    rhs = np.array([4] * 17 + [1, 4], np.uint32)
+    progress("gather 17 pairs on one expert")
+    y = agq.gather_qmv(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs))
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, 4)
+    check_close(y, y_ref, A, "gather one expert")
+
+
+def test_gather_out_of_range_indices_give_nan_rows():
+    E, N, K, R = 3, 130, 1024, 4
+    planes = [si.draw_quantized_weight(15, e, N, K, 8) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(15, 99, R, K)
+    lhs = np.array([0, 9, 2, 3], np.uint32)     # 9 >= R
+    rhs = np.array([1, 0, 7, 2], np.uint32)     # 7 >= E
+    progress("gather invalid indices")
+    y = agq.gather_qmv(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs), bits=8)
+    torch.cuda.synchronize()
+    yh = bf16_host(y)
+    assert np.all(np.isnan(yh[1])) and np.all(np.isnan(yh[2]))
+    ok = np.array([0, 3])
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs[ok], rhs[ok], K, 8)
+    check_close(y[torch.as_tensor(ok, device=y.device)], y_ref, A, "valid pairs")
+
+
+def test_wide_rows_equal_single_row_results():
+    """Row m of qmv_wide and qmv on x[m] both meet the tolerance against the same oracle."""
+    N, K = 4096, 14336
+    d = si.draw_quantized_weight(16, 4, N, K, 4)
+    w, s, b = dev_weight(d)
+    x = si.draw_activations(16, 1, 3, K)
+    progress("wide vs single rows")
+    yw = agq.qmv_wide(bf16_dev(x), w, s, b)
+    y_ref, A = oracle.qmv(x, d["w"], d["scales"], d["biases"], K, 4, rows=np.arange(0, N, 7))
+    cols = torch.arange(0, N, 7, device="cuda")
+    check_close(yw[:, cols], y_ref, A, "wide")
+    for m in range(3):
+        y1 = agq.qmv(bf16_dev(x[m]), w, s, b)
+        check_close(y1[cols][None], y_ref[m:m + 1], A[m:m + 1], f"single {m}")
