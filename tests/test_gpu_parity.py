@@ -173,7 +173,7 @@ def test_workload4_gather(moe, which):
     (4, 1, 1, 64), (8, 1, 1, 64), (4, 1, 7, 192), (8, 3, 7, 192), (4, 1, 33, 4160), (8, 1, 33, 4160),
     (4, 1, 1001, 896), (8, 1, 1001, 896), (4, 1, 300, 32768), (4, 1, 17, 131072), (8, 1, 9, 65536),
     (4, 5, 129, 1088), (4, 6, 77, 8192), (4, 7, 64, 16384), (8, 7, 64, 8192), (4, 3, 513, 12288),
-    (8, 2, 257, 4864), (4, 8, 4099, 4096), (8, 8, 1000, 896), (4, 1, 4097, 4096), (8, 4, 3, 30720),
+    (8, 2, 257, 4864), (4, 8, 4099, 4096), (8, 8, 1000, 896), (4, 1, 4097, 4096), (8, 4, 3, 16384),
 ])
 def test_shapes_and_ragged_tails(bits, M, N, K):
     d = si.draw_quantized_weight(7, 100 * bits + M, N, K, bits)
