@@ -18,7 +18,8 @@ import os
 
 import torch
 
-__all__ = ["qmv", "qmv_wide", "gather_qmv", "dequantize", "plan", "prepare_qmv", "AgqError", "LIB_PATH", "lib"]
+__all__ = ["qmv", "qmv_wide", "gather_qmv", "dequantize", "plan", "launch_plan", "prepare_qmv", "AgqError",
+           "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libagq.so")
 
@@ -42,6 +43,7 @@ class Plan(ctypes.Structure):
         ("mw", ctypes.c_int32), ("rows_per_iter", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
         ("groups_per_block", ctypes.c_int32), ("threads_per_block", ctypes.c_int32),
         ("rows_per_group", ctypes.c_int64), ("row_groups", ctypes.c_int64), ("blocks", ctypes.c_int64),
+        ("row_order", ctypes.c_int32), ("x_lds_bytes", ctypes.c_int32),
     ]
 
 
@@ -58,8 +60,10 @@ def _load(path: str = LIB_PATH):
     lib.agq_qmv_wide.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
     lib.agq_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.agq_dequantize.argtypes = [P, P, P, P, I64, I64, I, I, P]
-    lib.agq_plan_product.argtypes = [I64, I64, I64, I, I, I, I64, ctypes.POINTER(Plan)]
-    for f in (lib.agq_qmv, lib.agq_qmv_wide, lib.agq_gather_qmv, lib.agq_dequantize, lib.agq_plan_product):
+    lib.agq_plan_product.argtypes = [I64, I64, I64, I, I, I, I, I64, ctypes.POINTER(Plan)]
+    lib.agq_plan_launch.argtypes = [I64, I64, I64, I, I, I64, ctypes.POINTER(Plan)]
+    for f in (lib.agq_qmv, lib.agq_qmv_wide, lib.agq_gather_qmv, lib.agq_dequantize, lib.agq_plan_product,
+              lib.agq_plan_launch):
         f.restype = I
     return lib
 
@@ -237,8 +241,20 @@ def dequantize(w, scales, biases, bits: int = 4, group_size: int = 64, out=None)
     return out
 
 
-def plan(M: int, N: int, K: int, bits: int = 4, group_size: int = 64, num_cus: int = 256, experts: int = 0):
-    """The library's launch plan for a product of this shape (host only)."""
+def plan(M: int, N: int, K: int, bits: int = 4, group_size: int = 64, num_cus: int = 256, experts: int = 0,
+         waves_per_cu: int = 8):
+    """The library's launch plan for a product of this shape (host only).
+
+    ``waves_per_cu`` is the kernel's residency; the product calls take it from
+    the HIP occupancy query, so their grids can differ from this estimate.
+    """
     p = Plan()
-    _check(lib.agq_plan_product(M, N, K, bits, group_size, num_cus, experts, ctypes.byref(p)))
+    _check(lib.agq_plan_product(M, N, K, bits, group_size, num_cus, waves_per_cu, experts, ctypes.byref(p)))
+    return {name: getattr(p, name) for name, _ in Plan._fields_}
+
+
+def launch_plan(M: int, N: int, K: int, bits: int = 4, group_size: int = 64, experts: int = 0):
+    """The plan the product calls launch on the current device (queries HIP occupancy)."""
+    p = Plan()
+    _check(lib.agq_plan_launch(M, N, K, bits, group_size, experts, ctypes.byref(p)))
     return {name: getattr(p, name) for name, _ in Plan._fields_}

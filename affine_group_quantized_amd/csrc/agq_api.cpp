@@ -46,7 +46,7 @@ DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 
 // Current device's compute-unit count; checks once per device that it is gfx950.
-agq_status current_device(int *cus) {
+agq_status current_device(int *cus, int *ordinal) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(AGQ_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
@@ -67,6 +67,42 @@ agq_status current_device(int *cus) {
     }
     if (!d.gfx950) return fail(AGQ_ENOTSUP, "device %d is %s; libagq is built for gfx950 only", dev, d.arch);
     *cus = d.cus;
+    *ordinal = dev;
+    return AGQ_OK;
+}
+
+// Blocks of `sym` resident per compute unit, from the HIP occupancy query,
+// cached per kernel and device.
+struct OccEntry {
+    const void *sym;
+    int dev;
+    size_t lds;
+    int blocks_per_cu;
+};
+constexpr int kOccSlots = 256;
+OccEntry g_occ[kOccSlots];
+int g_occ_n = 0;
+std::mutex g_occ_mu;
+
+agq_status resident_waves(const void *sym, int threads, size_t lds, int cus, int dev, int64_t *waves) {
+    if (agq::kWavesPerCuOverride > 0) {
+        *waves = (int64_t)cus * agq::kWavesPerCuOverride;
+        return AGQ_OK;
+    }
+    int bpc = -1;
+    {
+        std::lock_guard<std::mutex> lock(g_occ_mu);
+        for (int i = 0; i < g_occ_n; ++i)
+            if (g_occ[i].sym == sym && g_occ[i].dev == dev && g_occ[i].lds == lds) bpc = g_occ[i].blocks_per_cu;
+    }
+    if (bpc < 0) {
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, sym, threads, lds);
+        if (e != hipSuccess) return fail(AGQ_EHIP, "occupancy query failed: %s", hipGetErrorString(e));
+        if (bpc < 1) bpc = 1;
+        std::lock_guard<std::mutex> lock(g_occ_mu);
+        if (g_occ_n < kOccSlots) g_occ[g_occ_n++] = OccEntry{sym, dev, lds, bpc};
+    }
+    *waves = (int64_t)cus * bpc * (threads / 64);
     return AGQ_OK;
 }
 
@@ -75,23 +111,66 @@ bool misaligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t
 constexpr int64_t kMaxN = int64_t(1) << 40;
 constexpr int64_t kMaxK = int64_t(1) << 30;
 
-// Format and operand checks shared by the products and dequantize.
-agq_status check_operands(const void *x, const void *w, const void *s, const void *b, const void *y, int64_t N,
-                          int64_t K, int bits, int group_size, bool need_x) {
-    if ((need_x && !x) || !w || !s || !b || !y) return fail(AGQ_EINVAL, "null tensor pointer");
-    if (N <= 0 || K <= 0) return fail(AGQ_EINVAL, "N and K must be positive (N=%lld, K=%lld)", (long long)N,
-                                      (long long)K);
-    if (N > kMaxN || K > kMaxK) return fail(AGQ_EINVAL, "N or K too large (N=%lld, K=%lld)", (long long)N,
-                                            (long long)K);
+// Format checks shared by every entry point.
+agq_status check_format(int64_t N, int64_t K, int bits, int group_size) {
+    if (N <= 0 || K <= 0)
+        return fail(AGQ_EINVAL, "N and K must be positive (N=%lld, K=%lld)", (long long)N, (long long)K);
+    if (N > kMaxN || K > kMaxK)
+        return fail(AGQ_EINVAL, "N or K too large (N=%lld, K=%lld)", (long long)N, (long long)K);
     if (group_size <= 0) return fail(AGQ_EINVAL, "group_size must be positive (got %d)", group_size);
     if (bits != 4 && bits != 8) return fail(AGQ_ENOTSUP, "bits=%d not supported (4 or 8)", bits);
     if (group_size != 64) return fail(AGQ_ENOTSUP, "group_size=%d not supported (64)", group_size);
     if (K % group_size != 0) return fail(AGQ_EINVAL, "K=%lld is not a multiple of group_size", (long long)K);
+    return AGQ_OK;
+}
+
+// Format and operand checks shared by the products and dequantize.
+agq_status check_operands(const void *x, const void *w, const void *s, const void *b, const void *y, int64_t N,
+                          int64_t K, int bits, int group_size, bool need_x) {
+    if ((need_x && !x) || !w || !s || !b || !y) return fail(AGQ_EINVAL, "null tensor pointer");
+    agq_status st = check_format(N, K, bits, group_size);
+    if (st != AGQ_OK) return st;
     if ((need_x && misaligned(x, 16)) || misaligned(w, 16))
         return fail(AGQ_EINVAL, "x and w must be 16-byte aligned");
     if (misaligned(s, 2) || misaligned(b, 2) || misaligned(y, 2))
         return fail(AGQ_EINVAL, "scales, biases and y must be 2-byte aligned");
     return AGQ_OK;
+}
+
+// Kernel and tiling for a product on the current device: the grid holds one
+// row group per resident wave set of the chosen kernel.
+agq_status launch_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t experts, agq::Plan *plan,
+                       const void **sym) {
+    const int64_t rows = experts > 0 ? 8 : M;
+    if (agq::plan_shape(rows, K, bits, experts, plan) != AGQ_OK)
+        return fail(AGQ_ENOTSUP, "K=%lld too large for %lld activation rows at %d bits", (long long)K,
+                    (long long)rows, bits);
+    int cus = 0, dev = 0;
+    agq_status st = current_device(&cus, &dev);
+    if (st != AGQ_OK) return st;
+    *sym = agq::product_kernel(bits, plan->mw, plan->cpt, experts > 0);
+    if (!*sym) return fail(AGQ_ENOTSUP, "no kernel for bits=%d rows=%d cpt=%d", bits, plan->mw, plan->cpt);
+    int64_t waves = 0;
+    st = resident_waves(*sym, plan->threads, (size_t)plan->x_lds_bytes, cus, dev, &waves);
+    if (st != AGQ_OK) return st;
+    agq::plan_grid(N, waves, experts, plan);
+    return AGQ_OK;
+}
+
+void export_plan(const agq::Plan &p, agq_plan *out) {
+    out->bits = p.bits;
+    out->chunks_per_row = p.C;
+    out->cpt = p.cpt;
+    out->mw = p.mw;
+    out->rows_per_iter = p.R;
+    out->waves_per_group = p.S;
+    out->groups_per_block = p.GPB;
+    out->threads_per_block = p.threads;
+    out->rows_per_group = p.RPG;
+    out->row_groups = p.TG;
+    out->blocks = p.blocks;
+    out->row_order = AGQ_ROW_ORDER_CONTIGUOUS ? 1 : 0;
+    out->x_lds_bytes = p.x_lds_bytes;
 }
 
 agq::ProductArgs make_args(const void *x, const uint32_t *w, const void *s, const void *b, void *y, int64_t N,
@@ -110,12 +189,13 @@ agq::ProductArgs make_args(const void *x, const uint32_t *w, const void *s, cons
     a.M = M;
     a.S = p.S;
     a.GPB = p.GPB;
+    a.x_lds = p.x_lds_bytes > 0 ? 1 : 0;
     return a;
 }
 
-agq_status launch(const void *sym, dim3 grid, dim3 block, void *arg, void *stream) {
+agq_status launch(const void *sym, dim3 grid, dim3 block, size_t lds, void *arg, void *stream) {
     void *args[] = {arg};
-    hipError_t e = hipLaunchKernel(sym, grid, block, args, 0, static_cast<hipStream_t>(stream));
+    hipError_t e = hipLaunchKernel(sym, grid, block, args, lds, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(AGQ_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return AGQ_OK;
 }
@@ -127,16 +207,13 @@ agq_status dense_product(const void *x, const uint32_t *w, const void *s, const 
     if (M <= 0) return fail(AGQ_EINVAL, "M must be positive (got %lld)", (long long)M);
     if (M > 8) return fail(AGQ_ENOTSUP, "M=%lld > 8 is a quantized GEMM, not a matvec", (long long)M);
     agq::Plan plan;
-    if (agq::make_plan(M, N, K, bits, 256, 0, &plan) != AGQ_OK)
+    if (agq::plan_shape(M, K, bits, 0, &plan) != AGQ_OK)  // host-only check before any HIP call
         return fail(AGQ_ENOTSUP, "K=%lld too large for M=%lld at %d bits", (long long)K, (long long)M, bits);
-    int cus = 0;
-    st = current_device(&cus);
+    const void *sym = nullptr;
+    st = launch_plan(M, N, K, bits, 0, &plan, &sym);
     if (st != AGQ_OK) return st;
-    agq::make_plan(M, N, K, bits, cus, 0, &plan);
-    const void *sym = agq::product_kernel(bits, plan.mw, plan.cpt, false);
-    if (!sym) return fail(AGQ_ENOTSUP, "no kernel for bits=%d M=%d cpt=%d", bits, plan.mw, plan.cpt);
     agq::ProductArgs a = make_args(x, w, s, b, y, N, K, bits, (int)M, plan);
-    return launch(sym, dim3((unsigned)plan.blocks), dim3(plan.threads), &a, stream);
+    return launch(sym, dim3((unsigned)plan.blocks), dim3(plan.threads), (size_t)plan.x_lds_bytes, &a, stream);
 }
 
 }  // namespace
@@ -184,20 +261,17 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
     if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
     if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
     agq::Plan plan;
-    if (agq::make_plan(8, N, K, bits, 256, E, &plan) != AGQ_OK)
+    if (agq::plan_shape(8, K, bits, E, &plan) != AGQ_OK)  // host-only check before any HIP call
         return fail(AGQ_ENOTSUP, "K=%lld too large for the gather at %d bits", (long long)K, bits);
-    int cus = 0;
-    st = current_device(&cus);
+    const void *sym = nullptr;
+    st = launch_plan(8, N, K, bits, E, &plan, &sym);
     if (st != AGQ_OK) return st;
-    agq::make_plan(8, N, K, bits, cus, E, &plan);
-    const void *sym = agq::product_kernel(bits, plan.mw, plan.cpt, true);
-    if (!sym) return fail(AGQ_ENOTSUP, "no gather kernel for bits=%d cpt=%d", bits, plan.cpt);
     agq::ProductArgs a = make_args(x, w, scales, biases, y, N, K, bits, (int)P, plan);
     a.lhs = lhs_indices;
     a.rhs = rhs_indices;
     a.R_x = (int32_t)R;
     a.E = (int32_t)E;
-    return launch(sym, dim3((unsigned)plan.blocks, (unsigned)E), dim3(plan.threads), &a, stream);
+    return launch(sym, dim3((unsigned)plan.blocks, (unsigned)E), dim3(plan.threads), 0, &a, stream);
 }
 
 agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *biases, float *out, int64_t rows,
@@ -205,8 +279,8 @@ agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *bia
     agq_status st = check_operands(nullptr, w, scales, biases, out, rows, K, bits, group_size, false);
     if (st != AGQ_OK) return st;
     if (misaligned(out, 16)) return fail(AGQ_EINVAL, "out must be 16-byte aligned");
-    int cus = 0;
-    st = current_device(&cus);
+    int cus = 0, dev = 0;
+    st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
     int64_t words_per_row = K * bits / 32;
     int64_t words = rows * words_per_row;
@@ -220,30 +294,35 @@ agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *bia
     return AGQ_OK;
 }
 
-agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group_size, int num_cus, int64_t experts,
-                            agq_plan *out) {
+agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group_size, int num_cus,
+                            int waves_per_cu, int64_t experts, agq_plan *out) {
     if (!out) return fail(AGQ_EINVAL, "null plan pointer");
-    if (N <= 0 || K <= 0 || N > kMaxN || K > kMaxK || group_size <= 0 || experts < 0)
-        return fail(AGQ_EINVAL, "bad shape");
-    if (bits != 4 && bits != 8) return fail(AGQ_ENOTSUP, "bits=%d not supported", bits);
-    if (group_size != 64) return fail(AGQ_ENOTSUP, "group_size=%d not supported", group_size);
-    if (K % group_size) return fail(AGQ_EINVAL, "K not a multiple of group_size");
-    if (experts == 0 && (M <= 0)) return fail(AGQ_EINVAL, "M must be positive");
+    agq_status st = check_format(N, K, bits, group_size);
+    if (st != AGQ_OK) return st;
+    if (experts < 0) return fail(AGQ_EINVAL, "experts must be >= 0");
+    if (experts == 0 && M <= 0) return fail(AGQ_EINVAL, "M must be positive");
+    if (experts == 0 && M > 8) return fail(AGQ_ENOTSUP, "M > 8");
+    if (num_cus <= 0 || waves_per_cu <= 0) return fail(AGQ_EINVAL, "num_cus and waves_per_cu must be positive");
+    agq::Plan p;
+    if (agq::make_plan(experts ? 8 : M, N, K, bits, (int64_t)num_cus * waves_per_cu, experts, &p) != AGQ_OK)
+        return fail(AGQ_ENOTSUP, "K too large");
+    export_plan(p, out);
+    return AGQ_OK;
+}
+
+agq_status agq_plan_launch(int64_t M, int64_t N, int64_t K, int bits, int group_size, int64_t experts,
+                           agq_plan *out) {
+    if (!out) return fail(AGQ_EINVAL, "null plan pointer");
+    agq_status st = check_format(N, K, bits, group_size);
+    if (st != AGQ_OK) return st;
+    if (experts < 0) return fail(AGQ_EINVAL, "experts must be >= 0");
+    if (experts == 0 && M <= 0) return fail(AGQ_EINVAL, "M must be positive");
     if (experts == 0 && M > 8) return fail(AGQ_ENOTSUP, "M > 8");
     agq::Plan p;
-    if (agq::make_plan(experts ? 8 : M, N, K, bits, num_cus, experts, &p) != AGQ_OK)
-        return fail(AGQ_ENOTSUP, "K too large");
-    out->bits = p.bits;
-    out->chunks_per_row = p.C;
-    out->cpt = p.cpt;
-    out->mw = p.mw;
-    out->rows_per_iter = p.R;
-    out->waves_per_group = p.S;
-    out->groups_per_block = p.GPB;
-    out->threads_per_block = p.threads;
-    out->rows_per_group = p.RPG;
-    out->row_groups = p.TG;
-    out->blocks = p.blocks;
+    const void *sym = nullptr;
+    st = launch_plan(M, N, K, bits, experts, &p, &sym);
+    if (st != AGQ_OK) return st;
+    export_plan(p, out);
     return AGQ_OK;
 }
 

@@ -9,30 +9,56 @@
 namespace agq {
 
 constexpr int kMaxWavesPerGroup = 8;   // kernels are built with __launch_bounds__(512)
-constexpr int kMaxCpt = 8;             // 16-byte chunks per lane in one wave's K segment
+#ifndef AGQ_MAX_CPT
+#define AGQ_MAX_CPT 7  // 8 chunks per lane plus two row buffers no longer fit in 256 VGPRs
+#endif
+constexpr int kMaxCpt = AGQ_MAX_CPT;   // 16-byte chunks per lane in one wave's K segment
 constexpr int kXRegBudget = 8;         // CPT * MW <= 8: staged activations use <= 128 VGPRs
 constexpr int kMaxPairs = 4096;        // gather: pair list kept in LDS as uint16
-constexpr int kWavesPerCuTarget = 8;
+#ifndef AGQ_WAVES_PER_CU
+#define AGQ_WAVES_PER_CU 0  // 0: size grids from the kernel's measured occupancy
+#endif
+#ifndef AGQ_LOADS_PER_LANE
+#define AGQ_LOADS_PER_LANE 8
+#endif
+constexpr int kWavesPerCuOverride = AGQ_WAVES_PER_CU;  // >0 forces this many waves per CU
+constexpr int kLoadsPerLane = AGQ_LOADS_PER_LANE;    // 16-byte weight loads in flight per lane
+#ifndef AGQ_PIPELINE
+#define AGQ_PIPELINE 1  // double-buffer the row loads (1) or rely on wave interleaving alone (0)
+#endif
+constexpr bool kPipelined = AGQ_PIPELINE != 0;
+#ifndef AGQ_ROW_ORDER_CONTIGUOUS
+#define AGQ_ROW_ORDER_CONTIGUOUS 0  // 0: row groups take R-row slices round-robin; 1: contiguous ranges
+#endif
 
-constexpr int floor_pow2(int v) { return v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
+constexpr int floor_pow2(int v) { return v >= 16 ? 16 : v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
 
-// Weight rows in flight per wave iteration. Aim for ~8 outstanding 16-byte
-// loads per lane; keep R*MW accumulators at or below 32.
+// Weight rows per wave iteration: aim for kLoadsPerLane outstanding 16-byte
+// loads per lane counting both buffers of the double-buffered loop; keep R*MW
+// accumulators at or below 16 (register pressure of the wide and gather forms).
 constexpr int rows_per_iter(int cpt, int mw) {
-    return floor_pow2(8 / cpt) < floor_pow2(32 / mw) ? floor_pow2(8 / cpt) : floor_pow2(32 / mw);
+    return floor_pow2(kLoadsPerLane / (kPipelined ? 2 : 1) / cpt) < floor_pow2(16 / mw)
+               ? floor_pow2(kLoadsPerLane / (kPipelined ? 2 : 1) / cpt)
+               : floor_pow2(16 / mw);
 }
+
+#ifndef AGQ_X_LDS_MAX
+#define AGQ_X_LDS_MAX 65536
+#endif
+constexpr int kXLdsMax = AGQ_X_LDS_MAX;  // largest activation block staged in LDS (bytes)
 
 struct Plan {
     int bits = 0, C = 0, cpt = 0, mw = 0, R = 0, S = 0, GPB = 0, threads = 0;
+    int x_lds_bytes = 0;  // dynamic LDS for x; 0 = waves stage x straight from global memory
     int64_t RPG = 0, TG = 0, blocks = 0;
 };
 
-// Returns AGQ_OK and fills `p`, or AGQ_ENOTSUP when K is too large for the
-// register-resident activation scheme at this M. Arguments are assumed valid
-// otherwise (bits in {4,8}, K % 64 == 0, N >= 1, 1 <= M <= 8). `experts` is 0
-// for the dense products and the number of expert planes for the gather, whose
-// grid repeats the row tiling once per plane.
-inline agq_status make_plan(int64_t M, int64_t N, int64_t K, int bits, int num_cus, int64_t experts, Plan *p) {
+// Kernel shape: chunks per lane, K split, rows per iteration, block size.
+// Returns AGQ_ENOTSUP when K is too large for the register-resident activation
+// scheme at this M. Arguments are assumed valid otherwise (bits in {4,8},
+// K % 64 == 0, N >= 1, 1 <= M <= 8). `experts` is 0 for the dense products and
+// the number of expert planes for the gather.
+inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Plan *p) {
     const bool gather = experts > 0;
     Plan q;
     q.bits = bits;
@@ -52,15 +78,39 @@ inline agq_status make_plan(int64_t M, int64_t N, int64_t K, int bits, int num_c
     q.R = rows_per_iter(q.cpt, q.mw);
     q.GPB = q.S == 1 ? 4 : (q.S == 2 ? 2 : 1);
     q.threads = 64 * q.S * q.GPB;
-    int64_t waves = (int64_t)(num_cus > 0 ? num_cus : 256) * kWavesPerCuTarget;
-    int64_t tg_target = waves / q.S / (gather ? experts : 1);
+    // The waves of a block share their K columns only when each row group is a
+    // single wave; then one LDS copy of x serves the whole block.
+    const int64_t xbytes = 2 * (int64_t)q.mw * K;
+    q.x_lds_bytes = (!gather && q.S == 1 && q.GPB > 1 && xbytes <= kXLdsMax) ? (int)xbytes : 0;
+    *p = q;
+    return AGQ_OK;
+}
+
+// Row tiling: one row group per resident wave set, so the whole grid is
+// resident at once (no second, partly empty round of waves). `resident_waves`
+// is the number of waves of this kernel the device holds at once (compute
+// units times waves per unit at the kernel's occupancy). For the gather, the
+// grid repeats per expert plane and the budget is shared among the planes.
+inline void plan_grid(int64_t N, int64_t resident_waves, int64_t experts, Plan *q) {
+    int64_t tg_target = resident_waves / q->S / (experts > 0 ? experts : 1);
     if (tg_target < 1) tg_target = 1;
-    int64_t rpg = (N + tg_target - 1) / tg_target;
-    rpg = ((rpg + q.R - 1) / q.R) * q.R;
-    if (rpg < q.R) rpg = q.R;
-    q.RPG = rpg;
-    q.TG = (N + rpg - 1) / rpg;
-    q.blocks = (q.TG + q.GPB - 1) / q.GPB;
+    // Iterations per group: a multiple of 2 when the row loop is double-buffered.
+    const int64_t step = kPipelined ? 2 : 1;
+    int64_t iters = (N + tg_target * q->R - 1) / (tg_target * q->R);
+    iters = ((iters + step - 1) / step) * step;
+    // The fewest groups that cover N rows in `iters` iterations of R rows.
+    q->TG = (N + iters * q->R - 1) / (iters * q->R);
+    q->RPG = iters * q->R;
+    q->blocks = (q->TG + q->GPB - 1) / q->GPB;
+    q->TG = q->blocks * q->GPB;  // every launched group walks rows (groups past N store nothing)
+}
+
+inline agq_status make_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t resident_waves, int64_t experts,
+                            Plan *p) {
+    Plan q;
+    agq_status st = plan_shape(M, K, bits, experts, &q);
+    if (st != AGQ_OK) return st;
+    plan_grid(N, resident_waves, experts, &q);
     *p = q;
     return AGQ_OK;
 }

@@ -29,13 +29,24 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // A 4-bit code q placed in the low mantissa bits of bfloat16 0x4300 (= 128.0)
-// reads as the exact value 128 + q. For packed word `w` (codes q0..q7 of eight
-// consecutive columns, low-first) this yields the bfloat16 pair
-// (128 + q_i, 128 + q_{i+4}) with one shift and one AND-OR.
-template <int I>
-__device__ __forceinline__ uint32_t nibble_pair(uint32_t w) {
-    return ((w >> (4 * I)) & 0x000F000Fu) | 0x43004300u;
+// reads as the exact value 128 + q. For a packed word w holding the codes
+// q0..q7 of eight consecutive columns (low-first), lo = w & 0x0F0F0F0F has
+// bytes (q0, q2, q4, q6) and hi = (w >> 4) & 0x0F0F0F0F has (q1, q3, q5, q7).
+// One byte permute against 0x43 bytes then yields the bfloat16 pair
+// (128 + q_a, 128 + q_b):
+//   perm(.., lo, kSelEven) = (q0, q4)   perm(.., lo, kSelOdd) = (q2, q6)
+//   perm(.., hi, kSelEven) = (q1, q5)   perm(.., hi, kSelOdd) = (q3, q7)
+// That is 7 VALU ops for 8 codes (and, shift, and, 4 v_perm_b32).
+constexpr uint32_t kMagic43 = 0x43434343u;
+constexpr uint32_t kSelEven = 0x04020400u;  // bytes: lo.b0, 0x43, lo.b2, 0x43
+constexpr uint32_t kSelOdd = 0x04030401u;   // bytes: lo.b1, 0x43, lo.b3, 0x43
+
+__device__ __forceinline__ uint32_t byte_perm(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }
+
+// Wave index within the block, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {

@@ -24,10 +24,10 @@
 //    deterministic.
 //
 // 4-bit inner loop. Each packed word gives four bfloat16 pairs (128 + q)
-// through nibble_pair(). v_dot2c_f32_bf16 multiplies them by activation pairs
-// staged in the same (i, i+4) column order. The accumulator starts at
-// -128 * sum(x) of the chunk, which cancels the offset. That is 0.875 integer
-// ops plus 0.5 dot ops per weight.
+// with one AND, one shift-AND and four byte permutes. v_dot2c_f32_bf16
+// multiplies them by activation pairs staged in the matching column order.
+// The accumulator starts at -128 * sum(x) of the chunk, which cancels the
+// offset. That is 0.875 integer ops plus 0.5 dot ops per weight.
 //
 // 8-bit inner loop: v_cvt_f32_ubyte{0..3} and fp32 FMA, two ops per weight.
 //
@@ -43,7 +43,14 @@
 
 namespace agq {
 
-constexpr int kRedSlots = kMaxWavesPerGroup * 64;  // per buffer: GPB*S*R*MW <= 8 waves * 64 values
+constexpr int kRedSlots = kMaxWavesPerGroup * 64;
+
+#ifndef AGQ_X_FIRST
+#define AGQ_X_FIRST 0  // 1: copy x into LDS before issuing the first weight loads
+#endif
+
+// Dynamic LDS of the dense product kernels: the block's copy of x [M, K] (bf16).
+extern __shared__ u32x4 g_xlds[];  // per buffer: GPB*S*R*MW <= 8 waves * 64 values
 
 template <int BITS>
 struct Fmt {
@@ -51,43 +58,35 @@ struct Fmt {
     static constexpr int CPG = 64 / EPC;    // chunks per 64-column group
 };
 
-// Stage one lane's activation slice for chunk `c` of activation row `xr`.
-// 4-bit: 16 bfloat16 pairs in (i, i+4) order per packed word. 8-bit: 16 fp32.
+// Turn one lane's raw activation chunk (4 x 16 B = 32 bf16 for 4-bit codes,
+// 2 x 16 B = 16 bf16 for 8-bit) into its staged form: 4-bit, 16 bfloat16 pairs
+// in the (i, i+4) order of the code pairs of each packed word; 8-bit, 16 fp32.
+// xs receives the chunk's sum of x. `keep` is all ones, or zero for a lane
+// past the end of the row.
 template <int BITS>
-__device__ __forceinline__ void stage_x(const uint16_t *__restrict__ xr, int c, bool valid, uint32_t (&xv)[16],
-                                        float &xs) {
+__device__ __forceinline__ void stage_from_words(const u32x4 *d, uint32_t keep, uint32_t (&xv)[16], float &xs) {
     if constexpr (BITS == 4) {
-        u32x4 d[4] = {};
-        if (valid) {
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(xr + (int64_t)c * 32);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) d[t] = p[t];
-        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            xv[4 * t + 0] = (d[t].x & 0xFFFFu) | (d[t].z << 16);
-            xv[4 * t + 1] = (d[t].x >> 16) | (d[t].z & 0xFFFF0000u);
-            xv[4 * t + 2] = (d[t].y & 0xFFFFu) | (d[t].w << 16);
-            xv[4 * t + 3] = (d[t].y >> 16) | (d[t].w & 0xFFFF0000u);
+            const u32x4 q = d[t] & keep;
+            xv[4 * t + 0] = (q.x & 0xFFFFu) | (q.z << 16);
+            xv[4 * t + 1] = (q.x >> 16) | (q.z & 0xFFFF0000u);
+            xv[4 * t + 2] = (q.y & 0xFFFFu) | (q.w << 16);
+            xv[4 * t + 3] = (q.y >> 16) | (q.w & 0xFFFF0000u);
         }
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) s = dot2_bf16(xv[i], 0x3F803F80u, s);
         xs = s;
     } else {
-        u32x4 d[2] = {};
-        if (valid) {
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(xr + (int64_t)c * 16);
-            d[0] = p[0];
-            d[1] = p[1];
-        }
         float s = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            uint32_t dw[4] = {d[t].x, d[t].y, d[t].z, d[t].w};
+            const u32x4 q = d[t] & keep;
+            const uint32_t dw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float lo = bf16_lo(dw[i]), hi = bf16_hi(dw[i]);
+                const float lo = bf16_lo(dw[i]), hi = bf16_hi(dw[i]);
                 xv[8 * t + 2 * i] = __float_as_uint(lo);
                 xv[8 * t + 2 * i + 1] = __float_as_uint(hi);
                 s += lo;
@@ -98,23 +97,60 @@ __device__ __forceinline__ void stage_x(const uint16_t *__restrict__ xr, int c, 
     }
 }
 
-// Partial dot product of one chunk with one staged activation slice.
+// Stage chunk `c` (in range) of activation row `xr` from global memory.
 template <int BITS>
-__device__ __forceinline__ float chunk_dot(const u32x4 &wv, const uint32_t (&xv)[16], float xs) {
+__device__ __forceinline__ void stage_x(const uint16_t *__restrict__ xr, int c, bool valid, uint32_t (&xv)[16],
+                                        float &xs) {
+    constexpr int W = BITS == 4 ? 4 : 2;
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(xr) + (int64_t)c * W;
+    u32x4 d[W];
+#pragma unroll
+    for (int t = 0; t < W; ++t) d[t] = p[t];
+    stage_from_words<BITS>(d, valid ? 0xFFFFFFFFu : 0u, xv, xs);
+}
+
+// The same from the block's LDS copy of x: row m starts at 16-byte word m*K/8.
+template <int BITS>
+__device__ __forceinline__ void stage_x_lds(int64_t row_word, int c, bool valid, uint32_t (&xv)[16], float &xs) {
+    constexpr int W = BITS == 4 ? 4 : 2;
+    const int base = (int)row_word + c * W;
+    u32x4 d[W];
+#pragma unroll
+    for (int t = 0; t < W; ++t) d[t] = g_xlds[base + t];
+    stage_from_words<BITS>(d, valid ? 0xFFFFFFFFu : 0u, xv, xs);
+}
+
+// Block-cooperative copy of the activation rows x[0..M) (contiguous, 16-byte
+// aligned) into LDS, then a barrier that every wave of the block must reach.
+// The waves then stage their lane slices from LDS instead of each pulling x
+// through L2.
+__device__ __forceinline__ void copy_x_to_lds(const uint16_t *__restrict__ x, int64_t elems) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(x);
+    const int n16 = (int)(elems / 8);
+    for (int i = threadIdx.x; i < n16; i += blockDim.x) g_xlds[i] = src[i];
+    __syncthreads();
+}
+
+// Partial dot product of one chunk with one staged activation slice.
+// 4-bit: the accumulator starts at -128 * sum(x) (nxs), cancelling the 128 offset
+// of the bfloat16 code pairs.
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(const u32x4 &wv, const uint32_t (&xv)[16], float nxs) {
+    const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
     if constexpr (BITS == 4) {
-        float d = -128.f * xs;
-        const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
+        float d = nxs;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            d = dot2_bf16(nibble_pair<0>(w[t]), xv[4 * t + 0], d);
-            d = dot2_bf16(nibble_pair<1>(w[t]), xv[4 * t + 1], d);
-            d = dot2_bf16(nibble_pair<2>(w[t]), xv[4 * t + 2], d);
-            d = dot2_bf16(nibble_pair<3>(w[t]), xv[4 * t + 3], d);
+            const uint32_t lo = w[t] & 0x0F0F0F0Fu;
+            const uint32_t hi = (w[t] >> 4) & 0x0F0F0F0Fu;
+            d = dot2_bf16(byte_perm(kMagic43, lo, kSelEven), xv[4 * t + 0], d);
+            d = dot2_bf16(byte_perm(kMagic43, hi, kSelEven), xv[4 * t + 1], d);
+            d = dot2_bf16(byte_perm(kMagic43, lo, kSelOdd), xv[4 * t + 2], d);
+            d = dot2_bf16(byte_perm(kMagic43, hi, kSelOdd), xv[4 * t + 3], d);
         }
         return d;
     } else {
         float d = 0.f;
-        const uint32_t w[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             d = fmaf(__uint_as_float(xv[4 * t + 0]), (float)(w[t] & 0xFFu), d);
@@ -126,120 +162,236 @@ __device__ __forceinline__ float chunk_dot(const u32x4 &wv, const uint32_t (&xv)
     }
 }
 
+// One iteration's worth of packed codes, scales and biases for R weight rows.
+template <int CPT, int R>
+struct RowBuf {
+    u32x4 w[R][CPT];
+    uint32_t s[R][CPT];
+    uint32_t b[R][CPT];
+};
+
+// Issue every load of rows [rb, rb + R) at once. Row and chunk indices are
+// clamped into range, so no load is conditional (a conditional load forces the
+// compiler to wait for it before the next one). Clamped duplicates are never
+// stored: out-of-range rows are skipped at the store and out-of-range chunks
+// meet zero activations. Row bases are wave-uniform scalar pointers and lane
+// offsets unsigned 32-bit byte offsets (the saddr + voffset load form).
+template <int BITS, int CPT, int R>
+__device__ __forceinline__ void load_rows(RowBuf<CPT, R> &buf, const u32x4 *__restrict__ wp,
+                                          const uint16_t *__restrict__ sp, const uint16_t *__restrict__ bp,
+                                          int64_t rb, int64_t row_last, const uint32_t (&woff)[CPT],
+                                          const uint32_t (&goff)[CPT], int64_t C, int64_t G) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = rb + r < row_last ? rb + r : row_last;
+        const char *wr = reinterpret_cast<const char *>(wp + row * C);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j)
+            buf.w[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr + woff[j]));
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t row = rb + r < row_last ? rb + r : row_last;
+        const char *sr = reinterpret_cast<const char *>(sp + row * G);
+        const char *br = reinterpret_cast<const char *>(bp + row * G);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            buf.s[r][j] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(sr + goff[j]));
+            buf.b[r][j] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(br + goff[j]));
+        }
+    }
+}
+
+// Partial sums of one lane for R rows and MW activation rows.
+template <int BITS, int CPT, int MW, int R>
+__device__ __forceinline__ void compute_rows(const RowBuf<CPT, R> &buf, const uint32_t (&xv)[MW][CPT][16],
+                                             const float (&xs)[MW][CPT], const float (&nxs)[MW][CPT],
+                                             float (&acc)[R][MW]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MW; ++m) acc[r][m] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const float sf = bf16_lo(buf.s[r][j]);
+            const float bf = bf16_lo(buf.b[r][j]);
+#pragma unroll
+            for (int m = 0; m < MW; ++m) {
+                const float d = chunk_dot<BITS>(buf.w[r][j], xv[m][j], nxs[m][j]);
+                acc[r][m] = fmaf(sf, d, acc[r][m]);
+                acc[r][m] = fmaf(bf, xs[m][j], acc[r][m]);
+            }
+        }
+    }
+}
+
+// Reduce lane partials to row results and store them (rows >= row1 are dropped).
+// With S > 1 the S waves of a row group combine through LDS in a fixed order.
+template <int MW, int R>
+__device__ __forceinline__ void finish_rows(float (&acc)[R][MW], uint16_t *const *yrow, int64_t rb, int64_t row1,
+                                            int S, int wig, int grp, int lane, float *buf) {
+    if (S == 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MW; ++m) {
+                const float t = wave_sum(acc[r][m]);
+                if (lane == 0 && rb + r < row1) yrow[m][rb + r] = f32_to_bf16(t);
+            }
+        return;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+            const float t = wave_sum(acc[r][m]);
+            if (lane == 0) buf[(grp * S + wig) * (R * MW) + r * MW + m] = t;
+        }
+    __syncthreads();
+    if (wig == 0 && lane < R * MW) {
+        const int r = lane / MW, m = lane % MW;
+        float t = 0.f;
+        for (int s = 0; s < S; ++s) t += buf[(grp * S + s) * (R * MW) + lane];
+        if (rb + r < row1) {
+#pragma unroll
+            for (int mm = 0; mm < MW; ++mm)
+                if (mm == m) yrow[mm][rb + r] = f32_to_bf16(t);
+        }
+    }
+}
+
+// The weight rows a row group visits: iteration `it` covers rows
+// [at(it), at(it) + R), dropping rows >= end.
+//  - Interleaved (default): row groups take R-row slices round-robin, so at
+//    any moment the whole grid reads one compact band of the matrix.
+//  - Contiguous: each group walks its own range of RPG rows.
+struct RowWalk {
+    int64_t first;   // first row of iteration 0
+    int64_t stride;  // rows between consecutive iterations
+    int64_t end;     // rows >= end are not stored (and loads clamp to end - 1)
+    __device__ __forceinline__ int64_t at(int it) const { return first + (int64_t)it * stride; }
+};
+
+template <int R>
+__device__ __forceinline__ RowWalk row_walk(const ProductArgs &a, int64_t rg, int64_t groups) {
+#if AGQ_ROW_ORDER_CONTIGUOUS
+    const int64_t row0 = rg * a.RPG;
+    return RowWalk{row0, R, row0 + a.RPG < a.N ? row0 + a.RPG : a.N};
+#else
+    return RowWalk{rg * R, groups * R, a.N};
+#endif
+}
+
 // Shared core: MW activation rows (xrow[m]) against weight rows [row0, row1) of
 // one plane; outputs to yrow[m][n]. `iters` must be equal for every row group of
 // the block when S > 1 (block-wide barriers).
+//
+// The row loop is software-pipelined over two register buffers: the loads of
+// the next R rows are in flight while the current R rows are computed.
 template <int BITS, int CPT, int MW, int R>
 __device__ __forceinline__ void product_rows(const ProductArgs &a, const u32x4 *__restrict__ wp,
                                              const uint16_t *__restrict__ sp, const uint16_t *__restrict__ bp,
                                              const uint16_t *const *xrow, uint16_t *const *yrow,
-                                             int64_t row0, int64_t row1, int iters, float *red) {
-    using F = Fmt<BITS>;
+                                             const RowWalk &walk, int iters, float *red,
+                                             bool x_in_lds = false) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int S = a.S;
     const int wig = wave % S;
     const int grp = wave / S;
 
-    int chunk[CPT];
+    int chunk[CPT];   // clamped chunk index: lanes past the row end reload the last chunk
     bool cv[CPT];
+    uint32_t woff[CPT], goff[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        chunk[j] = (wig * CPT + j) * 64 + lane;
-        cv[j] = chunk[j] < a.C;
+        const int c = (wig * CPT + j) * 64 + lane;
+        cv[j] = c < a.C;
+        chunk[j] = cv[j] ? c : a.C - 1;
+        woff[j] = (uint32_t)chunk[j] * 16u;
+        goff[j] = (uint32_t)(chunk[j] / Fmt<BITS>::CPG) * 2u;
     }
 
+    const int64_t C = a.C, G = a.G;
+    // Loads clamp to the last row of the walk, so iterations past the end
+    // re-read that row and store nothing; no load is ever out of bounds.
+    const int64_t row_last = walk.end - 1;
+    RowBuf<CPT, R> A;
+#if AGQ_PIPELINE
+    RowBuf<CPT, R> B;
+#endif
+#if AGQ_X_FIRST
+    if (x_in_lds) copy_x_to_lds(xrow[0], (int64_t)MW * a.K);  // block barrier: every wave of the block gets here
+#endif
+    // The first weight loads go out before the activation staging, so the
+    // staging overlaps their latency.
+    load_rows<BITS, CPT, R>(A, wp, sp, bp, walk.at(0), row_last, woff, goff, C, G);
+#if AGQ_PIPELINE
+    load_rows<BITS, CPT, R>(B, wp, sp, bp, walk.at(1), row_last, woff, goff, C, G);
+#endif
+
     uint32_t xv[MW][CPT][16];
-    float xs[MW][CPT];
+    float xs[MW][CPT], nxs[MW][CPT];
+    // Activation slices: from the block's LDS copy of x when there is one,
+    // otherwise straight from global memory (xrow).
+    if (x_in_lds) {
+#if !AGQ_X_FIRST
+        copy_x_to_lds(xrow[0], (int64_t)MW * a.K);  // block barrier: every wave of the block gets here
+#endif
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+#pragma unroll
+            for (int j = 0; j < CPT; ++j)
+                stage_x_lds<BITS>((int64_t)m * a.K / 8, chunk[j], cv[j], xv[m][j], xs[m][j]);
+    } else {
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) stage_x<BITS>(xrow[m], chunk[j], cv[j], xv[m][j], xs[m][j]);
+    }
 #pragma unroll
     for (int m = 0; m < MW; ++m)
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) stage_x<BITS>(xrow[m], chunk[j], cv[j], xv[m][j], xs[m][j]);
+        for (int j = 0; j < CPT; ++j) nxs[m][j] = BITS == 4 ? -128.f * xs[m][j] : 0.f;
 
-    const int64_t C = a.C, G = a.G;
-    for (int it = 0; it < iters; ++it) {
-        const int64_t rb = row0 + (int64_t)it * R;
-        u32x4 wv[R][CPT];
-        uint32_t sv[R][CPT], bv[R][CPT];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const bool rv = rb + r < row1;
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                wv[r][j] = u32x4{0u, 0u, 0u, 0u};
-                sv[r][j] = 0u;
-                bv[r][j] = 0u;
-                if (rv && cv[j]) {
-                    const int64_t row = rb + r;
-                    wv[r][j] = __builtin_nontemporal_load(wp + row * C + chunk[j]);
-                    const int64_t gi = row * G + chunk[j] / F::CPG;
-                    sv[r][j] = __builtin_nontemporal_load(sp + gi);
-                    bv[r][j] = __builtin_nontemporal_load(bp + gi);
-                }
-            }
-        }
-        float acc[R][MW];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < MW; ++m) acc[r][m] = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-#pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                const float sf = bf16_lo(sv[r][j]);
-                const float bf = bf16_lo(bv[r][j]);
-#pragma unroll
-                for (int m = 0; m < MW; ++m) {
-                    const float d = chunk_dot<BITS>(wv[r][j], xv[m][j], xs[m][j]);
-                    acc[r][m] = fmaf(sf, d, acc[r][m]);
-                    acc[r][m] = fmaf(bf, xs[m][j], acc[r][m]);
-                }
-            }
-        }
-        if (S == 1) {
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < MW; ++m) {
-                    const float t = wave_sum(acc[r][m]);
-                    if (lane == 0 && rb + r < row1) yrow[m][rb + r] = f32_to_bf16(t);
-                }
-        } else {
-            float *buf = red + (it & 1) * kRedSlots;
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < MW; ++m) {
-                    const float t = wave_sum(acc[r][m]);
-                    if (lane == 0) buf[(grp * S + wig) * (R * MW) + r * MW + m] = t;
-                }
-            __syncthreads();
-            if (wig == 0 && lane < R * MW) {
-                const int r = lane / MW, m = lane % MW;
-                float t = 0.f;
-                for (int s = 0; s < S; ++s) t += buf[(grp * S + s) * (R * MW) + lane];
-                if (rb + r < row1) {
-#pragma unroll
-                    for (int mm = 0; mm < MW; ++mm)
-                        if (mm == m) yrow[mm][rb + r] = f32_to_bf16(t);
-                }
-            }
-        }
+    float acc[R][MW];
+#if AGQ_PIPELINE
+    // `iters` is even. Each buffer is refilled right after it is consumed. The
+    // refill branches are wave-uniform; skipping the refills past the end
+    // matters: clamped, they would send every wave of the grid to the same
+    // last row at once.
+    for (int it = 0; it < iters; it += 2) {
+        compute_rows<BITS, CPT, MW, R>(A, xv, xs, nxs, acc);
+        finish_rows<MW, R>(acc, yrow, walk.at(it), walk.end, S, wig, grp, lane, red);
+        if (it + 2 < iters) load_rows<BITS, CPT, R>(A, wp, sp, bp, walk.at(it + 2), row_last, woff, goff, C, G);
+        compute_rows<BITS, CPT, MW, R>(B, xv, xs, nxs, acc);
+        finish_rows<MW, R>(acc, yrow, walk.at(it + 1), walk.end, S, wig, grp, lane, red + kRedSlots);
+        if (it + 3 < iters) load_rows<BITS, CPT, R>(B, wp, sp, bp, walk.at(it + 3), row_last, woff, goff, C, G);
     }
+#else
+    for (int it = 0; it < iters; ++it) {
+        const int64_t rb = walk.at(it);
+        if (it > 0) load_rows<BITS, CPT, R>(A, wp, sp, bp, rb, row_last, woff, goff, C, G);
+        compute_rows<BITS, CPT, MW, R>(A, xv, xs, nxs, acc);
+        finish_rows<MW, R>(acc, yrow, rb, walk.end, S, wig, grp, lane, red + (it & 1) * kRedSlots);
+    }
+#endif
     if (S > 1) __syncthreads();  // the LDS buffers are reused by the caller's next pass
 }
 
 template <int BITS, int CPT, int MW, int R>
 __global__ __launch_bounds__(512) void qmv_kernel(ProductArgs a) {
     __shared__ float red[2 * kRedSlots];
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int64_t rg = (int64_t)blockIdx.x * a.GPB + wave / a.S;
-    const int64_t row0 = rg * a.RPG;
-    int64_t row1 = row0 + a.RPG;
-    if (row1 > a.N) row1 = a.N;
-    if (a.S == 1 && row0 >= row1) return;  // no barriers on the S == 1 path
-    const int iters = (int)((a.RPG + R - 1) / R);
+    const RowWalk walk = row_walk<R>(a, rg, (int64_t)gridDim.x * a.GPB);
+    // A wave without rows may leave only when it meets no block barrier: with
+    // S == 1 and x read from global memory. (Otherwise it runs clamped re-reads
+    // of the last row and stores nothing.)
+    if (a.S == 1 && !a.x_lds && walk.first >= walk.end) return;
+    const int iters = (int)(a.RPG / R);             // RPG is a multiple of R (of 2R when pipelined)
     const uint16_t *xrow[MW];
     uint16_t *yrow[MW];
 #pragma unroll
@@ -247,13 +399,17 @@ __global__ __launch_bounds__(512) void qmv_kernel(ProductArgs a) {
         xrow[m] = a.x + (int64_t)m * a.K;
         yrow[m] = a.y + (int64_t)m * a.N;
     }
-    product_rows<BITS, CPT, MW, R>(a, a.w, a.s, a.b, xrow, yrow, row0, row1, iters, red);
+    product_rows<BITS, CPT, MW, R>(a, a.w, a.s, a.b, xrow, yrow, walk, iters, red, a.x_lds != 0);
 }
+
+// Rows per iteration of a gather pass with ME pairs: fewer rows in flight for the
+// widest passes (register pressure). Any R partitions the same rows exactly once.
+constexpr int gather_rows(int me, int r) { return me > 4 ? 1 : r; }
 
 template <int BITS, int ME, int R>
 __device__ __forceinline__ void gather_pass(const ProductArgs &a, const u32x4 *wp, const uint16_t *sp,
-                                            const uint16_t *bp, const uint16_t *plist, int base, int64_t row0,
-                                            int64_t row1, int iters, float *red) {
+                                            const uint16_t *bp, const uint16_t *plist, int base,
+                                            const RowWalk &walk, int iters, float *red) {
     const uint16_t *xrow[ME];
     uint16_t *yrow[ME];
 #pragma unroll
@@ -263,7 +419,16 @@ __device__ __forceinline__ void gather_pass(const ProductArgs &a, const u32x4 *w
         xrow[m] = a.x + xr * a.K;
         yrow[m] = a.y + (int64_t)p * a.N;
     }
-    product_rows<BITS, 1, ME, R>(a, wp, sp, bp, xrow, yrow, row0, row1, iters, red);
+    product_rows<BITS, 1, ME, R>(a, wp, sp, bp, xrow, yrow, walk, iters, red);
+}
+
+template <int BITS, int ME, int R>
+__device__ __forceinline__ void gather_pass_rows(const ProductArgs &a, const u32x4 *wp, const uint16_t *sp,
+                                                 const uint16_t *bp, const uint16_t *plist, int base, int64_t rg,
+                                                 int64_t groups, float *red) {
+    constexpr int RR = gather_rows(ME, R);
+    const RowWalk walk = row_walk<RR>(a, rg, groups);
+    gather_pass<BITS, ME, RR>(a, wp, sp, bp, plist, base, walk, (int)(a.RPG / RR), red);
 }
 
 // Compact (ascending) the pairs p < P that satisfy `pred` into list[]; wave 0 only.
@@ -290,12 +455,11 @@ __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
     __shared__ uint16_t plist[kMaxPairs];
     __shared__ int pcount;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const uint32_t e = blockIdx.y;
     const int64_t rg = (int64_t)blockIdx.x * a.GPB + wave / a.S;
-    const int64_t row0 = rg * a.RPG;
-    int64_t row1 = row0 + a.RPG;
-    if (row1 > a.N) row1 = a.N;
+    const int64_t groups = (int64_t)gridDim.x * a.GPB;
+    const RowWalk walk = row_walk<R>(a, rg, groups);
     const uint32_t *lhs = a.lhs, *rhs = a.rhs;
     const uint32_t nx = (uint32_t)a.R_x, ne = (uint32_t)a.E;
 
@@ -312,9 +476,14 @@ __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
         __syncthreads();
         const int nbad = pcount;
         const int wig = wave % a.S;
+        const int iters = (int)(a.RPG / R);
         for (int i = 0; i < nbad; ++i) {
             uint16_t *yr = a.y + (int64_t)plist[i] * a.N;
-            for (int64_t n = row0 + wig * 64 + lane; n < row1; n += 64 * a.S) yr[n] = 0x7FC0u;
+            for (int it = 0; it < iters; ++it)
+                for (int r = wig * 64 + lane; r < R; r += 64 * a.S) {
+                    const int64_t n = walk.at(it) + r;
+                    if (n < walk.end) yr[n] = 0x7FC0u;
+                }
         }
         __syncthreads();
     }
@@ -329,22 +498,21 @@ __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
     __syncthreads();
     const int count = pcount;
     if (count == 0) return;
-    if (a.S == 1 && row0 >= row1) return;
-    const int iters = (int)((a.RPG + R - 1) / R);
+    if (a.S == 1 && walk.first >= walk.end) return;
     const u32x4 *wp = a.w + (int64_t)e * a.N * a.C;
     const uint16_t *sp = a.s + (int64_t)e * a.N * a.G;
     const uint16_t *bp = a.b + (int64_t)e * a.N * a.G;
     for (int base = 0; base < count; base += 8) {
         const int me = count - base < 8 ? count - base : 8;
         switch (me) {
-            case 1: gather_pass<BITS, 1, R>(a, wp, sp, bp, plist, base, row0, row1, iters, red); break;
-            case 2: gather_pass<BITS, 2, R>(a, wp, sp, bp, plist, base, row0, row1, iters, red); break;
-            case 3: gather_pass<BITS, 3, R>(a, wp, sp, bp, plist, base, row0, row1, iters, red); break;
-            case 4: gather_pass<BITS, 4, R>(a, wp, sp, bp, plist, base, row0, row1, iters, red); break;
-            case 5: gather_pass<BITS, 5, R>(a, wp, sp, bp, plist, base, row0, row1, iters, red); break;
-            case 6: gather_pass<BITS, 6, R>(a, wp, sp, bp, plist, base, row0, row1, iters, red); break;
-            case 7: gather_pass<BITS, 7, R>(a, wp, sp, bp, plist, base, row0, row1, iters, red); break;
-            default: gather_pass<BITS, 8, R>(a, wp, sp, bp, plist, base, row0, row1, iters, red); break;
+            case 1: gather_pass_rows<BITS, 1, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
+            case 2: gather_pass_rows<BITS, 2, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
+            case 3: gather_pass_rows<BITS, 3, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
+            case 4: gather_pass_rows<BITS, 4, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
+            case 5: gather_pass_rows<BITS, 5, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
+            case 6: gather_pass_rows<BITS, 6, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
+            case 7: gather_pass_rows<BITS, 7, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
+            default: gather_pass_rows<BITS, 8, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
         }
     }
 }
@@ -393,7 +561,9 @@ static const void *qmv_by_cpt(int cpt) {
             case 5: return qmv_sym<BITS, MW, 5>();
             case 6: return qmv_sym<BITS, MW, 6>();
             case 7: return qmv_sym<BITS, MW, 7>();
-            case 8: return qmv_sym<BITS, MW, 8>();
+            case 8:
+                if constexpr (kMaxCpt >= 8) return qmv_sym<BITS, MW, 8>();
+                break;
         }
     } else if constexpr (kXRegBudget / MW >= 4) {
         switch (cpt) {

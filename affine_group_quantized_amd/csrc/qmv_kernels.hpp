@@ -26,6 +26,8 @@ struct ProductArgs {
     int32_t E;            // gather: expert planes
     int32_t S;            // waves per row group (K split)
     int32_t GPB;          // row groups per block
+    int32_t x_lds;        // 1: the block copies x [M, K] into dynamic LDS once, waves stage from there
+    int32_t pad_;
 };
 
 // Kernel symbol for (bits, activation rows per pass, chunks per lane), or NULL.

@@ -80,7 +80,7 @@ const char *agq_last_error(void);
  *   y      [N] BF16 (written)
  * bits must be 4 or 8 and group_size 64 (else AGQ_ENOTSUP); K must be a
  * positive multiple of group_size, and N positive (else AGQ_EINVAL). K above
- * 131072 (4-bit) or 65536 (8-bit) is AGQ_ENOTSUP.
+ * 114688 (4-bit) or 57344 (8-bit) is AGQ_ENOTSUP.
  */
 agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                    void *y, int64_t N, int64_t K, int bits, int group_size, void *stream);
@@ -90,8 +90,8 @@ agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const v
  * 1 <= M <= 8 activation rows, streaming each weight byte once for all M rows.
  *   x [M, K] BF16, y [M, N] BF16; w, scales and biases as in agq_qmv.
  * M > 8 is AGQ_ENOTSUP; that is a quantized GEMM, not a matvec. The K limit
- * shrinks with M: K <= 16384 * floor(8/M) for 4-bit and 8192 * floor(8/M)
- * for 8-bit (larger K is AGQ_ENOTSUP).
+ * shrinks with M: K <= 16384 * c for 4-bit and 8192 * c for 8-bit, with
+ * c = min(7, floor(8/M)) (larger K is AGQ_ENOTSUP).
  */
 agq_status agq_qmv_wide(const void *x, const uint32_t *w, const void *scales, const void *biases,
                         void *y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
@@ -133,8 +133,11 @@ agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *bia
 /*
  * Launch plan (host-only introspection; no HIP call). It describes how the
  * product kernels would tile a problem of this shape on a device with
- * `num_cus` compute units. `experts` is 0 for agq_qmv / agq_qmv_wide and E
- * for agq_gather_qmv (whose plan ignores M and sizes for 8 rows per pass).
+ * `num_cus` compute units holding `waves_per_cu` waves of the chosen kernel
+ * at once. The product entry points use the same tiling, with the residency
+ * that the HIP occupancy query reports for the kernel. `experts` is 0 for
+ * agq_qmv / agq_qmv_wide and E for agq_gather_qmv (whose plan ignores M and
+ * sizes for 8 rows per pass).
  */
 typedef struct agq_plan {
     int32_t bits;            /* 4 or 8 */
@@ -145,13 +148,25 @@ typedef struct agq_plan {
     int32_t waves_per_group; /* waves splitting K for one set of rows */
     int32_t groups_per_block;
     int32_t threads_per_block;
-    int64_t rows_per_group;
-    int64_t row_groups;
+    int64_t rows_per_group;  /* rows each group visits: iterations x rows_per_iter */
+    int64_t row_groups;      /* groups launched (blocks x groups_per_block) */
     int64_t blocks;          /* grid size (per expert for gather) */
+    int32_t row_order;       /* 0: group g takes rows (it*row_groups + g)*R + r (round-robin);
+                                1: group g takes rows [g*rows_per_group, (g+1)*rows_per_group) */
+    int32_t x_lds_bytes;     /* LDS per block holding x (0: waves read x from global memory) */
 } agq_plan;
 
 agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group_size,
-                            int num_cus, int64_t experts, agq_plan *plan);
+                            int num_cus, int waves_per_cu, int64_t experts, agq_plan *plan);
+
+/*
+ * The plan the product entry points launch on the current HIP device: the
+ * same tiling, with the residency the HIP occupancy query reports for the
+ * chosen kernel. Makes HIP calls (device properties, occupancy) but launches
+ * nothing. Errors as for the products.
+ */
+agq_status agq_plan_launch(int64_t M, int64_t N, int64_t K, int bits, int group_size, int64_t experts,
+                           agq_plan *plan);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -30,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("agq_qmv", "agq_qmv_wide", "agq_gather_qmv", "agq_dequantize", "agq_status_str",
-                 "agq_last_error", "agq_version", "agq_plan_product"):
+                 "agq_last_error", "agq_version", "agq_plan_product", "agq_plan_launch"):
         assert want in names
 
 
@@ -77,8 +78,8 @@ def gather(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: qmv(s=ctypes.c_void_p(0x10001)), EINVAL),
     (lambda: qmv(N=1 << 41), EINVAL),
     (lambda: qmv(K=1 << 31), EINVAL),
-    (lambda: qmv(K=131072 + 64), ENOTSUP),
-    (lambda: qmv(K=65536 + 64, bits=8), ENOTSUP),
+    (lambda: qmv(K=114688 + 64), ENOTSUP),
+    (lambda: qmv(K=57344 + 64, bits=8), ENOTSUP),
     (lambda: wide(M=0), EINVAL),
     (lambda: wide(M=-1), EINVAL),
     (lambda: wide(M=9), ENOTSUP),
@@ -102,33 +103,52 @@ def test_host_validation(call, status):
     assert lib.agq_last_error() != b""
 
 
+def visited_rows(p, N):
+    """Rows the kernels store, following the plan's row walk (host model of the kernel indexing)."""
+    R, TG, RPG = p["rows_per_iter"], p["row_groups"], p["rows_per_group"]
+    iters = RPG // R
+    g = np.arange(TG)[:, None, None]
+    it = np.arange(iters)[None, :, None]
+    r = np.arange(R)[None, None, :]
+    if p["row_order"] == 0:
+        rows = (it * TG + g) * R + r
+    else:
+        rows = g * RPG + it * R + r
+    rows = rows.reshape(-1)
+    return rows[rows < N]
+
+
 SHAPES = [  # (M, N, K, bits, experts)
     (1, 4096, 4096, 4, 0), (1, 6144, 4096, 4, 0), (1, 28672, 4096, 4, 0), (1, 4096, 14336, 4, 0),
     (1, 128256, 4096, 4, 0), (2, 14336, 4096, 4, 0), (4, 14336, 4096, 4, 0), (8, 14336, 4096, 4, 0),
     (2, 4096, 14336, 4, 0), (4, 4096, 14336, 4, 0), (8, 4096, 14336, 4, 0),
     (1, 4864, 896, 8, 0), (1, 896, 4864, 8, 0), (1, 1152, 896, 8, 0), (1, 151936, 896, 8, 0),
     (8, 14336, 4096, 4, 8), (8, 4096, 14336, 4, 8),
-    (1, 1, 64, 4, 0), (3, 7, 192, 8, 0), (5, 33, 1088, 4, 0), (7, 100, 8192, 8, 0), (1, 5, 131072, 4, 0),
+    (1, 1, 64, 4, 0), (3, 7, 192, 8, 0), (5, 33, 1088, 4, 0), (7, 100, 8192, 8, 0), (1, 5, 114688, 4, 0),
     (8, 3, 16384, 4, 0), (2, 9, 4096, 4, 3), (1, 2, 64, 8, 1),
 ]
 
 
 @pytest.mark.parametrize("M,N,K,bits,experts", SHAPES)
-@pytest.mark.parametrize("cus", [256, 304, 8])
-def test_plan_covers_the_problem(M, N, K, bits, experts, cus):
-    p = agq.plan(M, N, K, bits, 64, cus, experts)
+@pytest.mark.parametrize("cus,wpc", [(256, 8), (256, 12), (304, 16), (8, 2), (256, 1)])
+def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
+    p = agq.plan(M, N, K, bits, 64, cus, experts, waves_per_cu=wpc)
     C = K * bits // 128
     assert p["chunks_per_row"] == C
-    assert 1 <= p["cpt"] <= 8 and p["cpt"] * p["mw"] <= 8
+    assert 1 <= p["cpt"] <= 7 and p["cpt"] * p["mw"] <= 8
     assert 1 <= p["waves_per_group"] <= 8
     assert p["waves_per_group"] * p["cpt"] * 64 >= C                     # every chunk has a lane
     assert (p["waves_per_group"] - 1) * p["cpt"] * 64 < C                 # no wave is idle
     assert p["threads_per_block"] == 64 * p["waves_per_group"] * p["groups_per_block"] <= 512
-    assert p["rows_per_group"] % p["rows_per_iter"] == 0
-    assert p["row_groups"] * p["rows_per_group"] >= N                    # every row is covered
-    assert (p["row_groups"] - 1) * p["rows_per_group"] < N               # no group is empty
-    assert p["blocks"] * p["groups_per_block"] >= p["row_groups"]
-    assert p["rows_per_iter"] * p["mw"] <= 32
+    R, TG, RPG = p["rows_per_iter"], p["row_groups"], p["rows_per_group"]
+    assert RPG % (2 * R) == 0                                            # even iterations (double-buffered)
+    assert TG == p["blocks"] * p["groups_per_block"]
+    assert TG * RPG >= N                                                 # every row is covered
+    assert (TG - p["groups_per_block"]) * RPG < N                        # at most one block's groups spare
+    if N <= 300000:
+        rows = visited_rows(p, N)
+        assert rows.size == N and np.array_equal(np.sort(rows), np.arange(N))   # each row exactly once
+    assert p["rows_per_iter"] * p["mw"] <= 16
     if experts:
         assert p["mw"] == 8 and p["cpt"] == 1
     else:
