@@ -138,7 +138,8 @@ agq_status check_operands(const void *x, const void *w, const void *s, const voi
 }
 
 // Kernel and tiling for a product on the current device: the grid holds one
-// row group per resident wave set of the chosen kernel.
+// row group per resident wave set of the chosen kernel. Walks of at least
+// kDeepRows rows per group use the deep-load instantiation.
 agq_status launch_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t experts, agq::Plan *plan,
                        const void **sym) {
     const int64_t rows = experts > 0 ? 8 : M;
@@ -148,12 +149,21 @@ agq_status launch_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t expert
     int cus = 0, dev = 0;
     agq_status st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
-    *sym = agq::product_kernel(bits, plan->mw, plan->cpt, experts > 0);
-    if (!*sym) return fail(AGQ_ENOTSUP, "no kernel for bits=%d rows=%d cpt=%d", bits, plan->mw, plan->cpt);
-    int64_t waves = 0;
-    st = resident_waves(*sym, plan->threads, (size_t)plan->x_lds_bytes, cus, dev, &waves);
-    if (st != AGQ_OK) return st;
-    agq::plan_grid(N, waves, experts, plan);
+    for (int pass = 0; pass < 2; ++pass) {
+        *sym = agq::product_kernel(bits, plan->mw, plan->cpt, plan->R, plan->x_lds_bytes > 0, experts > 0);
+        if (!*sym)
+            return fail(AGQ_ENOTSUP, "no kernel for bits=%d rows=%d cpt=%d R=%d", bits, plan->mw, plan->cpt,
+                        plan->R);
+        int64_t waves = 0;
+        st = resident_waves(*sym, plan->threads, (size_t)plan->x_lds_bytes, cus, dev, &waves);
+        if (st != AGQ_OK) return st;
+        if (pass == 0 && agq::wants_deep(N, waves, plan->S, experts)) {
+            agq::plan_shape(rows, K, bits, experts, plan, true);
+            continue;
+        }
+        agq::plan_grid(N, waves, experts, plan);
+        return AGQ_OK;
+    }
     return AGQ_OK;
 }
 
@@ -189,7 +199,6 @@ agq::ProductArgs make_args(const void *x, const uint32_t *w, const void *s, cons
     a.M = M;
     a.S = p.S;
     a.GPB = p.GPB;
-    a.x_lds = p.x_lds_bytes > 0 ? 1 : 0;
     return a;
 }
 

@@ -18,11 +18,22 @@ constexpr int kMaxPairs = 4096;        // gather: pair list kept in LDS as uint1
 #ifndef AGQ_WAVES_PER_CU
 #define AGQ_WAVES_PER_CU 0  // 0: size grids from the kernel's measured occupancy
 #endif
-#ifndef AGQ_LOADS_PER_LANE
-#define AGQ_LOADS_PER_LANE 8
+#ifndef AGQ_LOADS_SHALLOW
+#define AGQ_LOADS_SHALLOW 4
+#endif
+#ifndef AGQ_LOADS_DEEP
+#define AGQ_LOADS_DEEP 8
+#endif
+#ifndef AGQ_DEEP_ROWS
+#define AGQ_DEEP_ROWS 16
 #endif
 constexpr int kWavesPerCuOverride = AGQ_WAVES_PER_CU;  // >0 forces this many waves per CU
-constexpr int kLoadsPerLane = AGQ_LOADS_PER_LANE;    // 16-byte weight loads in flight per lane
+// 16-byte weight loads in flight per lane (both row buffers). Short walks use
+// the shallow depth (more, lighter waves finish sooner); walks of at least
+// kDeepRows rows per row group use the deep one.
+constexpr int kLoadsShallow = AGQ_LOADS_SHALLOW;
+constexpr int kLoadsDeep = AGQ_LOADS_DEEP;
+constexpr int kDeepRows = AGQ_DEEP_ROWS;
 #ifndef AGQ_PIPELINE
 #define AGQ_PIPELINE 1  // double-buffer the row loads (1) or rely on wave interleaving alone (0)
 #endif
@@ -33,19 +44,21 @@ constexpr bool kPipelined = AGQ_PIPELINE != 0;
 
 constexpr int floor_pow2(int v) { return v >= 16 ? 16 : v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
 
-// Weight rows per wave iteration: aim for kLoadsPerLane outstanding 16-byte
-// loads per lane counting both buffers of the double-buffered loop; keep R*MW
+// Weight rows per wave iteration: aim for `loads` outstanding 16-byte loads
+// per lane counting both buffers of the double-buffered loop; keep R*MW
 // accumulators at or below 16 (register pressure of the wide and gather forms).
-constexpr int rows_per_iter(int cpt, int mw) {
-    return floor_pow2(kLoadsPerLane / (kPipelined ? 2 : 1) / cpt) < floor_pow2(16 / mw)
-               ? floor_pow2(kLoadsPerLane / (kPipelined ? 2 : 1) / cpt)
+constexpr int rows_per_iter(int cpt, int mw, int loads) {
+    return floor_pow2(loads / (kPipelined ? 2 : 1) / cpt) < floor_pow2(16 / mw)
+               ? floor_pow2(loads / (kPipelined ? 2 : 1) / cpt)
                : floor_pow2(16 / mw);
 }
 
 #ifndef AGQ_X_LDS_MAX
-#define AGQ_X_LDS_MAX 65536
+#define AGQ_X_LDS_MAX 32768
 #endif
-constexpr int kXLdsMax = AGQ_X_LDS_MAX;  // largest activation block staged in LDS (bytes)
+// Largest activation block staged in LDS (bytes): at most 8 16-byte words per
+// thread of a 256-thread block.
+constexpr int kXLdsMax = AGQ_X_LDS_MAX;
 
 struct Plan {
     int bits = 0, C = 0, cpt = 0, mw = 0, R = 0, S = 0, GPB = 0, threads = 0;
@@ -58,7 +71,7 @@ struct Plan {
 // scheme at this M. Arguments are assumed valid otherwise (bits in {4,8},
 // K % 64 == 0, N >= 1, 1 <= M <= 8). `experts` is 0 for the dense products and
 // the number of expert planes for the gather.
-inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Plan *p) {
+inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Plan *p, bool deep = false) {
     const bool gather = experts > 0;
     Plan q;
     q.bits = bits;
@@ -75,13 +88,16 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
         if (q.S > kMaxWavesPerGroup) return AGQ_ENOTSUP;
         q.cpt = (q.C + 64 * q.S - 1) / (64 * q.S);
     }
-    q.R = rows_per_iter(q.cpt, q.mw);
+    q.R = rows_per_iter(q.cpt, q.mw, deep ? kLoadsDeep : kLoadsShallow);
     q.GPB = q.S == 1 ? 4 : (q.S == 2 ? 2 : 1);
     q.threads = 64 * q.S * q.GPB;
     // The waves of a block share their K columns only when each row group is a
     // single wave; then one LDS copy of x serves the whole block.
     const int64_t xbytes = 2 * (int64_t)q.mw * K;
-    q.x_lds_bytes = (!gather && q.S == 1 && q.GPB > 1 && xbytes <= kXLdsMax) ? (int)xbytes : 0;
+    // (The kernel copies x with 256 threads holding at most MW*CPT 16-byte words each.)
+    // Long walks (the deep plan) amortize each wave's own staging of x over
+    // many rows, and skip the block barrier the LDS copy needs.
+    q.x_lds_bytes = (!gather && !deep && q.S == 1 && q.GPB == 4 && q.mw <= 4 && xbytes <= kXLdsMax) ? (int)xbytes : 0;
     *p = q;
     return AGQ_OK;
 }
@@ -105,11 +121,19 @@ inline void plan_grid(int64_t N, int64_t resident_waves, int64_t experts, Plan *
     q->TG = q->blocks * q->GPB;  // every launched group walks rows (groups past N store nothing)
 }
 
+// Whether a walk is long enough for the deep load depth.
+inline bool wants_deep(int64_t N, int64_t resident_waves, int S, int64_t experts) {
+    int64_t groups = resident_waves / S / (experts > 0 ? experts : 1);
+    if (groups < 1) groups = 1;
+    return N >= (int64_t)kDeepRows * groups;
+}
+
 inline agq_status make_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t resident_waves, int64_t experts,
                             Plan *p) {
     Plan q;
     agq_status st = plan_shape(M, K, bits, experts, &q);
     if (st != AGQ_OK) return st;
+    if (wants_deep(N, resident_waves, q.S, experts)) plan_shape(M, K, bits, experts, &q, true);
     plan_grid(N, resident_waves, experts, &q);
     *p = q;
     return AGQ_OK;

@@ -45,9 +45,6 @@ namespace agq {
 
 constexpr int kRedSlots = kMaxWavesPerGroup * 64;
 
-#ifndef AGQ_X_FIRST
-#define AGQ_X_FIRST 0  // 1: copy x into LDS before issuing the first weight loads
-#endif
 
 // Dynamic LDS of the dense product kernels: the block's copy of x [M, K] (bf16).
 extern __shared__ u32x4 g_xlds[];  // per buffer: GPB*S*R*MW <= 8 waves * 64 values
@@ -121,13 +118,35 @@ __device__ __forceinline__ void stage_x_lds(int64_t row_word, int c, bool valid,
 }
 
 // Block-cooperative copy of the activation rows x[0..M) (contiguous, 16-byte
-// aligned) into LDS, then a barrier that every wave of the block must reach.
-// The waves then stage their lane slices from LDS instead of each pulling x
-// through L2.
-__device__ __forceinline__ void copy_x_to_lds(const uint16_t *__restrict__ x, int64_t elems) {
+// aligned) into LDS, in two halves. fetch_x issues the global loads into
+// registers; store_x writes them to LDS and ends with a barrier that every
+// wave of the block must reach. Weight loads issued between the two stay in
+// flight: loads retire in order, so waiting for the x registers does not wait
+// for anything issued later. XW bounds the 16-byte words per thread; with one
+// wave per row group and 256 threads it is MW*CPT (4-bit) or MW*CPT/2 (8-bit).
+template <int XW>
+__device__ __forceinline__ void fetch_x(const uint16_t *__restrict__ x, int n16, u32x4 (&xr)[XW]) {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(x);
-    const int n16 = (int)(elems / 8);
-    for (int i = threadIdx.x; i < n16; i += blockDim.x) g_xlds[i] = src[i];
+    const int per = (n16 + (int)blockDim.x - 1) / (int)blockDim.x;  // block-uniform, <= XW
+#pragma unroll
+    for (int k = 0; k < XW; ++k) {
+        if (k < per) {  // uniform branch
+            const int i = (int)threadIdx.x + k * (int)blockDim.x;
+            xr[k] = src[i < n16 ? i : n16 - 1];
+        }
+    }
+}
+
+template <int XW>
+__device__ __forceinline__ void store_x(int n16, const u32x4 (&xr)[XW]) {
+    const int per = (n16 + (int)blockDim.x - 1) / (int)blockDim.x;
+#pragma unroll
+    for (int k = 0; k < XW; ++k) {
+        if (k < per) {
+            const int i = (int)threadIdx.x + k * (int)blockDim.x;
+            if (i < n16) g_xlds[i] = xr[k];
+        }
+    }
     __syncthreads();
 }
 
@@ -166,8 +185,8 @@ __device__ __forceinline__ float chunk_dot(const u32x4 &wv, const uint32_t (&xv)
 template <int CPT, int R>
 struct RowBuf {
     u32x4 w[R][CPT];
-    uint32_t s[R][CPT];
-    uint32_t b[R][CPT];
+    uint16_t s[R][CPT];  // 16-bit on purpose: a 32-bit copy would be zero-extended at the
+    uint16_t b[R][CPT];  // loop entry, forcing a wait for these loads before the next ones
 };
 
 // Issue every load of rows [rb, rb + R) at once. Row and chunk indices are
@@ -215,8 +234,8 @@ __device__ __forceinline__ void compute_rows(const RowBuf<CPT, R> &buf, const ui
     for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const float sf = bf16_lo(buf.s[r][j]);
-            const float bf = bf16_lo(buf.b[r][j]);
+            const float sf = bf16_lo((uint32_t)buf.s[r][j]);
+            const float bf = bf16_lo((uint32_t)buf.b[r][j]);
 #pragma unroll
             for (int m = 0; m < MW; ++m) {
                 const float d = chunk_dot<BITS>(buf.w[r][j], xv[m][j], nxs[m][j]);
@@ -290,12 +309,11 @@ __device__ __forceinline__ RowWalk row_walk(const ProductArgs &a, int64_t rg, in
 //
 // The row loop is software-pipelined over two register buffers: the loads of
 // the next R rows are in flight while the current R rows are computed.
-template <int BITS, int CPT, int MW, int R>
+template <int BITS, int CPT, int MW, int R, bool XL = false>
 __device__ __forceinline__ void product_rows(const ProductArgs &a, const u32x4 *__restrict__ wp,
                                              const uint16_t *__restrict__ sp, const uint16_t *__restrict__ bp,
                                              const uint16_t *const *xrow, uint16_t *const *yrow,
-                                             const RowWalk &walk, int iters, float *red,
-                                             bool x_in_lds = false) {
+                                             const RowWalk &walk, int iters, float *red) {
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int S = a.S;
@@ -322,24 +340,23 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const u32x4 *
 #if AGQ_PIPELINE
     RowBuf<CPT, R> B;
 #endif
-#if AGQ_X_FIRST
-    if (x_in_lds) copy_x_to_lds(xrow[0], (int64_t)MW * a.K);  // block barrier: every wave of the block gets here
-#endif
-    // The first weight loads go out before the activation staging, so the
-    // staging overlaps their latency.
+    // Order: x loads, then the first weight loads, then wait for x alone, fill
+    // LDS and stage, while the weight loads are in flight.
+    // XL (compile time): the block stages x through LDS. One code path per
+    // kernel keeps the compiler's load-wait placement exact.
+    const int n16 = XL ? (int)((int64_t)MW * a.K / 8) : 0;
+    constexpr int XW = BITS == 4 ? MW * CPT : (MW * CPT + 1) / 2;
+    u32x4 xr[XW];
+    if constexpr (XL) fetch_x(xrow[0], n16, xr);
     load_rows<BITS, CPT, R>(A, wp, sp, bp, walk.at(0), row_last, woff, goff, C, G);
-#if AGQ_PIPELINE
-    load_rows<BITS, CPT, R>(B, wp, sp, bp, walk.at(1), row_last, woff, goff, C, G);
-#endif
+    __builtin_amdgcn_sched_barrier(0);
 
     uint32_t xv[MW][CPT][16];
     float xs[MW][CPT], nxs[MW][CPT];
     // Activation slices: from the block's LDS copy of x when there is one,
     // otherwise straight from global memory (xrow).
-    if (x_in_lds) {
-#if !AGQ_X_FIRST
-        copy_x_to_lds(xrow[0], (int64_t)MW * a.K);  // block barrier: every wave of the block gets here
-#endif
+    if constexpr (XL) {
+        store_x(n16, xr);  // block barrier: every wave of the block gets here
 #pragma unroll
         for (int m = 0; m < MW; ++m)
 #pragma unroll
@@ -358,18 +375,32 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const u32x4 *
 
     float acc[R][MW];
 #if AGQ_PIPELINE
-    // `iters` is even. Each buffer is refilled right after it is consumed. The
-    // refill branches are wave-uniform; skipping the refills past the end
-    // matters: clamped, they would send every wave of the grid to the same
-    // last row at once.
-    for (int it = 0; it < iters; it += 2) {
+    // `iters` is even. The next buffer's loads are issued before the current
+    // buffer is consumed; the uniform branch skips the refill past the end
+    // (clamped, it would send every wave of the grid to the same last row).
+    // `iters` is even. The loop runs every pair but the last with unconditional
+    // loads, and the last pair is peeled: a conditional refill would make the
+    // compiler's load-wait counts conservative (it would wait for the refill
+    // too), and a clamped unconditional one would send every wave of the grid
+    // to the same last row at once. Scheduling barriers keep one buffer's use
+    // from being hoisted above the other buffer's loads.
+    int it = 0;
+    for (; it + 2 < iters; it += 2) {
+        load_rows<BITS, CPT, R>(B, wp, sp, bp, walk.at(it + 1), row_last, woff, goff, C, G);
+        __builtin_amdgcn_sched_barrier(0);
         compute_rows<BITS, CPT, MW, R>(A, xv, xs, nxs, acc);
         finish_rows<MW, R>(acc, yrow, walk.at(it), walk.end, S, wig, grp, lane, red);
-        if (it + 2 < iters) load_rows<BITS, CPT, R>(A, wp, sp, bp, walk.at(it + 2), row_last, woff, goff, C, G);
+        load_rows<BITS, CPT, R>(A, wp, sp, bp, walk.at(it + 2), row_last, woff, goff, C, G);
+        __builtin_amdgcn_sched_barrier(0);
         compute_rows<BITS, CPT, MW, R>(B, xv, xs, nxs, acc);
         finish_rows<MW, R>(acc, yrow, walk.at(it + 1), walk.end, S, wig, grp, lane, red + kRedSlots);
-        if (it + 3 < iters) load_rows<BITS, CPT, R>(B, wp, sp, bp, walk.at(it + 3), row_last, woff, goff, C, G);
     }
+    load_rows<BITS, CPT, R>(B, wp, sp, bp, walk.at(it + 1), row_last, woff, goff, C, G);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_rows<BITS, CPT, MW, R>(A, xv, xs, nxs, acc);
+    finish_rows<MW, R>(acc, yrow, walk.at(it), walk.end, S, wig, grp, lane, red);
+    compute_rows<BITS, CPT, MW, R>(B, xv, xs, nxs, acc);
+    finish_rows<MW, R>(acc, yrow, walk.at(it + 1), walk.end, S, wig, grp, lane, red + kRedSlots);
 #else
     for (int it = 0; it < iters; ++it) {
         const int64_t rb = walk.at(it);
@@ -381,7 +412,7 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const u32x4 *
     if (S > 1) __syncthreads();  // the LDS buffers are reused by the caller's next pass
 }
 
-template <int BITS, int CPT, int MW, int R>
+template <int BITS, int CPT, int MW, int R, bool XL>
 __global__ __launch_bounds__(512) void qmv_kernel(ProductArgs a) {
     __shared__ float red[2 * kRedSlots];
     const int wave = wave_id();
@@ -390,7 +421,7 @@ __global__ __launch_bounds__(512) void qmv_kernel(ProductArgs a) {
     // A wave without rows may leave only when it meets no block barrier: with
     // S == 1 and x read from global memory. (Otherwise it runs clamped re-reads
     // of the last row and stores nothing.)
-    if (a.S == 1 && !a.x_lds && walk.first >= walk.end) return;
+    if (a.S == 1 && !XL && walk.first >= walk.end) return;
     const int iters = (int)(a.RPG / R);             // RPG is a multiple of R (of 2R when pipelined)
     const uint16_t *xrow[MW];
     uint16_t *yrow[MW];
@@ -399,7 +430,7 @@ __global__ __launch_bounds__(512) void qmv_kernel(ProductArgs a) {
         xrow[m] = a.x + (int64_t)m * a.K;
         yrow[m] = a.y + (int64_t)m * a.N;
     }
-    product_rows<BITS, CPT, MW, R>(a, a.w, a.s, a.b, xrow, yrow, walk, iters, red, a.x_lds != 0);
+    product_rows<BITS, CPT, MW, R, XL>(a, a.w, a.s, a.b, xrow, yrow, walk, iters, red);
 }
 
 // Rows per iteration of a gather pass with ME pairs: fewer rows in flight for the
@@ -545,66 +576,87 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
 // ---------------------------------------------------------------------------
 // Kernel selection.
 
+template <int BITS, int MW, int CPT, int R>
+static const void *qmv_sym_xl(bool xl) {
+    // The LDS-staged form exists for MW <= 4 only (x fits the LDS budget then).
+    if constexpr (MW <= 4) {
+        if (xl) return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, true>);
+    } else {
+        if (xl) return nullptr;
+    }
+    return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, false>);
+}
+
 template <int BITS, int MW, int CPT>
-static const void *qmv_sym() {
-    return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, rows_per_iter(CPT, MW)>);
+static const void *qmv_sym(int R, bool xl) {
+    constexpr int RS = rows_per_iter(CPT, MW, kLoadsShallow), RD = rows_per_iter(CPT, MW, kLoadsDeep);
+    if (R == RS) return qmv_sym_xl<BITS, MW, CPT, RS>(xl);
+    if (R == RD) return qmv_sym_xl<BITS, MW, CPT, RD>(xl);
+    return nullptr;
 }
 
 template <int BITS, int MW>
-static const void *qmv_by_cpt(int cpt) {
+static const void *qmv_by_cpt(int cpt, int R, bool xl) {
     if constexpr (kXRegBudget / MW >= 8) {
         switch (cpt) {
-            case 1: return qmv_sym<BITS, MW, 1>();
-            case 2: return qmv_sym<BITS, MW, 2>();
-            case 3: return qmv_sym<BITS, MW, 3>();
-            case 4: return qmv_sym<BITS, MW, 4>();
-            case 5: return qmv_sym<BITS, MW, 5>();
-            case 6: return qmv_sym<BITS, MW, 6>();
-            case 7: return qmv_sym<BITS, MW, 7>();
+            case 1: return qmv_sym<BITS, MW, 1>(R, xl);
+            case 2: return qmv_sym<BITS, MW, 2>(R, xl);
+            case 3: return qmv_sym<BITS, MW, 3>(R, xl);
+            case 4: return qmv_sym<BITS, MW, 4>(R, xl);
+            case 5: return qmv_sym<BITS, MW, 5>(R, xl);
+            case 6: return qmv_sym<BITS, MW, 6>(R, xl);
+            case 7: return qmv_sym<BITS, MW, 7>(R, xl);
             case 8:
-                if constexpr (kMaxCpt >= 8) return qmv_sym<BITS, MW, 8>();
+                if constexpr (kMaxCpt >= 8) return qmv_sym<BITS, MW, 8>(R, xl);
                 break;
         }
     } else if constexpr (kXRegBudget / MW >= 4) {
         switch (cpt) {
-            case 1: return qmv_sym<BITS, MW, 1>();
-            case 2: return qmv_sym<BITS, MW, 2>();
-            case 3: return qmv_sym<BITS, MW, 3>();
-            case 4: return qmv_sym<BITS, MW, 4>();
+            case 1: return qmv_sym<BITS, MW, 1>(R, xl);
+            case 2: return qmv_sym<BITS, MW, 2>(R, xl);
+            case 3: return qmv_sym<BITS, MW, 3>(R, xl);
+            case 4: return qmv_sym<BITS, MW, 4>(R, xl);
         }
     } else if constexpr (kXRegBudget / MW >= 2) {
         switch (cpt) {
-            case 1: return qmv_sym<BITS, MW, 1>();
-            case 2: return qmv_sym<BITS, MW, 2>();
+            case 1: return qmv_sym<BITS, MW, 1>(R, xl);
+            case 2: return qmv_sym<BITS, MW, 2>(R, xl);
         }
     } else {
-        if (cpt == 1) return qmv_sym<BITS, MW, 1>();
+        if (cpt == 1) return qmv_sym<BITS, MW, 1>(R, xl);
     }
     return nullptr;
 }
 
 template <int BITS>
-static const void *qmv_by_mw(int mw, int cpt) {
+static const void *qmv_by_mw(int mw, int cpt, int R, bool xl) {
     switch (mw) {
-        case 1: return qmv_by_cpt<BITS, 1>(cpt);
-        case 2: return qmv_by_cpt<BITS, 2>(cpt);
-        case 3: return qmv_by_cpt<BITS, 3>(cpt);
-        case 4: return qmv_by_cpt<BITS, 4>(cpt);
-        case 5: return qmv_by_cpt<BITS, 5>(cpt);
-        case 6: return qmv_by_cpt<BITS, 6>(cpt);
-        case 7: return qmv_by_cpt<BITS, 7>(cpt);
-        case 8: return qmv_by_cpt<BITS, 8>(cpt);
+        case 1: return qmv_by_cpt<BITS, 1>(cpt, R, xl);
+        case 2: return qmv_by_cpt<BITS, 2>(cpt, R, xl);
+        case 3: return qmv_by_cpt<BITS, 3>(cpt, R, xl);
+        case 4: return qmv_by_cpt<BITS, 4>(cpt, R, xl);
+        case 5: return qmv_by_cpt<BITS, 5>(cpt, R, xl);
+        case 6: return qmv_by_cpt<BITS, 6>(cpt, R, xl);
+        case 7: return qmv_by_cpt<BITS, 7>(cpt, R, xl);
+        case 8: return qmv_by_cpt<BITS, 8>(cpt, R, xl);
     }
     return nullptr;
 }
 
-const void *product_kernel(int bits, int mw, int cpt, bool gather) {
+template <int BITS>
+static const void *gather_sym(int R) {
+    constexpr int RS = rows_per_iter(1, 8, kLoadsShallow), RD = rows_per_iter(1, 8, kLoadsDeep);
+    if (R == RS) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, RS>);
+    if (R == RD) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, RD>);
+    return nullptr;
+}
+
+const void *product_kernel(int bits, int mw, int cpt, int R, bool x_lds, bool gather) {
     if (gather) {
-        if (cpt != 1) return nullptr;
-        return bits == 4 ? reinterpret_cast<const void *>(&gather_qmv_kernel<4, rows_per_iter(1, 8)>)
-                         : reinterpret_cast<const void *>(&gather_qmv_kernel<8, rows_per_iter(1, 8)>);
+        if (cpt != 1 || mw != 8 || x_lds) return nullptr;
+        return bits == 4 ? gather_sym<4>(R) : gather_sym<8>(R);
     }
-    return bits == 4 ? qmv_by_mw<4>(mw, cpt) : qmv_by_mw<8>(mw, cpt);
+    return bits == 4 ? qmv_by_mw<4>(mw, cpt, R, x_lds) : qmv_by_mw<8>(mw, cpt, R, x_lds);
 }
 
 const void *dequant_kernel_sym(int bits) {

@@ -26,12 +26,12 @@ struct ProductArgs {
     int32_t E;            // gather: expert planes
     int32_t S;            // waves per row group (K split)
     int32_t GPB;          // row groups per block
-    int32_t x_lds;        // 1: the block copies x [M, K] into dynamic LDS once, waves stage from there
-    int32_t pad_;
+    int32_t pad_[2];
 };
 
-// Kernel symbol for (bits, activation rows per pass, chunks per lane), or NULL.
-const void *product_kernel(int bits, int mw, int cpt, bool gather);
+// Kernel symbol for (bits, activation rows per pass, chunks per lane, weight
+// rows per iteration, x staged through LDS), or NULL.
+const void *product_kernel(int bits, int mw, int cpt, int R, bool x_lds, bool gather);
 const void *dequant_kernel_sym(int bits);
 
 }  // namespace agq
