@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-shape", action="store_true", help="also time each matrix alone (to stderr)")
+    ap.add_argument("--write-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="summarize rocprofv3 CSV output of this benchmark into profiles/ and exit")
     return ap.parse_args()
 
 
@@ -97,8 +99,128 @@ def cpu_baseline(data, target_s):
     }
 
 
+KERNEL_SOURCES = ["affine_group_quantized_amd/csrc/qmv_kernels.hip", "affine_group_quantized_amd/csrc/qmv_device.hpp",
+                  "affine_group_quantized_amd/csrc/qmv_kernels.hpp", "affine_group_quantized_amd/csrc/plan.hpp"]
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "qmv_lm_head_128256x4096_hbm_traffic.md")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_name):
+    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+    or None when the summary is missing or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_MD) as f:
+            for line in f:
+                if line.startswith("traffic_json:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("source_hash") == kernel_source_hash() and rec.get("kernel") == kernel_name:
+                        return rec["bytes_per_launch"]
+    except OSError:
+        pass
+    return None
+
+
+def _read_csv(d, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def write_profiles(trace_dir, fetch_dir, write_dir):
+    """Summaries of rocprofv3 runs of this benchmark, as short markdown under profiles/.
+
+    trace_dir: --kernel-trace --stats --output-format csv; fetch_dir / write_dir:
+    --pmc FETCH_SIZE / --pmc WRITE_SIZE. The benchmark's weight clones run
+    __amd_rocclr_copyBuffer on buffers of known size, which calibrates the counters.
+    """
+    import statistics
+    lm_n, lm_k = 128256, 4096
+    lm_w = lm_n * lm_k // 2                      # bytes of lm_head codes, copied by one clone
+    stats = _read_csv(trace_dir, "kernel_stats.csv")
+    trace = _read_csv(trace_dir, "kernel_trace.csv")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    lines = ["# rocprofv3 kernel statistics: Llama-3-8B-shaped decode GEMV set, batch 1, 4-bit gs64", "",
+             "Command (from the repository root):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- "
+             "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline", "",
+             "| kernel | calls | average us | min us | max us | share of time |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"]
+        if "agq::" not in name:
+            continue
+        lines.append(f"| `{name.split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    by_grid = {}
+    for r in trace:
+        if "agq::qmv_kernel" in r["Kernel_Name"]:
+            by_grid.setdefault((r["Kernel_Name"].split("(")[0], r["Grid_Size_X"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines += ["", "Per launch shape (grid size in threads):", "", "| kernel | grid | launches | median us |",
+              "|---|---|---|---|"]
+    for (k, g), d in sorted(by_grid.items(), key=lambda kv: -statistics.median(kv[1])):
+        lines.append(f"| `{k}` | {g} | {len(d)} | {statistics.median(d):.2f} |")
+    with open(os.path.join(ROOT, "profiles", "qmv_llama_decode_set_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def counter(rows, cname):
+        out = {}
+        for r in rows:
+            if r["Counter_Name"] != cname:
+                continue
+            out.setdefault((r["Kernel_Name"].split("(")[0], int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return out
+
+    fetch = counter(_read_csv(fetch_dir, "counter_collection.csv"), "FETCH_SIZE")
+    write = counter(_read_csv(write_dir, "counter_collection.csv"), "WRITE_SIZE")
+    # The lm_head codes clone: the copyBuffer dispatch whose WRITE_SIZE is largest.
+    cf = max((v for k, v in fetch.items() if "copyBuffer" in k[0]), key=lambda v: max(v))
+    cw = max((v for k, v in write.items() if "copyBuffer" in k[0]), key=lambda v: max(v))
+    fetch_scale = lm_w / (max(cf) * 1024.0)
+    write_scale = lm_w / (max(cw) * 1024.0)
+    lm_key = max((k for k in fetch if "qmv_kernel" in k[0]), key=lambda k: statistics.median(fetch[k]))
+    f_kib = statistics.median(fetch[lm_key])
+    w_kib = statistics.median(write.get(lm_key, [0.0]))
+    traffic = f_kib * 1024 * fetch_scale + w_kib * 1024 * write_scale
+    algo = lm_n * lm_k // 2 + 4 * lm_n * lm_k // 64 + 2 * lm_k + 2 * lm_n
+    kname = lm_key[0].replace("void agq::", "")
+    rec = {"kernel": kname, "bytes_per_launch": round(traffic), "fetch_kib": f_kib, "write_kib": w_kib,
+           "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+           "algorithmic_bytes": algo, "source_hash": kernel_source_hash()}
+    md = ["# HBM traffic of the lm_head launch (128256x4096, 4-bit gs64, batch 1)", "",
+          "Commands (from the repository root), one counter per run:", "",
+          "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- "
+          "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+          "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o bench -- "
+          "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline", "",
+          "Calibration: the benchmark clones the lm_head codes (%d bytes) with `__amd_rocclr_copyBuffer`; "
+          "that dispatch reads %.1f KiB FETCH_SIZE and %.1f KiB WRITE_SIZE, so the counters are scaled by "
+          "%.4f (fetch) and %.4f (write)." % (lm_w, max(cf), max(cw), fetch_scale, write_scale), "",
+          "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
+          "|---|---|---|---|---|---|",
+          f"| `{kname}` | {f_kib:.1f} | {w_kib:.1f} | {traffic:.0f} | {algo} | {traffic / algo:.4f} |", "",
+          "traffic_json: " + json.dumps(rec)]
+    with open(TRAFFIC_MD, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
+    if args.write_profiles:
+        write_profiles(*args.write_profiles)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
@@ -143,7 +265,8 @@ def main():
         by_kernel.setdefault(kern(plans[n]), []).append(n)
     dom_key = max(by_kernel, key=lambda k: sum(algo_bytes(mats[n]["N"], mats[n]["K"], 4) for n in by_kernel[k]))
     dom = set(by_kernel[dom_key])
-    dom_name = "qmv_kernel<BITS=4, CPT=%d, MW=%d, R=%d>" % (dom_key[0], dom_key[1], dom_key[2])
+    dom_xl = "true" if plans[sorted(dom)[0]]["x_lds_bytes"] else "false"
+    dom_name = "qmv_kernel<4, %d, %d, %d, %s>" % (dom_key[0], dom_key[1], dom_key[2], dom_xl)
 
     stream = torch.cuda.Stream(dev)
     calls = [{name: agq.prepare_qmv(mats[name]["x"], *mats[name]["copies"][r], mats[name]["y"], bits=4,
@@ -240,7 +363,7 @@ def main():
                    "graph_replay_value": round(graph_gbps, 2),
                    "graph_replay_ms_per_step": round(graph_ms / args.steps, 5)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(dom_name),
                      "kernel": dom_name, "shapes": sorted(dom), "launches_per_step": launches_per_step,
                      "avg_launch_us": round(avg_launch_s * 1e6, 3)},
     }
