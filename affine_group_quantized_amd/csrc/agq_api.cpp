@@ -150,7 +150,8 @@ agq_status launch_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t expert
     agq_status st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
     for (int pass = 0; pass < 2; ++pass) {
-        *sym = agq::product_kernel(bits, plan->mw, plan->cpt, plan->R, plan->x_lds_bytes > 0, experts > 0);
+        *sym = agq::product_kernel(bits, plan->mw, plan->cpt, plan->R, plan->NB, plan->x_lds_bytes > 0,
+                                   experts > 0);
         if (!*sym)
             return fail(AGQ_ENOTSUP, "no kernel for bits=%d rows=%d cpt=%d R=%d", bits, plan->mw, plan->cpt,
                         plan->R);
@@ -173,6 +174,7 @@ void export_plan(const agq::Plan &p, agq_plan *out) {
     out->cpt = p.cpt;
     out->mw = p.mw;
     out->rows_per_iter = p.R;
+    out->stages = p.NB;
     out->waves_per_group = p.S;
     out->groups_per_block = p.GPB;
     out->threads_per_block = p.threads;

@@ -24,20 +24,25 @@ constexpr int kMaxPairs = 4096;        // gather: pair list kept in LDS as uint1
 #ifndef AGQ_LOADS_DEEP
 #define AGQ_LOADS_DEEP 8
 #endif
+#ifndef AGQ_STAGES_SHALLOW
+#define AGQ_STAGES_SHALLOW 2
+#endif
+#ifndef AGQ_STAGES_DEEP
+#define AGQ_STAGES_DEEP 2
+#endif
 #ifndef AGQ_DEEP_ROWS
 #define AGQ_DEEP_ROWS 16
 #endif
 constexpr int kWavesPerCuOverride = AGQ_WAVES_PER_CU;  // >0 forces this many waves per CU
-// 16-byte weight loads in flight per lane (both row buffers). Short walks use
-// the shallow depth (more, lighter waves finish sooner); walks of at least
-// kDeepRows rows per row group use the deep one.
+// 16-byte weight loads in flight per lane, counting every stage of the load
+// ring, and the ring depth. Short walks use the shallow plan (more, lighter
+// waves finish sooner); walks of at least kDeepRows rows per row group use the
+// deep one.
 constexpr int kLoadsShallow = AGQ_LOADS_SHALLOW;
 constexpr int kLoadsDeep = AGQ_LOADS_DEEP;
+constexpr int kStagesShallow = AGQ_STAGES_SHALLOW;
+constexpr int kStagesDeep = AGQ_STAGES_DEEP;
 constexpr int kDeepRows = AGQ_DEEP_ROWS;
-#ifndef AGQ_PIPELINE
-#define AGQ_PIPELINE 1  // double-buffer the row loads (1) or rely on wave interleaving alone (0)
-#endif
-constexpr bool kPipelined = AGQ_PIPELINE != 0;
 #ifndef AGQ_ROW_ORDER_CONTIGUOUS
 #define AGQ_ROW_ORDER_CONTIGUOUS 0  // 0: row groups take R-row slices round-robin; 1: contiguous ranges
 #endif
@@ -45,13 +50,16 @@ constexpr bool kPipelined = AGQ_PIPELINE != 0;
 constexpr int floor_pow2(int v) { return v >= 16 ? 16 : v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
 
 // Weight rows per wave iteration: aim for `loads` outstanding 16-byte loads
-// per lane counting both buffers of the double-buffered loop; keep R*MW
-// accumulators at or below 16 (register pressure of the wide and gather forms).
-constexpr int rows_per_iter(int cpt, int mw, int loads) {
-    return floor_pow2(loads / (kPipelined ? 2 : 1) / cpt) < floor_pow2(16 / mw)
-               ? floor_pow2(loads / (kPipelined ? 2 : 1) / cpt)
-               : floor_pow2(16 / mw);
+// per lane over the `stages` buffers of the load ring; keep R*MW accumulators
+// at or below 16 (register pressure of the wide and gather forms).
+constexpr int rows_per_iter(int cpt, int mw, int loads, int stages) {
+    return floor_pow2(loads / stages / cpt) < floor_pow2(16 / mw) ? floor_pow2(loads / stages / cpt)
+                                                                  : floor_pow2(16 / mw);
 }
+constexpr int plan_rows(int cpt, int mw, bool deep) {
+    return deep ? rows_per_iter(cpt, mw, kLoadsDeep, kStagesDeep) : rows_per_iter(cpt, mw, kLoadsShallow, kStagesShallow);
+}
+constexpr int plan_stages(bool deep) { return deep ? kStagesDeep : kStagesShallow; }
 
 #ifndef AGQ_X_LDS_MAX
 #define AGQ_X_LDS_MAX 32768
@@ -61,7 +69,7 @@ constexpr int rows_per_iter(int cpt, int mw, int loads) {
 constexpr int kXLdsMax = AGQ_X_LDS_MAX;
 
 struct Plan {
-    int bits = 0, C = 0, cpt = 0, mw = 0, R = 0, S = 0, GPB = 0, threads = 0;
+    int bits = 0, C = 0, cpt = 0, mw = 0, R = 0, NB = 0, S = 0, GPB = 0, threads = 0;
     int x_lds_bytes = 0;  // dynamic LDS for x; 0 = waves stage x straight from global memory
     int64_t RPG = 0, TG = 0, blocks = 0;
 };
@@ -88,7 +96,8 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
         if (q.S > kMaxWavesPerGroup) return AGQ_ENOTSUP;
         q.cpt = (q.C + 64 * q.S - 1) / (64 * q.S);
     }
-    q.R = rows_per_iter(q.cpt, q.mw, deep ? kLoadsDeep : kLoadsShallow);
+    q.R = plan_rows(q.cpt, q.mw, deep);
+    q.NB = plan_stages(deep);
     q.GPB = q.S == 1 ? 4 : (q.S == 2 ? 2 : 1);
     q.threads = 64 * q.S * q.GPB;
     // The waves of a block share their K columns only when each row group is a
@@ -110,8 +119,8 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
 inline void plan_grid(int64_t N, int64_t resident_waves, int64_t experts, Plan *q) {
     int64_t tg_target = resident_waves / q->S / (experts > 0 ? experts : 1);
     if (tg_target < 1) tg_target = 1;
-    // Iterations per group: a multiple of 2 when the row loop is double-buffered.
-    const int64_t step = kPipelined ? 2 : 1;
+    // Iterations per group: a multiple of the load ring depth.
+    const int64_t step = q->NB;
     int64_t iters = (N + tg_target * q->R - 1) / (tg_target * q->R);
     iters = ((iters + step - 1) / step) * step;
     // The fewest groups that cover N rows in `iters` iterations of R rows.

@@ -53,20 +53,48 @@ __device__ __forceinline__ float dpp_f32(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float readlane_f32(float v, int lane) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+// One halving step of a transposed wave reduction. For lanes l < 32 the swap
+// returns (a[l], a[l+32]); for l >= 32 it returns (b[l-32], b[l]). The sum
+// therefore holds a's 32 pair sums in the low half and b's in the high half:
+// two vectors fold into one with one swap and one add.
+__device__ __forceinline__ float fold32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum over the 64 lanes of a wave, the same bits in every lane. DPP butterflies
-// (quad swaps, then half-row and row mirrors) leave each 16-lane row holding its
-// row sum in every lane; the four row sums are then added in a fixed order.
-// Every lane of the wave must be active.
-__device__ __forceinline__ float wave_sum(float v) {
+// The same step inside each 32-lane half: lanes [0,16) of a half get a's sums
+// l + (l+16), lanes [16,32) get b's.
+__device__ __forceinline__ float fold16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the 16 lanes of each row, the same bits in every lane of the row:
+// DPP butterflies over lane pairs l^1, l^2, then the half-row and row mirrors.
+__device__ __forceinline__ float row_sum16(float v) {
     v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
     v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
     v += dpp_f32<0x141>(v);  // row_half_mirror
     v += dpp_f32<0x140>(v);  // row_mirror
-    return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+    return v;
+}
+
+// Wave sums of V lane-partial vectors at once. Value i ends up in every lane of
+// 16-lane row rho of t[i / 4], where i % 4 == sum_slot(rho). Every value is
+// summed by the same tree (pairs l^32, l^16, l^1, l^2, then the mirrors) and
+// floating-point addition is commutative, so a value's bits do not depend on
+// its slot. Every lane of the wave must be active.
+constexpr int sum_regs(int V) { return (V + 3) / 4; }
+__device__ __forceinline__ int sum_slot(int rho) { return ((rho & 1) << 1) | (rho >> 1); }
+
+template <int V>
+__device__ __forceinline__ void wave_sums(const float (&v)[V], float (&t)[sum_regs(V)]) {
+    constexpr int NU = (V + 1) / 2;
+    float u[NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) u[i] = fold32(v[2 * i], 2 * i + 1 < V ? v[2 * i + 1] : 0.f);
+#pragma unroll
+    for (int j = 0; j < sum_regs(V); ++j) t[j] = row_sum16(fold16(u[2 * j], 2 * j + 1 < NU ? u[2 * j + 1] : 0.f));
 }
 
 }  // namespace agq

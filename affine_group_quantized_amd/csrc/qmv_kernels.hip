@@ -19,9 +19,11 @@
 //  - S waves, each owning one K segment, form a row group that walks a
 //    contiguous range of RPG weight rows, R rows per iteration. All loads of
 //    an iteration (R*CPT 16-byte chunks per lane) are issued before any use.
-//  - Lane partial sums are reduced with DPP inside the wave. With S > 1 they
-//    are then combined through LDS in a fixed order, so results are bitwise
-//    deterministic.
+//  - The R*MW lane partials of an iteration are reduced together: cross-half
+//    swaps (v_permlane32_swap, v_permlane16_swap) fold pairs of them into one
+//    register, then DPP finishes each 16-lane row, about 2.5 VALU ops per
+//    value. With S > 1 the waves' sums are combined through LDS in a fixed
+//    order, so results are bitwise deterministic.
 //
 // 4-bit inner loop. Each packed word gives four bfloat16 pairs (128 + q)
 // with one AND, one shift-AND and four byte permutes. v_dot2c_f32_bf16
@@ -43,7 +45,6 @@
 
 namespace agq {
 
-constexpr int kRedSlots = kMaxWavesPerGroup * 64;
 
 
 // Dynamic LDS of the dense product kernels: the block's copy of x [M, K] (bf16).
@@ -94,16 +95,14 @@ __device__ __forceinline__ void stage_from_words(const u32x4 *d, uint32_t keep, 
     }
 }
 
-// Stage chunk `c` (in range) of activation row `xr` from global memory.
+// Raw activation words of chunk `c` (in range) of activation row `xr`, from
+// global memory: 4 x 16 B (4-bit codes) or 2 x 16 B (8-bit codes).
 template <int BITS>
-__device__ __forceinline__ void stage_x(const uint16_t *__restrict__ xr, int c, bool valid, uint32_t (&xv)[16],
-                                        float &xs) {
+__device__ __forceinline__ void fetch_x_chunk(const uint16_t *__restrict__ xr, int c, u32x4 (&d)[BITS == 4 ? 4 : 2]) {
     constexpr int W = BITS == 4 ? 4 : 2;
     const u32x4 *p = reinterpret_cast<const u32x4 *>(xr) + (int64_t)c * W;
-    u32x4 d[W];
 #pragma unroll
     for (int t = 0; t < W; ++t) d[t] = p[t];
-    stage_from_words<BITS>(d, valid ? 0xFFFFFFFFu : 0u, xv, xs);
 }
 
 // The same from the block's LDS copy of x: row m starts at 16-byte word m*K/8.
@@ -189,34 +188,52 @@ struct RowBuf {
     uint16_t b[R][CPT];  // loop entry, forcing a wait for these loads before the next ones
 };
 
-// Issue every load of rows [rb, rb + R) at once. Row and chunk indices are
-// clamped into range, so no load is conditional (a conditional load forces the
-// compiler to wait for it before the next one). Clamped duplicates are never
-// stored: out-of-range rows are skipped at the store and out-of-range chunks
-// meet zero activations. Row bases are wave-uniform scalar pointers and lane
-// offsets unsigned 32-bit byte offsets (the saddr + voffset load form).
-template <int BITS, int CPT, int R>
-__device__ __forceinline__ void load_rows(RowBuf<CPT, R> &buf, const u32x4 *__restrict__ wp,
-                                          const uint16_t *__restrict__ sp, const uint16_t *__restrict__ bp,
-                                          int64_t rb, int64_t row_last, const uint32_t (&woff)[CPT],
-                                          const uint32_t (&goff)[CPT], int64_t C, int64_t G) {
+// Third descriptor word of a raw buffer (gfx9 family: 32-bit data format,
+// no swizzle, stride 0) and the non-temporal cache policy of its loads.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kLoadNT = 2;
+
+// Descriptor over `bytes` bytes at `base`. Loads at offsets >= bytes return
+// zero without touching memory, so a descriptor of 0 bytes turns every load
+// through it into a zero fill.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+// The rows, scales and biases of one weight plane, with their row pitches.
+struct Plane {
+    const u32x4 *w;
+    const uint16_t *s, *b;
+    int64_t C, G;  // 16-byte chunks and 64-column groups per row
+};
+
+// Issue every load of rows [rb, rb + R) at once, through one buffer
+// descriptor per row and array. A row at or past `end` gets an empty
+// descriptor (its loads return zero and read nothing); chunks past the row end
+// fall outside the row's descriptor and read zero too. No load is conditional,
+// so the compiler's load-wait counts stay exact. Lane offsets are 32-bit byte
+// offsets; row bases are scalar.
+template <int CPT, int R>
+__device__ __forceinline__ void load_rows(RowBuf<CPT, R> &buf, const Plane &pl, int64_t rb, int64_t end,
+                                          const uint32_t (&woff)[CPT], const uint32_t (&goff)[CPT]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int64_t row = rb + r < row_last ? rb + r : row_last;
-        const char *wr = reinterpret_cast<const char *>(wp + row * C);
+        const bool in = rb + r < end;
+        const int64_t row = in ? rb + r : 0;
+        const __amdgpu_buffer_rsrc_t wr = byte_range(pl.w + row * pl.C, in ? (uint32_t)pl.C * 16u : 0u);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j)
-            buf.w[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr + woff[j]));
+        for (int j = 0; j < CPT; ++j) buf.w[r][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[j], 0, kLoadNT);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int64_t row = rb + r < row_last ? rb + r : row_last;
-        const char *sr = reinterpret_cast<const char *>(sp + row * G);
-        const char *br = reinterpret_cast<const char *>(bp + row * G);
+        const bool in = rb + r < end;
+        const int64_t row = in ? rb + r : 0;
+        const __amdgpu_buffer_rsrc_t sr = byte_range(pl.s + row * pl.G, in ? (uint32_t)pl.G * 2u : 0u);
+        const __amdgpu_buffer_rsrc_t br = byte_range(pl.b + row * pl.G, in ? (uint32_t)pl.G * 2u : 0u);
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            buf.s[r][j] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(sr + goff[j]));
-            buf.b[r][j] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(br + goff[j]));
+            buf.s[r][j] = __builtin_amdgcn_raw_buffer_load_b16(sr, goff[j], 0, kLoadNT);
+            buf.b[r][j] = __builtin_amdgcn_raw_buffer_load_b16(br, goff[j], 0, kLoadNT);
         }
     }
 }
@@ -246,50 +263,23 @@ __device__ __forceinline__ void compute_rows(const RowBuf<CPT, R> &buf, const ui
     }
 }
 
-// Reduce lane partials to row results and store them (rows >= row1 are dropped).
-// With S > 1 the S waves of a row group combine through LDS in a fixed order.
-template <int MW, int R>
-__device__ __forceinline__ void finish_rows(float (&acc)[R][MW], uint16_t *const *yrow, int64_t rb, int64_t row1,
-                                            int S, int wig, int grp, int lane, float *buf) {
-    if (S == 1) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < MW; ++m) {
-                const float t = wave_sum(acc[r][m]);
-                if (lane == 0 && rb + r < row1) yrow[m][rb + r] = f32_to_bf16(t);
-            }
-        return;
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < MW; ++m) {
-            const float t = wave_sum(acc[r][m]);
-            if (lane == 0) buf[(grp * S + wig) * (R * MW) + r * MW + m] = t;
-        }
-    __syncthreads();
-    if (wig == 0 && lane < R * MW) {
-        const int r = lane / MW, m = lane % MW;
-        float t = 0.f;
-        for (int s = 0; s < S; ++s) t += buf[(grp * S + s) * (R * MW) + lane];
-        if (rb + r < row1) {
-#pragma unroll
-            for (int mm = 0; mm < MW; ++mm)
-                if (mm == m) yrow[mm][rb + r] = f32_to_bf16(t);
-        }
-    }
-}
+// Output rows of the dense products: activation row m writes y[m, :].
+struct DenseOut {
+    uint16_t *y;
+    int64_t N;
+    __device__ __forceinline__ uint16_t *operator()(int m) const { return y + (int64_t)m * N; }
+};
 
 // The weight rows a row group visits: iteration `it` covers rows
 // [at(it), at(it) + R), dropping rows >= end.
 //  - Interleaved (default): row groups take R-row slices round-robin, so at
 //    any moment the whole grid reads one compact band of the matrix.
 //  - Contiguous: each group walks its own range of RPG rows.
+// Iterations past the walk land on rows >= end.
 struct RowWalk {
     int64_t first;   // first row of iteration 0
     int64_t stride;  // rows between consecutive iterations
-    int64_t end;     // rows >= end are not stored (and loads clamp to end - 1)
+    int64_t end;     // rows >= end are neither read nor stored
     __device__ __forceinline__ int64_t at(int it) const { return first + (int64_t)it * stride; }
 };
 
@@ -303,163 +293,213 @@ __device__ __forceinline__ RowWalk row_walk(const ProductArgs &a, int64_t rg, in
 #endif
 }
 
-// Shared core: MW activation rows (xrow[m]) against weight rows [row0, row1) of
-// one plane; outputs to yrow[m][n]. `iters` must be equal for every row group of
-// the block when S > 1 (block-wide barriers).
+// Reduce the lane partials of iteration `it` to row results and store them.
+// All R*MW values are reduced together (wave_sums); value i = r*MW + m leaves
+// in row rho = lane/16 of register i/4, and the first lane of that row owns it.
+//  - S == 1: that lane stores it.
+//  - S > 1: it goes to the wave's LDS slot for the iteration. Every F
+//    iterations (and after the last) the block meets at one barrier and the
+//    first wave of each row group adds the S waves' slots in a fixed order and
+//    stores the rows. Two slot regions alternate, so one barrier per flush
+//    suffices: a region is written again only after the next barrier, which
+//    the combining wave reaches after its reads.
+template <int MW, int R>
+struct Flush {
+    static constexpr int V = R * MW;
+    static constexpr int F = 64 / V;  // iterations per flush: F*V <= 64 values, one per lane
+};
+constexpr int kSlotFloats = 64;  // per wave and region
+constexpr int kBlockWaves = 8;   // __launch_bounds__(512)
+
+template <int MW, int R, typename Out>
+__device__ __forceinline__ void finish_rows(float (&acc)[R][MW], const Out &out, const RowWalk &walk, int it,
+                                            int iters, int S, int wig, int grp, int lane, float *red) {
+    constexpr int V = Flush<MW, R>::V;
+    float v[V], t[sum_regs(V)];
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = acc[i / MW][i % MW];
+    wave_sums<V>(v, t);
+    const int rho = lane >> 4;
+    const bool leader = (lane & 15) == 0;
+    if (S == 1) {
+        const int64_t rb = walk.at(it);
+#pragma unroll
+        for (int j = 0; j < sum_regs(V); ++j) {
+            const int i = 4 * j + sum_slot(rho);
+            const int r = i / MW, m = i % MW;
+            if (leader && i < V && rb + r < walk.end) out(m)[rb + r] = f32_to_bf16(t[j]);
+        }
+        return;
+    }
+    constexpr int F = Flush<MW, R>::F;
+    const int slot = it % F;
+    float *region = red + ((it / F) & 1) * (kBlockWaves * kSlotFloats);
+#pragma unroll
+    for (int j = 0; j < sum_regs(V); ++j) {
+        const int i = 4 * j + sum_slot(rho);
+        if (leader && i < V) region[(grp * S + wig) * kSlotFloats + slot * V + i] = t[j];
+    }
+    if (slot == F - 1 || it == iters - 1) {  // uniform over the block (equal iteration counts)
+        __syncthreads();
+        if (wig == 0 && lane < (slot + 1) * V) {
+            float tot = 0.f;
+            for (int s = 0; s < S; ++s) tot += region[(grp * S + s) * kSlotFloats + lane];
+            const int i = lane % V, r = i / MW, m = i % MW;
+            const int64_t row = walk.at(it - slot + lane / V) + r;
+            if (row < walk.end) out(m)[row] = f32_to_bf16(tot);
+        }
+    }
+}
+
+// Shared core: MW activation rows (xrow[m]) against the weight rows that
+// `walk` visits in one plane; row n of activation row m goes to out(m)[n].
+// `iters` (a multiple of NB) must be equal for every row group of the block
+// when S > 1 or XL (block-wide barriers).
 //
-// The row loop is software-pipelined over two register buffers: the loads of
-// the next R rows are in flight while the current R rows are computed.
-template <int BITS, int CPT, int MW, int R, bool XL = false>
-__device__ __forceinline__ void product_rows(const ProductArgs &a, const u32x4 *__restrict__ wp,
-                                             const uint16_t *__restrict__ sp, const uint16_t *__restrict__ bp,
-                                             const uint16_t *const *xrow, uint16_t *const *yrow,
-                                             const RowWalk &walk, int iters, float *red) {
+// The row loop streams through a ring of NB register buffers: each buffer is
+// refilled with the rows NB iterations ahead as soon as it has been consumed.
+// Rows past the walk read nothing (empty descriptors).
+template <int BITS, int CPT, int MW, int R, int NB, bool XL = false, typename Out>
+__device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &pl, const uint16_t *const *xrow,
+                                             const Out &out, const RowWalk &walk, int iters, float *red) {
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int S = a.S;
     const int wig = wave % S;
     const int grp = wave / S;
 
-    int chunk[CPT];   // clamped chunk index: lanes past the row end reload the last chunk
+    int chunk[CPT];
     bool cv[CPT];
     uint32_t woff[CPT], goff[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        const int c = (wig * CPT + j) * 64 + lane;
-        cv[j] = c < a.C;
-        chunk[j] = cv[j] ? c : a.C - 1;
+        chunk[j] = (wig * CPT + j) * 64 + lane;
+        cv[j] = chunk[j] < a.C;
         woff[j] = (uint32_t)chunk[j] * 16u;
         goff[j] = (uint32_t)(chunk[j] / Fmt<BITS>::CPG) * 2u;
     }
 
-    const int64_t C = a.C, G = a.G;
-    // Loads clamp to the last row of the walk, so iterations past the end
-    // re-read that row and store nothing; no load is ever out of bounds.
-    const int64_t row_last = walk.end - 1;
-    RowBuf<CPT, R> A;
-#if AGQ_PIPELINE
-    RowBuf<CPT, R> B;
-#endif
-    // Order: x loads, then the first weight loads, then wait for x alone, fill
-    // LDS and stage, while the weight loads are in flight.
-    // XL (compile time): the block stages x through LDS. One code path per
-    // kernel keeps the compiler's load-wait placement exact.
+    RowBuf<CPT, R> buf[NB];
+    // Order: x loads, then the first iteration's weight loads, then wait for x
+    // alone (loads retire in order) and stage it while those are in flight;
+    // then the loads of the other NB-1 ring stages. (Issuing every stage ahead
+    // of the staging delays the first stage's data for a wave that cannot
+    // start before it.)
+    // XL (compile time): the block copies x into LDS and every wave stages its
+    // slice from there; otherwise each wave reads its slice from global memory.
+    // One code path per kernel keeps the compiler's load-wait placement exact.
+    // Lanes past the row end read a clamped chunk and stage zeros.
+    constexpr int XC = BITS == 4 ? 4 : 2;  // 16-byte words of x per chunk
     const int n16 = XL ? (int)((int64_t)MW * a.K / 8) : 0;
-    constexpr int XW = BITS == 4 ? MW * CPT : (MW * CPT + 1) / 2;
+    constexpr int XW = XL ? (BITS == 4 ? MW * CPT : (MW * CPT + 1) / 2) : 1;
     u32x4 xr[XW];
-    if constexpr (XL) fetch_x(xrow[0], n16, xr);
-    load_rows<BITS, CPT, R>(A, wp, sp, bp, walk.at(0), row_last, woff, goff, C, G);
+    u32x4 xraw[XL ? 1 : MW][XL ? 1 : CPT][XC];
+    if constexpr (XL) {
+        fetch_x(xrow[0], n16, xr);
+    } else {
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) fetch_x_chunk<BITS>(xrow[m], cv[j] ? chunk[j] : a.C - 1, xraw[m][j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_rows<CPT, R>(buf[0], pl, walk.at(0), walk.end, woff, goff);
     __builtin_amdgcn_sched_barrier(0);
 
     uint32_t xv[MW][CPT][16];
     float xs[MW][CPT], nxs[MW][CPT];
-    // Activation slices: from the block's LDS copy of x when there is one,
-    // otherwise straight from global memory (xrow).
     if constexpr (XL) {
         store_x(n16, xr);  // block barrier: every wave of the block gets here
 #pragma unroll
         for (int m = 0; m < MW; ++m)
 #pragma unroll
             for (int j = 0; j < CPT; ++j)
-                stage_x_lds<BITS>((int64_t)m * a.K / 8, chunk[j], cv[j], xv[m][j], xs[m][j]);
+                stage_x_lds<BITS>((int64_t)m * a.K / 8, cv[j] ? chunk[j] : a.C - 1, cv[j], xv[m][j], xs[m][j]);
     } else {
 #pragma unroll
         for (int m = 0; m < MW; ++m)
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) stage_x<BITS>(xrow[m], chunk[j], cv[j], xv[m][j], xs[m][j]);
+            for (int j = 0; j < CPT; ++j) stage_from_words<BITS>(xraw[m][j], cv[j] ? 0xFFFFFFFFu : 0u, xv[m][j], xs[m][j]);
     }
 #pragma unroll
     for (int m = 0; m < MW; ++m)
 #pragma unroll
         for (int j = 0; j < CPT; ++j) nxs[m][j] = BITS == 4 ? -128.f * xs[m][j] : 0.f;
-
-    float acc[R][MW];
-#if AGQ_PIPELINE
-    // `iters` is even. The next buffer's loads are issued before the current
-    // buffer is consumed; the uniform branch skips the refill past the end
-    // (clamped, it would send every wave of the grid to the same last row).
-    // `iters` is even. The loop runs every pair but the last with unconditional
-    // loads, and the last pair is peeled: a conditional refill would make the
-    // compiler's load-wait counts conservative (it would wait for the refill
-    // too), and a clamped unconditional one would send every wave of the grid
-    // to the same last row at once. Scheduling barriers keep one buffer's use
-    // from being hoisted above the other buffer's loads.
-    int it = 0;
-    for (; it + 2 < iters; it += 2) {
-        load_rows<BITS, CPT, R>(B, wp, sp, bp, walk.at(it + 1), row_last, woff, goff, C, G);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_rows<BITS, CPT, MW, R>(A, xv, xs, nxs, acc);
-        finish_rows<MW, R>(acc, yrow, walk.at(it), walk.end, S, wig, grp, lane, red);
-        load_rows<BITS, CPT, R>(A, wp, sp, bp, walk.at(it + 2), row_last, woff, goff, C, G);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_rows<BITS, CPT, MW, R>(B, xv, xs, nxs, acc);
-        finish_rows<MW, R>(acc, yrow, walk.at(it + 1), walk.end, S, wig, grp, lane, red + kRedSlots);
-    }
-    load_rows<BITS, CPT, R>(B, wp, sp, bp, walk.at(it + 1), row_last, woff, goff, C, G);
+#pragma unroll
+    for (int p = 1; p < NB; ++p) load_rows<CPT, R>(buf[p], pl, walk.at(p), walk.end, woff, goff);
     __builtin_amdgcn_sched_barrier(0);
-    compute_rows<BITS, CPT, MW, R>(A, xv, xs, nxs, acc);
-    finish_rows<MW, R>(acc, yrow, walk.at(it), walk.end, S, wig, grp, lane, red);
-    compute_rows<BITS, CPT, MW, R>(B, xv, xs, nxs, acc);
-    finish_rows<MW, R>(acc, yrow, walk.at(it + 1), walk.end, S, wig, grp, lane, red + kRedSlots);
-#else
-    for (int it = 0; it < iters; ++it) {
-        const int64_t rb = walk.at(it);
-        if (it > 0) load_rows<BITS, CPT, R>(A, wp, sp, bp, rb, row_last, woff, goff, C, G);
-        compute_rows<BITS, CPT, MW, R>(A, xv, xs, nxs, acc);
-        finish_rows<MW, R>(acc, yrow, rb, walk.end, S, wig, grp, lane, red + (it & 1) * kRedSlots);
+
+    // Every turn of the ring but the last refills each buffer NB iterations
+    // ahead once it is consumed; the last turn (iterations iters-NB .. iters-1)
+    // issues no loads. (Refills past the walk would read nothing, but each
+    // load instruction still costs address-unit time.)
+    float acc[R][MW];
+    int it0 = 0;
+    for (; it0 + NB < iters; it0 += NB) {
+#pragma unroll
+        for (int p = 0; p < NB; ++p) {
+            compute_rows<BITS, CPT, MW, R>(buf[p], xv, xs, nxs, acc);
+            finish_rows<MW, R>(acc, out, walk, it0 + p, iters, S, wig, grp, lane, red);
+            load_rows<CPT, R>(buf[p], pl, walk.at(it0 + p + NB), walk.end, woff, goff);
+            // Keep the next buffer's use below this refill.
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-#endif
-    if (S > 1) __syncthreads();  // the LDS buffers are reused by the caller's next pass
+#pragma unroll
+    for (int p = 0; p < NB; ++p) {
+        compute_rows<BITS, CPT, MW, R>(buf[p], xv, xs, nxs, acc);
+        finish_rows<MW, R>(acc, out, walk, it0 + p, iters, S, wig, grp, lane, red);
+    }
+    if (S > 1) __syncthreads();  // the LDS slots are reused by the caller's next pass
 }
 
-template <int BITS, int CPT, int MW, int R, bool XL>
+// LDS slots of the K-split combine: two regions of kSlotFloats per wave.
+constexpr int kRedFloats = 2 * kBlockWaves * kSlotFloats;
+
+template <int BITS, int CPT, int MW, int R, int NB, bool XL>
 __global__ __launch_bounds__(512) void qmv_kernel(ProductArgs a) {
-    __shared__ float red[2 * kRedSlots];
+    __shared__ float red[kRedFloats];
     const int wave = wave_id();
     const int64_t rg = (int64_t)blockIdx.x * a.GPB + wave / a.S;
     const RowWalk walk = row_walk<R>(a, rg, (int64_t)gridDim.x * a.GPB);
     // A wave without rows may leave only when it meets no block barrier: with
-    // S == 1 and x read from global memory. (Otherwise it runs clamped re-reads
-    // of the last row and stores nothing.)
+    // S == 1 and x read from global memory. (Otherwise it walks rows past the
+    // end, which read nothing and store nothing.)
     if (a.S == 1 && !XL && walk.first >= walk.end) return;
-    const int iters = (int)(a.RPG / R);             // RPG is a multiple of R (of 2R when pipelined)
+    const int iters = (int)(a.RPG / R);  // RPG is a multiple of NB*R
     const uint16_t *xrow[MW];
-    uint16_t *yrow[MW];
 #pragma unroll
-    for (int m = 0; m < MW; ++m) {
-        xrow[m] = a.x + (int64_t)m * a.K;
-        yrow[m] = a.y + (int64_t)m * a.N;
-    }
-    product_rows<BITS, CPT, MW, R, XL>(a, a.w, a.s, a.b, xrow, yrow, walk, iters, red);
+    for (int m = 0; m < MW; ++m) xrow[m] = a.x + (int64_t)m * a.K;
+    const Plane pl{a.w, a.s, a.b, a.C, a.G};
+    product_rows<BITS, CPT, MW, R, NB, XL>(a, pl, xrow, DenseOut{a.y, a.N}, walk, iters, red);
 }
+
+// Output rows of a gather pass: its m-th pair p = plist[m] writes y[p, :].
+struct GatherOut {
+    uint16_t *y;
+    int64_t N;
+    const uint16_t *plist;
+    __device__ __forceinline__ uint16_t *operator()(int m) const { return y + (int64_t)plist[m] * N; }
+};
 
 // Rows per iteration of a gather pass with ME pairs: fewer rows in flight for the
 // widest passes (register pressure). Any R partitions the same rows exactly once.
 constexpr int gather_rows(int me, int r) { return me > 4 ? 1 : r; }
 
-template <int BITS, int ME, int R>
-__device__ __forceinline__ void gather_pass(const ProductArgs &a, const u32x4 *wp, const uint16_t *sp,
-                                            const uint16_t *bp, const uint16_t *plist, int base,
-                                            const RowWalk &walk, int iters, float *red) {
+template <int BITS, int ME, int R, int NB>
+__device__ __forceinline__ void gather_pass(const ProductArgs &a, const Plane &pl, const uint16_t *plist, int base,
+                                            int64_t rg, int64_t groups, float *red) {
+    constexpr int RR = gather_rows(ME, R);
+    const RowWalk walk = row_walk<RR>(a, rg, groups);
     const uint16_t *xrow[ME];
-    uint16_t *yrow[ME];
 #pragma unroll
     for (int m = 0; m < ME; ++m) {
         const int p = plist[base + m];
         const int64_t xr = a.lhs ? (int64_t)a.lhs[p] : (int64_t)p;
         xrow[m] = a.x + xr * a.K;
-        yrow[m] = a.y + (int64_t)p * a.N;
     }
-    product_rows<BITS, 1, ME, R>(a, wp, sp, bp, xrow, yrow, walk, iters, red);
-}
-
-template <int BITS, int ME, int R>
-__device__ __forceinline__ void gather_pass_rows(const ProductArgs &a, const u32x4 *wp, const uint16_t *sp,
-                                                 const uint16_t *bp, const uint16_t *plist, int base, int64_t rg,
-                                                 int64_t groups, float *red) {
-    constexpr int RR = gather_rows(ME, R);
-    const RowWalk walk = row_walk<RR>(a, rg, groups);
-    gather_pass<BITS, ME, RR>(a, wp, sp, bp, plist, base, walk, (int)(a.RPG / RR), red);
+    // RPG is a multiple of NB*R, so RPG / RR is a multiple of NB.
+    product_rows<BITS, 1, ME, RR, NB>(a, pl, xrow, GatherOut{a.y, a.N, plist + base}, walk, (int)(a.RPG / RR), red);
 }
 
 // Compact (ascending) the pairs p < P that satisfy `pred` into list[]; wave 0 only.
@@ -480,9 +520,9 @@ __device__ __forceinline__ int compact_pairs(int P, uint16_t *list, Pred pred) {
 // blockIdx.y = expert plane e; blockIdx.x = row tile. Pairs routed to e are
 // grouped in LDS, so each used plane streams from memory once per pass of up
 // to 8 pairs. A block whose expert has no pairs exits before reading weights.
-template <int BITS, int R>
+template <int BITS, int R, int NB>
 __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
-    __shared__ float red[2 * kRedSlots];
+    __shared__ float red[kRedFloats];
     __shared__ uint16_t plist[kMaxPairs];
     __shared__ int pcount;
     const int lane = threadIdx.x & 63;
@@ -530,20 +570,18 @@ __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
     const int count = pcount;
     if (count == 0) return;
     if (a.S == 1 && walk.first >= walk.end) return;
-    const u32x4 *wp = a.w + (int64_t)e * a.N * a.C;
-    const uint16_t *sp = a.s + (int64_t)e * a.N * a.G;
-    const uint16_t *bp = a.b + (int64_t)e * a.N * a.G;
+    const Plane pl{a.w + (int64_t)e * a.N * a.C, a.s + (int64_t)e * a.N * a.G, a.b + (int64_t)e * a.N * a.G, a.C, a.G};
     for (int base = 0; base < count; base += 8) {
         const int me = count - base < 8 ? count - base : 8;
         switch (me) {
-            case 1: gather_pass_rows<BITS, 1, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
-            case 2: gather_pass_rows<BITS, 2, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
-            case 3: gather_pass_rows<BITS, 3, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
-            case 4: gather_pass_rows<BITS, 4, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
-            case 5: gather_pass_rows<BITS, 5, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
-            case 6: gather_pass_rows<BITS, 6, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
-            case 7: gather_pass_rows<BITS, 7, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
-            default: gather_pass_rows<BITS, 8, R>(a, wp, sp, bp, plist, base, rg, groups, red); break;
+            case 1: gather_pass<BITS, 1, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 2: gather_pass<BITS, 2, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 3: gather_pass<BITS, 3, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 4: gather_pass<BITS, 4, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 5: gather_pass<BITS, 5, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 6: gather_pass<BITS, 6, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 7: gather_pass<BITS, 7, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            default: gather_pass<BITS, 8, R, NB>(a, pl, plist, base, rg, groups, red); break;
         }
     }
 }
@@ -576,87 +614,90 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
 // ---------------------------------------------------------------------------
 // Kernel selection.
 
-template <int BITS, int MW, int CPT, int R>
+template <int BITS, int MW, int CPT, int R, int NB>
 static const void *qmv_sym_xl(bool xl) {
     // The LDS-staged form exists for MW <= 4 only (x fits the LDS budget then).
     if constexpr (MW <= 4) {
-        if (xl) return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, true>);
+        if (xl) return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, NB, true>);
     } else {
         if (xl) return nullptr;
     }
-    return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, false>);
+    return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, NB, false>);
 }
 
+// The shallow and the deep plan of each (MW, CPT).
 template <int BITS, int MW, int CPT>
-static const void *qmv_sym(int R, bool xl) {
-    constexpr int RS = rows_per_iter(CPT, MW, kLoadsShallow), RD = rows_per_iter(CPT, MW, kLoadsDeep);
-    if (R == RS) return qmv_sym_xl<BITS, MW, CPT, RS>(xl);
-    if (R == RD) return qmv_sym_xl<BITS, MW, CPT, RD>(xl);
+static const void *qmv_sym(int R, int NB, bool xl) {
+    constexpr int RS = plan_rows(CPT, MW, false), RD = plan_rows(CPT, MW, true);
+    constexpr int NS = plan_stages(false), ND = plan_stages(true);
+    if (R == RS && NB == NS) return qmv_sym_xl<BITS, MW, CPT, RS, NS>(xl);
+    if (R == RD && NB == ND) return qmv_sym_xl<BITS, MW, CPT, RD, ND>(xl);
     return nullptr;
 }
 
 template <int BITS, int MW>
-static const void *qmv_by_cpt(int cpt, int R, bool xl) {
+static const void *qmv_by_cpt(int cpt, int R, int NB, bool xl) {
     if constexpr (kXRegBudget / MW >= 8) {
         switch (cpt) {
-            case 1: return qmv_sym<BITS, MW, 1>(R, xl);
-            case 2: return qmv_sym<BITS, MW, 2>(R, xl);
-            case 3: return qmv_sym<BITS, MW, 3>(R, xl);
-            case 4: return qmv_sym<BITS, MW, 4>(R, xl);
-            case 5: return qmv_sym<BITS, MW, 5>(R, xl);
-            case 6: return qmv_sym<BITS, MW, 6>(R, xl);
-            case 7: return qmv_sym<BITS, MW, 7>(R, xl);
+            case 1: return qmv_sym<BITS, MW, 1>(R, NB, xl);
+            case 2: return qmv_sym<BITS, MW, 2>(R, NB, xl);
+            case 3: return qmv_sym<BITS, MW, 3>(R, NB, xl);
+            case 4: return qmv_sym<BITS, MW, 4>(R, NB, xl);
+            case 5: return qmv_sym<BITS, MW, 5>(R, NB, xl);
+            case 6: return qmv_sym<BITS, MW, 6>(R, NB, xl);
+            case 7: return qmv_sym<BITS, MW, 7>(R, NB, xl);
             case 8:
-                if constexpr (kMaxCpt >= 8) return qmv_sym<BITS, MW, 8>(R, xl);
+                if constexpr (kMaxCpt >= 8) return qmv_sym<BITS, MW, 8>(R, NB, xl);
                 break;
         }
     } else if constexpr (kXRegBudget / MW >= 4) {
         switch (cpt) {
-            case 1: return qmv_sym<BITS, MW, 1>(R, xl);
-            case 2: return qmv_sym<BITS, MW, 2>(R, xl);
-            case 3: return qmv_sym<BITS, MW, 3>(R, xl);
-            case 4: return qmv_sym<BITS, MW, 4>(R, xl);
+            case 1: return qmv_sym<BITS, MW, 1>(R, NB, xl);
+            case 2: return qmv_sym<BITS, MW, 2>(R, NB, xl);
+            case 3: return qmv_sym<BITS, MW, 3>(R, NB, xl);
+            case 4: return qmv_sym<BITS, MW, 4>(R, NB, xl);
         }
     } else if constexpr (kXRegBudget / MW >= 2) {
         switch (cpt) {
-            case 1: return qmv_sym<BITS, MW, 1>(R, xl);
-            case 2: return qmv_sym<BITS, MW, 2>(R, xl);
+            case 1: return qmv_sym<BITS, MW, 1>(R, NB, xl);
+            case 2: return qmv_sym<BITS, MW, 2>(R, NB, xl);
         }
     } else {
-        if (cpt == 1) return qmv_sym<BITS, MW, 1>(R, xl);
+        if (cpt == 1) return qmv_sym<BITS, MW, 1>(R, NB, xl);
     }
     return nullptr;
 }
 
 template <int BITS>
-static const void *qmv_by_mw(int mw, int cpt, int R, bool xl) {
+static const void *qmv_by_mw(int mw, int cpt, int R, int NB, bool xl) {
     switch (mw) {
-        case 1: return qmv_by_cpt<BITS, 1>(cpt, R, xl);
-        case 2: return qmv_by_cpt<BITS, 2>(cpt, R, xl);
-        case 3: return qmv_by_cpt<BITS, 3>(cpt, R, xl);
-        case 4: return qmv_by_cpt<BITS, 4>(cpt, R, xl);
-        case 5: return qmv_by_cpt<BITS, 5>(cpt, R, xl);
-        case 6: return qmv_by_cpt<BITS, 6>(cpt, R, xl);
-        case 7: return qmv_by_cpt<BITS, 7>(cpt, R, xl);
-        case 8: return qmv_by_cpt<BITS, 8>(cpt, R, xl);
+        case 1: return qmv_by_cpt<BITS, 1>(cpt, R, NB, xl);
+        case 2: return qmv_by_cpt<BITS, 2>(cpt, R, NB, xl);
+        case 3: return qmv_by_cpt<BITS, 3>(cpt, R, NB, xl);
+        case 4: return qmv_by_cpt<BITS, 4>(cpt, R, NB, xl);
+        case 5: return qmv_by_cpt<BITS, 5>(cpt, R, NB, xl);
+        case 6: return qmv_by_cpt<BITS, 6>(cpt, R, NB, xl);
+        case 7: return qmv_by_cpt<BITS, 7>(cpt, R, NB, xl);
+        case 8: return qmv_by_cpt<BITS, 8>(cpt, R, NB, xl);
     }
     return nullptr;
 }
 
 template <int BITS>
-static const void *gather_sym(int R) {
-    constexpr int RS = rows_per_iter(1, 8, kLoadsShallow), RD = rows_per_iter(1, 8, kLoadsDeep);
-    if (R == RS) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, RS>);
-    if (R == RD) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, RD>);
+static const void *gather_sym(int R, int NB) {
+    constexpr int RS = plan_rows(1, 8, false), RD = plan_rows(1, 8, true);
+    constexpr int NS = plan_stages(false), ND = plan_stages(true);
+    if (R == RS && NB == NS) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, RS, NS>);
+    if (R == RD && NB == ND) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, RD, ND>);
     return nullptr;
 }
 
-const void *product_kernel(int bits, int mw, int cpt, int R, bool x_lds, bool gather) {
+const void *product_kernel(int bits, int mw, int cpt, int R, int NB, bool x_lds, bool gather) {
     if (gather) {
         if (cpt != 1 || mw != 8 || x_lds) return nullptr;
-        return bits == 4 ? gather_sym<4>(R) : gather_sym<8>(R);
+        return bits == 4 ? gather_sym<4>(R, NB) : gather_sym<8>(R, NB);
     }
-    return bits == 4 ? qmv_by_mw<4>(mw, cpt, R, x_lds) : qmv_by_mw<8>(mw, cpt, R, x_lds);
+    return bits == 4 ? qmv_by_mw<4>(mw, cpt, R, NB, x_lds) : qmv_by_mw<8>(mw, cpt, R, NB, x_lds);
 }
 
 const void *dequant_kernel_sym(int bits) {

@@ -154,6 +154,9 @@ typedef struct agq_plan {
     int32_t row_order;       /* 0: group g takes rows (it*row_groups + g)*R + r (round-robin);
                                 1: group g takes rows [g*rows_per_group, (g+1)*rows_per_group) */
     int32_t x_lds_bytes;     /* LDS per block holding x (0: waves read x from global memory) */
+    int32_t stages;          /* depth of each wave's ring of in-flight row loads; rows_per_group is a
+                                multiple of stages x rows_per_iter */
+    int32_t reserved_;
 } agq_plan;
 
 agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group_size,

@@ -141,7 +141,7 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
     assert (p["waves_per_group"] - 1) * p["cpt"] * 64 < C                 # no wave is idle
     assert p["threads_per_block"] == 64 * p["waves_per_group"] * p["groups_per_block"] <= 512
     R, TG, RPG = p["rows_per_iter"], p["row_groups"], p["rows_per_group"]
-    assert RPG % (2 * R) == 0                                            # even iterations (double-buffered)
+    assert p["stages"] >= 1 and RPG % (p["stages"] * R) == 0              # whole turns of the load ring
     assert TG == p["blocks"] * p["groups_per_block"]
     assert TG * RPG >= N                                                 # every row is covered
     assert (TG - p["groups_per_block"]) * RPG < N                        # at most one block's groups spare
