@@ -30,6 +30,12 @@ constexpr int kMaxPairs = 4096;        // gather: pair list kept in LDS as uint1
 #ifndef AGQ_STAGES_DEEP
 #define AGQ_STAGES_DEEP 2
 #endif
+#ifndef AGQ_LOADS_WIDE
+#define AGQ_LOADS_WIDE 4
+#endif
+#ifndef AGQ_STAGES_WIDE
+#define AGQ_STAGES_WIDE 2
+#endif
 #ifndef AGQ_DEEP_ROWS
 #define AGQ_DEEP_ROWS 16
 #endif
@@ -43,6 +49,11 @@ constexpr int kLoadsDeep = AGQ_LOADS_DEEP;
 constexpr int kStagesShallow = AGQ_STAGES_SHALLOW;
 constexpr int kStagesDeep = AGQ_STAGES_DEEP;
 constexpr int kDeepRows = AGQ_DEEP_ROWS;
+// Several activation rows per pass (MW > 1: the wide and gather forms): x
+// takes 16*MW*CPT VGPRs per lane, residency is low, and each wave needs more
+// rows in flight. One plan for short and long walks.
+constexpr int kLoadsWide = AGQ_LOADS_WIDE;
+constexpr int kStagesWide = AGQ_STAGES_WIDE;
 #ifndef AGQ_ROW_ORDER_CONTIGUOUS
 #define AGQ_ROW_ORDER_CONTIGUOUS 0  // 0: row groups take R-row slices round-robin; 1: contiguous ranges
 #endif
@@ -57,10 +68,18 @@ constexpr int rows_per_iter(int cpt, int mw, int loads, int stages) {
                                                                   : floor_pow2(16 / mw);
 }
 constexpr int plan_rows(int cpt, int mw, bool deep) {
-    return deep ? rows_per_iter(cpt, mw, kLoadsDeep, kStagesDeep) : rows_per_iter(cpt, mw, kLoadsShallow, kStagesShallow);
+    return mw > 1  ? rows_per_iter(cpt, mw, kLoadsWide, kStagesWide)
+           : deep ? rows_per_iter(cpt, mw, kLoadsDeep, kStagesDeep)
+                  : rows_per_iter(cpt, mw, kLoadsShallow, kStagesShallow);
 }
-constexpr int plan_stages(bool deep) { return deep ? kStagesDeep : kStagesShallow; }
+constexpr int plan_stages(int mw, bool deep) { return mw > 1 ? kStagesWide : deep ? kStagesDeep : kStagesShallow; }
 
+#ifndef AGQ_GPB_S1
+#define AGQ_GPB_S1 4  // row groups (waves) per block when one wave covers a row
+#endif
+#ifndef AGQ_XL_DEEP
+#define AGQ_XL_DEEP 0  // stage x through LDS for long walks too
+#endif
 #ifndef AGQ_X_LDS_MAX
 #define AGQ_X_LDS_MAX 32768
 #endif
@@ -97,8 +116,8 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
         q.cpt = (q.C + 64 * q.S - 1) / (64 * q.S);
     }
     q.R = plan_rows(q.cpt, q.mw, deep);
-    q.NB = plan_stages(deep);
-    q.GPB = q.S == 1 ? 4 : (q.S == 2 ? 2 : 1);
+    q.NB = plan_stages(q.mw, deep);
+    q.GPB = q.S == 1 ? AGQ_GPB_S1 : (q.S == 2 ? 2 : 1);
     q.threads = 64 * q.S * q.GPB;
     // The waves of a block share their K columns only when each row group is a
     // single wave; then one LDS copy of x serves the whole block.
@@ -106,7 +125,7 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
     // (The kernel copies x with 256 threads holding at most MW*CPT 16-byte words each.)
     // Long walks (the deep plan) amortize each wave's own staging of x over
     // many rows, and skip the block barrier the LDS copy needs.
-    q.x_lds_bytes = (!gather && !deep && q.S == 1 && q.GPB == 4 && q.mw <= 4 && xbytes <= kXLdsMax) ? (int)xbytes : 0;
+    q.x_lds_bytes = (!gather && (AGQ_XL_DEEP || !deep) && q.S == 1 && q.GPB >= 4 && q.mw <= 4 && xbytes <= kXLdsMax) ? (int)xbytes : 0;
     *p = q;
     return AGQ_OK;
 }

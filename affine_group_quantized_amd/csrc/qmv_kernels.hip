@@ -629,9 +629,11 @@ static const void *qmv_sym_xl(bool xl) {
 template <int BITS, int MW, int CPT>
 static const void *qmv_sym(int R, int NB, bool xl) {
     constexpr int RS = plan_rows(CPT, MW, false), RD = plan_rows(CPT, MW, true);
-    constexpr int NS = plan_stages(false), ND = plan_stages(true);
+    constexpr int NS = plan_stages(MW, false), ND = plan_stages(MW, true);
     if (R == RS && NB == NS) return qmv_sym_xl<BITS, MW, CPT, RS, NS>(xl);
-    if (R == RD && NB == ND) return qmv_sym_xl<BITS, MW, CPT, RD, ND>(xl);
+    if constexpr (RD != RS || ND != NS) {
+        if (R == RD && NB == ND) return qmv_sym_xl<BITS, MW, CPT, RD, ND>(xl);
+    }
     return nullptr;
 }
 
@@ -685,10 +687,8 @@ static const void *qmv_by_mw(int mw, int cpt, int R, int NB, bool xl) {
 
 template <int BITS>
 static const void *gather_sym(int R, int NB) {
-    constexpr int RS = plan_rows(1, 8, false), RD = plan_rows(1, 8, true);
-    constexpr int NS = plan_stages(false), ND = plan_stages(true);
-    if (R == RS && NB == NS) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, RS, NS>);
-    if (R == RD && NB == ND) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, RD, ND>);
+    constexpr int R8 = plan_rows(1, 8, false), N8 = plan_stages(8, false);  // one plan for every walk
+    if (R == R8 && NB == N8) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, R8, N8>);
     return nullptr;
 }
 
