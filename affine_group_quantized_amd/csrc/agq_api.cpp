@@ -72,10 +72,12 @@ agq_status current_device(int *cus, int *ordinal) {
 }
 
 // Blocks of `sym` resident per compute unit, from the HIP occupancy query,
-// cached per kernel and device.
+// cached per kernel, block size, dynamic LDS and device. (One kernel can run
+// with several block sizes: the K split S sets the waves per block.)
 struct OccEntry {
     const void *sym;
     int dev;
+    int threads;
     size_t lds;
     int blocks_per_cu;
 };
@@ -93,14 +95,15 @@ agq_status resident_waves(const void *sym, int threads, size_t lds, int cus, int
     {
         std::lock_guard<std::mutex> lock(g_occ_mu);
         for (int i = 0; i < g_occ_n; ++i)
-            if (g_occ[i].sym == sym && g_occ[i].dev == dev && g_occ[i].lds == lds) bpc = g_occ[i].blocks_per_cu;
+            if (g_occ[i].sym == sym && g_occ[i].dev == dev && g_occ[i].threads == threads && g_occ[i].lds == lds)
+                bpc = g_occ[i].blocks_per_cu;
     }
     if (bpc < 0) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, sym, threads, lds);
         if (e != hipSuccess) return fail(AGQ_EHIP, "occupancy query failed: %s", hipGetErrorString(e));
         if (bpc < 1) bpc = 1;
         std::lock_guard<std::mutex> lock(g_occ_mu);
-        if (g_occ_n < kOccSlots) g_occ[g_occ_n++] = OccEntry{sym, dev, lds, bpc};
+        if (g_occ_n < kOccSlots) g_occ[g_occ_n++] = OccEntry{sym, dev, threads, lds, bpc};
     }
     *waves = (int64_t)cus * bpc * (threads / 64);
     return AGQ_OK;
@@ -150,8 +153,8 @@ agq_status launch_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t expert
     agq_status st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
     for (int pass = 0; pass < 2; ++pass) {
-        *sym = agq::product_kernel(bits, plan->mw, plan->cpt, plan->R, plan->NB, plan->x_lds_bytes > 0,
-                                   experts > 0);
+        *sym = agq::product_kernel(bits, plan->mw, plan->cpt, plan->R, plan->NB,
+                                   plan->x_lds_bytes > 0 ? plan->S : 0, experts > 0);
         if (!*sym)
             return fail(AGQ_ENOTSUP, "no kernel for bits=%d rows=%d cpt=%d R=%d", bits, plan->mw, plan->cpt,
                         plan->R);
@@ -183,6 +186,7 @@ void export_plan(const agq::Plan &p, agq_plan *out) {
     out->blocks = p.blocks;
     out->row_order = AGQ_ROW_ORDER_CONTIGUOUS ? 1 : 0;
     out->x_lds_bytes = p.x_lds_bytes;
+    out->resident_waves = (int32_t)p.resident;
 }
 
 agq::ProductArgs make_args(const void *x, const uint32_t *w, const void *s, const void *b, void *y, int64_t N,

@@ -54,6 +54,10 @@ constexpr int kDeepRows = AGQ_DEEP_ROWS;
 // rows in flight. One plan for short and long walks.
 constexpr int kLoadsWide = AGQ_LOADS_WIDE;
 constexpr int kStagesWide = AGQ_STAGES_WIDE;
+#ifndef AGQ_GATHER_OVERSUB
+#define AGQ_GATHER_OVERSUB 4
+#endif
+constexpr int kGatherOversub = AGQ_GATHER_OVERSUB;  // gather grid: resident groups x this
 #ifndef AGQ_ROW_ORDER_CONTIGUOUS
 #define AGQ_ROW_ORDER_CONTIGUOUS 0  // 0: row groups take R-row slices round-robin; 1: contiguous ranges
 #endif
@@ -81,16 +85,16 @@ constexpr int plan_stages(int mw, bool deep) { return mw > 1 ? kStagesWide : dee
 #define AGQ_XL_DEEP 0  // stage x through LDS for long walks too
 #endif
 #ifndef AGQ_X_LDS_MAX
-#define AGQ_X_LDS_MAX 32768
+#define AGQ_X_LDS_MAX 65536
 #endif
-// Largest activation block staged in LDS (bytes): at most 8 16-byte words per
-// thread of a 256-thread block.
+// Largest activation block staged in LDS (bytes).
 constexpr int kXLdsMax = AGQ_X_LDS_MAX;
 
 struct Plan {
     int bits = 0, C = 0, cpt = 0, mw = 0, R = 0, NB = 0, S = 0, GPB = 0, threads = 0;
     int x_lds_bytes = 0;  // dynamic LDS for x; 0 = waves stage x straight from global memory
     int64_t RPG = 0, TG = 0, blocks = 0;
+    int64_t resident = 0;  // waves of this kernel the device holds at once (grid sizing input)
 };
 
 // Kernel shape: chunks per lane, K split, rows per iteration, block size.
@@ -119,24 +123,32 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
     q.NB = plan_stages(q.mw, deep);
     q.GPB = q.S == 1 ? AGQ_GPB_S1 : (q.S == 2 ? 2 : 1);
     q.threads = 64 * q.S * q.GPB;
-    // The waves of a block share their K columns only when each row group is a
-    // single wave; then one LDS copy of x serves the whole block.
-    const int64_t xbytes = 2 * (int64_t)q.mw * K;
-    // (The kernel copies x with 256 threads holding at most MW*CPT 16-byte words each.)
+    // One LDS copy of x [MW, K] can serve a whole 256-thread block: four
+    // single-wave row groups, or two row groups of two K segments (the kernel
+    // fills it with 256 threads holding at most MW*CPT*S 16-byte words each).
+    // Without it every row group reads x from global memory, which for several
+    // activation rows costs more L2 traffic than the weights themselves.
     // Long walks (the deep plan) amortize each wave's own staging of x over
     // many rows, and skip the block barrier the LDS copy needs.
-    q.x_lds_bytes = (!gather && (AGQ_XL_DEEP || !deep) && q.S == 1 && q.GPB >= 4 && q.mw <= 4 && xbytes <= kXLdsMax) ? (int)xbytes : 0;
+    const int64_t xbytes = 2 * (int64_t)q.mw * K;
+    const bool block256 = (q.S == 1 && q.GPB == 4) || (q.S == 2 && q.GPB == 2);
+    q.x_lds_bytes = (!gather && (AGQ_XL_DEEP || !deep) && block256 && xbytes <= kXLdsMax) ? (int)xbytes : 0;
     *p = q;
     return AGQ_OK;
 }
 
 // Row tiling: one row group per resident wave set, so the whole grid is
-// resident at once (no second, partly empty round of waves). `resident_waves`
+// resident at once (no second, partly empty round of waves), except for the
+// gather (below). `resident_waves`
 // is the number of waves of this kernel the device holds at once (compute
 // units times waves per unit at the kernel's occupancy). For the gather, the
 // grid repeats per expert plane and the budget is shared among the planes.
 inline void plan_grid(int64_t N, int64_t resident_waves, int64_t experts, Plan *q) {
-    int64_t tg_target = resident_waves / q->S / (experts > 0 ? experts : 1);
+    q->resident = resident_waves;
+    // The gather's planes carry different numbers of pairs, so its grid is
+    // oversubscribed: blocks of lightly loaded planes finish early and the
+    // hardware hands their compute units the blocks still waiting.
+    int64_t tg_target = resident_waves * (experts > 0 ? kGatherOversub : 1) / q->S / (experts > 0 ? experts : 1);
     if (tg_target < 1) tg_target = 1;
     // Iterations per group: a multiple of the load ring depth.
     const int64_t step = q->NB;

@@ -354,12 +354,12 @@ __device__ __forceinline__ void finish_rows(float (&acc)[R][MW], const Out &out,
 // Shared core: MW activation rows (xrow[m]) against the weight rows that
 // `walk` visits in one plane; row n of activation row m goes to out(m)[n].
 // `iters` (a multiple of NB) must be equal for every row group of the block
-// when S > 1 or XL (block-wide barriers).
+// when S > 1 or XS > 0 (block-wide barriers).
 //
 // The row loop streams through a ring of NB register buffers: each buffer is
 // refilled with the rows NB iterations ahead as soon as it has been consumed.
 // Rows past the walk read nothing (empty descriptors).
-template <int BITS, int CPT, int MW, int R, int NB, bool XL = false, typename Out>
+template <int BITS, int CPT, int MW, int R, int NB, int XS = 0, typename Out>
 __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &pl, const uint16_t *const *xrow,
                                              const Out &out, const RowWalk &walk, int iters, float *red) {
     const int lane = threadIdx.x & 63;
@@ -390,8 +390,11 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
     // One code path per kernel keeps the compiler's load-wait placement exact.
     // Lanes past the row end read a clamped chunk and stage zeros.
     constexpr int XC = BITS == 4 ? 4 : 2;  // 16-byte words of x per chunk
+    constexpr bool XL = XS > 0;
     const int n16 = XL ? (int)((int64_t)MW * a.K / 8) : 0;
-    constexpr int XW = XL ? (BITS == 4 ? MW * CPT : (MW * CPT + 1) / 2) : 1;
+    // 16-byte words of x per thread of the 256-thread block: MW*K/8/256, at most
+    // MW*CPT*XS for 4-bit codes (K <= 32*64*CPT*XS) and half that for 8-bit.
+    constexpr int XW = XL ? (BITS == 4 ? MW * CPT * XS : (MW * CPT * XS + 1) / 2) : 1;
     u32x4 xr[XW];
     u32x4 xraw[XL ? 1 : MW][XL ? 1 : CPT][XC];
     if constexpr (XL) {
@@ -456,7 +459,7 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
 // LDS slots of the K-split combine: two regions of kSlotFloats per wave.
 constexpr int kRedFloats = 2 * kBlockWaves * kSlotFloats;
 
-template <int BITS, int CPT, int MW, int R, int NB, bool XL>
+template <int BITS, int CPT, int MW, int R, int NB, int XS>
 __global__ __launch_bounds__(512) void qmv_kernel(ProductArgs a) {
     __shared__ float red[kRedFloats];
     const int wave = wave_id();
@@ -465,13 +468,13 @@ __global__ __launch_bounds__(512) void qmv_kernel(ProductArgs a) {
     // A wave without rows may leave only when it meets no block barrier: with
     // S == 1 and x read from global memory. (Otherwise it walks rows past the
     // end, which read nothing and store nothing.)
-    if (a.S == 1 && !XL && walk.first >= walk.end) return;
+    if (a.S == 1 && XS == 0 && walk.first >= walk.end) return;
     const int iters = (int)(a.RPG / R);  // RPG is a multiple of NB*R
     const uint16_t *xrow[MW];
 #pragma unroll
     for (int m = 0; m < MW; ++m) xrow[m] = a.x + (int64_t)m * a.K;
     const Plane pl{a.w, a.s, a.b, a.C, a.G};
-    product_rows<BITS, CPT, MW, R, NB, XL>(a, pl, xrow, DenseOut{a.y, a.N}, walk, iters, red);
+    product_rows<BITS, CPT, MW, R, NB, XS>(a, pl, xrow, DenseOut{a.y, a.N}, walk, iters, red);
 }
 
 // Output rows of a gather pass: its m-th pair p = plist[m] writes y[p, :].
@@ -615,19 +618,18 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict
 // Kernel selection.
 
 template <int BITS, int MW, int CPT, int R, int NB>
-static const void *qmv_sym_xl(bool xl) {
-    // The LDS-staged form exists for MW <= 4 only (x fits the LDS budget then).
-    if constexpr (MW <= 4) {
-        if (xl) return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, NB, true>);
-    } else {
-        if (xl) return nullptr;
+static const void *qmv_sym_xl(int xs) {
+    switch (xs) {
+        case 0: return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, NB, 0>);
+        case 1: return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, NB, 1>);
+        case 2: return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, NB, 2>);
     }
-    return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, R, NB, false>);
+    return nullptr;
 }
 
 // The shallow and the deep plan of each (MW, CPT).
 template <int BITS, int MW, int CPT>
-static const void *qmv_sym(int R, int NB, bool xl) {
+static const void *qmv_sym(int R, int NB, int xl) {
     constexpr int RS = plan_rows(CPT, MW, false), RD = plan_rows(CPT, MW, true);
     constexpr int NS = plan_stages(MW, false), ND = plan_stages(MW, true);
     if (R == RS && NB == NS) return qmv_sym_xl<BITS, MW, CPT, RS, NS>(xl);
@@ -638,7 +640,7 @@ static const void *qmv_sym(int R, int NB, bool xl) {
 }
 
 template <int BITS, int MW>
-static const void *qmv_by_cpt(int cpt, int R, int NB, bool xl) {
+static const void *qmv_by_cpt(int cpt, int R, int NB, int xl) {
     if constexpr (kXRegBudget / MW >= 8) {
         switch (cpt) {
             case 1: return qmv_sym<BITS, MW, 1>(R, NB, xl);
@@ -671,7 +673,7 @@ static const void *qmv_by_cpt(int cpt, int R, int NB, bool xl) {
 }
 
 template <int BITS>
-static const void *qmv_by_mw(int mw, int cpt, int R, int NB, bool xl) {
+static const void *qmv_by_mw(int mw, int cpt, int R, int NB, int xl) {
     switch (mw) {
         case 1: return qmv_by_cpt<BITS, 1>(cpt, R, NB, xl);
         case 2: return qmv_by_cpt<BITS, 2>(cpt, R, NB, xl);
@@ -692,7 +694,7 @@ static const void *gather_sym(int R, int NB) {
     return nullptr;
 }
 
-const void *product_kernel(int bits, int mw, int cpt, int R, int NB, bool x_lds, bool gather) {
+const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather) {
     if (gather) {
         if (cpt != 1 || mw != 8 || x_lds) return nullptr;
         return bits == 4 ? gather_sym<4>(R, NB) : gather_sym<8>(R, NB);

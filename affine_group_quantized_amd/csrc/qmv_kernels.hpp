@@ -30,8 +30,9 @@ struct ProductArgs {
 };
 
 // Kernel symbol for (bits, activation rows per pass, chunks per lane, weight
-// rows per iteration, load ring stages, x staged through LDS), or NULL.
-const void *product_kernel(int bits, int mw, int cpt, int R, int NB, bool x_lds, bool gather);
+// rows per iteration, load ring stages, K segments per row group of a block's
+// LDS copy of x (0: none)), or NULL.
+const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather);
 const void *dequant_kernel_sym(int bits);
 
 }  // namespace agq

@@ -156,7 +156,8 @@ typedef struct agq_plan {
     int32_t x_lds_bytes;     /* LDS per block holding x (0: waves read x from global memory) */
     int32_t stages;          /* depth of each wave's ring of in-flight row loads; rows_per_group is a
                                 multiple of stages x rows_per_iter */
-    int32_t reserved_;
+    int32_t resident_waves;  /* waves of the chosen kernel the device holds at once, at this block size
+                                (agq_plan_product: num_cus x waves_per_cu); the grid is sized from it */
 } agq_plan;
 
 agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group_size,

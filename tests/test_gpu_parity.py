@@ -349,3 +349,21 @@ def test_wide_rows_equal_single_row_results():
     for m in range(3):
         y1 = agq.qmv(bf16_dev(x[m]), w, s, b)
         check_close(y1[cols][None], y_ref[m:m + 1], A[m:m + 1], f"single {m}")
+
+
+def test_launch_plans_size_each_block_size_separately():
+    """One kernel (8 activation rows, one chunk per lane, x staged per wave) runs with
+    256-thread blocks at K=4096 (2 waves per row group) and 448-thread blocks at K=14336
+    (7 waves per row group). The residency the grid is sized from must be that of the
+    block size in use, whatever was planned before: bigger blocks of the same kernel can
+    never hold more waves."""
+    shapes = {256: (8, 65536, 4096), 448: (8, 4096, 14336)}
+    for order in ((256, 448), (448, 256), (256, 448)):
+        plans = {t: agq.launch_plan(*shapes[t], 4) for t in order}
+        small, big = plans[256], plans[448]
+        for p, threads in ((small, 256), (big, 448)):
+            assert p["threads_per_block"] == threads and p["cpt"] == 1 and p["mw"] == 8
+            assert p["x_lds_bytes"] == 0
+            assert p["resident_waves"] % (threads // 64) == 0
+            assert p["blocks"] * threads // 64 <= p["resident_waves"]  # one round of resident blocks
+        assert big["resident_waves"] <= small["resident_waves"]
