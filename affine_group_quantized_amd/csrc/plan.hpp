@@ -12,7 +12,15 @@ constexpr int kMaxWavesPerGroup = 8;   // kernels are built with __launch_bounds
 #ifndef AGQ_MAX_CPT
 #define AGQ_MAX_CPT 7  // 8 chunks per lane plus two row buffers no longer fit in 256 VGPRs
 #endif
+#ifndef AGQ_PREF_CPT
+// Longer rows split K over more waves rather than holding more chunks per
+// lane, as long as 8 waves cover the row: 4 chunks keep 3 waves per SIMD
+// resident (4096x14336 at batch 1: 8.6 us with 2 waves of 4 chunks against
+// 9.5 us with one wave of 7).
+#define AGQ_PREF_CPT 4
+#endif
 constexpr int kMaxCpt = AGQ_MAX_CPT;   // 16-byte chunks per lane in one wave's K segment
+constexpr int kPrefCpt = AGQ_PREF_CPT;
 constexpr int kXRegBudget = 8;         // CPT * MW <= 8: staged activations use <= 128 VGPRs
 constexpr int kMaxPairs = 4096;        // gather: pair list kept in LDS as uint16
 #ifndef AGQ_WAVES_PER_CU
@@ -110,6 +118,8 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
     q.mw = gather ? 8 : (int)M;
     int cptmax = kXRegBudget / q.mw;
     if (cptmax > kMaxCpt) cptmax = kMaxCpt;
+    // The preferred cap, unless only a larger one keeps S within a block.
+    if (cptmax > kPrefCpt && (q.C + 64 * kPrefCpt - 1) / (64 * kPrefCpt) <= kMaxWavesPerGroup) cptmax = kPrefCpt;
     int need = (q.C + 63) / 64;
     if (need <= cptmax) {
         q.cpt = need;

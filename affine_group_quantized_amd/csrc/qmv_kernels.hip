@@ -647,9 +647,15 @@ static const void *qmv_by_cpt(int cpt, int R, int NB, int xl) {
             case 2: return qmv_sym<BITS, MW, 2>(R, NB, xl);
             case 3: return qmv_sym<BITS, MW, 3>(R, NB, xl);
             case 4: return qmv_sym<BITS, MW, 4>(R, NB, xl);
-            case 5: return qmv_sym<BITS, MW, 5>(R, NB, xl);
-            case 6: return qmv_sym<BITS, MW, 6>(R, NB, xl);
-            case 7: return qmv_sym<BITS, MW, 7>(R, NB, xl);
+            case 5:
+                if constexpr (kMaxCpt >= 5) return qmv_sym<BITS, MW, 5>(R, NB, xl);
+                break;
+            case 6:
+                if constexpr (kMaxCpt >= 6) return qmv_sym<BITS, MW, 6>(R, NB, xl);
+                break;
+            case 7:
+                if constexpr (kMaxCpt >= 7) return qmv_sym<BITS, MW, 7>(R, NB, xl);
+                break;
             case 8:
                 if constexpr (kMaxCpt >= 8) return qmv_sym<BITS, MW, 8>(R, NB, xl);
                 break;
