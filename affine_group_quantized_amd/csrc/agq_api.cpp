@@ -145,7 +145,7 @@ agq_status check_operands(const void *x, const void *w, const void *s, const voi
 // kDeepRows rows per group use the deep-load instantiation.
 agq_status launch_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t experts, agq::Plan *plan,
                        const void **sym) {
-    const int64_t rows = experts > 0 ? 8 : M;
+    const int64_t rows = experts > 0 ? agq::kGatherMW : M;
     if (agq::plan_shape(rows, K, bits, experts, plan) != AGQ_OK)
         return fail(AGQ_ENOTSUP, "K=%lld too large for %lld activation rows at %d bits", (long long)K,
                     (long long)rows, bits);
@@ -319,7 +319,8 @@ agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group
     if (experts == 0 && M > 8) return fail(AGQ_ENOTSUP, "M > 8");
     if (num_cus <= 0 || waves_per_cu <= 0) return fail(AGQ_EINVAL, "num_cus and waves_per_cu must be positive");
     agq::Plan p;
-    if (agq::make_plan(experts ? 8 : M, N, K, bits, (int64_t)num_cus * waves_per_cu, experts, &p) != AGQ_OK)
+    if (agq::make_plan(experts ? agq::kGatherMW : M, N, K, bits, (int64_t)num_cus * waves_per_cu, experts, &p) !=
+        AGQ_OK)
         return fail(AGQ_ENOTSUP, "K too large");
     export_plan(p, out);
     return AGQ_OK;

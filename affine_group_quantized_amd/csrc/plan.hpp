@@ -62,6 +62,19 @@ constexpr int kDeepRows = AGQ_DEEP_ROWS;
 // rows in flight. One plan for short and long walks.
 constexpr int kLoadsWide = AGQ_LOADS_WIDE;
 constexpr int kStagesWide = AGQ_STAGES_WIDE;
+#ifndef AGQ_GATHER_MW
+// Pairs per pass of the gather. Planes with more pairs take several passes,
+// each reading the plane again; fewer pairs per pass keep x in fewer VGPRs
+// and more waves resident. On the Mixtral-shaped workload (2 to 8 pairs per
+// plane) passes of 8 win: 86.5 + 96.2 us for W1 + W2 against 88.1 + 99.8 us
+// with passes of 4.
+#define AGQ_GATHER_MW 8
+#endif
+constexpr int kGatherMW = AGQ_GATHER_MW;
+#ifndef AGQ_GATHER_XREG
+#define AGQ_GATHER_XREG 8  // gather: CPT * MW <= this (16 VGPRs of staged activations per unit)
+#endif
+constexpr int kGatherXReg = AGQ_GATHER_XREG;
 #ifndef AGQ_GATHER_OVERSUB
 #define AGQ_GATHER_OVERSUB 4
 #endif
@@ -115,8 +128,9 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
     Plan q;
     q.bits = bits;
     q.C = (int)(K * bits / 128);
-    q.mw = gather ? 8 : (int)M;
-    int cptmax = kXRegBudget / q.mw;
+    q.mw = gather ? kGatherMW : (int)M;
+    int cptmax = (gather ? kGatherXReg : kXRegBudget) / q.mw;
+    if (cptmax < 1) cptmax = 1;
     if (cptmax > kMaxCpt) cptmax = kMaxCpt;
     // The preferred cap, unless only a larger one keeps S within a block.
     if (cptmax > kPrefCpt && (q.C + 64 * kPrefCpt - 1) / (64 * kPrefCpt) <= kMaxWavesPerGroup) cptmax = kPrefCpt;

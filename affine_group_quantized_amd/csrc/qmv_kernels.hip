@@ -489,7 +489,7 @@ struct GatherOut {
 // widest passes (register pressure). Any R partitions the same rows exactly once.
 constexpr int gather_rows(int me, int r) { return me > 4 ? 1 : r; }
 
-template <int BITS, int ME, int R, int NB>
+template <int BITS, int CPT, int ME, int R, int NB>
 __device__ __forceinline__ void gather_pass(const ProductArgs &a, const Plane &pl, const uint16_t *plist, int base,
                                             int64_t rg, int64_t groups, float *red) {
     constexpr int RR = gather_rows(ME, R);
@@ -502,7 +502,7 @@ __device__ __forceinline__ void gather_pass(const ProductArgs &a, const Plane &p
         xrow[m] = a.x + xr * a.K;
     }
     // RPG is a multiple of NB*R, so RPG / RR is a multiple of NB.
-    product_rows<BITS, 1, ME, RR, NB>(a, pl, xrow, GatherOut{a.y, a.N, plist + base}, walk, (int)(a.RPG / RR), red);
+    product_rows<BITS, CPT, ME, RR, NB>(a, pl, xrow, GatherOut{a.y, a.N, plist + base}, walk, (int)(a.RPG / RR), red);
 }
 
 // Compact (ascending) the pairs p < P that satisfy `pred` into list[]; wave 0 only.
@@ -522,8 +522,8 @@ __device__ __forceinline__ int compact_pairs(int P, uint16_t *list, Pred pred) {
 
 // blockIdx.y = expert plane e; blockIdx.x = row tile. Pairs routed to e are
 // grouped in LDS, so each used plane streams from memory once per pass of up
-// to 8 pairs. A block whose expert has no pairs exits before reading weights.
-template <int BITS, int R, int NB>
+// to kGatherMW pairs. A block whose expert has no pairs exits before reading weights.
+template <int BITS, int CPT, int R, int NB>
 __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
     __shared__ float red[kRedFloats];
     __shared__ uint16_t plist[kMaxPairs];
@@ -574,17 +574,23 @@ __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
     if (count == 0) return;
     if (a.S == 1 && walk.first >= walk.end) return;
     const Plane pl{a.w + (int64_t)e * a.N * a.C, a.s + (int64_t)e * a.N * a.G, a.b + (int64_t)e * a.N * a.G, a.C, a.G};
-    for (int base = 0; base < count; base += 8) {
-        const int me = count - base < 8 ? count - base : 8;
+    for (int base = 0; base < count; base += kGatherMW) {
+        const int me = count - base < kGatherMW ? count - base : kGatherMW;
         switch (me) {
-            case 1: gather_pass<BITS, 1, R, NB>(a, pl, plist, base, rg, groups, red); break;
-            case 2: gather_pass<BITS, 2, R, NB>(a, pl, plist, base, rg, groups, red); break;
-            case 3: gather_pass<BITS, 3, R, NB>(a, pl, plist, base, rg, groups, red); break;
-            case 4: gather_pass<BITS, 4, R, NB>(a, pl, plist, base, rg, groups, red); break;
-            case 5: gather_pass<BITS, 5, R, NB>(a, pl, plist, base, rg, groups, red); break;
-            case 6: gather_pass<BITS, 6, R, NB>(a, pl, plist, base, rg, groups, red); break;
-            case 7: gather_pass<BITS, 7, R, NB>(a, pl, plist, base, rg, groups, red); break;
-            default: gather_pass<BITS, 8, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 1: gather_pass<BITS, CPT, 1, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 2: gather_pass<BITS, CPT, 2, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 3: gather_pass<BITS, CPT, 3, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 4: gather_pass<BITS, CPT, 4, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            default:
+                if constexpr (kGatherMW > 4) {
+                    switch (me) {
+                        case 5: gather_pass<BITS, CPT, 5, R, NB>(a, pl, plist, base, rg, groups, red); break;
+                        case 6: gather_pass<BITS, CPT, 6, R, NB>(a, pl, plist, base, rg, groups, red); break;
+                        case 7: gather_pass<BITS, CPT, 7, R, NB>(a, pl, plist, base, rg, groups, red); break;
+                        default: gather_pass<BITS, CPT, 8, R, NB>(a, pl, plist, base, rg, groups, red); break;
+                    }
+                }
+                break;
         }
     }
 }
@@ -693,17 +699,28 @@ static const void *qmv_by_mw(int mw, int cpt, int R, int NB, int xl) {
     return nullptr;
 }
 
+template <int BITS, int CPT>
+static const void *gather_sym_cpt(int R, int NB) {
+    constexpr int RG = plan_rows(CPT, kGatherMW, false), NG = plan_stages(kGatherMW, false);  // one plan for every walk
+    if (R == RG && NB == NG) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, CPT, RG, NG>);
+    return nullptr;
+}
+
 template <int BITS>
-static const void *gather_sym(int R, int NB) {
-    constexpr int R8 = plan_rows(1, 8, false), N8 = plan_stages(8, false);  // one plan for every walk
-    if (R == R8 && NB == N8) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, R8, N8>);
+static const void *gather_sym(int cpt, int R, int NB) {
+    switch (cpt) {
+        case 1: return gather_sym_cpt<BITS, 1>(R, NB);
+        case 2:
+            if constexpr (kGatherXReg / kGatherMW >= 2) return gather_sym_cpt<BITS, 2>(R, NB);
+            break;
+    }
     return nullptr;
 }
 
 const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather) {
     if (gather) {
-        if (cpt != 1 || mw != 8 || x_lds) return nullptr;
-        return bits == 4 ? gather_sym<4>(R, NB) : gather_sym<8>(R, NB);
+        if (mw != kGatherMW || x_lds) return nullptr;
+        return bits == 4 ? gather_sym<4>(cpt, R, NB) : gather_sym<8>(cpt, R, NB);
     }
     return bits == 4 ? qmv_by_mw<4>(mw, cpt, R, NB, x_lds) : qmv_by_mw<8>(mw, cpt, R, NB, x_lds);
 }

@@ -150,6 +150,6 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
         assert rows.size == N and np.array_equal(np.sort(rows), np.arange(N))   # each row exactly once
     assert p["rows_per_iter"] * p["mw"] <= 16
     if experts:
-        assert p["mw"] == 8 and p["cpt"] == 1
+        assert p["mw"] == 8 and p["cpt"] == 1   # passes of up to 8 pairs, one chunk per lane
     else:
         assert p["mw"] == M
