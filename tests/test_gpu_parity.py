@@ -367,3 +367,95 @@ def test_launch_plans_size_each_block_size_separately():
             assert p["resident_waves"] % (threads // 64) == 0
             assert p["blocks"] * threads // 64 <= p["resident_waves"]  # one round of resident blocks
         assert big["resident_waves"] <= small["resident_waves"]
+
+
+def test_graph_replays_match_eager():
+    """The three products captured in one HIP graph: every replay, with eager work and
+    synchronizations in between, reproduces the eager outputs bit for bit."""
+    N, K, E, P = 1500, 4096, 3, 5
+    d = si.draw_quantized_weight(17, 1, N, K, 4)
+    planes = [si.draw_quantized_weight(17, 2 + e, N, K, 4) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(17, 9, 4, K)
+    w, s, b = dev_weight(d)
+    ws, ss, bs = u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"])
+    xd = bf16_dev(x)
+    rhs = u32_dev(np.array([2, 0, 2, 1, 0], np.uint32))
+    lhs = u32_dev(np.array([0, 3, 1, 1, 2], np.uint32))
+    y1 = torch.empty(N, dtype=torch.bfloat16, device="cuda")
+    y4 = torch.empty((4, N), dtype=torch.bfloat16, device="cuda")
+    yg = torch.empty((P, N), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        agq.qmv(xd[0], w, s, b, out=y1)
+        agq.qmv_wide(xd, w, s, b, out=y4)
+        agq.gather_qmv(xd, ws, ss, bs, rhs_indices=rhs, lhs_indices=lhs, out=yg)
+
+    progress("graph capture of qmv, qmv_wide, gather_qmv")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        run()  # eager, also primes the launch-plan caches outside capture
+    torch.cuda.synchronize()
+    eager = [bf16_bits_host(t).copy() for t in (y1, y4, yg)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (y1, y4, yg):
+            t.zero_()
+        agq.qmv(xd[1], w, s, b)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((y1, y4, yg), eager):
+            assert np.array_equal(bf16_bits_host(got), want), f"replay {rep}"
+    y_ref, A = oracle.qmv(x[:1], d["w"], d["scales"], d["biases"], K, 4, rows=np.arange(0, N, 11))
+    check_close(y1[None][:, torch.arange(0, N, 11, device="cuda")], y_ref, A, "graph qmv")
+
+
+def test_gather_at_the_pair_limit():
+    """4096 pairs (the most one call takes) over 3 planes, with repeated x rows."""
+    E, N, K, R, P = 3, 96, 128, 64, 4096
+    planes = [si.draw_quantized_weight(18, e, N, K, 4) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(18, 99, R, K)
+    rng = np.random.default_rng([18, 1])
+    lhs = rng.integers(0, R, P).astype(np.uint32)
+    rhs = rng.integers(0, E, P).astype(np.uint32)
+    progress("gather with 4096 pairs")
+    y = agq.gather_qmv(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs))
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, 4)
+    check_close(y, y_ref, A, "gather 4096 pairs")
+
+
+def test_calls_on_a_side_stream():
+    """Work is queued on the stream handed in (or current at preparation), not the null stream."""
+    N, K = 777, 2048
+    d = si.draw_quantized_weight(19, 1, N, K, 8)
+    w, s, b = dev_weight(d)
+    x = si.draw_activations(19, 2, 2, K)
+    xd = bf16_dev(x)
+    y = torch.empty((2, N), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    call = agq.prepare_qmv(xd, w, s, b, y, bits=8, stream=side)
+    progress("prepared qmv_wide on a side stream")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        y.fill_(float("nan"))
+        call()
+    side.synchronize()
+    y_ref, A = oracle.qmv(x, d["w"], d["scales"], d["biases"], K, 8)
+    check_close(y, y_ref, A, "side stream")
+
+
+@pytest.mark.parametrize("bits,M,K", [(4, 2, 65536), (8, 2, 32768), (4, 8, 16384)])
+def test_k_limits_of_the_wide_form(bits, M, K):
+    """The largest K per M: eight waves split each row."""
+    p = agq.plan(M, 5, K, bits, 64, 256, 0)
+    assert p["waves_per_group"] == 8 or M == 8
+    d = si.draw_quantized_weight(20, 100 * bits + M, 5, K, bits)
+    x = si.draw_activations(20, M, M, K)
+    run_qmv_case(f"K limit M={M} bits={bits}", x, d, K, bits, M=M)
