@@ -153,3 +153,21 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
         assert p["mw"] == 8 and p["cpt"] == 1   # passes of up to 8 pairs, one chunk per lane
     else:
         assert p["mw"] == M
+
+
+def test_plain_c_client_builds_and_runs(tmp_path):
+    """The header compiles as C99 with warnings as errors, a C program links against
+    the library, and its host-only calls behave as from Python."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(ROOT, "tests", "c", "abi_client.c")
+    lib_dir = os.path.dirname(agq.LIB_PATH)
+    exe = str(tmp_path / "abi_client")
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    src, "-L", lib_dir, "-lagq", f"-Wl,-rpath,{lib_dir}", "-o", exe], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "failures 0" in out.stdout
