@@ -102,6 +102,9 @@ constexpr int plan_stages(int mw, bool deep) { return mw > 1 ? kStagesWide : dee
 #ifndef AGQ_GPB_S1
 #define AGQ_GPB_S1 4  // row groups (waves) per block when one wave covers a row
 #endif
+#ifndef AGQ_GPB_S2
+#define AGQ_GPB_S2 4  // row groups per block when two waves split a row (one LDS copy of x for 8 waves)
+#endif
 #ifndef AGQ_XL_DEEP
 #define AGQ_XL_DEEP 0  // stage x through LDS for long walks too
 #endif
@@ -145,18 +148,19 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
     }
     q.R = plan_rows(q.cpt, q.mw, deep);
     q.NB = plan_stages(q.mw, deep);
-    q.GPB = q.S == 1 ? AGQ_GPB_S1 : (q.S == 2 ? 2 : 1);
+    q.GPB = q.S == 1 ? AGQ_GPB_S1 : (q.S == 2 ? AGQ_GPB_S2 : 1);
     q.threads = 64 * q.S * q.GPB;
-    // One LDS copy of x [MW, K] can serve a whole 256-thread block: four
-    // single-wave row groups, or two row groups of two K segments (the kernel
-    // fills it with 256 threads holding at most MW*CPT*S 16-byte words each).
+    // One LDS copy of x [MW, K] can serve a whole block of single-wave row
+    // groups, or of row groups of two K segments (the kernel fills it with the
+    // block's threads, at most MW*CPT*S 16-byte words each for 256 threads).
     // Without it every row group reads x from global memory, which for several
     // activation rows costs more L2 traffic than the weights themselves.
     // Long walks (the deep plan) amortize each wave's own staging of x over
     // many rows, and skip the block barrier the LDS copy needs.
     const int64_t xbytes = 2 * (int64_t)q.mw * K;
-    const bool block256 = (q.S == 1 && q.GPB == 4) || (q.S == 2 && q.GPB == 2);
-    q.x_lds_bytes = (!gather && (AGQ_XL_DEEP || !deep) && block256 && xbytes <= kXLdsMax) ? (int)xbytes : 0;
+    // (At least 256 threads: the fill's per-thread share is sized for 256.)
+    const bool shared = (q.S == 1 && q.GPB >= 4) || (q.S == 2 && q.GPB >= 2);
+    q.x_lds_bytes = (!gather && (AGQ_XL_DEEP || !deep) && shared && xbytes <= kXLdsMax) ? (int)xbytes : 0;
     *p = q;
     return AGQ_OK;
 }
