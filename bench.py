@@ -265,8 +265,9 @@ def main():
         by_kernel.setdefault(kern(plans[n]), []).append(n)
     dom_key = max(by_kernel, key=lambda k: sum(algo_bytes(mats[n]["N"], mats[n]["K"], 4) for n in by_kernel[k]))
     dom = set(by_kernel[dom_key])
-    dom_xl = "true" if plans[sorted(dom)[0]]["x_lds_bytes"] else "false"
-    dom_name = "qmv_kernel<4, %d, %d, %d, %d, %s>" % (dom_key[0], dom_key[1], dom_key[2], dom_key[3], dom_xl)
+    p0 = plans[sorted(dom)[0]]
+    dom_xs = p0["waves_per_group"] if p0["x_lds_bytes"] else 0  # K segments of the block's LDS copy of x
+    dom_name = "qmv_kernel<4, %d, %d, %d, %d, %d>" % (dom_key[0], dom_key[1], dom_key[2], dom_key[3], dom_xs)
 
     stream = torch.cuda.Stream(dev)
     calls = [{name: agq.prepare_qmv(mats[name]["x"], *mats[name]["copies"][r], mats[name]["y"], bits=4,
