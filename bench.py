@@ -259,15 +259,16 @@ def main():
 
     # Kernel instantiation of each product, as the launch planner picks it on this device.
     plans = {n: agq.launch_plan(1, mats[n]["N"], mats[n]["K"], 4) for n in SHAPES}
-    kern = lambda p: (p["cpt"], p["mw"], p["rows_per_iter"], p["stages"])  # noqa: E731
+    kern = lambda p: (p["cpt"], p["mw"], p["rows_per_iter"], p["stages"],  # noqa: E731
+                      p["waves_per_group"] if p["x_lds_bytes"] else 0)
     by_kernel = {}
     for n in SHAPES:
         by_kernel.setdefault(kern(plans[n]), []).append(n)
     dom_key = max(by_kernel, key=lambda k: sum(algo_bytes(mats[n]["N"], mats[n]["K"], 4) for n in by_kernel[k]))
     dom = set(by_kernel[dom_key])
-    p0 = plans[sorted(dom)[0]]
-    dom_xs = p0["waves_per_group"] if p0["x_lds_bytes"] else 0  # K segments of the block's LDS copy of x
-    dom_name = "qmv_kernel<4, %d, %d, %d, %d, %d>" % (dom_key[0], dom_key[1], dom_key[2], dom_key[3], dom_xs)
+    # Template arguments: bits, chunks per lane, activation rows, rows per iteration, ring
+    # stages, K segments of the block's LDS copy of x (0: none).
+    dom_name = "qmv_kernel<4, %d, %d, %d, %d, %d>" % dom_key
 
     stream = torch.cuda.Stream(dev)
     calls = [{name: agq.prepare_qmv(mats[name]["x"], *mats[name]["copies"][r], mats[name]["y"], bits=4,
