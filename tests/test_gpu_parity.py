@@ -353,11 +353,11 @@ def test_wide_rows_equal_single_row_results():
 
 def test_launch_plans_size_each_block_size_separately():
     """One kernel (8 activation rows, one chunk per lane, x staged per wave) runs with
-    256-thread blocks at K=4096 (2 waves per row group) and 448-thread blocks at K=14336
-    (7 waves per row group). The residency the grid is sized from must be that of the
-    block size in use, whatever was planned before: bigger blocks of the same kernel can
-    never hold more waves."""
-    shapes = {256: (8, 65536, 4096), 448: (8, 4096, 14336)}
+    256-thread blocks at K=2048 (four single-wave row groups, two blocks per compute
+    unit) and 448-thread blocks at K=14336 (one row group of 7 waves, one block). The
+    residency the grid is sized from must be that of the block size in use, whatever was
+    planned before: bigger blocks of the same kernel can never hold more waves."""
+    shapes = {256: (8, 65536, 2048), 448: (8, 4096, 14336)}
     for order in ((256, 448), (448, 256), (256, 448)):
         plans = {t: agq.launch_plan(*shapes[t], 4) for t in order}
         small, big = plans[256], plans[448]
