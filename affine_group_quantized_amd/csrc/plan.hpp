@@ -109,10 +109,11 @@ constexpr int plan_stages(int mw, bool deep) { return mw > 1 ? kStagesWide : dee
 #define AGQ_XL_DEEP 0  // stage x through LDS for long walks too
 #endif
 #ifndef AGQ_X_LDS_MAX
-#define AGQ_X_LDS_MAX 65536
+#define AGQ_X_LDS_MAX 81920
 #endif
 // Largest activation block staged in LDS (bytes).
 constexpr int kXLdsMax = AGQ_X_LDS_MAX;
+constexpr int kXLdsPerChunk = 68;
 
 struct Plan {
     int bits = 0, C = 0, cpt = 0, mw = 0, R = 0, NB = 0, S = 0, GPB = 0, threads = 0;
@@ -150,14 +151,15 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
     q.NB = plan_stages(q.mw, deep);
     q.GPB = q.S == 1 ? AGQ_GPB_S1 : (q.S == 2 ? AGQ_GPB_S2 : 1);
     q.threads = 64 * q.S * q.GPB;
-    // One LDS copy of x [MW, K] can serve a whole block of single-wave row
-    // groups, or of row groups of two K segments (the kernel fills it with the
-    // block's threads, at most MW*CPT*S 16-byte words each for 256 threads).
+    // One LDS copy of x, in staging form, can serve a whole block of
+    // single-wave row groups, or of row groups of two K segments.
     // Without it every row group reads x from global memory, which for several
     // activation rows costs more L2 traffic than the weights themselves.
     // Long walks (the deep plan) amortize each wave's own staging of x over
     // many rows, and skip the block barrier the LDS copy needs.
-    const int64_t xbytes = 2 * (int64_t)q.mw * K;
+    // LDS bytes of the copy: per activation row and covered chunk, sixteen
+    // 32-bit staged values and the chunk's sum of x (4-bit and 8-bit alike).
+    const int64_t xbytes = (int64_t)q.mw * 64 * q.cpt * q.S * kXLdsPerChunk;
     // (At least 256 threads: the fill's per-thread share is sized for 256.)
     const bool shared = (q.S == 1 && q.GPB >= 4) || (q.S == 2 && q.GPB >= 2);
     q.x_lds_bytes = (!gather && (AGQ_XL_DEEP || !deep) && shared && xbytes <= kXLdsMax) ? (int)xbytes : 0;

@@ -47,8 +47,8 @@ namespace agq {
 
 
 
-// Dynamic LDS of the dense product kernels: the block's copy of x [M, K] (bf16).
-extern __shared__ u32x4 g_xlds[];  // per buffer: GPB*S*R*MW <= 8 waves * 64 values
+// Dynamic LDS of the dense product kernels: the block's copy of x (XFill).
+extern __shared__ u32x4 g_xlds[];
 
 template <int BITS>
 struct Fmt {
@@ -56,43 +56,64 @@ struct Fmt {
     static constexpr int CPG = 64 / EPC;    // chunks per 64-column group
 };
 
-// Turn one lane's raw activation chunk (4 x 16 B = 32 bf16 for 4-bit codes,
-// 2 x 16 B = 16 bf16 for 8-bit) into its staged form: 4-bit, 16 bfloat16 pairs
-// in the (i, i+4) order of the code pairs of each packed word; 8-bit, 16 fp32.
-// xs receives the chunk's sum of x. `keep` is all ones, or zero for a lane
-// past the end of the row.
+// Activation staging. A lane's slice of one activation row for one chunk is
+// sixteen 32-bit registers:
+//  - 4-bit codes: 32 bf16 values as 16 bfloat16 pairs, in the order of the
+//    code pairs a packed word unpacks to: for each 16-byte word of x
+//    (x0..x7), the pairs (x0,x4), (x1,x5), (x2,x6), (x3,x7);
+//  - 8-bit codes: 16 values widened to fp32;
+// plus the chunk's sum of x: in one running sum when a wave stages from
+// global memory, per 16-byte word and then pairwise in the block's LDS copy.
+// (The two orders can differ only in the last bit of that sum.)
+
+// Stage form of one 16-byte word of x (8 bf16) for 4-bit codes: four pairs.
+__device__ __forceinline__ void pairs_of_word(const u32x4 &q, uint32_t (&o)[4]) {
+    o[0] = byte_perm(q.z, q.x, 0x05040100u);  // (x0, x4)
+    o[1] = byte_perm(q.z, q.x, 0x07060302u);  // (x1, x5)
+    o[2] = byte_perm(q.w, q.y, 0x05040100u);  // (x2, x6)
+    o[3] = byte_perm(q.w, q.y, 0x07060302u);  // (x3, x7)
+}
+
+// Sum of the 8 bf16 values of a 16-byte word, given as any four pairs of it.
+__device__ __forceinline__ float word_sum(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    constexpr uint32_t kOnes = 0x3F803F80u;  // bfloat16 pair (1, 1)
+    return dot2_bf16(d, kOnes, dot2_bf16(c, kOnes, dot2_bf16(b, kOnes, dot2_bf16(a, kOnes, 0.f))));
+}
+
+// Stage one chunk from its raw words (4 x 16 B for 4-bit codes, 2 x 16 B for
+// 8-bit) read from global memory. `keep` is all ones, or zero for a lane past
+// the end of the row.
 template <int BITS>
 __device__ __forceinline__ void stage_from_words(const u32x4 *d, uint32_t keep, uint32_t (&xv)[16], float &xs) {
+    // (Masks and shifts rather than byte permutes, and one running sum: measured
+    // faster here than the permute-and-pairwise form the LDS fill uses.)
+    constexpr uint32_t kOnes = 0x3F803F80u;  // bfloat16 pair (1, 1)
+    float s = 0.f;
     if constexpr (BITS == 4) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const u32x4 q = d[t] & keep;
-            xv[4 * t + 0] = (q.x & 0xFFFFu) | (q.z << 16);
-            xv[4 * t + 1] = (q.x >> 16) | (q.z & 0xFFFF0000u);
-            xv[4 * t + 2] = (q.y & 0xFFFFu) | (q.w << 16);
-            xv[4 * t + 3] = (q.y >> 16) | (q.w & 0xFFFF0000u);
+            xv[4 * t + 0] = (q.x & 0xFFFFu) | (q.z << 16);         // (x0, x4)
+            xv[4 * t + 1] = (q.x >> 16) | (q.z & 0xFFFF0000u);     // (x1, x5)
+            xv[4 * t + 2] = (q.y & 0xFFFFu) | (q.w << 16);         // (x2, x6)
+            xv[4 * t + 3] = (q.y >> 16) | (q.w & 0xFFFF0000u);     // (x3, x7)
         }
-        float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s = dot2_bf16(xv[i], 0x3F803F80u, s);
-        xs = s;
+        for (int i = 0; i < 16; ++i) s = dot2_bf16(xv[i], kOnes, s);
     } else {
-        float s = 0.f;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const u32x4 q = d[t] & keep;
             const uint32_t dw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float lo = bf16_lo(dw[i]), hi = bf16_hi(dw[i]);
-                xv[8 * t + 2 * i] = __float_as_uint(lo);
-                xv[8 * t + 2 * i + 1] = __float_as_uint(hi);
-                s += lo;
-                s += hi;
+                xv[8 * t + 2 * i] = __float_as_uint(bf16_lo(dw[i]));
+                xv[8 * t + 2 * i + 1] = __float_as_uint(bf16_hi(dw[i]));
+                s = dot2_bf16(dw[i], kOnes, s);
             }
         }
-        xs = s;
     }
+    xs = s;
 }
 
 // Raw activation words of chunk `c` (in range) of activation row `xr`, from
@@ -105,48 +126,99 @@ __device__ __forceinline__ void fetch_x_chunk(const uint16_t *__restrict__ xr, i
     for (int t = 0; t < W; ++t) d[t] = p[t];
 }
 
-// The same from the block's LDS copy of x: row m starts at 16-byte word m*K/8.
-template <int BITS>
-__device__ __forceinline__ void stage_x_lds(int64_t row_word, int c, bool valid, uint32_t (&xv)[16], float &xs) {
-    constexpr int W = BITS == 4 ? 4 : 2;
-    const int base = (int)row_word + c * W;
-    u32x4 d[W];
-#pragma unroll
-    for (int t = 0; t < W; ++t) d[t] = g_xlds[base + t];
-    stage_from_words<BITS>(d, valid ? 0xFFFFFFFFu : 0u, xv, xs);
-}
+// The block's LDS copy of x [MW, K], already in staging form. Activation row
+// m, chunk c < CP (CP = 64*CPT*XS, the chunks the block's lanes cover; zero
+// past the row) is four 16-byte words at word (m*CP + c)*4; its sum of x is
+// float (m*CP + c) after the MW*CP*4 words.
+template <int BITS, int MW, int CPT, int XS>
+struct XFill {
+    static constexpr int RAW = BITS == 4 ? 4 : 2;      // raw 16-byte words of x per chunk
+    static constexpr int CP = 64 * CPT * XS;           // chunks per activation row in LDS
+    static constexpr int WORDS = MW * CP * RAW;        // raw words of the padded copy
+    static constexpr int PER = (WORDS + 255) / 256;    // per thread, for blocks of >= 256 threads
+    static constexpr int BYTES = MW * CP * 68;         // LDS bytes
+};
 
-// Block-cooperative copy of the activation rows x[0..M) (contiguous, 16-byte
+__device__ __forceinline__ float *x_lds_sums(int words) { return reinterpret_cast<float *>(g_xlds + words); }
+
+// Block-cooperative copy of the activation rows x[0..MW) (contiguous, 16-byte
 // aligned) into LDS, in two halves. fetch_x issues the global loads into
-// registers; store_x writes them to LDS and ends with a barrier that every
+// registers: thread t takes raw words t, t + blockDim, ... of the padded copy.
+// store_x converts them to staging form, adds each chunk's word sums across
+// the neighbouring lanes that hold them, and ends with a barrier that every
 // wave of the block must reach. Weight loads issued between the two stay in
 // flight: loads retire in order, so waiting for the x registers does not wait
-// for anything issued later. XW bounds the 16-byte words per thread; with one
-// wave per row group and 256 threads it is MW*CPT (4-bit) or MW*CPT/2 (8-bit).
-template <int XW>
-__device__ __forceinline__ void fetch_x(const uint16_t *__restrict__ x, int n16, u32x4 (&xr)[XW]) {
+// for anything issued later.
+template <int BITS, int MW, int CPT, int XS>
+__device__ __forceinline__ void fetch_x(const uint16_t *__restrict__ x, int K, int C,
+                                        u32x4 (&xr)[XFill<BITS, MW, CPT, XS>::PER]) {
+    using F = XFill<BITS, MW, CPT, XS>;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(x);
-    const int per = (n16 + (int)blockDim.x - 1) / (int)blockDim.x;  // block-uniform, <= XW
+    const int per = (F::WORDS + (int)blockDim.x - 1) / (int)blockDim.x;  // block-uniform, <= PER
 #pragma unroll
-    for (int k = 0; k < XW; ++k) {
+    for (int k = 0; k < F::PER; ++k) {
         if (k < per) {  // uniform branch
             const int i = (int)threadIdx.x + k * (int)blockDim.x;
-            xr[k] = src[i < n16 ? i : n16 - 1];
+            const int m = i / (F::CP * F::RAW), c = (i / F::RAW) % F::CP, t = i % F::RAW;
+            const bool ok = i < F::WORDS && c < C;
+            // Words past a row or past the copy read word 0 and are zeroed in store_x.
+            xr[k] = src[ok ? (int64_t)m * (K / 8) + (int64_t)c * F::RAW + t : 0];
         }
     }
 }
 
-template <int XW>
-__device__ __forceinline__ void store_x(int n16, const u32x4 (&xr)[XW]) {
-    const int per = (n16 + (int)blockDim.x - 1) / (int)blockDim.x;
+template <int BITS, int MW, int CPT, int XS>
+__device__ __forceinline__ void store_x(int C, const u32x4 (&xr)[XFill<BITS, MW, CPT, XS>::PER]) {
+    using F = XFill<BITS, MW, CPT, XS>;
+    float *sums = x_lds_sums(MW * F::CP * 4);
+    const int per = (F::WORDS + (int)blockDim.x - 1) / (int)blockDim.x;
 #pragma unroll
-    for (int k = 0; k < XW; ++k) {
-        if (k < per) {
+    for (int k = 0; k < F::PER; ++k) {
+        if (k < per) {  // uniform branch: every lane runs the DPP below
             const int i = (int)threadIdx.x + k * (int)blockDim.x;
-            if (i < n16) g_xlds[i] = xr[k];
+            const int chunk = i / F::RAW, c = chunk % F::CP, t = i % F::RAW;
+            const bool in = i < F::WORDS;
+            const u32x4 q = in && c < C ? xr[k] : u32x4{0u, 0u, 0u, 0u};
+            float p;
+            if constexpr (BITS == 4) {
+                uint32_t o[4];
+                pairs_of_word(q, o);
+                if (in) g_xlds[chunk * 4 + t] = u32x4{o[0], o[1], o[2], o[3]};
+                p = word_sum(o[0], o[1], o[2], o[3]);
+                // The chunk's four words are in four neighbouring lanes (t = lane % 4):
+                // (p0 + p1) + (p2 + p3) in every lane of the quad.
+                p += dpp_f32<0xB1>(p);  // quad_perm [1,0,3,2]
+                p += dpp_f32<0x4E>(p);  // quad_perm [2,3,0,1]
+            } else {
+                if (in) {
+                    g_xlds[chunk * 4 + 2 * t] = u32x4{__float_as_uint(bf16_lo(q.x)), __float_as_uint(bf16_hi(q.x)),
+                                                      __float_as_uint(bf16_lo(q.y)), __float_as_uint(bf16_hi(q.y))};
+                    g_xlds[chunk * 4 + 2 * t + 1] = u32x4{__float_as_uint(bf16_lo(q.z)), __float_as_uint(bf16_hi(q.z)),
+                                                          __float_as_uint(bf16_lo(q.w)), __float_as_uint(bf16_hi(q.w))};
+                }
+                p = word_sum(q.x, q.y, q.z, q.w);
+                p += dpp_f32<0xB1>(p);  // the chunk's two words: lanes 2j, 2j+1
+            }
+            if (in && t == 0) sums[chunk] = p;
         }
     }
     __syncthreads();
+}
+
+// Stage chunk c (< CP) of activation row m from the block's LDS copy.
+template <int BITS, int MW, int CPT, int XS>
+__device__ __forceinline__ void stage_x_lds(int m, int c, uint32_t (&xv)[16], float &xs) {
+    using F = XFill<BITS, MW, CPT, XS>;
+    const int chunk = m * F::CP + c;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const u32x4 d = g_xlds[chunk * 4 + t];
+        xv[4 * t + 0] = d.x;
+        xv[4 * t + 1] = d.y;
+        xv[4 * t + 2] = d.z;
+        xv[4 * t + 3] = d.w;
+    }
+    xs = x_lds_sums(MW * F::CP * 4)[chunk];
 }
 
 // Partial dot product of one chunk with one staged activation slice.
@@ -385,20 +457,17 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
     // then the loads of the other NB-1 ring stages. (Issuing every stage ahead
     // of the staging delays the first stage's data for a wave that cannot
     // start before it.)
-    // XL (compile time): the block copies x into LDS and every wave stages its
-    // slice from there; otherwise each wave reads its slice from global memory.
-    // One code path per kernel keeps the compiler's load-wait placement exact.
-    // Lanes past the row end read a clamped chunk and stage zeros.
+    // XS > 0 (compile time): the block copies x into LDS in staging form and
+    // every wave reads its slice from there; otherwise each wave reads and
+    // stages its slice from global memory. One code path per kernel keeps the
+    // compiler's load-wait placement exact. Lanes past the row end stage zeros.
     constexpr int XC = BITS == 4 ? 4 : 2;  // 16-byte words of x per chunk
     constexpr bool XL = XS > 0;
-    const int n16 = XL ? (int)((int64_t)MW * a.K / 8) : 0;
-    // 16-byte words of x per thread of the 256-thread block: MW*K/8/256, at most
-    // MW*CPT*XS for 4-bit codes (K <= 32*64*CPT*XS) and half that for 8-bit.
-    constexpr int XW = XL ? (BITS == 4 ? MW * CPT * XS : (MW * CPT * XS + 1) / 2) : 1;
-    u32x4 xr[XW];
+    using XF = XFill<BITS, MW, CPT, XS == 0 ? 1 : XS>;
+    u32x4 xr[XL ? XF::PER : 1];
     u32x4 xraw[XL ? 1 : MW][XL ? 1 : CPT][XC];
     if constexpr (XL) {
-        fetch_x(xrow[0], n16, xr);
+        fetch_x<BITS, MW, CPT, XS>(xrow[0], a.K, a.C, xr);
     } else {
 #pragma unroll
         for (int m = 0; m < MW; ++m)
@@ -412,12 +481,11 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
     uint32_t xv[MW][CPT][16];
     float xs[MW][CPT], nxs[MW][CPT];
     if constexpr (XL) {
-        store_x(n16, xr);  // block barrier: every wave of the block gets here
+        store_x<BITS, MW, CPT, XS>(a.C, xr);  // block barrier: every wave of the block gets here
 #pragma unroll
         for (int m = 0; m < MW; ++m)
 #pragma unroll
-            for (int j = 0; j < CPT; ++j)
-                stage_x_lds<BITS>((int64_t)m * a.K / 8, cv[j] ? chunk[j] : a.C - 1, cv[j], xv[m][j], xs[m][j]);
+            for (int j = 0; j < CPT; ++j) stage_x_lds<BITS, MW, CPT, XS>(m, chunk[j], xv[m][j], xs[m][j]);
     } else {
 #pragma unroll
         for (int m = 0; m < MW; ++m)
