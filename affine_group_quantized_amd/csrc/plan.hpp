@@ -44,6 +44,9 @@ constexpr int kMaxPairs = 4096;        // gather: pair list kept in LDS as uint1
 #ifndef AGQ_STAGES_WIDE
 #define AGQ_STAGES_WIDE 2
 #endif
+#ifndef AGQ_STAGES_WIDE1
+#define AGQ_STAGES_WIDE1 4
+#endif
 #ifndef AGQ_DEEP_ROWS
 #define AGQ_DEEP_ROWS 16
 #endif
@@ -62,6 +65,10 @@ constexpr int kDeepRows = AGQ_DEEP_ROWS;
 // rows in flight. One plan for short and long walks.
 constexpr int kLoadsWide = AGQ_LOADS_WIDE;
 constexpr int kStagesWide = AGQ_STAGES_WIDE;
+// Ring depth of the wide form when one wave covers a whole row (S == 1): such
+// waves hold fewer activation registers than the K-split shapes of the same
+// instantiation, and room for more rows in flight.
+constexpr int kStagesWide1 = AGQ_STAGES_WIDE1;
 #ifndef AGQ_GATHER_MW
 // Pairs per pass of the gather. Planes with more pairs take several passes,
 // each reading the plane again; fewer pairs per pass keep x in fewer VGPRs
@@ -92,12 +99,18 @@ constexpr int rows_per_iter(int cpt, int mw, int loads, int stages) {
     return floor_pow2(loads / stages / cpt) < floor_pow2(16 / mw) ? floor_pow2(loads / stages / cpt)
                                                                   : floor_pow2(16 / mw);
 }
-constexpr int plan_rows(int cpt, int mw, bool deep) {
-    return mw > 1  ? rows_per_iter(cpt, mw, kLoadsWide, kStagesWide)
+// Whether the deeper whole-row ring fits the register file: roughly 6 VGPRs
+// per chunk and stage for codes, scales and biases, and 16 per chunk and
+// activation row for x (4 chunks at 2 rows and 4 stages spill).
+constexpr bool wide1_fits(int cpt, int mw) { return cpt * (6 * kStagesWide1 + 16 * mw) <= 200; }
+constexpr int plan_stages(int mw, bool deep, bool whole_row = false, int cpt = 1) {
+    return mw > 1 ? (whole_row && wide1_fits(cpt, mw) ? kStagesWide1 : kStagesWide) : deep ? kStagesDeep : kStagesShallow;
+}
+constexpr int plan_rows(int cpt, int mw, bool deep, bool whole_row = false) {
+    return mw > 1  ? rows_per_iter(cpt, mw, kLoadsWide, plan_stages(mw, deep, whole_row, cpt))
            : deep ? rows_per_iter(cpt, mw, kLoadsDeep, kStagesDeep)
                   : rows_per_iter(cpt, mw, kLoadsShallow, kStagesShallow);
 }
-constexpr int plan_stages(int mw, bool deep) { return mw > 1 ? kStagesWide : deep ? kStagesDeep : kStagesShallow; }
 
 #ifndef AGQ_GPB_S1
 #define AGQ_GPB_S1 4  // row groups (waves) per block when one wave covers a row
@@ -147,8 +160,9 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
         if (q.S > kMaxWavesPerGroup) return AGQ_ENOTSUP;
         q.cpt = (q.C + 64 * q.S - 1) / (64 * q.S);
     }
-    q.R = plan_rows(q.cpt, q.mw, deep);
-    q.NB = plan_stages(q.mw, deep);
+    const bool whole_row = !gather && q.S == 1;
+    q.R = plan_rows(q.cpt, q.mw, deep, whole_row);
+    q.NB = plan_stages(q.mw, deep, whole_row, q.cpt);
     q.GPB = q.S == 1 ? AGQ_GPB_S1 : (q.S == 2 ? AGQ_GPB_S2 : 1);
     q.threads = 64 * q.S * q.GPB;
     // One LDS copy of x, in staging form, can serve a whole block of

@@ -701,14 +701,22 @@ static const void *qmv_sym_xl(int xs) {
     return nullptr;
 }
 
-// The shallow and the deep plan of each (MW, CPT).
+// The shallow and the deep plan of each (MW, CPT), and for several activation
+// rows the plan of waves that cover a whole row (which never split K, so no
+// more than one LDS segment).
 template <int BITS, int MW, int CPT>
 static const void *qmv_sym(int R, int NB, int xl) {
     constexpr int RS = plan_rows(CPT, MW, false), RD = plan_rows(CPT, MW, true);
     constexpr int NS = plan_stages(MW, false), ND = plan_stages(MW, true);
+    constexpr int RW = plan_rows(CPT, MW, false, true), NW = plan_stages(MW, false, true, CPT);
     if (R == RS && NB == NS) return qmv_sym_xl<BITS, MW, CPT, RS, NS>(xl);
     if constexpr (RD != RS || ND != NS) {
         if (R == RD && NB == ND) return qmv_sym_xl<BITS, MW, CPT, RD, ND>(xl);
+    }
+    if constexpr (MW > 1 && (RW != RS || NW != NS)) {
+        if (R == RW && NB == NW && xl <= 1)
+            return xl ? reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, RW, NW, 1>)
+                      : reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, RW, NW, 0>);
     }
     return nullptr;
 }
