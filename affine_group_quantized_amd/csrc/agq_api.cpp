@@ -286,7 +286,8 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
     a.rhs = rhs_indices;
     a.R_x = (int32_t)R;
     a.E = (int32_t)E;
-    return launch(sym, dim3((unsigned)plan.blocks, (unsigned)E), dim3(plan.threads), 0, &a, stream);
+    return launch(sym, dim3((unsigned)plan.blocks, (unsigned)E), dim3(plan.threads), (size_t)plan.x_lds_bytes, &a,
+                  stream);
 }
 
 agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *biases, float *out, int64_t rows,

@@ -174,9 +174,11 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
     // LDS bytes of the copy: per activation row and covered chunk, sixteen
     // 32-bit staged values and the chunk's sum of x (4-bit and 8-bit alike).
     const int64_t xbytes = (int64_t)q.mw * 64 * q.cpt * q.S * kXLdsPerChunk;
-    // (At least 256 threads: the fill's per-thread share is sized for 256.)
-    const bool shared = (q.S == 1 && q.GPB >= 4) || (q.S == 2 && q.GPB >= 2);
-    q.x_lds_bytes = (!gather && (AGQ_XL_DEEP || !deep) && shared && xbytes <= kXLdsMax) ? (int)xbytes : 0;
+    // (At least 256 threads per segment: the fill's per-thread share is sized
+    // for 256*S threads.)
+    const bool shared = (q.S == 1 || q.S == 2) && q.GPB >= 4;
+    // (The gather's passes are short walks whatever the plane's length.)
+    q.x_lds_bytes = ((gather || AGQ_XL_DEEP || !deep) && shared && xbytes <= kXLdsMax) ? (int)xbytes : 0;
     *p = q;
     return AGQ_OK;
 }

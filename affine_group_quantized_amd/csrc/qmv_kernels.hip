@@ -130,18 +130,20 @@ __device__ __forceinline__ void fetch_x_chunk(const uint16_t *__restrict__ xr, i
 // m, chunk c < CP (CP = 64*CPT*XS, the chunks the block's lanes cover; zero
 // past the row) is four 16-byte words at word (m*CP + c)*4; its sum of x is
 // float (m*CP + c) after the MW*CP*4 words.
-template <int BITS, int MW, int CPT, int XS>
+// FT: the fewest threads a block filling the copy has (the registers each
+// thread holds between fetch_x and store_x are sized for it).
+template <int BITS, int MW, int CPT, int XS, int FT = 256>
 struct XFill {
     static constexpr int RAW = BITS == 4 ? 4 : 2;      // raw 16-byte words of x per chunk
     static constexpr int CP = 64 * CPT * XS;           // chunks per activation row in LDS
     static constexpr int WORDS = MW * CP * RAW;        // raw words of the padded copy
-    static constexpr int PER = (WORDS + 255) / 256;    // per thread, for blocks of >= 256 threads
+    static constexpr int PER = (WORDS + FT - 1) / FT;  // per thread
     static constexpr int BYTES = MW * CP * 68;         // LDS bytes
 };
 
 __device__ __forceinline__ float *x_lds_sums(int words) { return reinterpret_cast<float *>(g_xlds + words); }
 
-// Block-cooperative copy of the activation rows x[0..MW) (contiguous, 16-byte
+// Block-cooperative copy of the activation rows rows(0..MW) (each 16-byte
 // aligned) into LDS, in two halves. fetch_x issues the global loads into
 // registers: thread t takes raw words t, t + blockDim, ... of the padded copy.
 // store_x converts them to staging form, adds each chunk's word sums across
@@ -149,11 +151,9 @@ __device__ __forceinline__ float *x_lds_sums(int words) { return reinterpret_cas
 // wave of the block must reach. Weight loads issued between the two stay in
 // flight: loads retire in order, so waiting for the x registers does not wait
 // for anything issued later.
-template <int BITS, int MW, int CPT, int XS>
-__device__ __forceinline__ void fetch_x(const uint16_t *__restrict__ x, int K, int C,
-                                        u32x4 (&xr)[XFill<BITS, MW, CPT, XS>::PER]) {
-    using F = XFill<BITS, MW, CPT, XS>;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(x);
+template <int BITS, int MW, int CPT, int XS, int FT, typename Rows>
+__device__ __forceinline__ void fetch_x(const Rows &rows, int C, u32x4 (&xr)[XFill<BITS, MW, CPT, XS, FT>::PER]) {
+    using F = XFill<BITS, MW, CPT, XS, FT>;
     const int per = (F::WORDS + (int)blockDim.x - 1) / (int)blockDim.x;  // block-uniform, <= PER
 #pragma unroll
     for (int k = 0; k < F::PER; ++k) {
@@ -161,15 +161,16 @@ __device__ __forceinline__ void fetch_x(const uint16_t *__restrict__ x, int K, i
             const int i = (int)threadIdx.x + k * (int)blockDim.x;
             const int m = i / (F::CP * F::RAW), c = (i / F::RAW) % F::CP, t = i % F::RAW;
             const bool ok = i < F::WORDS && c < C;
-            // Words past a row or past the copy read word 0 and are zeroed in store_x.
-            xr[k] = src[ok ? (int64_t)m * (K / 8) + (int64_t)c * F::RAW + t : 0];
+            // Words past a row or past the copy read word 0 of row 0 and are zeroed in store_x.
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(rows(ok ? m : 0));
+            xr[k] = src[ok ? c * F::RAW + t : 0];
         }
     }
 }
 
-template <int BITS, int MW, int CPT, int XS>
-__device__ __forceinline__ void store_x(int C, const u32x4 (&xr)[XFill<BITS, MW, CPT, XS>::PER]) {
-    using F = XFill<BITS, MW, CPT, XS>;
+template <int BITS, int MW, int CPT, int XS, int FT>
+__device__ __forceinline__ void store_x(int C, const u32x4 (&xr)[XFill<BITS, MW, CPT, XS, FT>::PER]) {
+    using F = XFill<BITS, MW, CPT, XS, FT>;
     float *sums = x_lds_sums(MW * F::CP * 4);
     const int per = (F::WORDS + (int)blockDim.x - 1) / (int)blockDim.x;
 #pragma unroll
@@ -336,6 +337,31 @@ __device__ __forceinline__ void compute_rows(const RowBuf<CPT, R> &buf, const ui
 }
 
 // Output rows of the dense products: activation row m writes y[m, :].
+// Activation row m of a dense product: x[m, :]. (fill_threads: the fill
+// registers of the LDS copy are sized for 256-thread blocks whatever the
+// segment count, which measured faster for two segments than sizing them for
+// the 512 threads such blocks have.)
+struct DenseRows {
+    const uint16_t *x;
+    int64_t K;
+    __device__ __forceinline__ const uint16_t *operator()(int m) const { return x + (int64_t)m * K; }
+    template <int XS>
+    static constexpr int fill_threads() { return 256; }
+};
+
+// Activation row m of a gather pass: x[xlist[m], :], with the pass's x rows
+// listed in LDS.
+struct GatherRows {
+    const uint16_t *x;
+    int64_t K;
+    const uint32_t *xlist;
+    __device__ __forceinline__ const uint16_t *operator()(int m) const { return x + (int64_t)xlist[m] * K; }
+    // 256 threads per segment: sized for 256 threads, a two-segment copy of
+    // eight rows spills the gather's registers.
+    template <int XS>
+    static constexpr int fill_threads() { return 256 * XS; }
+};
+
 struct DenseOut {
     uint16_t *y;
     int64_t N;
@@ -423,16 +449,16 @@ __device__ __forceinline__ void finish_rows(float (&acc)[R][MW], const Out &out,
     }
 }
 
-// Shared core: MW activation rows (xrow[m]) against the weight rows that
-// `walk` visits in one plane; row n of activation row m goes to out(m)[n].
+// Shared core: MW activation rows (xrows(m), m < MW) against the weight rows
+// that `walk` visits in one plane; row n of activation row m goes to out(m)[n].
 // `iters` (a multiple of NB) must be equal for every row group of the block
 // when S > 1 or XS > 0 (block-wide barriers).
 //
 // The row loop streams through a ring of NB register buffers: each buffer is
 // refilled with the rows NB iterations ahead as soon as it has been consumed.
 // Rows past the walk read nothing (empty descriptors).
-template <int BITS, int CPT, int MW, int R, int NB, int XS = 0, typename Out>
-__device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &pl, const uint16_t *const *xrow,
+template <int BITS, int CPT, int MW, int R, int NB, int XS, typename Rows, typename Out>
+__device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &pl, const Rows &xrows,
                                              const Out &out, const RowWalk &walk, int iters, float *red) {
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -463,16 +489,19 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
     // compiler's load-wait placement exact. Lanes past the row end stage zeros.
     constexpr int XC = BITS == 4 ? 4 : 2;  // 16-byte words of x per chunk
     constexpr bool XL = XS > 0;
-    using XF = XFill<BITS, MW, CPT, XS == 0 ? 1 : XS>;
+    constexpr int FT = Rows::template fill_threads<XS == 0 ? 1 : XS>();
+    using XF = XFill<BITS, MW, CPT, XS == 0 ? 1 : XS, FT>;
     u32x4 xr[XL ? XF::PER : 1];
     u32x4 xraw[XL ? 1 : MW][XL ? 1 : CPT][XC];
     if constexpr (XL) {
-        fetch_x<BITS, MW, CPT, XS>(xrow[0], a.K, a.C, xr);
+        fetch_x<BITS, MW, CPT, XS, FT>(xrows, a.C, xr);
     } else {
 #pragma unroll
-        for (int m = 0; m < MW; ++m)
+        for (int m = 0; m < MW; ++m) {
+            const uint16_t *xm = xrows(m);
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) fetch_x_chunk<BITS>(xrow[m], cv[j] ? chunk[j] : a.C - 1, xraw[m][j]);
+            for (int j = 0; j < CPT; ++j) fetch_x_chunk<BITS>(xm, cv[j] ? chunk[j] : a.C - 1, xraw[m][j]);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     load_rows<CPT, R>(buf[0], pl, walk.at(0), walk.end, woff, goff);
@@ -481,7 +510,7 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
     uint32_t xv[MW][CPT][16];
     float xs[MW][CPT], nxs[MW][CPT];
     if constexpr (XL) {
-        store_x<BITS, MW, CPT, XS>(a.C, xr);  // block barrier: every wave of the block gets here
+        store_x<BITS, MW, CPT, XS, FT>(a.C, xr);  // block barrier: every wave of the block gets here
 #pragma unroll
         for (int m = 0; m < MW; ++m)
 #pragma unroll
@@ -538,11 +567,8 @@ __global__ __launch_bounds__(512) void qmv_kernel(ProductArgs a) {
     // end, which read nothing and store nothing.)
     if (a.S == 1 && XS == 0 && walk.first >= walk.end) return;
     const int iters = (int)(a.RPG / R);  // RPG is a multiple of NB*R
-    const uint16_t *xrow[MW];
-#pragma unroll
-    for (int m = 0; m < MW; ++m) xrow[m] = a.x + (int64_t)m * a.K;
     const Plane pl{a.w, a.s, a.b, a.C, a.G};
-    product_rows<BITS, CPT, MW, R, NB, XS>(a, pl, xrow, DenseOut{a.y, a.N}, walk, iters, red);
+    product_rows<BITS, CPT, MW, R, NB, XS>(a, pl, DenseRows{a.x, a.K}, DenseOut{a.y, a.N}, walk, iters, red);
 }
 
 // Output rows of a gather pass: its m-th pair p = plist[m] writes y[p, :].
@@ -557,20 +583,17 @@ struct GatherOut {
 // widest passes (register pressure). Any R partitions the same rows exactly once.
 constexpr int gather_rows(int me, int r) { return me > 4 ? 1 : r; }
 
-template <int BITS, int CPT, int ME, int R, int NB>
-__device__ __forceinline__ void gather_pass(const ProductArgs &a, const Plane &pl, const uint16_t *plist, int base,
-                                            int64_t rg, int64_t groups, float *red) {
+template <int BITS, int CPT, int ME, int R, int NB, int XS>
+__device__ __forceinline__ void gather_pass(const ProductArgs &a, const Plane &pl, const uint16_t *plist,
+                                            const uint32_t *xlist, int base, int64_t rg, int64_t groups, float *red) {
     constexpr int RR = gather_rows(ME, R);
     const RowWalk walk = row_walk<RR>(a, rg, groups);
-    const uint16_t *xrow[ME];
-#pragma unroll
-    for (int m = 0; m < ME; ++m) {
-        const int p = plist[base + m];
-        const int64_t xr = a.lhs ? (int64_t)a.lhs[p] : (int64_t)p;
-        xrow[m] = a.x + xr * a.K;
-    }
     // RPG is a multiple of NB*R, so RPG / RR is a multiple of NB.
-    product_rows<BITS, CPT, ME, RR, NB>(a, pl, xrow, GatherOut{a.y, a.N, plist + base}, walk, (int)(a.RPG / RR), red);
+    product_rows<BITS, CPT, ME, RR, NB, XS>(a, pl, GatherRows{a.x, a.K, xlist + base},
+                                            GatherOut{a.y, a.N, plist + base}, walk, (int)(a.RPG / RR), red);
+    // The next pass refills the block's LDS copy of x. (With S > 1 the block
+    // has already met at the end of product_rows.)
+    if (XS > 0 && a.S == 1) __syncthreads();
 }
 
 // Compact (ascending) the pairs p < P that satisfy `pred` into list[]; wave 0 only.
@@ -591,10 +614,11 @@ __device__ __forceinline__ int compact_pairs(int P, uint16_t *list, Pred pred) {
 // blockIdx.y = expert plane e; blockIdx.x = row tile. Pairs routed to e are
 // grouped in LDS, so each used plane streams from memory once per pass of up
 // to kGatherMW pairs. A block whose expert has no pairs exits before reading weights.
-template <int BITS, int CPT, int R, int NB>
+template <int BITS, int CPT, int R, int NB, int XS>
 __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
     __shared__ float red[kRedFloats];
     __shared__ uint16_t plist[kMaxPairs];
+    __shared__ uint32_t xlist[kMaxPairs];  // x row of each listed pair
     __shared__ int pcount;
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
@@ -635,27 +659,33 @@ __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
             const uint32_t ex = rhs ? rhs[p] : (uint32_t)p;
             return ex == e && xr < nx;
         });
+        // (LDS accesses of one wave complete in order: plist is written above.)
+        for (int i = lane; i < c; i += 64) {
+            const int p = plist[i];
+            xlist[i] = lhs ? lhs[p] : (uint32_t)p;
+        }
         if (lane == 0) pcount = c;
     }
     __syncthreads();
     const int count = pcount;
     if (count == 0) return;
-    if (a.S == 1 && walk.first >= walk.end) return;
+    // Waves without rows leave only where they meet no block barrier.
+    if (a.S == 1 && XS == 0 && walk.first >= walk.end) return;
     const Plane pl{a.w + (int64_t)e * a.N * a.C, a.s + (int64_t)e * a.N * a.G, a.b + (int64_t)e * a.N * a.G, a.C, a.G};
     for (int base = 0; base < count; base += kGatherMW) {
         const int me = count - base < kGatherMW ? count - base : kGatherMW;
         switch (me) {
-            case 1: gather_pass<BITS, CPT, 1, R, NB>(a, pl, plist, base, rg, groups, red); break;
-            case 2: gather_pass<BITS, CPT, 2, R, NB>(a, pl, plist, base, rg, groups, red); break;
-            case 3: gather_pass<BITS, CPT, 3, R, NB>(a, pl, plist, base, rg, groups, red); break;
-            case 4: gather_pass<BITS, CPT, 4, R, NB>(a, pl, plist, base, rg, groups, red); break;
+            case 1: gather_pass<BITS, CPT, 1, R, NB, XS>(a, pl, plist, xlist, base, rg, groups, red); break;
+            case 2: gather_pass<BITS, CPT, 2, R, NB, XS>(a, pl, plist, xlist, base, rg, groups, red); break;
+            case 3: gather_pass<BITS, CPT, 3, R, NB, XS>(a, pl, plist, xlist, base, rg, groups, red); break;
+            case 4: gather_pass<BITS, CPT, 4, R, NB, XS>(a, pl, plist, xlist, base, rg, groups, red); break;
             default:
                 if constexpr (kGatherMW > 4) {
                     switch (me) {
-                        case 5: gather_pass<BITS, CPT, 5, R, NB>(a, pl, plist, base, rg, groups, red); break;
-                        case 6: gather_pass<BITS, CPT, 6, R, NB>(a, pl, plist, base, rg, groups, red); break;
-                        case 7: gather_pass<BITS, CPT, 7, R, NB>(a, pl, plist, base, rg, groups, red); break;
-                        default: gather_pass<BITS, CPT, 8, R, NB>(a, pl, plist, base, rg, groups, red); break;
+                        case 5: gather_pass<BITS, CPT, 5, R, NB, XS>(a, pl, plist, xlist, base, rg, groups, red); break;
+                        case 6: gather_pass<BITS, CPT, 6, R, NB, XS>(a, pl, plist, xlist, base, rg, groups, red); break;
+                        case 7: gather_pass<BITS, CPT, 7, R, NB, XS>(a, pl, plist, xlist, base, rg, groups, red); break;
+                        default: gather_pass<BITS, CPT, 8, R, NB, XS>(a, pl, plist, xlist, base, rg, groups, red); break;
                     }
                 }
                 break;
@@ -776,18 +806,23 @@ static const void *qmv_by_mw(int mw, int cpt, int R, int NB, int xl) {
 }
 
 template <int BITS, int CPT>
-static const void *gather_sym_cpt(int R, int NB) {
+static const void *gather_sym_cpt(int R, int NB, int xs) {
     constexpr int RG = plan_rows(CPT, kGatherMW, false), NG = plan_stages(kGatherMW, false);  // one plan for every walk
-    if (R == RG && NB == NG) return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, CPT, RG, NG>);
+    if (R != RG || NB != NG) return nullptr;
+    switch (xs) {
+        case 0: return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, CPT, RG, NG, 0>);
+        case 1: return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, CPT, RG, NG, 1>);
+        case 2: return reinterpret_cast<const void *>(&gather_qmv_kernel<BITS, CPT, RG, NG, 2>);
+    }
     return nullptr;
 }
 
 template <int BITS>
-static const void *gather_sym(int cpt, int R, int NB) {
+static const void *gather_sym(int cpt, int R, int NB, int xs) {
     switch (cpt) {
-        case 1: return gather_sym_cpt<BITS, 1>(R, NB);
+        case 1: return gather_sym_cpt<BITS, 1>(R, NB, xs);
         case 2:
-            if constexpr (kGatherXReg / kGatherMW >= 2) return gather_sym_cpt<BITS, 2>(R, NB);
+            if constexpr (kGatherXReg / kGatherMW >= 2) return gather_sym_cpt<BITS, 2>(R, NB, xs);
             break;
     }
     return nullptr;
@@ -795,8 +830,8 @@ static const void *gather_sym(int cpt, int R, int NB) {
 
 const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather) {
     if (gather) {
-        if (mw != kGatherMW || x_lds) return nullptr;
-        return bits == 4 ? gather_sym<4>(cpt, R, NB) : gather_sym<8>(cpt, R, NB);
+        if (mw != kGatherMW) return nullptr;
+        return bits == 4 ? gather_sym<4>(cpt, R, NB, x_lds) : gather_sym<8>(cpt, R, NB, x_lds);
     }
     return bits == 4 ? qmv_by_mw<4>(mw, cpt, R, NB, x_lds) : qmv_by_mw<8>(mw, cpt, R, NB, x_lds);
 }

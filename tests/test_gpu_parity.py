@@ -317,6 +317,27 @@ def test_gather_many_pairs_one_expert_and_unused_experts():
     check_close(y, y_ref, A, "gather one expert")
 
 
+def test_gather_passes_through_the_block_copy_of_x():
+    """Several passes per plane (21 pairs on one expert: 8, 8 and 5) through the block's
+    LDS copy of x with two K segments, with repeated and scattered x rows."""
+    E, N, K, R = 3, 1030, 4096, 24
+    plan = agq.launch_plan(8, N, K, 4, experts=E)
+    assert plan["x_lds_bytes"] > 0 and plan["waves_per_group"] == 2
+    planes = [si.draw_quantized_weight(21, e, N, K, 4) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(21, 99, R, K)
+    rng = np.random.default_rng([21, 1])
+    rhs = np.array([1] * 21 + [0] * 5 + [2] * 4, np.uint32)
+    rng.shuffle(rhs)
+    lhs = rng.integers(0, R, len(rhs)).astype(np.uint32)
+    progress("gather, several passes through the LDS copy of x")
+    y = agq.gather_qmv(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs))
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, 4)
+    check_close(y, y_ref, A, "gather passes")
+
+
 def test_gather_out_of_range_indices_give_nan_rows():
     E, N, K, R = 3, 130, 1024, 4
     planes = [si.draw_quantized_weight(15, e, N, K, 8) for e in range(E)]
