@@ -155,6 +155,29 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
         assert p["mw"] == M
 
 
+@pytest.mark.parametrize("M,K,experts,stages", [
+    (2, 4096, 0, 4), (4, 4096, 0, 4), (8, 2048, 0, 4),   # one wave covers a row: four-stage ring
+    (2, 8192, 0, 2),                                     # ... unless its registers would not fit
+    (2, 14336, 0, 2), (8, 4096, 0, 2), (4, 14336, 0, 2), # K split over waves
+    (1, 4096, 0, 2), (8, 2048, 3, 2), (8, 4096, 3, 2),   # batch 1 and the gather
+])
+def test_plan_ring_depth(M, K, experts, stages):
+    p = agq.plan(M, 4096, K, 4, 64, 256, experts, waves_per_cu=8)
+    assert p["stages"] == stages
+    if M > 1 and not experts:
+        assert (p["waves_per_group"] == 1) == (stages == 4 or (M, K) == (2, 8192))
+
+
+@pytest.mark.parametrize("K,bytes_", [(2048, 8 * 64 * 1 * 1 * 68), (4096, 8 * 64 * 1 * 2 * 68), (14336, 0)])
+def test_gather_plan_lds_copy_of_x(K, bytes_):
+    """Gather blocks whose row groups share columns (one or two K segments, four groups)
+    stage each pass's x rows through one LDS copy; seven-segment groups do not."""
+    p = agq.plan(8, 4096, K, 4, 64, 256, 8, waves_per_cu=8)
+    assert p["x_lds_bytes"] == bytes_
+    if bytes_:
+        assert p["groups_per_block"] == 4 and p["threads_per_block"] == 256 * p["waves_per_group"]
+
+
 def test_plain_c_client_builds_and_runs(tmp_path):
     """The header compiles as C99 with warnings as errors, a C program links against
     the library, and its host-only calls behave as from Python."""
