@@ -16,9 +16,12 @@
 //  - A lane's columns are the same for every weight row. Its slice of the
 //    activations is therefore loaded once and kept in VGPRs for the whole
 //    kernel: as bfloat16 pairs (4-bit) or fp32 (8-bit).
-//  - S waves, each owning one K segment, form a row group that walks a
-//    contiguous range of RPG weight rows, R rows per iteration. All loads of
-//    an iteration (R*CPT 16-byte chunks per lane) are issued before any use.
+//  - S waves, each owning one K segment, form a row group that visits RPG
+//    weight rows, R rows per iteration; row groups take R-row slices
+//    round-robin. Each wave streams its rows through a ring of NB register
+//    buffers, refilled NB iterations ahead.
+//  - Where a block's row groups share columns, the block copies x into LDS
+//    once, already in staging form, and the waves read their slices there.
 //  - The R*MW lane partials of an iteration are reduced together: cross-half
 //    swaps (v_permlane32_swap, v_permlane16_swap) fold pairs of them into one
 //    register, then DPP finishes each 16-lane row, about 2.5 VALU ops per
@@ -47,7 +50,7 @@ namespace agq {
 
 
 
-// Dynamic LDS of the dense product kernels: the block's copy of x (XFill).
+// Dynamic LDS of the product kernels: the block's copy of x (XFill).
 extern __shared__ u32x4 g_xlds[];
 
 template <int BITS>
@@ -336,7 +339,6 @@ __device__ __forceinline__ void compute_rows(const RowBuf<CPT, R> &buf, const ui
     }
 }
 
-// Output rows of the dense products: activation row m writes y[m, :].
 // Activation row m of a dense product: x[m, :]. (fill_threads: the fill
 // registers of the LDS copy are sized for 256-thread blocks whatever the
 // segment count, which measured faster for two segments than sizing them for
@@ -362,6 +364,7 @@ struct GatherRows {
     static constexpr int fill_threads() { return 256 * XS; }
 };
 
+// Output rows of the dense products: activation row m writes y[m, :].
 struct DenseOut {
     uint16_t *y;
     int64_t N;
@@ -669,8 +672,11 @@ __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
     __syncthreads();
     const int count = pcount;
     if (count == 0) return;
-    // Waves without rows leave only where they meet no block barrier.
-    if (a.S == 1 && XS == 0 && walk.first >= walk.end) return;
+    // Waves without rows leave only where they meet no block barrier. Passes
+    // walk R or one row per iteration (gather_rows); a group has no rows in
+    // any pass when it has none one row at a time.
+    const RowWalk walk1 = row_walk<1>(a, rg, groups);
+    if (a.S == 1 && XS == 0 && walk1.first >= walk1.end) return;
     const Plane pl{a.w + (int64_t)e * a.N * a.C, a.s + (int64_t)e * a.N * a.G, a.b + (int64_t)e * a.N * a.G, a.C, a.G};
     for (int base = 0; base < count; base += kGatherMW) {
         const int me = count - base < kGatherMW ? count - base : kGatherMW;

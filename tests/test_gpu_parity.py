@@ -338,6 +338,24 @@ def test_gather_passes_through_the_block_copy_of_x():
     check_close(y, y_ref, A, "gather passes")
 
 
+@pytest.mark.parametrize("N", [1, 5, 9])
+def test_gather_tiny_planes_with_wide_passes(N):
+    """Planes of a few rows, single-wave row groups, and passes of more than four pairs
+    (which walk one row per iteration while shorter passes walk two)."""
+    E, K, R = 2, 1024, 8
+    planes = [si.draw_quantized_weight(22, 10 * N + e, N, K, 4) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(22, N, R, K)
+    rhs = np.array([1, 1, 0, 1, 1, 1, 1], np.uint32)
+    lhs = np.array([0, 3, 7, 1, 5, 2, 6], np.uint32)
+    progress(f"gather tiny plane N={N}")
+    y = agq.gather_qmv(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs))
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, 4)
+    check_close(y, y_ref, A, f"gather N={N}")
+
+
 def test_gather_out_of_range_indices_give_nan_rows():
     E, N, K, R = 3, 130, 1024, 4
     planes = [si.draw_quantized_weight(15, e, N, K, 8) for e in range(E)]
