@@ -22,6 +22,14 @@ constexpr int kMaxWavesPerGroup = 8;   // kernels are built with __launch_bounds
 constexpr int kMaxCpt = AGQ_MAX_CPT;   // 16-byte chunks per lane in one wave's K segment
 constexpr int kPrefCpt = AGQ_PREF_CPT;
 constexpr int kXRegBudget = 8;         // CPT * MW <= 8: staged activations use <= 128 VGPRs
+#ifndef AGQ_XREG_WIDE
+#define AGQ_XREG_WIDE 2
+#endif
+// Preferred budget for several activation rows: one chunk per lane at M >= 2,
+// splitting K over more waves (each holding less x, so more of them stay
+// resident), as long as 8 waves cover the row; kXRegBudget past that.
+// 14336x4096 at M = 2 / 4: 9.2 / 12.3 us against 9.8 / 13.1 us with 2 chunks.
+constexpr int kXRegWide = AGQ_XREG_WIDE;
 constexpr int kMaxPairs = 4096;        // gather: pair list kept in LDS as uint16
 #ifndef AGQ_WAVES_PER_CU
 #define AGQ_WAVES_PER_CU 0  // 0: size grids from the kernel's measured occupancy
@@ -46,6 +54,9 @@ constexpr int kMaxPairs = 4096;        // gather: pair list kept in LDS as uint1
 #endif
 #ifndef AGQ_STAGES_WIDE1
 #define AGQ_STAGES_WIDE1 4
+#endif
+#ifndef AGQ_WIDE1_KSPLIT
+#define AGQ_WIDE1_KSPLIT 0  // 1: the deeper ring for K-split wide plans too
 #endif
 #ifndef AGQ_DEEP_ROWS
 #define AGQ_DEEP_ROWS 16
@@ -150,7 +161,9 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
     if (cptmax < 1) cptmax = 1;
     if (cptmax > kMaxCpt) cptmax = kMaxCpt;
     // The preferred cap, unless only a larger one keeps S within a block.
-    if (cptmax > kPrefCpt && (q.C + 64 * kPrefCpt - 1) / (64 * kPrefCpt) <= kMaxWavesPerGroup) cptmax = kPrefCpt;
+    int pref = gather ? cptmax : q.mw > 1 ? kXRegWide / q.mw : kPrefCpt;
+    if (pref < 1) pref = 1;
+    if (cptmax > pref && (q.C + 64 * pref - 1) / (64 * pref) <= kMaxWavesPerGroup) cptmax = pref;
     int need = (q.C + 63) / 64;
     if (need <= cptmax) {
         q.cpt = need;
@@ -160,7 +173,7 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
         if (q.S > kMaxWavesPerGroup) return AGQ_ENOTSUP;
         q.cpt = (q.C + 64 * q.S - 1) / (64 * q.S);
     }
-    const bool whole_row = !gather && q.S == 1;
+    const bool whole_row = !gather && (AGQ_WIDE1_KSPLIT || q.S == 1);
     q.R = plan_rows(q.cpt, q.mw, deep, whole_row);
     q.NB = plan_stages(q.mw, deep, whole_row, q.cpt);
     q.GPB = q.S == 1 ? AGQ_GPB_S1 : (q.S == 2 ? AGQ_GPB_S2 : 1);

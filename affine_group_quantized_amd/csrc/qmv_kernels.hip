@@ -750,9 +750,12 @@ static const void *qmv_sym(int R, int NB, int xl) {
         if (R == RD && NB == ND) return qmv_sym_xl<BITS, MW, CPT, RD, ND>(xl);
     }
     if constexpr (MW > 1 && (RW != RS || NW != NS)) {
-        if (R == RW && NB == NW && xl <= 1)
+        if constexpr (AGQ_WIDE1_KSPLIT) {
+            if (R == RW && NB == NW) return qmv_sym_xl<BITS, MW, CPT, RW, NW>(xl);
+        } else if (R == RW && NB == NW && xl <= 1) {
             return xl ? reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, RW, NW, 1>)
                       : reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, RW, NW, 0>);
+        }
     }
     return nullptr;
 }

@@ -156,16 +156,25 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
 
 
 @pytest.mark.parametrize("M,K,experts,stages", [
-    (2, 4096, 0, 4), (4, 4096, 0, 4), (8, 2048, 0, 4),   # one wave covers a row: four-stage ring
-    (2, 8192, 0, 2),                                     # ... unless its registers would not fit
-    (2, 14336, 0, 2), (8, 4096, 0, 2), (4, 14336, 0, 2), # K split over waves
+    (2, 2048, 0, 4), (4, 1024, 0, 4), (8, 2048, 0, 4),   # one wave covers a row: four-stage ring
+    (2, 4096, 0, 2), (2, 14336, 0, 2), (8, 4096, 0, 2), (4, 14336, 0, 2),  # K split over waves
     (1, 4096, 0, 2), (8, 2048, 3, 2), (8, 4096, 3, 2),   # batch 1 and the gather
 ])
 def test_plan_ring_depth(M, K, experts, stages):
     p = agq.plan(M, 4096, K, 4, 64, 256, experts, waves_per_cu=8)
     assert p["stages"] == stages
     if M > 1 and not experts:
-        assert (p["waves_per_group"] == 1) == (stages == 4 or (M, K) == (2, 8192))
+        assert (p["waves_per_group"] == 1) == (stages == 4)
+
+
+@pytest.mark.parametrize("M,K,cpt,waves", [
+    (2, 4096, 1, 2), (4, 4096, 1, 2), (2, 14336, 1, 7), (2, 16384, 1, 8),  # one chunk while 8 waves cover K
+    (2, 32768, 4, 4), (2, 65536, 4, 8), (4, 32768, 2, 8), (3, 24576, 2, 6),  # past that, up to 8/M chunks
+    (1, 14336, 4, 2), (1, 65536, 4, 8), (1, 114688, 7, 8),                   # batch 1: up to 4, then 7
+])
+def test_plan_chunks_per_lane(M, K, cpt, waves):
+    p = agq.plan(M, 4096, K, 4, 64, 256, 0, waves_per_cu=8)
+    assert (p["cpt"], p["waves_per_group"]) == (cpt, waves)
 
 
 @pytest.mark.parametrize("K,bytes_", [(2048, 8 * 64 * 1 * 1 * 68), (4096, 8 * 64 * 1 * 2 * 68), (14336, 0)])
