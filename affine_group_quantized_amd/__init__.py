@@ -44,7 +44,7 @@ class Plan(ctypes.Structure):
         ("groups_per_block", ctypes.c_int32), ("threads_per_block", ctypes.c_int32),
         ("rows_per_group", ctypes.c_int64), ("row_groups", ctypes.c_int64), ("blocks", ctypes.c_int64),
         ("row_order", ctypes.c_int32), ("x_lds_bytes", ctypes.c_int32), ("stages", ctypes.c_int32),
-        ("resident_waves", ctypes.c_int32),
+        ("resident_waves", ctypes.c_int32), ("engine", ctypes.c_int32),
     ]
 
 

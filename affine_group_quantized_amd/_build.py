@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libagq.so")
 
-SOURCES = ["qmv_kernels.hip", "agq_api.cpp"]
+SOURCES = ["qmv_kernels.hip", "qmv_mfma.hip", "agq_api.cpp"]
 
 # Packed-FP32 instructions are disabled for all device code.
 HIPCC_FLAGS = [

@@ -171,7 +171,64 @@ agq_status launch_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t expert
     return AGQ_OK;
 }
 
+// Matrix-core plan on the current device: the grid is sized from the
+// occupancy of the chosen kernel at its block size.
+agq_status launch_mfma_plan(int64_t M, int64_t N, int64_t K, int64_t experts, agq::MfmaPlan *plan,
+                            const void **sym) {
+    agq::mfma_shape(N, K, experts, plan);
+    if (experts == 0) agq::mfma_x_lds(M, K, plan);
+    int cus = 0, dev = 0;
+    agq_status st = current_device(&cus, &dev);
+    if (st != AGQ_OK) return st;
+    *sym = agq::mfma_kernel(plan->T, experts > 0, plan->x_lds_bytes > 0);
+    if (!*sym) return fail(AGQ_ENOTSUP, "no matrix-core kernel for %d tiles", plan->T);
+    int64_t waves = 0;
+    st = resident_waves(*sym, plan->threads, (size_t)plan->x_lds_bytes, cus, dev, &waves);
+    if (st != AGQ_OK) return st;
+    agq::mfma_grid(waves, experts, plan);
+    return AGQ_OK;
+}
+
+void export_mfma_plan(const agq::MfmaPlan &p, int64_t K, agq_plan *out) {
+    *out = agq_plan{};
+    out->bits = 4;
+    out->chunks_per_row = (int32_t)(K / 32);
+    out->cpt = 0;
+    out->mw = 16;
+    out->rows_per_iter = 16 * p.T;
+    out->stages = agq::kMfmaRing;
+    out->waves_per_group = p.S;
+    out->groups_per_block = 1;
+    out->threads_per_block = p.threads;
+    out->rows_per_group = (int64_t)p.BPG * 16 * p.T;
+    out->row_groups = p.groups;
+    out->blocks = p.groups;
+    out->row_order = 0;
+    out->x_lds_bytes = p.x_lds_bytes;
+    out->resident_waves = (int32_t)p.resident;
+    out->engine = 1;
+}
+
+agq::MfmaArgs make_mfma_args(const void *x, const uint32_t *w, const void *s, const void *b, void *y, int64_t N,
+                             int64_t K, int M, const agq::MfmaPlan &p) {
+    agq::MfmaArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = w;
+    a.s = static_cast<const uint16_t *>(s);
+    a.b = static_cast<const uint16_t *>(b);
+    a.y = static_cast<uint16_t *>(y);
+    a.N = N;
+    a.K = (int32_t)K;
+    a.G = (int32_t)(K / 64);
+    a.M = M;
+    a.S = p.S;
+    a.SPW = p.SPW;
+    a.BPG = p.BPG;
+    return a;
+}
+
 void export_plan(const agq::Plan &p, agq_plan *out) {
+    *out = agq_plan{};
     out->bits = p.bits;
     out->chunks_per_row = p.C;
     out->cpt = p.cpt;
@@ -187,6 +244,7 @@ void export_plan(const agq::Plan &p, agq_plan *out) {
     out->row_order = AGQ_ROW_ORDER_CONTIGUOUS ? 1 : 0;
     out->x_lds_bytes = p.x_lds_bytes;
     out->resident_waves = (int32_t)p.resident;
+    out->engine = 0;
 }
 
 agq::ProductArgs make_args(const void *x, const uint32_t *w, const void *s, const void *b, void *y, int64_t N,
@@ -221,6 +279,14 @@ agq_status dense_product(const void *x, const uint32_t *w, const void *s, const 
     if (st != AGQ_OK) return st;
     if (M <= 0) return fail(AGQ_EINVAL, "M must be positive (got %lld)", (long long)M);
     if (M > 8) return fail(AGQ_ENOTSUP, "M=%lld > 8 is a quantized GEMM, not a matvec", (long long)M);
+    if (agq::mfma_eligible(M, K, bits, 0, M)) {
+        agq::MfmaPlan mp;
+        const void *sym = nullptr;
+        st = launch_mfma_plan(M, N, K, 0, &mp, &sym);
+        if (st != AGQ_OK) return st;
+        agq::MfmaArgs a = make_mfma_args(x, w, s, b, y, N, K, (int)M, mp);
+        return launch(sym, dim3((unsigned)mp.groups), dim3(mp.threads), (size_t)mp.x_lds_bytes, &a, stream);
+    }
     agq::Plan plan;
     if (agq::plan_shape(M, K, bits, 0, &plan) != AGQ_OK)  // host-only check before any HIP call
         return fail(AGQ_ENOTSUP, "K=%lld too large for M=%lld at %d bits", (long long)K, (long long)M, bits);
@@ -275,6 +341,18 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
     if (R > INT32_MAX) return fail(AGQ_EINVAL, "R too large");
     if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
     if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
+    if (agq::mfma_eligible(8, K, bits, E, R)) {
+        agq::MfmaPlan mp;
+        const void *sym = nullptr;
+        st = launch_mfma_plan(8, N, K, E, &mp, &sym);
+        if (st != AGQ_OK) return st;
+        agq::MfmaArgs a = make_mfma_args(x, w, scales, biases, y, N, K, (int)P, mp);
+        a.lhs = lhs_indices;
+        a.rhs = rhs_indices;
+        a.R_x = (int32_t)R;
+        a.E = (int32_t)E;
+        return launch(sym, dim3((unsigned)mp.groups, (unsigned)E), dim3(mp.threads), 0, &a, stream);
+    }
     agq::Plan plan;
     if (agq::plan_shape(8, K, bits, E, &plan) != AGQ_OK)  // host-only check before any HIP call
         return fail(AGQ_ENOTSUP, "K=%lld too large for the gather at %d bits", (long long)K, bits);
@@ -319,6 +397,14 @@ agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group
     if (experts == 0 && M <= 0) return fail(AGQ_EINVAL, "M must be positive");
     if (experts == 0 && M > 8) return fail(AGQ_ENOTSUP, "M > 8");
     if (num_cus <= 0 || waves_per_cu <= 0) return fail(AGQ_EINVAL, "num_cus and waves_per_cu must be positive");
+    if (agq::mfma_eligible(M, K, bits, experts, experts ? 1 : M)) {
+        agq::MfmaPlan mp;
+        agq::mfma_shape(N, K, experts, &mp);
+        if (experts == 0) agq::mfma_x_lds(M, K, &mp);
+        agq::mfma_grid((int64_t)num_cus * waves_per_cu, experts, &mp);
+        export_mfma_plan(mp, K, out);
+        return AGQ_OK;
+    }
     agq::Plan p;
     if (agq::make_plan(experts ? agq::kGatherMW : M, N, K, bits, (int64_t)num_cus * waves_per_cu, experts, &p) !=
         AGQ_OK)
@@ -335,6 +421,14 @@ agq_status agq_plan_launch(int64_t M, int64_t N, int64_t K, int bits, int group_
     if (experts < 0) return fail(AGQ_EINVAL, "experts must be >= 0");
     if (experts == 0 && M <= 0) return fail(AGQ_EINVAL, "M must be positive");
     if (experts == 0 && M > 8) return fail(AGQ_ENOTSUP, "M > 8");
+    if (agq::mfma_eligible(M, K, bits, experts, experts ? 1 : M)) {
+        agq::MfmaPlan mp;
+        const void *sym = nullptr;
+        st = launch_mfma_plan(M, N, K, experts, &mp, &sym);
+        if (st != AGQ_OK) return st;
+        export_mfma_plan(mp, K, out);
+        return AGQ_OK;
+    }
     agq::Plan p;
     const void *sym = nullptr;
     st = launch_plan(M, N, K, bits, experts, &p, &sym);

@@ -227,6 +227,96 @@ inline bool wants_deep(int64_t N, int64_t resident_waves, int S, int64_t experts
     return N >= (int64_t)kDeepRows * groups;
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core plan (4-bit codes, several activation rows, and the gather).
+
+#ifndef AGQ_MFMA_MIN_ROWS
+// Activation rows from which dense 4-bit products use the matrix cores (0:
+// never). Below it the VALU form is as fast or faster: 14336x4096 at M = 2 /
+// 4 / 6 / 8 takes 9.9 / 12.6 / 16.1 / 19.3 us on the VALU and 12.1 / 12.6 /
+// 13.4 / 14.1 us on the matrix cores.
+#define AGQ_MFMA_MIN_ROWS 5
+#endif
+#ifndef AGQ_MFMA_TILES
+#define AGQ_MFMA_TILES 0  // 16-row tiles per band: 1, 2, or 0 to choose from the shape
+#endif
+constexpr int kMfmaMinRows = AGQ_MFMA_MIN_ROWS;
+constexpr int kMfmaRing = 4;       // 128-column segments in flight per wave (one block of scales)
+constexpr int kMfmaMaxWaves = 8;   // waves per block (LDS of the K-split combine is sized for it)
+#ifndef AGQ_MFMA_MAX_S
+#define AGQ_MFMA_MAX_S 4  // smaller blocks pack two or more per compute unit (8: 10-35% slower)
+#endif
+#ifndef AGQ_MFMA_X_LDS_MAX
+#define AGQ_MFMA_X_LDS_MAX 65536  // largest activation block copied to LDS (bytes); 0: never
+#endif
+constexpr int kMfmaXLdsMax = AGQ_MFMA_X_LDS_MAX;
+constexpr int kMfmaXPer = 16;  // 16-byte words of x each thread copies
+constexpr int kMfmaMaxS = AGQ_MFMA_MAX_S;  // most waves splitting K
+
+struct MfmaPlan {
+    int x_lds_bytes = 0;  // LDS copy of x (dense only); 0: waves load their operands from global memory
+    int T = 0;          // 16-row tiles per band
+    int S = 0;          // waves per block, splitting K
+    int SPW = 0;        // 128-column segments per wave
+    int BPG = 0;        // bands per block
+    int64_t bands = 0;  // bands per plane
+    int64_t groups = 0; // blocks per plane
+    int threads = 0;
+    int64_t resident = 0;
+};
+
+// Whether a product runs on the matrix cores: 4-bit codes, K a multiple of
+// 512 (whole blocks of 8 groups, 16-byte aligned scale rows), and several
+// activation rows, or the gather (whose passes take up to 16 pairs). Byte
+// offsets into x are 32-bit: the activation block must stay below 2 GiB.
+inline bool mfma_eligible(int64_t M, int64_t K, int bits, int64_t experts, int64_t x_rows) {
+    if (kMfmaMinRows <= 0 || bits != 4 || K % 512 != 0) return false;
+    if (x_rows * K * 2 + K * 2 >= (int64_t(1) << 31)) return false;
+    return experts > 0 || M >= kMfmaMinRows;
+}
+
+// K split: the most waves (at most 8) that divide the row's 4-segment blocks
+// evenly; bands of two tiles unless that leaves fewer than one band-wave per
+// SIMD of the device.
+inline void mfma_shape(int64_t N, int64_t K, int64_t experts, MfmaPlan *p) {
+    const int nseg = (int)(K / 128), blocks4 = nseg / kMfmaRing;
+    int S = 1;
+    for (int s = kMfmaMaxS; s >= 1; --s)
+        if (blocks4 % s == 0) {
+            S = s;
+            break;
+        }
+    p->S = S;
+    p->SPW = nseg / S;
+    p->threads = 64 * S;
+    int T = AGQ_MFMA_TILES;
+    if (T != 1 && T != 2) {
+        const int64_t planes = experts > 0 ? experts : 1;
+        T = ((N + 31) / 32) * S * planes >= 1024 ? 2 : 1;
+    }
+    p->T = T;
+    p->bands = (N + 16 * T - 1) / (16 * T);
+}
+
+// LDS copy of the activation rows for a dense product when the block's
+// threads can stage it (kMfmaXPer words each) and it fits kMfmaXLdsMax.
+inline void mfma_x_lds(int64_t M, int64_t K, MfmaPlan *p) {
+    const int64_t bytes = M * K * 2;
+    const bool fits = bytes <= kMfmaXLdsMax && (bytes / 16 + p->threads - 1) / p->threads <= kMfmaXPer;
+    p->x_lds_bytes = fits ? (int)(bytes + 16) : 0;
+}
+
+// Blocks per plane: every block resident at once (the gather oversubscribes,
+// as its planes carry different numbers of pairs), each walking BPG bands.
+inline void mfma_grid(int64_t resident_waves, int64_t experts, MfmaPlan *p) {
+    p->resident = resident_waves;
+    int64_t budget = resident_waves * (experts > 0 ? kGatherOversub : 1) / p->S / (experts > 0 ? experts : 1);
+    if (budget < 1) budget = 1;
+    const int64_t bpg = (p->bands + budget - 1) / budget;
+    p->BPG = (int)bpg;
+    p->groups = (p->bands + bpg - 1) / bpg;
+}
+
 inline agq_status make_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t resident_waves, int64_t experts,
                             Plan *p) {
     Plan q;

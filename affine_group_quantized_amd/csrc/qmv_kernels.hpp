@@ -29,10 +29,35 @@ struct ProductArgs {
     int32_t pad_[2];
 };
 
+// Argument block of the matrix-core kernels (4-bit codes, K a multiple of
+// 512): bands of 16*T weight rows, S waves per block splitting K into slices
+// of SPW 128-column segments, each block walking BPG bands round-robin.
+struct MfmaArgs {
+    const uint16_t *x;    // activation rows, bf16 [rows, K]
+    const uint32_t *w;    // packed codes [planes, N, K/8]
+    const uint16_t *s;    // bf16 scales [planes, N, K/64]
+    const uint16_t *b;    // bf16 biases [planes, N, K/64]
+    uint16_t *y;          // bf16 outputs [M or P, N]
+    const uint32_t *lhs;  // gather: x row per pair (NULL = identity)
+    const uint32_t *rhs;  // gather: expert per pair (NULL = identity)
+    int64_t N;            // weight rows per plane
+    int32_t K;            // columns
+    int32_t G;            // 64-column groups per weight row
+    int32_t M;            // activation rows (dense) or pairs P (gather)
+    int32_t R_x;          // gather: rows of x
+    int32_t E;            // gather: expert planes
+    int32_t S;            // waves per block (K split)
+    int32_t SPW;          // 128-column segments per wave (a multiple of 4)
+    int32_t BPG;          // bands each block walks
+};
+
 // Kernel symbol for (bits, activation rows per pass, chunks per lane, weight
 // rows per iteration, load ring stages, K segments per row group of a block's
 // LDS copy of x (0: none)), or NULL.
 const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather);
 const void *dequant_kernel_sym(int bits);
+// Matrix-core kernel with bands of 16*tiles rows (tiles 1 or 2), activations
+// from an LDS copy (x_lds, dense only) or from global memory, or NULL.
+const void *mfma_kernel(int tiles, bool gather, bool x_lds);
 
 }  // namespace agq

@@ -1,0 +1,498 @@
+// Small-batch affine group-quantized products on the gfx950 matrix cores.
+//
+// Same operands and result as the VALU kernels (qmv_kernels.hip): BF16
+// activations x [M, K], U32-packed 4-bit codes (low-first) [N, K/8], BF16
+// scale and bias per 64-column group (operand triple of "MLX CUDA Cleanup
+// Plan", Target Architecture §1), and
+//     y[m,n] = sum_g s[n,g] * (sum_{k in g} x[m,k]*(128+q[n,k]) - 128*X[m,g]) + b[n,g]*X[m,g]
+//            = sum_g s[n,g] * D[m,n,g] + (b[n,g] - 128*s[n,g]) * X[m,g],
+// with X[m,g] the sum of x over group g. This is sum_k x*(s*q + b) regrouped.
+//
+// With several activation rows the VALU form issues 4*M dot products per
+// packed word and becomes issue-bound (M = 8: about 60 VALU instructions per
+// word). Here v_mfma_f32_16x16x32_bf16 forms D:
+//  - A (16 x 32): activation rows, lane l holds row m = l % 16. Rows past the
+//    pass read zero (the buffer descriptor's range), so up to 16 rows share
+//    one instruction.
+//  - B (32 x 16): 16 weight rows as bfloat16 (128 + q), lane l holds row
+//    n = l % 16. A code q sits in the low mantissa bits of 0x4300 (128.0),
+//    so one byte permute per two codes builds the operand.
+//  - D (16 x 16): lane l holds D[4*(l/16) + r][l % 16], r < 4.
+// In A and B alike, lane group g = l / 16 supplies 8 of the 32 columns, as
+// the four bfloat16 pairs (c0,c4), (c1,c5), (c2,c6), (c3,c7) of one packed
+// word (8 consecutive columns c0..c7). The activations are arranged the same
+// way, so only the pairing of lanes with columns matters.
+//
+// Work decomposition. A tile is 16 weight rows; a band is T tiles. K splits
+// into segments of 128 columns (64 bytes of codes per row, two groups). Each
+// lane group loads one 16-byte quarter of a tile row's segment, so one load
+// instruction reads 64 contiguous bytes from each of 16 rows. One
+// v_permlane32_swap per two words then regroups the words so that each MFMA
+// sees columns of a single 64-column group (the scale changes per group):
+// after swapping words (0,2) and (1,3) between the wave halves, words 0 and
+// 1 of every lane hold columns of the segment's first group and words 2 and
+// 3 of the second. Slot (h, t) (h = group, t = word) of lane group g covers
+// columns 64h + 32(g%2) + 8(t + 2(g/2)) .. +8 of the segment.
+//
+// S waves split K (each owns SPW consecutive segments) and form a block; the
+// block walks bands round-robin. Per segment a wave loads the A operands of
+// its activation slice (L2-resident, shared by the band's T tiles), the codes
+// of T tiles, and every fourth segment the scales and biases of the next 8
+// groups of each tile row. Loads run 4 segments ahead in a ring. X[m,g]
+// comes from the same A operands against an all-ones B. At the end of a band
+// the S waves' partial sums meet in LDS in a fixed order, so results are
+// deterministic.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+#include "qmv_device.hpp"
+#include "qmv_kernels.hpp"
+
+namespace agq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kRing = kMfmaRing;  // segments in flight per wave (one block of scales)
+constexpr uint32_t kOnes = 0x3F803F80u;  // bfloat16 pair (1, 1)
+constexpr int kRsrcW3 = 0x00020000;      // raw buffer, 32-bit data format
+// Cache policy of the code, scale and bias loads. Each load reads half of a
+// 128-byte line (codes) or 16 bytes of it (scales); other loads read the rest
+// shortly after, so the lines are cached normally (2: non-temporal measured
+// 3-10% slower).
+#ifndef AGQ_MFMA_W_POLICY
+#define AGQ_MFMA_W_POLICY 0
+#endif
+#ifndef AGQ_MFMA_S_POLICY
+#define AGQ_MFMA_S_POLICY 0
+#endif
+constexpr int kWPolicy = AGQ_MFMA_W_POLICY;
+constexpr int kSPolicy = AGQ_MFMA_S_POLICY;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_of(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcW3);
+}
+
+__device__ __forceinline__ f32x4 mfma(const u32x4 &a, const u32x4 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// B operand slice of one packed word: (128 + q) pairs (q0,q4), (q1,q5), (q2,q6), (q3,q7).
+__device__ __forceinline__ u32x4 code_pairs(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    return u32x4{byte_perm(kMagic43, lo, kSelEven), byte_perm(kMagic43, hi, kSelEven),
+                 byte_perm(kMagic43, lo, kSelOdd), byte_perm(kMagic43, hi, kSelOdd)};
+}
+
+// A operand slice of 8 activations x0..x7 (one 16-byte word): (x0,x4), (x1,x5), (x2,x6), (x3,x7).
+__device__ __forceinline__ u32x4 act_pairs(const u32x4 &q) {
+    return u32x4{byte_perm(q.z, q.x, 0x05040100u), byte_perm(q.z, q.x, 0x07060302u),
+                 byte_perm(q.w, q.y, 0x05040100u), byte_perm(q.w, q.y, 0x07060302u)};
+}
+
+// One segment's loads: activation words of the 4 slots (h,t) = (0,0), (0,1),
+// (1,0), (1,1) and 16 bytes of codes per tile.
+template <int T, bool XL>
+struct Seg {
+    u32x4 x[XL ? 1 : 4];  // (unused when the activations come from the block's LDS copy)
+    u32x4 w[T];
+};
+
+// The block's LDS copy of the pass's activation rows (XL), already in A
+// operand form: word ((s*4 + i)*4 + g)*Mp + m holds slot i of lane group g,
+// row m, segment s; one zero word follows for lanes of rows past the pass.
+extern __shared__ u32x4 g_mfma_x[];
+constexpr int kXPer = 16;  // 16-byte words of x each thread stages (the host checks the copy fits)
+
+// Scales and biases of 8 groups (4 segments) per tile row: dword j holds the
+// bf16 pair of segment j's two groups.
+template <int T>
+struct ScaleBlock {
+    u32x4 s[T], b[T];
+};
+
+// Per-wave constants of a pass.
+struct Lanes {
+    uint32_t woff;      // byte offset of the lane's code quarter within a tile: row (l%16), quarter l/16
+    uint32_t soff;      // byte offset of the lane's scale row within a tile
+    uint32_t xoff[4];   // byte offsets of the lane's activation words for the 4 slots, segment 0
+};
+
+// One plane's band geometry and operand ranges.
+struct Band {
+    const uint8_t *w;  // plane codes
+    const uint16_t *s, *b;
+    int64_t N;
+    uint32_t rowbytes;  // K / 2
+    int32_t G;
+};
+
+template <int T, bool SCALES, bool XL>
+__device__ __forceinline__ void load_seg(Seg<T, XL> &u, ScaleBlock<T> &sb, const Band &bd, const Lanes &ln,
+                                         __amdgpu_buffer_rsrc_t xr, int64_t band, int seg) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int64_t row0 = band * (16 * T) + 16 * t;
+        const int64_t left = bd.N - row0;
+        const uint32_t rows = left <= 0 ? 0u : left >= 16 ? 16u : (uint32_t)left;
+        const int64_t r0 = left <= 0 ? 0 : row0;
+        u.w[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.w + r0 * bd.rowbytes, rows * bd.rowbytes),
+                                                       ln.woff, seg * 64, kWPolicy);
+        if constexpr (SCALES) {
+            const uint32_t sbytes = rows * (uint32_t)bd.G * 2u;
+            sb.s[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.s + r0 * bd.G, sbytes), ln.soff, seg * 4,
+                                                            kSPolicy);
+            sb.b[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.b + r0 * bd.G, sbytes), ln.soff, seg * 4,
+                                                            kSPolicy);
+        }
+    }
+    if constexpr (!XL) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u.x[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, ln.xoff[i], seg * 256, 0);
+    }
+}
+
+// Fold one segment into the band's accumulators. sd/bd: the bf16 scale and
+// bias pairs of the segment's two groups for the lane's row of each tile.
+template <int T, bool XL>
+__device__ __forceinline__ void compute_seg(const Seg<T, XL> &u, const uint32_t (&sd)[T], const uint32_t (&bd)[T],
+                                            f32x4 (&acc)[T], uint32_t xbase, uint32_t xmult, int seg) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
+    u32x4 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (XL)
+            a[i] = g_mfma_x[xbase + (uint32_t)(seg * 4 + i) * xmult];
+        else
+            a[i] = act_pairs(u.x[i]);
+    }
+    // X[m, g] of the two groups, in the D layout.
+    const f32x4 x0 = mfma(a[1], ones, mfma(a[0], ones, z));
+    const f32x4 x1 = mfma(a[3], ones, mfma(a[2], ones, z));
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const auto p02 = __builtin_amdgcn_permlane32_swap(u.w[t].x, u.w[t].z, false, false);
+        const auto p13 = __builtin_amdgcn_permlane32_swap(u.w[t].y, u.w[t].w, false, false);
+        const f32x4 d0 = mfma(a[1], code_pairs(p13[0]), mfma(a[0], code_pairs(p02[0]), z));
+        const f32x4 d1 = mfma(a[3], code_pairs(p13[1]), mfma(a[2], code_pairs(p02[1]), z));
+        const float s0 = bf16_lo(sd[t]), s1 = bf16_hi(sd[t]);
+        const float c0 = fmaf(-128.f, s0, bf16_lo(bd[t])), c1 = fmaf(-128.f, s1, bf16_hi(bd[t]));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = acc[t][r];
+            v = fmaf(s0, d0[r], v);
+            v = fmaf(c0, x0[r], v);
+            v = fmaf(s1, d1[r], v);
+            v = fmaf(c1, x1[r], v);
+            acc[t][r] = v;
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t dword(const u32x4 &v, int j) {
+    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// LDS partial sums of the K split: two regions (alternating bands) of
+// kMfmaMaxS waves x T tiles x 4 values x 64 lanes.
+template <int T>
+struct Red {
+    static constexpr int REGION = kMfmaMaxS * T * 4 * 64;
+    static constexpr int FLOATS = 2 * REGION;
+};
+
+// Sum the S waves' partials of a finished band and store the rows. out(m)
+// is the output row of activation row m (m < mrows), or nullptr.
+template <int T, typename Out>
+__device__ __forceinline__ void finish_band(f32x4 (&acc)[T], float *red, int S, int wig, int lane, int64_t band,
+                                            int parity, int64_t N, int mrows, const Out &out) {
+    const int g = lane >> 4, nl = lane & 15;
+    if (S > 1) {
+        float *reg = red + parity * Red<T>::REGION;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) reg[((wig * T + t) * 4 + r) * 64 + lane] = acc[t][r];
+        __syncthreads();
+        if (wig == 0) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = 0.f;
+                    for (int w = 0; w < S; ++w) v += reg[((w * T + t) * 4 + r) * 64 + lane];
+                    acc[t][r] = v;
+                }
+        }
+    }
+    if (wig == 0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int64_t n = band * (16 * T) + 16 * t + nl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * g + r;
+                if (m < mrows && n < N) out(m)[n] = f32_to_bf16(acc[t][r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// One pass: activation rows through the x descriptor `xr` (lane offsets in
+// `ln`), against the plane's bands rg, rg + groups, ... (BPG of them).
+// Every wave of the block walks the same number of segments, so the block
+// meets at the same band boundaries.
+//
+// XL: the block first copies the pass's activation rows into LDS in A
+// operand form (x loads issued before the first codes, so waiting for them
+// does not wait for the codes), and the waves read their operands there:
+// 4 LDS reads per segment instead of 4 buffer loads that mostly address rows
+// past the pass.
+template <int T, bool XL, typename Out>
+__device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, const Lanes &ln,
+                                          __amdgpu_buffer_rsrc_t xr, int mrows, const Out &out, int64_t rg,
+                                          int64_t groups, float *red) {
+    const int lane = threadIdx.x & 63;
+    const int wig = wave_id();
+    const int S = a.S, SPW = a.SPW;
+    const int seg0 = wig * SPW;
+    const int turns = a.BPG * (SPW / kRing);  // rings of 4 segments over the walk
+    const int tpb = SPW / kRing;               // turns per band
+
+    Seg<T, XL> buf[kRing];
+    ScaleBlock<T> next, cur;
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // LDS copy of x: source word q (16 bytes) is row q / (K/8), 8-column word
+    // c8 = q % (K/8), at byte q*16 of the dense rows.
+    const uint32_t words = (uint32_t)mrows * (uint32_t)(a.K / 8);
+    const int per = (int)((words + blockDim.x - 1) / blockDim.x);  // <= kXPer (host check)
+    u32x4 xraw[XL ? kXPer : 1];
+    if constexpr (XL) {
+#pragma unroll
+        for (int k = 0; k < kXPer; ++k)
+            if (k < per)  // uniform branch
+                xraw[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, (threadIdx.x + k * blockDim.x) * 16u, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Turn j covers segments seg0 + 4*(j % tpb) .. +3 of band rg + (j / tpb) * groups.
+    load_seg<T, true, XL>(buf[0], next, bd, ln, xr, rg, seg0);
+#pragma unroll
+    for (int p = 1; p < kRing; ++p) load_seg<T, false, XL>(buf[p], next, bd, ln, xr, rg, seg0 + p);
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint32_t xbase = 0, xmult = 0;
+    if constexpr (XL) {
+        const uint32_t Mp = (uint32_t)mrows, wpr = (uint32_t)(a.K / 8);
+#pragma unroll
+        for (int k = 0; k < kXPer; ++k) {
+            const uint32_t q = threadIdx.x + k * blockDim.x;
+            if (k < per && q < words) {
+                const uint32_t m = q / wpr, c8 = q % wpr;
+                const uint32_t sgm = c8 >> 4, c16 = c8 & 15u, h = c16 >> 3, rem = c16 & 7u;
+                const uint32_t g = (rem >> 2) | (((rem >> 1) & 1u) << 1), i = 2u * h + (rem & 1u);
+                g_mfma_x[((sgm * 4u + i) * 4u + g) * Mp + m] = act_pairs(xraw[k]);
+            }
+        }
+        if (threadIdx.x == 0) g_mfma_x[words] = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+        const uint32_t m = (uint32_t)lane & 15u, g = (uint32_t)lane >> 4;
+        xbase = m < Mp ? g * Mp + m : words;
+        xmult = m < Mp ? 4u * Mp : 0u;
+    }
+
+    int j = 0;
+    for (; j + 1 < turns; ++j) {
+        const int bi = j / tpb;
+        const int64_t band = rg + (int64_t)bi * groups;
+        const int jn = j + 1;
+        const int64_t nband = rg + (int64_t)(jn / tpb) * groups;
+        const int nseg = seg0 + kRing * (jn % tpb);
+#pragma unroll
+        for (int p = 0; p < kRing; ++p) {
+            if (p == 0) cur = next;
+            uint32_t sd[T], bdw[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                sd[t] = dword(cur.s[t], p);
+                bdw[t] = dword(cur.b[t], p);
+            }
+            compute_seg<T, XL>(buf[p], sd, bdw, acc, xbase, xmult, seg0 + kRing * (j % tpb) + p);
+            if (p == 0)
+                load_seg<T, true, XL>(buf[0], next, bd, ln, xr, nband, nseg);
+            else
+                load_seg<T, false, XL>(buf[p], next, bd, ln, xr, nband, nseg + p);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if ((j + 1) % tpb == 0) finish_band<T>(acc, red, S, wig, lane, band, bi & 1, bd.N, mrows, out);
+    }
+    {
+        const int bi = j / tpb;
+        const int64_t band = rg + (int64_t)bi * groups;
+#pragma unroll
+        for (int p = 0; p < kRing; ++p) {
+            if (p == 0) cur = next;
+            uint32_t sd[T], bdw[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                sd[t] = dword(cur.s[t], p);
+                bdw[t] = dword(cur.b[t], p);
+            }
+            compute_seg<T, XL>(buf[p], sd, bdw, acc, xbase, xmult, seg0 + kRing * (j % tpb) + p);
+        }
+        finish_band<T>(acc, red, S, wig, lane, band, bi & 1, bd.N, mrows, out);
+    }
+    if (S > 1 || XL) __syncthreads();  // the LDS regions and the copy of x are reused by the next pass
+}
+
+// Lane constants shared by the dense and gather kernels; xrow: the lane's
+// activation row byte offset (or the descriptor's end for lanes past the pass).
+__device__ __forceinline__ Lanes lane_consts(const MfmaArgs &a, uint32_t xrow) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t g = (uint32_t)lane >> 4, nl = (uint32_t)lane & 15u;
+    Lanes ln;
+    ln.woff = nl * (uint32_t)(a.K / 2) + 16u * g;
+    ln.soff = nl * (uint32_t)a.G * 2u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t h = (uint32_t)i >> 1, t = (uint32_t)i & 1u;
+        const uint32_t col = 64u * h + 32u * (g & 1u) + 8u * (t + 2u * (g >> 1));
+        ln.xoff[i] = xrow + 2u * col;
+    }
+    return ln;
+}
+
+struct RowsOut {
+    uint16_t *y;
+    int64_t N;
+    __device__ __forceinline__ uint16_t *operator()(int m) const { return y + (int64_t)m * N; }
+};
+
+struct PairsOut {
+    uint16_t *y;
+    int64_t N;
+    const uint16_t *plist;
+    __device__ __forceinline__ uint16_t *operator()(int m) const { return y + (int64_t)plist[m] * N; }
+};
+
+}  // namespace
+
+template <int T, bool XL>
+__global__ __launch_bounds__(512) void qmv_mfma_kernel(MfmaArgs a) {
+    __shared__ float red[Red<T>::FLOATS];
+    const int lane = threadIdx.x & 63;
+    const uint32_t m = (uint32_t)lane & 15u;
+    const uint32_t xbytes = (uint32_t)a.M * (uint32_t)a.K * 2u;
+    // Lanes of rows m >= M start at the descriptor's end and read zeros.
+    const Lanes ln = lane_consts(a, m * (uint32_t)a.K * 2u);
+    const Band bd{reinterpret_cast<const uint8_t *>(a.w), a.s, a.b, a.N, (uint32_t)(a.K / 2), a.G};
+    mfma_pass<T, XL>(a, bd, ln, range_of(a.x, xbytes), a.M, RowsOut{a.y, a.N}, blockIdx.x, gridDim.x, red);
+}
+
+// blockIdx.y = expert plane e. The pairs routed to e are listed in LDS and
+// taken 16 per pass, so each used plane streams once per 16 pairs; blocks of
+// planes without pairs exit before reading weights. Blocks of plane 0 also
+// write NaN rows for pairs whose indices are out of range.
+template <int T>
+__global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
+    __shared__ float red[Red<T>::FLOATS];
+    __shared__ uint16_t plist[kMaxPairs];
+    __shared__ uint32_t xlist[kMaxPairs];
+    __shared__ int pcount;
+    const int lane = threadIdx.x & 63;
+    const int wig = wave_id();
+    const uint32_t e = blockIdx.y;
+    const int64_t rg = blockIdx.x, groups = gridDim.x;
+    const uint32_t *lhs = a.lhs, *rhs = a.rhs;
+    const uint32_t nx = (uint32_t)a.R_x, ne = (uint32_t)a.E;
+    const int P = a.M;
+
+    auto compact = [&](auto pred) {
+        int count = 0;
+        for (int base = 0; base < P; base += 64) {
+            const int p = base + lane;
+            const bool take = p < P && pred(p);
+            const uint64_t mask = __ballot(take);
+            if (take) plist[count + __popcll(mask & ((1ull << lane) - 1ull))] = (uint16_t)p;
+            count += __popcll(mask);
+        }
+        return count;
+    };
+
+    if (e == 0) {
+        if (wig == 0) {
+            const int c = compact([&](int p) {
+                const uint32_t xr = lhs ? lhs[p] : (uint32_t)p;
+                const uint32_t ex = rhs ? rhs[p] : (uint32_t)p;
+                return xr >= nx || ex >= ne;
+            });
+            if (lane == 0) pcount = c;
+        }
+        __syncthreads();
+        const int nbad = pcount;
+        for (int i = 0; i < nbad; ++i) {
+            uint16_t *yr = a.y + (int64_t)plist[i] * a.N;
+            for (int bi = 0; bi < a.BPG; ++bi) {
+                const int64_t row0 = (rg + (int64_t)bi * groups) * (16 * T);
+                for (int r = (int)threadIdx.x; r < 16 * T; r += (int)blockDim.x)
+                    if (row0 + r < a.N) yr[row0 + r] = 0x7FC0u;
+            }
+        }
+        __syncthreads();
+    }
+    if (wig == 0) {
+        const int c = compact([&](int p) {
+            const uint32_t xr = lhs ? lhs[p] : (uint32_t)p;
+            const uint32_t ex = rhs ? rhs[p] : (uint32_t)p;
+            return ex == e && xr < nx;
+        });
+        for (int i = lane; i < c; i += 64) {
+            const int p = plist[i];
+            xlist[i] = lhs ? lhs[p] : (uint32_t)p;
+        }
+        if (lane == 0) pcount = c;
+    }
+    __syncthreads();
+    const int count = pcount;
+    if (count == 0) return;
+    const uint32_t xbytes = (uint32_t)a.R_x * (uint32_t)a.K * 2u;
+    const __amdgpu_buffer_rsrc_t xr = range_of(a.x, xbytes);
+    const int64_t plane = (int64_t)e * a.N;
+    const Band bd{reinterpret_cast<const uint8_t *>(a.w) + plane * (a.K / 2), a.s + plane * a.G, a.b + plane * a.G,
+                  a.N, (uint32_t)(a.K / 2), a.G};
+    for (int base = 0; base < count; base += 16) {
+        const int me = count - base < 16 ? count - base : 16;
+        const int m = lane & 15;
+        const Lanes ln = lane_consts(a, m < me ? xlist[base + m] * (uint32_t)a.K * 2u : xbytes);
+        mfma_pass<T, false>(a, bd, ln, xr, me, PairsOut{a.y, a.N, plist + base}, rg, groups, red);
+    }
+}
+
+const void *mfma_kernel(int tiles, bool gather, bool x_lds) {
+    if (gather) {
+        if (x_lds) return nullptr;
+        return tiles == 1 ? reinterpret_cast<const void *>(&gather_mfma_kernel<1>)
+             : tiles == 2 ? reinterpret_cast<const void *>(&gather_mfma_kernel<2>)
+                          : nullptr;
+    }
+    switch (tiles * 2 + (x_lds ? 1 : 0)) {
+        case 2: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, false>);
+        case 3: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, true>);
+        case 4: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, false>);
+        case 5: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, true>);
+    }
+    return nullptr;
+}
+
+}  // namespace agq

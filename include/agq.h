@@ -158,6 +158,12 @@ typedef struct agq_plan {
                                 multiple of stages x rows_per_iter */
     int32_t resident_waves;  /* waves of the chosen kernel the device holds at once, at this block size
                                 (agq_plan_product: num_cus x waves_per_cu); the grid is sized from it */
+    int32_t engine;          /* 0: VALU dot products (the fields above as described);
+                                1: matrix cores (4-bit, K % 512 == 0, several activation rows or the
+                                gather): bands of rows_per_iter = 16*tiles rows, waves_per_group waves
+                                splitting K per block, one band group per block (groups_per_block 1,
+                                blocks = row_groups), mw = 16 rows per pass, cpt = 0, stages = 128-column
+                                segments in flight per wave */
 } agq_plan;
 
 agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group_size,

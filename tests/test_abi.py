@@ -135,19 +135,36 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
     p = agq.plan(M, N, K, bits, 64, cus, experts, waves_per_cu=wpc)
     C = K * bits // 128
     assert p["chunks_per_row"] == C
-    assert 1 <= p["cpt"] <= 7 and p["cpt"] * p["mw"] <= 8
-    assert 1 <= p["waves_per_group"] <= 8
-    assert p["waves_per_group"] * p["cpt"] * 64 >= C                     # every chunk has a lane
-    assert (p["waves_per_group"] - 1) * p["cpt"] * 64 < C                 # no wave is idle
-    assert p["threads_per_block"] == 64 * p["waves_per_group"] * p["groups_per_block"] <= 512
     R, TG, RPG = p["rows_per_iter"], p["row_groups"], p["rows_per_group"]
-    assert p["stages"] >= 1 and RPG % (p["stages"] * R) == 0              # whole turns of the load ring
     assert TG == p["blocks"] * p["groups_per_block"]
     assert TG * RPG >= N                                                 # every row is covered
     assert (TG - p["groups_per_block"]) * RPG < N                        # at most one block's groups spare
     if N <= 300000:
         rows = visited_rows(p, N)
         assert rows.size == N and np.array_equal(np.sort(rows), np.arange(N))   # each row exactly once
+    mfma = bits == 4 and K % 512 == 0 and (M >= 5 or experts > 0)
+    assert p["engine"] == (1 if mfma else 0)
+    if mfma:
+        # Matrix cores: bands of 16 or 32 rows, up to 4 waves splitting K into equal
+        # slices of whole 4-segment (512-column) blocks, one band group per block.
+        assert R in (16, 32) and p["mw"] == 16 and p["cpt"] == 0 and p["stages"] == 4
+        S = p["waves_per_group"]
+        assert 1 <= S <= 4 and (K // 512) % S == 0
+        assert all((K // 512) % s for s in range(S + 1, 5))                 # the most waves that divide
+        if experts:
+            assert p["x_lds_bytes"] == 0
+        else:   # LDS copy of x when it fits in 64 KB and 16 words per thread
+            fits = M * K * 2 <= 65536 and -(-M * K * 2 // 16 // (64 * S)) <= 16
+            assert p["x_lds_bytes"] == (M * K * 2 + 16 if fits else 0)
+        assert p["groups_per_block"] == 1 and p["threads_per_block"] == 64 * S
+        assert RPG % R == 0
+        return
+    assert 1 <= p["cpt"] <= 7 and p["cpt"] * p["mw"] <= 8
+    assert 1 <= p["waves_per_group"] <= 8
+    assert p["waves_per_group"] * p["cpt"] * 64 >= C                     # every chunk has a lane
+    assert (p["waves_per_group"] - 1) * p["cpt"] * 64 < C                 # no wave is idle
+    assert p["threads_per_block"] == 64 * p["waves_per_group"] * p["groups_per_block"] <= 512
+    assert p["stages"] >= 1 and RPG % (p["stages"] * R) == 0              # whole turns of the load ring
     assert p["rows_per_iter"] * p["mw"] <= 16
     if experts:
         assert p["mw"] == 8 and p["cpt"] == 1   # passes of up to 8 pairs, one chunk per lane
@@ -155,13 +172,18 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
         assert p["mw"] == M
 
 
+# The VALU plans of several activation rows, probed with 8-bit codes at half the
+# 4-bit K (the same chunks per row, so the same plan): 4-bit products with K a
+# multiple of 512 and at least 5 rows, and 4-bit gathers, run on the matrix cores.
 @pytest.mark.parametrize("M,K,experts,stages", [
     (2, 2048, 0, 4), (4, 1024, 0, 4), (8, 2048, 0, 4),   # one wave covers a row: four-stage ring
     (2, 4096, 0, 2), (2, 14336, 0, 2), (8, 4096, 0, 2), (4, 14336, 0, 2),  # K split over waves
     (1, 4096, 0, 2), (8, 2048, 3, 2), (8, 4096, 3, 2),   # batch 1 and the gather
 ])
 def test_plan_ring_depth(M, K, experts, stages):
-    p = agq.plan(M, 4096, K, 4, 64, 256, experts, waves_per_cu=8)
+    bits, K = (4, K) if M == 1 and not experts else (8, K // 2)
+    p = agq.plan(M, 4096, K, bits, 64, 256, experts, waves_per_cu=8)
+    assert p["engine"] == 0
     assert p["stages"] == stages
     if M > 1 and not experts:
         assert (p["waves_per_group"] == 1) == (stages == 4)
@@ -173,7 +195,9 @@ def test_plan_ring_depth(M, K, experts, stages):
     (1, 14336, 4, 2), (1, 65536, 4, 8), (1, 114688, 7, 8),                   # batch 1: up to 4, then 7
 ])
 def test_plan_chunks_per_lane(M, K, cpt, waves):
-    p = agq.plan(M, 4096, K, 4, 64, 256, 0, waves_per_cu=8)
+    bits, K = (4, K) if M == 1 else (8, K // 2)
+    p = agq.plan(M, 4096, K, bits, 64, 256, 0, waves_per_cu=8)
+    assert p["engine"] == 0
     assert (p["cpt"], p["waves_per_group"]) == (cpt, waves)
 
 
@@ -181,8 +205,8 @@ def test_plan_chunks_per_lane(M, K, cpt, waves):
 def test_gather_plan_lds_copy_of_x(K, bytes_):
     """Gather blocks whose row groups share columns (one or two K segments, four groups)
     stage each pass's x rows through one LDS copy; seven-segment groups do not."""
-    p = agq.plan(8, 4096, K, 4, 64, 256, 8, waves_per_cu=8)
-    assert p["x_lds_bytes"] == bytes_
+    p = agq.plan(8, 4096, K // 2, 8, 64, 256, 8, waves_per_cu=8)
+    assert p["engine"] == 0 and p["x_lds_bytes"] == bytes_
     if bytes_:
         assert p["groups_per_block"] == 4 and p["threads_per_block"] == 256 * p["waves_per_group"]
 

@@ -181,6 +181,41 @@ def test_shapes_and_ragged_tails(bits, M, N, K):
     run_qmv_case(f"shape M={M}", x, d, K, bits, M=None if M == 1 else M)
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (5, 31, 512), (6, 17, 1536), (8, 1, 2560), (5, 100, 3584), (6, 1000, 4096), (7, 33, 14336),
+    (5, 2049, 6144), (7, 4111, 4096), (8, 4097, 2048), (6, 16400, 2048), (8, 16401, 1024),
+])
+def test_matrix_core_shapes(M, N, K):
+    """4-bit products of several rows on the matrix cores: K splits of 1, 3 and 4 waves,
+    bands of one and two tiles, ragged last tiles, and activations from the block's LDS
+    copy or from global memory."""
+    plan = agq.launch_plan(M, N, K, 4)
+    assert plan["engine"] == 1
+    d = si.draw_quantized_weight(23, M, N, K, 4)
+    x = si.draw_activations(23, 100 + M, M, K)
+    run_qmv_case(f"mfma M={M} N={N} K={K} S={plan['waves_per_group']} band={plan['rows_per_iter']} "
+                 f"xlds={plan['x_lds_bytes']}",
+                 x, d, K, 4, M=M)
+
+
+def test_gather_matrix_core_passes_of_sixteen():
+    """33 pairs on one expert (passes of 16, 16 and 1) and 3 on another, repeated x rows."""
+    E, N, K, R = 4, 70, 1024, 9
+    assert agq.launch_plan(8, N, K, 4, experts=E)["engine"] == 1
+    planes = [si.draw_quantized_weight(24, e, N, K, 4) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(24, 99, R, K)
+    rhs = np.array([2] * 33 + [0] * 3, np.uint32)
+    np.random.default_rng([24, 1]).shuffle(rhs)
+    lhs = (np.arange(len(rhs)) * 5 % R).astype(np.uint32)
+    progress("gather, passes of 16 on the matrix cores")
+    y = agq.gather_qmv(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs))
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, 4)
+    check_close(y, y_ref, A, "gather passes of 16")
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 def test_constant_code_closed_form_adversarial(bits):
     """|y| equals sum|x*w| here, so the bf16 output rounding alone can approach 4e-3*A."""
@@ -318,12 +353,13 @@ def test_gather_many_pairs_one_expert_and_unused_experts():
 
 
 def test_gather_passes_through_the_block_copy_of_x():
-    """Several passes per plane (21 pairs on one expert: 8, 8 and 5) through the block's
-    LDS copy of x with two K segments, with repeated and scattered x rows."""
-    E, N, K, R = 3, 1030, 4096, 24
-    plan = agq.launch_plan(8, N, K, 4, experts=E)
-    assert plan["x_lds_bytes"] > 0 and plan["waves_per_group"] == 2
-    planes = [si.draw_quantized_weight(21, e, N, K, 4) for e in range(E)]
+    """VALU gather (8-bit codes): several passes per plane (21 pairs on one expert: 8, 8
+    and 5) through the block's LDS copy of x with two K segments, with repeated and
+    scattered x rows."""
+    E, N, K, R, bits = 3, 1030, 2048, 24, 8
+    plan = agq.launch_plan(8, N, K, bits, experts=E)
+    assert plan["engine"] == 0 and plan["x_lds_bytes"] > 0 and plan["waves_per_group"] == 2
+    planes = [si.draw_quantized_weight(21, e, N, K, bits) for e in range(E)]
     st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
     x = si.draw_activations(21, 99, R, K)
     rng = np.random.default_rng([21, 1])
@@ -332,9 +368,9 @@ def test_gather_passes_through_the_block_copy_of_x():
     lhs = rng.integers(0, R, len(rhs)).astype(np.uint32)
     progress("gather, several passes through the LDS copy of x")
     y = agq.gather_qmv(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
-                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs))
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs), bits=bits)
     torch.cuda.synchronize()
-    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, 4)
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, bits)
     check_close(y, y_ref, A, "gather passes")
 
 
@@ -396,9 +432,9 @@ def test_launch_plans_size_each_block_size_separately():
     unit) and 448-thread blocks at K=14336 (one row group of 7 waves, one block). The
     residency the grid is sized from must be that of the block size in use, whatever was
     planned before: bigger blocks of the same kernel can never hold more waves."""
-    shapes = {256: (8, 65536, 2048), 448: (8, 4096, 14336)}
+    shapes = {256: (8, 65536, 1024), 448: (8, 4096, 7168)}  # 8-bit: the VALU form
     for order in ((256, 448), (448, 256), (256, 448)):
-        plans = {t: agq.launch_plan(*shapes[t], 4) for t in order}
+        plans = {t: agq.launch_plan(*shapes[t], 8) for t in order}
         small, big = plans[256], plans[448]
         for p, threads in ((small, 256), (big, 448)):
             assert p["threads_per_block"] == threads and p["cpt"] == 1 and p["mw"] == 8
@@ -492,9 +528,9 @@ def test_calls_on_a_side_stream():
 
 @pytest.mark.parametrize("bits,M,K", [(4, 2, 65536), (8, 2, 32768), (4, 8, 16384)])
 def test_k_limits_of_the_wide_form(bits, M, K):
-    """The largest K per M: eight waves split each row."""
+    """The largest K per M: eight waves split each row (on the matrix cores, four)."""
     p = agq.plan(M, 5, K, bits, 64, 256, 0)
-    assert p["waves_per_group"] == 8 or M == 8
+    assert p["waves_per_group"] == (4 if p["engine"] == 1 else 8) or M == 8
     d = si.draw_quantized_weight(20, 100 * bits + M, 5, K, bits)
     x = si.draw_activations(20, M, M, K)
     run_qmv_case(f"K limit M={M} bits={bits}", x, d, K, bits, M=M)
