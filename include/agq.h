@@ -89,7 +89,9 @@ agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const v
  * Small-batch matvec ("qmv_wide"): y[m, n] = sum_k x[m, k] * w_hat[n, k] for
  * 1 <= M <= 8 activation rows, streaming each weight byte once for all M rows.
  *   x [M, K] BF16, y [M, N] BF16; w, scales and biases as in agq_qmv.
- * M > 8 is AGQ_ENOTSUP; that is a quantized GEMM, not a matvec. The K limit
+ * M > 8 is AGQ_ENOTSUP; that is a quantized GEMM, not a matvec. With 4-bit
+ * codes, M >= 5 and K a multiple of 512 the product runs on the matrix cores
+ * and K is limited only by M*K*2 < 2^31 bytes of x. Otherwise the K limit
  * shrinks with M: K <= 16384 * c for 4-bit and 8192 * c for 8-bit, with
  * c = min(7, floor(8/M)) (larger K is AGQ_ENOTSUP).
  */
@@ -111,7 +113,9 @@ agq_status agq_qmv_wide(const void *x, const uint32_t *w, const void *scales, co
  * over the top-k slots is applied. P may be at most 4096. Index values are
  * device data and cannot be checked on the host. A pair whose lhs >= R or
  * rhs >= E gets an all-NaN output row, and no memory outside the arrays is
- * read. K limits are those of agq_qmv_wide at M = 8.
+ * read. With 4-bit codes and K a multiple of 512 the gather runs on the
+ * matrix cores, 16 pairs per pass, and K is limited only by R*K*2 < 2^31
+ * bytes of x; otherwise K limits are those of agq_qmv_wide at M = 8.
  */
 agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y,

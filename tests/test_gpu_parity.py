@@ -526,9 +526,10 @@ def test_calls_on_a_side_stream():
     check_close(y, y_ref, A, "side stream")
 
 
-@pytest.mark.parametrize("bits,M,K", [(4, 2, 65536), (8, 2, 32768), (4, 8, 16384)])
+@pytest.mark.parametrize("bits,M,K", [(4, 2, 65536), (8, 2, 32768), (4, 8, 16384), (4, 6, 65536)])
 def test_k_limits_of_the_wide_form(bits, M, K):
-    """The largest K per M: eight waves split each row (on the matrix cores, four)."""
+    """The largest K per M on the VALU (eight waves split each row); the matrix cores
+    (four waves) have no such limit."""
     p = agq.plan(M, 5, K, bits, 64, 256, 0)
     assert p["waves_per_group"] == (4 if p["engine"] == 1 else 8) or M == 8
     d = si.draw_quantized_weight(20, 100 * bits + M, 5, K, bits)
