@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--per-shape", action="store_true", help="also time each matrix alone (to stderr)")
     ap.add_argument("--write-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="summarize rocprofv3 CSV output of this benchmark into profiles/ and exit")
+    ap.add_argument("--workload", choices=["llama", "wide", "gather"], default="llama",
+                    help="llama: the batch-1 decode set (the JSON line); wide: 14336x4096 and 4096x14336 at "
+                         "M = 2..8; gather: the Mixtral-shaped expert gather (per-shape lines on stdout)")
+    ap.add_argument("--calls", type=int, default=200, help="timed calls per shape (--workload wide/gather)")
     return ap.parse_args()
 
 
@@ -216,8 +220,161 @@ def write_profiles(trace_dir, fetch_dir, write_dir):
     print(json.dumps(rec))
 
 
+def time_calls(torch, fn, calls, repeats=5):
+    """Median over `repeats` of the mean event-timed duration of `calls` back-to-back calls."""
+    for i in range(20):
+        fn(i)
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(calls):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / calls)
+    return sorted(per)[len(per) // 2]
+
+
+def other_workload(args):
+    """Per-shape timing of the small-batch (workload 2) or gather (workload 4) products.
+
+    Weights rotate over at least 512 MiB of distinct copies, so reads come from HBM.
+    One line per shape: us/call, GB/s of algorithmic bytes, % of the HBM peak, and the
+    launch plan's engine (0: VALU dot products, 1: matrix cores).
+    """
+    import numpy as np
+    import torch
+
+    import seeded_inputs as si
+    import affine_group_quantized_amd as agq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def u32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to(dev)
+
+    def report(label, us, nbytes, plan):
+        gb = nbytes / (us * 1e-6) / 1e9
+        print(json.dumps({"shape": label, "us_per_call": round(us, 3), "GB/s": round(gb, 1),
+                          "pct_of_hbm_peak": round(100 * gb / HBM_PEAK_GBPS, 2), "bytes": nbytes,
+                          "engine": plan["engine"], "waves_per_group": plan["waves_per_group"],
+                          "rows_per_iter": plan["rows_per_iter"], "blocks": plan["blocks"]}), flush=True)
+
+    if args.workload == "wide":
+        wl = si.workload(2)
+        for name in ("w_a", "w_b"):
+            m = wl[name]
+            N, K = m["N"], m["K"]
+            wbytes = N * K // 2 + 4 * N * K // 64
+            rot = max(2, math.ceil(ROTATION_BYTES / wbytes))
+            cp = [(u32(m["w"]), bf16(m["scales"]), bf16(m["biases"])) for _ in range(rot)]
+            xall = bf16(wl["x4096"] if K == 4096 else wl["x14336"])
+            for M in (2, 4, 6, 8):
+                x = xall[:M].contiguous()
+                y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+                agq.qmv_wide(x, *cp[0], bits=4, out=y)  # validates the operands once
+                st = torch.cuda.current_stream().cuda_stream
+                ptrs = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr()) for c in cp]
+                # Raw C calls (pointers prepared above) keep the host ahead of the GPU.
+                us = time_calls(torch, lambda i: agq.lib.agq_qmv_wide(x.data_ptr(), *ptrs[i % rot], y.data_ptr(),
+                                                                      M, N, K, 4, 64, st), args.calls)
+                report(f"{N}x{K} M={M}", us, algo_bytes(N, K, 4, M), agq.launch_plan(M, N, K, 4))
+            del cp
+            torch.cuda.empty_cache()
+    else:
+        moe = si.workload(4)
+        rhs = moe["rhs"]
+        P = len(rhs)
+        used = len(set(rhs.tolist()))
+        for which in ("w1", "w2"):
+            m = moe[which]
+            K, N, E = m["K"], m["N"], m["E"]
+            x = bf16(moe["x"] if which == "w1" else moe["h"])
+            lhs = u32(moe["lhs1"]) if which == "w1" else None
+            R = x.shape[0]
+            rot = max(2, math.ceil(ROTATION_BYTES / (E * (N * K // 2 + 4 * N * K // 64))))
+            cp = [(u32(m["w"]), bf16(m["scales"]), bf16(m["biases"])) for _ in range(rot)]
+            ri = u32(rhs)
+            y = torch.empty(P, N, dtype=torch.bfloat16, device=dev)
+            agq.gather_qmv(x, *cp[0], rhs_indices=ri, lhs_indices=lhs, bits=4, out=y)  # validates once
+            st = torch.cuda.current_stream().cuda_stream
+            ptrs = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr()) for c in cp]
+            lp = None if lhs is None else lhs.data_ptr()
+            us = time_calls(torch, lambda i: agq.lib.agq_gather_qmv(x.data_ptr(), *ptrs[i % rot], lp, ri.data_ptr(),
+                                                                    y.data_ptr(), P, R, E, N, K, 4, 64, st),
+                            max(1, args.calls // 4))
+            nbytes = used * (N * K // 2 + 4 * N * K // 64) + 2 * R * K + 2 * P * N + 8 * P
+            report(f"gather {which} {E}x{N}x{K} P={P} ({used} planes used)", us, nbytes,
+                   agq.launch_plan(8, N, K, 4, experts=E))
+            del cp
+            torch.cuda.empty_cache()
+
+
+def write_workload_profile(workload, trace_dir, fetch_dir, write_dir):
+    """Summary of rocprofv3 runs of `bench.py --workload wide|gather` under profiles/.
+
+    Kernel statistics per instantiation, and the HBM bytes per launch from FETCH_SIZE and
+    WRITE_SIZE, scaled by the calibration recorded with the lm_head counters (the same
+    counters on the same device; these runs clone no buffers to calibrate with).
+    """
+    import statistics
+    with open(TRAFFIC_MD) as f:
+        cal = next(json.loads(line.split(":", 1)[1]) for line in f if line.startswith("traffic_json:"))
+    stats = _read_csv(trace_dir, "kernel_stats.csv")
+    flags = {"wide": "--workload wide --calls 40", "gather": "--workload gather --calls 40"}[workload]
+    pflags = {"wide": "--workload wide --calls 8", "gather": "--workload gather --calls 8"}[workload]
+    title = {"wide": "small-batch products 14336x4096 and 4096x14336 at M = 2, 4, 6, 8 (4-bit gs64)",
+             "gather": "Mixtral-shaped expert gather, 8 planes of 14336x4096 (W1) and 4096x14336 (W2), "
+                       "32 pairs (4-bit gs64)"}[workload]
+    lines = [f"# rocprofv3 kernel statistics: {title}", "", "Commands (from the repository root):", "",
+             f"    rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- python3 bench.py {flags}",
+             f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- python3 bench.py {pflags}",
+             f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o bench -- python3 bench.py {pflags}", "",
+             "Kernels `qmv_mfma_kernel` and `gather_mfma_kernel` run on the matrix cores (template arguments: "
+             "16-row tiles per band, LDS copy of x); `qmv_kernel` is the VALU form.", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        if "agq::" in r["Name"]:
+            lines.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+
+    def counter(d, cname):
+        out = {}
+        for r in _read_csv(d, "counter_collection.csv"):
+            if r["Counter_Name"] == cname and "agq::" in r["Kernel_Name"]:
+                out.setdefault((r["Kernel_Name"].split("(")[0], int(r["Grid_Size"])), []).append(
+                    float(r["Counter_Value"]))
+        return out
+
+    fetch, write = counter(fetch_dir, "FETCH_SIZE"), counter(write_dir, "WRITE_SIZE")
+    lines += ["", "HBM bytes per launch (FETCH_SIZE x %.4f + WRITE_SIZE x %.4f, KiB scaled to bytes; the "
+              "factors come from the lm_head counter calibration):" % (cal["fetch_scale"], cal["write_scale"]), "",
+              "| kernel | grid (threads) | launches | HBM MB per launch |", "|---|---|---|---|"]
+    for k in sorted(fetch, key=lambda k: (k[0], k[1])):
+        f_kib = statistics.median(fetch[k])
+        w_kib = statistics.median(write.get(k, [0.0]))
+        mb = (f_kib * cal["fetch_scale"] + w_kib * cal["write_scale"]) * 1024 / 1e6
+        lines.append(f"| `{k[0].replace('void agq::', '')}` | {k[1]} | {len(fetch[k])} | {mb:.2f} |")
+    out = os.path.join(ROOT, "profiles", f"qmv_{workload}_kernel_stats_and_traffic.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def main():
     args = parse()
+    if args.write_profiles and args.workload != "llama":
+        write_workload_profile(args.workload, *args.write_profiles)
+        return
+    if args.workload != "llama":
+        other_workload(args)
+        return
     if args.write_profiles:
         write_profiles(*args.write_profiles)
         return
