@@ -176,14 +176,14 @@ agq_status launch_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t expert
 agq_status launch_mfma_plan(int64_t M, int64_t N, int64_t K, int64_t experts, agq::MfmaPlan *plan,
                             const void **sym) {
     agq::mfma_shape(N, K, experts, plan);
-    if (experts == 0) agq::mfma_x_lds(M, K, plan);
+    agq::mfma_x_lds(M, K, experts, M, plan);  // (gather: M is the pair count P)
     int cus = 0, dev = 0;
     agq_status st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
     *sym = agq::mfma_kernel(plan->T, experts > 0, plan->x_lds_bytes > 0);
     if (!*sym) return fail(AGQ_ENOTSUP, "no matrix-core kernel for %d tiles", plan->T);
     int64_t waves = 0;
-    st = resident_waves(*sym, plan->threads, (size_t)plan->x_lds_bytes, cus, dev, &waves);
+    st = resident_waves(*sym, plan->threads, (size_t)plan->lds_bytes, cus, dev, &waves);
     if (st != AGQ_OK) return st;
     agq::mfma_grid(waves, experts, plan);
     return AGQ_OK;
@@ -194,7 +194,7 @@ void export_mfma_plan(const agq::MfmaPlan &p, int64_t K, agq_plan *out) {
     out->bits = 4;
     out->chunks_per_row = (int32_t)(K / 32);
     out->cpt = 0;
-    out->mw = 16;
+    out->mw = p.pass_rows;
     out->rows_per_iter = 16 * p.T;
     out->stages = agq::kMfmaRing;
     out->waves_per_group = p.S;
@@ -224,6 +224,7 @@ agq::MfmaArgs make_mfma_args(const void *x, const uint32_t *w, const void *s, co
     a.S = p.S;
     a.SPW = p.SPW;
     a.BPG = p.BPG;
+    a.XCAP = p.pass_rows;
     return a;
 }
 
@@ -285,7 +286,7 @@ agq_status dense_product(const void *x, const uint32_t *w, const void *s, const 
         st = launch_mfma_plan(M, N, K, 0, &mp, &sym);
         if (st != AGQ_OK) return st;
         agq::MfmaArgs a = make_mfma_args(x, w, s, b, y, N, K, (int)M, mp);
-        return launch(sym, dim3((unsigned)mp.groups), dim3(mp.threads), (size_t)mp.x_lds_bytes, &a, stream);
+        return launch(sym, dim3((unsigned)mp.groups), dim3(mp.threads), (size_t)mp.lds_bytes, &a, stream);
     }
     agq::Plan plan;
     if (agq::plan_shape(M, K, bits, 0, &plan) != AGQ_OK)  // host-only check before any HIP call
@@ -344,14 +345,15 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
     if (agq::mfma_eligible(8, K, bits, E, R)) {
         agq::MfmaPlan mp;
         const void *sym = nullptr;
-        st = launch_mfma_plan(8, N, K, E, &mp, &sym);
+        st = launch_mfma_plan(P, N, K, E, &mp, &sym);
         if (st != AGQ_OK) return st;
         agq::MfmaArgs a = make_mfma_args(x, w, scales, biases, y, N, K, (int)P, mp);
         a.lhs = lhs_indices;
         a.rhs = rhs_indices;
         a.R_x = (int32_t)R;
         a.E = (int32_t)E;
-        return launch(sym, dim3((unsigned)mp.groups, (unsigned)E), dim3(mp.threads), 0, &a, stream);
+        return launch(sym, dim3((unsigned)mp.groups, (unsigned)E), dim3(mp.threads), (size_t)mp.lds_bytes, &a,
+                      stream);
     }
     agq::Plan plan;
     if (agq::plan_shape(8, K, bits, E, &plan) != AGQ_OK)  // host-only check before any HIP call
@@ -400,7 +402,7 @@ agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group
     if (agq::mfma_eligible(M, K, bits, experts, experts ? 1 : M)) {
         agq::MfmaPlan mp;
         agq::mfma_shape(N, K, experts, &mp);
-        if (experts == 0) agq::mfma_x_lds(M, K, &mp);
+        agq::mfma_x_lds(M, K, experts, experts ? 32 : M, &mp);  // (gather plans assume 32 pairs)
         agq::mfma_grid((int64_t)num_cus * waves_per_cu, experts, &mp);
         export_mfma_plan(mp, K, out);
         return AGQ_OK;

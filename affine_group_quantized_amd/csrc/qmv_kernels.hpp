@@ -49,6 +49,8 @@ struct MfmaArgs {
     int32_t S;            // waves per block (K split)
     int32_t SPW;          // 128-column segments per wave (a multiple of 4)
     int32_t BPG;          // bands each block walks
+    int32_t XCAP;         // gather: pairs per pass (the rows of the LDS copy of x, or 16 without one)
+    int32_t pad_;
 };
 
 // Kernel symbol for (bits, activation rows per pass, chunks per lane, weight
@@ -57,7 +59,7 @@ struct MfmaArgs {
 const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather);
 const void *dequant_kernel_sym(int bits);
 // Matrix-core kernel with bands of 16*tiles rows (tiles 1 or 2), activations
-// from an LDS copy (x_lds, dense only) or from global memory, or NULL.
+// from an LDS copy (x_lds) or from global memory, or NULL.
 const void *mfma_kernel(int tiles, bool gather, bool x_lds);
 
 }  // namespace agq

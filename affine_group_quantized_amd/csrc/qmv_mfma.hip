@@ -256,10 +256,11 @@ __device__ __forceinline__ void finish_band(f32x4 (&acc)[T], float *red, int S, 
 // does not wait for the codes), and the waves read their operands there:
 // 4 LDS reads per segment instead of 4 buffer loads that mostly address rows
 // past the pass.
+// xrows: the x row of each pass row (gather), or nullptr for rows 0..mrows-1.
 template <int T, bool XL, typename Out>
 __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, const Lanes &ln,
-                                          __amdgpu_buffer_rsrc_t xr, int mrows, const Out &out, int64_t rg,
-                                          int64_t groups, float *red) {
+                                          __amdgpu_buffer_rsrc_t xr, uint32_t xend, int mrows, const uint32_t *xrows,
+                                          const Out &out, int64_t rg, int64_t groups, float *red) {
     const int lane = threadIdx.x & 63;
     const int wig = wave_id();
     const int S = a.S, SPW = a.SPW;
@@ -273,16 +274,22 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // LDS copy of x: source word q (16 bytes) is row q / (K/8), 8-column word
-    // c8 = q % (K/8), at byte q*16 of the dense rows.
+    // LDS copy of x: source word q (16 bytes) is pass row q / (K/8), 8-column
+    // word c8 = q % (K/8): byte q*16 of dense rows, or of x row xrows[q / (K/8)].
+    // Words past the pass read from xend, the end of the x range (zeros).
     const uint32_t words = (uint32_t)mrows * (uint32_t)(a.K / 8);
     const int per = (int)((words + blockDim.x - 1) / blockDim.x);  // <= kXPer (host check)
     u32x4 xraw[XL ? kXPer : 1];
     if constexpr (XL) {
+        const uint32_t wpr = (uint32_t)(a.K / 8);
 #pragma unroll
         for (int k = 0; k < kXPer; ++k)
-            if (k < per)  // uniform branch
-                xraw[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, (threadIdx.x + k * blockDim.x) * 16u, 0, 0);
+            if (k < per) {  // uniform branch
+                const uint32_t q = threadIdx.x + k * blockDim.x;
+                uint32_t off = q * 16u;
+                if (xrows) off = q < words ? (xrows[q / wpr] * wpr + q % wpr) * 16u : xend;
+                xraw[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+            }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -397,19 +404,23 @@ __global__ __launch_bounds__(512) void qmv_mfma_kernel(MfmaArgs a) {
     // Lanes of rows m >= M start at the descriptor's end and read zeros.
     const Lanes ln = lane_consts(a, m * (uint32_t)a.K * 2u);
     const Band bd{reinterpret_cast<const uint8_t *>(a.w), a.s, a.b, a.N, (uint32_t)(a.K / 2), a.G};
-    mfma_pass<T, XL>(a, bd, ln, range_of(a.x, xbytes), a.M, RowsOut{a.y, a.N}, blockIdx.x, gridDim.x, red);
+    mfma_pass<T, XL>(a, bd, ln, range_of(a.x, xbytes), xbytes, a.M, nullptr, RowsOut{a.y, a.N}, blockIdx.x,
+                     gridDim.x, red);
 }
 
 // blockIdx.y = expert plane e. The pairs routed to e are listed in LDS and
-// taken 16 per pass, so each used plane streams once per 16 pairs; blocks of
-// planes without pairs exit before reading weights. Blocks of plane 0 also
-// write NaN rows for pairs whose indices are out of range.
-template <int T>
+// taken a.XCAP per pass (16, or the rows of the block's LDS copy of x with
+// XL), so each used plane streams once per pass; blocks of planes without
+// pairs exit before reading weights. Blocks of plane 0 also write NaN rows for
+// pairs whose indices are out of range. Dynamic LDS: the copy of x (XL),
+// then the pair list (P uint16, padded to 16 bytes) and their x rows (P uint32).
+template <int T, bool XL>
 __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
     __shared__ float red[Red<T>::FLOATS];
-    __shared__ uint16_t plist[kMaxPairs];
-    __shared__ uint32_t xlist[kMaxPairs];
     __shared__ int pcount;
+    const uint32_t xl_words = XL ? (uint32_t)a.XCAP * (uint32_t)(a.K / 8) + 1u : 0u;
+    uint16_t *plist = reinterpret_cast<uint16_t *>(g_mfma_x + xl_words);
+    uint32_t *xlist = reinterpret_cast<uint32_t *>(g_mfma_x + xl_words + ((uint32_t)a.M * 2u + 15u) / 16u);
     const int lane = threadIdx.x & 63;
     const int wig = wave_id();
     const uint32_t e = blockIdx.y;
@@ -471,20 +482,25 @@ __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
     const int64_t plane = (int64_t)e * a.N;
     const Band bd{reinterpret_cast<const uint8_t *>(a.w) + plane * (a.K / 2), a.s + plane * a.G, a.b + plane * a.G,
                   a.N, (uint32_t)(a.K / 2), a.G};
-    for (int base = 0; base < count; base += 16) {
-        const int me = count - base < 16 ? count - base : 16;
+    const int ps = a.XCAP;
+    for (int base = 0; base < count; base += ps) {
+        const int me = count - base < ps ? count - base : ps;
         const int m = lane & 15;
         const Lanes ln = lane_consts(a, m < me ? xlist[base + m] * (uint32_t)a.K * 2u : xbytes);
-        mfma_pass<T, false>(a, bd, ln, xr, me, PairsOut{a.y, a.N, plist + base}, rg, groups, red);
+        mfma_pass<T, XL>(a, bd, ln, xr, xbytes, me, xlist + base, PairsOut{a.y, a.N, plist + base}, rg, groups,
+                         red);
     }
 }
 
 const void *mfma_kernel(int tiles, bool gather, bool x_lds) {
     if (gather) {
-        if (x_lds) return nullptr;
-        return tiles == 1 ? reinterpret_cast<const void *>(&gather_mfma_kernel<1>)
-             : tiles == 2 ? reinterpret_cast<const void *>(&gather_mfma_kernel<2>)
-                          : nullptr;
+        switch (tiles * 2 + (x_lds ? 1 : 0)) {
+            case 2: return reinterpret_cast<const void *>(&gather_mfma_kernel<1, false>);
+            case 3: return reinterpret_cast<const void *>(&gather_mfma_kernel<1, true>);
+            case 4: return reinterpret_cast<const void *>(&gather_mfma_kernel<2, false>);
+            case 5: return reinterpret_cast<const void *>(&gather_mfma_kernel<2, true>);
+        }
+        return nullptr;
     }
     switch (tiles * 2 + (x_lds ? 1 : 0)) {
         case 2: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, false>);

@@ -147,15 +147,16 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
     if mfma:
         # Matrix cores: bands of 16 or 32 rows, up to 4 waves splitting K into equal
         # slices of whole 4-segment (512-column) blocks, one band group per block.
-        assert R in (16, 32) and p["mw"] == 16 and p["cpt"] == 0 and p["stages"] == 4
+        assert R in (16, 32) and p["cpt"] == 0 and p["stages"] == 4
         S = p["waves_per_group"]
         assert 1 <= S <= 4 and (K // 512) % S == 0
         assert all((K // 512) % s for s in range(S + 1, 5))                 # the most waves that divide
-        if experts:
-            assert p["x_lds_bytes"] == 0
-        else:   # LDS copy of x when it fits in 64 KB and 16 words per thread
-            fits = M * K * 2 <= 65536 and -(-M * K * 2 // 16 // (64 * S)) <= 16
-            assert p["x_lds_bytes"] == (M * K * 2 + 16 if fits else 0)
+        def fits(rows):   # LDS copy of x when it fits in 64 KB and 16 words per thread
+            return rows * K * 2 <= 65536 and -(-rows * K * 2 // 16 // (64 * S)) <= 16
+        if experts:       # passes of 16 pairs, operands from L2
+            assert p["mw"] == 16 and p["x_lds_bytes"] == 0
+        else:
+            assert p["x_lds_bytes"] == (M * K * 2 + 16 if fits(M) else 0)
         assert p["groups_per_block"] == 1 and p["threads_per_block"] == 64 * S
         assert RPG % R == 0
         return

@@ -285,30 +285,34 @@ def test_deterministic_and_power_of_two_scaling(bits, M):
     assert y4.shape == y1.shape
 
 
-def test_row_permutation_equivariance():
+@pytest.mark.parametrize("M", [1, 8])   # VALU and matrix cores
+def test_row_permutation_equivariance(M):
     N, K = 1000, 4096
     d = si.draw_quantized_weight(11, 4, N, K, 4)
-    x = bf16_dev(si.draw_activations(11, 1, 1, K))[0]
+    x = bf16_dev(si.draw_activations(11, M, M, K))
     perm = np.random.default_rng(2).permutation(N)
     w, s, b = dev_weight(d)
     wp, sp, bp = dev_weight({k: v[perm] for k, v in d.items()})
-    progress("row permutation")
-    y = bf16_bits_host(agq.qmv(x, w, s, b))
-    yp = bf16_bits_host(agq.qmv(x, wp, sp, bp))
-    assert np.array_equal(yp, y[perm])
+    progress(f"row permutation M={M}")
+    f = (lambda *a: agq.qmv(x[0], *a)[None]) if M == 1 else (lambda *a: agq.qmv_wide(x, *a))
+    y = bf16_bits_host(f(w, s, b))
+    yp = bf16_bits_host(f(wp, sp, bp))
+    assert np.array_equal(yp, y[:, perm])
 
 
-def test_output_guard_region_untouched():
+@pytest.mark.parametrize("M", [3, 6])   # VALU and matrix cores
+def test_output_guard_region_untouched(M):
     N, K = 1003, 4096
     d = si.draw_quantized_weight(12, 4, N, K, 4)
     w, s, b = dev_weight(d)
-    x = bf16_dev(si.draw_activations(12, 1, 3, K))
-    buf = torch.full((3 * N + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
-    sentinel = bf16_bits_host(buf[3 * N:]).copy()
-    progress("guard region")
-    agq.qmv_wide(x, w, s, b, out=buf[:3 * N].view(3, N))
+    x = bf16_dev(si.draw_activations(12, 1, M, K))
+    buf = torch.full((M * N + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    sentinel = bf16_bits_host(buf[M * N:]).copy()
+    progress(f"guard region M={M}")
+    agq.qmv_wide(x, w, s, b, out=buf[:M * N].view(M, N))
     torch.cuda.synchronize()
-    assert np.array_equal(bf16_bits_host(buf[3 * N:]), sentinel)
+    assert np.array_equal(bf16_bits_host(buf[M * N:]), sentinel)
+    assert not np.any(np.isnan(bf16_host(buf[:M * N])))
 
 
 def test_gather_matches_per_pair_qmv_and_identity_forms():
@@ -376,8 +380,8 @@ def test_gather_passes_through_the_block_copy_of_x():
 
 @pytest.mark.parametrize("N", [1, 5, 9])
 def test_gather_tiny_planes_with_wide_passes(N):
-    """Planes of a few rows, single-wave row groups, and passes of more than four pairs
-    (which walk one row per iteration while shorter passes walk two)."""
+    """Planes of a few rows (one ragged 16-row tile on the matrix cores) with six pairs
+    on one plane and one on the other."""
     E, K, R = 2, 1024, 8
     planes = [si.draw_quantized_weight(22, 10 * N + e, N, K, 4) for e in range(E)]
     st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
@@ -392,21 +396,22 @@ def test_gather_tiny_planes_with_wide_passes(N):
     check_close(y, y_ref, A, f"gather N={N}")
 
 
-def test_gather_out_of_range_indices_give_nan_rows():
+@pytest.mark.parametrize("bits", [8, 4])   # VALU and matrix-core gathers
+def test_gather_out_of_range_indices_give_nan_rows(bits):
     E, N, K, R = 3, 130, 1024, 4
-    planes = [si.draw_quantized_weight(15, e, N, K, 8) for e in range(E)]
+    planes = [si.draw_quantized_weight(15, e, N, K, bits) for e in range(E)]
     st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
     x = si.draw_activations(15, 99, R, K)
     lhs = np.array([0, 9, 2, 3], np.uint32)     # 9 >= R
     rhs = np.array([1, 0, 7, 2], np.uint32)     # 7 >= E
     progress("gather invalid indices")
     y = agq.gather_qmv(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
-                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs), bits=8)
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs), bits=bits)
     torch.cuda.synchronize()
     yh = bf16_host(y)
     assert np.all(np.isnan(yh[1])) and np.all(np.isnan(yh[2]))
     ok = np.array([0, 3])
-    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs[ok], rhs[ok], K, 8)
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs[ok], rhs[ok], K, bits)
     check_close(y[torch.as_tensor(ok, device=y.device)], y_ref, A, "valid pairs")
 
 
@@ -451,47 +456,52 @@ def test_graph_replays_match_eager():
     d = si.draw_quantized_weight(17, 1, N, K, 4)
     planes = [si.draw_quantized_weight(17, 2 + e, N, K, 4) for e in range(E)]
     st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
-    x = si.draw_activations(17, 9, 4, K)
+    x = si.draw_activations(17, 9, 8, K)
     w, s, b = dev_weight(d)
     ws, ss, bs = u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"])
     xd = bf16_dev(x)
+    x4 = xd[:4].contiguous()
     rhs = u32_dev(np.array([2, 0, 2, 1, 0], np.uint32))
     lhs = u32_dev(np.array([0, 3, 1, 1, 2], np.uint32))
     y1 = torch.empty(N, dtype=torch.bfloat16, device="cuda")
     y4 = torch.empty((4, N), dtype=torch.bfloat16, device="cuda")
+    y8 = torch.empty((8, N), dtype=torch.bfloat16, device="cuda")
     yg = torch.empty((P, N), dtype=torch.bfloat16, device="cuda")
+    outs = (y1, y4, y8, yg)
 
     def run():
         agq.qmv(xd[0], w, s, b, out=y1)
-        agq.qmv_wide(xd, w, s, b, out=y4)
+        agq.qmv_wide(x4, w, s, b, out=y4)     # VALU
+        agq.qmv_wide(xd, w, s, b, out=y8)     # matrix cores
         agq.gather_qmv(xd, ws, ss, bs, rhs_indices=rhs, lhs_indices=lhs, out=yg)
 
-    progress("graph capture of qmv, qmv_wide, gather_qmv")
+    progress("graph capture of qmv, qmv_wide (M = 4 and 8), gather_qmv")
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         run()  # eager, also primes the launch-plan caches outside capture
     torch.cuda.synchronize()
-    eager = [bf16_bits_host(t).copy() for t in (y1, y4, yg)]
+    eager = [bf16_bits_host(t).copy() for t in outs]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
         run()
     torch.cuda.synchronize()
     for rep in range(4):
-        for t in (y1, y4, yg):
+        for t in outs:
             t.zero_()
         agq.qmv(xd[1], w, s, b)  # unrelated eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for got, want in zip((y1, y4, yg), eager):
+        for got, want in zip(outs, eager):
             assert np.array_equal(bf16_bits_host(got), want), f"replay {rep}"
     y_ref, A = oracle.qmv(x[:1], d["w"], d["scales"], d["biases"], K, 4, rows=np.arange(0, N, 11))
     check_close(y1[None][:, torch.arange(0, N, 11, device="cuda")], y_ref, A, "graph qmv")
 
 
-def test_gather_at_the_pair_limit():
+@pytest.mark.parametrize("K", [128, 512])   # VALU and matrix-core gathers
+def test_gather_at_the_pair_limit(K):
     """4096 pairs (the most one call takes) over 3 planes, with repeated x rows."""
-    E, N, K, R, P = 3, 96, 128, 64, 4096
+    E, N, R, P = 3, 96, 64, 4096
     planes = [si.draw_quantized_weight(18, e, N, K, 4) for e in range(E)]
     st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
     x = si.draw_activations(18, 99, R, K)
