@@ -241,7 +241,10 @@ inline bool wants_deep(int64_t N, int64_t resident_waves, int S, int64_t experts
 #define AGQ_MFMA_TILES 0  // 16-row tiles per band: 1, 2, or 0 to choose from the shape
 #endif
 constexpr int kMfmaMinRows = AGQ_MFMA_MIN_ROWS;
-constexpr int kMfmaRing = 4;       // 128-column segments in flight per wave (one block of scales)
+#ifndef AGQ_MFMA_RING
+#define AGQ_MFMA_RING 4  // 128-column segments in flight per wave: 4 or 8 (scales load in blocks of 4)
+#endif
+constexpr int kMfmaRing = AGQ_MFMA_RING;
 constexpr int kMfmaMaxWaves = 8;   // waves per block (LDS of the K-split combine is sized for it)
 #ifndef AGQ_MFMA_MAX_S
 #define AGQ_MFMA_MAX_S 4  // smaller blocks pack two or more per compute unit (8: 10-35% slower)
@@ -272,7 +275,7 @@ struct MfmaPlan {
 // activation rows, or the gather (whose passes take up to 16 pairs). Byte
 // offsets into x are 32-bit: the activation block must stay below 2 GiB.
 inline bool mfma_eligible(int64_t M, int64_t K, int bits, int64_t experts, int64_t x_rows) {
-    if (kMfmaMinRows <= 0 || bits != 4 || K % 512 != 0) return false;
+    if (kMfmaMinRows <= 0 || bits != 4 || K % (128 * kMfmaRing) != 0) return false;
     if (x_rows * K * 2 + K * 2 >= (int64_t(1) << 31)) return false;
     return experts > 0 || M >= kMfmaMinRows;
 }
@@ -281,7 +284,7 @@ inline bool mfma_eligible(int64_t M, int64_t K, int bits, int64_t experts, int64
 // evenly; bands of two tiles unless that leaves fewer than one band-wave per
 // SIMD of the device.
 inline void mfma_shape(int64_t N, int64_t K, int64_t experts, MfmaPlan *p) {
-    const int nseg = (int)(K / 128), blocks4 = nseg / kMfmaRing;
+    const int nseg = (int)(K / 128), blocks4 = nseg / kMfmaRing;  // whole rings per row
     int S = 1;
     for (int s = kMfmaMaxS; s >= 1; --s)
         if (blocks4 % s == 0) {

@@ -57,7 +57,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
-constexpr int kRing = kMfmaRing;  // segments in flight per wave (one block of scales)
+constexpr int kRing = kMfmaRing;  // segments in flight per wave
+constexpr int kSB = 4;            // segments per block of scales (8 groups, 16 bytes per row)
+// Line loads (LL): codes in whole 128-byte lines, 8 rows per load, moved to
+// their lanes through a 2 KB LDS buffer per wave and tile; otherwise 64-byte
+// quarters of 16 rows per load. Kernels that read x from L2 use line loads
+// (gather W1 / W2: 78.2 / 76.7 -> 73.1 / 66.0 us; 4096x14336 at M = 8: 16.0
+// -> 14.7 us); kernels with the LDS copy of x do not, since the extra LDS
+// costs resident blocks (14336x4096 at M = 8: 14.1 against 15.8 us).
 constexpr uint32_t kOnes = 0x3F803F80u;  // bfloat16 pair (1, 1)
 constexpr int kRsrcW3 = 0x00020000;      // raw buffer, 32-bit data format
 // Cache policy of the code, scale and bias loads. Each load reads half of a
@@ -119,6 +126,9 @@ struct ScaleBlock {
 // Per-wave constants of a pass.
 struct Lanes {
     uint32_t woff;      // byte offset of the lane's code quarter within a tile: row (l%16), quarter l/16
+    uint32_t wlo;       // line loads: byte offset of the lane's 16 bytes in rows 0-7 of a tile's 128-byte window
+    uint32_t wslot[2];  // line loads: LDS slots (16-byte units) the lane writes its rows 0-7 and 8-15 data to
+    uint32_t rslot[2];  // line loads: LDS slots the lane reads segments 0 and 1 of the window from
     uint32_t soff;      // byte offset of the lane's scale row within a tile
     uint32_t xoff[4];   // byte offsets of the lane's activation words for the 4 slots, segment 0
 };
@@ -132,7 +142,13 @@ struct Band {
     int32_t G;
 };
 
-template <int T, bool SCALES, bool XL>
+// Codes of one segment per tile. Quarter loads (LL false): the lane's
+// own 16 bytes, row l%16 and quarter l/16, 64 bytes from each of 16 rows per
+// instruction. Line loads: units of a segment pair take turns; the even unit
+// reads rows 0-7 and the odd one rows 8-15 of the pair's 128-byte window (8
+// whole lines per instruction), and compute_pair moves the bytes to their
+// lanes through LDS.
+template <int T, bool SCALES, bool XL, bool LL>
 __device__ __forceinline__ void load_seg(Seg<T, XL> &u, ScaleBlock<T> &sb, const Band &bd, const Lanes &ln,
                                          __amdgpu_buffer_rsrc_t xr, int64_t band, int seg) {
 #pragma unroll
@@ -141,8 +157,13 @@ __device__ __forceinline__ void load_seg(Seg<T, XL> &u, ScaleBlock<T> &sb, const
         const int64_t left = bd.N - row0;
         const uint32_t rows = left <= 0 ? 0u : left >= 16 ? 16u : (uint32_t)left;
         const int64_t r0 = left <= 0 ? 0 : row0;
-        u.w[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.w + r0 * bd.rowbytes, rows * bd.rowbytes),
-                                                       ln.woff, seg * 64, kWPolicy);
+        if constexpr (LL)
+            u.w[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.w + r0 * bd.rowbytes, rows * bd.rowbytes),
+                                                           ln.wlo + ((uint32_t)seg & 1u) * 8u * bd.rowbytes,
+                                                           (seg >> 1) * 128, kWPolicy);
+        else
+            u.w[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.w + r0 * bd.rowbytes, rows * bd.rowbytes),
+                                                           ln.woff, seg * 64, kWPolicy);
         if constexpr (SCALES) {
             const uint32_t sbytes = rows * (uint32_t)bd.G * 2u;
             sb.s[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.s + r0 * bd.G, sbytes), ln.soff, seg * 4,
@@ -160,8 +181,9 @@ __device__ __forceinline__ void load_seg(Seg<T, XL> &u, ScaleBlock<T> &sb, const
 // Fold one segment into the band's accumulators. sd/bd: the bf16 scale and
 // bias pairs of the segment's two groups for the lane's row of each tile.
 template <int T, bool XL>
-__device__ __forceinline__ void compute_seg(const Seg<T, XL> &u, const uint32_t (&sd)[T], const uint32_t (&bd)[T],
-                                            f32x4 (&acc)[T], uint32_t xbase, uint32_t xmult, int seg) {
+__device__ __forceinline__ void compute_seg(const Seg<T, XL> &u, const u32x4 (&w)[T], const uint32_t (&sd)[T],
+                                            const uint32_t (&bd)[T], f32x4 (&acc)[T], uint32_t xbase, uint32_t xmult,
+                                            int seg) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
     u32x4 a[4];
@@ -177,8 +199,8 @@ __device__ __forceinline__ void compute_seg(const Seg<T, XL> &u, const uint32_t 
     const f32x4 x1 = mfma(a[3], ones, mfma(a[2], ones, z));
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        const auto p02 = __builtin_amdgcn_permlane32_swap(u.w[t].x, u.w[t].z, false, false);
-        const auto p13 = __builtin_amdgcn_permlane32_swap(u.w[t].y, u.w[t].w, false, false);
+        const auto p02 = __builtin_amdgcn_permlane32_swap(w[t].x, w[t].z, false, false);
+        const auto p13 = __builtin_amdgcn_permlane32_swap(w[t].y, w[t].w, false, false);
         const f32x4 d0 = mfma(a[1], code_pairs(p13[0]), mfma(a[0], code_pairs(p02[0]), z));
         const f32x4 d1 = mfma(a[3], code_pairs(p13[1]), mfma(a[2], code_pairs(p02[1]), z));
         const float s0 = bf16_lo(sd[t]), s1 = bf16_hi(sd[t]);
@@ -192,6 +214,37 @@ __device__ __forceinline__ void compute_seg(const Seg<T, XL> &u, const uint32_t 
             v = fmaf(c1, x1[r], v);
             acc[t][r] = v;
         }
+    }
+}
+
+// Segments p and p+1 (a 128-byte window) of every tile. With line loads, the
+// even unit holds rows 0-7 and the odd one rows 8-15 of the window; each
+// lane writes both to the wave's LDS buffer and reads back its own row and
+// quarter of either segment (the layout quarter loads give directly). Slots
+// are XOR-swizzled so that neither the writes nor the reads conflict.
+// A wave's LDS accesses complete in order, so the buffer needs no barrier.
+template <int T, bool XL, bool LL>
+__device__ __forceinline__ void compute_pair(const Seg<T, XL> &u0, const Seg<T, XL> &u1, const uint32_t (&sd0)[T],
+                                             const uint32_t (&bd0)[T], const uint32_t (&sd1)[T],
+                                             const uint32_t (&bd1)[T], f32x4 (&acc)[T], uint32_t xbase,
+                                             uint32_t xmult, int seg, const Lanes &ln, u32x4 *wt) {
+    if constexpr (LL) {
+        u32x4 w0[T], w1[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            wt[t * 128 + ln.wslot[0]] = u0.w[t];
+            wt[t * 128 + ln.wslot[1]] = u1.w[t];
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            w0[t] = wt[t * 128 + ln.rslot[0]];
+            w1[t] = wt[t * 128 + ln.rslot[1]];
+        }
+        compute_seg<T, XL>(u0, w0, sd0, bd0, acc, xbase, xmult, seg);
+        compute_seg<T, XL>(u1, w1, sd1, bd1, acc, xbase, xmult, seg + 1);
+    } else {
+        compute_seg<T, XL>(u0, u0.w, sd0, bd0, acc, xbase, xmult, seg);
+        compute_seg<T, XL>(u1, u1.w, sd1, bd1, acc, xbase, xmult, seg + 1);
     }
 }
 
@@ -257,19 +310,20 @@ __device__ __forceinline__ void finish_band(f32x4 (&acc)[T], float *red, int S, 
 // 4 LDS reads per segment instead of 4 buffer loads that mostly address rows
 // past the pass.
 // xrows: the x row of each pass row (gather), or nullptr for rows 0..mrows-1.
-template <int T, bool XL, typename Out>
+template <int T, bool XL, bool LL, typename Out>
 __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, const Lanes &ln,
                                           __amdgpu_buffer_rsrc_t xr, uint32_t xend, int mrows, const uint32_t *xrows,
-                                          const Out &out, int64_t rg, int64_t groups, float *red) {
+                                          const Out &out, int64_t rg, int64_t groups, float *red, u32x4 *wt_all) {
     const int lane = threadIdx.x & 63;
     const int wig = wave_id();
     const int S = a.S, SPW = a.SPW;
     const int seg0 = wig * SPW;
-    const int turns = a.BPG * (SPW / kRing);  // rings of 4 segments over the walk
+    const int turns = a.BPG * (SPW / kRing);  // turns of the ring over the walk
     const int tpb = SPW / kRing;               // turns per band
+    u32x4 *wt = wt_all + wig * T * 128;        // the wave's buffer for line loads (2 KB per tile)
 
     Seg<T, XL> buf[kRing];
-    ScaleBlock<T> next, cur;
+    ScaleBlock<T> next[kRing / kSB], cur;
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -294,9 +348,13 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
     __builtin_amdgcn_sched_barrier(0);
 
     // Turn j covers segments seg0 + 4*(j % tpb) .. +3 of band rg + (j / tpb) * groups.
-    load_seg<T, true, XL>(buf[0], next, bd, ln, xr, rg, seg0);
 #pragma unroll
-    for (int p = 1; p < kRing; ++p) load_seg<T, false, XL>(buf[p], next, bd, ln, xr, rg, seg0 + p);
+    for (int p = 0; p < kRing; ++p) {
+        if (p % kSB == 0)
+            load_seg<T, true, XL, LL>(buf[p], next[p / kSB], bd, ln, xr, rg, seg0 + p);
+        else
+            load_seg<T, false, XL, LL>(buf[p], next[0], bd, ln, xr, rg, seg0 + p);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     uint32_t xbase = 0, xmult = 0;
@@ -327,19 +385,23 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
         const int64_t nband = rg + (int64_t)(jn / tpb) * groups;
         const int nseg = seg0 + kRing * (jn % tpb);
 #pragma unroll
-        for (int p = 0; p < kRing; ++p) {
-            if (p == 0) cur = next;
-            uint32_t sd[T], bdw[T];
+        for (int p = 0; p < kRing; p += 2) {
+            if (p % kSB == 0) cur = next[p / kSB];
+            uint32_t sd0[T], bd0[T], sd1[T], bd1[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                sd[t] = dword(cur.s[t], p);
-                bdw[t] = dword(cur.b[t], p);
+                sd0[t] = dword(cur.s[t], p % kSB);
+                bd0[t] = dword(cur.b[t], p % kSB);
+                sd1[t] = dword(cur.s[t], (p + 1) % kSB);
+                bd1[t] = dword(cur.b[t], (p + 1) % kSB);
             }
-            compute_seg<T, XL>(buf[p], sd, bdw, acc, xbase, xmult, seg0 + kRing * (j % tpb) + p);
-            if (p == 0)
-                load_seg<T, true, XL>(buf[0], next, bd, ln, xr, nband, nseg);
+            compute_pair<T, XL, LL>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, xbase, xmult,
+                                seg0 + kRing * (j % tpb) + p, ln, wt);
+            if (p % kSB == 0)
+                load_seg<T, true, XL, LL>(buf[p], next[p / kSB], bd, ln, xr, nband, nseg + p);
             else
-                load_seg<T, false, XL>(buf[p], next, bd, ln, xr, nband, nseg + p);
+                load_seg<T, false, XL, LL>(buf[p], next[0], bd, ln, xr, nband, nseg + p);
+            load_seg<T, false, XL, LL>(buf[p + 1], next[0], bd, ln, xr, nband, nseg + p + 1);
             __builtin_amdgcn_sched_barrier(0);
         }
         if ((j + 1) % tpb == 0) finish_band<T>(acc, red, S, wig, lane, band, bi & 1, bd.N, mrows, out);
@@ -348,15 +410,18 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
         const int bi = j / tpb;
         const int64_t band = rg + (int64_t)bi * groups;
 #pragma unroll
-        for (int p = 0; p < kRing; ++p) {
-            if (p == 0) cur = next;
-            uint32_t sd[T], bdw[T];
+        for (int p = 0; p < kRing; p += 2) {
+            if (p % kSB == 0) cur = next[p / kSB];
+            uint32_t sd0[T], bd0[T], sd1[T], bd1[T];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                sd[t] = dword(cur.s[t], p);
-                bdw[t] = dword(cur.b[t], p);
+                sd0[t] = dword(cur.s[t], p % kSB);
+                bd0[t] = dword(cur.b[t], p % kSB);
+                sd1[t] = dword(cur.s[t], (p + 1) % kSB);
+                bd1[t] = dword(cur.b[t], (p + 1) % kSB);
             }
-            compute_seg<T, XL>(buf[p], sd, bdw, acc, xbase, xmult, seg0 + kRing * (j % tpb) + p);
+            compute_pair<T, XL, LL>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, xbase, xmult,
+                                seg0 + kRing * (j % tpb) + p, ln, wt);
         }
         finish_band<T>(acc, red, S, wig, lane, band, bi & 1, bd.N, mrows, out);
     }
@@ -370,6 +435,17 @@ __device__ __forceinline__ Lanes lane_consts(const MfmaArgs &a, uint32_t xrow) {
     const uint32_t g = (uint32_t)lane >> 4, nl = (uint32_t)lane & 15u;
     Lanes ln;
     ln.woff = nl * (uint32_t)(a.K / 2) + 16u * g;
+    // Line loads: the lane reads row l/8 (or 8 + l/8), bytes 16*(l%8) of a
+    // 128-byte window: segment sg = (l%8)/4, quarter q = l%4. The LDS slot of
+    // (row, segment, quarter) is segment*64 + quarter*16 + (row ^ 2*(segment*4 + quarter)).
+    {
+        const uint32_t l = (uint32_t)lane, sg = (l & 7u) >> 2, q = l & 3u, f = 2u * (sg * 4u + q);
+        ln.wlo = (l >> 3) * (uint32_t)(a.K / 2) + 16u * (l & 7u);
+        ln.wslot[0] = sg * 64u + q * 16u + ((l >> 3) ^ f);
+        ln.wslot[1] = sg * 64u + q * 16u + ((8u + (l >> 3)) ^ f);
+        ln.rslot[0] = 0u * 64u + g * 16u + (nl ^ (2u * (0u * 4u + g)));
+        ln.rslot[1] = 1u * 64u + g * 16u + (nl ^ (2u * (1u * 4u + g)));
+    }
     ln.soff = nl * (uint32_t)a.G * 2u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -398,14 +474,15 @@ struct PairsOut {
 template <int T, bool XL>
 __global__ __launch_bounds__(512) void qmv_mfma_kernel(MfmaArgs a) {
     __shared__ float red[Red<T>::FLOATS];
+    __shared__ u32x4 wt[XL ? 1 : kMfmaMaxS * T * 128];  // line loads (without the copy of x)
     const int lane = threadIdx.x & 63;
     const uint32_t m = (uint32_t)lane & 15u;
     const uint32_t xbytes = (uint32_t)a.M * (uint32_t)a.K * 2u;
     // Lanes of rows m >= M start at the descriptor's end and read zeros.
     const Lanes ln = lane_consts(a, m * (uint32_t)a.K * 2u);
     const Band bd{reinterpret_cast<const uint8_t *>(a.w), a.s, a.b, a.N, (uint32_t)(a.K / 2), a.G};
-    mfma_pass<T, XL>(a, bd, ln, range_of(a.x, xbytes), xbytes, a.M, nullptr, RowsOut{a.y, a.N}, blockIdx.x,
-                     gridDim.x, red);
+    mfma_pass<T, XL, !XL>(a, bd, ln, range_of(a.x, xbytes), xbytes, a.M, nullptr, RowsOut{a.y, a.N}, blockIdx.x,
+                          gridDim.x, red, wt);
 }
 
 // blockIdx.y = expert plane e. The pairs routed to e are listed in LDS and
@@ -417,6 +494,7 @@ __global__ __launch_bounds__(512) void qmv_mfma_kernel(MfmaArgs a) {
 template <int T, bool XL>
 __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
     __shared__ float red[Red<T>::FLOATS];
+    __shared__ u32x4 wt[XL ? 1 : kMfmaMaxS * T * 128];  // line loads (without the copy of x)
     __shared__ int pcount;
     const uint32_t xl_words = XL ? (uint32_t)a.XCAP * (uint32_t)(a.K / 8) + 1u : 0u;
     uint16_t *plist = reinterpret_cast<uint16_t *>(g_mfma_x + xl_words);
@@ -487,8 +565,8 @@ __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
         const int me = count - base < ps ? count - base : ps;
         const int m = lane & 15;
         const Lanes ln = lane_consts(a, m < me ? xlist[base + m] * (uint32_t)a.K * 2u : xbytes);
-        mfma_pass<T, XL>(a, bd, ln, xr, xbytes, me, xlist + base, PairsOut{a.y, a.N, plist + base}, rg, groups,
-                         red);
+        mfma_pass<T, XL, !XL>(a, bd, ln, xr, xbytes, me, xlist + base, PairsOut{a.y, a.N, plist + base}, rg,
+                              groups, red, wt);
     }
 }
 
