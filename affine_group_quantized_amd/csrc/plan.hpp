@@ -250,7 +250,10 @@ constexpr int kMfmaMaxWaves = 8;   // waves per block (LDS of the K-split combin
 #define AGQ_MFMA_MAX_S 4  // smaller blocks pack two or more per compute unit (8: 10-35% slower)
 #endif
 #ifndef AGQ_MFMA_X_LDS_MAX
-#define AGQ_MFMA_X_LDS_MAX 65536  // largest activation block copied to LDS (bytes); 0: never
+// Largest activation block copied to LDS (bytes); 0: never. Off: without the
+// copy the kernels load codes in whole lines (line loads need LDS of their
+// own), and that measured faster (14336x4096 at M = 8: 13.6 against 14.3 us).
+#define AGQ_MFMA_X_LDS_MAX 0
 #endif
 constexpr int kMfmaXLdsMax = AGQ_MFMA_X_LDS_MAX;
 constexpr int kMfmaXPer = 16;  // 16-byte words of x each thread copies

@@ -151,12 +151,8 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
         S = p["waves_per_group"]
         assert 1 <= S <= 4 and (K // 512) % S == 0
         assert all((K // 512) % s for s in range(S + 1, 5))                 # the most waves that divide
-        def fits(rows):   # LDS copy of x when it fits in 64 KB and 16 words per thread
-            return rows * K * 2 <= 65536 and -(-rows * K * 2 // 16 // (64 * S)) <= 16
-        if experts:       # passes of 16 pairs, operands from L2
-            assert p["mw"] == 16 and p["x_lds_bytes"] == 0
-        else:
-            assert p["x_lds_bytes"] == (M * K * 2 + 16 if fits(M) else 0)
+        # Passes of 16 rows (the gather's pairs), operands from L2 (no LDS copy of x).
+        assert p["mw"] == 16 and p["x_lds_bytes"] == 0
         assert p["groups_per_block"] == 1 and p["threads_per_block"] == 64 * S
         assert RPG % R == 0
         return

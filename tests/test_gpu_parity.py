@@ -187,8 +187,8 @@ def test_shapes_and_ragged_tails(bits, M, N, K):
 ])
 def test_matrix_core_shapes(M, N, K):
     """4-bit products of several rows on the matrix cores: K splits of 1, 3 and 4 waves,
-    bands of one and two tiles, ragged last tiles, and activations from the block's LDS
-    copy or from global memory."""
+    bands of one and two tiles, and ragged last tiles (rows past N in a load's 8-row
+    half of a tile read zeros)."""
     plan = agq.launch_plan(M, N, K, 4)
     assert plan["engine"] == 1
     d = si.draw_quantized_weight(23, M, N, K, 4)
