@@ -67,12 +67,13 @@ constexpr int kSB = 4;            // segments per block of scales (8 groups, 16 
 // costs resident blocks (14336x4096 at M = 8: 14.1 against 15.8 us).
 constexpr uint32_t kOnes = 0x3F803F80u;  // bfloat16 pair (1, 1)
 constexpr int kRsrcW3 = 0x00020000;      // raw buffer, 32-bit data format
-// Cache policy of the code, scale and bias loads. Each load reads half of a
-// 128-byte line (codes) or 16 bytes of it (scales); other loads read the rest
-// shortly after, so the lines are cached normally (2: non-temporal measured
-// 3-10% slower).
+// Cache policy of the code, scale and bias loads. Codes stream through once
+// in whole lines (line loads): non-temporal, which keeps the L2 for x (gather
+// W1 / W2: 74.7 / 69.6 -> 70.0 / 63.8 us). Scale loads read 16 bytes of a
+// line and later loads the rest, so they are cached normally (non-temporal:
+// 2-8% slower). (With quarter loads, non-temporal codes were 3-10% slower.)
 #ifndef AGQ_MFMA_W_POLICY
-#define AGQ_MFMA_W_POLICY 0
+#define AGQ_MFMA_W_POLICY 2
 #endif
 #ifndef AGQ_MFMA_S_POLICY
 #define AGQ_MFMA_S_POLICY 0
