@@ -19,6 +19,7 @@
 
 #include "agq.h"
 #include "plan.hpp"
+#include "plan_mfma.hpp"
 #include "qmv_kernels.hpp"
 
 namespace {

@@ -47,6 +47,7 @@
 #include <stdint.h>
 
 #include "plan.hpp"
+#include "plan_mfma.hpp"
 #include "qmv_device.hpp"
 #include "qmv_kernels.hpp"
 

@@ -145,12 +145,12 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
     mfma = bits == 4 and K % 512 == 0 and (M >= 5 or experts > 0)
     assert p["engine"] == (1 if mfma else 0)
     if mfma:
-        # Matrix cores: bands of 16 or 32 rows, up to 4 waves splitting K into equal
-        # slices of whole 4-segment (512-column) blocks, one band group per block.
+        # Matrix cores: bands of 16 or 32 rows, up to 4 waves (2 for the gather) splitting
+        # K into equal slices of whole 4-segment (512-column) blocks, one band group per block.
         assert R in (16, 32) and p["cpt"] == 0 and p["stages"] == 4
-        S = p["waves_per_group"]
-        assert 1 <= S <= 4 and (K // 512) % S == 0
-        assert all((K // 512) % s for s in range(S + 1, 5))                 # the most waves that divide
+        S, smax = p["waves_per_group"], (2 if experts else 4)
+        assert 1 <= S <= smax and (K // 512) % S == 0
+        assert all((K // 512) % s for s in range(S + 1, smax + 1))           # the most waves that divide
         # Passes of 16 rows (the gather's pairs), operands from L2 (no LDS copy of x).
         assert p["mw"] == 16 and p["x_lds_bytes"] == 0
         assert p["groups_per_block"] == 1 and p["threads_per_block"] == 64 * S
