@@ -24,24 +24,28 @@
 // way, so only the pairing of lanes with columns matters.
 //
 // Work decomposition. A tile is 16 weight rows; a band is T tiles. K splits
-// into segments of 128 columns (64 bytes of codes per row, two groups). Each
-// lane group loads one 16-byte quarter of a tile row's segment, so one load
-// instruction reads 64 contiguous bytes from each of 16 rows. One
-// v_permlane32_swap per two words then regroups the words so that each MFMA
-// sees columns of a single 64-column group (the scale changes per group):
-// after swapping words (0,2) and (1,3) between the wave halves, words 0 and
-// 1 of every lane hold columns of the segment's first group and words 2 and
-// 3 of the second. Slot (h, t) (h = group, t = word) of lane group g covers
-// columns 64h + 32(g%2) + 8(t + 2(g/2)) .. +8 of the segment.
+// into segments of 128 columns (64 bytes of codes per row, two groups),
+// processed in pairs (a 128-byte window per row). Lane group g of the B
+// operand needs the 16-byte quarter g of its row's segment. Line loads read
+// the window in whole 128-byte lines, 8 rows per instruction, and each lane
+// moves its pieces to their lanes through a per-wave LDS buffer; quarter
+// loads (kernels with an LDS copy of x) read the quarters directly, 64
+// contiguous bytes from each of 16 rows. One v_permlane32_swap per two words
+// then regroups the words so that each MFMA sees columns of a single
+// 64-column group (the scale changes per group): after swapping words (0,2)
+// and (1,3) between the wave halves, words 0 and 1 of every lane hold columns
+// of the segment's first group and words 2 and 3 of the second. Slot (h, t)
+// (h = group, t = word) of lane group g covers columns
+// 64h + 32(g%2) + 8(t + 2(g/2)) .. +8 of the segment.
 //
 // S waves split K (each owns SPW consecutive segments) and form a block; the
 // block walks bands round-robin. Per segment a wave loads the A operands of
-// its activation slice (L2-resident, shared by the band's T tiles), the codes
-// of T tiles, and every fourth segment the scales and biases of the next 8
-// groups of each tile row. Loads run 4 segments ahead in a ring. X[m,g]
-// comes from the same A operands against an all-ones B. At the end of a band
-// the S waves' partial sums meet in LDS in a fixed order, so results are
-// deterministic.
+// its activation slice (from L2, shared by the band's T tiles, or from the
+// block's LDS copy), the codes of T tiles, and every fourth segment the
+// scales and biases of the next 8 groups of each tile row. Loads run 4
+// segments ahead in a ring. X[m,g] comes from the same A operands against an
+// all-ones B. At the end of a band the S waves' partial sums meet in LDS in a
+// fixed order, so results are deterministic.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
