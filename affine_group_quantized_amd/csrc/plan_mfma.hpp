@@ -12,8 +12,9 @@ namespace agq {
 #ifndef AGQ_MFMA_MIN_ROWS
 // Activation rows from which dense 4-bit products use the matrix cores (0:
 // never). Below it the VALU form is as fast or faster: 14336x4096 at M = 4 /
-// 6 / 8 takes 12.2 / 16.1 / 19.2 us on the VALU and 12.6 / 12.8 / 13.3 us on
-// the matrix cores.
+// 5 / 6 / 8 takes 12.6 / 14.9 / 16.1 / 19.2 us on the VALU and 12.6-13.0 /
+// 12.6-13.0 / 12.8 / 13.3 us on the matrix cores; 4096x14336 at M = 4 / 5,
+// 13.1 / 15.3 against 13.5-13.7 / 13.5 us.
 #define AGQ_MFMA_MIN_ROWS 5
 #endif
 #ifndef AGQ_MFMA_TILES
