@@ -50,6 +50,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "plan.hpp"
 #include "plan_mfma.hpp"
 #include "qmv_device.hpp"
@@ -108,13 +110,33 @@ __device__ __forceinline__ u32x4 act_pairs(const u32x4 &q) {
                  byte_perm(q.w, q.y, 0x05040100u), byte_perm(q.w, q.y, 0x07060302u)};
 }
 
-// One segment's loads: activation words of the 4 slots (h,t) = (0,0), (0,1),
-// (1,0), (1,1) and 16 bytes of codes per tile.
-template <int T, bool XL>
+// One segment's loads: 16 bytes of codes per tile, and the lane's 4 / XQ
+// activation words (XQ: activation row sets per 16 lanes, below).
+template <int T, bool XL, int XQ>
 struct Seg {
-    u32x4 x[XL ? 1 : 4];  // (unused when the activations come from the block's LDS copy)
+    u32x4 x[XL ? 1 : 4 / XQ];  // (unused when the activations come from the block's LDS copy)
     u32x4 w[T];
 };
+
+// Compact activation loads. The A operand needs slots i = 0..3 (i = 2h + t) of
+// each pass row m in lane m of every lane group, and with few rows most lanes
+// would load nothing. For passes of up to 4 rows (XQ = 4) lane m of a group
+// loads slot m / 4 of row m % 4, one load instead of 4, and rotations within
+// the 16-lane row bring slot i of row r from lane r + 4i to lane r. Lanes
+// m >= 4 then hold other slots of the same rows: their A rows, and the D rows
+// they produce, are never stored. (In general, XQ row sets of R = 16 / XQ rows
+// take L = 4 / XQ loads; lane m loads slots (m / R) * L .. +L-1 of row m % R.
+// XQ = 2 for up to 8 rows measured slower than the 4 full loads: 14336x4096
+// at M = 8, 13.3 -> 13.9 us, the rotations costing more VALU issue than the
+// loads they save.)
+template <int N>
+__device__ __forceinline__ u32x4 row_ror(const u32x4 &v) {
+    // DPP row_ror:N: lane i of each 16-lane row receives lane (i - N) mod 16.
+    return u32x4{(uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, 0x120 + N, 0xF, 0xF, true),
+                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, 0x120 + N, 0xF, 0xF, true),
+                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, 0x120 + N, 0xF, 0xF, true),
+                 (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, 0x120 + N, 0xF, 0xF, true)};
+}
 
 // The block's LDS copy of the pass's activation rows (XL), already in A
 // operand form: word ((s*4 + i)*4 + g)*Mp + m holds slot i of lane group g,
@@ -136,7 +158,7 @@ struct Lanes {
     uint32_t wslot[2];  // line loads: LDS slots (16-byte units) the lane writes its rows 0-7 and 8-15 data to
     uint32_t rslot[2];  // line loads: LDS slots the lane reads segments 0 and 1 of the window from
     uint32_t soff;      // byte offset of the lane's scale row within a tile
-    uint32_t xoff[4];   // byte offsets of the lane's activation words for the 4 slots, segment 0
+    uint32_t xoff[4];   // byte offsets of the lane's 4 / XQ activation words (compact loads), segment 0
 };
 
 // One plane's band geometry and operand ranges.
@@ -154,8 +176,8 @@ struct Band {
 // reads rows 0-7 and the odd one rows 8-15 of the pair's 128-byte window (8
 // whole lines per instruction), and compute_pair moves the bytes to their
 // lanes through LDS.
-template <int T, bool SCALES, bool XL, bool LL>
-__device__ __forceinline__ void load_seg(Seg<T, XL> &u, ScaleBlock<T> &sb, const Band &bd, const Lanes &ln,
+template <int T, bool SCALES, bool XL, bool LL, int XQ>
+__device__ __forceinline__ void load_seg(Seg<T, XL, XQ> &u, ScaleBlock<T> &sb, const Band &bd, const Lanes &ln,
                                          __amdgpu_buffer_rsrc_t xr, int64_t band, int seg) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -180,25 +202,32 @@ __device__ __forceinline__ void load_seg(Seg<T, XL> &u, ScaleBlock<T> &sb, const
     }
     if constexpr (!XL) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u.x[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, ln.xoff[i], seg * 256, 0);
+        for (int i = 0; i < 4 / XQ; ++i)
+            u.x[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, ln.xoff[i], seg * 256, 0);
     }
 }
 
 // Fold one segment into the band's accumulators. sd/bd: the bf16 scale and
 // bias pairs of the segment's two groups for the lane's row of each tile.
-template <int T, bool XL>
-__device__ __forceinline__ void compute_seg(const Seg<T, XL> &u, const u32x4 (&w)[T], const uint32_t (&sd)[T],
+template <int T, bool XL, int XQ>
+__device__ __forceinline__ void compute_seg(const Seg<T, XL, XQ> &u, const u32x4 (&w)[T], const uint32_t (&sd)[T],
                                             const uint32_t (&bd)[T], f32x4 (&acc)[T], uint32_t xbase, uint32_t xmult,
                                             int seg) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
     u32x4 a[4];
+    if constexpr (XL) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if constexpr (XL)
-            a[i] = g_mfma_x[xbase + (uint32_t)(seg * 4 + i) * xmult];
-        else
-            a[i] = act_pairs(u.x[i]);
+        for (int i = 0; i < 4; ++i) a[i] = g_mfma_x[xbase + (uint32_t)(seg * 4 + i) * xmult];
+    } else if constexpr (XQ == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = act_pairs(u.x[i]);
+    } else {
+        static_assert(XQ == 4, "activation loads: 4 full loads (XQ 1) or one compact load (XQ 4)");
+        a[0] = act_pairs(u.x[0]);
+        a[1] = row_ror<12>(a[0]);
+        a[2] = row_ror<8>(a[0]);
+        a[3] = row_ror<4>(a[0]);
     }
     // X[m, g] of the two groups, in the D layout.
     const f32x4 x0 = mfma(a[1], ones, mfma(a[0], ones, z));
@@ -229,8 +258,8 @@ __device__ __forceinline__ void compute_seg(const Seg<T, XL> &u, const u32x4 (&w
 // quarter of either segment (the layout quarter loads give directly). Slots
 // are XOR-swizzled so that neither the writes nor the reads conflict.
 // A wave's LDS accesses complete in order, so the buffer needs no barrier.
-template <int T, bool XL, bool LL>
-__device__ __forceinline__ void compute_pair(const Seg<T, XL> &u0, const Seg<T, XL> &u1, const uint32_t (&sd0)[T],
+template <int T, bool XL, bool LL, int XQ>
+__device__ __forceinline__ void compute_pair(const Seg<T, XL, XQ> &u0, const Seg<T, XL, XQ> &u1, const uint32_t (&sd0)[T],
                                              const uint32_t (&bd0)[T], const uint32_t (&sd1)[T],
                                              const uint32_t (&bd1)[T], f32x4 (&acc)[T], uint32_t xbase,
                                              uint32_t xmult, int seg, const Lanes &ln, u32x4 *wt) {
@@ -246,11 +275,11 @@ __device__ __forceinline__ void compute_pair(const Seg<T, XL> &u0, const Seg<T, 
             w0[t] = wt[t * 128 + ln.rslot[0]];
             w1[t] = wt[t * 128 + ln.rslot[1]];
         }
-        compute_seg<T, XL>(u0, w0, sd0, bd0, acc, xbase, xmult, seg);
-        compute_seg<T, XL>(u1, w1, sd1, bd1, acc, xbase, xmult, seg + 1);
+        compute_seg<T, XL, XQ>(u0, w0, sd0, bd0, acc, xbase, xmult, seg);
+        compute_seg<T, XL, XQ>(u1, w1, sd1, bd1, acc, xbase, xmult, seg + 1);
     } else {
-        compute_seg<T, XL>(u0, u0.w, sd0, bd0, acc, xbase, xmult, seg);
-        compute_seg<T, XL>(u1, u1.w, sd1, bd1, acc, xbase, xmult, seg + 1);
+        compute_seg<T, XL, XQ>(u0, u0.w, sd0, bd0, acc, xbase, xmult, seg);
+        compute_seg<T, XL, XQ>(u1, u1.w, sd1, bd1, acc, xbase, xmult, seg + 1);
     }
 }
 
@@ -316,7 +345,7 @@ __device__ __forceinline__ void finish_band(f32x4 (&acc)[T], float *red, int S, 
 // 4 LDS reads per segment instead of 4 buffer loads that mostly address rows
 // past the pass.
 // xrows: the x row of each pass row (gather), or nullptr for rows 0..mrows-1.
-template <int T, bool XL, bool LL, typename Out>
+template <int T, bool XL, bool LL, int XQ, typename Out>
 __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, const Lanes &ln,
                                           __amdgpu_buffer_rsrc_t xr, uint32_t xend, int mrows, const uint32_t *xrows,
                                           const Out &out, int64_t rg, int64_t groups, float *red, u32x4 *wt_all) {
@@ -328,7 +357,7 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
     const int tpb = SPW / kRing;               // turns per band
     u32x4 *wt = wt_all + wig * T * 128;        // the wave's buffer for line loads (2 KB per tile)
 
-    Seg<T, XL> buf[kRing];
+    Seg<T, XL, XQ> buf[kRing];
     ScaleBlock<T> next[kRing / kSB], cur;
     f32x4 acc[T];
 #pragma unroll
@@ -357,9 +386,9 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
 #pragma unroll
     for (int p = 0; p < kRing; ++p) {
         if (p % kSB == 0)
-            load_seg<T, true, XL, LL>(buf[p], next[p / kSB], bd, ln, xr, rg, seg0 + p);
+            load_seg<T, true, XL, LL, XQ>(buf[p], next[p / kSB], bd, ln, xr, rg, seg0 + p);
         else
-            load_seg<T, false, XL, LL>(buf[p], next[0], bd, ln, xr, rg, seg0 + p);
+            load_seg<T, false, XL, LL, XQ>(buf[p], next[0], bd, ln, xr, rg, seg0 + p);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -401,13 +430,13 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
                 sd1[t] = dword(cur.s[t], (p + 1) % kSB);
                 bd1[t] = dword(cur.b[t], (p + 1) % kSB);
             }
-            compute_pair<T, XL, LL>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, xbase, xmult,
+            compute_pair<T, XL, LL, XQ>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, xbase, xmult,
                                 seg0 + kRing * (j % tpb) + p, ln, wt);
             if (p % kSB == 0)
-                load_seg<T, true, XL, LL>(buf[p], next[p / kSB], bd, ln, xr, nband, nseg + p);
+                load_seg<T, true, XL, LL, XQ>(buf[p], next[p / kSB], bd, ln, xr, nband, nseg + p);
             else
-                load_seg<T, false, XL, LL>(buf[p], next[0], bd, ln, xr, nband, nseg + p);
-            load_seg<T, false, XL, LL>(buf[p + 1], next[0], bd, ln, xr, nband, nseg + p + 1);
+                load_seg<T, false, XL, LL, XQ>(buf[p], next[0], bd, ln, xr, nband, nseg + p);
+            load_seg<T, false, XL, LL, XQ>(buf[p + 1], next[0], bd, ln, xr, nband, nseg + p + 1);
             __builtin_amdgcn_sched_barrier(0);
         }
         if ((j + 1) % tpb == 0) finish_band<T>(acc, red, S, wig, lane, band, bi & 1, bd.N, mrows, out);
@@ -426,7 +455,7 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
                 sd1[t] = dword(cur.s[t], (p + 1) % kSB);
                 bd1[t] = dword(cur.b[t], (p + 1) % kSB);
             }
-            compute_pair<T, XL, LL>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, xbase, xmult,
+            compute_pair<T, XL, LL, XQ>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, xbase, xmult,
                                 seg0 + kRing * (j % tpb) + p, ln, wt);
         }
         finish_band<T>(acc, red, S, wig, lane, band, bi & 1, bd.N, mrows, out);
@@ -434,8 +463,10 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
     if (S > 1 || XL) __syncthreads();  // the LDS regions and the copy of x are reused by the next pass
 }
 
-// Lane constants shared by the dense and gather kernels; xrow: the lane's
-// activation row byte offset (or the descriptor's end for lanes past the pass).
+// Lane constants shared by the dense and gather kernels; xrow: byte offset of
+// the activation row the lane loads, pass row (lane % 16) % (16 / XQ) (or the
+// descriptor's end for rows past the pass).
+template <int XQ>
 __device__ __forceinline__ Lanes lane_consts(const MfmaArgs &a, uint32_t xrow) {
     const int lane = threadIdx.x & 63;
     const uint32_t g = (uint32_t)lane >> 4, nl = (uint32_t)lane & 15u;
@@ -454,10 +485,11 @@ __device__ __forceinline__ Lanes lane_consts(const MfmaArgs &a, uint32_t xrow) {
     }
     ln.soff = nl * (uint32_t)a.G * 2u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t h = (uint32_t)i >> 1, t = (uint32_t)i & 1u;
+    for (int j = 0; j < 4 / XQ; ++j) {
+        const uint32_t i = (nl / (16u / XQ)) * (4u / XQ) + (uint32_t)j;  // slot
+        const uint32_t h = i >> 1, t = i & 1u;
         const uint32_t col = 64u * h + 32u * (g & 1u) + 8u * (t + 2u * (g >> 1));
-        ln.xoff[i] = xrow + 2u * col;
+        ln.xoff[j] = xrow + 2u * col;
     }
     return ln;
 }
@@ -475,6 +507,20 @@ struct PairsOut {
     __device__ __forceinline__ uint16_t *operator()(int m) const { return y + (int64_t)plist[m] * N; }
 };
 
+// Calls f with the activation row sets per 16 lanes (XQ) for a pass of `rows`
+// rows: the compact load (4) up to 4 rows when SMALL, else 4 full loads (1).
+// The LDS copy of x takes XQ = 1.
+template <bool XL, bool SMALL, typename F>
+__device__ __forceinline__ void with_xq(int rows, F &&f) {
+    if constexpr (!XL && SMALL) {
+        if (rows <= 4) {
+            f(std::integral_constant<int, 4>{});
+            return;
+        }
+    }
+    f(std::integral_constant<int, 1>{});
+}
+
 }  // namespace
 
 template <int T, bool XL>
@@ -484,11 +530,14 @@ __global__ __launch_bounds__(512) void qmv_mfma_kernel(MfmaArgs a) {
     const int lane = threadIdx.x & 63;
     const uint32_t m = (uint32_t)lane & 15u;
     const uint32_t xbytes = (uint32_t)a.M * (uint32_t)a.K * 2u;
-    // Lanes of rows m >= M start at the descriptor's end and read zeros.
-    const Lanes ln = lane_consts(a, m * (uint32_t)a.K * 2u);
     const Band bd{reinterpret_cast<const uint8_t *>(a.w), a.s, a.b, a.N, (uint32_t)(a.K / 2), a.G};
-    mfma_pass<T, XL, !XL>(a, bd, ln, range_of(a.x, xbytes), xbytes, a.M, nullptr, RowsOut{a.y, a.N}, blockIdx.x,
-                          gridDim.x, red, wt);
+    with_xq<XL, (kMfmaMinRows <= 4)>(a.M, [&](auto xq) {
+        constexpr int XQ = decltype(xq)::value;
+        // Lanes of rows >= M start at the descriptor's end and read zeros.
+        const Lanes ln = lane_consts<XQ>(a, (m % (16u / XQ)) * (uint32_t)a.K * 2u);
+        mfma_pass<T, XL, !XL, XQ>(a, bd, ln, range_of(a.x, xbytes), xbytes, a.M, nullptr, RowsOut{a.y, a.N},
+                                  blockIdx.x, gridDim.x, red, wt);
+    });
 }
 
 // blockIdx.y = expert plane e. The pairs routed to e are listed in LDS and
@@ -569,10 +618,13 @@ __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
     const int ps = a.XCAP;
     for (int base = 0; base < count; base += ps) {
         const int me = count - base < ps ? count - base : ps;
-        const int m = lane & 15;
-        const Lanes ln = lane_consts(a, m < me ? xlist[base + m] * (uint32_t)a.K * 2u : xbytes);
-        mfma_pass<T, XL, !XL>(a, bd, ln, xr, xbytes, me, xlist + base, PairsOut{a.y, a.N, plist + base}, rg,
-                              groups, red, wt);
+        with_xq<XL, true>(me, [&](auto xq) {
+            constexpr int XQ = decltype(xq)::value;
+            const int r = (lane & 15) % (16 / XQ);
+            const Lanes ln = lane_consts<XQ>(a, r < me ? xlist[base + r] * (uint32_t)a.K * 2u : xbytes);
+            mfma_pass<T, XL, !XL, XQ>(a, bd, ln, xr, xbytes, me, xlist + base, PairsOut{a.y, a.N, plist + base},
+                                      rg, groups, red, wt);
+        });
     }
 }
 

@@ -94,3 +94,34 @@ def test_load_offsets_cover_each_tile_window_once():
             for b in range(16):
                 seen.add((row, col + b))
         assert seen == {(r, c) for r in range(16) for c in range(128)}
+
+
+def dpp_row_ror(vals, n):
+    """DPP row_ror:n on per-lane values: lane i of each 16-lane row receives lane (i - n) mod 16."""
+    return [vals[16 * (l // 16) + (l % 16 - n) % 16] for l in range(64)]
+
+
+def test_compact_activation_loads_fill_every_slot_of_the_pass_rows():
+    """Compact x loads (XQ row sets per 16 lanes) plus row rotations give lane r < 16/XQ
+    of every lane group slots 0-3 of pass row r, the words the full 4-load form reads."""
+    rotations = {1: [None, None, None, None], 2: [None, None, 8, 8], 4: [None, 12, 8, 4]}
+    for xq, rots in rotations.items():
+        R, L = 16 // xq, 4 // xq
+        # load j of lane l: (row, slot, lane group) it fetched
+        loads = []
+        for j in range(L):
+            per_lane = []
+            for l in range(64):
+                m, g = l % 16, l // 16
+                per_lane.append((m % R, (m // R) * L + j, g))
+            loads.append(per_lane)
+        for i in range(4):
+            src = loads[i % L]
+            got = src if rots[i] is None else dpp_row_ror(src, rots[i])
+            for l in range(64):
+                m, g = l % 16, l // 16
+                if m < R:
+                    assert got[l] == (m, i, g), (xq, i, l, got[l])
+                # the word's columns are those of the codes in slot i of the lane's group
+                row, slot, gg = got[l]
+                assert gg == g
