@@ -181,7 +181,7 @@ agq_status launch_mfma_plan(int64_t M, int64_t N, int64_t K, int64_t experts, ag
     int cus = 0, dev = 0;
     agq_status st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
-    *sym = agq::mfma_kernel(plan->T, experts > 0, plan->x_lds_bytes > 0);
+    *sym = agq::mfma_kernel(plan->T, experts > 0, plan->x_lds_bytes > 0, experts == 0 && M <= 4);
     if (!*sym) return fail(AGQ_ENOTSUP, "no matrix-core kernel for %d tiles", plan->T);
     int64_t waves = 0;
     st = resident_waves(*sym, plan->threads, (size_t)plan->lds_bytes, cus, dev, &waves);

@@ -11,11 +11,12 @@ namespace agq {
 
 #ifndef AGQ_MFMA_MIN_ROWS
 // Activation rows from which dense 4-bit products use the matrix cores (0:
-// never). Below it the VALU form is as fast or faster: 14336x4096 at M = 4 /
-// 5 / 6 / 8 takes 12.6 / 14.9 / 16.1 / 19.2 us on the VALU and 12.6-13.0 /
-// 12.6-13.0 / 12.8 / 13.3 us on the matrix cores; 4096x14336 at M = 4 / 5,
-// 13.1 / 15.3 against 13.5-13.7 / 13.5 us.
-#define AGQ_MFMA_MIN_ROWS 5
+// never). Below it the VALU form is as fast or faster: 14336x4096 at M = 2 /
+// 3 / 4 / 5 / 8 takes 9.6 / 11.0 / 12.2 / 14.9 / 19.2 us on the VALU and
+// 11.4 / 11.6-11.8 / 11.9 / 12.6-13.0 / 13.3 us on the matrix cores (at
+// M <= 4 with the compact activation load); 4096x14336 at M = 2 / 3 / 4,
+// 10.4 / 12.4 / 13.0 against 12.1-12.3 / 12.35 / 12.7 us.
+#define AGQ_MFMA_MIN_ROWS 4
 #endif
 #ifndef AGQ_MFMA_TILES
 #define AGQ_MFMA_TILES 0  // 16-row tiles per band: 1, 2, or 0 to choose from the shape

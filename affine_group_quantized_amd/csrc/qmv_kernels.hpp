@@ -59,7 +59,8 @@ struct MfmaArgs {
 const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather);
 const void *dequant_kernel_sym(int bits);
 // Matrix-core kernel with bands of 16*tiles rows (tiles 1 or 2), activations
-// from an LDS copy (x_lds) or from global memory, or NULL.
-const void *mfma_kernel(int tiles, bool gather, bool x_lds);
+// from an LDS copy (x_lds) or from global memory, or NULL. compact_x (dense,
+// at most 4 activation rows, no LDS copy): one activation load per segment.
+const void *mfma_kernel(int tiles, bool gather, bool x_lds, bool compact_x);
 
 }  // namespace agq

@@ -507,12 +507,13 @@ struct PairsOut {
     __device__ __forceinline__ uint16_t *operator()(int m) const { return y + (int64_t)plist[m] * N; }
 };
 
-// Calls f with the activation row sets per 16 lanes (XQ) for a pass of `rows`
-// rows: the compact load (4) up to 4 rows when SMALL, else 4 full loads (1).
-// The LDS copy of x takes XQ = 1.
-template <bool XL, bool SMALL, typename F>
+// Calls f with the activation row sets per 16 lanes (XQ) for a gather pass of
+// `rows` rows: the compact load (4) up to 4 rows, else 4 full loads (1). The
+// LDS copy of x takes XQ = 1. (Dense products choose on the host, as separate
+// kernels: one kernel holding both forms made 14336x4096 at M = 8 0.5 us slower.)
+template <bool XL, typename F>
 __device__ __forceinline__ void with_xq(int rows, F &&f) {
-    if constexpr (!XL && SMALL) {
+    if constexpr (!XL) {
         if (rows <= 4) {
             f(std::integral_constant<int, 4>{});
             return;
@@ -523,21 +524,20 @@ __device__ __forceinline__ void with_xq(int rows, F &&f) {
 
 }  // namespace
 
-template <int T, bool XL>
+// XQ: 4 for the compact activation load (M <= 4), else 1.
+template <int T, bool XL, int XQ>
 __global__ __launch_bounds__(512) void qmv_mfma_kernel(MfmaArgs a) {
+    static_assert(XQ == 1 || !XL, "the LDS copy of x takes the 4-load form");
     __shared__ float red[Red<T>::FLOATS];
     __shared__ u32x4 wt[XL ? 1 : kMfmaMaxS * T * 128];  // line loads (without the copy of x)
     const int lane = threadIdx.x & 63;
     const uint32_t m = (uint32_t)lane & 15u;
     const uint32_t xbytes = (uint32_t)a.M * (uint32_t)a.K * 2u;
     const Band bd{reinterpret_cast<const uint8_t *>(a.w), a.s, a.b, a.N, (uint32_t)(a.K / 2), a.G};
-    with_xq<XL, (kMfmaMinRows <= 4)>(a.M, [&](auto xq) {
-        constexpr int XQ = decltype(xq)::value;
-        // Lanes of rows >= M start at the descriptor's end and read zeros.
-        const Lanes ln = lane_consts<XQ>(a, (m % (16u / XQ)) * (uint32_t)a.K * 2u);
-        mfma_pass<T, XL, !XL, XQ>(a, bd, ln, range_of(a.x, xbytes), xbytes, a.M, nullptr, RowsOut{a.y, a.N},
-                                  blockIdx.x, gridDim.x, red, wt);
-    });
+    // Lanes of rows >= M start at the descriptor's end and read zeros.
+    const Lanes ln = lane_consts<XQ>(a, (m % (16u / XQ)) * (uint32_t)a.K * 2u);
+    mfma_pass<T, XL, !XL, XQ>(a, bd, ln, range_of(a.x, xbytes), xbytes, a.M, nullptr, RowsOut{a.y, a.N}, blockIdx.x,
+                              gridDim.x, red, wt);
 }
 
 // blockIdx.y = expert plane e. The pairs routed to e are listed in LDS and
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
     const int ps = a.XCAP;
     for (int base = 0; base < count; base += ps) {
         const int me = count - base < ps ? count - base : ps;
-        with_xq<XL, true>(me, [&](auto xq) {
+        with_xq<XL>(me, [&](auto xq) {
             constexpr int XQ = decltype(xq)::value;
             const int r = (lane & 15) % (16 / XQ);
             const Lanes ln = lane_consts<XQ>(a, r < me ? xlist[base + r] * (uint32_t)a.K * 2u : xbytes);
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
     }
 }
 
-const void *mfma_kernel(int tiles, bool gather, bool x_lds) {
+const void *mfma_kernel(int tiles, bool gather, bool x_lds, bool compact_x) {
     if (gather) {
         switch (tiles * 2 + (x_lds ? 1 : 0)) {
             case 2: return reinterpret_cast<const void *>(&gather_mfma_kernel<1, false>);
@@ -638,11 +638,18 @@ const void *mfma_kernel(int tiles, bool gather, bool x_lds) {
         }
         return nullptr;
     }
+    if (compact_x && !x_lds) {
+        switch (tiles) {
+            case 1: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, false, 4>);
+            case 2: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, false, 4>);
+        }
+        return nullptr;
+    }
     switch (tiles * 2 + (x_lds ? 1 : 0)) {
-        case 2: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, false>);
-        case 3: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, true>);
-        case 4: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, false>);
-        case 5: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, true>);
+        case 2: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, false, 1>);
+        case 3: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, true, 1>);
+        case 4: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, false, 1>);
+        case 5: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, true, 1>);
     }
     return nullptr;
 }

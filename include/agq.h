@@ -90,7 +90,7 @@ agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const v
  * 1 <= M <= 8 activation rows, streaming each weight byte once for all M rows.
  *   x [M, K] BF16, y [M, N] BF16; w, scales and biases as in agq_qmv.
  * M > 8 is AGQ_ENOTSUP; that is a quantized GEMM, not a matvec. With 4-bit
- * codes, M >= 5 and K a multiple of 512 the product runs on the matrix cores
+ * codes, M >= 4 and K a multiple of 512 the product runs on the matrix cores
  * and K is limited only by M*K*2 < 2^31 bytes of x. Otherwise the K limit
  * shrinks with M: K <= 16384 * c for 4-bit and 8192 * c for 8-bit, with
  * c = min(7, floor(8/M)) (larger K is AGQ_ENOTSUP).

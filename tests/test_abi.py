@@ -142,7 +142,7 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
     if N <= 300000:
         rows = visited_rows(p, N)
         assert rows.size == N and np.array_equal(np.sort(rows), np.arange(N))   # each row exactly once
-    mfma = bits == 4 and K % 512 == 0 and (M >= 5 or experts > 0)
+    mfma = bits == 4 and K % 512 == 0 and (M >= 4 or experts > 0)
     assert p["engine"] == (1 if mfma else 0)
     if mfma:
         # Matrix cores: bands of 16 or 32 rows, up to 4 waves (2 for the gather) splitting

@@ -184,11 +184,13 @@ def test_shapes_and_ragged_tails(bits, M, N, K):
 @pytest.mark.parametrize("M,N,K", [
     (5, 31, 512), (6, 17, 1536), (8, 1, 2560), (5, 100, 3584), (6, 1000, 4096), (7, 33, 14336),
     (5, 2049, 6144), (7, 4111, 4096), (8, 4097, 2048), (6, 16400, 2048), (8, 16401, 1024),
+    (4, 31, 512), (4, 100, 3584), (4, 4111, 4096), (4, 16401, 1024),
 ])
 def test_matrix_core_shapes(M, N, K):
     """4-bit products of several rows on the matrix cores: K splits of 1, 3 and 4 waves,
-    bands of one and two tiles, and ragged last tiles (rows past N in a load's 8-row
-    half of a tile read zeros)."""
+    bands of one and two tiles, ragged last tiles (rows past N in a load's 8-row half of a
+    tile read zeros), and M = 4, whose kernel loads each activation segment once per lane
+    group and rotates the words into place."""
     plan = agq.launch_plan(M, N, K, 4)
     assert plan["engine"] == 1
     d = si.draw_quantized_weight(23, M, N, K, 4)
