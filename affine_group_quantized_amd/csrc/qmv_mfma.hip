@@ -111,24 +111,31 @@ __device__ __forceinline__ u32x4 act_pairs(const u32x4 &q) {
 }
 
 // One segment's loads: 16 bytes of codes per tile, and the lane's 4 / XQ
-// activation words (XQ: activation row sets per 16 lanes, below).
+// activation words (XQ: the activation load form, below).
 template <int T, bool XL, int XQ>
 struct Seg {
     u32x4 x[XL ? 1 : 4 / XQ];  // (unused when the activations come from the block's LDS copy)
     u32x4 w[T];
 };
 
-// Compact activation loads. The A operand needs slots i = 0..3 (i = 2h + t) of
+// Activation load forms. The A operand needs slots i = 0..3 (i = 2h + t) of
 // each pass row m in lane m of every lane group, and with few rows most lanes
-// would load nothing. For passes of up to 4 rows (XQ = 4) lane m of a group
-// loads slot m / 4 of row m % 4, one load instead of 4, and rotations within
-// the 16-lane row bring slot i of row r from lane r + 4i to lane r. Lanes
-// m >= 4 then hold other slots of the same rows: their A rows, and the D rows
-// they produce, are never stored. (In general, XQ row sets of R = 16 / XQ rows
-// take L = 4 / XQ loads; lane m loads slots (m / R) * L .. +L-1 of row m % R.
-// XQ = 2 for up to 8 rows measured slower than the 4 full loads: 14336x4096
-// at M = 8, 13.3 -> 13.9 us, the rotations costing more VALU issue than the
-// loads they save.)
+// of a direct load would read nothing.
+//  - XQ = 1 (passes of up to 16 rows): 4 loads per lane, slots 0-3 of its row.
+//  - XQ = 4 (up to 4 rows): lane m of a group loads slot m / 4 of row m % 4,
+//    one load instead of 4, and rotations within the 16-lane row bring slot i
+//    of row r from lane r + 4i to lane r.
+//  - XQ = 2 (up to 8 rows): staged. Load k of lane m in group g reads word m
+//    (columns 8m..8m+7) of segment row 4k + g, contiguous 256-byte rows. At
+//    compute time the lane unpacks its two words into A operand form (half
+//    the byte permutes of XQ = 1) and writes them to a 4 KB per-wave LDS
+//    buffer (both segments of the pair), slot row*16 + (word ^ row), from
+//    which every lane reads its 4 slots. Writes and reads are free of bank
+//    conflicts, and the LDS pipe takes work off the VALU, which bounds these
+//    kernels. (Rotations for 8 rows instead, two loads and 8 moves per
+//    segment, measured slower than XQ = 1: 14336x4096 at M = 8, 13.3 -> 13.9 us.)
+// Lanes m >= 16 / XQ then hold other slots of the same rows: their A rows, and
+// the D rows they produce, are never stored.
 template <int N>
 __device__ __forceinline__ u32x4 row_ror(const u32x4 &v) {
     // DPP row_ror:N: lane i of each 16-lane row receives lane (i - N) mod 16.
@@ -159,6 +166,8 @@ struct Lanes {
     uint32_t rslot[2];  // line loads: LDS slots the lane reads segments 0 and 1 of the window from
     uint32_t soff;      // byte offset of the lane's scale row within a tile
     uint32_t xoff[4];   // byte offsets of the lane's 4 / XQ activation words (compact loads), segment 0
+    uint32_t xw[2];     // staged activations (XQ 2): LDS slots the lane writes its two words to
+    uint32_t xrd[4];    // staged activations: LDS slots of the lane's 4 A operand words
 };
 
 // One plane's band geometry and operand ranges.
@@ -212,7 +221,7 @@ __device__ __forceinline__ void load_seg(Seg<T, XL, XQ> &u, ScaleBlock<T> &sb, c
 template <int T, bool XL, int XQ>
 __device__ __forceinline__ void compute_seg(const Seg<T, XL, XQ> &u, const u32x4 (&w)[T], const uint32_t (&sd)[T],
                                             const uint32_t (&bd)[T], f32x4 (&acc)[T], uint32_t xbase, uint32_t xmult,
-                                            int seg) {
+                                            int seg, const u32x4 *ax) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
     u32x4 a[4];
@@ -222,8 +231,11 @@ __device__ __forceinline__ void compute_seg(const Seg<T, XL, XQ> &u, const u32x4
     } else if constexpr (XQ == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[i] = act_pairs(u.x[i]);
+    } else if constexpr (XQ == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = ax[i];
     } else {
-        static_assert(XQ == 4, "activation loads: 4 full loads (XQ 1) or one compact load (XQ 4)");
+        static_assert(XQ == 4, "activation loads: 4 full loads (XQ 1), staged (XQ 2) or compact (XQ 4)");
         a[0] = act_pairs(u.x[0]);
         a[1] = row_ror<12>(a[0]);
         a[2] = row_ror<8>(a[0]);
@@ -263,6 +275,22 @@ __device__ __forceinline__ void compute_pair(const Seg<T, XL, XQ> &u0, const Seg
                                              const uint32_t (&bd0)[T], const uint32_t (&sd1)[T],
                                              const uint32_t (&bd1)[T], f32x4 (&acc)[T], uint32_t xbase,
                                              uint32_t xmult, int seg, const Lanes &ln, u32x4 *wt) {
+    u32x4 a0[XQ == 2 ? 4 : 1], a1[XQ == 2 ? 4 : 1];
+    if constexpr (XQ == 2) {
+        // Staged activations: both segments' rows, already in A operand form,
+        // through the 4 KB after the wave's code buffer, then each lane's slots.
+        u32x4 *xs = wt + T * 128;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            xs[ln.xw[k]] = act_pairs(u0.x[k]);
+            xs[128 + ln.xw[k]] = act_pairs(u1.x[k]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a0[i] = xs[ln.xrd[i]];
+            a1[i] = xs[128 + ln.xrd[i]];
+        }
+    }
     if constexpr (LL) {
         u32x4 w0[T], w1[T];
 #pragma unroll
@@ -275,11 +303,11 @@ __device__ __forceinline__ void compute_pair(const Seg<T, XL, XQ> &u0, const Seg
             w0[t] = wt[t * 128 + ln.rslot[0]];
             w1[t] = wt[t * 128 + ln.rslot[1]];
         }
-        compute_seg<T, XL, XQ>(u0, w0, sd0, bd0, acc, xbase, xmult, seg);
-        compute_seg<T, XL, XQ>(u1, w1, sd1, bd1, acc, xbase, xmult, seg + 1);
+        compute_seg<T, XL, XQ>(u0, w0, sd0, bd0, acc, xbase, xmult, seg, a0);
+        compute_seg<T, XL, XQ>(u1, w1, sd1, bd1, acc, xbase, xmult, seg + 1, a1);
     } else {
-        compute_seg<T, XL, XQ>(u0, u0.w, sd0, bd0, acc, xbase, xmult, seg);
-        compute_seg<T, XL, XQ>(u1, u1.w, sd1, bd1, acc, xbase, xmult, seg + 1);
+        compute_seg<T, XL, XQ>(u0, u0.w, sd0, bd0, acc, xbase, xmult, seg, a0);
+        compute_seg<T, XL, XQ>(u1, u1.w, sd1, bd1, acc, xbase, xmult, seg + 1, a1);
     }
 }
 
@@ -355,7 +383,8 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
     const int seg0 = wig * SPW;
     const int turns = a.BPG * (SPW / kRing);  // turns of the ring over the walk
     const int tpb = SPW / kRing;               // turns per band
-    u32x4 *wt = wt_all + wig * T * 128;        // the wave's buffer for line loads (2 KB per tile)
+    // The wave's buffer: 2 KB per tile for line loads, then 4 KB of staged activations (XQ 2).
+    u32x4 *wt = wt_all + wig * (T * 128 + (XQ == 2 ? 256 : 0));
 
     Seg<T, XL, XQ> buf[kRing];
     ScaleBlock<T> next[kRing / kSB], cur;
@@ -463,11 +492,10 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
     if (S > 1 || XL) __syncthreads();  // the LDS regions and the copy of x are reused by the next pass
 }
 
-// Lane constants shared by the dense and gather kernels; xrow: byte offset of
-// the activation row the lane loads, pass row (lane % 16) % (16 / XQ) (or the
-// descriptor's end for rows past the pass).
-template <int XQ>
-__device__ __forceinline__ Lanes lane_consts(const MfmaArgs &a, uint32_t xrow) {
+// Lane constants shared by the dense and gather kernels; rowoff(r): byte
+// offset of pass row r in x (or the descriptor's end for rows past the pass).
+template <int XQ, typename RowOff>
+__device__ __forceinline__ Lanes lane_consts(const MfmaArgs &a, RowOff rowoff) {
     const int lane = threadIdx.x & 63;
     const uint32_t g = (uint32_t)lane >> 4, nl = (uint32_t)lane & 15u;
     Lanes ln;
@@ -484,12 +512,30 @@ __device__ __forceinline__ Lanes lane_consts(const MfmaArgs &a, uint32_t xrow) {
         ln.rslot[1] = 1u * 64u + g * 16u + (nl ^ (2u * (1u * 4u + g)));
     }
     ln.soff = nl * (uint32_t)a.G * 2u;
+    if constexpr (XQ == 2) {
+        // Staged: load k reads word nl (columns 8*nl..+7 of the segment) of
+        // row 4k + g; LDS slot of (row, word) is row*16 + (word ^ row).
 #pragma unroll
-    for (int j = 0; j < 4 / XQ; ++j) {
-        const uint32_t i = (nl / (16u / XQ)) * (4u / XQ) + (uint32_t)j;  // slot
-        const uint32_t h = i >> 1, t = i & 1u;
-        const uint32_t col = 64u * h + 32u * (g & 1u) + 8u * (t + 2u * (g >> 1));
-        ln.xoff[j] = xrow + 2u * col;
+        for (int k = 0; k < 2; ++k) {
+            const uint32_t row = 4u * (uint32_t)k + g;
+            ln.xoff[k] = rowoff(row) + 16u * nl;
+            ln.xw[k] = row * 16u + (nl ^ row);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t h = (uint32_t)i >> 1, t = (uint32_t)i & 1u, row = nl & 7u;
+            const uint32_t word = 8u * h + 4u * (g & 1u) + t + 2u * (g >> 1);
+            ln.xrd[i] = row * 16u + (word ^ row);
+        }
+    } else {
+        const uint32_t xrow = rowoff(nl % (16u / XQ));
+#pragma unroll
+        for (int j = 0; j < 4 / XQ; ++j) {
+            const uint32_t i = (nl / (16u / XQ)) * (4u / XQ) + (uint32_t)j;  // slot
+            const uint32_t h = i >> 1, t = i & 1u;
+            const uint32_t col = 64u * h + 32u * (g & 1u) + 8u * (t + 2u * (g >> 1));
+            ln.xoff[j] = xrow + 2u * col;
+        }
     }
     return ln;
 }
@@ -507,15 +553,21 @@ struct PairsOut {
     __device__ __forceinline__ uint16_t *operator()(int m) const { return y + (int64_t)plist[m] * N; }
 };
 
-// Calls f with the activation row sets per 16 lanes (XQ) for a gather pass of
-// `rows` rows: the compact load (4) up to 4 rows, else 4 full loads (1). The
-// LDS copy of x takes XQ = 1. (Dense products choose on the host, as separate
-// kernels: one kernel holding both forms made 14336x4096 at M = 8 0.5 us slower.)
+// Calls f with the activation load form (XQ) for a gather pass of `rows`
+// rows: 4 up to 4 rows, 2 up to 8, else 1. The LDS copy of x takes XQ = 1.
+// (Dense products choose on the host, as separate kernels: one kernel holding
+// two forms made 14336x4096 at M = 8 0.5 us slower.) For the gather's few
+// pairs per plane the rotations beat staging: Mixtral-shaped W1, 64.5 against
+// 66.3 us with staged passes of up to 4 pairs.
 template <bool XL, typename F>
 __device__ __forceinline__ void with_xq(int rows, F &&f) {
     if constexpr (!XL) {
         if (rows <= 4) {
             f(std::integral_constant<int, 4>{});
+            return;
+        }
+        if (rows <= 8) {
+            f(std::integral_constant<int, 2>{});
             return;
         }
     }
@@ -524,18 +576,18 @@ __device__ __forceinline__ void with_xq(int rows, F &&f) {
 
 }  // namespace
 
-// XQ: 4 for the compact activation load (M <= 4), else 1.
+// XQ: the activation load form, 4 for M <= 4, 2 (staged) for M = 5..8, and 1
+// with the LDS copy of x.
 template <int T, bool XL, int XQ>
 __global__ __launch_bounds__(512) void qmv_mfma_kernel(MfmaArgs a) {
     static_assert(XQ == 1 || !XL, "the LDS copy of x takes the 4-load form");
     __shared__ float red[Red<T>::FLOATS];
-    __shared__ u32x4 wt[XL ? 1 : kMfmaMaxS * T * 128];  // line loads (without the copy of x)
-    const int lane = threadIdx.x & 63;
-    const uint32_t m = (uint32_t)lane & 15u;
+    // line loads (without the copy of x), and the staged activations
+    __shared__ u32x4 wt[XL ? 1 : kMfmaMaxS * (T * 128 + (XQ == 2 ? 256 : 0))];
     const uint32_t xbytes = (uint32_t)a.M * (uint32_t)a.K * 2u;
     const Band bd{reinterpret_cast<const uint8_t *>(a.w), a.s, a.b, a.N, (uint32_t)(a.K / 2), a.G};
     // Lanes of rows >= M start at the descriptor's end and read zeros.
-    const Lanes ln = lane_consts<XQ>(a, (m % (16u / XQ)) * (uint32_t)a.K * 2u);
+    const Lanes ln = lane_consts<XQ>(a, [&](uint32_t r) { return r * (uint32_t)a.K * 2u; });
     mfma_pass<T, XL, !XL, XQ>(a, bd, ln, range_of(a.x, xbytes), xbytes, a.M, nullptr, RowsOut{a.y, a.N}, blockIdx.x,
                               gridDim.x, red, wt);
 }
@@ -549,7 +601,9 @@ __global__ __launch_bounds__(512) void qmv_mfma_kernel(MfmaArgs a) {
 template <int T, bool XL>
 __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
     __shared__ float red[Red<T>::FLOATS];
-    __shared__ u32x4 wt[XL ? 1 : kMfmaMaxS * T * 128];  // line loads (without the copy of x)
+    // line loads (without the copy of x), and the staged activations; the
+    // planner gives the gather at most kMfmaGatherMaxS waves per block
+    __shared__ u32x4 wt[XL ? 1 : kMfmaGatherMaxS * (T * 128 + 256)];
     __shared__ int pcount;
     const uint32_t xl_words = XL ? (uint32_t)a.XCAP * (uint32_t)(a.K / 8) + 1u : 0u;
     uint16_t *plist = reinterpret_cast<uint16_t *>(g_mfma_x + xl_words);
@@ -620,8 +674,9 @@ __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
         const int me = count - base < ps ? count - base : ps;
         with_xq<XL>(me, [&](auto xq) {
             constexpr int XQ = decltype(xq)::value;
-            const int r = (lane & 15) % (16 / XQ);
-            const Lanes ln = lane_consts<XQ>(a, r < me ? xlist[base + r] * (uint32_t)a.K * 2u : xbytes);
+            const Lanes ln = lane_consts<XQ>(a, [&](uint32_t r) {
+                return (int)r < me ? xlist[base + r] * (uint32_t)a.K * 2u : xbytes;
+            });
             mfma_pass<T, XL, !XL, XQ>(a, bd, ln, xr, xbytes, me, xlist + base, PairsOut{a.y, a.N, plist + base},
                                       rg, groups, red, wt);
         });
@@ -646,9 +701,9 @@ const void *mfma_kernel(int tiles, bool gather, bool x_lds, bool compact_x) {
         return nullptr;
     }
     switch (tiles * 2 + (x_lds ? 1 : 0)) {
-        case 2: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, false, 1>);
+        case 2: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, false, 2>);
         case 3: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, true, 1>);
-        case 4: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, false, 1>);
+        case 4: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, false, 2>);
         case 5: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, true, 1>);
     }
     return nullptr;

@@ -125,3 +125,37 @@ def test_compact_activation_loads_fill_every_slot_of_the_pass_rows():
                 # the word's columns are those of the codes in slot i of the lane's group
                 row, slot, gg = got[l]
                 assert gg == g
+
+
+def test_staged_activations_are_a_conflict_free_exchange():
+    """Staged activation form (up to 8 rows): load k of lane l reads word l % 16 of row
+    4k + l // 16; LDS slot of (row, word) is row*16 + (word ^ row). Every (row, word) of a
+    segment lands in its own slot, each lane reads back the words of its A operand slots,
+    and no 16-lane pass of a write or a read hits one 16-byte bank slot twice (lanes m and
+    m + 8 read one address, a broadcast)."""
+    data = {}
+    for k in range(2):
+        slots = []
+        for l in range(64):
+            row, word = 4 * k + l // 16, l % 16
+            slot = row * 16 + (word ^ row)
+            assert 0 <= slot < 128 and slot not in data
+            data[slot] = (row, word)
+            slots.append(slot)
+        for p in range(4):
+            assert len({s % 16 for s in slots[16 * p:16 * p + 16]}) == 16
+    assert len(data) == 128
+    for i in range(4):
+        h, t = i >> 1, i & 1
+        reads = []
+        for l in range(64):
+            m, g = l % 16, l // 16
+            row = m & 7
+            word = 8 * h + 4 * (g & 1) + t + 2 * (g >> 1)
+            slot = row * 16 + (word ^ row)
+            assert data[slot] == (row, word)
+            assert list(range(8 * word, 8 * word + 8)) == slot_columns(h, t, g)
+            reads.append(slot)
+        for p in range(4):
+            part = reads[16 * p:16 * p + 16]
+            assert len({s % 16 for s in part}) == len(set(part)) == 8
