@@ -218,6 +218,26 @@ def test_gather_matrix_core_passes_of_sixteen():
     check_close(y, y_ref, A, "gather passes of 16")
 
 
+def test_gather_matrix_core_activation_load_forms():
+    """Planes with 4, 5, 8, 9 and 16 pairs in one call: each side of the pass sizes at
+    which the kernel switches its activation load (one rotated load up to 4 rows, staged
+    through LDS up to 8, four loads beyond), over ragged tiles and K split over 2 waves."""
+    E, N, K, R = 6, 45, 2048, 13
+    assert agq.launch_plan(8, N, K, 4, experts=E)["engine"] == 1
+    planes = [si.draw_quantized_weight(25, e, N, K, 4) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(25, 98, R, K)
+    rhs = np.array([0] * 4 + [1] * 5 + [2] * 8 + [3] * 9 + [5] * 16, np.uint32)
+    np.random.default_rng([25, 1]).shuffle(rhs)
+    lhs = (np.arange(len(rhs)) * 7 % R).astype(np.uint32)
+    progress("gather, activation load forms on the matrix cores")
+    y = agq.gather_qmv(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs))
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, 4)
+    check_close(y, y_ref, A, "gather activation load forms")
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 def test_constant_code_closed_form_adversarial(bits):
     """|y| equals sum|x*w| here, so the bf16 output rounding alone can approach 4e-3*A."""
