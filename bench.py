@@ -337,7 +337,8 @@ def write_workload_profile(workload, trace_dir, fetch_dir, write_dir):
              f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- python3 bench.py {pflags}",
              f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o bench -- python3 bench.py {pflags}", "",
              "Kernels `qmv_mfma_kernel` and `gather_mfma_kernel` run on the matrix cores (template arguments: "
-             "16-row tiles per band, LDS copy of x); `qmv_kernel` is the VALU form.", "",
+             "16-row tiles per band, LDS copy of x, and for `qmv_mfma_kernel` the activation load form: 4 = one "
+             "rotated load for M <= 4, 2 = staged through LDS for M = 5-8); `qmv_kernel` is the VALU form.", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in stats:
         if "agq::" in r["Name"]:
