@@ -220,10 +220,18 @@ def write_profiles(trace_dir, fetch_dir, write_dir):
     print(json.dumps(rec))
 
 
-def time_calls(torch, fn, calls, repeats=5):
-    """Median over `repeats` of the mean event-timed duration of `calls` back-to-back calls."""
-    for i in range(20):
+def time_calls(torch, fn, calls, repeats=5, warm_s=0.3):
+    """Median over `repeats` of the mean event-timed duration of `calls` back-to-back calls.
+
+    Untimed warm-up: at least 20 calls and `warm_s` seconds of them. The first product
+    timed in a process otherwise reads 3-8 us slow, as if the clocks were still ramping."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < 20 or time.perf_counter() - t0 < warm_s:
         fn(i)
+        i += 1
+        if i % 20 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     per = []
     for _ in range(repeats):
