@@ -110,6 +110,42 @@ def pin_dequant_quantizer_roundtrip(lib):
         assert np.array_equal(q2.reshape(64, 4, 64)[full], qg[full])
 
 
+def _fits_binary32(v: Fraction) -> bool:
+    """Whether an exact dyadic rational is a binary32 value: its odd significand has at
+    most 24 bits (the values here are far inside the normal exponent range)."""
+    if v == 0:
+        return True
+    num, den = abs(v.numerator), v.denominator
+    assert den & (den - 1) == 0, "dyadic rationals only"
+    while num % 2 == 0:
+        num //= 2
+    return num < (1 << 24)
+
+
+def pin_dequant_not_f32_count(lib):
+    """The count of dequantized weights that binary32 cannot hold, against an exact count.
+
+    Groups: s = 129*2^-17 with b = 2^15 (every nonzero code needs more than 24 bits),
+    the same s with b = 2^8 (codes that are multiples of 4 fit, others do not), and
+    s = 1, b = 1/2 (everything fits). The expected count comes from integer reasoning
+    on the exact rational s*q + b, not from a floating-point round trip."""
+    for bits in (4, 8):
+        K = 192
+        g = np.random.default_rng(60 + bits)
+        q = g.integers(0, 2 ** bits, size=(3, K), dtype=np.uint8)
+        q[0, :5] = 0
+        s = np.array([[0x3A81, 0x3A81, 0x3F80]] * 3, np.uint16)
+        b = np.array([[0x4700, 0x4380, 0x3F00]] * 3, np.uint16)
+        want = 0
+        for n in range(3):
+            for k in range(K):
+                v = _frac_bf16(s[n, k // 64]) * int(q[n, k]) + _frac_bf16(b[n, k // 64])
+                want += not _fits_binary32(v)
+        assert 0 < want < 3 * K
+        _, got = oracle.dequantize(pack_codes(q, bits), s, b, K, bits, lib=lib)
+        assert got == want, (bits, got, want)
+
+
 def pin_dot_exact_bruteforce(lib):
     for bits in (4, 8):
         for seed, (M, N, K) in enumerate([(2, 3, 64), (1, 2, 128), (3, 4, 192)]):

@@ -34,6 +34,8 @@ MUTANTS = {
                          "row_dot(x + m * K, w + n * words, scales,"),
     "expert_plane_ignored": ("const uint32_t *we = w + e * N * words;", "const uint32_t *we = w;"),
     "lhs_ignored": ("int64_t r = lhs ? (int64_t)lhs[p] : p;", "int64_t r = p % R;"),
+    "not_f32_never_counted": ("if ((double)(float)v != v) ++bad;", "if ((float)v != (float)v) ++bad;"),
+    "not_f32_inverted": ("if ((double)(float)v != v) ++bad;", "if ((double)(float)v == v) ++bad;"),
 }
 
 
