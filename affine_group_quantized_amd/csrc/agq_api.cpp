@@ -88,10 +88,6 @@ int g_occ_n = 0;
 std::mutex g_occ_mu;
 
 agq_status resident_waves(const void *sym, int threads, size_t lds, int cus, int dev, int64_t *waves) {
-    if (agq::kWavesPerCuOverride > 0) {
-        *waves = (int64_t)cus * agq::kWavesPerCuOverride;
-        return AGQ_OK;
-    }
     int bpc = -1;
     {
         std::lock_guard<std::mutex> lock(g_occ_mu);
@@ -177,11 +173,11 @@ agq_status launch_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t expert
 agq_status launch_mfma_plan(int64_t M, int64_t N, int64_t K, int64_t experts, agq::MfmaPlan *plan,
                             const void **sym) {
     agq::mfma_shape(N, K, experts, plan);
-    agq::mfma_x_lds(M, K, experts, M, plan);  // (gather: M is the pair count P)
+    agq::mfma_lds(experts, M, plan);  // (gather: M is the pair count P)
     int cus = 0, dev = 0;
     agq_status st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
-    *sym = agq::mfma_kernel(plan->T, experts > 0, plan->x_lds_bytes > 0, experts == 0 && M <= 4);
+    *sym = agq::mfma_kernel(plan->T, experts > 0, experts == 0 && M <= 4);
     if (!*sym) return fail(AGQ_ENOTSUP, "no matrix-core kernel for %d tiles", plan->T);
     int64_t waves = 0;
     st = resident_waves(*sym, plan->threads, (size_t)plan->lds_bytes, cus, dev, &waves);
@@ -205,7 +201,7 @@ void export_mfma_plan(const agq::MfmaPlan &p, int64_t K, agq_plan *out) {
     out->row_groups = p.groups;
     out->blocks = p.groups;
     out->row_order = 0;
-    out->x_lds_bytes = p.x_lds_bytes;
+    out->x_lds_bytes = 0;
     out->resident_waves = (int32_t)p.resident;
     out->engine = 1;
 }
@@ -225,7 +221,6 @@ agq::MfmaArgs make_mfma_args(const void *x, const uint32_t *w, const void *s, co
     a.S = p.S;
     a.SPW = p.SPW;
     a.BPG = p.BPG;
-    a.XCAP = p.pass_rows;
     return a;
 }
 
@@ -243,7 +238,7 @@ void export_plan(const agq::Plan &p, agq_plan *out) {
     out->rows_per_group = p.RPG;
     out->row_groups = p.TG;
     out->blocks = p.blocks;
-    out->row_order = AGQ_ROW_ORDER_CONTIGUOUS ? 1 : 0;
+    out->row_order = 0;
     out->x_lds_bytes = p.x_lds_bytes;
     out->resident_waves = (int32_t)p.resident;
     out->engine = 0;
@@ -403,7 +398,7 @@ agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group
     if (agq::mfma_eligible(M, K, bits, experts, experts ? 1 : M)) {
         agq::MfmaPlan mp;
         agq::mfma_shape(N, K, experts, &mp);
-        agq::mfma_x_lds(M, K, experts, experts ? 32 : M, &mp);  // (gather plans assume 32 pairs)
+        agq::mfma_lds(experts, 32, &mp);  // (gather plans assume 32 pairs)
         agq::mfma_grid((int64_t)num_cus * waves_per_cu, experts, &mp);
         export_mfma_plan(mp, K, out);
         return AGQ_OK;

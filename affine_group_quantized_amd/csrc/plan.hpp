@@ -9,97 +9,46 @@
 namespace agq {
 
 constexpr int kMaxWavesPerGroup = 8;   // kernels are built with __launch_bounds__(512)
-#ifndef AGQ_MAX_CPT
-#define AGQ_MAX_CPT 7  // 8 chunks per lane plus two row buffers no longer fit in 256 VGPRs
-#endif
-#ifndef AGQ_PREF_CPT
-// Longer rows split K over more waves rather than holding more chunks per
-// lane, as long as 8 waves cover the row: 4 chunks keep 3 waves per SIMD
-// resident (4096x14336 at batch 1: 8.6 us with 2 waves of 4 chunks against
-// 9.5 us with one wave of 7).
-#define AGQ_PREF_CPT 4
-#endif
-constexpr int kMaxCpt = AGQ_MAX_CPT;   // 16-byte chunks per lane in one wave's K segment
-constexpr int kPrefCpt = AGQ_PREF_CPT;
+// 16-byte chunks per lane within a wave's K segment: at most 7 (8 chunks per
+// lane plus two row buffers no longer fit in 256 VGPRs). Longer rows split K
+// over more waves rather than holding more chunks per lane, as long as 8 waves
+// cover the row: 4 chunks keep 3 waves per SIMD resident (4096x14336 at batch
+// 1: 8.6 us with 2 waves of 4 chunks against 9.5 us with one wave of 7).
+constexpr int kMaxCpt = 7;
+constexpr int kPrefCpt = 4;
 constexpr int kXRegBudget = 8;         // CPT * MW <= 8: staged activations use <= 128 VGPRs
-#ifndef AGQ_XREG_WIDE
-#define AGQ_XREG_WIDE 2
-#endif
 // Preferred budget for several activation rows: one chunk per lane at M >= 2,
 // splitting K over more waves (each holding less x, so more of them stay
 // resident), as long as 8 waves cover the row; kXRegBudget past that.
 // 14336x4096 at M = 2 / 4: 9.2 / 12.3 us against 9.8 / 13.1 us with 2 chunks.
-constexpr int kXRegWide = AGQ_XREG_WIDE;
+constexpr int kXRegWide = 2;
 constexpr int kMaxPairs = 4096;        // gather: pair list kept in LDS as uint16
-#ifndef AGQ_WAVES_PER_CU
-#define AGQ_WAVES_PER_CU 0  // 0: size grids from the kernel's measured occupancy
-#endif
-#ifndef AGQ_LOADS_SHALLOW
-#define AGQ_LOADS_SHALLOW 4
-#endif
-#ifndef AGQ_LOADS_DEEP
-#define AGQ_LOADS_DEEP 8
-#endif
-#ifndef AGQ_STAGES_SHALLOW
-#define AGQ_STAGES_SHALLOW 2
-#endif
-#ifndef AGQ_STAGES_DEEP
-#define AGQ_STAGES_DEEP 2
-#endif
-#ifndef AGQ_LOADS_WIDE
-#define AGQ_LOADS_WIDE 4
-#endif
-#ifndef AGQ_STAGES_WIDE
-#define AGQ_STAGES_WIDE 2
-#endif
-#ifndef AGQ_STAGES_WIDE1
-#define AGQ_STAGES_WIDE1 4
-#endif
-#ifndef AGQ_WIDE1_KSPLIT
-#define AGQ_WIDE1_KSPLIT 0  // 1: the deeper ring for K-split wide plans too
-#endif
-#ifndef AGQ_DEEP_ROWS
-#define AGQ_DEEP_ROWS 16
-#endif
-constexpr int kWavesPerCuOverride = AGQ_WAVES_PER_CU;  // >0 forces this many waves per CU
 // 16-byte weight loads in flight per lane, counting every stage of the load
 // ring, and the ring depth. Short walks use the shallow plan (more, lighter
 // waves finish sooner); walks of at least kDeepRows rows per row group use the
 // deep one.
-constexpr int kLoadsShallow = AGQ_LOADS_SHALLOW;
-constexpr int kLoadsDeep = AGQ_LOADS_DEEP;
-constexpr int kStagesShallow = AGQ_STAGES_SHALLOW;
-constexpr int kStagesDeep = AGQ_STAGES_DEEP;
-constexpr int kDeepRows = AGQ_DEEP_ROWS;
+constexpr int kLoadsShallow = 4;
+constexpr int kLoadsDeep = 8;
+constexpr int kStagesShallow = 2;
+constexpr int kStagesDeep = 2;
+constexpr int kDeepRows = 16;
 // Several activation rows per pass (MW > 1: the wide and gather forms): x
 // takes 16*MW*CPT VGPRs per lane, residency is low, and each wave needs more
 // rows in flight. One plan for short and long walks.
-constexpr int kLoadsWide = AGQ_LOADS_WIDE;
-constexpr int kStagesWide = AGQ_STAGES_WIDE;
+constexpr int kLoadsWide = 4;
+constexpr int kStagesWide = 2;
 // Ring depth of the wide form when one wave covers a whole row (S == 1): such
 // waves hold fewer activation registers than the K-split shapes of the same
 // instantiation, and room for more rows in flight.
-constexpr int kStagesWide1 = AGQ_STAGES_WIDE1;
-#ifndef AGQ_GATHER_MW
-// Pairs per pass of the gather. Planes with more pairs take several passes,
-// each reading the plane again; fewer pairs per pass keep x in fewer VGPRs
-// and more waves resident. On the Mixtral-shaped workload (2 to 8 pairs per
-// plane) passes of 8 win: 86.5 + 96.2 us for W1 + W2 against 88.1 + 99.8 us
-// with passes of 4.
-#define AGQ_GATHER_MW 8
-#endif
-constexpr int kGatherMW = AGQ_GATHER_MW;
-#ifndef AGQ_GATHER_XREG
-#define AGQ_GATHER_XREG 8  // gather: CPT * MW <= this (16 VGPRs of staged activations per unit)
-#endif
-constexpr int kGatherXReg = AGQ_GATHER_XREG;
-#ifndef AGQ_GATHER_OVERSUB
-#define AGQ_GATHER_OVERSUB 4
-#endif
-constexpr int kGatherOversub = AGQ_GATHER_OVERSUB;  // gather grid: resident groups x this
-#ifndef AGQ_ROW_ORDER_CONTIGUOUS
-#define AGQ_ROW_ORDER_CONTIGUOUS 0  // 0: row groups take R-row slices round-robin; 1: contiguous ranges
-#endif
+constexpr int kStagesWide1 = 4;
+// Pairs per pass of the VALU gather. Planes with more pairs take several
+// passes, each reading the plane again; fewer pairs per pass keep x in fewer
+// VGPRs and more waves resident. On the Mixtral-shaped workload (2 to 8 pairs
+// per plane) passes of 8 win: 86.5 + 96.2 us for W1 + W2 against 88.1 + 99.8
+// us with passes of 4.
+constexpr int kGatherMW = 8;
+constexpr int kGatherXReg = 8;         // gather: CPT * MW <= this (16 VGPRs of staged activations per unit)
+constexpr int kGatherOversub = 4;      // gather grid: resident groups x this
 
 constexpr int floor_pow2(int v) { return v >= 16 ? 16 : v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
 
@@ -123,20 +72,13 @@ constexpr int plan_rows(int cpt, int mw, bool deep, bool whole_row = false) {
                   : rows_per_iter(cpt, mw, kLoadsShallow, kStagesShallow);
 }
 
-#ifndef AGQ_GPB_S1
-#define AGQ_GPB_S1 4  // row groups (waves) per block when one wave covers a row
-#endif
-#ifndef AGQ_GPB_S2
-#define AGQ_GPB_S2 4  // row groups per block when two waves split a row (one LDS copy of x for 8 waves)
-#endif
-#ifndef AGQ_XL_DEEP
-#define AGQ_XL_DEEP 0  // stage x through LDS for long walks too
-#endif
-#ifndef AGQ_X_LDS_MAX
-#define AGQ_X_LDS_MAX 81920
-#endif
-// Largest activation block staged in LDS (bytes).
-constexpr int kXLdsMax = AGQ_X_LDS_MAX;
+// Row groups per block: 4 single-wave groups, or 4 two-wave groups (one LDS
+// copy of x for 8 waves); one group for S >= 3.
+constexpr int kGpbS1 = 4;
+constexpr int kGpbS2 = 4;
+// Largest activation block staged in LDS (bytes; 20 and 40 KB caps measured
+// slower: down 7.9 -> 8.9 us).
+constexpr int kXLdsMax = 81920;
 constexpr int kXLdsPerChunk = 68;
 
 struct Plan {
@@ -173,10 +115,10 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
         if (q.S > kMaxWavesPerGroup) return AGQ_ENOTSUP;
         q.cpt = (q.C + 64 * q.S - 1) / (64 * q.S);
     }
-    const bool whole_row = !gather && (AGQ_WIDE1_KSPLIT || q.S == 1);
+    const bool whole_row = !gather && q.S == 1;
     q.R = plan_rows(q.cpt, q.mw, deep, whole_row);
     q.NB = plan_stages(q.mw, deep, whole_row, q.cpt);
-    q.GPB = q.S == 1 ? AGQ_GPB_S1 : (q.S == 2 ? AGQ_GPB_S2 : 1);
+    q.GPB = q.S == 1 ? kGpbS1 : (q.S == 2 ? kGpbS2 : 1);
     q.threads = 64 * q.S * q.GPB;
     // One LDS copy of x, in staging form, can serve a whole block of
     // single-wave row groups, or of row groups of two K segments.
@@ -191,7 +133,7 @@ inline agq_status plan_shape(int64_t M, int64_t K, int bits, int64_t experts, Pl
     // for 256*S threads.)
     const bool shared = (q.S == 1 || q.S == 2) && q.GPB >= 4;
     // (The gather's passes are short walks whatever the plane's length.)
-    q.x_lds_bytes = ((gather || AGQ_XL_DEEP || !deep) && shared && xbytes <= kXLdsMax) ? (int)xbytes : 0;
+    q.x_lds_bytes = ((gather || !deep) && shared && xbytes <= kXLdsMax) ? (int)xbytes : 0;
     *p = q;
     return AGQ_OK;
 }

@@ -372,11 +372,9 @@ struct DenseOut {
 };
 
 // The weight rows a row group visits: iteration `it` covers rows
-// [at(it), at(it) + R), dropping rows >= end.
-//  - Interleaved (default): row groups take R-row slices round-robin, so at
-//    any moment the whole grid reads one compact band of the matrix.
-//  - Contiguous: each group walks its own range of RPG rows.
-// Iterations past the walk land on rows >= end.
+// [at(it), at(it) + R), dropping rows >= end. Row groups take R-row slices
+// round-robin, so at any moment the whole grid reads one compact band of the
+// matrix. Iterations past the walk land on rows >= end.
 struct RowWalk {
     int64_t first;   // first row of iteration 0
     int64_t stride;  // rows between consecutive iterations
@@ -386,12 +384,7 @@ struct RowWalk {
 
 template <int R>
 __device__ __forceinline__ RowWalk row_walk(const ProductArgs &a, int64_t rg, int64_t groups) {
-#if AGQ_ROW_ORDER_CONTIGUOUS
-    const int64_t row0 = rg * a.RPG;
-    return RowWalk{row0, R, row0 + a.RPG < a.N ? row0 + a.RPG : a.N};
-#else
     return RowWalk{rg * R, groups * R, a.N};
-#endif
 }
 
 // Reduce the lane partials of iteration `it` to row results and store them.
@@ -739,7 +732,7 @@ static const void *qmv_sym_xl(int xs) {
 
 // The shallow and the deep plan of each (MW, CPT), and for several activation
 // rows the plan of waves that cover a whole row (which never split K, so no
-// more than one LDS segment).
+// more than one LDS segment). The deep plan reads x per wave (no LDS copy).
 template <int BITS, int MW, int CPT>
 static const void *qmv_sym(int R, int NB, int xl) {
     constexpr int RS = plan_rows(CPT, MW, false), RD = plan_rows(CPT, MW, true);
@@ -747,15 +740,12 @@ static const void *qmv_sym(int R, int NB, int xl) {
     constexpr int RW = plan_rows(CPT, MW, false, true), NW = plan_stages(MW, false, true, CPT);
     if (R == RS && NB == NS) return qmv_sym_xl<BITS, MW, CPT, RS, NS>(xl);
     if constexpr (RD != RS || ND != NS) {
-        if (R == RD && NB == ND) return qmv_sym_xl<BITS, MW, CPT, RD, ND>(xl);
+        if (R == RD && NB == ND && xl == 0) return reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, RD, ND, 0>);
     }
     if constexpr (MW > 1 && (RW != RS || NW != NS)) {
-        if constexpr (AGQ_WIDE1_KSPLIT) {
-            if (R == RW && NB == NW) return qmv_sym_xl<BITS, MW, CPT, RW, NW>(xl);
-        } else if (R == RW && NB == NW && xl <= 1) {
+        if (R == RW && NB == NW && xl <= 1)
             return xl ? reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, RW, NW, 1>)
                       : reinterpret_cast<const void *>(&qmv_kernel<BITS, CPT, MW, RW, NW, 0>);
-        }
     }
     return nullptr;
 }

@@ -49,8 +49,7 @@ struct MfmaArgs {
     int32_t S;            // waves per block (K split)
     int32_t SPW;          // 128-column segments per wave (a multiple of 4)
     int32_t BPG;          // bands each block walks
-    int32_t XCAP;         // gather: pairs per pass (the rows of the LDS copy of x, or 16 without one)
-    int32_t pad_;
+    int32_t pad_[2];
 };
 
 // Kernel symbol for (bits, activation rows per pass, chunks per lane, weight
@@ -58,9 +57,10 @@ struct MfmaArgs {
 // LDS copy of x (0: none)), or NULL.
 const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather);
 const void *dequant_kernel_sym(int bits);
-// Matrix-core kernel with bands of 16*tiles rows (tiles 1 or 2), activations
-// from an LDS copy (x_lds) or from global memory, or NULL. compact_x (dense,
-// at most 4 activation rows, no LDS copy): one activation load per segment.
-const void *mfma_kernel(int tiles, bool gather, bool x_lds, bool compact_x);
+// Matrix-core kernel with bands of 16*tiles rows (tiles 1 or 2). compact_x
+// (dense, at most 4 activation rows): one activation load per segment;
+// otherwise (dense, 5-8 rows) activations staged through LDS. The gather
+// chooses its load form per pass.
+const void *mfma_kernel(int tiles, bool gather, bool compact_x);
 
 }  // namespace agq

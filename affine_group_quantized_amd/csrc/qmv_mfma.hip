@@ -28,9 +28,9 @@
 // processed in pairs (a 128-byte window per row). Lane group g of the B
 // operand needs the 16-byte quarter g of its row's segment. Line loads read
 // the window in whole 128-byte lines, 8 rows per instruction, and each lane
-// moves its pieces to their lanes through a per-wave LDS buffer; quarter
-// loads (kernels with an LDS copy of x) read the quarters directly, 64
-// contiguous bytes from each of 16 rows. One v_permlane32_swap per two words
+// moves its pieces to their lanes through a per-wave LDS buffer. (Reading the
+// quarters directly, 64 contiguous bytes from each of 16 rows per
+// instruction, measured slower.) One v_permlane32_swap per two words
 // then regroups the words so that each MFMA sees columns of a single
 // 64-column group (the scale changes per group): after swapping words (0,2)
 // and (1,3) between the wave halves, words 0 and 1 of every lane hold columns
@@ -40,8 +40,8 @@
 //
 // S waves split K (each owns SPW consecutive segments) and form a block; the
 // block walks bands round-robin. Per segment a wave loads the A operands of
-// its activation slice (from L2, shared by the band's T tiles, or from the
-// block's LDS copy), the codes of T tiles, and every fourth segment the
+// its activation slice (from L2, shared by the band's T tiles), the codes of
+// T tiles, and every fourth segment the
 // scales and biases of the next 8 groups of each tile row. Loads run 4
 // segments ahead in a ring. X[m,g] comes from the same A operands against an
 // all-ones B. At the end of a band the S waves' partial sums meet in LDS in a
@@ -66,27 +66,18 @@ namespace {
 
 constexpr int kRing = kMfmaRing;  // segments in flight per wave
 constexpr int kSB = 4;            // segments per block of scales (8 groups, 16 bytes per row)
-// Line loads (LL): codes in whole 128-byte lines, 8 rows per load, moved to
-// their lanes through a 2 KB LDS buffer per wave and tile; otherwise 64-byte
-// quarters of 16 rows per load. Kernels that read x from L2 use line loads
-// (gather W1 / W2: 78.2 / 76.7 -> 73.1 / 66.0 us; 4096x14336 at M = 8: 16.0
-// -> 14.7 us); kernels with the LDS copy of x do not, since the extra LDS
-// costs resident blocks (14336x4096 at M = 8: 14.1 against 15.8 us).
+// Codes load in whole 128-byte lines, 8 rows per load, and move to their lanes
+// through a 2 KB LDS buffer per wave and tile (gather W1 / W2: 78.2 / 76.7 ->
+// 73.1 / 66.0 us against 64-byte quarters of 16 rows per load; 4096x14336 at
+// M = 8: 16.0 -> 14.7 us).
 constexpr uint32_t kOnes = 0x3F803F80u;  // bfloat16 pair (1, 1)
 constexpr int kRsrcW3 = 0x00020000;      // raw buffer, 32-bit data format
 // Cache policy of the code, scale and bias loads. Codes stream through once
-// in whole lines (line loads): non-temporal, which keeps the L2 for x (gather
-// W1 / W2: 74.7 / 69.6 -> 70.0 / 63.8 us). Scale loads read 16 bytes of a
-// line and later loads the rest, so they are cached normally (non-temporal:
-// 2-8% slower). (With quarter loads, non-temporal codes were 3-10% slower.)
-#ifndef AGQ_MFMA_W_POLICY
-#define AGQ_MFMA_W_POLICY 2
-#endif
-#ifndef AGQ_MFMA_S_POLICY
-#define AGQ_MFMA_S_POLICY 0
-#endif
-constexpr int kWPolicy = AGQ_MFMA_W_POLICY;
-constexpr int kSPolicy = AGQ_MFMA_S_POLICY;
+// in whole lines: non-temporal, which keeps the L2 for x (gather W1 / W2:
+// 74.7 / 69.6 -> 70.0 / 63.8 us). Scale loads read 16 bytes of a line and
+// later loads the rest, so they are cached normally (non-temporal: 2-8% slower).
+constexpr int kWPolicy = 2;
+constexpr int kSPolicy = 0;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_of(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcW3);
@@ -112,9 +103,9 @@ __device__ __forceinline__ u32x4 act_pairs(const u32x4 &q) {
 
 // One segment's loads: 16 bytes of codes per tile, and the lane's 4 / XQ
 // activation words (XQ: the activation load form, below).
-template <int T, bool XL, int XQ>
+template <int T, int XQ>
 struct Seg {
-    u32x4 x[XL ? 1 : 4 / XQ];  // (unused when the activations come from the block's LDS copy)
+    u32x4 x[4 / XQ];
     u32x4 w[T];
 };
 
@@ -145,11 +136,8 @@ __device__ __forceinline__ u32x4 row_ror(const u32x4 &v) {
                  (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, 0x120 + N, 0xF, 0xF, true)};
 }
 
-// The block's LDS copy of the pass's activation rows (XL), already in A
-// operand form: word ((s*4 + i)*4 + g)*Mp + m holds slot i of lane group g,
-// row m, segment s; one zero word follows for lanes of rows past the pass.
-extern __shared__ u32x4 g_mfma_x[];
-constexpr int kXPer = 16;  // 16-byte words of x each thread stages (the host checks the copy fits)
+// Dynamic LDS of the gather kernel: its pair list and their x rows.
+extern __shared__ u32x4 g_mfma_dyn[];
 
 // Scales and biases of 8 groups (4 segments) per tile row: dword j holds the
 // bf16 pair of segment j's two groups.
@@ -160,7 +148,6 @@ struct ScaleBlock {
 
 // Per-wave constants of a pass.
 struct Lanes {
-    uint32_t woff;      // byte offset of the lane's code quarter within a tile: row (l%16), quarter l/16
     uint32_t wlo;       // line loads: byte offset of the lane's 16 bytes in rows 0-7 of a tile's 128-byte window
     uint32_t wslot[2];  // line loads: LDS slots (16-byte units) the lane writes its rows 0-7 and 8-15 data to
     uint32_t rslot[2];  // line loads: LDS slots the lane reads segments 0 and 1 of the window from
@@ -179,14 +166,12 @@ struct Band {
     int32_t G;
 };
 
-// Codes of one segment per tile. Quarter loads (LL false): the lane's
-// own 16 bytes, row l%16 and quarter l/16, 64 bytes from each of 16 rows per
-// instruction. Line loads: units of a segment pair take turns; the even unit
-// reads rows 0-7 and the odd one rows 8-15 of the pair's 128-byte window (8
-// whole lines per instruction), and compute_pair moves the bytes to their
-// lanes through LDS.
-template <int T, bool SCALES, bool XL, bool LL, int XQ>
-__device__ __forceinline__ void load_seg(Seg<T, XL, XQ> &u, ScaleBlock<T> &sb, const Band &bd, const Lanes &ln,
+// Codes of one segment per tile. Units of a segment pair take turns: the
+// even unit reads rows 0-7 and the odd one rows 8-15 of the pair's 128-byte
+// window (8 whole lines per instruction), and compute_pair moves the bytes to
+// their lanes through LDS.
+template <int T, bool SCALES, int XQ>
+__device__ __forceinline__ void load_seg(Seg<T, XQ> &u, ScaleBlock<T> &sb, const Band &bd, const Lanes &ln,
                                          __amdgpu_buffer_rsrc_t xr, int64_t band, int seg) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -194,13 +179,9 @@ __device__ __forceinline__ void load_seg(Seg<T, XL, XQ> &u, ScaleBlock<T> &sb, c
         const int64_t left = bd.N - row0;
         const uint32_t rows = left <= 0 ? 0u : left >= 16 ? 16u : (uint32_t)left;
         const int64_t r0 = left <= 0 ? 0 : row0;
-        if constexpr (LL)
-            u.w[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.w + r0 * bd.rowbytes, rows * bd.rowbytes),
-                                                           ln.wlo + ((uint32_t)seg & 1u) * 8u * bd.rowbytes,
-                                                           (seg >> 1) * 128, kWPolicy);
-        else
-            u.w[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.w + r0 * bd.rowbytes, rows * bd.rowbytes),
-                                                           ln.woff, seg * 64, kWPolicy);
+        u.w[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.w + r0 * bd.rowbytes, rows * bd.rowbytes),
+                                                       ln.wlo + ((uint32_t)seg & 1u) * 8u * bd.rowbytes,
+                                                       (seg >> 1) * 128, kWPolicy);
         if constexpr (SCALES) {
             const uint32_t sbytes = rows * (uint32_t)bd.G * 2u;
             sb.s[t] = __builtin_amdgcn_raw_buffer_load_b128(range_of(bd.s + r0 * bd.G, sbytes), ln.soff, seg * 4,
@@ -209,26 +190,19 @@ __device__ __forceinline__ void load_seg(Seg<T, XL, XQ> &u, ScaleBlock<T> &sb, c
                                                             kSPolicy);
         }
     }
-    if constexpr (!XL) {
 #pragma unroll
-        for (int i = 0; i < 4 / XQ; ++i)
-            u.x[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, ln.xoff[i], seg * 256, 0);
-    }
+    for (int i = 0; i < 4 / XQ; ++i) u.x[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, ln.xoff[i], seg * 256, 0);
 }
 
 // Fold one segment into the band's accumulators. sd/bd: the bf16 scale and
 // bias pairs of the segment's two groups for the lane's row of each tile.
-template <int T, bool XL, int XQ>
-__device__ __forceinline__ void compute_seg(const Seg<T, XL, XQ> &u, const u32x4 (&w)[T], const uint32_t (&sd)[T],
-                                            const uint32_t (&bd)[T], f32x4 (&acc)[T], uint32_t xbase, uint32_t xmult,
-                                            int seg, const u32x4 *ax) {
+template <int T, int XQ>
+__device__ __forceinline__ void compute_seg(const Seg<T, XQ> &u, const u32x4 (&w)[T], const uint32_t (&sd)[T],
+                                            const uint32_t (&bd)[T], f32x4 (&acc)[T], const u32x4 *ax) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
     u32x4 a[4];
-    if constexpr (XL) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = g_mfma_x[xbase + (uint32_t)(seg * 4 + i) * xmult];
-    } else if constexpr (XQ == 1) {
+    if constexpr (XQ == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[i] = act_pairs(u.x[i]);
     } else if constexpr (XQ == 2) {
@@ -264,17 +238,16 @@ __device__ __forceinline__ void compute_seg(const Seg<T, XL, XQ> &u, const u32x4
     }
 }
 
-// Segments p and p+1 (a 128-byte window) of every tile. With line loads, the
-// even unit holds rows 0-7 and the odd one rows 8-15 of the window; each
-// lane writes both to the wave's LDS buffer and reads back its own row and
-// quarter of either segment (the layout quarter loads give directly). Slots
-// are XOR-swizzled so that neither the writes nor the reads conflict.
-// A wave's LDS accesses complete in order, so the buffer needs no barrier.
-template <int T, bool XL, bool LL, int XQ>
-__device__ __forceinline__ void compute_pair(const Seg<T, XL, XQ> &u0, const Seg<T, XL, XQ> &u1, const uint32_t (&sd0)[T],
+// Segments p and p+1 (a 128-byte window) of every tile. The even unit holds
+// rows 0-7 and the odd one rows 8-15 of the window; each lane writes both to
+// the wave's LDS buffer and reads back its own row and quarter of either
+// segment. Slots are XOR-swizzled so that neither the writes nor the reads
+// conflict. A wave's LDS accesses complete in order, so the buffer needs no
+// barrier.
+template <int T, int XQ>
+__device__ __forceinline__ void compute_pair(const Seg<T, XQ> &u0, const Seg<T, XQ> &u1, const uint32_t (&sd0)[T],
                                              const uint32_t (&bd0)[T], const uint32_t (&sd1)[T],
-                                             const uint32_t (&bd1)[T], f32x4 (&acc)[T], uint32_t xbase,
-                                             uint32_t xmult, int seg, const Lanes &ln, u32x4 *wt) {
+                                             const uint32_t (&bd1)[T], f32x4 (&acc)[T], const Lanes &ln, u32x4 *wt) {
     u32x4 a0[XQ == 2 ? 4 : 1], a1[XQ == 2 ? 4 : 1];
     if constexpr (XQ == 2) {
         // Staged activations: both segments' rows, already in A operand form,
@@ -291,24 +264,19 @@ __device__ __forceinline__ void compute_pair(const Seg<T, XL, XQ> &u0, const Seg
             a1[i] = xs[128 + ln.xrd[i]];
         }
     }
-    if constexpr (LL) {
-        u32x4 w0[T], w1[T];
+    u32x4 w0[T], w1[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            wt[t * 128 + ln.wslot[0]] = u0.w[t];
-            wt[t * 128 + ln.wslot[1]] = u1.w[t];
-        }
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            w0[t] = wt[t * 128 + ln.rslot[0]];
-            w1[t] = wt[t * 128 + ln.rslot[1]];
-        }
-        compute_seg<T, XL, XQ>(u0, w0, sd0, bd0, acc, xbase, xmult, seg, a0);
-        compute_seg<T, XL, XQ>(u1, w1, sd1, bd1, acc, xbase, xmult, seg + 1, a1);
-    } else {
-        compute_seg<T, XL, XQ>(u0, u0.w, sd0, bd0, acc, xbase, xmult, seg, a0);
-        compute_seg<T, XL, XQ>(u1, u1.w, sd1, bd1, acc, xbase, xmult, seg + 1, a1);
+    for (int t = 0; t < T; ++t) {
+        wt[t * 128 + ln.wslot[0]] = u0.w[t];
+        wt[t * 128 + ln.wslot[1]] = u1.w[t];
     }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        w0[t] = wt[t * 128 + ln.rslot[0]];
+        w1[t] = wt[t * 128 + ln.rslot[1]];
+    }
+    compute_seg<T, XQ>(u0, w0, sd0, bd0, acc, a0);
+    compute_seg<T, XQ>(u1, w1, sd1, bd1, acc, a1);
 }
 
 __device__ __forceinline__ uint32_t dword(const u32x4 &v, int j) {
@@ -366,17 +334,10 @@ __device__ __forceinline__ void finish_band(f32x4 (&acc)[T], float *red, int S, 
 // `ln`), against the plane's bands rg, rg + groups, ... (BPG of them).
 // Every wave of the block walks the same number of segments, so the block
 // meets at the same band boundaries.
-//
-// XL: the block first copies the pass's activation rows into LDS in A
-// operand form (x loads issued before the first codes, so waiting for them
-// does not wait for the codes), and the waves read their operands there:
-// 4 LDS reads per segment instead of 4 buffer loads that mostly address rows
-// past the pass.
-// xrows: the x row of each pass row (gather), or nullptr for rows 0..mrows-1.
-template <int T, bool XL, bool LL, int XQ, typename Out>
+template <int T, int XQ, typename Out>
 __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, const Lanes &ln,
-                                          __amdgpu_buffer_rsrc_t xr, uint32_t xend, int mrows, const uint32_t *xrows,
-                                          const Out &out, int64_t rg, int64_t groups, float *red, u32x4 *wt_all) {
+                                          __amdgpu_buffer_rsrc_t xr, int mrows, const Out &out, int64_t rg,
+                                          int64_t groups, float *red, u32x4 *wt_all) {
     const int lane = threadIdx.x & 63;
     const int wig = wave_id();
     const int S = a.S, SPW = a.SPW;
@@ -386,60 +347,22 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
     // The wave's buffer: 2 KB per tile for line loads, then 4 KB of staged activations (XQ 2).
     u32x4 *wt = wt_all + wig * (T * 128 + (XQ == 2 ? 256 : 0));
 
-    Seg<T, XL, XQ> buf[kRing];
+    Seg<T, XQ> buf[kRing];
     ScaleBlock<T> next[kRing / kSB], cur;
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // LDS copy of x: source word q (16 bytes) is pass row q / (K/8), 8-column
-    // word c8 = q % (K/8): byte q*16 of dense rows, or of x row xrows[q / (K/8)].
-    // Words past the pass read from xend, the end of the x range (zeros).
-    const uint32_t words = (uint32_t)mrows * (uint32_t)(a.K / 8);
-    const int per = (int)((words + blockDim.x - 1) / blockDim.x);  // <= kXPer (host check)
-    u32x4 xraw[XL ? kXPer : 1];
-    if constexpr (XL) {
-        const uint32_t wpr = (uint32_t)(a.K / 8);
-#pragma unroll
-        for (int k = 0; k < kXPer; ++k)
-            if (k < per) {  // uniform branch
-                const uint32_t q = threadIdx.x + k * blockDim.x;
-                uint32_t off = q * 16u;
-                if (xrows) off = q < words ? (xrows[q / wpr] * wpr + q % wpr) * 16u : xend;
-                xraw[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
-            }
-    }
     __builtin_amdgcn_sched_barrier(0);
 
     // Turn j covers segments seg0 + 4*(j % tpb) .. +3 of band rg + (j / tpb) * groups.
 #pragma unroll
     for (int p = 0; p < kRing; ++p) {
         if (p % kSB == 0)
-            load_seg<T, true, XL, LL, XQ>(buf[p], next[p / kSB], bd, ln, xr, rg, seg0 + p);
+            load_seg<T, true, XQ>(buf[p], next[p / kSB], bd, ln, xr, rg, seg0 + p);
         else
-            load_seg<T, false, XL, LL, XQ>(buf[p], next[0], bd, ln, xr, rg, seg0 + p);
+            load_seg<T, false, XQ>(buf[p], next[0], bd, ln, xr, rg, seg0 + p);
     }
     __builtin_amdgcn_sched_barrier(0);
-
-    uint32_t xbase = 0, xmult = 0;
-    if constexpr (XL) {
-        const uint32_t Mp = (uint32_t)mrows, wpr = (uint32_t)(a.K / 8);
-#pragma unroll
-        for (int k = 0; k < kXPer; ++k) {
-            const uint32_t q = threadIdx.x + k * blockDim.x;
-            if (k < per && q < words) {
-                const uint32_t m = q / wpr, c8 = q % wpr;
-                const uint32_t sgm = c8 >> 4, c16 = c8 & 15u, h = c16 >> 3, rem = c16 & 7u;
-                const uint32_t g = (rem >> 2) | (((rem >> 1) & 1u) << 1), i = 2u * h + (rem & 1u);
-                g_mfma_x[((sgm * 4u + i) * 4u + g) * Mp + m] = act_pairs(xraw[k]);
-            }
-        }
-        if (threadIdx.x == 0) g_mfma_x[words] = u32x4{0u, 0u, 0u, 0u};
-        __syncthreads();
-        const uint32_t m = (uint32_t)lane & 15u, g = (uint32_t)lane >> 4;
-        xbase = m < Mp ? g * Mp + m : words;
-        xmult = m < Mp ? 4u * Mp : 0u;
-    }
 
     int j = 0;
     for (; j + 1 < turns; ++j) {
@@ -459,13 +382,12 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
                 sd1[t] = dword(cur.s[t], (p + 1) % kSB);
                 bd1[t] = dword(cur.b[t], (p + 1) % kSB);
             }
-            compute_pair<T, XL, LL, XQ>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, xbase, xmult,
-                                seg0 + kRing * (j % tpb) + p, ln, wt);
+            compute_pair<T, XQ>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, ln, wt);
             if (p % kSB == 0)
-                load_seg<T, true, XL, LL, XQ>(buf[p], next[p / kSB], bd, ln, xr, nband, nseg + p);
+                load_seg<T, true, XQ>(buf[p], next[p / kSB], bd, ln, xr, nband, nseg + p);
             else
-                load_seg<T, false, XL, LL, XQ>(buf[p], next[0], bd, ln, xr, nband, nseg + p);
-            load_seg<T, false, XL, LL, XQ>(buf[p + 1], next[0], bd, ln, xr, nband, nseg + p + 1);
+                load_seg<T, false, XQ>(buf[p], next[0], bd, ln, xr, nband, nseg + p);
+            load_seg<T, false, XQ>(buf[p + 1], next[0], bd, ln, xr, nband, nseg + p + 1);
             __builtin_amdgcn_sched_barrier(0);
         }
         if ((j + 1) % tpb == 0) finish_band<T>(acc, red, S, wig, lane, band, bi & 1, bd.N, mrows, out);
@@ -484,12 +406,11 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
                 sd1[t] = dword(cur.s[t], (p + 1) % kSB);
                 bd1[t] = dword(cur.b[t], (p + 1) % kSB);
             }
-            compute_pair<T, XL, LL, XQ>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, xbase, xmult,
-                                seg0 + kRing * (j % tpb) + p, ln, wt);
+            compute_pair<T, XQ>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, ln, wt);
         }
         finish_band<T>(acc, red, S, wig, lane, band, bi & 1, bd.N, mrows, out);
     }
-    if (S > 1 || XL) __syncthreads();  // the LDS regions and the copy of x are reused by the next pass
+    if (S > 1) __syncthreads();  // the LDS regions are reused by the next pass
 }
 
 // Lane constants shared by the dense and gather kernels; rowoff(r): byte
@@ -499,7 +420,6 @@ __device__ __forceinline__ Lanes lane_consts(const MfmaArgs &a, RowOff rowoff) {
     const int lane = threadIdx.x & 63;
     const uint32_t g = (uint32_t)lane >> 4, nl = (uint32_t)lane & 15u;
     Lanes ln;
-    ln.woff = nl * (uint32_t)(a.K / 2) + 16u * g;
     // Line loads: the lane reads row l/8 (or 8 + l/8), bytes 16*(l%8) of a
     // 128-byte window: segment sg = (l%8)/4, quarter q = l%4. The LDS slot of
     // (row, segment, quarter) is segment*64 + quarter*16 + (row ^ 2*(segment*4 + quarter)).
@@ -554,60 +474,53 @@ struct PairsOut {
 };
 
 // Calls f with the activation load form (XQ) for a gather pass of `rows`
-// rows: 4 up to 4 rows, 2 up to 8, else 1. The LDS copy of x takes XQ = 1.
-// (Dense products choose on the host, as separate kernels: one kernel holding
-// two forms made 14336x4096 at M = 8 0.5 us slower.) For the gather's few
-// pairs per plane the rotations beat staging: Mixtral-shaped W1, 64.5 against
-// 66.3 us with staged passes of up to 4 pairs.
-template <bool XL, typename F>
+// rows: 4 up to 4 rows, 2 up to 8, else 1. (Dense products choose on the
+// host, as separate kernels: one kernel holding two forms made 14336x4096 at
+// M = 8 0.5 us slower.) For the gather's few pairs per plane the rotations
+// beat staging: Mixtral-shaped W1, 64.5 against 66.3 us with staged passes of
+// up to 4 pairs.
+template <typename F>
 __device__ __forceinline__ void with_xq(int rows, F &&f) {
-    if constexpr (!XL) {
-        if (rows <= 4) {
-            f(std::integral_constant<int, 4>{});
-            return;
-        }
-        if (rows <= 8) {
-            f(std::integral_constant<int, 2>{});
-            return;
-        }
+    if (rows <= 4) {
+        f(std::integral_constant<int, 4>{});
+        return;
+    }
+    if (rows <= 8) {
+        f(std::integral_constant<int, 2>{});
+        return;
     }
     f(std::integral_constant<int, 1>{});
 }
 
 }  // namespace
 
-// XQ: the activation load form, 4 for M <= 4, 2 (staged) for M = 5..8, and 1
-// with the LDS copy of x.
-template <int T, bool XL, int XQ>
+// XQ: the activation load form, 4 for M <= 4 and 2 (staged) for M = 5..8.
+template <int T, int XQ>
 __global__ __launch_bounds__(512) void qmv_mfma_kernel(MfmaArgs a) {
-    static_assert(XQ == 1 || !XL, "the LDS copy of x takes the 4-load form");
     __shared__ float red[Red<T>::FLOATS];
-    // line loads (without the copy of x), and the staged activations
-    __shared__ u32x4 wt[XL ? 1 : kMfmaMaxS * (T * 128 + (XQ == 2 ? 256 : 0))];
+    // line loads, and the staged activations
+    __shared__ u32x4 wt[kMfmaMaxS * (T * 128 + (XQ == 2 ? 256 : 0))];
     const uint32_t xbytes = (uint32_t)a.M * (uint32_t)a.K * 2u;
     const Band bd{reinterpret_cast<const uint8_t *>(a.w), a.s, a.b, a.N, (uint32_t)(a.K / 2), a.G};
     // Lanes of rows >= M start at the descriptor's end and read zeros.
     const Lanes ln = lane_consts<XQ>(a, [&](uint32_t r) { return r * (uint32_t)a.K * 2u; });
-    mfma_pass<T, XL, !XL, XQ>(a, bd, ln, range_of(a.x, xbytes), xbytes, a.M, nullptr, RowsOut{a.y, a.N}, blockIdx.x,
-                              gridDim.x, red, wt);
+    mfma_pass<T, XQ>(a, bd, ln, range_of(a.x, xbytes), a.M, RowsOut{a.y, a.N}, blockIdx.x, gridDim.x, red, wt);
 }
 
 // blockIdx.y = expert plane e. The pairs routed to e are listed in LDS and
-// taken a.XCAP per pass (16, or the rows of the block's LDS copy of x with
-// XL), so each used plane streams once per pass; blocks of planes without
-// pairs exit before reading weights. Blocks of plane 0 also write NaN rows for
-// pairs whose indices are out of range. Dynamic LDS: the copy of x (XL),
-// then the pair list (P uint16, padded to 16 bytes) and their x rows (P uint32).
-template <int T, bool XL>
+// taken 16 per pass, so each used plane streams once per pass; blocks of
+// planes without pairs exit before reading weights. Blocks of plane 0 also
+// write NaN rows for pairs whose indices are out of range. Dynamic LDS: the
+// pair list (P uint16, padded to 16 bytes) and their x rows (P uint32).
+template <int T>
 __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
     __shared__ float red[Red<T>::FLOATS];
-    // line loads (without the copy of x), and the staged activations; the
-    // planner gives the gather at most kMfmaGatherMaxS waves per block
-    __shared__ u32x4 wt[XL ? 1 : kMfmaGatherMaxS * (T * 128 + 256)];
+    // line loads and the staged activations; the planner gives the gather at
+    // most kMfmaGatherMaxS waves per block
+    __shared__ u32x4 wt[kMfmaGatherMaxS * (T * 128 + 256)];
     __shared__ int pcount;
-    const uint32_t xl_words = XL ? (uint32_t)a.XCAP * (uint32_t)(a.K / 8) + 1u : 0u;
-    uint16_t *plist = reinterpret_cast<uint16_t *>(g_mfma_x + xl_words);
-    uint32_t *xlist = reinterpret_cast<uint32_t *>(g_mfma_x + xl_words + ((uint32_t)a.M * 2u + 15u) / 16u);
+    uint16_t *plist = reinterpret_cast<uint16_t *>(g_mfma_dyn);
+    uint32_t *xlist = reinterpret_cast<uint32_t *>(g_mfma_dyn + ((uint32_t)a.M * 2u + 15u) / 16u);
     const int lane = threadIdx.x & 63;
     const int wig = wave_id();
     const uint32_t e = blockIdx.y;
@@ -669,44 +582,25 @@ __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
     const int64_t plane = (int64_t)e * a.N;
     const Band bd{reinterpret_cast<const uint8_t *>(a.w) + plane * (a.K / 2), a.s + plane * a.G, a.b + plane * a.G,
                   a.N, (uint32_t)(a.K / 2), a.G};
-    const int ps = a.XCAP;
-    for (int base = 0; base < count; base += ps) {
-        const int me = count - base < ps ? count - base : ps;
-        with_xq<XL>(me, [&](auto xq) {
+    for (int base = 0; base < count; base += 16) {
+        const int me = count - base < 16 ? count - base : 16;
+        with_xq(me, [&](auto xq) {
             constexpr int XQ = decltype(xq)::value;
             const Lanes ln = lane_consts<XQ>(a, [&](uint32_t r) {
                 return (int)r < me ? xlist[base + r] * (uint32_t)a.K * 2u : xbytes;
             });
-            mfma_pass<T, XL, !XL, XQ>(a, bd, ln, xr, xbytes, me, xlist + base, PairsOut{a.y, a.N, plist + base},
-                                      rg, groups, red, wt);
+            mfma_pass<T, XQ>(a, bd, ln, xr, me, PairsOut{a.y, a.N, plist + base}, rg, groups, red, wt);
         });
     }
 }
 
-const void *mfma_kernel(int tiles, bool gather, bool x_lds, bool compact_x) {
-    if (gather) {
-        switch (tiles * 2 + (x_lds ? 1 : 0)) {
-            case 2: return reinterpret_cast<const void *>(&gather_mfma_kernel<1, false>);
-            case 3: return reinterpret_cast<const void *>(&gather_mfma_kernel<1, true>);
-            case 4: return reinterpret_cast<const void *>(&gather_mfma_kernel<2, false>);
-            case 5: return reinterpret_cast<const void *>(&gather_mfma_kernel<2, true>);
-        }
-        return nullptr;
-    }
-    if (compact_x && !x_lds) {
-        switch (tiles) {
-            case 1: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, false, 4>);
-            case 2: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, false, 4>);
-        }
-        return nullptr;
-    }
-    switch (tiles * 2 + (x_lds ? 1 : 0)) {
-        case 2: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, false, 2>);
-        case 3: return reinterpret_cast<const void *>(&qmv_mfma_kernel<1, true, 1>);
-        case 4: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, false, 2>);
-        case 5: return reinterpret_cast<const void *>(&qmv_mfma_kernel<2, true, 1>);
-    }
-    return nullptr;
+const void *mfma_kernel(int tiles, bool gather, bool compact_x) {
+    if (gather) return tiles == 1 ? reinterpret_cast<const void *>(&gather_mfma_kernel<1>)
+                                   : reinterpret_cast<const void *>(&gather_mfma_kernel<2>);
+    if (compact_x) return tiles == 1 ? reinterpret_cast<const void *>(&qmv_mfma_kernel<1, 4>)
+                                     : reinterpret_cast<const void *>(&qmv_mfma_kernel<2, 4>);
+    return tiles == 1 ? reinterpret_cast<const void *>(&qmv_mfma_kernel<1, 2>)
+                      : reinterpret_cast<const void *>(&qmv_mfma_kernel<2, 2>);
 }
 
 }  // namespace agq
