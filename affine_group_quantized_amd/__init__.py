@@ -18,7 +18,7 @@ import os
 
 import torch
 
-__all__ = ["qmv", "qmv_wide", "gather_qmv", "dequantize", "plan", "launch_plan", "prepare_qmv", "AgqError",
+__all__ = ["qmv", "qmv_wide", "gather_qmv", "qmm", "gather_qmm", "dequantize", "plan", "launch_plan", "prepare_qmv", "AgqError",
            "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libagq.so")
@@ -60,11 +60,13 @@ def _load(path: str = LIB_PATH):
     lib.agq_qmv.argtypes = [P, P, P, P, P, I64, I64, I, I, P]
     lib.agq_qmv_wide.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
     lib.agq_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
+    lib.agq_qmm.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
+    lib.agq_gather_qmm.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.agq_dequantize.argtypes = [P, P, P, P, I64, I64, I, I, P]
     lib.agq_plan_product.argtypes = [I64, I64, I64, I, I, I, I, I64, ctypes.POINTER(Plan)]
     lib.agq_plan_launch.argtypes = [I64, I64, I64, I, I, I64, ctypes.POINTER(Plan)]
-    for f in (lib.agq_qmv, lib.agq_qmv_wide, lib.agq_gather_qmv, lib.agq_dequantize, lib.agq_plan_product,
-              lib.agq_plan_launch):
+    for f in (lib.agq_qmv, lib.agq_qmv_wide, lib.agq_gather_qmv, lib.agq_qmm, lib.agq_gather_qmm, lib.agq_dequantize,
+              lib.agq_plan_product, lib.agq_plan_launch):
         f.restype = I
     return lib
 
@@ -184,8 +186,36 @@ def qmv_wide(x, w, scales, biases, bits: int = 4, group_size: int = 64, out=None
     return out
 
 
-def gather_qmv(x, w, scales, biases, rhs_indices=None, lhs_indices=None, bits: int = 4, group_size: int = 64,
+def qmm(x, w, scales, biases, bits: int = 4, group_size: int = 64, out=None):
+    """Quantized matrix-matrix product: ``x`` [M, K] bf16 (any M) -> ``y`` [M, N] bf16."""
+    device = x.device
+    _need(x, "x", _BF16, device)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    (N,) = _weights(w, scales, biases, K, bits, group_size, device, 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    else:
+        _need(out, "out", _BF16, device)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    with torch.cuda.device(device):
+        _check(lib.agq_qmm(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(out), M, N, K, bits, group_size,
+                           _stream(device)))
+    return out
+
+
+def gather_qmm(x, w, scales, biases, rhs_indices=None, lhs_indices=None, bits: int = 4, group_size: int = 64,
                out=None, num_pairs: int | None = None):
+    """Expert-gathered matrix-matrix product (MoE prefill); arguments and result as
+    :func:`gather_qmv`, for any number of pairs per expert."""
+    return gather_qmv(x, w, scales, biases, rhs_indices, lhs_indices, bits, group_size, out, num_pairs,
+                      _fn="agq_gather_qmm")
+
+
+def gather_qmv(x, w, scales, biases, rhs_indices=None, lhs_indices=None, bits: int = 4, group_size: int = 64,
+               out=None, num_pairs: int | None = None, _fn: str = "agq_gather_qmv"):
     """Expert-gathered product, one output row per (token, expert) pair.
 
     ``x`` [R, K] bf16; ``w`` [E, N, K*bits/32]; ``scales``/``biases`` [E, N, K/64];
@@ -217,8 +247,8 @@ def gather_qmv(x, w, scales, biases, rhs_indices=None, lhs_indices=None, bits: i
         if tuple(out.shape) != (P, N):
             raise ValueError("out has the wrong shape")
     with torch.cuda.device(device):
-        _check(lib.agq_gather_qmv(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(lhs_indices),
-                                  _ptr(rhs_indices), _ptr(out), P, R, E, N, K, bits, group_size, _stream(device)))
+        _check(getattr(lib, _fn)(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(lhs_indices),
+                                 _ptr(rhs_indices), _ptr(out), P, R, E, N, K, bits, group_size, _stream(device)))
     return out
 
 

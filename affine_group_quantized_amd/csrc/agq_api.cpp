@@ -20,6 +20,7 @@
 #include "agq.h"
 #include "plan.hpp"
 #include "plan_mfma.hpp"
+#include "qmm.hpp"
 #include "qmv_kernels.hpp"
 
 namespace {
@@ -103,6 +104,31 @@ agq_status resident_waves(const void *sym, int threads, size_t lds, int cus, int
         if (g_occ_n < kOccSlots) g_occ[g_occ_n++] = OccEntry{sym, dev, threads, lds, bpc};
     }
     *waves = (int64_t)cus * bpc * (threads / 64);
+    return AGQ_OK;
+}
+
+// Dynamic LDS above the runtime's default 64 KB needs the kernel's limit raised
+// first (once per kernel, device and size).
+constexpr size_t kDefaultDynLds = 65536;
+constexpr size_t kMaxDynLds = 160 * 1024;
+struct LdsEntry {
+    const void *sym;
+    int dev;
+    size_t bytes;
+};
+LdsEntry g_lds[64];
+int g_lds_n = 0;
+std::mutex g_lds_mu;
+
+agq_status allow_lds(const void *sym, size_t bytes, int dev) {
+    if (bytes <= kDefaultDynLds) return AGQ_OK;
+    if (bytes > kMaxDynLds) return fail(AGQ_ENOTSUP, "%zu bytes of LDS exceed the compute unit's", bytes);
+    std::lock_guard<std::mutex> lock(g_lds_mu);
+    for (int i = 0; i < g_lds_n; ++i)
+        if (g_lds[i].sym == sym && g_lds[i].dev == dev && g_lds[i].bytes >= bytes) return AGQ_OK;
+    hipError_t e = hipFuncSetAttribute(sym, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return fail(AGQ_EHIP, "raising the kernel's LDS limit failed: %s", hipGetErrorString(e));
+    if (g_lds_n < 64) g_lds[g_lds_n++] = LdsEntry{sym, dev, bytes};
     return AGQ_OK;
 }
 
@@ -364,6 +390,80 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
     a.E = (int32_t)E;
     return launch(sym, dim3((unsigned)plan.blocks, (unsigned)E), dim3(plan.threads), (size_t)plan.x_lds_bytes, &a,
                   stream);
+}
+
+agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases, void *y, int64_t M,
+                   int64_t N, int64_t K, int bits, int group_size, void *stream) {
+    agq_status st = check_operands(x, w, scales, biases, y, N, K, bits, group_size, true);
+    if (st != AGQ_OK) return st;
+    if (M <= 0) return fail(AGQ_EINVAL, "M must be positive (got %lld)", (long long)M);
+    if (M * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (M*K*2 bytes)");
+    const agq::QmmKernel k = agq::qmm_kernel_for(bits, false);
+    if ((int64_t)k.bn * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
+    const int64_t mt = (M + k.bm - 1) / k.bm, nt = (N + k.bn - 1) / k.bn;
+    if (mt > 65535 || nt > INT32_MAX) return fail(AGQ_ENOTSUP, "grid too large (M=%lld, N=%lld)", (long long)M,
+                                                  (long long)N);
+    int cus = 0, dev = 0;
+    st = current_device(&cus, &dev);
+    if (st != AGQ_OK) return st;
+    agq::QmmArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = w;
+    a.s = static_cast<const uint16_t *>(scales);
+    a.b = static_cast<const uint16_t *>(biases);
+    a.y = static_cast<uint16_t *>(y);
+    a.N = N;
+    a.M = (int32_t)M;
+    a.K = (int32_t)K;
+    a.G = (int32_t)(K / 64);
+    a.rowbytes = (int32_t)(K * bits / 8);
+    a.xbytes = (uint32_t)(M * K * 2);
+    return launch(k.sym, dim3((unsigned)nt, (unsigned)mt), dim3(256), (size_t)k.lds, &a, stream);
+}
+
+agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases,
+                          const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y, int64_t P, int64_t R,
+                          int64_t E, int64_t N, int64_t K, int bits, int group_size, void *stream) {
+    agq_status st = check_operands(x, w, scales, biases, y, N, K, bits, group_size, true);
+    if (st != AGQ_OK) return st;
+    if (P <= 0 || R <= 0 || E <= 0)
+        return fail(AGQ_EINVAL, "P, R and E must be positive (P=%lld, R=%lld, E=%lld)", (long long)P,
+                    (long long)R, (long long)E);
+    if (!lhs_indices && R != P) return fail(AGQ_EINVAL, "lhs_indices == NULL requires R == P");
+    if (!rhs_indices && E != P) return fail(AGQ_EINVAL, "rhs_indices == NULL requires E == P");
+    if (misaligned(lhs_indices, 4) || misaligned(rhs_indices, 4))
+        return fail(AGQ_EINVAL, "index arrays must be 4-byte aligned");
+    if (P > agq::kMaxPairs) return fail(AGQ_ENOTSUP, "P=%lld pairs exceeds %d", (long long)P, agq::kMaxPairs);
+    if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
+    if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
+    if (R * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (R*K*2 bytes)");
+    const agq::QmmKernel k = agq::qmm_kernel_for(bits, true);
+    if ((int64_t)k.bn * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
+    const int64_t nt = (N + k.bn - 1) / k.bn;
+    if (nt > INT32_MAX) return fail(AGQ_ENOTSUP, "N too large");
+    int cus = 0, dev = 0;
+    st = current_device(&cus, &dev);
+    if (st != AGQ_OK) return st;
+    agq::QmmArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = w;
+    a.s = static_cast<const uint16_t *>(scales);
+    a.b = static_cast<const uint16_t *>(biases);
+    a.y = static_cast<uint16_t *>(y);
+    a.lhs = lhs_indices;
+    a.rhs = rhs_indices;
+    a.N = N;
+    a.M = (int32_t)P;
+    a.K = (int32_t)K;
+    a.G = (int32_t)(K / 64);
+    a.rowbytes = (int32_t)(K * bits / 8);
+    a.xbytes = (uint32_t)(R * K * 2);
+    a.R_x = (int32_t)R;
+    a.E = (int32_t)E;
+    const size_t lds = (size_t)k.lds + (size_t)((P * 2 + 15) / 16 * 16 + P * 4);
+    st = allow_lds(k.sym, lds, dev);
+    if (st != AGQ_OK) return st;
+    return launch(k.sym, dim3((unsigned)nt, (unsigned)E), dim3(256), lds, &a, stream);
 }
 
 agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *biases, float *out, int64_t rows,

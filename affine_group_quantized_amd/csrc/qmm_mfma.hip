@@ -1,0 +1,402 @@
+// Affine group-quantized matrix-matrix product (qmm) and its expert-gathered
+// form (gather_qmm) on the gfx950 matrix cores: the prefill-side products that
+// "epic: CUDA (MLX backend) prefill and decode acceleration program" names in
+// its Code-audit findings (qmm / gather_gemm) and whose MoE form carries that
+// page's largest measured gap (Diagnosis (baseline), the MoE prefill row).
+//
+// Same operands as the matvec kernels: BF16 activations x [M, K] (or the x
+// rows the gather's pairs select), U32-packed 4- or 8-bit codes (low-first)
+// [N, K*bits/32], BF16 scale and bias per 64-column group; y [M, N] BF16.
+//
+// Exactness. A dequantized weight s*q + b needs up to 24 significant bits, so
+// rounding it to bfloat16 for the matrix cores could cost up to 2^-8 of
+// sum |x*w| per output. Instead the B operand holds values that bfloat16
+// represents exactly, and the scale and bias are applied per group in fp32:
+//   4-bit: B = 128 + q (a code in the low mantissa bits of 0x4300),
+//          y += s*D + (b - 128*s)*X
+//   8-bit: B = q (at most 8 significant bits),
+//          y += s*D + b*X
+// where D is the group's dot product of x with B (v_mfma_f32_16x16x32_bf16,
+// exact products, fp32 sums) and X the group's sum of x (the same A operands
+// against an all-ones B).
+//
+// Tiling. A block of 4 waves (2 x 2) computes a tile of BM = 32*TM activation
+// rows by BN = 32*TN weight rows; wave (wm, wn) owns 16*TM x 16*TN of it. K
+// advances one 64-column group at a time. Per group the block stages into LDS:
+//  - x: BM rows x 8 words of 8 columns (16 bytes each), already in A-operand
+//    order (4-bit: the bfloat16 pairs (c0,c4) (c1,c5) (c2,c6) (c3,c7) of each
+//    8-column word, matching the code unpack; 8-bit: natural order);
+//  - codes: BN rows x 8 words, unpacked to B-operand bfloat16 (each weight is
+//    unpacked once per block and read by both waves of its column);
+//  - the group's scale and bias of each of the BN rows.
+// Word w of a row sits at slot w ^ (row & 7): the 16 lanes of a lane group
+// read 16 rows of one word, and the XOR spreads them over all 64 banks.
+// Global loads run DEPTH groups ahead in registers; the LDS tiles are double
+// buffered, so each group costs one block barrier.
+//
+// Lanes and MFMA operands (16x16x32, bf16): lane l, g = l / 16, i = l % 16.
+// A: row i of the 16-row sub-tile, words 4*step + g; B: weight row i of the
+// sub-tile, the same words; D: lane holds D[4*g + r][i], r < 4.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmm.hpp"
+#include "qmv_device.hpp"
+
+namespace agq {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRsrc = 0x00020000;  // raw buffer, 32-bit data format
+constexpr uint32_t kOne2 = 0x3F803F80u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrc);
+}
+
+__device__ __forceinline__ f32x4 mma(const u32x4 &a, const u32x4 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+}
+
+// A-operand order of one 8-column word of x for 4-bit codes.
+__device__ __forceinline__ u32x4 x_pairs(const u32x4 &q) {
+    return u32x4{byte_perm(q.z, q.x, 0x05040100u), byte_perm(q.z, q.x, 0x07060302u),
+                 byte_perm(q.w, q.y, 0x05040100u), byte_perm(q.w, q.y, 0x07060302u)};
+}
+
+// B operand of one packed 4-bit word: bfloat16 (128 + q) pairs (q0,q4) (q1,q5) (q2,q6) (q3,q7).
+__device__ __forceinline__ u32x4 codes4(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    return u32x4{byte_perm(kMagic43, lo, kSelEven), byte_perm(kMagic43, hi, kSelEven),
+                 byte_perm(kMagic43, lo, kSelOdd), byte_perm(kMagic43, hi, kSelOdd)};
+}
+
+// B operand of two packed 8-bit words (8 codes, natural order) as bfloat16 q.
+// (float)q has at most 8 significant bits, so its top half is q exactly.
+__device__ __forceinline__ uint32_t pair8(float a, float b) {
+    return byte_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+__device__ __forceinline__ u32x4 codes8(uint32_t w0, uint32_t w1) {
+    // (float of a masked byte compiles to v_cvt_f32_ubyte{0..3})
+    return u32x4{pair8((float)(w0 & 0xFFu), (float)((w0 >> 8) & 0xFFu)),
+                 pair8((float)((w0 >> 16) & 0xFFu), (float)(w0 >> 24)),
+                 pair8((float)(w1 & 0xFFu), (float)((w1 >> 8) & 0xFFu)),
+                 pair8((float)((w1 >> 16) & 0xFFu), (float)(w1 >> 24))};
+}
+
+template <int BITS, int TM, int TN>
+struct Tile {
+    static constexpr int BM = 32 * TM, BN = 32 * TN;
+    static constexpr int THREADS = 256;
+    static constexpr int XW = BM * 8;                  // 16-byte x words per group
+    static constexpr int XPT = XW / THREADS;           // per thread
+    static constexpr int WB = BN * 8 * BITS;           // bytes of codes per group
+    static constexpr int WPT = WB / 16 / THREADS;      // 16-byte code loads per thread (BITS * BN / 512)
+    static constexpr int WPT1 = WPT > 0 ? WPT : 1;
+    static constexpr int WTHREADS = WB / 16;           // threads that load codes
+    // LDS per buffer: x words, B words, scale and bias (bf16 each) per weight row.
+    static constexpr int LDS_X = XW * 16, LDS_W = BN * 8 * 16, LDS_SB = BN * 4;
+    static constexpr int LDS_BUF = LDS_X + LDS_W + LDS_SB;
+    static_assert(XW % THREADS == 0, "x tile words must divide among the threads");
+    static_assert(WPT > 0 || WTHREADS <= THREADS, "a code tile smaller than the block takes one load per thread");
+};
+
+// Registers of one group's global loads.
+template <int BITS, int TM, int TN>
+struct Stage {
+    using TT = Tile<BITS, TM, TN>;
+    u32x4 x[TT::XPT];
+    u32x4 w[TT::WPT1];
+    uint16_t sb;  // the scale (threads < BN) or bias (threads BN .. 2*BN-1) of one weight row
+};
+
+// Which x row a tile row reads and which output row it writes.
+struct DenseMap {
+    int64_t m0;  // first activation row of the tile
+    int64_t M;
+    __device__ __forceinline__ int64_t xrow(int r) const { return m0 + r < M ? m0 + r : -1; }
+    __device__ __forceinline__ int64_t yrow(int r) const { return m0 + r < M ? m0 + r : -1; }
+};
+struct GatherMap {
+    const uint16_t *plist;  // pairs of the tile (LDS)
+    const uint32_t *xlist;  // their x rows (LDS)
+    int count;              // pairs in the tile
+    __device__ __forceinline__ int64_t xrow(int r) const { return r < count ? (int64_t)xlist[r] : -1; }
+    __device__ __forceinline__ int64_t yrow(int r) const { return r < count ? (int64_t)plist[r] : -1; }
+};
+
+// Global loads of group `grp` for the block's tile. Rows outside the tile
+// (x rows past M or the pass, weight rows past N) read zero through the
+// buffer ranges; every load is unconditional.
+template <int BITS, int TM, int TN, typename Map>
+__device__ __forceinline__ void load_group(Stage<BITS, TM, TN> &st, const QmmArgs &a, const Map &map,
+                                           __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t wr,
+                                           __amdgpu_buffer_rsrc_t sr, __amdgpu_buffer_rsrc_t br, int grp,
+                                           uint32_t xbytes) {
+    using TT = Tile<BITS, TM, TN>;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < TT::XPT; ++k) {
+        const int idx = t + k * TT::THREADS;  // x word: row idx / 8, word idx % 8
+        const int64_t row = map.xrow(idx >> 3);
+        const uint32_t off = row >= 0 ? (uint32_t)(row * a.K + grp * 64 + (idx & 7) * 8) * 2u : xbytes;
+        st.x[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+    }
+    // Codes: weight row n = t / (BITS/2), 16-byte piece t % (BITS/2) of the row's 32*BITS/8... bytes
+    // (4-bit: 32 bytes per row per group, two threads; 8-bit: 64 bytes, four threads).
+    constexpr int PPR = BITS / 2;  // 16-byte pieces per row per group
+#pragma unroll
+    for (int k = 0; k < TT::WPT1; ++k) {
+        const int idx = t + k * TT::THREADS;
+        const uint32_t row = (uint32_t)(idx / PPR), piece = (uint32_t)(idx % PPR);
+        const uint32_t off = row * (uint32_t)a.rowbytes + (uint32_t)grp * (uint32_t)(8 * BITS) + piece * 16u;
+        st.w[k] = (TT::WPT > 0 || t < TT::WTHREADS) ? __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2)
+                                                    : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (t < 2 * TT::BN) {
+        const uint32_t row = (uint32_t)(t % TT::BN);
+        const uint32_t off = (row * (uint32_t)a.G + (uint32_t)grp) * 2u;
+        st.sb = t < TT::BN ? __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0)
+                           : __builtin_amdgcn_raw_buffer_load_b16(br, off, 0, 0);
+    }
+}
+
+template <int BITS, int TM, int TN>
+__device__ __forceinline__ void store_group(const Stage<BITS, TM, TN> &st, uint8_t *buf) {
+    using TT = Tile<BITS, TM, TN>;
+    u32x4 *xs = reinterpret_cast<u32x4 *>(buf);
+    u32x4 *ws = reinterpret_cast<u32x4 *>(buf + TT::LDS_X);
+    uint16_t *sb = reinterpret_cast<uint16_t *>(buf + TT::LDS_X + TT::LDS_W);
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < TT::XPT; ++k) {
+        const int idx = t + k * TT::THREADS;
+        const int row = idx >> 3, word = idx & 7;
+        xs[row * 8 + (word ^ (row & 7))] = BITS == 4 ? x_pairs(st.x[k]) : st.x[k];
+    }
+    constexpr int PPR = BITS / 2;
+#pragma unroll
+    for (int k = 0; k < TT::WPT1; ++k) {
+        const int idx = t + k * TT::THREADS;
+        if (TT::WPT > 0 || t < TT::WTHREADS) {
+            const int row = idx / PPR, piece = idx % PPR;
+            const u32x4 v = st.w[k];
+            if constexpr (BITS == 4) {
+                // 4 words = 4 B-operand words (8 columns each): words 4*piece .. +3
+                const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int word = 4 * piece + i;
+                    ws[row * 8 + (word ^ (row & 7))] = codes4(d[i]);
+                }
+            } else {
+                // 4 words = 2 B-operand words: words 2*piece, 2*piece + 1
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int word = 2 * piece + i;
+                    ws[row * 8 + (word ^ (row & 7))] = codes8(i == 0 ? v.x : v.z, i == 0 ? v.y : v.w);
+                }
+            }
+        }
+    }
+    if (t < 2 * TT::BN) sb[t] = st.sb;  // scales [0, BN), biases [BN, 2*BN)
+}
+
+// One group's products on the wave's 16*TM x 16*TN sub-tiles, folded into acc.
+template <int BITS, int TM, int TN>
+__device__ __forceinline__ void compute_group(const uint8_t *buf, int wm, int wn, f32x4 (&acc)[TM][TN]) {
+    using TT = Tile<BITS, TM, TN>;
+    const u32x4 *xs = reinterpret_cast<const u32x4 *>(buf);
+    const u32x4 *ws = reinterpret_cast<const u32x4 *>(buf + TT::LDS_X);
+    const uint16_t *sb = reinterpret_cast<const uint16_t *>(buf + TT::LDS_X + TT::LDS_W);
+    const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const u32x4 ones = {kOne2, kOne2, kOne2, kOne2};
+    f32x4 d[TM][TN], xsum[TM];
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+        const int word = 4 * step + g;
+        u32x4 av[TM], bv[TN];
+#pragma unroll
+        for (int m = 0; m < TM; ++m) {
+            const int row = wm * 16 * TM + 16 * m + i;
+            av[m] = xs[row * 8 + (word ^ (row & 7))];
+        }
+#pragma unroll
+        for (int n = 0; n < TN; ++n) {
+            const int row = wn * 16 * TN + 16 * n + i;
+            bv[n] = ws[row * 8 + (word ^ (row & 7))];
+        }
+#pragma unroll
+        for (int m = 0; m < TM; ++m) {
+            xsum[m] = mma(av[m], ones, step == 0 ? z : xsum[m]);
+#pragma unroll
+            for (int n = 0; n < TN; ++n) d[m][n] = mma(av[m], bv[n], step == 0 ? z : d[m][n]);
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < TN; ++n) {
+        const int row = wn * 16 * TN + 16 * n + i;
+        const float s = bf16_lo(sb[row]), b = bf16_lo(sb[TT::BN + row]);
+        const float c = BITS == 4 ? fmaf(-128.f, s, b) : b;
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[m][n][r] = fmaf(s, d[m][n][r], fmaf(c, xsum[m][r], acc[m][n][r]));
+    }
+}
+
+// The tile rows [.., BM) of `map` against weight rows [n0, n0 + BN) of one plane.
+template <int BITS, int TM, int TN, int DEPTH, typename Map>
+__device__ __forceinline__ void qmm_tile(const QmmArgs &a, const Map &map, const uint32_t *w, const uint16_t *s,
+                                         const uint16_t *b, int64_t n0, uint8_t *lds) {
+    using TT = Tile<BITS, TM, TN>;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
+    const int64_t nrows = a.N - n0 < TT::BN ? a.N - n0 : TT::BN;
+    const uint32_t xbytes = a.xbytes;
+    const __amdgpu_buffer_rsrc_t xr = span(a.x, xbytes);
+    const __amdgpu_buffer_rsrc_t wr = span(w + n0 * (a.rowbytes / 4), (uint32_t)(nrows * a.rowbytes));
+    const __amdgpu_buffer_rsrc_t sr = span(s + n0 * a.G, (uint32_t)(nrows * a.G * 2));
+    const __amdgpu_buffer_rsrc_t br = span(b + n0 * a.G, (uint32_t)(nrows * a.G * 2));
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    Stage<BITS, TM, TN> st[DEPTH];
+#pragma unroll
+    for (int p = 0; p < DEPTH; ++p)
+        load_group<BITS, TM, TN>(st[p], a, map, xr, wr, sr, br, p < a.G ? p : a.G - 1, xbytes);
+    store_group<BITS, TM, TN>(st[0], lds);
+    __syncthreads();
+    // Group grp computes from LDS buffer grp & 1 while the loads of grp + DEPTH
+    // go out into the register stage grp just freed.
+    for (int grp0 = 0; grp0 < a.G; grp0 += DEPTH) {
+#pragma unroll
+        for (int p = 0; p < DEPTH; ++p) {
+            const int grp = grp0 + p;
+            if (grp < a.G) {  // uniform
+                compute_group<BITS, TM, TN>(lds + (grp & 1) * TT::LDS_BUF, wm, wn, acc);
+                if (grp + 1 < a.G) store_group<BITS, TM, TN>(st[(p + 1) % DEPTH], lds + ((grp + 1) & 1) * TT::LDS_BUF);
+                const int nxt = grp + DEPTH;
+                load_group<BITS, TM, TN>(st[p], a, map, xr, wr, sr, br, nxt < a.G ? nxt : a.G - 1, xbytes);
+                __syncthreads();
+            }
+        }
+    }
+    // Store: lane holds rows 4g + r of sub-tile m, weight row i of sub-tile n.
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t yr = map.yrow(wm * 16 * TM + 16 * m + 4 * g + r);
+            if (yr < 0) continue;
+#pragma unroll
+            for (int n = 0; n < TN; ++n) {
+                const int64_t col = wn * 16 * TN + 16 * n + i;
+                if (col < nrows) a.y[yr * a.N + n0 + col] = f32_to_bf16(acc[m][n][r]);
+            }
+        }
+}
+
+}  // namespace
+
+// Dense: blockIdx.x = weight-row tile, blockIdx.y = activation-row tile.
+template <int BITS, int TM, int TN, int DEPTH>
+__global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
+    using TT = Tile<BITS, TM, TN>;
+    const DenseMap map{(int64_t)blockIdx.y * TT::BM, a.M};
+    qmm_tile<BITS, TM, TN, DEPTH>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * TT::BN, qmm_lds);
+}
+
+// Gather: blockIdx.x = weight-row tile, blockIdx.y = expert plane e. The
+// block lists the pairs routed to e (ascending p) and walks them BM at a
+// time. Blocks of plane 0 also write NaN rows for pairs whose indices are out
+// of range. LDS after the tile buffers: pair list (uint16) and x rows (uint32).
+template <int BITS, int TM, int TN, int DEPTH>
+__global__ __launch_bounds__(256) void gather_qmm_kernel(QmmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
+    using TT = Tile<BITS, TM, TN>;
+    uint16_t *plist = reinterpret_cast<uint16_t *>(qmm_lds + 2 * TT::LDS_BUF);
+    uint32_t *xlist = reinterpret_cast<uint32_t *>(qmm_lds + 2 * TT::LDS_BUF + ((a.M * 2 + 15) / 16) * 16);
+    __shared__ int wave_counts[4];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const uint32_t e = blockIdx.y;
+    const int64_t n0 = (int64_t)blockIdx.x * TT::BN;
+    const uint32_t nx = (uint32_t)a.R_x, ne = (uint32_t)a.E;
+
+    // Block-wide ordered compaction of the pairs p < P that satisfy pred into plist.
+    auto compact = [&](auto pred) {
+        int total = 0;
+        for (int base = 0; base < a.M; base += 256) {
+            const int p = base + t;
+            const bool take = p < a.M && pred(p);
+            const uint64_t mask = __ballot(take);
+            if (lane == 0) wave_counts[wave] = __popcll(mask);
+            __syncthreads();
+            int before = total;
+            for (int v = 0; v < wave; ++v) before += wave_counts[v];
+            if (take) plist[before + __popcll(mask & ((1ull << lane) - 1ull))] = (uint16_t)p;
+            total += wave_counts[0] + wave_counts[1] + wave_counts[2] + wave_counts[3];
+            __syncthreads();
+        }
+        return total;
+    };
+    if (e == 0) {
+        const int nbad = compact([&](int p) {
+            const uint32_t xr = a.lhs ? a.lhs[p] : (uint32_t)p;
+            const uint32_t ex = a.rhs ? a.rhs[p] : (uint32_t)p;
+            return xr >= nx || ex >= ne;
+        });
+        for (int k = 0; k < nbad; ++k)
+            for (int c = t; c < TT::BN; c += 256)
+                if (n0 + c < a.N) a.y[(int64_t)plist[k] * a.N + n0 + c] = 0x7FC0u;
+        __syncthreads();
+    }
+    const int count = compact([&](int p) {
+        const uint32_t xr = a.lhs ? a.lhs[p] : (uint32_t)p;
+        const uint32_t ex = a.rhs ? a.rhs[p] : (uint32_t)p;
+        return ex == e && xr < nx;
+    });
+    for (int k = t; k < count; k += 256) xlist[k] = a.lhs ? a.lhs[plist[k]] : (uint32_t)plist[k];
+    __syncthreads();
+    if (count == 0) return;
+    const int64_t plane = (int64_t)e * a.N;
+    const uint32_t *w = a.w + plane * (a.rowbytes / 4);
+    const uint16_t *s = a.s + plane * a.G, *b = a.b + plane * a.G;
+    for (int base = 0; base < count; base += TT::BM) {
+        const GatherMap map{plist + base, xlist + base, count - base < TT::BM ? count - base : TT::BM};
+        qmm_tile<BITS, TM, TN, DEPTH>(a, map, w, s, b, n0, qmm_lds);
+        __syncthreads();  // the LDS tiles are refilled by the next pass
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel selection.
+
+template <int BITS>
+static QmmKernel qmm_pick(bool gather) {
+    constexpr int TM = kQmmTM, TN = kQmmTN, D = kQmmDepth;
+    QmmKernel k;
+    k.sym = gather ? reinterpret_cast<const void *>(&gather_qmm_kernel<BITS, TM, TN, D>)
+                   : reinterpret_cast<const void *>(&qmm_kernel<BITS, TM, TN, D>);
+    k.bm = Tile<BITS, TM, TN>::BM;
+    k.bn = Tile<BITS, TM, TN>::BN;
+    k.lds = 2 * Tile<BITS, TM, TN>::LDS_BUF;
+    return k;
+}
+
+QmmKernel qmm_kernel_for(int bits, bool gather) { return bits == 4 ? qmm_pick<4>(gather) : qmm_pick<8>(gather); }
+
+}  // namespace agq

@@ -15,15 +15,16 @@
  * of word k / (32/bits) of packed row n. W is [N out, K in]. Arithmetic is in
  * fp32, and outputs are BF16, rounded to nearest even.
  *
- * The three product entry points map to the decode kernels those pages
- * discuss:
+ * The product entry points map to the kernels those pages discuss:
  *  - agq_qmv is the batch-1 matvec;
  *  - agq_qmv_wide is the small-batch "qmv_wide" / multirow variant for
  *    M*B > 1, named in "epic: CUDA (MLX backend) prefill and decode
  *    acceleration program", Code-audit findings, and in the post-reboot
  *    re-measurement pasted into mlxcel PR #727;
  *  - agq_gather_qmv is the expert-gathered (MoE) form of the gather_qmm path
- *    in the same epic.
+ *    in the same epic;
+ *  - agq_qmm and agq_gather_qmm are the matrix-matrix (prefill) forms of the
+ *    two.
  *
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers to contiguous row-major arrays. The
@@ -65,10 +66,15 @@ typedef enum agq_status {
 /* Library ABI version (major*10000 + minor*100 + patch). */
 int agq_version(void);
 
-/* Human-readable name of a status code. The string is static. */
+/*
+ * Status handling. "MLX CUDA Cleanup Plan", Target Architecture §4, keeps the
+ * runtime-facing layer to small safe wrappers for status handling, streams
+ * and memory; these two calls are that wrapper here.
+ * agq_status_str: human-readable name of a status code (a static string).
+ * agq_last_error: detail message of the last non-OK status returned on the
+ * calling thread ("" if none); valid until the thread's next failing call.
+ */
 const char *agq_status_str(agq_status status);
-
-/* Detail message of the last non-OK status returned on this thread ("" if none). */
 const char *agq_last_error(void);
 
 /*
@@ -123,7 +129,41 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
                           int bits, int group_size, void *stream);
 
 /*
- * Dequantize to fp32: out[n, k] = scale[n, k/64] * q[n, k] + bias[n, k/64],
+ * Quantized matrix-matrix product ("qmm", the prefill form): for any M >= 1,
+ *     y[m, n] = sum_k x[m, k] * w_hat[n, k]
+ *   x [M, K] BF16, y [M, N] BF16; w, scales and biases as in agq_qmv.
+ * The quantized GEMM that "epic: CUDA (MLX backend) prefill and decode
+ * acceleration program", Code-audit findings, names beside qmv_wide (its
+ * JIT-compiled qmm), and that Phase 6 of that epic (#637, quantized GEMM for
+ * prefill) plans. It runs on the matrix cores with bfloat16 operands that
+ * hold the codes exactly (128 + q for 4-bit, q for 8-bit) and applies each
+ * group's scale and bias in fp32, so its error bound is that of the matvec
+ * forms. M*K*2 must stay below 2^31 (else AGQ_ENOTSUP). Argument checks and
+ * errors as for agq_qmv.
+ */
+agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases, void *y,
+                   int64_t M, int64_t N, int64_t K, int bits, int group_size, void *stream);
+
+/*
+ * Expert-gathered matrix-matrix product (MoE prefill, the gather_qmm of the
+ * same epic: its Diagnosis (baseline) MoE prefill row is the largest measured
+ * gap on those pages, and Phase 3 (#629) targets it). Same arguments and
+ * result as agq_gather_qmv, for any number of pairs per expert: each plane
+ * that some pair uses streams once per 64 of its pairs, with every tile of x
+ * rows gathered through the pair's lhs index. P may be at most 4096; R*K*2
+ * must stay below 2^31. Out-of-range indices give NaN rows, as in
+ * agq_gather_qmv.
+ */
+agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases,
+                          const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y,
+                          int64_t P, int64_t R, int64_t E, int64_t N, int64_t K,
+                          int bits, int group_size, void *stream);
+
+/*
+ * The dequantization step on its own, as a check of the unpack and affine map
+ * of "MLX CUDA Cleanup Plan", Target Architecture §1 (U32-packed codes with
+ * BF16 scales and biases), against which the products can be verified bit for
+ * bit. Dequantize to fp32: out[n, k] = scale[n, k/64] * q[n, k] + bias[n, k/64],
  * formed with one fused multiply-add, so each output is the exact value
  * rounded once to binary32. The exact value is representable, and the result
  * therefore exact, unless the bias exceeds the scale by more than about 2^15

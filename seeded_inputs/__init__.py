@@ -42,7 +42,7 @@ CHUNK_ROWS = 1024
 __all__ = [
     "GROUP_SIZE", "CHUNK_ROWS", "stream", "bf16_bits", "bf16_to_f32",
     "pack_codes", "quantize_rows", "draw_activations", "draw_quantized_weight",
-    "random_codes", "workload", "WORKLOADS", "moe_expert_ids",
+    "random_codes", "workload", "WORKLOADS", "moe_expert_ids", "moe_prefill",
 ]
 
 
@@ -189,6 +189,18 @@ WORKLOADS = {
 }
 
 MOE = {"experts": 8, "tokens": 16, "top_k": 2, "hidden": 4096, "ffn": 14336, "bits": 4}
+
+
+def moe_prefill(tokens: int = 512) -> dict:
+    """Routing and activations of a Mixtral-shaped MoE prefill (stream cfg 5): ``x``
+    [tokens, 4096] ~ N(0,1) bf16, ``ids`` [tokens, 2] distinct experts per token,
+    ``rhs`` = ids flattened (pair p = token*2 + slot) and ``lhs`` = the token of each
+    pair. The expert planes are those of workload 4 (its ``w1``)."""
+    m = MOE
+    ids = moe_expert_ids(5, 1, tokens, m["experts"], m["top_k"])
+    return {"x": draw_activations(5, 0, tokens, m["hidden"]), "ids": ids,
+            "rhs": ids.reshape(-1).astype(np.uint32),
+            "lhs": np.repeat(np.arange(tokens, dtype=np.uint32), m["top_k"])}
 
 
 def workload(cfg: int, only=None, keep_codes: bool = False) -> dict:

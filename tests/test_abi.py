@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("agq_qmv", "agq_qmv_wide", "agq_gather_qmv", "agq_dequantize", "agq_status_str",
-                 "agq_last_error", "agq_version", "agq_plan_product", "agq_plan_launch"):
+    for want in ("agq_qmv", "agq_qmv_wide", "agq_gather_qmv", "agq_qmm", "agq_gather_qmm", "agq_dequantize",
+                 "agq_status_str", "agq_last_error", "agq_version", "agq_plan_product", "agq_plan_launch"):
         assert want in names
 
 
@@ -58,6 +58,14 @@ def wide(M=2, x=A, N=16, K=64, bits=4, gs=64):
 
 def gather(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     return lib.agq_gather_qmv(x, A, A, A, lhs, rhs, A, P, R, E, N, K, bits, gs, None)
+
+
+def qmm(M=16, x=A, N=16, K=64, bits=4, gs=64, y=A):
+    return lib.agq_qmm(x, A, A, A, y, M, N, K, bits, gs, None)
+
+
+def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
+    return lib.agq_gather_qmm(x, A, A, A, lhs, rhs, A, P, R, E, N, K, bits, gs, None)
 
 
 @pytest.mark.parametrize("call,status", [
@@ -95,6 +103,20 @@ def gather(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: gather(P=4097, R=4097, E=4), ENOTSUP),
     (lambda: gather(E=70000), ENOTSUP),
     (lambda: gather(K=16384 + 64), ENOTSUP),
+    (lambda: qmm(M=0), EINVAL),
+    (lambda: qmm(x=NUL), EINVAL),
+    (lambda: qmm(y=NUL), EINVAL),
+    (lambda: qmm(K=96), EINVAL),
+    (lambda: qmm(bits=2), ENOTSUP),
+    (lambda: qmm(gs=128, K=128), ENOTSUP),
+    (lambda: qmm(x=A2), EINVAL),
+    (lambda: qmm(M=1 << 20, K=1024), ENOTSUP),
+    (lambda: gqmm(P=0), EINVAL),
+    (lambda: gqmm(lhs=NUL, R=3), EINVAL),
+    (lambda: gqmm(rhs=NUL, E=3), EINVAL),
+    (lambda: gqmm(P=4097, R=4097, E=4), ENOTSUP),
+    (lambda: gqmm(E=70000), ENOTSUP),
+    (lambda: gqmm(R=1 << 20, K=1024), ENOTSUP),
     (lambda: lib.agq_dequantize(A, A, A, ctypes.c_void_p(0x10004), 4, 64, 4, 64, None), EINVAL),
     (lambda: lib.agq_dequantize(A, A, A, A, 4, 64, 5, 64, None), ENOTSUP),
 ])

@@ -1,0 +1,160 @@
+"""GPU parity of the quantized GEMM forms (agq_qmm, agq_gather_qmm) against the CPU oracle.
+
+Same tolerance as the matvec forms: |y_gpu - y_ref| <= 2e-3 * sum_k |x_k * w_hat_k| per
+output element, plus half a bf16 ulp of y_ref where K <= 128 (there |y| can come close to
+that sum, and the bf16 output rounding alone can exceed 2e-3 of it). Shapes cover one and several 64-row activation tiles, ragged activation
+and weight-row tails, K of one group, and both code widths. Where the oracle would take
+minutes, the checked output rows are every row that sits on a tile or sub-tile seam (n
+mod 128 in {0, 15, 16, 31, 32, 63, 64, 127}) plus every 13th row.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from gpu_util import bf16_bits_host, bf16_dev, bf16_host, check_close, progress, u32_dev
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import affine_group_quantized_amd as agq  # noqa: E402
+
+
+def seam_rows(N):
+    n = np.arange(N)
+    keep = np.isin(n % 128, [0, 15, 16, 31, 32, 63, 64, 127]) | (n % 13 == 0) | (n == N - 1)
+    return n[keep]
+
+
+def dev_weight(d):
+    return u32_dev(d["w"]), bf16_dev(d["scales"]), bf16_dev(d["biases"])
+
+
+@pytest.mark.parametrize("bits,M,N,K,sample", [
+    (4, 9, 100, 512, False), (4, 16, 257, 4096, False), (4, 64, 128, 4096, False), (4, 65, 300, 1088, False),
+    (4, 33, 64, 192, False), (4, 1, 5, 64, False), (4, 8, 1000, 4096, False), (4, 200, 131, 64, False),
+    (4, 512, 4099, 4096, True), (4, 130, 14336, 4096, True), (4, 96, 4096, 14336, True),
+    (8, 9, 100, 896, False), (8, 65, 300, 4864, False), (8, 100, 129, 64, False), (8, 512, 1000, 896, True),
+])
+def test_qmm_shapes(bits, M, N, K, sample):
+    d = si.draw_quantized_weight(30, 100 * bits + M, N, K, bits)
+    x = si.draw_activations(30, 1000 + M, M, K)
+    w, s, b = dev_weight(d)
+    progress(f"qmm bits={bits} M={M} N={N} K={K}")
+    y = agq.qmm(bf16_dev(x), w, s, b, bits=bits)
+    torch.cuda.synchronize()
+    rows = seam_rows(N) if sample else None
+    y_ref, A = oracle.qmv(x, d["w"], d["scales"], d["biases"], K, bits, rows=rows)
+    yg = y if rows is None else y[:, torch.as_tensor(rows, device=y.device)]
+    # With one or two groups |y| can approach sum|x*w|, and then half a bf16 ulp of output
+    # rounding alone exceeds 2e-3 of it: those shapes also allow that half ulp.
+    worst = check_close(yg, y_ref, A, f"qmm M={M} N={N} K={K} bits={bits}", extra_half_ulp=K <= 128)
+    progress(f"qmm: ok, worst |err|/A = {worst:.3e}")
+
+
+def test_qmm_is_deterministic_and_scales_by_powers_of_two():
+    N, K, M = 700, 4096, 100
+    d = si.draw_quantized_weight(31, 1, N, K, 4)
+    w, s, b = dev_weight(d)
+    xd = bf16_dev(si.draw_activations(31, 2, M, K))
+    progress("qmm determinism")
+    y1 = bf16_bits_host(agq.qmm(xd, w, s, b))
+    y2 = bf16_bits_host(agq.qmm(xd, w, s, b))
+    assert np.array_equal(y1, y2)
+    assert np.array_equal(bf16_host(agq.qmm(xd * 8, w, s, b)), 8 * bf16_host(agq.qmm(xd, w, s, b)))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_qmm_one_hot_columns_are_bitwise_weights(bits):
+    """x = e_k gives y[n] = bf16(w_hat[n, k]) exactly on the matrix-core GEMM (one exact
+    product per output; the group correction cancels the 128 offset exactly)."""
+    N, K = 300, 256
+    d = si.draw_quantized_weight(32, bits, N, K, bits)
+    w, s, b = dev_weight(d)
+    ref, bad = oracle.dequantize(d["w"], d["scales"], d["biases"], K, bits)
+    assert bad == 0
+    want = si.bf16_bits(ref.astype(np.float32))
+    cols = np.arange(K)
+    x = np.zeros((K, K), np.uint16)
+    x[cols, cols] = 0x3F80
+    progress(f"qmm one-hot bits={bits}")
+    got = bf16_bits_host(agq.qmm(bf16_dev(x), w, s, b, bits=bits))
+    assert np.array_equal(got, want.T)
+
+
+@pytest.fixture(scope="module")
+def moe_w1():
+    progress("generating the Mixtral-shaped W1 planes")
+    return si.workload(4, only=("w1",))["w1"]
+
+
+def test_gather_qmm_mixtral_prefill(moe_w1):
+    """512 tokens, top-2 of 8 experts (1024 pairs) through the Mixtral-shaped W1 planes."""
+    m = moe_w1
+    pre = si.moe_prefill(512)
+    E, N, K = m["E"], m["N"], m["K"]
+    progress(f"gather_qmm prefill P={len(pre['rhs'])} E={E} N={N} K={K}")
+    y = agq.gather_qmm(bf16_dev(pre["x"]), u32_dev(m["w"]), bf16_dev(m["scales"]), bf16_dev(m["biases"]),
+                       rhs_indices=u32_dev(pre["rhs"]), lhs_indices=u32_dev(pre["lhs"]))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([seam_rows(N)[::4], [0, 127, 128, N - 1]]))
+    y_ref, A = oracle.gather_qmv(pre["x"], m["w"], m["scales"], m["biases"], pre["lhs"], pre["rhs"], K, 4,
+                                 rows=rows)
+    worst = check_close(y[:, torch.as_tensor(rows, device=y.device)], y_ref, A, "gather_qmm prefill")
+    progress(f"gather_qmm prefill: ok, worst |err|/A = {worst:.3e}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gather_qmm_edges(bits):
+    """Experts with 0, 1, 64, 65 and 150 pairs, repeated and scattered x rows, an
+    out-of-range pair of each kind (NaN rows), and NULL indices as the identity."""
+    E, N, K, R = 5, 200, 1024, 70
+    planes = [si.draw_quantized_weight(33, 10 * bits + e, N, K, bits) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(33, bits, R, K)
+    rng = np.random.default_rng([33, bits])
+    rhs = np.array([1] * 1 + [2] * 64 + [3] * 65 + [4] * 150, np.uint32)
+    rng.shuffle(rhs)
+    lhs = rng.integers(0, R, len(rhs)).astype(np.uint32)
+    lhs_bad, rhs_bad = lhs.copy(), rhs.copy()
+    lhs_bad[7], rhs_bad[11] = R + 3, E
+    w, s, b = u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"])
+    xd = bf16_dev(x)
+    progress(f"gather_qmm edges bits={bits}")
+    y = agq.gather_qmm(xd, w, s, b, rhs_indices=u32_dev(rhs_bad), lhs_indices=u32_dev(lhs_bad), bits=bits)
+    torch.cuda.synchronize()
+    yh = bf16_host(y)
+    assert np.all(np.isnan(yh[7])) and np.all(np.isnan(yh[11]))
+    ok = np.array([p for p in range(len(rhs)) if p not in (7, 11)])
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs[ok], rhs[ok], K, bits)
+    check_close(y[torch.as_tensor(ok, device=y.device)], y_ref, A, "gather_qmm edges")
+    # the matvec gather gives results within the same tolerance
+    yv = agq.gather_qmv(xd, w, s, b, rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs), bits=bits)
+    check_close(yv[torch.as_tensor(ok, device=y.device)], y_ref, A, "gather_qmv edges")
+    # NULL indices: identity
+    y_id = agq.gather_qmm(xd[:E], w, s, b, bits=bits)
+    y_ex = agq.gather_qmm(xd[:E], w, s, b, rhs_indices=u32_dev(np.arange(E, dtype=np.uint32)),
+                          lhs_indices=u32_dev(np.arange(E, dtype=np.uint32)), bits=bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits_host(y_id), bf16_bits_host(y_ex))
+
+
+def test_gather_qmm_at_the_pair_limit():
+    E, N, K, R, P = 3, 96, 512, 64, 4096
+    planes = [si.draw_quantized_weight(34, e, N, K, 4) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(34, 99, R, K)
+    rng = np.random.default_rng([34, 1])
+    lhs = rng.integers(0, R, P).astype(np.uint32)
+    rhs = rng.integers(0, E, P).astype(np.uint32)
+    progress("gather_qmm with 4096 pairs")
+    y = agq.gather_qmm(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs))
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, 4)
+    check_close(y, y_ref, A, "gather_qmm 4096 pairs")
