@@ -197,18 +197,19 @@ agq_status launch_plan(int64_t M, int64_t N, int64_t K, int bits, int64_t expert
 // Matrix-core plan on the current device: the grid is sized from the
 // occupancy of the chosen kernel at its block size.
 agq_status launch_mfma_plan(int64_t M, int64_t N, int64_t K, int64_t experts, agq::MfmaPlan *plan,
-                            const void **sym) {
+                            const void **sym, int passes = 1) {
     agq::mfma_shape(N, K, experts, plan);
     agq::mfma_lds(experts, M, plan);  // (gather: M is the pair count P)
     int cus = 0, dev = 0;
     agq_status st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
-    *sym = agq::mfma_kernel(plan->T, experts > 0, experts == 0 && M <= 4);
+    *sym = agq::mfma_kernel(plan->T, experts > 0, (int)(M < 16 ? M : 16));
     if (!*sym) return fail(AGQ_ENOTSUP, "no matrix-core kernel for %d tiles", plan->T);
     int64_t waves = 0;
     st = resident_waves(*sym, plan->threads, (size_t)plan->lds_bytes, cus, dev, &waves);
     if (st != AGQ_OK) return st;
-    agq::mfma_grid(waves, experts, plan);
+    // Passes of 16 rows in one launch share the residency, so they run together.
+    agq::mfma_grid(waves / passes, experts, plan);
     return AGQ_OK;
 }
 
@@ -398,7 +399,21 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
     if (st != AGQ_OK) return st;
     if (M <= 0) return fail(AGQ_EINVAL, "M must be positive (got %lld)", (long long)M);
     if (M * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (M*K*2 bytes)");
-    const agq::QmmKernel k = agq::qmm_kernel_for(bits, false);
+    // Up to 8 rows: the matvec kernels. Up to kQmmPassRows rows of 4-bit codes (K
+    // a multiple of 512): the matrix-core matvec kernel, one grid row per pass of
+    // 16 rows. Beyond: the tiled GEMM.
+    if (M <= 8) return dense_product(x, w, scales, biases, y, M, N, K, bits, group_size, stream);
+    if (M <= agq::kQmmPassRows && agq::mfma_eligible(M, K, bits, 0, M)) {
+        agq::MfmaPlan mp;
+        const void *sym = nullptr;
+        const int passes = (int)((M + 15) / 16);
+        st = launch_mfma_plan(M, N, K, 0, &mp, &sym, passes);
+        if (st != AGQ_OK) return st;
+        agq::MfmaArgs a = make_mfma_args(x, w, scales, biases, y, N, K, (int)M, mp);
+        return launch(sym, dim3((unsigned)mp.groups, (unsigned)passes), dim3(mp.threads), (size_t)mp.lds_bytes, &a,
+                      stream);
+    }
+    const agq::QmmKernel k = agq::qmm_kernel_for(bits, false, M);
     if ((int64_t)k.bn * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
     const int64_t mt = (M + k.bm - 1) / k.bm, nt = (N + k.bn - 1) / k.bn;
     if (mt > 65535 || nt > INT32_MAX) return fail(AGQ_ENOTSUP, "grid too large (M=%lld, N=%lld)", (long long)M,
@@ -437,7 +452,7 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
     if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
     if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
     if (R * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (R*K*2 bytes)");
-    const agq::QmmKernel k = agq::qmm_kernel_for(bits, true);
+    const agq::QmmKernel k = agq::qmm_kernel_for(bits, true, (P + E - 1) / E);
     if ((int64_t)k.bn * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
     const int64_t nt = (N + k.bn - 1) / k.bn;
     if (nt > INT32_MAX) return fail(AGQ_ENOTSUP, "N too large");

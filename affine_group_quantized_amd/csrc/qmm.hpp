@@ -7,11 +7,16 @@
 
 namespace agq {
 
-// Tile shape: a block of 4 waves computes 32*kQmmTM activation rows by
-// 32*kQmmTN weight rows; global loads run kQmmDepth 64-column groups ahead.
-constexpr int kQmmTM = 2;
-constexpr int kQmmTN = 4;
-constexpr int kQmmDepth = 4;
+// Tile shapes: a block of 4 waves computes 32*TM activation rows by 32*TN
+// weight rows; global loads run DEPTH 64-column groups ahead. Measured on the
+// Llama-3-8B shapes (4-bit, TFLOP/s): 64 x 64 tiles with loads 4 groups ahead
+// lead at M = 64 (o: 51 against 40 with 64 x 128), 128 x 64 tiles with loads
+// 2 groups ahead from M = 512 (gate_up M = 2048: 393 against 295 with 64 x 128
+// and 353 with 128 x 128; the Mixtral-shaped prefill gather 279 against 212).
+// Up to this many activation rows (dense), or pairs per expert plane (gather): 64 x 64 tiles.
+constexpr int kQmmSmallM = 128;
+constexpr int kQmmSmallPairs = 64;
+constexpr int kQmmPassRows = 128;  // 4-bit products of up to this many rows run on the matvec kernel in passes of 16
 
 // Passed by value as the single kernel argument.
 struct QmmArgs {
@@ -39,6 +44,7 @@ struct QmmKernel {
     int lds = 0;         // dynamic LDS bytes of the tile buffers
 };
 
-QmmKernel qmm_kernel_for(int bits, bool gather);
+// The kernel for `rows` activation rows (dense M, or the gather's pairs per expert plane).
+QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows);
 
 }  // namespace agq

@@ -385,9 +385,8 @@ __global__ __launch_bounds__(256) void gather_qmm_kernel(QmmArgs a) {
 // ---------------------------------------------------------------------------
 // Kernel selection.
 
-template <int BITS>
+template <int BITS, int TM, int TN, int D>
 static QmmKernel qmm_pick(bool gather) {
-    constexpr int TM = kQmmTM, TN = kQmmTN, D = kQmmDepth;
     QmmKernel k;
     k.sym = gather ? reinterpret_cast<const void *>(&gather_qmm_kernel<BITS, TM, TN, D>)
                    : reinterpret_cast<const void *>(&qmm_kernel<BITS, TM, TN, D>);
@@ -397,6 +396,10 @@ static QmmKernel qmm_pick(bool gather) {
     return k;
 }
 
-QmmKernel qmm_kernel_for(int bits, bool gather) { return bits == 4 ? qmm_pick<4>(gather) : qmm_pick<8>(gather); }
+QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows) {
+    const bool small = rows <= (gather ? kQmmSmallPairs : kQmmSmallM);
+    if (bits == 4) return small ? qmm_pick<4, 2, 2, 4>(gather) : qmm_pick<4, 4, 2, 2>(gather);
+    return small ? qmm_pick<8, 2, 2, 4>(gather) : qmm_pick<8, 4, 2, 2>(gather);
+}
 
 }  // namespace agq

@@ -57,10 +57,11 @@ struct MfmaArgs {
 // LDS copy of x (0: none)), or NULL.
 const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather);
 const void *dequant_kernel_sym(int bits);
-// Matrix-core kernel with bands of 16*tiles rows (tiles 1 or 2). compact_x
-// (dense, at most 4 activation rows): one activation load per segment;
-// otherwise (dense, 5-8 rows) activations staged through LDS. The gather
-// chooses its load form per pass.
-const void *mfma_kernel(int tiles, bool gather, bool compact_x);
+// Matrix-core kernel with bands of 16*tiles rows (tiles 1 or 2). Dense
+// products choose the activation load form by their rows per pass: one
+// rotated load per segment up to 4 rows, staged through LDS up to 8, four
+// loads for passes of 9-16 rows (launched with one grid row per pass of 16).
+// The gather chooses its form per pass.
+const void *mfma_kernel(int tiles, bool gather, int rows);
 
 }  // namespace agq

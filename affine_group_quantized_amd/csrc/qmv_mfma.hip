@@ -494,17 +494,24 @@ __device__ __forceinline__ void with_xq(int rows, F &&f) {
 
 }  // namespace
 
-// XQ: the activation load form, 4 for M <= 4 and 2 (staged) for M = 5..8.
+// XQ: the activation load form, 4 for M <= 4, 2 (staged) for M = 5..8, and 1
+// for passes of up to 16 rows. blockIdx.y = pass: activation rows
+// [16*pass, 16*pass + 16) of M (one pass for M <= 16). The passes of a launch
+// walk the same bands at about the same time, so a band's codes read from HBM
+// once serve the later passes from L2.
 template <int T, int XQ>
 __global__ __launch_bounds__(512) void qmv_mfma_kernel(MfmaArgs a) {
     __shared__ float red[Red<T>::FLOATS];
     // line loads, and the staged activations
     __shared__ u32x4 wt[kMfmaMaxS * (T * 128 + (XQ == 2 ? 256 : 0))];
-    const uint32_t xbytes = (uint32_t)a.M * (uint32_t)a.K * 2u;
+    const int m0 = (int)blockIdx.y * 16;
+    const int mrows = a.M - m0 < 16 ? a.M - m0 : 16;
+    const uint32_t xbytes = (uint32_t)mrows * (uint32_t)a.K * 2u;
     const Band bd{reinterpret_cast<const uint8_t *>(a.w), a.s, a.b, a.N, (uint32_t)(a.K / 2), a.G};
-    // Lanes of rows >= M start at the descriptor's end and read zeros.
+    // Lanes of rows >= mrows start at the descriptor's end and read zeros.
     const Lanes ln = lane_consts<XQ>(a, [&](uint32_t r) { return r * (uint32_t)a.K * 2u; });
-    mfma_pass<T, XQ>(a, bd, ln, range_of(a.x, xbytes), a.M, RowsOut{a.y, a.N}, blockIdx.x, gridDim.x, red, wt);
+    mfma_pass<T, XQ>(a, bd, ln, range_of(a.x + (int64_t)m0 * a.K, xbytes), mrows,
+                     RowsOut{a.y + (int64_t)m0 * a.N, a.N}, blockIdx.x, gridDim.x, red, wt);
 }
 
 // blockIdx.y = expert plane e. The pairs routed to e are listed in LDS and
@@ -594,13 +601,15 @@ __global__ __launch_bounds__(512) void gather_mfma_kernel(MfmaArgs a) {
     }
 }
 
-const void *mfma_kernel(int tiles, bool gather, bool compact_x) {
+const void *mfma_kernel(int tiles, bool gather, int rows) {
     if (gather) return tiles == 1 ? reinterpret_cast<const void *>(&gather_mfma_kernel<1>)
                                    : reinterpret_cast<const void *>(&gather_mfma_kernel<2>);
-    if (compact_x) return tiles == 1 ? reinterpret_cast<const void *>(&qmv_mfma_kernel<1, 4>)
+    if (rows <= 4) return tiles == 1 ? reinterpret_cast<const void *>(&qmv_mfma_kernel<1, 4>)
                                      : reinterpret_cast<const void *>(&qmv_mfma_kernel<2, 4>);
-    return tiles == 1 ? reinterpret_cast<const void *>(&qmv_mfma_kernel<1, 2>)
-                      : reinterpret_cast<const void *>(&qmv_mfma_kernel<2, 2>);
+    if (rows <= 8) return tiles == 1 ? reinterpret_cast<const void *>(&qmv_mfma_kernel<1, 2>)
+                                     : reinterpret_cast<const void *>(&qmv_mfma_kernel<2, 2>);
+    return tiles == 1 ? reinterpret_cast<const void *>(&qmv_mfma_kernel<1, 1>)
+                      : reinterpret_cast<const void *>(&qmv_mfma_kernel<2, 1>);
 }
 
 }  // namespace agq

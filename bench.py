@@ -38,7 +38,9 @@ the five matrices, median of 3 calls per shape.
 
 Other workloads (--workload): c0 (4096x4096), wide (14336x4096 and 4096x14336 at
 M = 2..8), c3 (0.5B-class 8-bit shapes), gather (Mixtral-shaped expert gather),
-calib (the read ceiling and the empty-kernel launch floor); one JSON line per shape.
+qmm (quantized GEMM at M = 16..2048 and the Mixtral-shaped prefill gather, against the
+2.5 PFLOP/s bf16 matrix-core peak and HBM), calib (the read ceiling and the
+empty-kernel launch floor); one JSON line per shape.
 """
 from __future__ import annotations
 
@@ -54,6 +56,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
 ROTATION_BYTES = 512 * 1024 * 1024
 SHAPES = ["qkv", "o", "gate_up", "down", "lm_head"]
 METRIC = "qmv achieved HBM GB/s (% of MI355X peak) + us/call, 4-bit gs64 decode shapes"
@@ -81,7 +84,7 @@ def parse():
     ap.add_argument("--write-profiles", nargs="+", metavar="DIR",
                     help="summarize rocprofv3 CSV output of this benchmark into profiles/ and exit: "
                          "TRACE_DIR [FETCH_DIR WRITE_DIR]")
-    ap.add_argument("--workload", choices=["llama", "c0", "wide", "c3", "gather", "calib"], default="llama")
+    ap.add_argument("--workload", choices=["llama", "c0", "wide", "c3", "gather", "qmm", "calib"], default="llama")
     ap.add_argument("--calls", type=int, default=200, help="calls per timed loop of one shape")
     return ap.parse_args()
 
@@ -439,7 +442,7 @@ def other_workload(args):
     stream = torch.cuda.current_stream(dev)
     st = stream.cuda_stream
     calib = None
-    if not args.no_calib and args.workload != "calib":
+    if not args.no_calib and args.workload not in ("calib", "qmm"):
         calib = ReadCeiling(torch, stream, 300 * 1024 * 1024)
 
     def emit(rec):
@@ -454,6 +457,10 @@ def other_workload(args):
             us, cfg = calib.ceiling(nb)
             emit({"read_bytes": nb, "us": round(us, 3), "GB/s": round(nb / us / 1e3, 1),
                   "pct_of_hbm_peak": round(100 * nb / us / 1e3 / HBM_PEAK_GBPS, 2), **cfg})
+        return
+
+    if args.workload == "qmm":
+        qmm_workload(args, torch, si, agq, bf16, u32, stream, st, emit)
         return
 
     if args.workload in ("c0", "c3"):
@@ -523,6 +530,64 @@ def other_workload(args):
                             agq.launch_plan(8, N, K, 4, experts=E), calib.ceiling(nb) if calib else None))
             del cp
             torch.cuda.empty_cache()
+
+
+def qmm_line(label, us, us_min, flops, nbytes, plan=None):
+    tf = flops / (us * 1e-6) / 1e12
+    gb = nbytes / (us * 1e-6) / 1e9
+    bound_us = max(flops / (MFMA_BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBPS * 1e9)) * 1e6
+    rec = {"shape": label, "us_per_call": round(us, 3), "us_min": round(us_min, 3), "TFLOP/s": round(tf, 1),
+           "pct_of_mfma_bf16_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2), "GB/s": round(gb, 1),
+           "pct_of_hbm_peak": round(100 * gb / HBM_PEAK_GBPS, 2), "flops": flops, "bytes": nbytes,
+           "bound": "mfma" if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBPS * 1e9) else "hbm",
+           "pct_of_binding_roofline": round(100 * bound_us / us, 2)}
+    return rec
+
+
+def qmm_workload(args, torch, si, agq, bf16, u32, stream, st, emit):
+    """Quantized GEMM (prefill): Llama-3-8B-shaped 4-bit matrices at M = 16 .. 2048 activation
+    rows, and the Mixtral-shaped expert gather at 512 tokens, top-2 (1024 pairs over the 8 W1
+    planes). Algorithmic flops are 2*M*N*K (2*P*N*K for the gather); bytes are the codes,
+    scales and biases read once (used planes only), x and y."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    wl = si.workload(1, only=("o", "gate_up", "down"))
+    for name in ("o", "gate_up", "down"):
+        m = wl[name]
+        N, K = m["N"], m["K"]
+        cp = rotation(u32, bf16, m, weight_bytes(N, K, 4))
+        rot = len(cp)
+        ptrs = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr()) for c in cp]
+        for M in (16, 64, 256, 512, 2048):
+            x = bf16(si.draw_activations(6, M, M, K))
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            agq.qmm(x, *cp[0], bits=4, out=y)
+            calls = max(4, min(args.calls, int(2e6 / (2 * M * N * K / 1e9 + 1))))
+            us, us_min = time_shape(torch, lambda i: agq.lib.agq_qmm(x.data_ptr(), *ptrs[i % rot], y.data_ptr(), M,
+                                                                     N, K, 4, 64, st), calls, 5, stream)
+            emit(qmm_line(f"qmm {name} {N}x{K} M={M}", us, us_min, 2 * M * N * K,
+                          weight_bytes(N, K, 4) + 2 * M * K + 2 * M * N))
+            del x, y
+        del cp
+        torch.cuda.empty_cache()
+    moe = si.workload(4, only=("w1",))
+    m = moe["w1"]
+    pre = si.moe_prefill(512)
+    E, N, K = m["E"], m["N"], m["K"]
+    rhs, lhs = pre["rhs"], pre["lhs"]
+    P, R = len(rhs), pre["x"].shape[0]
+    used = len(set(rhs.tolist()))
+    cp = rotation(u32, bf16, m, E * weight_bytes(N, K, 4))
+    rot = len(cp)
+    ptrs = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr()) for c in cp]
+    x, ri, li = bf16(pre["x"]), u32(rhs), u32(lhs)
+    y = torch.empty(P, N, dtype=torch.bfloat16, device=dev)
+    agq.gather_qmm(x, *cp[0], rhs_indices=ri, lhs_indices=li, out=y)
+    us, us_min = time_shape(torch, lambda i: agq.lib.agq_gather_qmm(x.data_ptr(), *ptrs[i % rot], li.data_ptr(),
+                                                                    ri.data_ptr(), y.data_ptr(), P, R, E, N, K, 4,
+                                                                    64, st), 20, 5, stream)
+    emit(qmm_line(f"gather_qmm w1 {E}x{N}x{K} P={P} (512 tokens top-2, {used} planes used)", us, us_min,
+                  2 * P * N * K, used * weight_bytes(N, K, 4) + 2 * R * K + 2 * P * N + 8 * P))
 
 
 # ----------------------------------------------------------------------------- main workload

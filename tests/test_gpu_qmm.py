@@ -40,6 +40,7 @@ def dev_weight(d):
     (4, 33, 64, 192, False), (4, 1, 5, 64, False), (4, 8, 1000, 4096, False), (4, 200, 131, 64, False),
     (4, 512, 4099, 4096, True), (4, 130, 14336, 4096, True), (4, 96, 4096, 14336, True),
     (8, 9, 100, 896, False), (8, 65, 300, 4864, False), (8, 100, 129, 64, False), (8, 512, 1000, 896, True),
+    (4, 17, 129, 512, False), (4, 100, 333, 2048, False), (4, 128, 1000, 14336, True), (4, 300, 200, 4096, False),
 ])
 def test_qmm_shapes(bits, M, N, K, sample):
     d = si.draw_quantized_weight(30, 100 * bits + M, N, K, bits)
@@ -55,6 +56,27 @@ def test_qmm_shapes(bits, M, N, K, sample):
     # rounding alone exceeds 2e-3 of it: those shapes also allow that half ulp.
     worst = check_close(yg, y_ref, A, f"qmm M={M} N={N} K={K} bits={bits}", extra_half_ulp=K <= 128)
     progress(f"qmm: ok, worst |err|/A = {worst:.3e}")
+
+
+@pytest.mark.parametrize("M", [9, 40, 128])
+def test_qmm_passes_agree_with_the_tiled_gemm(M):
+    """4-bit products of 9-128 rows run on the matrix-core matvec kernel, one grid row per
+    16-row pass; the same rows through agq_gather_qmm (identity routing onto one plane, the
+    tiled GEMM) meet the same tolerance against the oracle."""
+    N, K = 520, 2048
+    d = si.draw_quantized_weight(35, M, N, K, 4)
+    x = si.draw_activations(35, 100 + M, M, K)
+    w, s, b = dev_weight(d)
+    xd = bf16_dev(x)
+    progress(f"qmm passes vs tiled M={M}")
+    y1 = agq.qmm(xd, w, s, b)
+    zero = u32_dev(np.zeros(M, np.uint32))
+    y2 = agq.gather_qmm(xd, w[None], s[None], b[None], rhs_indices=zero,
+                        lhs_indices=u32_dev(np.arange(M, dtype=np.uint32)))
+    torch.cuda.synchronize()
+    y_ref, A = oracle.qmv(x, d["w"], d["scales"], d["biases"], K, 4)
+    check_close(y1, y_ref, A, "passes")
+    check_close(y2, y_ref, A, "tiled")
 
 
 def test_qmm_is_deterministic_and_scales_by_powers_of_two():
