@@ -54,7 +54,8 @@ def _bind(lib):
     lib.agqo_dequantize.argtypes = [P, P, P, I64, I64, I, I, P, P]
     lib.agqo_qmv.argtypes = [P, I64, P, P, P, I64, I64, I, I, P, I64, P, P]
     lib.agqo_gather_qmv.argtypes = [P, I64, P, P, P, I64, I64, I64, I, I, P, P, I64, P, I64, P, P]
-    for f in (lib.agqo_unpack, lib.agqo_dequantize, lib.agqo_qmv, lib.agqo_gather_qmv):
+    lib.agqo_moe_swiglu.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, I, I, P, P]
+    for f in (lib.agqo_unpack, lib.agqo_dequantize, lib.agqo_qmv, lib.agqo_gather_qmv, lib.agqo_moe_swiglu):
         f.restype = I
     return lib
 
@@ -135,4 +136,28 @@ def gather_qmv(x, w, scales, biases, lhs, rhs, K: int, bits: int, group_size: in
     a = np.empty_like(y)
     _check(lib.agqo_gather_qmv(_p(x), x.shape[0], _p(w), _p(s), _p(b), e, n, K, bits, group_size,
                                _p(lh), _p(rh), P, _p(r), nrows, _p(y), _p(a)))
+    return y, a
+
+
+def moe_swiglu(x, gate, up, down, experts, weights, bits: int, group_size: int = 64, lib=None):
+    """Decode MoE layer with SwiGLU experts (float64, exact dequantization).
+
+    ``x`` [T, H] bf16; ``gate``/``up``: dicts of ``w`` [E, F, H*bits/32], ``scales``/``biases``
+    [E, F, H/64]; ``down``: ``w`` [E, H, F*bits/32], ``scales``/``biases`` [E, H, F/64];
+    ``experts`` [T, k] uint32; ``weights`` [T, k] float32 router weights.
+    Returns (y float64 [T, H], A float64 [T, H])."""
+    lib = lib or load()
+    x = _c(x, np.uint16)
+    T, H = x.shape
+    ex = _c(experts, np.uint32)
+    r = _c(weights, np.float32)
+    k = ex.shape[1]
+    E, F = gate["w"].shape[0], gate["w"].shape[1]
+    arrs = []
+    for d in (gate, up, down):
+        arrs += [_c(d["w"], np.uint32), _c(d["scales"], np.uint16), _c(d["biases"], np.uint16)]
+    y = np.empty((T, H), dtype=np.float64)
+    a = np.empty_like(y)
+    _check(lib.agqo_moe_swiglu(_p(x), T, H, F, E, k, *[_p(v) for v in arrs], _p(ex), _p(r), bits, group_size,
+                               _p(y), _p(a)))
     return y, a

@@ -29,12 +29,23 @@
  *    bits * (k % (32/bits)), i.e. low-first;
  *  - W is [N out, K in] and y[m, n] = sum_k x[m, k] * w[n, k].
  *
+ * The decode MoE layer (agqo_moe_swiglu) composes these steps the way the
+ * fused decode-MoE kernel of "epic: CUDA (MLX backend) prefill and decode
+ * acceleration program" (Code-audit findings; Phase 2, #626) does: each
+ * token's top-k experts take a gate and an up projection of the token, the
+ * gated unit silu(gate) * up (the GLU stage the "MLX CUDA Cleanup Plan",
+ * Phase 5, moves onto the device), a down projection, and the router-weighted
+ * sum over the k experts. The pages name the kernel and the stages but print
+ * no formula; this is the plainest reading, in exact float64 with no
+ * intermediate rounding.
+ *
  * Every function here is pinned by the CPU test suite to known-answer words,
  * closed forms, exact rational brute force and a float64 BLAS product.
  */
 #include <stdint.h>
 #include <string.h>
 #include <math.h>
+#include <stdlib.h>
 
 #define AGQO_OK 0
 #define AGQO_EARG (-1)
@@ -180,5 +191,73 @@ int agqo_gather_qmv(const uint16_t *x, int64_t R,
                     K, bits, group_size, &y[p * nrows + i], &a[p * nrows + i]);
         }
     }
+    return AGQO_OK;
+}
+
+/* silu(z) = z * sigmoid(z) = z / (1 + exp(-z)). */
+static double silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+/* Decode MoE layer with a SwiGLU expert MLP, for T tokens with k experts each:
+ *   g  = W_gate[e] x_t      (F values; W_gate planes [E, F, H])
+ *   u  = W_up[e]   x_t      (F values; W_up planes   [E, F, H])
+ *   h  = silu(g) * u        (elementwise)
+ *   o  = W_down[e] h        (H values; W_down planes [E, H, F])
+ *   y_t = sum_{j < k} r[t, j] * o   with e = experts[t, j]
+ * in float64, summing slot by slot in increasing j and each dot product in
+ * increasing column index. x is [T, H] bf16; experts [T, k] uint32; r [T, k]
+ * float (router weights, already normalized by the caller); y [T, H].
+ * a[t, m] = sum_j |r[t, j]| * sum_n |w_down[e][m, n] * h_n|, the scale of the
+ * rounding tolerance of the final projection. */
+int agqo_moe_swiglu(const uint16_t *x, int64_t T, int64_t H, int64_t F, int64_t E, int64_t k,
+                    const uint32_t *wg, const uint16_t *sg, const uint16_t *bg,
+                    const uint32_t *wu, const uint16_t *su, const uint16_t *bu,
+                    const uint32_t *wd, const uint16_t *sd, const uint16_t *bd,
+                    const uint32_t *experts, const float *r, int bits, int group_size,
+                    double *y, double *a)
+{
+    if (!x || !wg || !sg || !bg || !wu || !su || !bu || !wd || !sd || !bd || !experts || !r || !y || !a)
+        return AGQO_EARG;
+    if (T <= 0 || H <= 0 || F <= 0 || E <= 0 || k <= 0) return AGQO_EARG;
+    if (check_format(H, bits, group_size) || check_format(F, bits, group_size)) return AGQO_EARG;
+    int64_t hw = H * bits / 32, hg = H / group_size;   /* gate/up rows: H columns */
+    int64_t fw = F * bits / 32, fg = F / group_size;   /* down rows: F columns */
+    double *h = (double *)malloc((size_t)F * sizeof(double));
+    if (!h) return AGQO_EARG;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t m = 0; m < H; ++m) {
+            y[t * H + m] = 0.0;
+            a[t * H + m] = 0.0;
+        }
+        for (int64_t j = 0; j < k; ++j) {
+            int64_t e = (int64_t)experts[t * k + j];
+            if (e < 0 || e >= E) {
+                free(h);
+                return AGQO_EINDEX;
+            }
+            double rw = (double)r[t * k + j];
+            for (int64_t f = 0; f < F; ++f) {
+                double g, u, dummy;
+                const int64_t row = e * F + f;
+                row_dot(x + t * H, wg + row * hw, sg + row * hg, bg + row * hg, H, bits, group_size, &g, &dummy);
+                row_dot(x + t * H, wu + row * hw, su + row * hg, bu + row * hg, H, bits, group_size, &u, &dummy);
+                h[f] = silu(g) * u;
+            }
+            for (int64_t m = 0; m < H; ++m) {
+                const int64_t row = e * H + m;
+                double dot = 0.0, size = 0.0;
+                for (int64_t f = 0; f < F; ++f) {
+                    double part = weight_at(wd + row * fw, sd + row * fg, bd + row * fg, f, bits, group_size) * h[f];
+                    dot += part;
+                    size += fabs(part);
+                }
+                y[t * H + m] += rw * dot;
+                a[t * H + m] += fabs(rw) * size;
+            }
+        }
+    }
+    free(h);
     return AGQO_OK;
 }

@@ -15,11 +15,16 @@ Anchors used:
     codes taken from before packing;
   * a float64 BLAS product on a densely built weight matrix;
   * an integer-valued special case, which must come out exact;
-  * the constant-code closed form sum_g (s_g*c + b_g) * sum_{k in g} x_k.
+  * the constant-code closed form sum_g (s_g*c + b_g) * sum_{k in g} x_k;
+  * for the decode MoE layer: the odd part of silu (silu(z) - silu(-z) = z, so
+    negated gate planes with router weights +1 and -1 leave an exp-free
+    polynomial), saturation (silu(64) = 64 and silu(-64) ~ 0 in float64), and
+    exact-rational projections with silu written through tanh.
 """
 from __future__ import annotations
 
 import json
+import math
 import os
 from fractions import Fraction
 
@@ -245,6 +250,102 @@ def pin_row_subset(lib):
         ys, as_ = oracle.qmv(x, pack_codes(q, bits), s, b, 192, bits, rows=np.array([5, 1]), lib=lib)
         for i, n in enumerate([5, 1]):
             assert abs(ys[0, i] - float(ye[n])) <= 2 * 192 * U53 * as_[0, i]
+
+
+def _moe_planes(seed, E, F, H, bits, codes=False):
+    """Random gate/up/down planes: dicts of packed w, scales, biases (and the codes)."""
+    out = []
+    for i, (n, kdim) in enumerate(((F, H), (F, H), (H, F))):
+        g = np.random.default_rng([seed, i])
+        q = g.integers(0, 2 ** bits, size=(E, n, kdim), dtype=np.uint8)
+        sc = bf16_bits((0.01 + 0.02 * g.random((E, n, kdim // 64))).astype(np.float32))
+        bi = bf16_bits((-0.05 + 0.03 * g.standard_normal((E, n, kdim // 64))).astype(np.float32))
+        d = {"w": pack_codes(q, bits), "scales": sc, "biases": bi}
+        if codes:
+            d["codes"] = q
+        out.append(d)
+    return out
+
+
+def _dense(d, bits):
+    """float64 dequantized planes from the codes (independent of the oracle's unpack)."""
+    s = bf16_to_f32(d["scales"]).astype(np.float64)
+    b = bf16_to_f32(d["biases"]).astype(np.float64)
+    return np.repeat(s, 64, axis=-1) * d["codes"].astype(np.float64) + np.repeat(b, 64, axis=-1)
+
+
+def pin_moe_odd_part_of_silu(lib):
+    """Expert 1 is expert 0 with its gate plane negated (bf16 sign flips), the same up and
+    down planes; with router weights +1 and -1 the silu terms cancel to the polynomial
+    W_down (g * u), computed here from the codes."""
+    bits, H, F = 4, 128, 192
+    gate, up, down = _moe_planes(50, 1, F, H, bits, codes=True)
+    neg = {k: v.copy() for k, v in gate.items()}
+    neg["scales"] = neg["scales"] ^ np.uint16(0x8000)
+    neg["biases"] = neg["biases"] ^ np.uint16(0x8000)
+    g2 = {k: np.concatenate([gate[k], neg[k]]) for k in ("w", "scales", "biases")}
+    u2 = {k: np.concatenate([up[k], up[k]]) for k in ("w", "scales", "biases")}
+    d2 = {k: np.concatenate([down[k], down[k]]) for k in ("w", "scales", "biases")}
+    x = bf16_bits(np.random.default_rng(51).standard_normal((2, H)).astype(np.float32))
+    ex = np.array([[0, 1], [1, 0]], np.uint32)
+    r = np.array([[1.0, -1.0], [-1.0, 1.0]], np.float32)
+    y, a = oracle.moe_swiglu(x, g2, u2, d2, ex, r, bits, lib=lib)
+    xd = bf16_to_f32(x).astype(np.float64)
+    g = xd @ _dense(gate, bits)[0].T
+    u = xd @ _dense(up, bits)[0].T
+    want = (g * u) @ _dense(down, bits)[0].T
+    assert np.all(np.abs(y - want) <= 1e-12 * a), np.max(np.abs(y - want) / a)
+
+
+def pin_moe_silu_saturation(lib):
+    """Gate planes of constant weight +1 (or -1) against x with 64 ones: every gate value is
+    +64 (or -64), silu(64) = 64 and silu(-64) ~ -1e-26 in float64, so h = 64 * u (or ~0)."""
+    bits, H, F, E = 4, 128, 64, 2
+    _, up, down = _moe_planes(52, E, F, H, bits, codes=True)
+    zero = np.zeros((E, F, H // 64), np.uint16)
+    x = np.zeros((1, H), np.uint16)
+    x[0, 5:69] = 0x3F80
+    ex = np.array([[1, 0]], np.uint32)
+    r = np.array([[0.75, 0.25]], np.float32)
+    xd = bf16_to_f32(x).astype(np.float64)
+    for sign, bias in ((1, 0x3F80), (-1, 0xBF80)):
+        gate = {"w": np.zeros((E, F, H * bits // 32), np.uint32), "scales": zero,
+                "biases": np.full((E, F, H // 64), bias, np.uint16)}
+        y, a = oracle.moe_swiglu(x, gate, up, down, ex, r, bits, lib=lib)
+        if sign > 0:
+            want = np.zeros(H)
+            for j in range(2):
+                e = int(ex[0, j])
+                u = xd[0] @ _dense(up, bits)[e].T
+                want += float(r[0, j]) * (_dense(down, bits)[e] @ (64.0 * u))
+            assert np.all(np.abs(y[0] - want) <= 1e-12 * a[0]), np.max(np.abs(y[0] - want) / np.maximum(a[0], 1e-300))
+        else:
+            assert np.all(np.abs(y) <= 1e-20), np.max(np.abs(y))
+
+
+def pin_moe_bruteforce_tanh_form(lib):
+    """Tiny layers in exact rationals for the projections, silu written through tanh
+    (sigmoid(z) = (1 + tanh(z/2)) / 2), the down projection and the router sum in float64."""
+    for bits in (4, 8):
+        T, H, F, E, k = 2, 64, 64, 3, 2
+        gate, up, down = _moe_planes(53 + bits, E, F, H, bits, codes=True)
+        x = bf16_bits(np.random.default_rng(54 + bits).standard_normal((T, H)).astype(np.float32))
+        ex = np.array([[2, 0], [1, 2]], np.uint32)
+        r = np.array([[0.625, 0.375], [0.5, 0.5]], np.float32)
+        y, a = oracle.moe_swiglu(x, gate, up, down, ex, r, bits, lib=lib)
+        for t in range(T):
+            want = np.zeros(H)
+            for j in range(k):
+                e = int(ex[t, j])
+                h = np.empty(F)
+                for f in range(F):
+                    g = float(_exact_row(x[t], gate["codes"][e, f], gate["scales"][e, f], gate["biases"][e, f])[0])
+                    u = float(_exact_row(x[t], up["codes"][e, f], up["scales"][e, f], up["biases"][e, f])[0])
+                    h[f] = g * 0.5 * (1.0 + math.tanh(0.5 * g)) * u
+                want += float(r[t, j]) * (_dense(down, bits)[e] @ h)
+            assert np.all(np.abs(y[t] - want) <= 1e-12 * a[t]), (bits, t, np.max(np.abs(y[t] - want) / np.maximum(a[t], 1e-300)))
+            # the tolerance scale: sum_j |r| * sum_n |w_down * h|
+            assert np.all(a[t] > 0)
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -36,6 +36,15 @@ MUTANTS = {
     "lhs_ignored": ("int64_t r = lhs ? (int64_t)lhs[p] : p;", "int64_t r = p % R;"),
     "not_f32_never_counted": ("if ((double)(float)v != v) ++bad;", "if ((float)v != (float)v) ++bad;"),
     "not_f32_inverted": ("if ((double)(float)v != v) ++bad;", "if ((double)(float)v == v) ++bad;"),
+    "moe_gate_up_swapped": ("h[f] = silu(g) * u;", "h[f] = silu(u) * g;"),
+    "moe_no_silu": ("h[f] = silu(g) * u;", "h[f] = g * u;"),
+    "moe_sigmoid_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "moe_router_weight_dropped": ("y[t * H + m] += rw * dot;", "y[t * H + m] += dot;"),
+    "moe_magnitude_signed": ("size += fabs(part);", "size += part;"),
+    "moe_down_expert_ignored": ("const int64_t row = e * H + m;", "const int64_t row = m;"),
+    "moe_token_row_ignored": ("row_dot(x + t * H, wg", "row_dot(x, wg"),
+    "moe_up_with_gate_scales": ("row_dot(x + t * H, wu + row * hw, su + row * hg,",
+                                "row_dot(x + t * H, wu + row * hw, sg + row * hg,"),
 }
 
 
