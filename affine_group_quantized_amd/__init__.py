@@ -18,7 +18,7 @@ import os
 
 import torch
 
-__all__ = ["qmv", "qmv_wide", "gather_qmv", "qmm", "gather_qmm", "dequantize", "plan", "launch_plan", "prepare_qmv", "AgqError",
+__all__ = ["qmv", "qmv_wide", "gather_qmv", "qmm", "gather_qmm", "moe_decode", "moe_decode_workspace", "dequantize", "plan", "launch_plan", "prepare_qmv", "AgqError",
            "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libagq.so")
@@ -62,6 +62,10 @@ def _load(path: str = LIB_PATH):
     lib.agq_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.agq_qmm.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
     lib.agq_gather_qmm.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
+    lib.agq_moe_decode_workspace.argtypes = [I64, I64, I64]
+    lib.agq_moe_decode_workspace.restype = I64
+    lib.agq_moe_decode.argtypes = [P] * 14 + [I64] * 6 + [I, I, P]
+    lib.agq_moe_decode.restype = I
     lib.agq_dequantize.argtypes = [P, P, P, P, I64, I64, I, I, P]
     lib.agq_plan_product.argtypes = [I64, I64, I64, I, I, I, I, I64, ctypes.POINTER(Plan)]
     lib.agq_plan_launch.argtypes = [I64, I64, I64, I, I, I64, ctypes.POINTER(Plan)]
@@ -249,6 +253,52 @@ def gather_qmv(x, w, scales, biases, rhs_indices=None, lhs_indices=None, bits: i
     with torch.cuda.device(device):
         _check(getattr(lib, _fn)(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(lhs_indices),
                                  _ptr(rhs_indices), _ptr(out), P, R, E, N, K, bits, group_size, _stream(device)))
+    return out
+
+
+def moe_decode_workspace(T: int, k: int, F: int) -> int:
+    """Bytes of device workspace agq_moe_decode needs for T tokens, k experts each, F units."""
+    return int(lib.agq_moe_decode_workspace(T, k, F))
+
+
+def moe_decode(x, gate, up, down, experts, weights, bits: int = 4, group_size: int = 64, out=None, workspace=None):
+    """Fused decode MoE layer with SwiGLU experts.
+
+    ``x`` [T, H] bf16; ``gate``/``up``: (w [E, F, H*bits/32], scales, biases [E, F, H/64]);
+    ``down``: (w [E, H, F*bits/32], scales, biases [E, H, F/64]); ``experts`` [T, k] int32/uint32;
+    ``weights`` [T, k] float32. Returns ``y`` [T, H] bf16. ``workspace`` (uint8, at least
+    :func:`moe_decode_workspace` bytes) is allocated here when not given.
+    """
+    device = x.device
+    _need(x, "x", _BF16, device)
+    if x.dim() != 2:
+        raise ValueError("x must be [T, H]")
+    T, H = x.shape
+    E, F = _weights(*gate, H, bits, group_size, device, 2)
+    if tuple(_weights(*up, H, bits, group_size, device, 2)) != (E, F):
+        raise ValueError("gate and up planes must have the same shape")
+    if tuple(_weights(*down, F, bits, group_size, device, 2)) != (E, H):
+        raise ValueError(f"down planes must be [{E}, {H}, .]")
+    _need(experts, "experts", _U32, device)
+    _need(weights, "weights", (torch.float32,), device)
+    if experts.dim() != 2 or experts.shape[0] != T or tuple(weights.shape) != tuple(experts.shape):
+        raise ValueError("experts and weights must be [T, k]")
+    k = experts.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+    else:
+        _need(out, "out", _BF16, device)
+        if tuple(out.shape) != (T, H):
+            raise ValueError("out has the wrong shape")
+    need = moe_decode_workspace(T, k, F)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    else:
+        _need(workspace, "workspace", (torch.uint8,), device)
+    with torch.cuda.device(device):
+        _check(lib.agq_moe_decode(_ptr(x), *[_ptr(t) for t in gate], *[_ptr(t) for t in up],
+                                  *[_ptr(t) for t in down], _ptr(experts), _ptr(weights), _ptr(out), _ptr(workspace),
+                                  workspace.numel(), T, k, E, H, F, bits, group_size, _stream(device)))
     return out
 
 

@@ -19,6 +19,7 @@
 
 #include "agq.h"
 #include "plan.hpp"
+#include "moe.hpp"
 #include "plan_mfma.hpp"
 #include "qmm.hpp"
 #include "qmv_kernels.hpp"
@@ -479,6 +480,103 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
     st = allow_lds(k.sym, lds, dev);
     if (st != AGQ_OK) return st;
     return launch(k.sym, dim3((unsigned)nt, (unsigned)E), dim3(256), lds, &a, stream);
+}
+
+int64_t agq_moe_decode_workspace(int64_t T, int64_t k, int64_t F) {
+    if (T <= 0 || k <= 0 || F <= 0) return 0;
+    return 4 * T * k * F;  // two bf16 rows of F per pair
+}
+
+agq_status agq_moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate, const void *b_gate,
+                          const uint32_t *w_up, const void *s_up, const void *b_up, const uint32_t *w_down,
+                          const void *s_down, const void *b_down, const uint32_t *experts, const float *weights,
+                          void *y, void *workspace, int64_t workspace_bytes, int64_t T, int64_t k, int64_t E,
+                          int64_t H, int64_t F, int bits, int group_size, void *stream) {
+    if (!x || !w_gate || !s_gate || !b_gate || !w_up || !s_up || !b_up || !w_down || !s_down || !b_down || !experts ||
+        !weights || !y || !workspace)
+        return fail(AGQ_EINVAL, "null pointer");
+    if (T <= 0 || k <= 0 || E <= 0 || H <= 0 || F <= 0)
+        return fail(AGQ_EINVAL, "T, k, E, H and F must be positive");
+    agq_status st = check_format(F, H, bits, group_size);
+    if (st != AGQ_OK) return st;
+    st = check_format(H, F, bits, group_size);
+    if (st != AGQ_OK) return st;
+    if (misaligned(x, 16) || misaligned(w_gate, 16) || misaligned(w_up, 16) || misaligned(w_down, 16) ||
+        misaligned(workspace, 16))
+        return fail(AGQ_EINVAL, "x, the code planes and the workspace must be 16-byte aligned");
+    if (misaligned(s_gate, 2) || misaligned(b_gate, 2) || misaligned(s_up, 2) || misaligned(b_up, 2) ||
+        misaligned(s_down, 2) || misaligned(b_down, 2) || misaligned(y, 2) || misaligned(experts, 4) ||
+        misaligned(weights, 4))
+        return fail(AGQ_EINVAL, "misaligned scales, biases, y, experts or weights");
+    if (bits != 4 || H % 512 != 0 || F % 512 != 0)
+        return fail(AGQ_ENOTSUP, "the fused MoE takes 4-bit codes with H and F multiples of 512");
+    if (T > agq::kMoeMaxTokens) return fail(AGQ_ENOTSUP, "T=%lld tokens exceeds %d", (long long)T, agq::kMoeMaxTokens);
+    const int64_t P = T * k;
+    if (P > agq::kMaxPairs) return fail(AGQ_ENOTSUP, "T*k=%lld pairs exceeds %d", (long long)P, agq::kMaxPairs);
+    if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
+    if (E * (H > F ? H : F) > kMaxN) return fail(AGQ_EINVAL, "E*H or E*F too large");
+    if (2 * P * F * 2 >= (int64_t(1) << 32) || T * H * 2 >= (int64_t(1) << 31))
+        return fail(AGQ_ENOTSUP, "activations too large");
+    if (workspace_bytes < agq_moe_decode_workspace(T, k, F))
+        return fail(AGQ_EINVAL, "workspace of %lld bytes is below the %lld needed", (long long)workspace_bytes,
+                    (long long)agq_moe_decode_workspace(T, k, F));
+    int cus = 0, dev = 0;
+    st = current_device(&cus, &dev);
+    if (st != AGQ_OK) return st;
+    agq::MoeArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.h = static_cast<uint16_t *>(workspace);
+    a.y = static_cast<uint16_t *>(y);
+    a.wg = w_gate;
+    a.sg = static_cast<const uint16_t *>(s_gate);
+    a.bg = static_cast<const uint16_t *>(b_gate);
+    a.wu = w_up;
+    a.su = static_cast<const uint16_t *>(s_up);
+    a.bu = static_cast<const uint16_t *>(b_up);
+    a.wd = w_down;
+    a.sd = static_cast<const uint16_t *>(s_down);
+    a.bd = static_cast<const uint16_t *>(b_down);
+    a.experts = experts;
+    a.weights = weights;
+    a.T = (int32_t)T;
+    a.k = (int32_t)k;
+    a.P = (int32_t)P;
+    a.E = (int32_t)E;
+    a.H = H;
+    a.F = F;
+    // Launch 1: dual bands of 16 units, K = H split over at most 2 waves, the
+    // grid oversubscribed like the gather's.
+    const int b4h = (int)(H / 512);
+    a.S1 = b4h % 2 == 0 ? 2 : 1;
+    a.SPW1 = (int)(H / 128) / a.S1;
+    const int64_t bands1 = (F + 15) / 16;
+    const void *k1 = agq::moe_kernel(false);
+    const size_t lds1 = (size_t)((P * 2 + 15) / 16 * 16 + P * 4);
+    int64_t waves1 = 0;
+    st = resident_waves(k1, 64 * a.S1, lds1, cus, dev, &waves1);
+    if (st != AGQ_OK) return st;
+    int64_t budget = waves1 * agq::kGatherOversub / a.S1 / E;
+    if (budget < 1) budget = 1;
+    a.BPG1 = (int32_t)((bands1 + budget - 1) / budget);
+    const int64_t groups1 = (bands1 + a.BPG1 - 1) / a.BPG1;
+    // Launch 2: one band of 16 output rows per block, K = F split over the most
+    // waves (at most kMoeMaxS) that divide its 512-column blocks.
+    const int b4f = (int)(F / 512);
+    int S2 = 1;
+    for (int s = agq::kMoeMaxS; s >= 1; --s)
+        if (b4f % s == 0) {
+            S2 = s;
+            break;
+        }
+    a.SPW2 = (int)(F / 128) / S2;
+    const int64_t bands2 = (H + 15) / 16;
+    const void *k2 = agq::moe_kernel(true);
+    const size_t lds2 = (size_t)((P * 2 + 15) / 16 * 16 + 4 * (2 * (E + 1) + (T + 3) / 4 * 4) + T * 16 * 4);
+    st = allow_lds(k2, lds2, dev);
+    if (st != AGQ_OK) return st;
+    st = launch(k1, dim3((unsigned)groups1, (unsigned)E), dim3(64 * a.S1), lds1, &a, stream);
+    if (st != AGQ_OK) return st;
+    return launch(k2, dim3((unsigned)bands2), dim3(64 * S2), lds2, &a, stream);
 }
 
 agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *biases, float *out, int64_t rows,

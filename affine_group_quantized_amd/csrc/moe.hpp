@@ -1,0 +1,33 @@
+// Argument block and kernel lookup of the fused decode-MoE kernels (moe_mfma.hip).
+#pragma once
+
+#include <stdint.h>
+
+namespace agq {
+
+constexpr int kMoeMaxS = 8;         // most waves splitting F in the down projection
+constexpr int kMoeMaxTokens = 256;  // tokens per call (the down kernel keeps a band of every token in LDS)
+
+// Passed by value as the single kernel argument of both launches.
+struct MoeArgs {
+    const uint16_t *x;        // tokens [T, H] bf16
+    uint16_t *h;              // workspace [2P, F] bf16: per pair the hi and lo rows of silu(gate) * up
+    uint16_t *y;              // [T, H] bf16
+    const uint32_t *wg;       // gate planes [E, F, H/8] (4-bit codes)
+    const uint16_t *sg, *bg;  // [E, F, H/64]
+    const uint32_t *wu;       // up planes [E, F, H/8]
+    const uint16_t *su, *bu;
+    const uint32_t *wd;       // down planes [E, H, F/8]
+    const uint16_t *sd, *bd;  // [E, H, F/64]
+    const uint32_t *experts;  // [T, k] expert per pair (pair p = t*k + j)
+    const float *weights;     // [T, k] router weight per pair
+    int32_t T, k, P, E;
+    int64_t H, F;
+    int32_t S1, SPW1, BPG1;   // gate/up launch: waves per block, segments per wave, bands per block
+    int32_t SPW2;             // down launch: segments per wave (waves per block = blockDim / 64)
+};
+
+// moe_gate_up_kernel (down = false), or moe_down_kernel (bands of 16 output rows).
+const void *moe_kernel(bool down);
+
+}  // namespace agq

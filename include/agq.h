@@ -24,7 +24,9 @@
  *  - agq_gather_qmv is the expert-gathered (MoE) form of the gather_qmm path
  *    in the same epic;
  *  - agq_qmm and agq_gather_qmm are the matrix-matrix (prefill) forms of the
- *    two.
+ *    two;
+ *  - agq_moe_decode is a whole decode MoE layer (gate, up, SwiGLU, down and
+ *    the router-weighted sum) in two launches.
  *
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers to contiguous row-major arrays. The
@@ -32,7 +34,8 @@
  *    `stream` completes. Outputs must not overlap inputs.
  *  - `stream` is a hipStream_t (NULL = the null stream). Each call queues
  *    its kernels on that stream and returns at once. It never synchronizes,
- *    allocates or copies. The current HIP device must be the one that holds
+ *    allocates or copies; scratch memory, where a call needs it, is a
+ *    workspace the caller passes in. The current HIP device must be the one that holds
  *    the buffers.
  *  - BF16 tensors are passed as `const void *` and hold raw bfloat16 bit
  *    patterns.
@@ -157,6 +160,43 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
 agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y,
                           int64_t P, int64_t R, int64_t E, int64_t N, int64_t K,
+                          int bits, int group_size, void *stream);
+
+/*
+ * Fused decode MoE layer with SwiGLU experts: the fused decode-MoE kernel of
+ * "epic: CUDA (MLX backend) prefill and decode acceleration program",
+ * Code-audit findings (+55% decode on qwen3-30b-a3b) and Phase 2 (#626), with
+ * the GLU stage that "MLX CUDA Cleanup Plan", Phase 5, moves onto the device.
+ * For token t and its experts e_j = experts[t, j] with router weights
+ * r[t, j] (j < k):
+ *     h_j  = silu(W_gate[e_j] x_t) * (W_up[e_j] x_t),  silu(z) = z / (1 + exp(-z))
+ *     y_t  = sum_j r[t, j] * (W_down[e_j] h_j)
+ *   x            [T, H] BF16
+ *   w_gate, w_up [E, F, H*bits/32] U32; s_gate, b_gate, s_up, b_up [E, F, H/64] BF16
+ *   w_down       [E, H, F*bits/32] U32; s_down, b_down [E, H, F/64] BF16
+ *   experts      [T, k] uint32 expert per (token, slot)
+ *   weights      [T, k] float router weights (applied as given, not normalized)
+ *   y            [T, H] BF16 (written)
+ *   workspace    device scratch of at least agq_moe_decode_workspace(T, k, F)
+ *                bytes, 16-byte aligned, owned by the caller; its contents on
+ *                return are unspecified. Two calls that overlap in time must
+ *                not share one.
+ * Two kernel launches on `stream`: the gate and up projections with the
+ * SwiGLU (each used expert's planes streamed once), then the down projection
+ * with the router-weighted sum over slots, accumulated per output band in a
+ * fixed order (bitwise deterministic). The intermediate h keeps about 17
+ * significant bits. Supports 4-bit codes, group size 64, H and F multiples of
+ * 512, T <= 256 tokens and T*k <= 4096 (else AGQ_ENOTSUP). A token with an
+ * expert id >= E gets an all-NaN output row. Argument checks and errors as
+ * for agq_qmv; a workspace below the size needed is AGQ_EINVAL.
+ */
+int64_t agq_moe_decode_workspace(int64_t T, int64_t k, int64_t F);
+agq_status agq_moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate, const void *b_gate,
+                          const uint32_t *w_up, const void *s_up, const void *b_up,
+                          const uint32_t *w_down, const void *s_down, const void *b_down,
+                          const uint32_t *experts, const float *weights, void *y,
+                          void *workspace, int64_t workspace_bytes,
+                          int64_t T, int64_t k, int64_t E, int64_t H, int64_t F,
                           int bits, int group_size, void *stream);
 
 /*

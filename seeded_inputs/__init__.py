@@ -42,7 +42,7 @@ CHUNK_ROWS = 1024
 __all__ = [
     "GROUP_SIZE", "CHUNK_ROWS", "stream", "bf16_bits", "bf16_to_f32",
     "pack_codes", "quantize_rows", "draw_activations", "draw_quantized_weight",
-    "random_codes", "workload", "WORKLOADS", "moe_expert_ids", "moe_prefill",
+    "random_codes", "workload", "WORKLOADS", "moe_expert_ids", "moe_prefill", "moe_layer",
 ]
 
 
@@ -189,6 +189,21 @@ WORKLOADS = {
 }
 
 MOE = {"experts": 8, "tokens": 16, "top_k": 2, "hidden": 4096, "ffn": 14336, "bits": 4}
+
+
+def moe_layer() -> dict:
+    """The rest of a Mixtral-shaped decode MoE layer around workload 4: the up planes
+    ``w3`` (8 x [14336, 4096], 4-bit gs64, streams t = 19..26, drawn like W1) and
+    router weights ``weights`` [16, 2]: per token the softmax of 2 logits ~ N(0, 1)
+    sorted in decreasing order (stream t = 27), float32. Workload 4's ``w1`` are the
+    gate planes, ``w2`` the down planes and ``ids`` the experts."""
+    m = MOE
+    planes = [draw_quantized_weight(4, 19 + e, m["ffn"], m["hidden"], m["bits"]) for e in range(m["experts"])]
+    w3 = {key: np.stack([p[key] for p in planes]) for key in planes[0]}
+    w3.update(N=m["ffn"], K=m["hidden"], bits=m["bits"], E=m["experts"])
+    z = -np.sort(-stream(4, 27).standard_normal((m["tokens"], m["top_k"])), axis=1)
+    ez = np.exp(z - z[:, :1])
+    return {"w3": w3, "weights": (ez / ez.sum(axis=1, keepdims=True)).astype(np.float32)}
 
 
 def moe_prefill(tokens: int = 512) -> dict:

@@ -40,6 +40,11 @@ def test_library_exports_every_declared_symbol(name):
     assert hasattr(lib, name), name
 
 
+def test_moe_workspace_size():
+    assert lib.agq_moe_decode_workspace(16, 2, 14336) == 4 * 32 * 14336
+    assert lib.agq_moe_decode_workspace(0, 2, 14336) == 0
+
+
 def test_status_strings():
     assert lib.agq_status_str(0) == b"AGQ_OK"
     assert lib.agq_status_str(1) == b"AGQ_EINVAL"
@@ -62,6 +67,10 @@ def gather(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
 
 def qmm(M=16, x=A, N=16, K=64, bits=4, gs=64, y=A):
     return lib.agq_qmm(x, A, A, A, y, M, N, K, bits, gs, None)
+
+
+def moe(T=4, k=2, E=4, H=512, F=1024, bits=4, gs=64, x=A, ws=A, wsb=1 << 30, ex=A):
+    return lib.agq_moe_decode(x, A, A, A, A, A, A, A, A, A, ex, A, A, ws, wsb, T, k, E, H, F, bits, gs, None)
 
 
 def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
@@ -117,6 +126,19 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: gqmm(P=4097, R=4097, E=4), ENOTSUP),
     (lambda: gqmm(E=70000), ENOTSUP),
     (lambda: gqmm(R=1 << 20, K=1024), ENOTSUP),
+    (lambda: moe(x=NUL), EINVAL),
+    (lambda: moe(ws=NUL), EINVAL),
+    (lambda: moe(T=0), EINVAL),
+    (lambda: moe(k=0), EINVAL),
+    (lambda: moe(H=96), EINVAL),
+    (lambda: moe(bits=8), ENOTSUP),
+    (lambda: moe(H=640), ENOTSUP),
+    (lambda: moe(F=1088), ENOTSUP),
+    (lambda: moe(T=257), ENOTSUP),
+    (lambda: moe(T=256, k=17), ENOTSUP),
+    (lambda: moe(wsb=4 * 4 * 2 * 1024 - 1), EINVAL),
+    (lambda: moe(ws=ctypes.c_void_p(0x10008)), EINVAL),
+    (lambda: moe(ex=ctypes.c_void_p(0x10002)), EINVAL),
     (lambda: lib.agq_dequantize(A, A, A, ctypes.c_void_p(0x10004), 4, 64, 4, 64, None), EINVAL),
     (lambda: lib.agq_dequantize(A, A, A, A, 4, 64, 5, 64, None), ENOTSUP),
 ])
