@@ -39,8 +39,9 @@ the five matrices, median of 3 calls per shape.
 Other workloads (--workload): c0 (4096x4096), wide (14336x4096 and 4096x14336 at
 M = 2..8), c3 (0.5B-class 8-bit shapes), gather (Mixtral-shaped expert gather),
 qmm (quantized GEMM at M = 16..2048 and the Mixtral-shaped prefill gather, against the
-2.5 PFLOP/s bf16 matrix-core peak and HBM), calib (the read ceiling and the
-empty-kernel launch floor); one JSON line per shape.
+2.5 PFLOP/s bf16 matrix-core peak and HBM), moe (the fused Mixtral-shaped decode MoE
+layer against its unfused products), calib (the read ceiling and the empty-kernel
+launch floor); one JSON line per shape.
 """
 from __future__ import annotations
 
@@ -84,7 +85,8 @@ def parse():
     ap.add_argument("--write-profiles", nargs="+", metavar="DIR",
                     help="summarize rocprofv3 CSV output of this benchmark into profiles/ and exit: "
                          "TRACE_DIR [FETCH_DIR WRITE_DIR]")
-    ap.add_argument("--workload", choices=["llama", "c0", "wide", "c3", "gather", "qmm", "calib"], default="llama")
+    ap.add_argument("--workload", choices=["llama", "c0", "wide", "c3", "gather", "qmm", "moe", "calib"],
+                    default="llama")
     ap.add_argument("--calls", type=int, default=200, help="calls per timed loop of one shape")
     return ap.parse_args()
 
@@ -442,7 +444,7 @@ def other_workload(args):
     stream = torch.cuda.current_stream(dev)
     st = stream.cuda_stream
     calib = None
-    if not args.no_calib and args.workload not in ("calib", "qmm"):
+    if not args.no_calib and args.workload not in ("calib", "qmm", "moe"):
         calib = ReadCeiling(torch, stream, 300 * 1024 * 1024)
 
     def emit(rec):
@@ -461,6 +463,9 @@ def other_workload(args):
 
     if args.workload == "qmm":
         qmm_workload(args, torch, si, agq, bf16, u32, stream, st, emit)
+        return
+    if args.workload == "moe":
+        moe_workload(args, torch, si, agq, bf16, u32, stream, emit)
         return
 
     if args.workload in ("c0", "c3"):
@@ -588,6 +593,49 @@ def qmm_workload(args, torch, si, agq, bf16, u32, stream, st, emit):
                                                                     64, st), 20, 5, stream)
     emit(qmm_line(f"gather_qmm w1 {E}x{N}x{K} P={P} (512 tokens top-2, {used} planes used)", us, us_min,
                   2 * P * N * K, used * weight_bytes(N, K, 4) + 2 * R * K + 2 * P * N + 8 * P))
+
+
+def moe_workload(args, torch, si, agq, bf16, u32, stream, emit):
+    """The Mixtral-shaped decode MoE layer (16 tokens, top-2 of 8 experts, H 4096, F 14336):
+    agq_moe_decode (two launches) against the same layer from the unfused products (gate and
+    up through agq_gather_qmv, SwiGLU and the weighted sum in torch, down through
+    agq_gather_qmv). Weights rotate over >= 512 MiB of copies. Bytes: the used planes of
+    the three matrices, x, h (written and read twice: hi and lo rows) and y."""
+    import numpy as np
+    moe = si.workload(4)
+    lay = si.moe_layer()
+    T, k = moe["ids"].shape
+    E, F, H = moe["w1"]["E"], moe["w1"]["N"], moe["w1"]["K"]
+    used = len(set(moe["ids"].reshape(-1).tolist()))
+    wb = weight_bytes(F, H, 4)
+    cp = [[(u32(d["w"]), bf16(d["scales"]), bf16(d["biases"])) for d in (moe["w1"], lay["w3"], moe["w2"])]]
+    rot = max(2, math.ceil(ROTATION_BYTES / (3 * E * wb)))
+    for _ in range(rot - 1):
+        cp.append([tuple(t.clone() for t in trio) for trio in cp[0]])
+    x = bf16(moe["x"])
+    ids = u32(moe["ids"])
+    w = torch.as_tensor(lay["weights"], device="cuda")
+    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(agq.moe_decode_workspace(T, k, F), dtype=torch.uint8, device="cuda")
+    fused = lambda i: agq.moe_decode(x, *cp[i % rot], ids, w, out=y, workspace=ws)  # noqa: E731
+    rhs = u32(moe["ids"].reshape(-1))
+    lhs = u32(np.repeat(np.arange(T, dtype=np.uint32), k))
+
+    def unfused(i):
+        g_, u_, d_ = cp[i % rot]
+        g = agq.gather_qmv(x, *g_, rhs_indices=rhs, lhs_indices=lhs).float()
+        u = agq.gather_qmv(x, *u_, rhs_indices=rhs, lhs_indices=lhs).float()
+        h = (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
+        o = agq.gather_qmv(h, *d_, rhs_indices=rhs).float()
+        return (o.view(T, k, H) * w[:, :, None]).sum(1).to(torch.bfloat16)
+
+    nbytes = 3 * used * wb + 2 * T * H + 3 * 4 * T * k * F + 2 * T * H + 8 * T * k
+    for label, fn in (("moe_decode fused (2 launches)", fused), ("unfused: 3 gathers + torch SwiGLU/sum", unfused)):
+        us, us_min = time_shape(torch, fn, 20, 5, stream)
+        gb = nbytes / (us * 1e-6) / 1e9
+        emit({"shape": f"{label}: Mixtral-shaped layer, {T} tokens top-{k} of {E}, H {H}, F {F} ({used} experts used)",
+              "us_per_call": round(us, 3), "us_min": round(us_min, 3), "us_per_token": round(us / T, 3),
+              "GB/s": round(gb, 1), "pct_of_hbm_peak": round(100 * gb / HBM_PEAK_GBPS, 2), "bytes": nbytes})
 
 
 # ----------------------------------------------------------------------------- main workload
