@@ -322,6 +322,15 @@ agq_status dense_product(const void *x, const uint32_t *w, const void *s, const 
     return launch(sym, dim3((unsigned)plan.blocks), dim3(plan.threads), (size_t)plan.x_lds_bytes, &a, stream);
 }
 
+// Declared here, defined after the entry points that use it.
+agq_status moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate, const void *b_gate,
+                      const uint32_t *w_up, const void *s_up, const void *b_up, const uint32_t *w_down,
+                      const void *s_down, const void *b_down, const uint32_t *experts, const float *weights,
+                      void *y, void *workspace, int64_t workspace_bytes, int64_t T, int64_t k, int64_t E,
+                      int64_t H, int64_t F, int bits, int group_size, void *stream, bool use_scratch);
+// Non-null stand-in for the scratch pointer during the host checks.
+const int kScratchStandIn = 0;
+
 }  // namespace
 
 extern "C" {
@@ -492,6 +501,31 @@ agq_status agq_moe_decode(const void *x, const uint32_t *w_gate, const void *s_g
                           const void *s_down, const void *b_down, const uint32_t *experts, const float *weights,
                           void *y, void *workspace, int64_t workspace_bytes, int64_t T, int64_t k, int64_t E,
                           int64_t H, int64_t F, int bits, int group_size, void *stream) {
+    return moe_decode(x, w_gate, s_gate, b_gate, w_up, s_up, b_up, w_down, s_down, b_down, experts, weights, y,
+                      workspace, workspace_bytes, T, k, E, H, F, bits, group_size, stream, false);
+}
+
+agq_status agq_moe_decode_noalloc(const void *x, const uint32_t *w_gate, const void *s_gate, const void *b_gate,
+                                  const uint32_t *w_up, const void *s_up, const void *b_up, const uint32_t *w_down,
+                                  const void *s_down, const void *b_down, const uint32_t *experts,
+                                  const float *weights, void *y, int64_t T, int64_t k, int64_t E, int64_t H,
+                                  int64_t F, int bits, int group_size, void *stream) {
+    // The workspace pointer is filled in from the device's scratch array once
+    // every host check has passed (a non-null stand-in passes the null check).
+    return moe_decode(x, w_gate, s_gate, b_gate, w_up, s_up, b_up, w_down, s_down, b_down, experts, weights, y,
+                      const_cast<int *>(&kScratchStandIn), agq::kMoeScratchBytes, T, k, E, H, F, bits, group_size,
+                      stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+agq_status moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate, const void *b_gate,
+                      const uint32_t *w_up, const void *s_up, const void *b_up, const uint32_t *w_down,
+                      const void *s_down, const void *b_down, const uint32_t *experts, const float *weights,
+                      void *y, void *workspace, int64_t workspace_bytes, int64_t T, int64_t k, int64_t E,
+                      int64_t H, int64_t F, int bits, int group_size, void *stream, bool use_scratch) {
     if (!x || !w_gate || !s_gate || !b_gate || !w_up || !s_up || !b_up || !w_down || !s_down || !b_down || !experts ||
         !weights || !y || !workspace)
         return fail(AGQ_EINVAL, "null pointer");
@@ -502,7 +536,7 @@ agq_status agq_moe_decode(const void *x, const uint32_t *w_gate, const void *s_g
     st = check_format(H, F, bits, group_size);
     if (st != AGQ_OK) return st;
     if (misaligned(x, 16) || misaligned(w_gate, 16) || misaligned(w_up, 16) || misaligned(w_down, 16) ||
-        misaligned(workspace, 16))
+        (!use_scratch && misaligned(workspace, 16)))
         return fail(AGQ_EINVAL, "x, the code planes and the workspace must be 16-byte aligned");
     if (misaligned(s_gate, 2) || misaligned(b_gate, 2) || misaligned(s_up, 2) || misaligned(b_up, 2) ||
         misaligned(s_down, 2) || misaligned(b_down, 2) || misaligned(y, 2) || misaligned(experts, 4) ||
@@ -517,12 +551,21 @@ agq_status agq_moe_decode(const void *x, const uint32_t *w_gate, const void *s_g
     if (E * (H > F ? H : F) > kMaxN) return fail(AGQ_EINVAL, "E*H or E*F too large");
     if (2 * P * F * 2 >= (int64_t(1) << 32) || T * H * 2 >= (int64_t(1) << 31))
         return fail(AGQ_ENOTSUP, "activations too large");
-    if (workspace_bytes < agq_moe_decode_workspace(T, k, F))
+    if (workspace_bytes < agq_moe_decode_workspace(T, k, F)) {
+        if (use_scratch)
+            return fail(AGQ_ENOTSUP, "T*k*F needs %lld bytes of scratch; the allocation-free call holds %lld",
+                        (long long)agq_moe_decode_workspace(T, k, F), (long long)workspace_bytes);
         return fail(AGQ_EINVAL, "workspace of %lld bytes is below the %lld needed", (long long)workspace_bytes,
                     (long long)agq_moe_decode_workspace(T, k, F));
+    }
     int cus = 0, dev = 0;
     st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
+    if (use_scratch) {
+        hipError_t e = agq::moe_scratch(dev, &workspace);
+        if (e != hipSuccess)
+            return fail(AGQ_EHIP, "scratch address of device %d: %s", dev, hipGetErrorString(e));
+    }
     agq::MoeArgs a{};
     a.x = static_cast<const uint16_t *>(x);
     a.h = static_cast<uint16_t *>(workspace);
@@ -578,6 +621,10 @@ agq_status agq_moe_decode(const void *x, const uint32_t *w_gate, const void *s_g
     if (st != AGQ_OK) return st;
     return launch(k2, dim3((unsigned)bands2), dim3(64 * S2), lds2, &a, stream);
 }
+
+}  // namespace
+
+extern "C" {
 
 agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *biases, float *out, int64_t rows,
                           int64_t K, int bits, int group_size, void *stream) {

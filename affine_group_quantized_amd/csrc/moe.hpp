@@ -1,6 +1,7 @@
 // Argument block and kernel lookup of the fused decode-MoE kernels (moe_mfma.hip).
 #pragma once
 
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace agq {
@@ -29,5 +30,14 @@ struct MoeArgs {
 
 // moe_gate_up_kernel (down = false), or moe_down_kernel (bands of 16 output rows).
 const void *moe_kernel(bool down);
+
+// Bytes of the per-device scratch array of the allocation-free MoE call
+// (agq_moe_decode_noalloc): 8 MiB, h for T*k*F <= 2M (for example 16 tokens
+// top-2 at F = 14336 take 1.8 MiB).
+constexpr int64_t kMoeScratchBytes = int64_t(8) << 20;
+
+// Device address of the scratch array on device `dev` (the current device),
+// looked up once per device.
+hipError_t moe_scratch(int dev, void **ptr);
 
 }  // namespace agq

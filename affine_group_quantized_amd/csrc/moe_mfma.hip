@@ -22,11 +22,41 @@
 // results are bitwise deterministic; the block writes its band of y once.
 // A pair whose expert id is out of range makes its token's output row NaN.
 
+#include <mutex>
+
 #include "mfma_core.hpp"
 #include "moe.hpp"
 
 namespace agq {
 using namespace mfma;
+
+// Scratch of agq_moe_decode_noalloc, for callers that cannot allocate: one
+// array per device, alive until the process ends. Every call on a device
+// shares it and it keeps the last call's contents (nothing in it has to start
+// at zero: the first launch writes every h row the second reads). Calls that
+// overlap in time on one device race on it.
+static __device__ __align__(256) uint8_t scratch[kMoeScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+void *g_scratch_ptr[kScratchDevices] = {};
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t moe_scratch(int dev, void **ptr) {
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // The host-side name of the array is a stand-in, not a device address:
+        // ask the runtime where this device's copy lives.
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 namespace {
 

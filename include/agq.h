@@ -200,6 +200,24 @@ agq_status agq_moe_decode(const void *x, const uint32_t *w_gate, const void *s_g
                           int bits, int group_size, void *stream);
 
 /*
+ * agq_moe_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The intermediate h lives in a scratch
+ * array the library holds on each device (8 MiB, kept until the process
+ * ends): T*k*F must stay at or below 2M (4*T*k*F bytes), else AGQ_ENOTSUP.
+ * The call allocates nothing. Every call on a device shares that array and it
+ * keeps the last call's contents, so calls that overlap in time on one device
+ * (on different streams) race and must not be issued. Otherwise the same
+ * arguments, result and errors as agq_moe_decode.
+ */
+agq_status agq_moe_decode_noalloc(const void *x, const uint32_t *w_gate, const void *s_gate, const void *b_gate,
+                                  const uint32_t *w_up, const void *s_up, const void *b_up,
+                                  const uint32_t *w_down, const void *s_down, const void *b_down,
+                                  const uint32_t *experts, const float *weights, void *y,
+                                  int64_t T, int64_t k, int64_t E, int64_t H, int64_t F,
+                                  int bits, int group_size, void *stream);
+
+/*
  * The dequantization step on its own, as a check of the unpack and affine map
  * of "MLX CUDA Cleanup Plan", Target Architecture §1 (U32-packed codes with
  * BF16 scales and biases), against which the products can be verified bit for
