@@ -62,7 +62,7 @@ def _load(path: str = LIB_PATH):
     lib.agq_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.agq_qmm.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
     lib.agq_gather_qmm.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
-    lib.agq_moe_decode_workspace.argtypes = [I64, I64, I64]
+    lib.agq_moe_decode_workspace.argtypes = [I64, I64, I64, I64]
     lib.agq_moe_decode_workspace.restype = I64
     lib.agq_moe_decode.argtypes = [P] * 14 + [I64] * 6 + [I, I, P]
     lib.agq_moe_decode.restype = I
@@ -256,9 +256,9 @@ def gather_qmv(x, w, scales, biases, rhs_indices=None, lhs_indices=None, bits: i
     return out
 
 
-def moe_decode_workspace(T: int, k: int, F: int) -> int:
-    """Bytes of device workspace agq_moe_decode needs for T tokens, k experts each, F units."""
-    return int(lib.agq_moe_decode_workspace(T, k, F))
+def moe_decode_workspace(T: int, k: int, H: int, F: int) -> int:
+    """Bytes of device workspace agq_moe_decode needs for T tokens, k experts each, width H, F units."""
+    return int(lib.agq_moe_decode_workspace(T, k, H, F))
 
 
 def moe_decode(x, gate, up, down, experts, weights, bits: int = 4, group_size: int = 64, out=None, workspace=None):
@@ -290,7 +290,7 @@ def moe_decode(x, gate, up, down, experts, weights, bits: int = 4, group_size: i
         _need(out, "out", _BF16, device)
         if tuple(out.shape) != (T, H):
             raise ValueError("out has the wrong shape")
-    need = moe_decode_workspace(T, k, F)
+    need = moe_decode_workspace(T, k, H, F)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
     else:

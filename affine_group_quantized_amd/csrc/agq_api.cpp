@@ -491,9 +491,9 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
     return launch(k.sym, dim3((unsigned)nt, (unsigned)E), dim3(256), lds, &a, stream);
 }
 
-int64_t agq_moe_decode_workspace(int64_t T, int64_t k, int64_t F) {
-    if (T <= 0 || k <= 0 || F <= 0) return 0;
-    return 4 * T * k * F;  // two bf16 rows of F per pair
+int64_t agq_moe_decode_workspace(int64_t T, int64_t k, int64_t H, int64_t F) {
+    if (T <= 0 || k <= 0 || H <= 0 || F <= 0) return 0;
+    return 4 * T * k * F + 4 * T * k * H;  // per pair: two bf16 rows of F (h), one fp32 row of H (o)
 }
 
 agq_status agq_moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate, const void *b_gate,
@@ -549,14 +549,14 @@ agq_status moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate,
     if (P > agq::kMaxPairs) return fail(AGQ_ENOTSUP, "T*k=%lld pairs exceeds %d", (long long)P, agq::kMaxPairs);
     if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
     if (E * (H > F ? H : F) > kMaxN) return fail(AGQ_EINVAL, "E*H or E*F too large");
-    if (2 * P * F * 2 >= (int64_t(1) << 32) || T * H * 2 >= (int64_t(1) << 31))
+    if (2 * P * F * 2 >= (int64_t(1) << 32) || T * H * 2 >= (int64_t(1) << 31) || P * H * 4 >= (int64_t(1) << 40))
         return fail(AGQ_ENOTSUP, "activations too large");
-    if (workspace_bytes < agq_moe_decode_workspace(T, k, F)) {
+    if (workspace_bytes < agq_moe_decode_workspace(T, k, H, F)) {
         if (use_scratch)
             return fail(AGQ_ENOTSUP, "T*k*F needs %lld bytes of scratch; the allocation-free call holds %lld",
-                        (long long)agq_moe_decode_workspace(T, k, F), (long long)workspace_bytes);
+                        (long long)agq_moe_decode_workspace(T, k, H, F), (long long)workspace_bytes);
         return fail(AGQ_EINVAL, "workspace of %lld bytes is below the %lld needed", (long long)workspace_bytes,
-                    (long long)agq_moe_decode_workspace(T, k, F));
+                    (long long)agq_moe_decode_workspace(T, k, H, F));
     }
     int cus = 0, dev = 0;
     st = current_device(&cus, &dev);
@@ -593,7 +593,7 @@ agq_status moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate,
     a.S1 = b4h % 2 == 0 ? 2 : 1;
     a.SPW1 = (int)(H / 128) / a.S1;
     const int64_t bands1 = (F + 15) / 16;
-    const void *k1 = agq::moe_kernel(false);
+    const void *k1 = agq::moe_kernel(0, 0);
     const size_t lds1 = (size_t)((P * 2 + 15) / 16 * 16 + P * 4);
     int64_t waves1 = 0;
     st = resident_waves(k1, 64 * a.S1, lds1, cus, dev, &waves1);
@@ -602,24 +602,32 @@ agq_status moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate,
     if (budget < 1) budget = 1;
     a.BPG1 = (int32_t)((bands1 + budget - 1) / budget);
     const int64_t groups1 = (bands1 + a.BPG1 - 1) / a.BPG1;
-    // Launch 2: one band of 16 output rows per block, K = F split over the most
-    // waves (at most kMoeMaxS) that divide its 512-column blocks.
+    // Launch 2: the down projection's gather, bands of 32 output rows when they
+    // give one band-wave per SIMD or more, K = F split over at most 2 waves.
+    a.o = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + 4 * P * F);
     const int b4f = (int)(F / 512);
-    int S2 = 1;
-    for (int s = agq::kMoeMaxS; s >= 1; --s)
-        if (b4f % s == 0) {
-            S2 = s;
-            break;
-        }
-    a.SPW2 = (int)(F / 128) / S2;
-    const int64_t bands2 = (H + 15) / 16;
-    const void *k2 = agq::moe_kernel(true);
-    const size_t lds2 = (size_t)((P * 2 + 15) / 16 * 16 + 4 * (2 * (E + 1) + (T + 3) / 4 * 4) + T * 16 * 4);
-    st = allow_lds(k2, lds2, dev);
+    a.S2 = b4f % 2 == 0 ? 2 : 1;
+    a.SPW2 = (int)(F / 128) / a.S2;
+    const int tiles2 = ((H + 31) / 32) * a.S2 * E >= 1024 ? 2 : 1;
+    const int64_t bands2 = (H + 16 * tiles2 - 1) / (16 * tiles2);
+    const void *k2 = agq::moe_kernel(1, tiles2);
+    const size_t lds2 = (size_t)((P * 2 + 15) / 16 * 16);
+    int64_t waves2 = 0;
+    st = resident_waves(k2, 64 * a.S2, lds2, cus, dev, &waves2);
     if (st != AGQ_OK) return st;
+    budget = waves2 * agq::kGatherOversub / a.S2 / E;
+    if (budget < 1) budget = 1;
+    a.BPG2 = (int32_t)((bands2 + budget - 1) / budget);
+    const int64_t groups2 = (bands2 + a.BPG2 - 1) / a.BPG2;
+    // Launch 3: the slot sum, one thread per output.
+    const void *k3 = agq::moe_kernel(2, 0);
+    int64_t blocks3 = (T * H + 255) / 256;
+    if (blocks3 > (int64_t)cus * 8) blocks3 = (int64_t)cus * 8;
     st = launch(k1, dim3((unsigned)groups1, (unsigned)E), dim3(64 * a.S1), lds1, &a, stream);
     if (st != AGQ_OK) return st;
-    return launch(k2, dim3((unsigned)bands2), dim3(64 * S2), lds2, &a, stream);
+    st = launch(k2, dim3((unsigned)groups2, (unsigned)E), dim3(64 * a.S2), lds2, &a, stream);
+    if (st != AGQ_OK) return st;
+    return launch(k3, dim3((unsigned)blocks3), dim3(256), 0, &a, stream);
 }
 
 }  // namespace

@@ -1,26 +1,28 @@
 // Fused decode MoE layer on the gfx950 matrix cores: the fused decode-MoE
 // kernel of "epic: CUDA (MLX backend) prefill and decode acceleration
-// program" (Code-audit findings, +55% on qwen3-30b-a3b; Phase 2, #626), here in
-// two launches. For T tokens with k experts each (pair p = t*k + j, expert
-// e = experts[p], router weight r[p]):
+// program" (Code-audit findings, +55% on qwen3-30b-a3b; Phase 2, #626). For T
+// tokens with k experts each (pair p = t*k + j, expert e = experts[p], router
+// weight r[p]):
 //
-//   launch 1 (moe_gate_up_kernel): h_p = silu(W_gate[e] x_t) * (W_up[e] x_t)
-//   launch 2 (moe_down_kernel):    y_t = sum_j r[p] * (W_down[e] h_p)
+//   moe_gate_up_kernel: h_p = silu(W_gate[e] x_t) * (W_up[e] x_t)
+//   moe_down_kernel:    o_p = r[p] * (W_down[e] h_p)          (fp32, per pair)
+//   moe_combine_kernel: y_t = sum_j o_{t*k + j}                (slot order)
 //
-// Launch 1 is the expert gather with dual bands: each band's two tiles are 16
-// rows of the gate plane and the same 16 rows of the up plane, so both values
-// of a unit meet in one lane and the SwiGLU epilogue runs there. h is kept at
-// about fp32 precision without an fp32 operand path: it is written as two
-// bfloat16 rows per pair, hi = bf16(h) and lo = bf16(h - hi), and the down
-// projection multiplies both (one more activation row each), so rounding h for
-// the matrix cores costs about 2^-17 of it instead of 2^-9.
-//
-// Launch 2 gives each block one 16-row band of the output (H rows) and walks
-// every expert that some pair uses, in increasing order, streaming that
-// plane's band once for all of its pairs. The router-weighted sum over a
-// token's k experts accumulates in LDS in that fixed order (no atomics), so
-// results are bitwise deterministic; the block writes its band of y once.
-// A pair whose expert id is out of range makes its token's output row NaN.
+// The first two are the expert gather: blocks of (band group, expert plane),
+// each used plane streamed once for all of its pairs. In the first, each
+// band's two tiles are 16 rows of the gate plane and the same 16 rows of the
+// up plane, so both values of a unit meet in one lane and the SwiGLU epilogue
+// runs there. h is kept at about fp32 precision without an fp32 operand path:
+// it is written as two bfloat16 rows per pair, hi = bf16(h) and lo =
+// bf16(h - hi), and the down projection multiplies both (one more activation
+// row each), so rounding h for the matrix cores costs about 2^-17 of it
+// instead of 2^-9. The down projection's epilogue adds the two rows and
+// applies the router weight; the combine sums each token's k slots in slot
+// order, so results are bitwise deterministic without atomics. (One kernel
+// per output band walking every expert in turn, combining in LDS, took 98 us
+// for the Mixtral-shaped down projection against 64 us for the gather: its
+// 256 blocks restart their load pipeline at every expert.)
+// A token with an expert id out of range gets a NaN output row.
 
 #include <mutex>
 
@@ -99,14 +101,14 @@ struct SwigluOut {
     }
 };
 
-// Router-weighted accumulation of a finished down-projection band into the
-// block's LDS rows. Pass rows come in (hi, lo) couples, so lane (g, nl)
-// holds both rows of the pass's pairs 2g and 2g + 1 (r = 0, 1 and 2, 3).
-struct CombineOut {
-    float *ylds;            // [tokens, 16*T]
+// Router-weighted fp32 rows of a finished down-projection band. Pass rows
+// come in (hi, lo) couples, so lane (g, nl) holds both rows of the pass's
+// pairs 2g and 2g + 1 (r = 0, 1 and 2, 3).
+struct WeightedOut {
+    float *o;               // [P, H] fp32
+    int64_t H;
     const uint16_t *plist;  // the pass's pairs
     const float *weights;   // router weight per pair
-    int k;
     template <int T>
     __device__ __forceinline__ void put(const f32x4 (&acc)[T], int64_t band, int g, int nl, int mrows,
                                         int64_t N) const {
@@ -118,14 +120,26 @@ struct CombineOut {
                 const int pp = 2 * g + q;  // pass pair
                 if (2 * pp < mrows && n < N) {
                     const int p = plist[pp];
-                    const float v = acc[t][2 * q] + acc[t][2 * q + 1];
-                    float &dst = ylds[(p / k) * (16 * T) + 16 * t + nl];
-                    dst = fmaf(weights[p], v, dst);
+                    o[(int64_t)p * H + n] = weights[p] * (acc[t][2 * q] + acc[t][2 * q + 1]);
                 }
             }
         }
     }
 };
+
+// The pairs p < P routed to plane e, ascending, into list (wave 0 of the block).
+__device__ __forceinline__ int pairs_of(const uint32_t *experts, int P, uint32_t e, uint16_t *list) {
+    const int lane = threadIdx.x & 63;
+    int count = 0;
+    for (int base = 0; base < P; base += 64) {
+        const int p = base + lane;
+        const bool take = p < P && experts[p] == e;
+        const uint64_t mask = __ballot(take);
+        if (take) list[count + __popcll(mask & ((1ull << lane) - 1ull))] = (uint16_t)p;
+        count += __popcll(mask);
+    }
+    return count;
+}
 
 }  // namespace
 
@@ -143,14 +157,7 @@ __global__ __launch_bounds__(512) void moe_gate_up_kernel(MoeArgs a) {
     const int wig = wave_id();
     const uint32_t e = blockIdx.y;
     if (wig == 0) {
-        int count = 0;
-        for (int base = 0; base < a.P; base += 64) {
-            const int p = base + lane;
-            const bool take = p < a.P && a.experts[p] == e;
-            const uint64_t mask = __ballot(take);
-            if (take) plist[count + __popcll(mask & ((1ull << lane) - 1ull))] = (uint16_t)p;
-            count += __popcll(mask);
-        }
+        const int count = pairs_of(a.experts, a.P, e, plist);
         for (int i = lane; i < count; i += 64) xlist[i] = (uint32_t)(plist[i] / a.k);
         if (lane == 0) pcount = count;
     }
@@ -180,100 +187,69 @@ __global__ __launch_bounds__(512) void moe_gate_up_kernel(MoeArgs a) {
     }
 }
 
-// blockIdx.x = output band (16*T rows of H). Every expert some pair uses, in
-// increasing order, then the band's rows of y.
+// blockIdx.y = expert e, blockIdx.x = band group (bands of 16*T rows of H).
+// The pairs routed to e are listed in LDS and taken 8 per pass, each as its
+// (hi, lo) rows of h: 16 activation rows per pass.
 template <int T>
 __global__ __launch_bounds__(512) void moe_down_kernel(MoeArgs a) {
-    __shared__ float red[Red<T, kMoeMaxS>::FLOATS];
-    __shared__ u32x4 wt[kMoeMaxS * (T * 128 + 256)];
+    __shared__ float red[Red<T>::FLOATS];
+    __shared__ u32x4 wt[kMfmaGatherMaxS * (T * 128 + 256)];
+    __shared__ int pcount;
     extern __shared__ u32x4 moe_dyn[];
-    // Dynamic LDS: pair list sorted by expert (P uint16, padded), per-expert
-    // counts and offsets (E + 1 ints each), a NaN flag per token, then the
-    // token rows of the band (T_tokens x 16*T floats).
     uint16_t *plist = reinterpret_cast<uint16_t *>(moe_dyn);
-    int *cnt = reinterpret_cast<int *>(moe_dyn + (a.P * 2 + 15) / 16);
-    int *off = cnt + a.E + 1;
-    int *bad = off + a.E + 1;
-    float *ylds = reinterpret_cast<float *>(bad + ((a.T + 3) / 4) * 4);
     const int lane = threadIdx.x & 63;
     const int wig = wave_id();
-    const int S = (int)(blockDim.x >> 6);
-    const uint32_t ne = (uint32_t)a.E;
-
-    for (int i = (int)threadIdx.x; i < a.T; i += (int)blockDim.x) bad[i] = 0;
-    for (int i = (int)threadIdx.x; i < a.T * 16 * T; i += (int)blockDim.x) ylds[i] = 0.f;
-    __syncthreads();
-    // Counts per expert (wave w takes experts w, w + S, ...), out-of-range ids.
-    for (int e = wig; e < a.E; e += S) {
-        int c = 0;
-        for (int base = 0; base < a.P; base += 64) {
-            const int p = base + lane;
-            c += __popcll(__ballot(p < a.P && a.experts[p] == (uint32_t)e));
-        }
-        if (lane == 0) cnt[e] = c;
-    }
-    for (int p = (int)threadIdx.x; p < a.P; p += (int)blockDim.x)
-        if (a.experts[p] >= ne) bad[p / a.k] = 1;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int s = 0;
-        for (int e = 0; e < a.E; ++e) {
-            off[e] = s;
-            s += cnt[e];
-        }
-        off[a.E] = s;
+    const uint32_t e = blockIdx.y;
+    if (wig == 0) {
+        const int count = pairs_of(a.experts, a.P, e, plist);
+        if (lane == 0) pcount = count;
     }
     __syncthreads();
-    // Each expert's pairs in increasing p.
-    for (int e = wig; e < a.E; e += S) {
-        int c = off[e];
-        for (int base = 0; base < a.P; base += 64) {
-            const int p = base + lane;
-            const bool take = p < a.P && a.experts[p] == (uint32_t)e;
-            const uint64_t mask = __ballot(take);
-            if (take) plist[c + __popcll(mask & ((1ull << lane) - 1ull))] = (uint16_t)p;
-            c += __popcll(mask);
-        }
-    }
-    __syncthreads();
-
+    const int count = pcount;
+    if (count == 0) return;
+    const int64_t plane = (int64_t)e * a.H;
     const uint32_t rowbytes = (uint32_t)(a.F / 2);
+    const Band bd{reinterpret_cast<const uint8_t *>(a.wd) + plane * rowbytes, a.sd + plane * (a.F / 64),
+                  a.bd + plane * (a.F / 64), a.H, rowbytes, (int32_t)(a.F / 64)};
     const uint32_t xbytes = (uint32_t)(2 * a.P) * (uint32_t)a.F * 2u;  // h: two rows per pair
     const __amdgpu_buffer_rsrc_t xr = range_of(a.h, xbytes);
-    const MfmaArgs pa = pass_args((int)a.F, S, a.SPW2, 1);
-    for (int e = 0; e < a.E; ++e) {
-        const int count = off[e + 1] - off[e];
-        if (count == 0) continue;  // uniform
-        const int64_t plane = (int64_t)e * a.H;
-        const Band bd{reinterpret_cast<const uint8_t *>(a.wd) + plane * rowbytes, a.sd + plane * (a.F / 64),
-                      a.bd + plane * (a.F / 64), a.H, rowbytes, (int32_t)(a.F / 64)};
-        const uint16_t *list = plist + off[e];
-        for (int base = 0; base < count; base += 8) {
-            const int me = count - base < 8 ? count - base : 8;
-            const int rows = 2 * me;  // (hi, lo) rows of h per pair
-            with_xq(rows, [&](auto xq) {
-                constexpr int XQ = decltype(xq)::value;
-                const Lanes ln = lane_consts<XQ>(pa, [&](uint32_t r) {
-                    return (int)r < rows ? (2u * list[base + (r >> 1)] + (r & 1u)) * (uint32_t)a.F * 2u : xbytes;
-                });
-                mfma_pass<T, XQ, CombineOut, false, kMoeMaxS>(pa, bd, ln, xr, rows,
-                                                              CombineOut{ylds, list + base, a.weights, a.k},
-                                                              blockIdx.x, gridDim.x, red, wt);
+    const MfmaArgs pa = pass_args((int)a.F, a.S2, a.SPW2, a.BPG2);
+    for (int base = 0; base < count; base += 8) {
+        const int me = count - base < 8 ? count - base : 8;
+        const int rows = 2 * me;
+        with_xq(rows, [&](auto xq) {
+            constexpr int XQ = decltype(xq)::value;
+            const Lanes ln = lane_consts<XQ>(pa, [&](uint32_t r) {
+                return (int)r < rows ? (2u * plist[base + (r >> 1)] + (r & 1u)) * (uint32_t)a.F * 2u : xbytes;
             });
-            __syncthreads();  // (S == 1 passes end without one) the next pass reuses the LDS buffers
-        }
-    }
-    __syncthreads();
-    const int64_t n0 = (int64_t)blockIdx.x * 16 * T;
-    for (int i = (int)threadIdx.x; i < a.T * 16 * T; i += (int)blockDim.x) {
-        const int t = i / (16 * T), c = i % (16 * T);
-        if (n0 + c < a.H) a.y[(int64_t)t * a.H + n0 + c] = bad[t] ? (uint16_t)0x7FC0u : f32_to_bf16(ylds[i]);
+            mfma_pass<T, XQ, WeightedOut>(pa, bd, ln, xr, rows, WeightedOut{a.o, a.H, plist + base, a.weights},
+                                          blockIdx.x, gridDim.x, red, wt);
+        });
     }
 }
 
-const void *moe_kernel(bool down) {
-    return down ? reinterpret_cast<const void *>(&moe_down_kernel<1>)
-                : reinterpret_cast<const void *>(&moe_gate_up_kernel);
+// y[t, n] = bf16(sum_j o[t*k + j, n]) in increasing j; NaN where one of the
+// token's expert ids is out of range.
+__global__ __launch_bounds__(256) void moe_combine_kernel(MoeArgs a) {
+    const int64_t total = (int64_t)a.T * a.H;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i / a.H, n = i - t * a.H;
+        float v = 0.f;
+        bool bad = false;
+        for (int j = 0; j < a.k; ++j) {
+            const int64_t p = t * a.k + j;
+            bad |= a.experts[p] >= (uint32_t)a.E;
+            v += a.o[p * a.H + n];
+        }
+        a.y[i] = bad ? (uint16_t)0x7FC0u : f32_to_bf16(v);
+    }
+}
+
+const void *moe_kernel(int stage, int tiles) {
+    if (stage == 0) return reinterpret_cast<const void *>(&moe_gate_up_kernel);
+    if (stage == 2) return reinterpret_cast<const void *>(&moe_combine_kernel);
+    return tiles == 1 ? reinterpret_cast<const void *>(&moe_down_kernel<1>)
+                      : reinterpret_cast<const void *>(&moe_down_kernel<2>);
 }
 
 }  // namespace agq

@@ -597,10 +597,12 @@ def qmm_workload(args, torch, si, agq, bf16, u32, stream, st, emit):
 
 def moe_workload(args, torch, si, agq, bf16, u32, stream, emit):
     """The Mixtral-shaped decode MoE layer (16 tokens, top-2 of 8 experts, H 4096, F 14336):
-    agq_moe_decode (two launches) against the same layer from the unfused products (gate and
+    agq_moe_decode (three launches) against the same layer from the unfused products (gate and
     up through agq_gather_qmv, SwiGLU and the weighted sum in torch, down through
     agq_gather_qmv). Weights rotate over >= 512 MiB of copies. Bytes: the used planes of
-    the three matrices, x, h (written and read twice: hi and lo rows) and y."""
+    the three matrices, x and y, the expert ids and router weights, and the two
+    intermediates written and read once each (h: two bf16 rows of F per pair; the fp32
+    down-projection row of H per pair)."""
     import numpy as np
     moe = si.workload(4)
     lay = si.moe_layer()
@@ -616,7 +618,7 @@ def moe_workload(args, torch, si, agq, bf16, u32, stream, emit):
     ids = u32(moe["ids"])
     w = torch.as_tensor(lay["weights"], device="cuda")
     y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(agq.moe_decode_workspace(T, k, F), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(agq.moe_decode_workspace(T, k, H, F), dtype=torch.uint8, device="cuda")
     fused = lambda i: agq.moe_decode(x, *cp[i % rot], ids, w, out=y, workspace=ws)  # noqa: E731
     rhs = u32(moe["ids"].reshape(-1))
     lhs = u32(np.repeat(np.arange(T, dtype=np.uint32), k))
@@ -629,8 +631,9 @@ def moe_workload(args, torch, si, agq, bf16, u32, stream, emit):
         o = agq.gather_qmv(h, *d_, rhs_indices=rhs).float()
         return (o.view(T, k, H) * w[:, :, None]).sum(1).to(torch.bfloat16)
 
-    nbytes = 3 * used * wb + 2 * T * H + 3 * 4 * T * k * F + 2 * T * H + 8 * T * k
-    for label, fn in (("moe_decode fused (2 launches)", fused), ("unfused: 3 gathers + torch SwiGLU/sum", unfused)):
+    P = T * k
+    nbytes = 3 * used * wb + 2 * T * H + 2 * T * H + 8 * P + 2 * (4 * P * F) + 2 * (4 * P * H)
+    for label, fn in (("moe_decode fused (3 launches)", fused), ("unfused: 3 gathers + torch SwiGLU/sum", unfused)):
         us, us_min = time_shape(torch, fn, 20, 5, stream)
         gb = nbytes / (us * 1e-6) / 1e9
         emit({"shape": f"{label}: Mixtral-shaped layer, {T} tokens top-{k} of {E}, H {H}, F {F} ({used} experts used)",

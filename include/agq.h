@@ -26,7 +26,7 @@
  *  - agq_qmm and agq_gather_qmm are the matrix-matrix (prefill) forms of the
  *    two;
  *  - agq_moe_decode is a whole decode MoE layer (gate, up, SwiGLU, down and
- *    the router-weighted sum) in two launches.
+ *    the router-weighted sum) in three launches.
  *
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers to contiguous row-major arrays. The
@@ -177,20 +177,21 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
  *   experts      [T, k] uint32 expert per (token, slot)
  *   weights      [T, k] float router weights (applied as given, not normalized)
  *   y            [T, H] BF16 (written)
- *   workspace    device scratch of at least agq_moe_decode_workspace(T, k, F)
- *                bytes, 16-byte aligned, owned by the caller; its contents on
- *                return are unspecified. Two calls that overlap in time must
- *                not share one.
- * Two kernel launches on `stream`: the gate and up projections with the
- * SwiGLU (each used expert's planes streamed once), then the down projection
- * with the router-weighted sum over slots, accumulated per output band in a
- * fixed order (bitwise deterministic). The intermediate h keeps about 17
- * significant bits. Supports 4-bit codes, group size 64, H and F multiples of
- * 512, T <= 256 tokens and T*k <= 4096 (else AGQ_ENOTSUP). A token with an
- * expert id >= E gets an all-NaN output row. Argument checks and errors as
- * for agq_qmv; a workspace below the size needed is AGQ_EINVAL.
+ *   workspace    device scratch of at least agq_moe_decode_workspace(T, k, H, F)
+ *                bytes (4*T*k*(F + H)), 16-byte aligned, owned by the caller;
+ *                its contents on return are unspecified. Two calls that
+ *                overlap in time must not share one.
+ * Three kernel launches on `stream`: the gate and up projections with the
+ * SwiGLU, and the down projection with the router weight, both as expert
+ * gathers (each used expert's planes streamed once for all of its pairs);
+ * then the sum over each token's k slots in slot order (bitwise
+ * deterministic). The intermediate h keeps about 17 significant bits.
+ * Supports 4-bit codes, group size 64, H and F multiples of 512, T <= 256
+ * tokens and T*k <= 4096 (else AGQ_ENOTSUP). A token with an expert id >= E
+ * gets an all-NaN output row. Argument checks and errors as for agq_qmv; a
+ * workspace below the size needed is AGQ_EINVAL.
  */
-int64_t agq_moe_decode_workspace(int64_t T, int64_t k, int64_t F);
+int64_t agq_moe_decode_workspace(int64_t T, int64_t k, int64_t H, int64_t F);
 agq_status agq_moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate, const void *b_gate,
                           const uint32_t *w_up, const void *s_up, const void *b_up,
                           const uint32_t *w_down, const void *s_down, const void *b_down,
@@ -202,9 +203,9 @@ agq_status agq_moe_decode(const void *x, const uint32_t *w_gate, const void *s_g
 /*
  * agq_moe_decode without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid allocation). The intermediate h lives in a scratch
- * array the library holds on each device (8 MiB, kept until the process
- * ends): T*k*F must stay at or below 2M (4*T*k*F bytes), else AGQ_ENOTSUP.
+ * harnesses that forbid allocation). The workspace lives in a scratch array
+ * the library holds on each device (8 MiB, kept until the process ends):
+ * 4*T*k*(F + H) bytes must fit in it, else AGQ_ENOTSUP.
  * The call allocates nothing. Every call on a device shares that array and it
  * keeps the last call's contents, so calls that overlap in time on one device
  * (on different streams) race and must not be issued. Otherwise the same

@@ -41,8 +41,10 @@ def test_library_exports_every_declared_symbol(name):
 
 
 def test_moe_workspace_size():
-    assert lib.agq_moe_decode_workspace(16, 2, 14336) == 4 * 32 * 14336
-    assert lib.agq_moe_decode_workspace(0, 2, 14336) == 0
+    lib.agq_moe_decode_workspace.argtypes = [ctypes.c_int64] * 4
+    lib.agq_moe_decode_workspace.restype = ctypes.c_int64
+    assert lib.agq_moe_decode_workspace(16, 2, 4096, 14336) == 4 * 32 * (14336 + 4096)
+    assert lib.agq_moe_decode_workspace(0, 2, 4096, 14336) == 0
 
 
 def test_status_strings():
@@ -136,7 +138,7 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: moe(F=1088), ENOTSUP),
     (lambda: moe(T=257), ENOTSUP),
     (lambda: moe(T=256, k=17), ENOTSUP),
-    (lambda: moe(wsb=4 * 4 * 2 * 1024 - 1), EINVAL),
+    (lambda: moe(wsb=4 * 4 * 2 * (1024 + 512) - 1), EINVAL),
     (lambda: moe(ws=ctypes.c_void_p(0x10008)), EINVAL),
     (lambda: moe(ex=ctypes.c_void_p(0x10002)), EINVAL),
     (lambda: lib.agq_dequantize(A, A, A, ctypes.c_void_p(0x10004), 4, 64, 4, 64, None), EINVAL),

@@ -74,6 +74,6 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     E, H, F = 2, 512, 14336 * 2
     z = torch.zeros(16, dtype=torch.int32, device="cuda")
     planes = [(z, z, z)] * 3
-    T, k = 64, 2  # 4*T*k*F bytes = 14.7 MB > 8 MiB
+    T, k = 64, 2  # 4*T*k*(F + H) bytes = 14.9 MB > 8 MiB
     rc = noalloc(z, planes, z, z.float(), z, T, k, E, H, F)
     assert rc == agq.AGQ_ENOTSUP and b"scratch" in lib.agq_last_error()
