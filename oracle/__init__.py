@@ -55,7 +55,9 @@ def _bind(lib):
     lib.agqo_qmv.argtypes = [P, I64, P, P, P, I64, I64, I, I, P, I64, P, P]
     lib.agqo_gather_qmv.argtypes = [P, I64, P, P, P, I64, I64, I64, I, I, P, P, I64, P, I64, P, P]
     lib.agqo_moe_swiglu.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, I, I, P, P]
-    for f in (lib.agqo_unpack, lib.agqo_dequantize, lib.agqo_qmv, lib.agqo_gather_qmv, lib.agqo_moe_swiglu):
+    lib.agqo_quantize.argtypes = [P, I64, I64, I, I, P, P, P]
+    for f in (lib.agqo_unpack, lib.agqo_dequantize, lib.agqo_qmv, lib.agqo_gather_qmv, lib.agqo_moe_swiglu,
+              lib.agqo_quantize):
         f.restype = I
     return lib
 
@@ -161,3 +163,15 @@ def moe_swiglu(x, gate, up, down, experts, weights, bits: int, group_size: int =
     _check(lib.agqo_moe_swiglu(_p(x), T, H, F, E, k, *[_p(v) for v in arrs], _p(ex), _p(r), bits, group_size,
                                _p(y), _p(a)))
     return y, a
+
+
+def quantize(w, bits: int, group_size: int = 64, lib=None):
+    """float32 ``[N, K]`` -> (packed uint32 ``[N, K*bits/32]``, scales bf16 ``[N, K/gs]``, biases bf16)."""
+    lib = lib or load()
+    w = _c(w, np.float32)
+    N, K = w.shape
+    wq = np.empty((N, K * bits // 32), dtype=np.uint32)
+    s = np.empty((N, K // group_size), dtype=np.uint16)
+    b = np.empty_like(s)
+    _check(lib.agqo_quantize(_p(w), N, K, bits, group_size, _p(wq), _p(s), _p(b)))
+    return wq, s, b

@@ -261,3 +261,57 @@ int agqo_moe_swiglu(const uint16_t *x, int64_t T, int64_t H, int64_t F, int64_t 
     free(h);
     return AGQO_OK;
 }
+
+/* binary32 -> bfloat16 bit pattern, round to nearest even (NaN stays NaN). */
+static uint16_t bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* Affine group quantizer, the recipe the workloads state: per row and group of
+ * group_size consecutive columns, in binary32,
+ *   scale = bf16((max - min) / (2^bits - 1)),  bias = bf16(min),
+ *   q = clamp(rint((w - bias) / scale), 0, 2^bits - 1)   (q = 0 where scale is 0)
+ * with rint rounding half to even, using the rounded scale and bias. Codes are
+ * packed low-first into uint32 words. w is [N, K] float; wq [N, K*bits/32];
+ * scales and biases [N, K/group_size] bf16. */
+int agqo_quantize(const float *w, int64_t N, int64_t K, int bits, int group_size,
+                  uint32_t *wq, uint16_t *scales, uint16_t *biases)
+{
+    if (!w || !wq || !scales || !biases || N <= 0) return AGQO_EARG;
+    if (check_format(K, bits, group_size)) return AGQO_EARG;
+    const int64_t groups = K / group_size, per_word = 32 / bits, words = K / per_word;
+    const float levels = (float)((1 << bits) - 1);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t i = 0; i < words; ++i) wq[n * words + i] = 0;
+        for (int64_t g = 0; g < groups; ++g) {
+            const float *wg = w + n * K + g * group_size;
+            float mx = wg[0], mn = wg[0];
+            for (int64_t j = 1; j < group_size; ++j) {
+                if (wg[j] > mx) mx = wg[j];
+                if (wg[j] < mn) mn = wg[j];
+            }
+            const float diff = mx - mn;
+            const uint16_t s16 = bf16_rne(diff / levels);
+            const uint16_t b16 = bf16_rne(mn);
+            scales[n * groups + g] = s16;
+            biases[n * groups + g] = b16;
+            const float s = (float)bf16_value(s16), b = (float)bf16_value(b16);
+            for (int64_t j = 0; j < group_size; ++j) {
+                uint32_t q = 0;
+                if (s != 0.0f) {
+                    const float num = wg[j] - b;
+                    const float r = rintf(num / s);
+                    q = r <= 0.0f ? 0u : r >= levels ? (uint32_t)levels : (uint32_t)r;
+                }
+                const int64_t k = g * group_size + j;
+                wq[n * words + k / per_word] |= q << (uint32_t)(bits * (k % per_word));
+            }
+        }
+    }
+    return AGQO_OK;
+}

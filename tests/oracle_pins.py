@@ -52,11 +52,11 @@ def _random_problem(seed, M, N, K, bits, E=None):
     return x, codes, scales, biases
 
 
-def _exact_row(xrow, qrow, srow, brow):
+def _exact_row(xrow, qrow, srow, brow, gs=64):
     y = Fraction(0)
     a = Fraction(0)
     for k in range(len(qrow)):
-        w = _frac_bf16(srow[k // 64]) * int(qrow[k]) + _frac_bf16(brow[k // 64])
+        w = _frac_bf16(srow[k // gs]) * int(qrow[k]) + _frac_bf16(brow[k // gs])
         t = _frac_bf16(xrow[k]) * w
         y += t
         a += abs(t)
@@ -162,6 +162,27 @@ def pin_dot_exact_bruteforce(lib):
                     bound = 2 * K * U53 * float(ae)
                     assert abs(y[m, n] - float(ye)) <= bound, (bits, M, N, K, m, n)
                     assert abs(a[m, n] - float(ae)) <= bound, (bits, M, N, K, m, n)
+
+
+def pin_other_group_sizes_bruteforce(lib):
+    """Groups of 32 and 128 columns: exact rationals over codes from before packing."""
+    for bits in (4, 8):
+        for gs, K in ((32, 96), (128, 256)):
+            g = np.random.default_rng([70, bits, gs])
+            M, N = 2, 3
+            q = g.integers(0, 2 ** bits, size=(N, K), dtype=np.uint8)
+            sc = bf16_bits((0.01 + 0.02 * g.random((N, K // gs))).astype(np.float32))
+            bi = bf16_bits((-0.05 + 0.03 * g.standard_normal((N, K // gs))).astype(np.float32))
+            x = bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+            y, a = oracle.qmv(x, pack_codes(q, bits), sc, bi, K, bits, group_size=gs, lib=lib)
+            for m in range(M):
+                for n in range(N):
+                    ye, ae = _exact_row(x[m], q[n], sc[n], bi[n], gs)
+                    assert abs(y[m, n] - float(ye)) <= 2 * K * U53 * float(ae), (bits, gs, m, n)
+            deq, _ = oracle.dequantize(pack_codes(q, bits), sc, bi, K, bits, group_size=gs, lib=lib)
+            want = np.repeat(bf16_to_f32(sc).astype(np.float64), gs, axis=1) * q + \
+                np.repeat(bf16_to_f32(bi).astype(np.float64), gs, axis=1)
+            assert np.array_equal(deq, want), (bits, gs)
 
 
 def pin_numpy_blas(lib):
@@ -346,6 +367,87 @@ def pin_moe_bruteforce_tanh_form(lib):
             assert np.all(np.abs(y[t] - want) <= 1e-12 * a[t]), (bits, t, np.max(np.abs(y[t] - want) / np.maximum(a[t], 1e-300)))
             # the tolerance scale: sum_j |r| * sum_n |w_down * h|
             assert np.all(a[t] > 0)
+
+
+def pin_quantize_known_groups(lib):
+    """Hand-worked groups: a ramp 1 + 0.5*c over codes c spanning 0 .. 2^bits - 1 gives
+    scale 0.5, bias 1 and codes c; a constant group gives scale 0, bias the constant, codes 0; ties round
+    to even codes; values beyond the ramp clamp."""
+    for bits in (4, 8):
+        lv = 2 ** bits - 1
+        K = 64
+        codes = np.concatenate([[0, lv], np.arange(1, K - 1) % (lv + 1)])  # spans 0 .. 2^bits - 1
+        ramp = (1.0 + 0.5 * codes).astype(np.float32)
+        const = np.full(K, -0.375, np.float32)
+        ties = np.zeros(K, np.float32)
+        ties[0], ties[1] = 0.0, float(lv)       # scale 1, bias 0
+        ties[2:6] = [0.5, 1.5, 2.5, 3.5]        # half-way values -> even codes 0, 2, 2, 4
+        w = np.stack([ramp, const, ties])
+        wq, sc, bi = oracle.quantize(w, bits, lib=lib)
+        q = oracle.unpack(wq, K, bits, lib=lib)
+        assert sc[0, 0] == 0x3F00 and bi[0, 0] == 0x3F80, (bits, hex(sc[0, 0]), hex(bi[0, 0]))
+        assert np.array_equal(q[0], codes)
+        assert sc[1, 0] == 0 and bi[1, 0] == 0xBEC0 and not q[1].any()
+        assert sc[2, 0] == 0x3F80 and bi[2, 0] == 0
+        assert q[2, :6].tolist() == [0, lv, 0, 2, 2, 4]
+
+
+def pin_quantize_properties(lib):
+    """On random groups: every code is in range; the scale and bias are the bf16 roundings
+    of (max - min)/(2^bits - 1) and min; values strictly inside the code range land within
+    half a scale (plus the float32 rounding of (w - b)/s) of their dequantized weight; the
+    dequantized weights re-quantize to the same codes, scales and biases wherever the codes
+    span the full range (then max and min are exactly representable on the grid)."""
+    for bits in (4, 8):
+        for gs in (32, 64, 128):
+            g = np.random.default_rng([71, bits, gs])
+            N, K = 6, 256
+            w = (0.02 * g.standard_normal((N, K))).astype(np.float32)
+            wq, sc, bi = oracle.quantize(w, bits, gs, lib=lib)
+            q = oracle.unpack(wq, K, bits, lib=lib)
+            lv = 2 ** bits - 1
+            wg = w.reshape(N, K // gs, gs).astype(np.float64)
+            s = bf16_to_f32(sc).astype(np.float64)
+            b = bf16_to_f32(bi).astype(np.float64)
+            assert np.array_equal(sc, bf16_bits(((wg.max(-1) - wg.min(-1)).astype(np.float32) /
+                                                 np.float32(lv)).astype(np.float32)))
+            assert np.array_equal(bi, bf16_bits(wg.min(-1).astype(np.float32)))
+            qg = q.reshape(N, K // gs, gs).astype(np.float64)
+            what = s[..., None] * qg + b[..., None]
+            inner = ((wg - b[..., None]) / s[..., None] > 0.5) & ((wg - b[..., None]) / s[..., None] < lv - 0.5)
+            err = np.abs(wg - what)
+            assert np.all(err[inner] <= (0.5 + 1e-5) * np.broadcast_to(s[..., None], err.shape)[inner])
+            deq, _ = oracle.dequantize(wq, sc, bi, K, bits, gs, lib=lib)
+            wq2, sc2, bi2 = oracle.quantize(deq.astype(np.float32), bits, gs, lib=lib)
+            full = (qg.min(-1) == 0) & (qg.max(-1) == lv)
+            assert full.any()
+            q2 = oracle.unpack(wq2, K, bits, lib=lib).reshape(N, K // gs, gs)
+            assert np.array_equal(sc2[full], sc[full]) and np.array_equal(bi2[full], bi[full])
+            assert np.array_equal(q2[full], qg[full].astype(np.uint8))
+
+
+def pin_quantize_codes_are_nearest(lib):
+    """Each code is the grid point s*q + b (q in 0 .. 2^bits - 1) nearest to its weight, up to
+    the float32 rounding of (w - b)/s. Groups offset far from zero (8-bit) make rounding the
+    scale and bias push some weights past either end of the grid, which only a clamp fixes."""
+    for bits in (4, 8):
+        lv = 2 ** bits - 1
+        g = np.random.default_rng([72, bits])
+        N, K = 64, 64
+        w = (0.02 * g.standard_normal((N, K))).astype(np.float32)
+        w[N // 2:] += (100 * g.random((N // 2, 1)) + 1).astype(np.float32)  # offset groups
+        wq, sc, bi = oracle.quantize(w, bits, lib=lib)
+        q = oracle.unpack(wq, K, bits, lib=lib).astype(np.int64)
+        s = bf16_to_f32(sc).astype(np.float64)[:, :1]
+        b = bf16_to_f32(bi).astype(np.float64)[:, :1]
+        grid = s[:, :, None] * np.arange(lv + 1)[None, None, :] + b[:, :, None]  # [N, 1, levels]
+        dist = np.abs(w.astype(np.float64)[:, :, None] - grid)
+        best = dist.min(-1)
+        got = np.take_along_axis(dist, q[:, :, None], -1)[..., 0]
+        assert np.all(got <= best + 1e-4 * s), np.max((got - best) / s)
+        outside = (w < b - 0.5 * s) | (w > b + (lv + 0.5) * s)
+        if bits == 8:
+            assert outside.any()  # the case needs clamping
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

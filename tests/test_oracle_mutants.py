@@ -43,6 +43,15 @@ MUTANTS = {
     "moe_magnitude_signed": ("size += fabs(part);", "size += part;"),
     "moe_down_expert_ignored": ("const int64_t row = e * H + m;", "const int64_t row = m;"),
     "moe_token_row_ignored": ("row_dot(x + t * H, wg", "row_dot(x, wg"),
+    "quant_levels_off_by_one": ("const float levels = (float)((1 << bits) - 1);",
+                                "const float levels = (float)(1 << bits);"),
+    "quant_bias_is_max": ("const uint16_t b16 = bf16_rne(mn);", "const uint16_t b16 = bf16_rne(mx);"),
+    "quant_truncates": ("const float r = rintf(num / s);", "const float r = floorf(num / s);"),
+    "quant_unrounded_scale": ("const float s = (float)bf16_value(s16), b = (float)bf16_value(b16);",
+                              "const float s = diff / levels, b = (float)bf16_value(b16);"),
+    "quant_no_clamp": ("q = r <= 0.0f ? 0u : r >= levels ? (uint32_t)levels : (uint32_t)r;",
+                       "q = (uint32_t)r & ((1u << bits) - 1u);"),
+    "quant_bf16_truncates": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "return (uint16_t)(u >> 16);"),
     "moe_up_with_gate_scales": ("row_dot(x + t * H, wu + row * hw, su + row * hg,",
                                 "row_dot(x + t * H, wu + row * hw, sg + row * hg,"),
 }
