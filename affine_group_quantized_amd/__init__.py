@@ -18,7 +18,8 @@ import os
 
 import torch
 
-__all__ = ["qmv", "qmv_wide", "gather_qmv", "qmm", "gather_qmm", "moe_decode", "moe_decode_workspace", "dequantize", "plan", "launch_plan", "prepare_qmv", "AgqError",
+__all__ = ["qmv", "qmv_wide", "gather_qmv", "qmm", "gather_qmm", "moe_decode", "moe_decode_workspace", "quantize",
+           "dequantize", "plan", "launch_plan", "prepare_qmv", "AgqError",
            "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libagq.so")
@@ -66,6 +67,8 @@ def _load(path: str = LIB_PATH):
     lib.agq_moe_decode_workspace.restype = I64
     lib.agq_moe_decode.argtypes = [P] * 14 + [I64] * 6 + [I, I, P]
     lib.agq_moe_decode.restype = I
+    lib.agq_quantize.argtypes = [P, I, P, P, P, I64, I64, I, I, P]
+    lib.agq_quantize.restype = I
     lib.agq_dequantize.argtypes = [P, P, P, P, I64, I64, I, I, P]
     lib.agq_plan_product.argtypes = [I64, I64, I64, I, I, I, I, I64, ctypes.POINTER(Plan)]
     lib.agq_plan_launch.argtypes = [I64, I64, I64, I, I, I64, ctypes.POINTER(Plan)]
@@ -300,6 +303,23 @@ def moe_decode(x, gate, up, down, experts, weights, bits: int = 4, group_size: i
                                   *[_ptr(t) for t in down], _ptr(experts), _ptr(weights), _ptr(out), _ptr(workspace),
                                   workspace.numel(), T, k, E, H, F, bits, group_size, _stream(device)))
     return out
+
+
+def quantize(w, bits: int = 4, group_size: int = 64):
+    """Affine group quantization on the device: ``w`` [..., K] float32 or bf16 ->
+    (codes int32 [..., K*bits/32], scales bf16 [..., K/group_size], biases bf16)."""
+    device = w.device
+    _need(w, "w", (torch.float32, torch.bfloat16), device)
+    K = w.shape[-1]
+    lead = tuple(w.shape[:-1])
+    rows = w.numel() // K
+    codes = torch.empty(lead + (K * bits // 32,), dtype=torch.int32, device=device)
+    scales = torch.empty(lead + (K // group_size,), dtype=torch.bfloat16, device=device)
+    biases = torch.empty_like(scales)
+    with torch.cuda.device(device):
+        _check(lib.agq_quantize(_ptr(w), 0 if w.dtype == torch.float32 else 1, _ptr(codes), _ptr(scales),
+                                _ptr(biases), rows, K, bits, group_size, _stream(device)))
+    return codes, scales, biases
 
 
 def dequantize(w, scales, biases, bits: int = 4, group_size: int = 64, out=None):

@@ -146,7 +146,8 @@ agq_status check_format(int64_t N, int64_t K, int bits, int group_size) {
         return fail(AGQ_EINVAL, "N or K too large (N=%lld, K=%lld)", (long long)N, (long long)K);
     if (group_size <= 0) return fail(AGQ_EINVAL, "group_size must be positive (got %d)", group_size);
     if (bits != 4 && bits != 8) return fail(AGQ_ENOTSUP, "bits=%d not supported (4 or 8)", bits);
-    if (group_size != 64) return fail(AGQ_ENOTSUP, "group_size=%d not supported (64)", group_size);
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(AGQ_ENOTSUP, "group_size=%d not supported (32, 64 or 128)", group_size);
     if (K % group_size != 0) return fail(AGQ_EINVAL, "K=%lld is not a multiple of group_size", (long long)K);
     return AGQ_OK;
 }
@@ -273,7 +274,7 @@ void export_plan(const agq::Plan &p, agq_plan *out) {
 }
 
 agq::ProductArgs make_args(const void *x, const uint32_t *w, const void *s, const void *b, void *y, int64_t N,
-                           int64_t K, int bits, int M, const agq::Plan &p) {
+                           int64_t K, int bits, int M, const agq::Plan &p, int group_size) {
     agq::ProductArgs a{};
     a.x = static_cast<const uint16_t *>(x);
     a.w = reinterpret_cast<const agq::u32x4 *>(w);
@@ -284,7 +285,13 @@ agq::ProductArgs make_args(const void *x, const uint32_t *w, const void *s, cons
     a.RPG = p.RPG;
     a.K = (int32_t)K;
     a.C = (int32_t)(K * bits / 128);
-    a.G = (int32_t)(K / 64);
+    a.G = (int32_t)(K / group_size);
+    int cpg = group_size * bits / 128;  // 16-byte chunks per group: 1, 2, 4 or 8
+    a.gshift = 0;
+    while (cpg > 1) {
+        cpg >>= 1;
+        ++a.gshift;
+    }
     a.M = M;
     a.S = p.S;
     a.GPB = p.GPB;
@@ -304,7 +311,7 @@ agq_status dense_product(const void *x, const uint32_t *w, const void *s, const 
     if (st != AGQ_OK) return st;
     if (M <= 0) return fail(AGQ_EINVAL, "M must be positive (got %lld)", (long long)M);
     if (M > 8) return fail(AGQ_ENOTSUP, "M=%lld > 8 is a quantized GEMM, not a matvec", (long long)M);
-    if (agq::mfma_eligible(M, K, bits, 0, M)) {
+    if (group_size == 64 && agq::mfma_eligible(M, K, bits, 0, M)) {
         agq::MfmaPlan mp;
         const void *sym = nullptr;
         st = launch_mfma_plan(M, N, K, 0, &mp, &sym);
@@ -318,7 +325,7 @@ agq_status dense_product(const void *x, const uint32_t *w, const void *s, const 
     const void *sym = nullptr;
     st = launch_plan(M, N, K, bits, 0, &plan, &sym);
     if (st != AGQ_OK) return st;
-    agq::ProductArgs a = make_args(x, w, s, b, y, N, K, bits, (int)M, plan);
+    agq::ProductArgs a = make_args(x, w, s, b, y, N, K, bits, (int)M, plan, group_size);
     return launch(sym, dim3((unsigned)plan.blocks), dim3(plan.threads), (size_t)plan.x_lds_bytes, &a, stream);
 }
 
@@ -375,7 +382,7 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
     if (R > INT32_MAX) return fail(AGQ_EINVAL, "R too large");
     if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
     if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
-    if (agq::mfma_eligible(8, K, bits, E, R)) {
+    if (group_size == 64 && agq::mfma_eligible(8, K, bits, E, R)) {
         agq::MfmaPlan mp;
         const void *sym = nullptr;
         st = launch_mfma_plan(P, N, K, E, &mp, &sym);
@@ -394,7 +401,7 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
     const void *sym = nullptr;
     st = launch_plan(8, N, K, bits, E, &plan, &sym);
     if (st != AGQ_OK) return st;
-    agq::ProductArgs a = make_args(x, w, scales, biases, y, N, K, bits, (int)P, plan);
+    agq::ProductArgs a = make_args(x, w, scales, biases, y, N, K, bits, (int)P, plan, group_size);
     a.lhs = lhs_indices;
     a.rhs = rhs_indices;
     a.R_x = (int32_t)R;
@@ -413,6 +420,7 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
     // a multiple of 512): the matrix-core matvec kernel, one grid row per pass of
     // 16 rows. Beyond: the tiled GEMM.
     if (M <= 8) return dense_product(x, w, scales, biases, y, M, N, K, bits, group_size, stream);
+    if (group_size != 64) return fail(AGQ_ENOTSUP, "qmm beyond 8 rows takes group size 64");
     if (M <= agq::kQmmPassRows && agq::mfma_eligible(M, K, bits, 0, M)) {
         agq::MfmaPlan mp;
         const void *sym = nullptr;
@@ -462,6 +470,7 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
     if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
     if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
     if (R * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (R*K*2 bytes)");
+    if (group_size != 64) return fail(AGQ_ENOTSUP, "gather_qmm takes group size 64");
     const agq::QmmKernel k = agq::qmm_kernel_for(bits, true, (P + E - 1) / E);
     if ((int64_t)k.bn * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
     const int64_t nt = (N + k.bn - 1) / k.bn;
@@ -542,8 +551,8 @@ agq_status moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate,
         misaligned(s_down, 2) || misaligned(b_down, 2) || misaligned(y, 2) || misaligned(experts, 4) ||
         misaligned(weights, 4))
         return fail(AGQ_EINVAL, "misaligned scales, biases, y, experts or weights");
-    if (bits != 4 || H % 512 != 0 || F % 512 != 0)
-        return fail(AGQ_ENOTSUP, "the fused MoE takes 4-bit codes with H and F multiples of 512");
+    if (bits != 4 || group_size != 64 || H % 512 != 0 || F % 512 != 0)
+        return fail(AGQ_ENOTSUP, "the fused MoE takes 4-bit codes, group size 64, H and F multiples of 512");
     if (T > agq::kMoeMaxTokens) return fail(AGQ_ENOTSUP, "T=%lld tokens exceeds %d", (long long)T, agq::kMoeMaxTokens);
     const int64_t P = T * k;
     if (P > agq::kMaxPairs) return fail(AGQ_ENOTSUP, "T*k=%lld pairs exceeds %d", (long long)P, agq::kMaxPairs);
@@ -634,6 +643,30 @@ agq_status moe_decode(const void *x, const uint32_t *w_gate, const void *s_gate,
 
 extern "C" {
 
+agq_status agq_quantize(const void *w, int w_dtype, uint32_t *codes, void *scales, void *biases, int64_t rows,
+                        int64_t K, int bits, int group_size, void *stream) {
+    if (!w || !codes || !scales || !biases) return fail(AGQ_EINVAL, "null tensor pointer");
+    if (w_dtype != AGQ_DTYPE_F32 && w_dtype != AGQ_DTYPE_BF16)
+        return fail(AGQ_EINVAL, "w_dtype must be AGQ_DTYPE_F32 or AGQ_DTYPE_BF16 (got %d)", w_dtype);
+    agq_status st = check_format(rows, K, bits, group_size);
+    if (st != AGQ_OK) return st;
+    if (misaligned(w, w_dtype == AGQ_DTYPE_F32 ? 4 : 2) || misaligned(codes, 4) || misaligned(scales, 2) ||
+        misaligned(biases, 2))
+        return fail(AGQ_EINVAL, "misaligned tensor pointer");
+    int cus = 0, dev = 0;
+    st = current_device(&cus, &dev);
+    if (st != AGQ_OK) return st;
+    int64_t groups = rows * (K / group_size);
+    int64_t blocks = (groups + 255) / 256;
+    if (blocks > (int64_t)cus * 16) blocks = (int64_t)cus * 16;
+    int gsi = group_size;
+    void *args[] = {&w, &groups, &K, &gsi, &codes, &scales, &biases};
+    hipError_t e = hipLaunchKernel(agq::quantize_kernel_for(bits, w_dtype == AGQ_DTYPE_BF16), dim3((unsigned)blocks),
+                                   dim3(256), args, 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(AGQ_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return AGQ_OK;
+}
+
 agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *biases, float *out, int64_t rows,
                           int64_t K, int bits, int group_size, void *stream) {
     agq_status st = check_operands(nullptr, w, scales, biases, out, rows, K, bits, group_size, false);
@@ -648,7 +681,8 @@ agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *bia
     int64_t cap = (int64_t)cus * 32;
     if (blocks > cap) blocks = cap;
     const void *sym = agq::dequant_kernel_sym(bits);
-    void *args[] = {&w, &scales, &biases, &out, &words, &words_per_row, &K};
+    int64_t gs = group_size;
+    void *args[] = {&w, &scales, &biases, &out, &words, &words_per_row, &K, &gs};
     hipError_t e = hipLaunchKernel(sym, dim3((unsigned)blocks), dim3(256), args, 0, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(AGQ_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return AGQ_OK;
@@ -663,7 +697,7 @@ agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group
     if (experts == 0 && M <= 0) return fail(AGQ_EINVAL, "M must be positive");
     if (experts == 0 && M > 8) return fail(AGQ_ENOTSUP, "M > 8");
     if (num_cus <= 0 || waves_per_cu <= 0) return fail(AGQ_EINVAL, "num_cus and waves_per_cu must be positive");
-    if (agq::mfma_eligible(M, K, bits, experts, experts ? 1 : M)) {
+    if (group_size == 64 && agq::mfma_eligible(M, K, bits, experts, experts ? 1 : M)) {
         agq::MfmaPlan mp;
         agq::mfma_shape(N, K, experts, &mp);
         agq::mfma_lds(experts, 32, &mp);  // (gather plans assume 32 pairs)
@@ -687,7 +721,7 @@ agq_status agq_plan_launch(int64_t M, int64_t N, int64_t K, int bits, int group_
     if (experts < 0) return fail(AGQ_EINVAL, "experts must be >= 0");
     if (experts == 0 && M <= 0) return fail(AGQ_EINVAL, "M must be positive");
     if (experts == 0 && M > 8) return fail(AGQ_ENOTSUP, "M > 8");
-    if (agq::mfma_eligible(M, K, bits, experts, experts ? 1 : M)) {
+    if (group_size == 64 && agq::mfma_eligible(M, K, bits, experts, experts ? 1 : M)) {
         agq::MfmaPlan mp;
         const void *sym = nullptr;
         st = launch_mfma_plan(M, N, K, experts, &mp, &sym);

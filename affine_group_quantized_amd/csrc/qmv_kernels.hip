@@ -9,7 +9,8 @@
 // per-group activation sums do not depend on n, so they are computed once.
 //
 // Work decomposition. A weight row is C 16-byte chunks. A 4-bit chunk holds 32
-// codes (half a group); an 8-bit chunk holds 16 codes (a quarter of a group).
+// codes, an 8-bit chunk 16: one scale group of 64 columns is 2 or 4 chunks
+// (group sizes 32 and 128 halve or double that; a chunk never spans groups).
 //  - Waves split K into segments of 64*CPT chunks. Lane l of a wave owns
 //    chunks seg + 64*j + l (j < CPT), so each load instruction of the wave
 //    reads 1 KB of contiguous memory.
@@ -53,11 +54,6 @@ namespace agq {
 // Dynamic LDS of the product kernels: the block's copy of x (XFill).
 extern __shared__ u32x4 g_xlds[];
 
-template <int BITS>
-struct Fmt {
-    static constexpr int EPC = 128 / BITS;  // codes per 16-byte chunk
-    static constexpr int CPG = 64 / EPC;    // chunks per 64-column group
-};
 
 // Activation staging. A lane's slice of one activation row for one chunk is
 // sixteen 32-bit registers:
@@ -470,7 +466,7 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
         chunk[j] = (wig * CPT + j) * 64 + lane;
         cv[j] = chunk[j] < a.C;
         woff[j] = (uint32_t)chunk[j] * 16u;
-        goff[j] = (uint32_t)(chunk[j] / Fmt<BITS>::CPG) * 2u;
+        goff[j] = (uint32_t)(chunk[j] >> a.gshift) * 2u;  // the chunk's scale group
     }
 
     RowBuf<CPT, R> buf[NB];
@@ -696,15 +692,15 @@ __global__ __launch_bounds__(512) void gather_qmv_kernel(ProductArgs a) {
 template <int BITS>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t *__restrict__ w, const uint16_t *__restrict__ s,
                                                       const uint16_t *__restrict__ b, float *__restrict__ out,
-                                                      int64_t words, int64_t words_per_row, int64_t K) {
+                                                      int64_t words, int64_t words_per_row, int64_t K, int64_t gs) {
     constexpr int PER = 32 / BITS;
     constexpr uint32_t MASK = (1u << BITS) - 1u;
-    const int64_t groups = K / 64;
+    const int64_t groups = K / gs;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t row = i / words_per_row;
         const int64_t k0 = (i - row * words_per_row) * PER;
-        const int64_t g = row * groups + k0 / 64;
+        const int64_t g = row * groups + k0 / gs;  // a word's codes share one group (gs >= 32 >= PER)
         const float sf = bf16_lo(s[g]);
         const float bf = bf16_lo(b[g]);
         const uint32_t word = w[i];

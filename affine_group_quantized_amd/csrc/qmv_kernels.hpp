@@ -26,7 +26,8 @@ struct ProductArgs {
     int32_t E;            // gather: expert planes
     int32_t S;            // waves per row group (K split)
     int32_t GPB;          // row groups per block
-    int32_t pad_[2];
+    int32_t gshift;       // log2 of 16-byte chunks per scale group (group sizes 32, 64, 128)
+    int32_t pad_;
 };
 
 // Argument block of the matrix-core kernels (4-bit codes, K a multiple of
@@ -57,6 +58,8 @@ struct MfmaArgs {
 // LDS copy of x (0: none)), or NULL.
 const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather);
 const void *dequant_kernel_sym(int bits);
+// Group quantizer kernel for 4- or 8-bit codes from fp32 or bf16 weights.
+const void *quantize_kernel_for(int bits, bool bf16_in);
 // Matrix-core kernel with bands of 16*tiles rows (tiles 1 or 2). Dense
 // products choose the activation load form by their rows per pass: one
 // rotated load per segment up to 4 rows, staged through LDS up to 8, four

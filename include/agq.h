@@ -87,9 +87,9 @@ const char *agq_last_error(void);
  *   scales [N, K/group_size] BF16
  *   biases [N, K/group_size] BF16
  *   y      [N] BF16 (written)
- * bits must be 4 or 8 and group_size 64 (else AGQ_ENOTSUP); K must be a
- * positive multiple of group_size, and N positive (else AGQ_EINVAL). K above
- * 114688 (4-bit) or 57344 (8-bit) is AGQ_ENOTSUP.
+ * bits must be 4 or 8 and group_size 32, 64 or 128 (else AGQ_ENOTSUP); K must
+ * be a positive multiple of group_size, and N positive (else AGQ_EINVAL). K
+ * above 114688 (4-bit) or 57344 (8-bit) is AGQ_ENOTSUP.
  */
 agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                    void *y, int64_t N, int64_t K, int bits, int group_size, void *stream);
@@ -99,8 +99,8 @@ agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const v
  * 1 <= M <= 8 activation rows, streaming each weight byte once for all M rows.
  *   x [M, K] BF16, y [M, N] BF16; w, scales and biases as in agq_qmv.
  * M > 8 is AGQ_ENOTSUP; that is a quantized GEMM, not a matvec. With 4-bit
- * codes, M >= 4 and K a multiple of 512 the product runs on the matrix cores
- * and K is limited only by M*K*2 < 2^31 bytes of x. Otherwise the K limit
+ * codes, group size 64, M >= 4 and K a multiple of 512 the product runs on
+ * the matrix cores and K is limited only by M*K*2 < 2^31 bytes of x. Otherwise the K limit
  * shrinks with M: K <= 16384 * c for 4-bit and 8192 * c for 8-bit, with
  * c = min(7, floor(8/M)) (larger K is AGQ_ENOTSUP).
  */
@@ -122,8 +122,8 @@ agq_status agq_qmv_wide(const void *x, const uint32_t *w, const void *scales, co
  * over the top-k slots is applied. P may be at most 4096. Index values are
  * device data and cannot be checked on the host. A pair whose lhs >= R or
  * rhs >= E gets an all-NaN output row, and no memory outside the arrays is
- * read. With 4-bit codes and K a multiple of 512 the gather runs on the
- * matrix cores, 16 pairs per pass, and K is limited only by R*K*2 < 2^31
+ * read. With 4-bit codes, group size 64 and K a multiple of 512 the gather
+ * runs on the matrix cores, 16 pairs per pass, and K is limited only by R*K*2 < 2^31
  * bytes of x; otherwise K limits are those of agq_qmv_wide at M = 8.
  */
 agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
@@ -141,8 +141,9 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
  * prefill) plans. It runs on the matrix cores with bfloat16 operands that
  * hold the codes exactly (128 + q for 4-bit, q for 8-bit) and applies each
  * group's scale and bias in fp32, so its error bound is that of the matvec
- * forms. M*K*2 must stay below 2^31 (else AGQ_ENOTSUP). Argument checks and
- * errors as for agq_qmv.
+ * forms. M*K*2 must stay below 2^31 (else AGQ_ENOTSUP). Beyond 8 rows it
+ * takes group size 64 (else AGQ_ENOTSUP). Argument checks and errors as for
+ * agq_qmv.
  */
 agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases, void *y,
                    int64_t M, int64_t N, int64_t K, int bits, int group_size, void *stream);
@@ -154,8 +155,8 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
  * result as agq_gather_qmv, for any number of pairs per expert: each plane
  * that some pair uses streams once per 64 of its pairs, with every tile of x
  * rows gathered through the pair's lhs index. P may be at most 4096; R*K*2
- * must stay below 2^31. Out-of-range indices give NaN rows, as in
- * agq_gather_qmv.
+ * must stay below 2^31; group size 64. Out-of-range indices give NaN rows, as
+ * in agq_gather_qmv.
  */
 agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y,
@@ -219,10 +220,32 @@ agq_status agq_moe_decode_noalloc(const void *x, const uint32_t *w_gate, const v
                                   int bits, int group_size, void *stream);
 
 /*
+ * Affine group quantizer on the device: the step before the products, which
+ * "MLX CUDA Cleanup Plan", Phase 5, moves off the host (repeated host-side
+ * quantization is one of the per-op overheads it lists), and which the
+ * quantized KV cache of "epic: CUDA (MLX backend) prefill and decode
+ * acceleration program", Phase 5 (#635), needs. Per row and group of
+ * group_size columns, in binary32:
+ *     scale = bf16((max - min) / (2^bits - 1)),  bias = bf16(min),
+ *     q = clamp(rint((w - bias) / scale), 0, 2^bits - 1)   (q = 0 where scale is 0)
+ * with correctly rounded division, rint to nearest even and the rounded scale
+ * and bias; codes packed low-first.
+ *   w       [rows, K] float (w_dtype AGQ_DTYPE_F32) or BF16 (AGQ_DTYPE_BF16)
+ *   codes   [rows, K*bits/32] U32 (written); scales, biases [rows, K/group_size] BF16 (written)
+ * bits 4 or 8; group_size 32, 64 or 128. Inputs must be finite. Errors as for
+ * agq_dequantize.
+ */
+#define AGQ_DTYPE_F32 0
+#define AGQ_DTYPE_BF16 1
+agq_status agq_quantize(const void *w, int w_dtype, uint32_t *codes, void *scales, void *biases, int64_t rows,
+                        int64_t K, int bits, int group_size, void *stream);
+
+/*
  * The dequantization step on its own, as a check of the unpack and affine map
  * of "MLX CUDA Cleanup Plan", Target Architecture §1 (U32-packed codes with
  * BF16 scales and biases), against which the products can be verified bit for
- * bit. Dequantize to fp32: out[n, k] = scale[n, k/64] * q[n, k] + bias[n, k/64],
+ * bit. Dequantize to fp32: out[n, k] = scale[n, k/gs] * q[n, k] + bias[n, k/gs]
+ * (gs = group_size: 32, 64 or 128),
  * formed with one fused multiply-add, so each output is the exact value
  * rounded once to binary32. The exact value is representable, and the result
  * therefore exact, unless the bias exceeds the scale by more than about 2^15

@@ -89,8 +89,9 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: qmv(K=96), EINVAL),
     (lambda: qmv(bits=3), ENOTSUP),
     (lambda: qmv(bits=2), ENOTSUP),
-    (lambda: qmv(gs=32), ENOTSUP),
-    (lambda: qmv(gs=128, K=128), ENOTSUP),
+    (lambda: qmv(gs=16), ENOTSUP),
+    (lambda: qmv(gs=256, K=256), ENOTSUP),
+    (lambda: qmv(gs=32, K=48), EINVAL),
     (lambda: qmv(gs=0), EINVAL),
     (lambda: qmv(x=A2), EINVAL),
     (lambda: qmv(w=A2), EINVAL),
@@ -119,7 +120,16 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: qmm(y=NUL), EINVAL),
     (lambda: qmm(K=96), EINVAL),
     (lambda: qmm(bits=2), ENOTSUP),
+    (lambda: qmm(gs=16, K=128), ENOTSUP),
     (lambda: qmm(gs=128, K=128), ENOTSUP),
+    (lambda: qmm(gs=32, K=128), ENOTSUP),
+    (lambda: gqmm(gs=32, K=128), ENOTSUP),
+    (lambda: moe(gs=32), ENOTSUP),
+    (lambda: lib.agq_quantize(A, 2, A, A, A, 4, 64, 4, 64, None), EINVAL),
+    (lambda: lib.agq_quantize(A, 0, A, A, A, 4, 64, 3, 64, None), ENOTSUP),
+    (lambda: lib.agq_quantize(A, 0, A, A, A, 4, 64, 4, 48, None), ENOTSUP),
+    (lambda: lib.agq_quantize(A2, 0, A, A, A, 4, 64, 4, 64, None), EINVAL),
+    (lambda: lib.agq_quantize(NUL, 0, A, A, A, 4, 64, 4, 64, None), EINVAL),
     (lambda: qmm(x=A2), EINVAL),
     (lambda: qmm(M=1 << 20, K=1024), ENOTSUP),
     (lambda: gqmm(P=0), EINVAL),
