@@ -56,8 +56,11 @@ def _bind(lib):
     lib.agqo_gather_qmv.argtypes = [P, I64, P, P, P, I64, I64, I64, I, I, P, P, I64, P, I64, P, P]
     lib.agqo_moe_swiglu.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, I, I, P, P]
     lib.agqo_quantize.argtypes = [P, I64, I64, I, I, P, P, P]
+    lib.agqo_qmv_fused.argtypes = [P, P, ctypes.c_double, P, P, P, I64, I64, I, I, P, I, P, P]
+    lib.agqo_bf16_round.argtypes = [ctypes.c_double]
+    lib.agqo_bf16_round.restype = ctypes.c_double
     for f in (lib.agqo_unpack, lib.agqo_dequantize, lib.agqo_qmv, lib.agqo_gather_qmv, lib.agqo_moe_swiglu,
-              lib.agqo_quantize):
+              lib.agqo_quantize, lib.agqo_qmv_fused):
         f.restype = I
     return lib
 
@@ -175,3 +178,26 @@ def quantize(w, bits: int, group_size: int = 64, lib=None):
     b = np.empty_like(s)
     _check(lib.agqo_quantize(_p(w), N, K, bits, group_size, _p(wq), _p(s), _p(b)))
     return wq, s, b
+
+
+ACT_NONE, ACT_SWIGLU, ACT_GEGLU = 0, 1, 2
+
+
+def qmv_fused(x, w, scales, biases, K: int, bits: int, group_size: int = 64, gamma=None, eps: float = 1e-5,
+              residual=None, act: int = ACT_NONE, lib=None):
+    """Batch-1 product with a fused RMS-norm prologue (``gamma``) and an epilogue (``residual``
+    add, or SwiGLU / GeGLU over row-interleaved gate/up pairs). -> (y float64, A float64)."""
+    lib = lib or load()
+    x = _c(x, np.uint16).reshape(K)
+    w = _c(w, np.uint32)
+    s = _c(scales, np.uint16)
+    b = _c(biases, np.uint16)
+    N = w.shape[0]
+    g = None if gamma is None else _c(gamma, np.uint16).reshape(K)
+    r = None if residual is None else _c(residual, np.uint16).reshape(N)
+    out = N if act == ACT_NONE else N // 2
+    y = np.empty(out, dtype=np.float64)
+    a = np.empty_like(y)
+    _check(lib.agqo_qmv_fused(_p(x), _p(g), float(eps), _p(w), _p(s), _p(b), N, K, bits, group_size, _p(r), act,
+                              _p(y), _p(a)))
+    return y, a

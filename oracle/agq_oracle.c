@@ -39,6 +39,15 @@
  * no formula; this is the plainest reading, in exact float64 with no
  * intermediate rounding.
  *
+ * The fused batch-1 projection (agqo_qmv_fused) adds the neighbouring stages
+ * that "MLX CUDA Cleanup Plan", Phase 5, lists for the device-resident decode
+ * layer: RMS norm before the product, residual add or a GLU (SwiGLU, GeGLU)
+ * after it, on projections that share one input (gate and up interleaved).
+ * The page names the stages only. Readings: RMS norm scales by
+ * 1/sqrt(mean(x^2) + eps) times a per-column weight and its output is a BF16
+ * activation (rounded to nearest even, as the layer's activations are BF16);
+ * gelu is the tanh form; silu(z) = z / (1 + e^-z).
+ *
  * Every function here is pinned by the CPU test suite to known-answer words,
  * closed forms, exact rational brute force and a float64 BLAS product.
  */
@@ -313,5 +322,98 @@ int agqo_quantize(const float *w, int64_t N, int64_t K, int bits, int group_size
             }
         }
     }
+    return AGQO_OK;
+}
+
+/* Nearest bfloat16 value to v (8 significant bits), ties to even; v finite and
+ * inside the normal range. */
+static double bf16_round(double v)
+{
+    if (v == 0.0) return v;
+    int e;
+    double m = frexp(v, &e); /* v = m * 2^e, 0.5 <= |m| < 1 */
+    double t = m * 256.0;    /* 8 significant bits above the point */
+    double r = floor(t);
+    double d = t - r;
+    if (d > 0.5 || (d == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    return ldexp(r, e - 8);
+}
+
+/* The rounding above, exported so the test suite can pin it on its own. */
+double agqo_bf16_round(double v)
+{
+    return bf16_round(v);
+}
+
+/* gelu through tanh: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))). */
+static double gelu_tanh(double z)
+{
+    return 0.5 * z * (1.0 + tanh(0.7978845608028654 * (z + 0.044715 * z * z * z)));
+}
+
+/* Batch-1 projection with the decode layer's neighbouring stages fused in:
+ *  - prologue (gamma != NULL): RMS norm of x, x_n[k] = bf16(x[k] * r * gamma[k])
+ *    with r = 1 / sqrt(sum_k x[k]^2 / K + eps), the normalized activation
+ *    rounded to bfloat16, the layer's activation type;
+ *  - the product v[n] = sum_k x_n[k] * w[n, k];
+ *  - epilogue act 0: y[n] = v[n] (+ residual[n] when residual != NULL);
+ *    act 1 (SwiGLU) and act 2 (GeGLU, gelu in its tanh form): rows come in
+ *    interleaved gate/up pairs, y[j] = act(v[2j]) * v[2j + 1], N/2 outputs.
+ * a[] is the scale of the rounding tolerance: sum_k |x_n[k] w[n, k]| for
+ * act 0, and 1.13 |v[2j+1]| A[2j] + |act(v[2j])| A[2j+1] for the GLU forms
+ * (1.13 bounds the slope of both activations). */
+int agqo_qmv_fused(const uint16_t *x, const uint16_t *gamma, double eps,
+                   const uint32_t *w, const uint16_t *scales, const uint16_t *biases,
+                   int64_t N, int64_t K, int bits, int group_size,
+                   const uint16_t *residual, int act, double *y, double *a)
+{
+    if (!x || !w || !scales || !biases || !y || !a || N <= 0) return AGQO_EARG;
+    if (check_format(K, bits, group_size)) return AGQO_EARG;
+    if (act < 0 || act > 2 || (act > 0 && (N % 2 != 0 || residual))) return AGQO_EARG;
+    double *xn = (double *)malloc((size_t)K * sizeof(double));
+    double *v = (double *)malloc((size_t)N * sizeof(double));
+    double *m = (double *)malloc((size_t)N * sizeof(double));
+    if (!xn || !v || !m) {
+        free(xn);
+        free(v);
+        free(m);
+        return AGQO_EARG;
+    }
+    double r = 1.0;
+    if (gamma) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) ss += bf16_value(x[k]) * bf16_value(x[k]);
+        r = 1.0 / sqrt(ss / (double)K + eps);
+    }
+    for (int64_t k = 0; k < K; ++k)
+        xn[k] = gamma ? bf16_round(bf16_value(x[k]) * r * bf16_value(gamma[k])) : bf16_value(x[k]);
+    const int64_t words = K * bits / 32, groups = K / group_size;
+    for (int64_t n = 0; n < N; ++n) {
+        double sum = 0.0, abs_sum = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double t = xn[k] * weight_at(w + n * words, scales + n * groups, biases + n * groups, k, bits,
+                                               group_size);
+            sum += t;
+            abs_sum += fabs(t);
+        }
+        v[n] = sum;
+        m[n] = abs_sum;
+    }
+    if (act == 0) {
+        for (int64_t n = 0; n < N; ++n) {
+            y[n] = v[n] + (residual ? bf16_value(residual[n]) : 0.0);
+            a[n] = m[n];
+        }
+    } else {
+        for (int64_t j = 0; j < N / 2; ++j) {
+            const double g = v[2 * j], u = v[2 * j + 1];
+            const double f = act == 1 ? silu(g) : gelu_tanh(g);
+            y[j] = f * u;
+            a[j] = 1.13 * fabs(u) * m[2 * j] + fabs(f) * m[2 * j + 1];
+        }
+    }
+    free(xn);
+    free(v);
+    free(m);
     return AGQO_OK;
 }

@@ -450,4 +450,109 @@ def pin_quantize_codes_are_nearest(lib):
             assert outside.any()  # the case needs clamping
 
 
+def pin_bf16_round_known_values(lib):
+    """Ties go to the even neighbour, everything else to the nearest: 1 + 2^-8 -> 1,
+    1 + 3*2^-8 -> 1 + 2^-6, 1 + 2^-8 + 2^-20 -> 1 + 2^-7, and the mirror images; on
+    doubles that are binary32 values the result is the bf16 RNE of that binary32 value."""
+    f = lib.agqo_bf16_round
+    for v, want in ((1 + 2 ** -8, 1.0), (1 + 3 * 2 ** -8, 1 + 2 ** -6), (1 + 2 ** -8 + 2 ** -20, 1 + 2 ** -7),
+                    (3.0, 3.0), (0.0, 0.0), (2 ** -130 * 1.5, 2 ** -130 * 1.5)):
+        assert f(v) == want and f(-v) == -want, (v, f(v), want)
+    vals = np.random.default_rng(90).standard_normal(2000).astype(np.float32)
+    want = bf16_to_f32(bf16_bits(vals)).astype(np.float64)
+    assert all(f(float(v)) == w for v, w in zip(vals, want))
+
+
+def _fused_problem(seed, N, K, bits=4):
+    g = np.random.default_rng([91, seed])
+    q = g.integers(0, 2 ** bits, size=(N, K), dtype=np.uint8)
+    sc = bf16_bits((0.01 + 0.02 * g.random((N, K // 64))).astype(np.float32))
+    bi = bf16_bits((-0.05 + 0.03 * g.standard_normal((N, K // 64))).astype(np.float32))
+    return q, sc, bi, g
+
+
+def pin_fused_reduces_to_qmv(lib):
+    """Without a norm and with no epilogue the fused projection is the plain product."""
+    q, sc, bi, g = _fused_problem(1, 9, 192)
+    x = bf16_bits(g.standard_normal((1, 192)).astype(np.float32))
+    w = pack_codes(q, 4)
+    y, a = oracle.qmv_fused(x, w, sc, bi, 192, 4, lib=lib)
+    y0, a0 = oracle.qmv(x, w, sc, bi, 192, 4, lib=lib)
+    assert np.array_equal(y, y0[0]) and np.array_equal(a, a0[0])
+
+
+def pin_fused_norm_closed_forms(lib):
+    """x of constant magnitude c with eps = 0 normalizes to the sign vector exactly; a norm
+    weight of 2 doubles the product exactly; scaling x by a power of two changes nothing;
+    a zero norm weight gives zero; with identity-like weights (8-bit, scale 1, bias 0, one
+    code 1 per row) every output is one normalized activation, hence a bf16 value."""
+    K, N = 256, 7
+    q, sc, bi, g = _fused_problem(2, N, K)
+    w = pack_codes(q, 4)
+    sign = np.where(g.random(K) < 0.5, -1.0, 1.0)
+    x = bf16_bits((0.09375 * sign).astype(np.float32))[None]
+    ones = np.full(K, 0x3F80, np.uint16)
+    y, _ = oracle.qmv_fused(x, w, sc, bi, K, 4, gamma=ones, eps=0.0, lib=lib)
+    ys, _ = oracle.qmv(bf16_bits(sign.astype(np.float32))[None], w, sc, bi, K, 4, lib=lib)
+    assert np.array_equal(y, ys[0])
+    xr = bf16_bits(g.standard_normal(K).astype(np.float32))[None]
+    gam = bf16_bits((0.5 + g.random(K)).astype(np.float32))
+    y1, _ = oracle.qmv_fused(xr, w, sc, bi, K, 4, gamma=gam, eps=0.0, lib=lib)
+    y8, _ = oracle.qmv_fused(bf16_bits(8 * bf16_to_f32(xr)), w, sc, bi, K, 4, gamma=gam, eps=0.0, lib=lib)
+    assert np.array_equal(y1, y8)
+    yo, _ = oracle.qmv_fused(xr, w, sc, bi, K, 4, gamma=ones, eps=1e-3, lib=lib)
+    y2, _ = oracle.qmv_fused(xr, w, sc, bi, K, 4, gamma=np.full(K, 0x4000, np.uint16), eps=1e-3, lib=lib)
+    assert np.array_equal(y2, 2 * yo)
+    yz, _ = oracle.qmv_fused(xr, w, sc, bi, K, 4, gamma=np.zeros(K, np.uint16), lib=lib)
+    assert not yz.any()
+    eye = np.zeros((64, 64), np.uint8)
+    eye[np.arange(64), np.arange(64)] = 1
+    yi, _ = oracle.qmv_fused(xr[:, :64], pack_codes(eye, 8), np.full((64, 1), 0x3F80, np.uint16),
+                             np.zeros((64, 1), np.uint16), 64, 8, gamma=gam[:64], eps=0.5, lib=lib)
+    assert np.array_equal(yi, bf16_to_f32(bf16_bits(yi.astype(np.float32))).astype(np.float64))
+    assert np.array_equal(yi.astype(np.float32).astype(np.float64), yi)
+
+
+def pin_fused_residual(lib):
+    q, sc, bi, g = _fused_problem(3, 11, 128)
+    w = pack_codes(q, 4)
+    x = bf16_bits(g.standard_normal((1, 128)).astype(np.float32))
+    res = bf16_bits(g.standard_normal(11).astype(np.float32))
+    y0, _ = oracle.qmv_fused(x, w, sc, bi, 128, 4, lib=lib)
+    y1, _ = oracle.qmv_fused(x, w, sc, bi, 128, 4, residual=res, lib=lib)
+    assert np.all(np.abs((y1 - y0) - bf16_to_f32(res)) <= 4e-16 * (np.abs(y1) + 1))
+
+
+def pin_fused_glu_odd_part(lib):
+    """Gate rows g and -g (bf16 sign flips) with the same up row: the outputs differ by
+    exactly g * u for SwiGLU and GeGLU alike (both activations have odd part z / 2)."""
+    K = 192
+    q, sc, bi, g = _fused_problem(4, 2, K)  # row 0: gate, row 1: up
+    x = bf16_bits(g.standard_normal((1, K)).astype(np.float32))
+    plain, _ = oracle.qmv(x, pack_codes(q, 4), sc, bi, K, 4, lib=lib)
+    gv, uv = plain[0]
+    q4 = np.stack([q[0], q[1], q[0], q[1]])
+    sc4 = np.stack([sc[0], sc[1], sc[0] ^ np.uint16(0x8000), sc[1]])
+    bi4 = np.stack([bi[0], bi[1], bi[0] ^ np.uint16(0x8000), bi[1]])
+    for act in (oracle.ACT_SWIGLU, oracle.ACT_GEGLU):
+        y, a = oracle.qmv_fused(x, pack_codes(q4, 4), sc4, bi4, K, 4, act=act, lib=lib)
+        assert abs((y[0] - y[1]) - gv * uv) <= 1e-13 * (abs(y[0]) + abs(y[1])), (act, y, gv * uv)
+
+
+def pin_fused_glu_values(lib):
+    """Gate rows of constant weight w_g against x of 64 ones give gate value 64*w_g: at 64
+    both activations return 64, at -64 about 0, at 1 silu(1) = e/(1 + e) = 0.7310585786300049
+    and the tanh form of gelu 0.5*(1 + tanh(sqrt(2/pi)*1.044715)) = 0.8411919906082768.
+    The up row has constant weight 1/2 (up value 32)."""
+    K = 64
+    x = np.full((1, K), 0x3F80, np.uint16)
+    zero = np.zeros((2, 1), np.uint16)
+    for gate_bias, want in ((0x3F80, {1: 64.0, 2: 64.0}), (0xBF80, {1: 0.0, 2: 0.0}),
+                            (0x3C80, {1: 0.7310585786300049, 2: 0.8411919906082768})):
+        b = np.array([[gate_bias], [0x3F00]], np.uint16)
+        for act in (1, 2):
+            y, _ = oracle.qmv_fused(x, np.zeros((2, K // 8), np.uint32), zero, b, K, 4, act=act, lib=lib)
+            assert abs(y[0] - 32.0 * want[act]) <= 1e-12 * 32.0, (hex(gate_bias), act, y[0])
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -52,6 +52,19 @@ MUTANTS = {
     "quant_no_clamp": ("q = r <= 0.0f ? 0u : r >= levels ? (uint32_t)levels : (uint32_t)r;",
                        "q = (uint32_t)r & ((1u << bits) - 1u);"),
     "quant_bf16_truncates": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "return (uint16_t)(u >> 16);"),
+    "fused_sum_not_mean": ("r = 1.0 / sqrt(ss / (double)K + eps);", "r = 1.0 / sqrt(ss + eps);"),
+    "fused_gamma_ignored": ("xn[k] = gamma ? bf16_round(bf16_value(x[k]) * r * bf16_value(gamma[k])) : bf16_value(x[k]);",
+                            "xn[k] = gamma ? bf16_round(bf16_value(x[k]) * r) : bf16_value(x[k]);"),
+    "fused_norm_not_rounded": ("xn[k] = gamma ? bf16_round(bf16_value(x[k]) * r * bf16_value(gamma[k])) : bf16_value(x[k]);",
+                               "xn[k] = gamma ? bf16_value(x[k]) * r * bf16_value(gamma[k]) : bf16_value(x[k]);"),
+    "fused_round_truncates": ("if (d > 0.5 || (d == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;", "if (d > 1.0) r += 1.0;"),
+    "fused_ties_away": ("if (d > 0.5 || (d == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;", "if (d >= 0.5) r += 1.0;"),
+    "fused_glu_swapped": ("const double g = v[2 * j], u = v[2 * j + 1];", "const double u = v[2 * j], g = v[2 * j + 1];"),
+    "fused_acts_swapped": ("const double f = act == 1 ? silu(g) : gelu_tanh(g);",
+                           "const double f = act == 2 ? silu(g) : gelu_tanh(g);"),
+    "fused_gelu_cubic": ("(z + 0.044715 * z * z * z)", "(z + 0.044715 * z * z)"),
+    "fused_magnitude_signed": ("abs_sum += fabs(t);", "abs_sum += t;"),
+    "fused_residual_dropped": ("y[n] = v[n] + (residual ? bf16_value(residual[n]) : 0.0);", "y[n] = v[n];"),
     "moe_up_with_gate_scales": ("row_dot(x + t * H, wu + row * hw, su + row * hg,",
                                 "row_dot(x + t * H, wu + row * hw, sg + row * hg,"),
 }
