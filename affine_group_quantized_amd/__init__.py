@@ -18,7 +18,7 @@ import os
 
 import torch
 
-__all__ = ["qmv", "qmv_wide", "gather_qmv", "qmm", "gather_qmm", "moe_decode", "moe_decode_workspace", "quantize",
+__all__ = ["qmv", "qmv_wide", "qmv_fused", "ACT_NONE", "ACT_SWIGLU", "ACT_GEGLU", "gather_qmv", "qmm", "gather_qmm", "moe_decode", "moe_decode_workspace", "quantize",
            "dequantize", "plan", "launch_plan", "prepare_qmv", "AgqError",
            "LIB_PATH", "lib"]
 
@@ -60,6 +60,7 @@ def _load(path: str = LIB_PATH):
     lib.agq_last_error.restype = ctypes.c_char_p
     lib.agq_qmv.argtypes = [P, P, P, P, P, I64, I64, I, I, P]
     lib.agq_qmv_wide.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
+    lib.agq_qmv_fused.argtypes = [P, P, ctypes.c_float, P, P, P, P, I, P, I64, I64, I, I, P]
     lib.agq_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.agq_qmm.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
     lib.agq_gather_qmm.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
@@ -72,7 +73,7 @@ def _load(path: str = LIB_PATH):
     lib.agq_dequantize.argtypes = [P, P, P, P, I64, I64, I, I, P]
     lib.agq_plan_product.argtypes = [I64, I64, I64, I, I, I, I, I64, ctypes.POINTER(Plan)]
     lib.agq_plan_launch.argtypes = [I64, I64, I64, I, I, I64, ctypes.POINTER(Plan)]
-    for f in (lib.agq_qmv, lib.agq_qmv_wide, lib.agq_gather_qmv, lib.agq_qmm, lib.agq_gather_qmm, lib.agq_dequantize,
+    for f in (lib.agq_qmv, lib.agq_qmv_wide, lib.agq_qmv_fused, lib.agq_gather_qmv, lib.agq_qmm, lib.agq_gather_qmm, lib.agq_dequantize,
               lib.agq_plan_product, lib.agq_plan_launch):
         f.restype = I
     return lib
@@ -142,6 +143,45 @@ def qmv(x, w, scales, biases, bits: int = 4, group_size: int = 64, out=None):
     with torch.cuda.device(device):
         _check(lib.agq_qmv(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(out), N, K, bits, group_size,
                            _stream(device)))
+    return out
+
+
+ACT_NONE, ACT_SWIGLU, ACT_GEGLU = 0, 1, 2
+
+
+def qmv_fused(x, w, scales, biases, bits: int = 4, group_size: int = 64, norm_weight=None, eps: float = 1e-5,
+              residual=None, act: int = ACT_NONE, out=None):
+    """Batch-1 product with an RMS-norm prologue and a residual or GLU epilogue.
+
+    ``x`` [K] bf16; ``norm_weight`` [K] bf16 or None (no norm); ``residual`` [N]
+    bf16 or None (act 0 only; may be ``out`` itself). act 0 returns [N]; acts 1
+    (SwiGLU) and 2 (GeGLU) take gate and up rows interleaved in ``w`` and
+    return [N/2].
+    """
+    device = x.device
+    _need(x, "x", _BF16, device)
+    K = x.shape[-1]
+    if x.numel() != K:
+        raise ValueError("qmv_fused takes a single activation row")
+    (N,) = _weights(w, scales, biases, K, bits, group_size, device, 1)
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", _BF16, device)
+        if norm_weight.numel() != K:
+            raise ValueError("norm_weight must have K elements")
+    if residual is not None:
+        _need(residual, "residual", _BF16, device)
+        if residual.numel() != N:
+            raise ValueError("residual must have N elements")
+    n_out = N if act == ACT_NONE else N // 2
+    if out is None:
+        out = torch.empty((n_out,), dtype=torch.bfloat16, device=device)
+    else:
+        _need(out, "out", _BF16, device)
+        if out.numel() != n_out:
+            raise ValueError("out has the wrong size")
+    with torch.cuda.device(device):
+        _check(lib.agq_qmv_fused(_ptr(x), _ptr(norm_weight), float(eps), _ptr(w), _ptr(scales), _ptr(biases),
+                                 _ptr(residual), act, _ptr(out), N, K, bits, group_size, _stream(device)))
     return out
 
 

@@ -366,6 +366,47 @@ agq_status agq_qmv_wide(const void *x, const uint32_t *w, const void *scales, co
     return dense_product(x, w, scales, biases, y, M, N, K, bits, group_size, stream);
 }
 
+agq_status agq_qmv_fused(const void *x, const void *norm_weight, float eps, const uint32_t *w, const void *scales,
+                         const void *biases, const void *residual, int act, void *y, int64_t N, int64_t K, int bits,
+                         int group_size, void *stream) {
+    agq_status st = check_operands(x, w, scales, biases, y, N, K, bits, group_size, true);
+    if (st != AGQ_OK) return st;
+    if (act < AGQ_ACT_NONE || act > AGQ_ACT_GEGLU) return fail(AGQ_EINVAL, "act=%d is not 0, 1 or 2", act);
+    if (act != AGQ_ACT_NONE && (N % 2 != 0 || residual))
+        return fail(AGQ_EINVAL, "a gated epilogue needs an even N (interleaved gate and up rows) and no residual");
+    if (!(eps >= 0.f) || eps > 3.0e38f) return fail(AGQ_EINVAL, "eps must be finite and >= 0");
+    if (misaligned(norm_weight, 16)) return fail(AGQ_EINVAL, "norm_weight must be 16-byte aligned");
+    if (misaligned(residual, 2)) return fail(AGQ_EINVAL, "residual must be 2-byte aligned");
+    if (N >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "N=%lld too large for the fused projection", (long long)N);
+    const bool glu = act != AGQ_ACT_NONE;
+    agq::Plan plan;
+    if (agq::plan_fused_shape(K, bits, glu, &plan) != AGQ_OK)  // host-only check before any HIP call
+        return fail(AGQ_ENOTSUP, "K=%lld too large for the fused projection at %d bits", (long long)K, bits);
+    int cus = 0, dev = 0;
+    st = current_device(&cus, &dev);
+    if (st != AGQ_OK) return st;
+    const void *sym = nullptr;
+    for (int pass = 0; pass < 2; ++pass) {
+        sym = agq::fused_kernel(bits, plan.cpt, plan.R, plan.NB, plan.x_lds_bytes > 0 ? plan.S : 0, act);
+        if (!sym) return fail(AGQ_ENOTSUP, "no fused kernel for bits=%d cpt=%d R=%d", bits, plan.cpt, plan.R);
+        int64_t waves = 0;
+        st = resident_waves(sym, plan.threads, (size_t)plan.x_lds_bytes, cus, dev, &waves);
+        if (st != AGQ_OK) return st;
+        if (pass == 0 && agq::wants_deep(N, waves, plan.S, 0)) {
+            agq::plan_fused_shape(K, bits, glu, &plan, true);
+            continue;
+        }
+        agq::plan_grid(N, waves, 0, &plan);
+        break;
+    }
+    agq::FusedArgs f{};
+    f.p = make_args(x, w, scales, biases, y, N, K, bits, 1, plan, group_size);
+    f.gamma = static_cast<const uint16_t *>(norm_weight);
+    f.res = static_cast<const uint16_t *>(residual);
+    f.eps = eps;
+    return launch(sym, dim3((unsigned)plan.blocks), dim3(plan.threads), (size_t)plan.x_lds_bytes, &f, stream);
+}
+
 agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y, int64_t P, int64_t R,
                           int64_t E, int64_t N, int64_t K, int bits, int group_size, void *stream) {

@@ -22,6 +22,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Both bfloat16 values of a pair times rs and times the matching norm weight,
+// each product rounded once to bfloat16: (x * rs) * g in fp32, then to nearest even.
+__device__ __forceinline__ uint32_t norm_pair(uint32_t x, uint32_t g, float rs) {
+    const float lo = bf16_lo(x) * rs * bf16_lo(g);
+    const float hi = bf16_hi(x) * rs * bf16_hi(g);
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
 // c + a.lo*b.lo + a.hi*b.hi on bfloat16 pairs (v_dot2c_f32_bf16), fp32 accumulate.
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,

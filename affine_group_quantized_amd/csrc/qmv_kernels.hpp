@@ -30,6 +30,17 @@ struct ProductArgs {
     int32_t pad_;
 };
 
+// Argument block of the fused batch-1 projection: the product's arguments
+// (one activation row) plus the norm weights (NULL: no norm), the norm's
+// epsilon and the residual rows (NULL: none).
+struct FusedArgs {
+    ProductArgs p;
+    const uint16_t *gamma;  // bf16 [K] or NULL
+    const uint16_t *res;    // bf16 [N] or NULL (act 0 only)
+    float eps;
+    int32_t pad_[3];
+};
+
 // Argument block of the matrix-core kernels (4-bit codes, K a multiple of
 // 512): bands of 16*T weight rows, S waves per block splitting K into slices
 // of SPW 128-column segments, each block walking BPG bands round-robin.
@@ -66,5 +77,9 @@ const void *quantize_kernel_for(int bits, bool bf16_in);
 // loads for passes of 9-16 rows (launched with one grid row per pass of 16).
 // The gather chooses its form per pass.
 const void *mfma_kernel(int tiles, bool gather, int rows);
+// Fused batch-1 projection kernel for (bits, chunks per lane, rows per
+// iteration, ring stages, K segments of the block's LDS copy of x (0: none),
+// epilogue: 0 plain or residual, 1 SwiGLU, 2 GeGLU), or NULL.
+const void *fused_kernel(int bits, int cpt, int R, int NB, int xs, int act);
 
 }  // namespace agq

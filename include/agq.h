@@ -149,6 +149,35 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
                    int64_t M, int64_t N, int64_t K, int bits, int group_size, void *stream);
 
 /*
+ * Fused batch-1 projection: the decode layer's neighbouring stages that "MLX
+ * CUDA Cleanup Plan", Phase 5, moves onto the device (RMS norm, residual add,
+ * GeGLU; projections that share an input concatenated: q/k/v, gate/up),
+ * folded into one agq_qmv launch:
+ *     x_n[k] = bf16(x[k] * rs * norm_weight[k]),  rs = 1 / sqrt(sum_k x[k]^2 / K + eps)
+ *              (when norm_weight != NULL; else x_n = x)
+ *     v[n]   = sum_k x_n[k] * (s[n, k/gs] * q[n, k] + b[n, k/gs])
+ *   act 0: y[n] = v[n] + residual[n] (residual may be NULL),   y [N] BF16
+ *   act 1: y[j] = silu(v[2j]) * v[2j + 1],  silu(z) = z / (1 + exp(-z)),   y [N/2] BF16
+ *   act 2: y[j] = gelu(v[2j]) * v[2j + 1],  gelu in its tanh form,         y [N/2] BF16
+ * For acts 1 and 2 the gate and up projections are concatenated with their
+ * rows interleaved (row 2j of w is gate row j, row 2j + 1 up row j), N even,
+ * and residual must be NULL. x [K], norm_weight [K] and residual [N] are BF16;
+ * w, scales and biases as for agq_qmv. The normalized activation is rounded to
+ * BF16 (the layer's activation type) before the product; rs and the products
+ * are fp32. residual may be the same buffer as y (an in-place residual add);
+ * no other overlap of y with an input is allowed. One kernel launch on
+ * `stream`. Supports bits 4 and 8, group sizes 32, 64 and 128, K up to 65536
+ * (4-bit) or 32768 (8-bit), N below 2^31; else AGQ_ENOTSUP. eps must be
+ * finite and >= 0. Argument checks and errors as for agq_qmv.
+ */
+#define AGQ_ACT_NONE 0
+#define AGQ_ACT_SWIGLU 1
+#define AGQ_ACT_GEGLU 2
+agq_status agq_qmv_fused(const void *x, const void *norm_weight, float eps, const uint32_t *w,
+                         const void *scales, const void *biases, const void *residual, int act,
+                         void *y, int64_t N, int64_t K, int bits, int group_size, void *stream);
+
+/*
  * Expert-gathered matrix-matrix product (MoE prefill, the gather_qmm of the
  * same epic: its Diagnosis (baseline) MoE prefill row is the largest measured
  * gap on those pages, and Phase 3 (#629) targets it). Same arguments and

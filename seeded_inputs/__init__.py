@@ -42,7 +42,7 @@ CHUNK_ROWS = 1024
 __all__ = [
     "GROUP_SIZE", "CHUNK_ROWS", "stream", "bf16_bits", "bf16_to_f32",
     "pack_codes", "quantize_rows", "draw_activations", "draw_quantized_weight",
-    "random_codes", "workload", "WORKLOADS", "moe_expert_ids", "moe_prefill", "moe_layer",
+    "random_codes", "workload", "WORKLOADS", "moe_expert_ids", "moe_prefill", "moe_layer", "decode_layer",
 ]
 
 
@@ -216,6 +216,20 @@ def moe_prefill(tokens: int = 512) -> dict:
     return {"x": draw_activations(5, 0, tokens, m["hidden"]), "ids": ids,
             "rhs": ids.reshape(-1).astype(np.uint32),
             "lhs": np.repeat(np.arange(tokens, dtype=np.uint32), m["top_k"])}
+
+
+def decode_layer() -> dict:
+    """The non-weight tensors of a Llama-shaped decode layer around workload 1's
+    projections (stream cfg 6): RMS-norm weights ``gamma_attn``, ``gamma_mlp`` and
+    ``gamma_final`` [4096] drawn as 1 + 0.1 * N(0, 1) (t = 0, 1, 2) and a residual
+    stream ``h`` [4096] ~ N(0, 1) (t = 3), all bf16, and ``eps`` = 1e-5. The
+    gate/up weight of workload 1 (28672 rows) is read as 14336 interleaved gate
+    and up row pairs."""
+    out = {"eps": 1e-5}
+    for t, name in enumerate(("gamma_attn", "gamma_mlp", "gamma_final")):
+        out[name] = bf16_bits(np.float32(1) + np.float32(0.1) * stream(6, t).standard_normal(4096, dtype=np.float32))
+    out["h"] = draw_activations(6, 3, 1, 4096)[0]
+    return out
 
 
 def workload(cfg: int, only=None, keep_codes: bool = False) -> dict:

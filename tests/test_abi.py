@@ -75,6 +75,10 @@ def moe(T=4, k=2, E=4, H=512, F=1024, bits=4, gs=64, x=A, ws=A, wsb=1 << 30, ex=
     return lib.agq_moe_decode(x, A, A, A, A, A, A, A, A, A, ex, A, A, ws, wsb, T, k, E, H, F, bits, gs, None)
 
 
+def fused(act=0, g=A, eps=1e-5, res=NUL, N=16, K=64, bits=4, gs=64, x=A, y=A):
+    return lib.agq_qmv_fused(x, g, eps, A, A, A, res, act, y, N, K, bits, gs, None)
+
+
 def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     return lib.agq_gather_qmm(x, A, A, A, lhs, rhs, A, P, R, E, N, K, bits, gs, None)
 
@@ -132,6 +136,21 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: lib.agq_quantize(NUL, 0, A, A, A, 4, 64, 4, 64, None), EINVAL),
     (lambda: qmm(x=A2), EINVAL),
     (lambda: qmm(M=1 << 20, K=1024), ENOTSUP),
+    (lambda: fused(act=3), EINVAL),
+    (lambda: fused(act=-1), EINVAL),
+    (lambda: fused(act=1, N=15), EINVAL),
+    (lambda: fused(act=2, res=A), EINVAL),
+    (lambda: fused(eps=-1.0), EINVAL),
+    (lambda: fused(eps=float("nan")), EINVAL),
+    (lambda: fused(eps=float("inf")), EINVAL),
+    (lambda: fused(g=A2), EINVAL),
+    (lambda: fused(res=ctypes.c_void_p(0x10001)), EINVAL),
+    (lambda: fused(x=NUL), EINVAL),
+    (lambda: fused(y=NUL), EINVAL),
+    (lambda: fused(bits=2), ENOTSUP),
+    (lambda: fused(K=65536 + 64), ENOTSUP),
+    (lambda: fused(K=32768 + 64, bits=8), ENOTSUP),
+    (lambda: fused(N=1 << 31), ENOTSUP),
     (lambda: gqmm(P=0), EINVAL),
     (lambda: gqmm(lhs=NUL, R=3), EINVAL),
     (lambda: gqmm(rhs=NUL, E=3), EINVAL),
