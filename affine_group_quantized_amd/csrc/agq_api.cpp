@@ -378,22 +378,27 @@ agq_status agq_qmv_fused(const void *x, const void *norm_weight, float eps, cons
     if (misaligned(norm_weight, 16)) return fail(AGQ_EINVAL, "norm_weight must be 16-byte aligned");
     if (misaligned(residual, 2)) return fail(AGQ_EINVAL, "residual must be 2-byte aligned");
     if (N >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "N=%lld too large for the fused projection", (long long)N);
+    // No stage to fuse: the plain batch-1 product.
+    if (!norm_weight && !residual && act == AGQ_ACT_NONE)
+        return dense_product(x, w, scales, biases, y, 1, N, K, bits, group_size, stream);
     const bool glu = act != AGQ_ACT_NONE;
+    const bool norm = norm_weight != nullptr;
+    const int epi = glu ? act : residual ? 0 : 3;
     agq::Plan plan;
-    if (agq::plan_fused_shape(K, bits, glu, &plan) != AGQ_OK)  // host-only check before any HIP call
+    if (agq::plan_fused_shape(K, bits, &plan) != AGQ_OK)  // host-only check before any HIP call
         return fail(AGQ_ENOTSUP, "K=%lld too large for the fused projection at %d bits", (long long)K, bits);
     int cus = 0, dev = 0;
     st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
     const void *sym = nullptr;
     for (int pass = 0; pass < 2; ++pass) {
-        sym = agq::fused_kernel(bits, plan.cpt, plan.R, plan.NB, plan.x_lds_bytes > 0 ? plan.S : 0, act);
+        sym = agq::fused_kernel(bits, plan.cpt, plan.R, plan.NB, plan.x_lds_bytes > 0 ? plan.S : 0, epi, norm);
         if (!sym) return fail(AGQ_ENOTSUP, "no fused kernel for bits=%d cpt=%d R=%d", bits, plan.cpt, plan.R);
         int64_t waves = 0;
         st = resident_waves(sym, plan.threads, (size_t)plan.x_lds_bytes, cus, dev, &waves);
         if (st != AGQ_OK) return st;
         if (pass == 0 && agq::wants_deep(N, waves, plan.S, 0)) {
-            agq::plan_fused_shape(K, bits, glu, &plan, true);
+            agq::plan_fused_shape(K, bits, &plan, true);
             continue;
         }
         agq::plan_grid(N, waves, 0, &plan);
@@ -404,6 +409,7 @@ agq_status agq_qmv_fused(const void *x, const void *norm_weight, float eps, cons
     f.gamma = static_cast<const uint16_t *>(norm_weight);
     f.res = static_cast<const uint16_t *>(residual);
     f.eps = eps;
+    f.inv_k = 1.f / (float)K;
     return launch(sym, dim3((unsigned)plan.blocks), dim3(plan.threads), (size_t)plan.x_lds_bytes, &f, stream);
 }
 

@@ -169,21 +169,25 @@ inline bool wants_deep(int64_t N, int64_t resident_waves, int S, int64_t experts
     return N >= (int64_t)kDeepRows * groups;
 }
 
-// The fused batch-1 projection uses the one-row plan, except that a gated
-// epilogue takes at least two rows per iteration, so that the gate and up rows
-// of a pair (rows 2j and 2j + 1) meet in one iteration. Plans of more than 4
-// chunks per lane (rows longer than 8 waves of 4) are not instantiated.
+// The fused batch-1 projection uses the one-row plan, except that the deep
+// plan also shares the block's LDS copy of x where the shallow one would (the
+// norm is applied while the block fills it, with far fewer registers than
+// normalizing per wave). A gated epilogue pairs gate row 2j with up row 2j + 1:
+// in one iteration when it reads two or more rows, else in consecutive
+// iterations of a walk over row pairs (the ring holds both). Plans of more
+// than 4 chunks per lane (rows longer than 8 waves of 4) are not instantiated.
 constexpr int kFusedMaxCpt = 4;
-constexpr int fused_rows(int cpt, bool deep, bool glu) {
-    return glu && plan_rows(cpt, 1, deep) < 2 ? 2 : plan_rows(cpt, 1, deep);
-}
 
-inline agq_status plan_fused_shape(int64_t K, int bits, bool glu, Plan *p, bool deep = false) {
+inline agq_status plan_fused_shape(int64_t K, int bits, Plan *p, bool deep = false) {
     Plan q;
     agq_status st = plan_shape(1, K, bits, 0, &q, deep);
     if (st != AGQ_OK) return st;
     if (q.cpt > kFusedMaxCpt) return AGQ_ENOTSUP;
-    q.R = fused_rows(q.cpt, deep, glu);
+    if (deep) {
+        Plan sh;
+        plan_shape(1, K, bits, 0, &sh, false);
+        q.x_lds_bytes = sh.x_lds_bytes;  // same S and chunks per lane as the deep plan
+    }
     *p = q;
     return AGQ_OK;
 }

@@ -179,12 +179,12 @@ __device__ __forceinline__ void store_x(int C, const u32x4 (&xr)[XFill<BITS, MW,
 }
 
 // The norm weights matching the raw words fetch_x loads (zeros where it loads
-// padding, and everywhere when gamma is NULL: empty descriptor).
+// padding).
 template <int BITS, int MW, int CPT, int XS, int FT>
 __device__ __forceinline__ void fetch_gamma(const uint16_t *gamma, int K, int C,
                                             u32x4 (&gr)[XFill<BITS, MW, CPT, XS, FT>::PER]) {
     using F = XFill<BITS, MW, CPT, XS, FT>;
-    const __amdgpu_buffer_rsrc_t rs = byte_range(gamma, gamma ? (uint32_t)K * 2u : 0u);
+    const __amdgpu_buffer_rsrc_t rs = byte_range(gamma, (uint32_t)K * 2u);
     const int per = (F::WORDS + (int)blockDim.x - 1) / (int)blockDim.x;
 #pragma unroll
     for (int k = 0; k < F::PER; ++k) {
@@ -203,7 +203,7 @@ __device__ __forceinline__ void fetch_gamma(const uint16_t *gamma, int K, int C,
 // sum of squares (wave sums, then the waves' sums in order through LDS `part`,
 // at one block barrier), then x_n = bf16(x * rs * gamma) word by word.
 template <int BITS, int MW, int CPT, int XS, int FT>
-__device__ __forceinline__ void rms_norm_fill(int C, int K, float eps, float *part,
+__device__ __forceinline__ void rms_norm_fill(int C, float inv_k, float eps, float *part,
                                               u32x4 (&xr)[XFill<BITS, MW, CPT, XS, FT>::PER],
                                               const u32x4 (&gr)[XFill<BITS, MW, CPT, XS, FT>::PER]) {
     using F = XFill<BITS, MW, CPT, XS, FT>;
@@ -230,7 +230,7 @@ __device__ __forceinline__ void rms_norm_fill(int C, int K, float eps, float *pa
     float tot = 0.f;
     const int waves = (int)blockDim.x >> 6;
     for (int w = 0; w < waves; ++w) tot += part[w];
-    const float rs = 1.f / sqrtf(tot / (float)K + eps);
+    const float rs = __builtin_amdgcn_rsqf(tot * inv_k + eps);
 #pragma unroll
     for (int k = 0; k < F::PER; ++k) {
         if (k < per) {
@@ -296,8 +296,18 @@ struct RowBuf {
     u32x4 w[R][CPT];
     uint16_t s[R][CPT];  // 16-bit on purpose: a 32-bit copy would be zero-extended at the
     uint16_t b[R][CPT];  // loop entry, forcing a wait for these loads before the next ones
-    uint16_t e[INIT ? R : 1];
+    uint32_t e[INIT ? R : 1];  // bf16 in the low half (scalar registers)
 };
+
+// The bf16 at p, read through the scalar data cache (p is wave-uniform): the
+// aligned dword holding it, then its half. The dword never crosses a page
+// boundary, so it reads nothing outside the page that holds p.
+typedef const __attribute__((address_space(4))) uint32_t scalar_u32;
+__device__ __forceinline__ uint32_t scalar_bf16(const uint16_t *p) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uint32_t w = *reinterpret_cast<scalar_u32 *>(a & ~(uintptr_t)3);
+    return (a & 2) ? (w >> 16) : (w & 0xFFFFu);
+}
 
 // The rows, scales and biases of one weight plane, with their row pitches.
 struct Plane {
@@ -337,13 +347,13 @@ __device__ __forceinline__ void load_rows(RowBuf<CPT, R, INIT> &buf, const Plane
         }
     }
     if constexpr (INIT) {
-        // Every lane reads the row's value (one load instruction); a null
-        // `init` gives empty descriptors, so the values read as zero.
+        // One scalar load per row (no vector-memory instruction); rows past
+        // the walk read row 0 and drop it.
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const bool in = rb + r < end && init;
-            const __amdgpu_buffer_rsrc_t er = byte_range(in ? init + rb + r : init, in ? 2u : 0u);
-            buf.e[r] = __builtin_amdgcn_raw_buffer_load_b16(er, 0, 0, kLoadNT);
+            const bool in = rb + r < end;
+            const uint32_t v = scalar_bf16(init + (in ? rb + r : 0));
+            buf.e[r] = in ? v : 0u;
         }
     }
 }
@@ -427,6 +437,18 @@ __device__ __forceinline__ RowWalk row_walk(const ProductArgs &a, int64_t rg, in
     return RowWalk{rg * R, groups * R, a.N};
 }
 
+// A walk over row pairs (2p, 2p + 1), one row per iteration: iterations 2i
+// and 2i + 1 read the two rows of pair first + i * stride. Gated epilogues use
+// it to meet a gate row and its up row in consecutive iterations.
+struct PairWalk {
+    int64_t first;   // first pair
+    int64_t stride;  // pairs between consecutive iteration pairs
+    int64_t end;     // rows >= end are neither read nor stored
+    __device__ __forceinline__ int64_t at(int it) const {
+        return 2 * (first + (int64_t)(it >> 1) * stride) + (it & 1);
+    }
+};
+
 // Reduce the lane partials of iteration `it` to row results and store them.
 // All R*MW values are reduced together (wave_sums); value i = r*MW + m leaves
 // in row rho = lane/16 of register i/4, and the first lane of that row owns it.
@@ -445,9 +467,12 @@ struct Flush {
 constexpr int kSlotFloats = 64;  // per wave and region
 constexpr int kBlockWaves = 8;   // __launch_bounds__(512)
 
-template <int MW, int R, typename Out>
-__device__ __forceinline__ void finish_rows(float (&acc)[R][MW], const Out &out, const RowWalk &walk, int it,
-                                            int iters, int S, int wig, int grp, int lane, float *red) {
+// Gated epilogues with one row per iteration (a PairWalk, S == 1) hold the
+// gate row's sum in `pend` until the up row's iteration.
+template <int MW, int R, typename Out, typename Walk>
+__device__ __forceinline__ void finish_rows(float (&acc)[R][MW], const Out &out, const Walk &walk, int it,
+                                            int iters, int S, int wig, int grp, int lane, float *red,
+                                            float &pend) {
     constexpr int V = Flush<MW, R>::V;
     float v[V], t[sum_regs(V)];
 #pragma unroll
@@ -461,7 +486,14 @@ __device__ __forceinline__ void finish_rows(float (&acc)[R][MW], const Out &out,
         for (int j = 0; j < sum_regs(V); ++j) {
             const int i = 4 * j + sum_slot(rho);
             const int r = i / MW, m = i % MW;
-            if constexpr (Out::kGlu) {
+            if constexpr (Out::kGlu && R == 1) {
+                // A PairWalk: even iterations reduce a gate row, odd ones its up row.
+                if (it & 1) {
+                    if (leader && rho == 0 && rb < walk.end) out.glu(rb >> 1, pend, t[j]);
+                } else {
+                    pend = t[j];
+                }
+            } else if constexpr (Out::kGlu) {
                 // One activation row, R even: the gate rows (i even) sit in lane rows
                 // 0 and 1, their up rows (i + 1) in lane rows 2 and 3 of the same register.
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[j]), __float_as_uint(t[j]),
@@ -485,7 +517,9 @@ __device__ __forceinline__ void finish_rows(float (&acc)[R][MW], const Out &out,
     if (slot == F - 1 || it == iters - 1) {  // uniform over the block (equal iteration counts)
         __syncthreads();
         if constexpr (Out::kGlu) {
-            // One activation row, R even: lane 2u holds a gate row, lane 2u + 1 its up row.
+            // One activation row: lane 2u holds a gate row, lane 2u + 1 its up row (R
+            // even, or a PairWalk with one row per iteration: flushes start at even
+            // iterations).
             // (Every lane of the wave sums, so the neighbour exchange sees active lanes;
             // lanes past the flushed values read slots they do not store.)
             if (wig == 0) {
@@ -520,17 +554,18 @@ template <int CPT, int R, bool INIT, int MW>
 __device__ __forceinline__ void add_init(const RowBuf<CPT, R, INIT> &buf, float (&acc)[R][MW], bool owner) {
     if constexpr (INIT) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r][0] += owner ? bf16_lo((uint32_t)buf.e[r]) : 0.f;
+        for (int r = 0; r < R; ++r) acc[r][0] += owner ? bf16_lo(buf.e[r]) : 0.f;
     }
 }
 
 // RMS norm of one activation row, applied to the raw bf16 words a wave has
-// loaded: x_n = bf16(x * rs * gamma) with rs = 1 / sqrt(sum(x^2) / K + eps).
+// loaded: x_n = bf16(x * rs * gamma) with rs = 1 / sqrt(sum(x^2) / K + eps)
+// (v_rsq_f32 of the mean square plus eps, the mean as a product with 1/K).
 // The sum of squares (lanes past the row end add nothing) is a wave sum; with
 // S > 1 the S waves of the row group add their sums through LDS, in order, at
 // one block barrier (every wave of the block calls this).
 template <int CPT, int XC, typename Rows>
-__device__ __forceinline__ void rms_norm_words(const Rows &xrows, const ProductArgs &a, u32x4 (&xw)[CPT][XC],
+__device__ __forceinline__ void rms_norm_words(const Rows &xrows, u32x4 (&xw)[CPT][XC],
                                                const u32x4 (&gw)[CPT][XC], const bool (&cv)[CPT], int S, int wig,
                                                int grp, int lane) {
     float ss = 0.f;
@@ -556,7 +591,7 @@ __device__ __forceinline__ void rms_norm_words(const Rows &xrows, const ProductA
         tot = 0.f;
         for (int s = 0; s < S; ++s) tot += xrows.part[grp * S + s];
     }
-    const float rs = 1.f / sqrtf(tot / (float)a.K + xrows.eps);
+    const float rs = __builtin_amdgcn_rsqf(tot * xrows.inv_k + xrows.eps);
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
 #pragma unroll
@@ -577,9 +612,9 @@ __device__ __forceinline__ void rms_norm_words(const Rows &xrows, const ProductA
 // The row loop streams through a ring of NB register buffers: each buffer is
 // refilled with the rows NB iterations ahead as soon as it has been consumed.
 // Rows past the walk read nothing (empty descriptors).
-template <int BITS, int CPT, int MW, int R, int NB, int XS, typename Rows, typename Out>
+template <int BITS, int CPT, int MW, int R, int NB, int XS, typename Rows, typename Out, typename Walk>
 __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &pl, const Rows &xrows,
-                                             const Out &out, const RowWalk &walk, int iters, float *red) {
+                                             const Out &out, const Walk &walk, int iters, float *red) {
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int S = a.S;
@@ -628,12 +663,11 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
         }
     }
     // The norm weights of the lane's columns (Rows::kNorm, x staged by each
-    // wave): zeros past the row end, and everywhere when the norm is off
-    // (empty descriptor).
+    // wave): zeros past the row end.
     u32x4 graw[Rows::kNorm && !XL ? CPT : 1][XC];
     if constexpr (Rows::kNorm && !XL) {
         static_assert(MW == 1, "the RMS norm prologue stages one activation row per wave");
-        const __amdgpu_buffer_rsrc_t gr = byte_range(xrows.gamma, xrows.gamma ? (uint32_t)a.K * 2u : 0u);
+        const __amdgpu_buffer_rsrc_t gr = byte_range(xrows.gamma, (uint32_t)a.K * 2u);
 #pragma unroll
         for (int j = 0; j < CPT; ++j)
 #pragma unroll
@@ -641,18 +675,19 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
                 graw[j][t] = __builtin_amdgcn_raw_buffer_load_b128(gr, (uint32_t)(chunk[j] * XC + t) * 16u, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_rows<CPT, R, INIT>(buf[0], pl, walk.at(0), walk.end, woff, goff, init);
+    // With the norm in the block's fill (two block barriers before the first
+    // product), every stage of the ring is issued first, so the weight stream
+    // runs during the prologue.
+    constexpr int EARLY = Rows::kNorm && XL ? NB : 1;
+#pragma unroll
+    for (int p = 0; p < EARLY; ++p) load_rows<CPT, R, INIT>(buf[p], pl, walk.at(p), walk.end, woff, goff, init);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (Rows::kNorm && !XL) {
-        if (xrows.gamma) rms_norm_words<CPT, XC>(xrows, a, xraw[0], graw, cv, S, wig, grp, lane);
-    }
+    if constexpr (Rows::kNorm && !XL) rms_norm_words<CPT, XC>(xrows, xraw[0], graw, cv, S, wig, grp, lane);
 
     uint32_t xv[MW][CPT][16];
     float xs[MW][CPT], nxs[MW][CPT];
     if constexpr (XL) {
-        if constexpr (Rows::kNorm) {
-            if (xrows.gamma) rms_norm_fill<BITS, MW, CPT, XS, FT>(a.C, a.K, xrows.eps, xrows.part, xr, gr);
-        }
+        if constexpr (Rows::kNorm) rms_norm_fill<BITS, MW, CPT, XS, FT>(a.C, xrows.inv_k, xrows.eps, xrows.part, xr, gr);
         store_x<BITS, MW, CPT, XS, FT>(a.C, xr);  // block barrier: every wave of the block gets here
 #pragma unroll
         for (int m = 0; m < MW; ++m)
@@ -669,7 +704,7 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
 #pragma unroll
         for (int j = 0; j < CPT; ++j) nxs[m][j] = BITS == 4 ? -128.f * xs[m][j] : 0.f;
 #pragma unroll
-    for (int p = 1; p < NB; ++p) load_rows<CPT, R, INIT>(buf[p], pl, walk.at(p), walk.end, woff, goff, init);
+    for (int p = EARLY; p < NB; ++p) load_rows<CPT, R, INIT>(buf[p], pl, walk.at(p), walk.end, woff, goff, init);
     __builtin_amdgcn_sched_barrier(0);
 
     // Every turn of the ring but the last refills each buffer NB iterations
@@ -677,13 +712,14 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
     // issues no loads. (Refills past the walk would read nothing, but each
     // load instruction still costs address-unit time.)
     float acc[R][MW];
+    float pend = 0.f;
     int it0 = 0;
     for (; it0 + NB < iters; it0 += NB) {
 #pragma unroll
         for (int p = 0; p < NB; ++p) {
             compute_rows<BITS, CPT, MW, R>(buf[p], xv, xs, nxs, acc);
             add_init(buf[p], acc, lane == 0 && wig == 0);
-            finish_rows<MW, R>(acc, out, walk, it0 + p, iters, S, wig, grp, lane, red);
+            finish_rows<MW, R>(acc, out, walk, it0 + p, iters, S, wig, grp, lane, red, pend);
             load_rows<CPT, R, INIT>(buf[p], pl, walk.at(it0 + p + NB), walk.end, woff, goff, init);
             // Keep the next buffer's use below this refill.
             __builtin_amdgcn_sched_barrier(0);
@@ -693,7 +729,7 @@ __device__ __forceinline__ void product_rows(const ProductArgs &a, const Plane &
     for (int p = 0; p < NB; ++p) {
         compute_rows<BITS, CPT, MW, R>(buf[p], xv, xs, nxs, acc);
         add_init(buf[p], acc, lane == 0 && wig == 0);
-        finish_rows<MW, R>(acc, out, walk, it0 + p, iters, S, wig, grp, lane, red);
+        finish_rows<MW, R>(acc, out, walk, it0 + p, iters, S, wig, grp, lane, red, pend);
     }
     if (S > 1) __syncthreads();  // the LDS slots are reused by the caller's next pass
 }

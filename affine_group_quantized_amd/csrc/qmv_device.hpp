@@ -22,12 +22,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 // Both bfloat16 values of a pair times rs and times the matching norm weight,
-// each product rounded once to bfloat16: (x * rs) * g in fp32, then to nearest even.
+// each product rounded once to bfloat16: (x * rs) * g in fp32, then to nearest
+// even (one v_cvt_pk_bf16_f32 for the pair).
 __device__ __forceinline__ uint32_t norm_pair(uint32_t x, uint32_t g, float rs) {
-    const float lo = bf16_lo(x) * rs * bf16_lo(g);
-    const float hi = bf16_hi(x) * rs * bf16_hi(g);
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    const f32x2 v = {bf16_lo(x) * rs * bf16_lo(g), bf16_hi(x) * rs * bf16_hi(g)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // c + a.lo*b.lo + a.hi*b.hi on bfloat16 pairs (v_dot2c_f32_bf16), fp32 accumulate.

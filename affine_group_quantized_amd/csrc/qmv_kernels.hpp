@@ -31,14 +31,15 @@ struct ProductArgs {
 };
 
 // Argument block of the fused batch-1 projection: the product's arguments
-// (one activation row) plus the norm weights (NULL: no norm), the norm's
-// epsilon and the residual rows (NULL: none).
+// (one activation row) plus the norm weights, the norm's epsilon and 1/K, and
+// the residual rows (each used only by the variants that have that stage).
 struct FusedArgs {
     ProductArgs p;
-    const uint16_t *gamma;  // bf16 [K] or NULL
-    const uint16_t *res;    // bf16 [N] or NULL (act 0 only)
+    const uint16_t *gamma;  // bf16 [K]
+    const uint16_t *res;    // bf16 [N]
     float eps;
-    int32_t pad_[3];
+    float inv_k;
+    int32_t pad_[2];
 };
 
 // Argument block of the matrix-core kernels (4-bit codes, K a multiple of
@@ -79,7 +80,7 @@ const void *quantize_kernel_for(int bits, bool bf16_in);
 const void *mfma_kernel(int tiles, bool gather, int rows);
 // Fused batch-1 projection kernel for (bits, chunks per lane, rows per
 // iteration, ring stages, K segments of the block's LDS copy of x (0: none),
-// epilogue: 0 plain or residual, 1 SwiGLU, 2 GeGLU), or NULL.
-const void *fused_kernel(int bits, int cpt, int R, int NB, int xs, int act);
+// epilogue: 0 residual, 1 SwiGLU, 2 GeGLU, 3 none; RMS norm prologue), or NULL.
+const void *fused_kernel(int bits, int cpt, int R, int NB, int xs, int epi, bool norm);
 
 }  // namespace agq

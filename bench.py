@@ -40,8 +40,12 @@ Other workloads (--workload): c0 (4096x4096), wide (14336x4096 and 4096x14336 at
 M = 2..8), c3 (0.5B-class 8-bit shapes), gather (Mixtral-shaped expert gather),
 qmm (quantized GEMM at M = 16..2048 and the Mixtral-shaped prefill gather, against the
 2.5 PFLOP/s bf16 matrix-core peak and HBM), moe (the fused Mixtral-shaped decode MoE
-layer against its unfused products), calib (the read ceiling and the empty-kernel
-launch floor); one JSON line per shape.
+layer against its unfused products), layer (the Llama-shaped decode layer's
+projections through agq_qmv_fused: norm + qkv, o + residual, norm + gate/up + SwiGLU,
+down + residual, final norm + lm_head, each against the bare product on the same
+weights and against the unfused sequence of torch norm / add / SwiGLU around the bare
+product), calib (the read ceiling and the empty-kernel launch floor); one JSON line per
+shape.
 """
 from __future__ import annotations
 
@@ -85,7 +89,7 @@ def parse():
     ap.add_argument("--write-profiles", nargs="+", metavar="DIR",
                     help="summarize rocprofv3 CSV output of this benchmark into profiles/ and exit: "
                          "TRACE_DIR [FETCH_DIR WRITE_DIR]")
-    ap.add_argument("--workload", choices=["llama", "c0", "wide", "c3", "gather", "qmm", "moe", "calib"],
+    ap.add_argument("--workload", choices=["llama", "c0", "wide", "c3", "gather", "qmm", "moe", "layer", "calib"],
                     default="llama")
     ap.add_argument("--calls", type=int, default=200, help="calls per timed loop of one shape")
     return ap.parse_args()
@@ -467,6 +471,9 @@ def other_workload(args):
     if args.workload == "moe":
         moe_workload(args, torch, si, agq, bf16, u32, stream, emit)
         return
+    if args.workload == "layer":
+        layer_workload(args, torch, si, agq, bf16, u32, stream, calib, emit)
+        return
 
     if args.workload in ("c0", "c3"):
         cfg = 0 if args.workload == "c0" else 3
@@ -639,6 +646,73 @@ def moe_workload(args, torch, si, agq, bf16, u32, stream, emit):
         emit({"shape": f"{label}: Mixtral-shaped layer, {T} tokens top-{k} of {E}, H {H}, F {F} ({used} experts used)",
               "us_per_call": round(us, 3), "us_min": round(us_min, 3), "us_per_token": round(us / T, 3),
               "GB/s": round(gb, 1), "pct_of_hbm_peak": round(100 * gb / HBM_PEAK_GBPS, 2), "bytes": nbytes})
+
+
+def layer_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
+    """The fused batch-1 projections of a Llama-shaped decode layer (workload 1's weights, the
+    decode_layer norm weights and residual). Per projection: agq_qmv_fused; the bare agq_qmv
+    on the same weights (what the fusion must not slow down); and the unfused sequence (torch
+    RMS norm in fp32 rounded to bf16, agq_qmv, torch residual add or SwiGLU). Bytes of the
+    fused call: weights + x + norm weight (when normed) + residual (when added) + y."""
+    wl = si.workload(1)
+    dl = si.decode_layer()
+    eps = dl["eps"]
+    st = stream.cuda_stream
+    g_attn, g_mlp, g_final = bf16(dl["gamma_attn"]), bf16(dl["gamma_mlp"]), bf16(dl["gamma_final"])
+    h = bf16(dl["h"])
+    x14 = bf16(wl["x14336"])[0]
+    x4 = bf16(wl["x4096"])[0]
+    # (name, activation, norm weight, residual, act)
+    steps = [("qkv", h, g_attn, None, 0), ("o", x4, None, h, 0), ("gate_up", h, g_mlp, None, 1),
+             ("down", x14, None, h, 0), ("lm_head", h, g_final, None, 0)]
+    silu = torch.nn.functional.silu
+
+    def rms(x, g):
+        xf = x.float()
+        return (xf * torch.rsqrt(xf.pow(2).mean() + eps) * g.float()).to(torch.bfloat16)
+
+    tot = {"fused": 0.0, "bare": 0.0, "unfused": 0.0}
+    for name, x, g, r, act in steps:
+        m = wl[name]
+        N, K = m["N"], m["K"]
+        cp = rotation(u32, bf16, m, weight_bytes(N, K, 4))
+        rot = len(cp)
+        ptrs = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr()) for c in cp]
+        n_out = N if act == 0 else N // 2
+        y = torch.empty(n_out, dtype=torch.bfloat16, device=x.device)
+        yb = torch.empty(N, dtype=torch.bfloat16, device=x.device)
+        agq.qmv_fused(x, *cp[0], norm_weight=g, eps=eps, residual=r, act=act, out=y)  # validates once
+        gp = None if g is None else g.data_ptr()
+        rp = None if r is None else r.data_ptr()
+        xp, yp, ybp = x.data_ptr(), y.data_ptr(), yb.data_ptr()
+        fused = lambda i: agq.lib.agq_qmv_fused(xp, gp, eps, *ptrs[i % rot], rp, act, yp, N, K, 4, 64, st)  # noqa
+        bare = lambda i: agq.lib.agq_qmv(xp, *ptrs[i % rot], ybp, N, K, 4, 64, st)  # noqa: E731
+
+        def unfused(i):
+            xin = x if g is None else rms(x, g)
+            v = agq.qmv(xin, *cp[i % rot])
+            if act:
+                vv = v.float().view(-1, 2)
+                return (silu(vv[:, 0]) * vv[:, 1]).to(torch.bfloat16)
+            return v if r is None else (v.float() + r.float()).to(torch.bfloat16)
+        nb = weight_bytes(N, K, 4) + 2 * K + (2 * K if g is not None else 0) + (2 * N if r is not None else 0) \
+            + 2 * n_out
+        ceil = calib.ceiling(nb) if calib else None
+        label = f"{name} {N}x{K}" + (" norm" if g is not None else "") + (" +residual" if r is not None else "") \
+            + (" SwiGLU" if act else "")
+        for kind, fn, calls in (("fused", fused, args.calls), ("bare", bare, args.calls),
+                                ("unfused", unfused, max(1, args.calls // 4))):
+            us, us_min = time_shape(torch, fn, calls, 5, stream)
+            tot[kind] += us
+            rec = shape_line(f"{kind}: {label}", us, us_min, nb, agq.launch_plan(1, N, K, 4) if kind == "bare"
+                             else None, ceil if kind == "fused" else None)
+            emit(rec)
+        del cp
+        torch.cuda.empty_cache()
+    emit({"layer": "Llama-shaped decode layer projections + lm_head, batch 1",
+          **{f"{k}_us": round(v, 3) for k, v in tot.items()},
+          "fused_over_bare": round(tot["fused"] / tot["bare"], 4),
+          "unfused_over_fused": round(tot["unfused"] / tot["fused"], 3)})
 
 
 # ----------------------------------------------------------------------------- main workload
