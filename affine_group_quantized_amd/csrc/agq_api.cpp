@@ -89,7 +89,18 @@ OccEntry g_occ[kOccSlots];
 int g_occ_n = 0;
 std::mutex g_occ_mu;
 
+// Each thread first looks in its own small direct-mapped copy of the cache, so
+// a steady stream of calls takes no lock and scans nothing.
+constexpr int kOccLocal = 16;
+thread_local OccEntry t_occ[kOccLocal];
+
 agq_status resident_waves(const void *sym, int threads, size_t lds, int cus, int dev, int64_t *waves) {
+    OccEntry &mine = t_occ[(reinterpret_cast<uintptr_t>(sym) >> 6 ^ (uintptr_t)threads ^ lds ^ (uintptr_t)dev) %
+                           kOccLocal];
+    if (mine.sym == sym && mine.dev == dev && mine.threads == threads && mine.lds == lds) {
+        *waves = (int64_t)cus * mine.blocks_per_cu * (threads / 64);
+        return AGQ_OK;
+    }
     int bpc = -1;
     {
         std::lock_guard<std::mutex> lock(g_occ_mu);
@@ -104,6 +115,7 @@ agq_status resident_waves(const void *sym, int threads, size_t lds, int cus, int
         std::lock_guard<std::mutex> lock(g_occ_mu);
         if (g_occ_n < kOccSlots) g_occ[g_occ_n++] = OccEntry{sym, dev, threads, lds, bpc};
     }
+    mine = OccEntry{sym, dev, threads, lds, bpc};
     *waves = (int64_t)cus * bpc * (threads / 64);
     return AGQ_OK;
 }

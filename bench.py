@@ -248,9 +248,9 @@ def cpu_baseline(shapes, xs, bits=4, calls=3):
 # ----------------------------------------------------------------------------- profiles
 
 
-KERNEL_SOURCES = ["affine_group_quantized_amd/csrc/qmv_kernels.hip", "affine_group_quantized_amd/csrc/qmv_device.hpp",
-                  "affine_group_quantized_amd/csrc/qmv_kernels.hpp", "affine_group_quantized_amd/csrc/plan.hpp",
-                  "affine_group_quantized_amd/csrc/agq_api.cpp"]
+KERNEL_SOURCES = ["affine_group_quantized_amd/csrc/qmv_kernels.hip", "affine_group_quantized_amd/csrc/qmv_core.hpp",
+                  "affine_group_quantized_amd/csrc/qmv_device.hpp", "affine_group_quantized_amd/csrc/qmv_kernels.hpp",
+                  "affine_group_quantized_amd/csrc/plan.hpp", "affine_group_quantized_amd/csrc/agq_api.cpp"]
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "qmv_llama_decode_set_hbm_traffic.md")
 
 
@@ -299,16 +299,26 @@ def _counter(d, cname, pred):
 
 WORKLOAD_FLAGS = {"llama": "--steps 20 --repeats 3 --no-cpu-baseline --no-calib --no-graph",
                   "c0": "--workload c0 --calls 100", "wide": "--workload wide --calls 40",
-                  "c3": "--workload c3 --calls 100", "gather": "--workload gather --calls 40"}
+                  "c3": "--workload c3 --calls 100", "gather": "--workload gather --calls 40",
+                  "qmm": "--workload qmm --calls 20", "moe": "--workload moe",
+                  "layer": "--workload layer --calls 40 --no-calib"}
 PMC_FLAGS = {"llama": "--steps 5 --repeats 1 --warmup 2 --warm-seconds 0 --no-cpu-baseline --no-calib --no-graph",
              "c0": "--workload c0 --calls 8", "wide": "--workload wide --calls 8", "c3": "--workload c3 --calls 8",
-             "gather": "--workload gather --calls 8"}
+             "gather": "--workload gather --calls 8", "qmm": "--workload qmm --calls 4", "moe": "--workload moe",
+             "layer": "--workload layer --calls 8 --no-calib"}
 TITLES = {"llama": "Llama-3-8B-shaped decode GEMV set, batch 1, 4-bit gs64",
           "c0": "single product 4096x4096, batch 1, 4-bit gs64",
           "wide": "small-batch products 14336x4096 and 4096x14336 at M = 2, 4, 6, 8 (4-bit gs64)",
           "c3": "0.5B-class decode GEMVs, batch 1, 8-bit gs64 (4864x896, 896x4864, 1152x896, 151936x896)",
           "gather": "Mixtral-shaped expert gather, 8 planes of 14336x4096 (W1) and 4096x14336 (W2), 32 pairs "
-                    "(4-bit gs64)"}
+                    "(4-bit gs64)",
+          "qmm": "quantized GEMM 14336x4096 / 4096x14336 at M = 16..2048 and the Mixtral-shaped prefill gather "
+                 "(512 tokens, top-2), 4-bit gs64",
+          "moe": "Mixtral-shaped decode MoE layer, 16 tokens top-2 of 8 experts, H 4096, F 14336, fused against "
+                 "unfused (4-bit gs64)",
+          "layer": "Llama-shaped decode layer projections through the fused batch-1 kernel (norm + qkv, "
+                   "o + residual, norm + gate/up + SwiGLU, down + residual, final norm + lm_head), against the "
+                   "bare products and the unfused sequence (4-bit gs64)"}
 
 
 def write_profiles(workload, dirs):
@@ -319,7 +329,8 @@ def write_profiles(workload, dirs):
     __amd_rocclr_copyBuffer, dispatches of known size that calibrate the counters; the
     other workloads reuse the factors recorded with the llama counters."""
     name = {"llama": "qmv_llama_decode_set", "c0": "qmv_c0_4096x4096", "wide": "qmv_wide", "c3": "qmv_c3_8bit",
-            "gather": "qmv_gather"}[workload]
+            "gather": "qmv_gather", "qmm": "qmm_prefill", "moe": "moe_decode_layer",
+            "layer": "qmv_fused_decode_layer"}[workload]
     stats = _read_csv(dirs[0], "kernel_stats.csv")
     trace = _read_csv(dirs[0], "kernel_trace.csv")
     cmd = f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- python3 bench.py " \
@@ -327,8 +338,12 @@ def write_profiles(workload, dirs):
     lines = [f"# rocprofv3 kernel statistics: {TITLES[workload]}", "", "Command (from the repository root):", "",
              f"    {cmd}", "",
              "Template arguments: `qmv_kernel<bits, chunks per lane, activation rows, rows per iteration, ring "
-             "stages, LDS-copy segments>` (VALU); `qmv_mfma_kernel<tiles per band, LDS copy of x, activation load "
-             "form>` and `gather_mfma_kernel<tiles, LDS copy>` (matrix cores).", "",
+             "stages, LDS-copy segments>` and `gather_qmv_kernel<bits, chunks per lane, rows per iteration, ring "
+             "stages, LDS-copy segments>` (VALU); `qmv_fused_kernel<bits, chunks per lane, rows per iteration, "
+             "ring stages, LDS-copy segments, epilogue (0 residual, 1 SwiGLU, 2 GeGLU, 3 none), norm>` (VALU); "
+             "`qmv_mfma_kernel<tiles per band, activation load form (4: compact, 2: staged, 1: four loads)>` and "
+             "`gather_mfma_kernel<tiles>` (matrix cores); `qmm_kernel` / `gather_qmm_kernel<bits, tile rows / 32, "
+             "tile columns / 32, ...>` and the MoE kernels (matrix cores).", "",
              "| kernel | calls | average us | min us | max us | share of time |", "|---|---|---|---|---|---|"]
     for r in stats:
         if "agq::" in r["Name"]:
@@ -836,6 +851,17 @@ def main():
             per_shape[name] = rec
             print(f"[bench] {name:8s} {json.dumps(rec)}", file=sys.stderr, flush=True)
 
+    # Host cost of one call (checks, plan, launch; the prepared one-C-call closure from Python),
+    # timed on the host over back-to-back steps while the GPU drains the queue behind it.
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        n_host = 100
+        t0 = time.perf_counter()
+        for i in range(n_host):
+            step(i)
+        host_s = time.perf_counter() - t0
+        torch.cuda.synchronize()
+
     dom_us = sum(per_shape[n]["us_per_call"] for n in dom) / len(dom)
     dom_bytes = sum(algo_bytes(mats[n]["N"], mats[n]["K"], 4) for n in dom) / len(dom)
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
@@ -849,7 +875,8 @@ def main():
               "ms_per_step_min": round(min(windows), 5), "ms_per_step_max": round(max(windows), 5),
               "pct_of_hbm_peak": round(100 * value_gbps / HBM_PEAK_GBPS, 2),
               "value_best_window": round(step_bytes / (min(windows) * 1e-3) / 1e9, 2),
-              "per_shape": per_shape}
+              "per_shape": per_shape,
+              "host_us_per_call": round(host_s / (n_host * len(SHAPES)) * 1e6, 3)}
     if graph is not None:
         config["graph_replay_value"] = round(step_bytes / (graph * 1e-3) / 1e9, 2)
         config["graph_replay_ms_per_step"] = round(graph, 5)
