@@ -490,14 +490,15 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
         return launch(sym, dim3((unsigned)mp.groups, (unsigned)passes), dim3(mp.threads), (size_t)mp.lds_bytes, &a,
                       stream);
     }
-    const agq::QmmKernel k = agq::qmm_kernel_for(bits, false, M);
-    if ((int64_t)k.bn * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
-    const int64_t mt = (M + k.bm - 1) / k.bm, nt = (N + k.bn - 1) / k.bn;
-    if (mt > 65535 || nt > INT32_MAX) return fail(AGQ_ENOTSUP, "grid too large (M=%lld, N=%lld)", (long long)M,
-                                                  (long long)N);
+    // (Checked for the smaller tile's grid, the larger of the two.)
+    if ((int64_t)agq::kQmmTileN * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
+    if ((M + agq::kQmmTileMinM - 1) / agq::kQmmTileMinM > 65535 || (N + agq::kQmmTileN - 1) / agq::kQmmTileN > INT32_MAX)
+        return fail(AGQ_ENOTSUP, "grid too large (M=%lld, N=%lld)", (long long)M, (long long)N);
     int cus = 0, dev = 0;
     st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
+    const agq::QmmKernel k = agq::qmm_kernel_for(bits, false, M, N, 1, cus);
+    const int64_t mt = (M + k.bm - 1) / k.bm, nt = (N + k.bn - 1) / k.bn;
     agq::QmmArgs a{};
     a.x = static_cast<const uint16_t *>(x);
     a.w = w;
@@ -530,13 +531,13 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
     if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
     if (R * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (R*K*2 bytes)");
     if (group_size != 64) return fail(AGQ_ENOTSUP, "gather_qmm takes group size 64");
-    const agq::QmmKernel k = agq::qmm_kernel_for(bits, true, (P + E - 1) / E);
-    if ((int64_t)k.bn * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
-    const int64_t nt = (N + k.bn - 1) / k.bn;
-    if (nt > INT32_MAX) return fail(AGQ_ENOTSUP, "N too large");
+    if ((int64_t)agq::kQmmTileN * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
+    if ((N + agq::kQmmTileN - 1) / agq::kQmmTileN > INT32_MAX) return fail(AGQ_ENOTSUP, "N too large");
     int cus = 0, dev = 0;
     st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
+    const agq::QmmKernel k = agq::qmm_kernel_for(bits, true, (P + E - 1) / E, N, E, cus);
+    const int64_t nt = (N + k.bn - 1) / k.bn;
     agq::QmmArgs a{};
     a.x = static_cast<const uint16_t *>(x);
     a.w = w;

@@ -8,14 +8,20 @@
 namespace agq {
 
 // Tile shapes: a block of 4 waves computes 32*TM activation rows by 32*TN
-// weight rows; global loads run DEPTH 64-column groups ahead. Measured on the
-// Llama-3-8B shapes (4-bit, TFLOP/s): 64 x 64 tiles with loads 4 groups ahead
-// lead at M = 64 (o: 51 against 40 with 64 x 128), 128 x 64 tiles with loads
-// 2 groups ahead from M = 512 (gate_up M = 2048: 393 against 295 with 64 x 128
-// and 353 with 128 x 128; the Mixtral-shaped prefill gather 279 against 212).
-// Up to this many activation rows (dense), or pairs per expert plane (gather): 64 x 64 tiles.
+// weight rows; global loads run DEPTH 64-column groups ahead. Two shapes:
+//  - 64 x 64 tiles, loads 4 groups ahead, each group's results folded a group
+//    later (latency over occupancy);
+//  - 128 x 64 tiles, loads 2 groups ahead (occupancy: 2 waves per SIMD).
+// The large tile wherever it leaves at least kQmmLargeBlocksPerCu blocks per
+// compute unit, and the activation rows (dense M, or pairs per expert plane)
+// exceed the small tile's threshold. Measured (4-bit, us): 4096x4096 at M =
+// 256 / 512 / 1024: small 43.0 / 56.4 / 112, large 59.8 / 66.8 / 76.8;
+// 4096x14336 at M = 256 / 512 / 1024: small 153 / 204 / 419, large 218 / 218 /
+// 266; 28672x4096 at M = 256 / 512: small 245 / 455, large 164 / 323; the
+// Mixtral-shaped prefill gather (1024 pairs): small 588, large 426.
 constexpr int kQmmSmallM = 128;
 constexpr int kQmmSmallPairs = 64;
+constexpr int kQmmLargeBlocksPerCu = 2;
 constexpr int kQmmPassRows = 128;  // 4-bit products of up to this many rows run on the matvec kernel in passes of 16
 
 // Passed by value as the single kernel argument.
@@ -44,7 +50,11 @@ struct QmmKernel {
     int lds = 0;         // dynamic LDS bytes of the tile buffers
 };
 
-// The kernel for `rows` activation rows (dense M, or the gather's pairs per expert plane).
-QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows);
+// The kernel for `rows` activation rows (dense M, or the gather's pairs per
+// expert plane) against N weight rows in `planes` planes on `cus` compute units.
+QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t planes, int cus);
+// Tile geometry shared by both shapes (the host checks use it before any HIP call).
+constexpr int kQmmTileN = 64;
+constexpr int kQmmTileMinM = 64;
 
 }  // namespace agq

@@ -102,6 +102,10 @@ struct Tile {
     // LDS per buffer: x words, B words, scale and bias (bf16 each) per weight row.
     static constexpr int LDS_X = XW * 16, LDS_W = BN * 8 * 16, LDS_SB = BN * 4;
     static constexpr int LDS_BUF = LDS_X + LDS_W + LDS_SB;
+    // Deferred folding of each group's results (qmm_tile): only small wave
+    // tiles have the registers for a second set of results (64x64 tiles stay
+    // at 2 waves per SIMD with it; 128x64 tiles would drop to 1).
+    static constexpr bool PIPE = TM * TN <= 4;
     static_assert(XW % THREADS == 0, "x tile words must divide among the threads");
     static_assert(WPT > 0 || WTHREADS <= THREADS, "a code tile smaller than the block takes one load per thread");
 };
@@ -207,9 +211,18 @@ __device__ __forceinline__ void store_group(const Stage<BITS, TM, TN> &st, uint8
     if (t < 2 * TT::BN) sb[t] = st.sb;  // scales [0, BN), biases [BN, 2*BN)
 }
 
-// One group's products on the wave's 16*TM x 16*TN sub-tiles, folded into acc.
+// One group's matrix-core products on the wave's 16*TM x 16*TN sub-tiles,
+// with the scale and the bias term of each weight row read out of LDS, so the
+// fp32 epilogue can run a group later (after the next group's MFMAs are in
+// flight), when the LDS buffer may already hold another group.
+template <int TM, int TN>
+struct GroupSums {
+    f32x4 d[TM][TN], xsum[TM];
+    float s[TN], c[TN];
+};
+
 template <int BITS, int TM, int TN>
-__device__ __forceinline__ void compute_group(const uint8_t *buf, int wm, int wn, f32x4 (&acc)[TM][TN]) {
+__device__ __forceinline__ void mfma_group(const uint8_t *buf, int wm, int wn, GroupSums<TM, TN> &gs) {
     using TT = Tile<BITS, TM, TN>;
     const u32x4 *xs = reinterpret_cast<const u32x4 *>(buf);
     const u32x4 *ws = reinterpret_cast<const u32x4 *>(buf + TT::LDS_X);
@@ -217,7 +230,13 @@ __device__ __forceinline__ void compute_group(const uint8_t *buf, int wm, int wn
     const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const u32x4 ones = {kOne2, kOne2, kOne2, kOne2};
-    f32x4 d[TM][TN], xsum[TM];
+#pragma unroll
+    for (int n = 0; n < TN; ++n) {
+        const int row = wn * 16 * TN + 16 * n + i;
+        const float sv = bf16_lo(sb[row]), bv = bf16_lo(sb[TT::BN + row]);
+        gs.s[n] = sv;
+        gs.c[n] = BITS == 4 ? fmaf(-128.f, sv, bv) : bv;
+    }
 #pragma unroll
     for (int step = 0; step < 2; ++step) {
         const int word = 4 * step + g;
@@ -234,25 +253,27 @@ __device__ __forceinline__ void compute_group(const uint8_t *buf, int wm, int wn
         }
 #pragma unroll
         for (int m = 0; m < TM; ++m) {
-            xsum[m] = mma(av[m], ones, step == 0 ? z : xsum[m]);
+            gs.xsum[m] = mma(av[m], ones, step == 0 ? z : gs.xsum[m]);
 #pragma unroll
-            for (int n = 0; n < TN; ++n) d[m][n] = mma(av[m], bv[n], step == 0 ? z : d[m][n]);
+            for (int n = 0; n < TN; ++n) gs.d[m][n] = mma(av[m], bv[n], step == 0 ? z : gs.d[m][n]);
         }
-    }
-#pragma unroll
-    for (int n = 0; n < TN; ++n) {
-        const int row = wn * 16 * TN + 16 * n + i;
-        const float s = bf16_lo(sb[row]), b = bf16_lo(sb[TT::BN + row]);
-        const float c = BITS == 4 ? fmaf(-128.f, s, b) : b;
-#pragma unroll
-        for (int m = 0; m < TM; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[m][n][r] = fmaf(s, d[m][n][r], fmaf(c, xsum[m][r], acc[m][n][r]));
     }
 }
 
+// acc += s * D + c * X for one group.
+template <int TM, int TN>
+__device__ __forceinline__ void fold_group(const GroupSums<TM, TN> &gs, f32x4 (&acc)[TM][TN]) {
+#pragma unroll
+    for (int n = 0; n < TN; ++n)
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[m][n][r] = fmaf(gs.s[n], gs.d[m][n][r], fmaf(gs.c[n], gs.xsum[m][r], acc[m][n][r]));
+}
+
 // The tile rows [.., BM) of `map` against weight rows [n0, n0 + BN) of one plane.
-template <int BITS, int TM, int TN, int DEPTH, typename Map>
+template <int BITS, int TM, int TN, int DEPTH, bool PIPE, typename Map>
 __device__ __forceinline__ void qmm_tile(const QmmArgs &a, const Map &map, const uint32_t *w, const uint16_t *s,
                                          const uint16_t *b, int64_t n0, uint8_t *lds) {
     using TT = Tile<BITS, TM, TN>;
@@ -279,19 +300,36 @@ __device__ __forceinline__ void qmm_tile(const QmmArgs &a, const Map &map, const
     store_group<BITS, TM, TN>(st[0], lds);
     __syncthreads();
     // Group grp computes from LDS buffer grp & 1 while the loads of grp + DEPTH
-    // go out into the register stage grp just freed.
+    // go out into the register stage grp just freed. With PIPE its MFMA results
+    // are folded into acc one group later, after the next group's MFMAs are
+    // issued, so their latency overlaps that work (at the cost of a second set
+    // of result registers).
+    static_assert(DEPTH % 2 == 0, "the pending results alternate between two slots");
+    GroupSums<TM, TN> gsum[2];
     for (int grp0 = 0; grp0 < a.G; grp0 += DEPTH) {
 #pragma unroll
         for (int p = 0; p < DEPTH; ++p) {
             const int grp = grp0 + p;
             if (grp < a.G) {  // uniform
-                compute_group<BITS, TM, TN>(lds + (grp & 1) * TT::LDS_BUF, wm, wn, acc);
+                mfma_group<BITS, TM, TN>(lds + (grp & 1) * TT::LDS_BUF, wm, wn, gsum[p & 1]);
+                if constexpr (PIPE) {
+                    if (grp > 0) fold_group<TM, TN>(gsum[(p + 1) & 1], acc);
+                } else {
+                    fold_group<TM, TN>(gsum[p & 1], acc);
+                }
                 if (grp + 1 < a.G) store_group<BITS, TM, TN>(st[(p + 1) % DEPTH], lds + ((grp + 1) & 1) * TT::LDS_BUF);
                 const int nxt = grp + DEPTH;
                 load_group<BITS, TM, TN>(st[p], a, map, xr, wr, sr, br, nxt < a.G ? nxt : a.G - 1, xbytes);
                 __syncthreads();
             }
         }
+    }
+    // The last group's results (slot (G - 1) & 1; constant indices keep gsum in registers).
+    if constexpr (PIPE) {
+        if ((a.G - 1) & 1)
+            fold_group<TM, TN>(gsum[1], acc);
+        else
+            fold_group<TM, TN>(gsum[0], acc);
     }
     // Store: lane holds rows 4g + r of sub-tile m, weight row i of sub-tile n.
 #pragma unroll
@@ -316,7 +354,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
     using TT = Tile<BITS, TM, TN>;
     const DenseMap map{(int64_t)blockIdx.y * TT::BM, a.M};
-    qmm_tile<BITS, TM, TN, DEPTH>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * TT::BN, qmm_lds);
+    qmm_tile<BITS, TM, TN, DEPTH, TT::PIPE>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * TT::BN, qmm_lds);
 }
 
 // Gather: blockIdx.x = weight-row tile, blockIdx.y = expert plane e. The
@@ -377,7 +415,7 @@ __global__ __launch_bounds__(256) void gather_qmm_kernel(QmmArgs a) {
     const uint16_t *s = a.s + plane * a.G, *b = a.b + plane * a.G;
     for (int base = 0; base < count; base += TT::BM) {
         const GatherMap map{plist + base, xlist + base, count - base < TT::BM ? count - base : TT::BM};
-        qmm_tile<BITS, TM, TN, DEPTH>(a, map, w, s, b, n0, qmm_lds);
+        qmm_tile<BITS, TM, TN, DEPTH, TT::PIPE>(a, map, w, s, b, n0, qmm_lds);
         __syncthreads();  // the LDS tiles are refilled by the next pass
     }
 }
@@ -396,8 +434,13 @@ static QmmKernel qmm_pick(bool gather) {
     return k;
 }
 
-QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows) {
-    const bool small = rows <= (gather ? kQmmSmallPairs : kQmmSmallM);
+QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t planes, int cus) {
+    static_assert(Tile<4, 2, 2>::BN == kQmmTileN && Tile<4, 4, 2>::BN == kQmmTileN && Tile<4, 2, 2>::BM == kQmmTileMinM,
+                  "the host checks assume these tile sizes");
+    constexpr int LBM = Tile<4, 4, 2>::BM;
+    const int64_t large_blocks = planes * ((rows + LBM - 1) / LBM) * ((N + kQmmTileN - 1) / kQmmTileN);
+    const bool small = rows <= (gather ? kQmmSmallPairs : kQmmSmallM) ||
+                       large_blocks < (int64_t)kQmmLargeBlocksPerCu * cus;
     if (bits == 4) return small ? qmm_pick<4, 2, 2, 4>(gather) : qmm_pick<4, 4, 2, 2>(gather);
     return small ? qmm_pick<8, 2, 2, 4>(gather) : qmm_pick<8, 4, 2, 2>(gather);
 }

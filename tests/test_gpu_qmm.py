@@ -41,8 +41,12 @@ def dev_weight(d):
     (4, 512, 4099, 4096, True), (4, 130, 14336, 4096, True), (4, 96, 4096, 14336, True),
     (8, 9, 100, 896, False), (8, 65, 300, 4864, False), (8, 100, 129, 64, False), (8, 512, 1000, 896, True),
     (4, 17, 129, 512, False), (4, 100, 333, 2048, False), (4, 128, 1000, 14336, True), (4, 300, 200, 4096, False),
+    # enough 128x64 tiles for two blocks per compute unit: the large tile
+    (4, 1024, 4100, 512, True), (8, 1000, 4096, 576, True),
 ])
 def test_qmm_shapes(bits, M, N, K, sample):
+    """Shapes on both tile sizes: the 128x64 tile where it gives at least two blocks per
+    compute unit (M > 128), the pipelined 64x64 tile otherwise."""
     d = si.draw_quantized_weight(30, 100 * bits + M, N, K, bits)
     x = si.draw_activations(30, 1000 + M, M, K)
     w, s, b = dev_weight(d)
