@@ -57,6 +57,11 @@ def _bind(lib):
     lib.agqo_moe_swiglu.argtypes = [P, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, I, I, P, P]
     lib.agqo_quantize.argtypes = [P, I64, I64, I, I, P, P, P]
     lib.agqo_qmv_fused.argtypes = [P, P, ctypes.c_double, P, P, P, I64, I64, I, I, P, I, P, P]
+    lib.agqo_qmv_nvfp4.argtypes = [P, I64, P, P, ctypes.c_double, I64, I64, P, I64, P, P]
+    lib.agqo_e2m1.argtypes = [ctypes.c_uint32]
+    lib.agqo_e2m1.restype = ctypes.c_double
+    lib.agqo_e4m3.argtypes = [ctypes.c_uint32]
+    lib.agqo_e4m3.restype = ctypes.c_double
     lib.agqo_bf16_round.argtypes = [ctypes.c_double]
     lib.agqo_bf16_round.restype = ctypes.c_double
     for f in (lib.agqo_unpack, lib.agqo_dequantize, lib.agqo_qmv, lib.agqo_gather_qmv, lib.agqo_moe_swiglu,
@@ -119,6 +124,23 @@ def qmv(x, w, scales, biases, K: int, bits: int, group_size: int = 64, rows=None
     a = np.empty_like(y)
     _check(lib.agqo_qmv(_p(x), x.shape[0], _p(w), _p(s), _p(b), n, K, bits, group_size,
                         _p(r), nrows, _p(y), _p(a)))
+    return y, a
+
+
+def qmv_nvfp4(x, w, scales, tensor_scale: float, K: int, rows=None, lib=None):
+    """NVFP4 product: ``x`` [M, K] bf16 bits, ``w`` [N, K/8] uint32 (E2M1 codes low-first),
+    ``scales`` [N, K/16] uint8 (E4M3) -> (y, A) float64 ``[M, nrows]``."""
+    lib = lib or load()
+    x = _c(x, np.uint16).reshape(-1, K)
+    w = _c(w, np.uint32)
+    s = _c(scales, np.uint8)
+    n = w.shape[0]
+    r = None if rows is None else _c(rows, np.int64)
+    nrows = n if r is None else r.shape[0]
+    y = np.empty((x.shape[0], nrows), dtype=np.float64)
+    a = np.empty_like(y)
+    _check(lib.agqo_qmv_nvfp4(_p(x), x.shape[0], _p(w), _p(s), float(tensor_scale), n, K, _p(r), nrows,
+                              _p(y), _p(a)))
     return y, a
 
 

@@ -39,6 +39,15 @@
  * no formula; this is the plainest reading, in exact float64 with no
  * intermediate rounding.
  *
+ * The NVFP4 product (agqo_qmv_nvfp4) is the structurally separate path of
+ * "MLX CUDA Cleanup Plan", Phase 3b (mode nvfp4, group size 16). The page
+ * names the format only. Readings: the public NVFP4 definition, 4-bit E2M1
+ * elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit) with one
+ * E4M3 scale (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, S.1111.111 = NaN) per 16 consecutive columns, and one fp32
+ * tensor scale; w = e2m1(q) * e4m3(s) * tensor_scale. Codes pack 8 per U32,
+ * low-first, as the affine 4-bit codes; scales are bytes [N, K/16].
+ *
  * The fused batch-1 projection (agqo_qmv_fused) adds the neighbouring stages
  * that "MLX CUDA Cleanup Plan", Phase 5, lists for the device-resident decode
  * layer: RMS norm before the product, residual add or a GLU (SwiGLU, GeGLU)
@@ -337,6 +346,60 @@ static double bf16_round(double v)
     double d = t - r;
     if (d > 0.5 || (d == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
     return ldexp(r, e - 8);
+}
+
+/* E2M1 (FP4) element from its 4-bit code: sign, exponent (bias 1), mantissa;
+ * exponent 0 is subnormal (m * 2^-1). */
+static double e2m1_value(uint32_t c)
+{
+    const double sign = (c & 8u) ? -1.0 : 1.0;
+    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    const double mag = e == 0 ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return sign * mag;
+}
+
+/* E4M3 (FP8) scale from its byte: sign, exponent (bias 7), mantissa; exponent
+ * 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN (no infinities). */
+static double e4m3_value(uint32_t b)
+{
+    const double sign = (b & 0x80u) ? -1.0 : 1.0;
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return sign * mag;
+}
+
+/* Exported for the pins. */
+double agqo_e2m1(uint32_t c) { return e2m1_value(c & 15u); }
+double agqo_e4m3(uint32_t b) { return e4m3_value(b & 255u); }
+
+/* NVFP4 product: y[m, i] = sum_k x[m, k] * e2m1(q[n_i, k]) * e4m3(s[n_i, k/16]) * tensor_scale,
+ * in the order unpack -> element value -> scaled weight -> dot product (increasing k),
+ * with a[m, i] = sum_k |x * w|. x [M, K] bf16; w [N, K/8] U32; scales [N, K/16] bytes;
+ * rows: an optional subset of output rows (NULL: all N). Output layout [M, nrows]. */
+int agqo_qmv_nvfp4(const uint16_t *x, int64_t M, const uint32_t *w, const uint8_t *scales, double tensor_scale,
+                   int64_t N, int64_t K, const int64_t *rows, int64_t nrows, double *y, double *a)
+{
+    if (!x || !w || !scales || !y || !a || M <= 0 || N <= 0 || K <= 0 || K % 16 != 0) return AGQO_EARG;
+    if (!rows) nrows = N;
+    if (nrows <= 0) return AGQO_EARG;
+    const int64_t words = K / 8, blocks = K / 16;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t i = 0; i < nrows; ++i) {
+            const int64_t n = rows ? rows[i] : i;
+            if (n < 0 || n >= N) return AGQO_EINDEX;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const uint32_t q = (w[n * words + k / 8] >> (4 * (k % 8))) & 15u;
+                const double wk = e2m1_value(q) * e4m3_value(scales[n * blocks + k / 16]) * tensor_scale;
+                const double t = bf16_value(x[m * K + k]) * wk;
+                acc += t;
+                mag += fabs(t);
+            }
+            y[m * nrows + i] = acc;
+            a[m * nrows + i] = mag;
+        }
+    return AGQO_OK;
 }
 
 /* The rounding above, exported so the test suite can pin it on its own. */

@@ -29,6 +29,7 @@ import os
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 import oracle
 from seeded_inputs import bf16_bits, bf16_to_f32, pack_codes, quantize_rows, draw_quantized_weight
@@ -553,6 +554,82 @@ def pin_fused_glu_values(lib):
         for act in (1, 2):
             y, _ = oracle.qmv_fused(x, np.zeros((2, K // 8), np.uint32), zero, b, K, 4, act=act, lib=lib)
             assert abs(y[0] - 32.0 * want[act]) <= 1e-12 * 32.0, (hex(gate_bias), act, y[0])
+
+
+def pin_e2m1_values(lib):
+    """The E2M1 value set of the NVFP4 format: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes
+    0..7, and the sign bit (code | 8) negates."""
+    want = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(8):
+        assert lib.agqo_e2m1(c) == want[c], (c, lib.agqo_e2m1(c))
+        assert lib.agqo_e2m1(c | 8) == -want[c]
+        assert math.copysign(1.0, lib.agqo_e2m1(c | 8)) == -1.0
+
+
+def pin_e4m3_matches_torch(lib):
+    """Every E4M3 byte decodes as torch's float8_e4m3fn does (an independent decoder), NaN
+    for S.1111.111; spot values 0x38 = 1, 0x7E = 448, 0x08 = 2^-6, 0x01 = 2^-9."""
+    torch = pytest.importorskip("torch")
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([lib.agqo_e4m3(b) for b in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert (lib.agqo_e4m3(0x38), lib.agqo_e4m3(0x7E), lib.agqo_e4m3(0x08), lib.agqo_e4m3(0x01)) == \
+        (1.0, 448.0, 2.0 ** -6, 2.0 ** -9)
+
+
+def _nvfp4_problem(seed, N, K):
+    g = np.random.default_rng([95, seed])
+    q = g.integers(0, 16, size=(N, K), dtype=np.uint8)
+    sc = g.integers(0x20, 0x50, size=(N, K // 16), dtype=np.uint8)  # E4M3 scales 2^-4 .. 2^2
+    x = bf16_bits(g.standard_normal((2, K)).astype(np.float32))
+    return q, sc, x
+
+
+def pin_nvfp4_bruteforce(lib):
+    """Exact rational brute force from the codes before packing (values from the E2M1 and
+    E4M3 tables written out here), at two tensor scales."""
+    e2m1 = [Fraction(v) for v in (0, 0.5, 1, 1.5, 2, 3, 4, 6)]
+
+    def e4m3(b):
+        e, m = (b >> 3) & 15, b & 7
+        mag = Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        return -mag if b & 0x80 else mag
+
+    N, K = 5, 48
+    q, sc, x = _nvfp4_problem(1, N, K)
+    w = pack_codes(q, 4)
+    for ts in (1.0, 0.375):
+        y, a = oracle.qmv_nvfp4(x, w, sc, ts, K, lib=lib)
+        xf = bf16_to_f32(x).astype(np.float64)
+        for m in range(2):
+            for n in range(N):
+                exact = sum(Fraction(float(xf[m, k])) * (e2m1[q[n, k] & 7] * (-1 if q[n, k] & 8 else 1)) *
+                            e4m3(int(sc[n, k // 16])) * Fraction(ts) for k in range(K))
+                assert abs(Fraction(y[m, n]) - exact) <= Fraction(1, 2 ** 40) * (abs(exact) + 1), (m, n)
+
+
+def pin_nvfp4_closed_forms(lib):
+    """A constant code c and scale byte b give e2m1(c) * e4m3(b) * ts * sum(x); doubling the
+    tensor scale doubles y exactly; the row subset selects rows."""
+    K, N = 64, 3
+    x = bf16_bits(np.random.default_rng(96).standard_normal((1, K)).astype(np.float32))
+    sx = float(np.sum(bf16_to_f32(x).astype(np.float64)))
+    for c, b, v in ((3, 0x38, 1.5), (15, 0x40, -12.0), (9, 0x30, -0.25)):
+        w = pack_codes(np.full((N, K), c, np.uint8), 4)
+        sc = np.full((N, K // 16), b, np.uint8)
+        y, a = oracle.qmv_nvfp4(x, w, sc, 0.5, K, lib=lib)
+        assert np.allclose(y, v * 0.5 * sx, rtol=1e-14, atol=1e-14), (c, b, y, v * sx)
+        ax = float(np.sum(np.abs(bf16_to_f32(x).astype(np.float64))))
+        assert np.allclose(a, abs(v) * 0.5 * ax, rtol=1e-14), (c, b, a)
+    q, sc, xx = _nvfp4_problem(2, 7, 128)
+    w = pack_codes(q, 4)
+    y1, _ = oracle.qmv_nvfp4(xx, w, sc, 1.0, 128, lib=lib)
+    y2, _ = oracle.qmv_nvfp4(xx, w, sc, 2.0, 128, lib=lib)
+    assert np.array_equal(y2, 2 * y1)
+    ys, _ = oracle.qmv_nvfp4(xx, w, sc, 1.0, 128, rows=np.array([6, 0, 3]), lib=lib)
+    assert np.array_equal(ys, y1[:, [6, 0, 3]])
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

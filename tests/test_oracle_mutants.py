@@ -65,6 +65,15 @@ MUTANTS = {
     "fused_gelu_cubic": ("(z + 0.044715 * z * z * z)", "(z + 0.044715 * z * z)"),
     "fused_magnitude_signed": ("abs_sum += fabs(t);", "abs_sum += t;"),
     "fused_residual_dropped": ("y[n] = v[n] + (residual ? bf16_value(residual[n]) : 0.0);", "y[n] = v[n];"),
+    "e2m1_bias_2": ("ldexp(1.0 + 0.5 * (double)m, (int)e - 1)", "ldexp(1.0 + 0.5 * (double)m, (int)e - 2)"),
+    "e2m1_no_subnormal": ("e == 0 ? 0.5 * (double)m :", "e == 0 ? 1.0 * (double)m :"),
+    "e2m1_sign_ignored": ("const double sign = (c & 8u) ? -1.0 : 1.0;", "const double sign = 1.0;"),
+    "e4m3_bias_8": ("ldexp(1.0 + (double)m / 8.0, (int)e - 7)", "ldexp(1.0 + (double)m / 8.0, (int)e - 8)"),
+    "e4m3_subnormal_scale": ("ldexp((double)m / 8.0, -6)", "ldexp((double)m / 8.0, -7)"),
+    "nvfp4_block_32": ("e4m3_value(scales[n * blocks + k / 16])", "e4m3_value(scales[n * blocks + k / 32])"),
+    "nvfp4_high_first": ("(w[n * words + k / 8] >> (4 * (k % 8))) & 15u", "(w[n * words + k / 8] >> (4 * (7 - k % 8))) & 15u"),
+    "nvfp4_magnitude_signed": ("mag += fabs(t);", "mag += t;"),
+    "nvfp4_tensor_scale_dropped": ("* e4m3_value(scales[n * blocks + k / 16]) * tensor_scale;", "* e4m3_value(scales[n * blocks + k / 16]);"),
     "moe_up_with_gate_scales": ("row_dot(x + t * H, wu + row * hw, su + row * hg,",
                                 "row_dot(x + t * H, wu + row * hw, sg + row * hg,"),
 }
