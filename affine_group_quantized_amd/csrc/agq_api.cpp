@@ -425,6 +425,55 @@ agq_status agq_qmv_fused(const void *x, const void *norm_weight, float eps, cons
     return launch(sym, dim3((unsigned)plan.blocks), dim3(plan.threads), (size_t)plan.x_lds_bytes, &f, stream);
 }
 
+agq_status agq_qmv_nvfp4(const void *x, const uint32_t *w, const void *scales, float tensor_scale, void *y, int64_t M,
+                         int64_t N, int64_t K, void *stream) {
+    if (!x || !w || !scales || !y) return fail(AGQ_EINVAL, "null tensor pointer");
+    if (M <= 0 || N <= 0 || K <= 0)
+        return fail(AGQ_EINVAL, "M, N and K must be positive (M=%lld, N=%lld, K=%lld)", (long long)M, (long long)N,
+                    (long long)K);
+    if (N > kMaxN || K > kMaxK) return fail(AGQ_EINVAL, "N or K too large (N=%lld, K=%lld)", (long long)N, (long long)K);
+    if (K % 16 != 0) return fail(AGQ_EINVAL, "K=%lld is not a multiple of the NVFP4 block of 16", (long long)K);
+    if (K % 32 != 0) return fail(AGQ_ENOTSUP, "K=%lld: the NVFP4 kernel reads 32-code chunks", (long long)K);
+    if (M > 4) return fail(AGQ_ENOTSUP, "M=%lld > 4 activation rows for the NVFP4 product", (long long)M);
+    if (!(tensor_scale == tensor_scale) || tensor_scale > 3.0e38f || tensor_scale < -3.0e38f)
+        return fail(AGQ_EINVAL, "tensor_scale must be finite");
+    if (misaligned(x, 16) || misaligned(w, 16)) return fail(AGQ_EINVAL, "x and w must be 16-byte aligned");
+    if (misaligned(scales, 2) || misaligned(y, 2)) return fail(AGQ_EINVAL, "scales and y must be 2-byte aligned");
+    agq::Plan plan;
+    if (agq::plan_shape(M, K, 4, 0, &plan) != AGQ_OK)  // host-only check before any HIP call
+        return fail(AGQ_ENOTSUP, "K=%lld too large for M=%lld NVFP4 rows", (long long)K, (long long)M);
+    int cus = 0, dev = 0;
+    agq_status st = current_device(&cus, &dev);
+    if (st != AGQ_OK) return st;
+    const void *sym = nullptr;
+    for (int pass = 0; pass < 2; ++pass) {
+        sym = agq::nvfp4_kernel_for(plan.mw, plan.cpt, plan.R, plan.NB);
+        if (!sym) return fail(AGQ_ENOTSUP, "no NVFP4 kernel for rows=%d cpt=%d R=%d", plan.mw, plan.cpt, plan.R);
+        int64_t waves = 0;
+        st = resident_waves(sym, plan.threads, 0, cus, dev, &waves);
+        if (st != AGQ_OK) return st;
+        if (pass == 0 && agq::wants_deep(N, waves, plan.S, 0)) {
+            agq::plan_shape(M, K, 4, 0, &plan, true);
+            continue;
+        }
+        agq::plan_grid(N, waves, 0, &plan);
+        break;
+    }
+    agq::Nvfp4Args a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = reinterpret_cast<const agq::u32x4 *>(w);
+    a.s = static_cast<const uint8_t *>(scales);
+    a.y = static_cast<uint16_t *>(y);
+    a.N = N;
+    a.RPG = plan.RPG;
+    a.K = (int32_t)K;
+    a.C = (int32_t)(K / 32);
+    a.S = plan.S;
+    a.GPB = plan.GPB;
+    a.ts = tensor_scale;
+    return launch(sym, dim3((unsigned)plan.blocks), dim3(plan.threads), 0, &a, stream);
+}
+
 agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y, int64_t P, int64_t R,
                           int64_t E, int64_t N, int64_t K, int bits, int group_size, void *stream) {

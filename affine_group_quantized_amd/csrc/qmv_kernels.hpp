@@ -42,6 +42,23 @@ struct FusedArgs {
     int32_t pad_[2];
 };
 
+// Argument block of the NVFP4 product (qmv_nvfp4.hip): 1-4 activation rows,
+// E2M1 codes in 16-byte chunks of 32, one E4M3 byte per 16 columns.
+struct Nvfp4Args {
+    const uint16_t *x;  // activation rows, bf16 [M, K]
+    const u32x4 *w;     // codes [N, C] chunks
+    const uint8_t *s;   // E4M3 scales [N, K/16]
+    uint16_t *y;        // bf16 outputs [M, N]
+    int64_t N;          // weight rows
+    int64_t RPG;        // weight rows per row group
+    int32_t K;          // columns
+    int32_t C;          // 16-byte chunks per row (K/32)
+    int32_t S;          // waves per row group (K split)
+    int32_t GPB;        // row groups per block
+    float ts;           // tensor scale
+    int32_t pad_[3];
+};
+
 // Argument block of the matrix-core kernels (4-bit codes, K a multiple of
 // 512): bands of 16*T weight rows, S waves per block splitting K into slices
 // of SPW 128-column segments, each block walking BPG bands round-robin.
@@ -82,5 +99,7 @@ const void *mfma_kernel(int tiles, bool gather, int rows);
 // iteration, ring stages, K segments of the block's LDS copy of x (0: none),
 // epilogue: 0 residual, 1 SwiGLU, 2 GeGLU, 3 none; RMS norm prologue), or NULL.
 const void *fused_kernel(int bits, int cpt, int R, int NB, int xs, int epi, bool norm);
+// NVFP4 product kernel for (activation rows 1-4, chunks per lane, rows per iteration, ring stages), or NULL.
+const void *nvfp4_kernel_for(int mw, int cpt, int R, int NB);
 
 }  // namespace agq

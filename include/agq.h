@@ -178,6 +178,28 @@ agq_status agq_qmv_fused(const void *x, const void *norm_weight, float eps, cons
                          void *y, int64_t N, int64_t K, int bits, int group_size, void *stream);
 
 /*
+ * NVFP4 matrix-vector product: the format path that "MLX CUDA Cleanup Plan",
+ * Phase 3b, names for the local checkpoint (mode nvfp4, group size 16) and
+ * keeps structurally separate from the affine path. The page names the
+ * format only; this reads it from the public NVFP4 definition:
+ *     y[m, n] = sum_k x[m, k] * e2m1(q[n, k]) * e4m3(s[n, k/16]) * tensor_scale
+ *   x      [M, K] BF16, 16-byte aligned, 1 <= M <= 4
+ *   w      [N, K/8] U32: 4-bit E2M1 codes (1 sign, 2 exponent bits with bias 1,
+ *          1 mantissa bit; values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}), 8 per word,
+ *          low-first, 16-byte aligned
+ *   scales [N, K/16] bytes: E4M3 (OCP e4m3fn: bias 7, no infinities,
+ *          S.1111.111 = NaN), 2-byte aligned
+ *   tensor_scale  fp32, finite
+ *   y      [M, N] BF16 (written)
+ * fp32 accumulation, one rounding of the sum to BF16. K must be a multiple
+ * of 16 (else AGQ_EINVAL) and of 32 (else AGQ_ENOTSUP), M at most 4 and K at
+ * most 114688 at M = 1 (as agq_qmv_wide at 4 bits); else AGQ_ENOTSUP. One
+ * kernel launch on `stream`. Argument checks and errors as for agq_qmv.
+ */
+agq_status agq_qmv_nvfp4(const void *x, const uint32_t *w, const void *scales, float tensor_scale, void *y,
+                         int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * Expert-gathered matrix-matrix product (MoE prefill, the gather_qmm of the
  * same epic: its Diagnosis (baseline) MoE prefill row is the largest measured
  * gap on those pages, and Phase 3 (#629) targets it). Same arguments and

@@ -42,7 +42,7 @@ CHUNK_ROWS = 1024
 __all__ = [
     "GROUP_SIZE", "CHUNK_ROWS", "stream", "bf16_bits", "bf16_to_f32",
     "pack_codes", "quantize_rows", "draw_activations", "draw_quantized_weight",
-    "random_codes", "workload", "WORKLOADS", "moe_expert_ids", "moe_prefill", "moe_layer", "decode_layer",
+    "random_codes", "workload", "WORKLOADS", "moe_expert_ids", "moe_prefill", "moe_layer", "decode_layer", "nvfp4_weight",
 ]
 
 
@@ -216,6 +216,35 @@ def moe_prefill(tokens: int = 512) -> dict:
     return {"x": draw_activations(5, 0, tokens, m["hidden"]), "ids": ids,
             "rhs": ids.reshape(-1).astype(np.uint32),
             "lhs": np.repeat(np.arange(tokens, dtype=np.uint32), m["top_k"])}
+
+
+_E2M1_MID = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)  # midpoints of 0, 0.5, 1, ..., 6
+
+
+def nvfp4_weight(cfg: int, t: int, n: int, k: int, std: float = 0.02) -> dict:
+    """A weight ``[n, k]`` ~ N(0, std) in NVFP4: ``tensor_scale`` = amax / (6 * 448) (fp32),
+    one E4M3 byte per 16 columns (torch's float8_e4m3fn rounding of amax_block / 6 /
+    tensor_scale), and the nearest E2M1 code of each w / (scale * tensor_scale) (ties to
+    the smaller magnitude), packed 8 per uint32 low-first. Rows are drawn in 1024-row
+    chunks (stream c). Returns ``w``, ``scales`` (uint8 ``[n, k/16]``) and ``tensor_scale``."""
+    import torch
+    parts = [(stream(cfg, t, c).standard_normal((min(CHUNK_ROWS, n - c * CHUNK_ROWS), k), dtype=np.float32)
+              * np.float32(std)) for c in range((n + CHUNK_ROWS - 1) // CHUNK_ROWS)]
+    amax = max(float(np.abs(p).max()) for p in parts)
+    ts = np.float32(max(amax, 1e-30) / (6.0 * 448.0))
+    wq = np.empty((n, k // 8), np.uint32)
+    scales = np.empty((n, k // 16), np.uint8)
+    for c, w in enumerate(parts):
+        r0, r1 = c * CHUNK_ROWS, c * CHUNK_ROWS + w.shape[0]
+        blk = np.abs(w.reshape(w.shape[0], k // 16, 16)).max(axis=2) / np.float32(6.0) / ts
+        s8 = torch.from_numpy(blk.astype(np.float32)).to(torch.float8_e4m3fn)
+        scales[r0:r1] = s8.view(torch.uint8).numpy()
+        sval = s8.to(torch.float32).numpy()
+        v = w.reshape(w.shape[0], k // 16, 16) / np.where(sval == 0, np.float32(1), sval)[..., None] / ts
+        idx = np.searchsorted(_E2M1_MID, np.abs(v), side="left").astype(np.uint8)
+        codes = (idx | ((v < 0).astype(np.uint8) << 3)).reshape(w.shape[0], k)
+        wq[r0:r1] = pack_codes(codes, 4)
+    return {"w": wq, "scales": scales, "tensor_scale": float(ts)}
 
 
 def decode_layer() -> dict:

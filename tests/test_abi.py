@@ -79,6 +79,10 @@ def fused(act=0, g=A, eps=1e-5, res=NUL, N=16, K=64, bits=4, gs=64, x=A, y=A):
     return lib.agq_qmv_fused(x, g, eps, A, A, A, res, act, y, N, K, bits, gs, None)
 
 
+def nvfp4(M=1, N=16, K=64, ts=1.0, x=A, w=A, s=A, y=A):
+    return lib.agq_qmv_nvfp4(x, w, s, ts, y, M, N, K, None)
+
+
 def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     return lib.agq_gather_qmm(x, A, A, A, lhs, rhs, A, P, R, E, N, K, bits, gs, None)
 
@@ -151,6 +155,18 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: fused(K=65536 + 64), ENOTSUP),
     (lambda: fused(K=32768 + 64, bits=8), ENOTSUP),
     (lambda: fused(N=1 << 31), ENOTSUP),
+    (lambda: nvfp4(x=NUL), EINVAL),
+    (lambda: nvfp4(s=NUL), EINVAL),
+    (lambda: nvfp4(M=0), EINVAL),
+    (lambda: nvfp4(M=5), ENOTSUP),
+    (lambda: nvfp4(K=24), EINVAL),
+    (lambda: nvfp4(K=48), ENOTSUP),
+    (lambda: nvfp4(ts=float("nan")), EINVAL),
+    (lambda: nvfp4(ts=float("inf")), EINVAL),
+    (lambda: nvfp4(s=ctypes.c_void_p(0x10001)), EINVAL),
+    (lambda: nvfp4(x=A2), EINVAL),
+    (lambda: nvfp4(K=114688 + 32), ENOTSUP),
+    (lambda: nvfp4(M=4, K=32768 + 32), ENOTSUP),
     (lambda: gqmm(P=0), EINVAL),
     (lambda: gqmm(lhs=NUL, R=3), EINVAL),
     (lambda: gqmm(rhs=NUL, E=3), EINVAL),
