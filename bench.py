@@ -89,7 +89,8 @@ def parse():
     ap.add_argument("--write-profiles", nargs="+", metavar="DIR",
                     help="summarize rocprofv3 CSV output of this benchmark into profiles/ and exit: "
                          "TRACE_DIR [FETCH_DIR WRITE_DIR]")
-    ap.add_argument("--workload", choices=["llama", "c0", "wide", "c3", "gather", "qmm", "moe", "layer", "calib"],
+    ap.add_argument("--workload", choices=["llama", "c0", "wide", "c3", "gather", "qmm", "moe", "layer", "nvfp4",
+                                                  "calib"],
                     default="llama")
     ap.add_argument("--calls", type=int, default=200, help="calls per timed loop of one shape")
     return ap.parse_args()
@@ -301,11 +302,11 @@ WORKLOAD_FLAGS = {"llama": "--steps 20 --repeats 3 --no-cpu-baseline --no-calib 
                   "c0": "--workload c0 --calls 100", "wide": "--workload wide --calls 40",
                   "c3": "--workload c3 --calls 100", "gather": "--workload gather --calls 40",
                   "qmm": "--workload qmm --calls 20", "moe": "--workload moe",
-                  "layer": "--workload layer --calls 40 --no-calib"}
+                  "layer": "--workload layer --calls 40 --no-calib", "nvfp4": "--workload nvfp4 --calls 40"}
 PMC_FLAGS = {"llama": "--steps 5 --repeats 1 --warmup 2 --warm-seconds 0 --no-cpu-baseline --no-calib --no-graph",
              "c0": "--workload c0 --calls 8", "wide": "--workload wide --calls 8", "c3": "--workload c3 --calls 8",
              "gather": "--workload gather --calls 8", "qmm": "--workload qmm --calls 4", "moe": "--workload moe",
-             "layer": "--workload layer --calls 8 --no-calib"}
+             "layer": "--workload layer --calls 8 --no-calib", "nvfp4": "--workload nvfp4 --calls 8 --no-calib"}
 TITLES = {"llama": "Llama-3-8B-shaped decode GEMV set, batch 1, 4-bit gs64",
           "c0": "single product 4096x4096, batch 1, 4-bit gs64",
           "wide": "small-batch products 14336x4096 and 4096x14336 at M = 2, 4, 6, 8 (4-bit gs64)",
@@ -318,7 +319,9 @@ TITLES = {"llama": "Llama-3-8B-shaped decode GEMV set, batch 1, 4-bit gs64",
                  "unfused (4-bit gs64)",
           "layer": "Llama-shaped decode layer projections through the fused batch-1 kernel (norm + qkv, "
                    "o + residual, norm + gate/up + SwiGLU, down + residual, final norm + lm_head), against the "
-                   "bare products and the unfused sequence (4-bit gs64)"}
+                   "bare products and the unfused sequence (4-bit gs64)",
+          "nvfp4": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, NVFP4 weights (E2M1 codes, E4M3 scale per "
+                   "16 columns), against the affine 4-bit gs64 product on the same shapes"}
 
 
 def write_profiles(workload, dirs):
@@ -330,7 +333,7 @@ def write_profiles(workload, dirs):
     other workloads reuse the factors recorded with the llama counters."""
     name = {"llama": "qmv_llama_decode_set", "c0": "qmv_c0_4096x4096", "wide": "qmv_wide", "c3": "qmv_c3_8bit",
             "gather": "qmv_gather", "qmm": "qmm_prefill", "moe": "moe_decode_layer",
-            "layer": "qmv_fused_decode_layer"}[workload]
+            "layer": "qmv_fused_decode_layer", "nvfp4": "qmv_nvfp4_llama_decode_set"}[workload]
     stats = _read_csv(dirs[0], "kernel_stats.csv")
     trace = _read_csv(dirs[0], "kernel_trace.csv")
     cmd = f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- python3 bench.py " \
@@ -355,7 +358,8 @@ def write_profiles(workload, dirs):
         if "agq::" in r["Kernel_Name"]:
             by_grid.setdefault((r["Kernel_Name"].split("(")[0].replace("void ", ""), int(r["Grid_Size_X"])),
                                []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines += ["", "Per launch shape (grid size in threads):", "",
+    lines += ["", "Per launch shape (grid size in threads; grids are sized by occupancy, not by N, so one kernel "
+              "and grid can serve several shapes of a workload, and then its row pools their launches):", "",
               "| kernel | grid | launches | median us | mean us |", "|---|---|---|---|---|"]
     for (k, g), d in sorted(by_grid.items(), key=lambda kv: -statistics.median(kv[1])):
         lines.append(f"| `{k}` | {g} | {len(d)} | {statistics.median(d):.2f} | {statistics.mean(d):.2f} |")
@@ -488,6 +492,9 @@ def other_workload(args):
         return
     if args.workload == "layer":
         layer_workload(args, torch, si, agq, bf16, u32, stream, calib, emit)
+        return
+    if args.workload == "nvfp4":
+        nvfp4_workload(args, torch, si, agq, bf16, u32, stream, calib, emit)
         return
 
     if args.workload in ("c0", "c3"):
@@ -728,6 +735,63 @@ def layer_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
           **{f"{k}_us": round(v, 3) for k, v in tot.items()},
           "fused_over_bare": round(tot["fused"] / tot["bare"], 4),
           "unfused_over_fused": round(tot["unfused"] / tot["fused"], 3)})
+
+
+def nvfp4_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
+    """Workload 1's five products with NVFP4 weights at M = 1 and 4, each against the affine
+    4-bit gs64 product (agq_qmv / agq_qmv_wide) on the same shape and activations. Both
+    formats carry N*K/2 code bytes and N*K/16 scale bytes, so the algorithmic bytes match.
+    The NVFP4 weights are nvfp4_weight rows (stream cfg 12) drawn for at most 4096 rows and
+    repeated down to N: every code word costs the kernel the same fixed-latency converts and
+    nothing branches on a value, so the timing does not depend on the values, and drawing
+    all 128256 lm_head rows would cost the host about 40 s."""
+    import numpy as np
+    wl = si.workload(1)
+    st = stream.cuda_stream
+    dev = stream.device
+    tot = {}
+    for t, name, N, K, _, xname in si.WORKLOADS[1]["w"]:
+        base = si.nvfp4_weight(12, t, min(N, 4096), K)
+        reps = -(-N // base["w"].shape[0])
+        w_h = np.tile(base["w"], (reps, 1))[:N]
+        s_h = np.tile(base["scales"], (reps, 1))[:N]
+        ts = base["tensor_scale"]
+        nb_w = N * K // 2 + N * K // 16
+        rot = max(2, math.ceil(ROTATION_BYTES / nb_w))
+        w0 = u32(w_h)
+        s0 = torch.from_numpy(np.ascontiguousarray(s_h)).to(dev)
+        fp4 = [(w0, s0)] + [(w0.clone(), s0.clone()) for _ in range(rot - 1)]
+        fptr = [(a.data_ptr(), b.data_ptr()) for a, b in fp4]
+        del w_h, s_h
+        m = wl[name]
+        aff = rotation(u32, bf16, m, weight_bytes(N, K, 4))
+        aptr = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr()) for c in aff]
+        arot = len(aff)
+        xall = bf16(si.draw_activations(12, 100 + t, 4, K))
+        for M in (1, 4):
+            x = xall[:M].contiguous()
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            agq.qmv_nvfp4(x, *fp4[0], ts, out=y)  # validates the operands once
+            xp, yp = x.data_ptr(), y.data_ptr()
+            nb = algo_bytes(N, K, 4, M)
+            ceil = calib.ceiling(nb) if calib else None
+            us, us_min = time_shape(torch, lambda i: agq.lib.agq_qmv_nvfp4(xp, *fptr[i % rot], ts, yp, M, N, K, st),
+                                    args.calls, 5, stream)
+            emit(shape_line(f"nvfp4: {name} {N}x{K} M={M}", us, us_min, nb, None, ceil))
+            if M == 1:
+                aff_fn = lambda i: agq.lib.agq_qmv(xp, *aptr[i % arot], yp, N, K, 4, 64, st)  # noqa: E731
+            else:
+                aff_fn = lambda i: agq.lib.agq_qmv_wide(xp, *aptr[i % arot], yp, M, N, K, 4, 64, st)  # noqa
+            ua, ua_min = time_shape(torch, aff_fn, args.calls, 5, stream)
+            emit(shape_line(f"affine: {name} {N}x{K} M={M}", ua, ua_min, nb, agq.launch_plan(M, N, K, 4), ceil))
+            for kind, v in (("nvfp4", us), ("affine", ua)):
+                tot[f"{kind}_m{M}_us"] = tot.get(f"{kind}_m{M}_us", 0.0) + v
+        del fp4, aff
+        torch.cuda.empty_cache()
+    emit({"set": "Llama-shaped decode products, NVFP4 against affine 4-bit gs64",
+          **{k: round(v, 3) for k, v in tot.items()},
+          "nvfp4_over_affine_m1": round(tot["nvfp4_m1_us"] / tot["affine_m1_us"], 4),
+          "nvfp4_over_affine_m4": round(tot["nvfp4_m4_us"] / tot["affine_m4_us"], 4)})
 
 
 # ----------------------------------------------------------------------------- main workload
