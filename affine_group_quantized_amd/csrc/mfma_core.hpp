@@ -208,20 +208,20 @@ __device__ __forceinline__ void load_seg(Seg<T, XQ> &u, ScaleBlock<T> &sb, const
 // Fold one segment into the band's accumulators. sd/bd: the bf16 scale and
 // bias pairs of the segment's two groups for the lane's row of each tile.
 template <int T, int XQ>
-__device__ __forceinline__ void compute_seg(const Seg<T, XQ> &u, const u32x4 (&w)[T], const uint32_t (&sd)[T],
+__device__ __forceinline__ void compute_seg(const u32x4 *ux, const u32x4 (&w)[T], const uint32_t (&sd)[T],
                                             const uint32_t (&bd)[T], f32x4 (&acc)[T], const u32x4 *ax) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
     u32x4 a[4];
     if constexpr (XQ == 1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = act_pairs(u.x[i]);
+        for (int i = 0; i < 4; ++i) a[i] = act_pairs(ux[i]);
     } else if constexpr (XQ == 2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[i] = ax[i];
     } else {
         static_assert(XQ == 4, "activation loads: 4 full loads (XQ 1), staged (XQ 2) or compact (XQ 4)");
-        a[0] = act_pairs(u.x[0]);
+        a[0] = act_pairs(ux[0]);
         a[1] = row_ror<12>(a[0]);
         a[2] = row_ror<8>(a[0]);
         a[3] = row_ror<4>(a[0]);
@@ -254,21 +254,41 @@ __device__ __forceinline__ void compute_seg(const Seg<T, XQ> &u, const u32x4 (&w
 // the wave's LDS buffer and reads back its own row and quarter of either
 // segment. Slots are XOR-swizzled so that neither the writes nor the reads
 // conflict. A wave's LDS accesses complete in order, so the buffer needs no
-// barrier.
-template <int T, int XQ>
-__device__ __forceinline__ void compute_pair(const Seg<T, XQ> &u0, const Seg<T, XQ> &u1, const uint32_t (&sd0)[T],
+// barrier. Once the pair's codes (and staged activations) sit in LDS, its
+// registers are free: `reload` issues the loads of the ring's next turn into
+// them before the arithmetic, so the refill waits for the data, not for the
+// compute (4096x14336 at M = 4 / 8: 12.75 / 13.16 -> 11.82 / 12.49 us).
+template <int T, int XQ, typename Reload>
+__device__ __forceinline__ void compute_pair(Seg<T, XQ> &u0, Seg<T, XQ> &u1, const uint32_t (&sd0)[T],
                                              const uint32_t (&bd0)[T], const uint32_t (&sd1)[T],
-                                             const uint32_t (&bd1)[T], f32x4 (&acc)[T], const Lanes &ln, u32x4 *wt) {
+                                             const uint32_t (&bd1)[T], f32x4 (&acc)[T], const Lanes &ln, u32x4 *wt,
+                                             Reload &&reload) {
     u32x4 a0[XQ == 2 ? 4 : 1], a1[XQ == 2 ? 4 : 1];
+    u32x4 *xs = wt + T * 128;
     if constexpr (XQ == 2) {
-        // Staged activations: both segments' rows, already in A operand form,
-        // through the 4 KB after the wave's code buffer, then each lane's slots.
-        u32x4 *xs = wt + T * 128;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             xs[ln.xw[k]] = act_pairs(u0.x[k]);
             xs[128 + ln.xw[k]] = act_pairs(u1.x[k]);
         }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        wt[t * 128 + ln.wslot[0]] = u0.w[t];
+        wt[t * 128 + ln.wslot[1]] = u1.w[t];
+    }
+    // The activation words of the compact and four-load forms stay in registers.
+    u32x4 x0[XQ == 2 ? 1 : 4 / XQ], x1[XQ == 2 ? 1 : 4 / XQ];
+    if constexpr (XQ != 2) {
+#pragma unroll
+        for (int i = 0; i < 4 / XQ; ++i) {
+            x0[i] = u0.x[i];
+            x1[i] = u1.x[i];
+        }
+    }
+    // The pair's buffers are free: the next loads go out before the arithmetic.
+    reload();
+    if constexpr (XQ == 2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             a0[i] = xs[ln.xrd[i]];
@@ -278,16 +298,11 @@ __device__ __forceinline__ void compute_pair(const Seg<T, XQ> &u0, const Seg<T, 
     u32x4 w0[T], w1[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        wt[t * 128 + ln.wslot[0]] = u0.w[t];
-        wt[t * 128 + ln.wslot[1]] = u1.w[t];
-    }
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
         w0[t] = wt[t * 128 + ln.rslot[0]];
         w1[t] = wt[t * 128 + ln.rslot[1]];
     }
-    compute_seg<T, XQ>(u0, w0, sd0, bd0, acc, a0);
-    compute_seg<T, XQ>(u1, w1, sd1, bd1, acc, a1);
+    compute_seg<T, XQ>(x0, w0, sd0, bd0, acc, a0);
+    compute_seg<T, XQ>(x1, w1, sd1, bd1, acc, a1);
 }
 
 __device__ __forceinline__ uint32_t dword(const u32x4 &v, int j) {
@@ -384,12 +399,13 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
                 sd1[t] = dword(cur.s[t], (p + 1) % kSB);
                 bd1[t] = dword(cur.b[t], (p + 1) % kSB);
             }
-            compute_pair<T, XQ>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, ln, wt);
-            if (p % kSB == 0)
-                load_seg<T, true, XQ, DUAL>(buf[p], next[p / kSB], bd, ln, xr, nband, nseg + p);
-            else
-                load_seg<T, false, XQ, DUAL>(buf[p], next[0], bd, ln, xr, nband, nseg + p);
-            load_seg<T, false, XQ, DUAL>(buf[p + 1], next[0], bd, ln, xr, nband, nseg + p + 1);
+            compute_pair<T, XQ>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, ln, wt, [&] {
+                if (p % kSB == 0)
+                    load_seg<T, true, XQ, DUAL>(buf[p], next[p / kSB], bd, ln, xr, nband, nseg + p);
+                else
+                    load_seg<T, false, XQ, DUAL>(buf[p], next[0], bd, ln, xr, nband, nseg + p);
+                load_seg<T, false, XQ, DUAL>(buf[p + 1], next[0], bd, ln, xr, nband, nseg + p + 1);
+            });
             __builtin_amdgcn_sched_barrier(0);
         }
         if ((j + 1) % tpb == 0) finish_band<T, MAXS>(acc, red, S, wig, lane, band, bi & 1, bd.N, mrows, out);
@@ -408,7 +424,7 @@ __device__ __forceinline__ void mfma_pass(const MfmaArgs &a, const Band &bd, con
                 sd1[t] = dword(cur.s[t], (p + 1) % kSB);
                 bd1[t] = dword(cur.b[t], (p + 1) % kSB);
             }
-            compute_pair<T, XQ>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, ln, wt);
+            compute_pair<T, XQ>(buf[p], buf[p + 1], sd0, bd0, sd1, bd1, acc, ln, wt, [] {});
         }
         finish_band<T, MAXS>(acc, red, S, wig, lane, band, bi & 1, bd.N, mrows, out);
     }
