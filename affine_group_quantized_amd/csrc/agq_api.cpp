@@ -539,8 +539,8 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
         return launch(sym, dim3((unsigned)mp.groups, (unsigned)passes), dim3(mp.threads), (size_t)mp.lds_bytes, &a,
                       stream);
     }
-    // (Checked for the smaller tile's grid, the larger of the two.)
-    if ((int64_t)agq::kQmmTileN * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
+    // (The weight range for the widest tile; the grid for the smallest.)
+    if ((int64_t)agq::kQmmHlTileN * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
     if ((M + agq::kQmmTileMinM - 1) / agq::kQmmTileMinM > 65535 || (N + agq::kQmmTileN - 1) / agq::kQmmTileN > INT32_MAX)
         return fail(AGQ_ENOTSUP, "grid too large (M=%lld, N=%lld)", (long long)M, (long long)N);
     int cus = 0, dev = 0;
@@ -560,6 +560,8 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
     a.G = (int32_t)(K / 64);
     a.rowbytes = (int32_t)(K * bits / 8);
     a.xbytes = (uint32_t)(M * K * 2);
+    st = allow_lds(k.sym, (size_t)k.lds, dev);
+    if (st != AGQ_OK) return st;
     return launch(k.sym, dim3((unsigned)nt, (unsigned)mt), dim3(256), (size_t)k.lds, &a, stream);
 }
 
@@ -580,7 +582,7 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
     if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
     if (R * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (R*K*2 bytes)");
     if (group_size != 64) return fail(AGQ_ENOTSUP, "gather_qmm takes group size 64");
-    if ((int64_t)agq::kQmmTileN * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
+    if ((int64_t)agq::kQmmHlTileN * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
     if ((N + agq::kQmmTileN - 1) / agq::kQmmTileN > INT32_MAX) return fail(AGQ_ENOTSUP, "N too large");
     int cus = 0, dev = 0;
     st = current_device(&cus, &dev);

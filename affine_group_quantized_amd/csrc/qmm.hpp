@@ -22,6 +22,12 @@ namespace agq {
 constexpr int kQmmSmallM = 128;
 constexpr int kQmmSmallPairs = 64;
 constexpr int kQmmLargeBlocksPerCu = 2;
+// Split-weight tiles (256 x 128, qmm_hl_kernel) from this many rows, where
+// their grid gives every compute unit a block (4-bit, us: 4096x4096 at M =
+// 2048: 157 -> 136; 28672x4096 at M = 512 / 2048: 326 / 1221 -> 279 / 994;
+// 4096x14336 at M = 2048: 554 -> 446). With 128-row tiles they lost at M =
+// 256 (28672x4096: 167 -> 221) and on the Mixtral prefill gather (430 -> 665).
+constexpr int kQmmHlMinRows = 256;
 constexpr int kQmmPassRows = 128;  // 4-bit products of up to this many rows run on the matvec kernel in passes of 16
 
 // Passed by value as the single kernel argument.
@@ -56,5 +62,6 @@ QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t
 // Tile geometry shared by both shapes (the host checks use it before any HIP call).
 constexpr int kQmmTileN = 64;
 constexpr int kQmmTileMinM = 64;
+constexpr int kQmmHlTileN = 128;  // weight rows of the large tiles (the widest tile)
 
 }  // namespace agq

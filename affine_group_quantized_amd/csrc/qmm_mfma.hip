@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qmm.hpp"
 #include "qmv_device.hpp"
 
@@ -346,6 +348,238 @@ __device__ __forceinline__ void qmm_tile(const QmmArgs &a, const Map &map, const
         }
 }
 
+// ---------------------------------------------------------------------------
+// Large tiles: the dequantized weight split into two bfloat16 parts.
+//
+// Where a grid of large tiles fills the device, the per-group fp32 correction
+// above costs more issue time than the matrix cores spend on the group. These
+// kernels take the weight itself to the matrix cores instead: each weight is
+// dequantized once per block, w = fma(s, q, b) in fp32 (the value
+// agq_dequantize writes), and split into w = hi + lo with hi = bf16(w) and
+// lo = bf16(w - hi). Both parts go to the B operand, so every 16x16x32 product
+// runs twice (hi, lo) and accumulates across all of K in the same registers:
+// no per-group fold and no sums of x. hi + lo holds 16 significant bits of w,
+// all of them whenever w needs at most 16 (every weight of the quantizer's
+// recipe needs at most 12 at 4 bits and 16 at 8 bits); otherwise the weight
+// is off by at most 2^-17 of itself. Infinite weights give NaN (lo = inf - inf).
+//
+// A block of 4 waves (2 x 2) computes BM = 32*TMW activation rows by 128
+// weight rows; wave (wm, wn) owns 16*TMW x 64. K advances one 64-column group
+// at a time: per group the block stages x (BM rows x 8 words of 8 columns,
+// natural order) and the weights' hi and lo parts (128 rows x 8 words each)
+// into LDS, word w of a row at slot w ^ (row & 7). Each thread dequantizes 32
+// columns of one weight row. Global loads run two groups ahead in registers;
+// the LDS buffers are double buffered (one block barrier per group).
+template <int BITS, int TMW>
+struct Hl {
+    static constexpr int BM = 32 * TMW, BN = 128, THREADS = 256;
+    static constexpr int LDS_X = BM * 128, LDS_B = BN * 128;
+    static constexpr int LDS_BUF = LDS_X + 2 * LDS_B;
+};
+
+template <int BITS, int TMW>
+struct HlStage {
+    u32x4 w[BITS / 4];  // the thread's 32 codes (4-bit: 16 bytes; 8-bit: 32 bytes)
+    uint16_t s, b;
+};
+// Vector-memory instructions of one hl_load (codes, scale, bias).
+template <int BITS>
+constexpr int kHlLoads = BITS / 4 + 2;
+
+// x of group grp into the LDS buffer's x tile with direct-to-LDS loads: wave w
+// writes 1 KB chunks c = w, w + 4, ... (rows 8c .. 8c + 7); lane L of a chunk
+// fills slot L % 8 of row 8c + L / 8, so it fetches that row's word
+// (L % 8) ^ (L / 8). Rows past the tile (or the pass) read zero.
+template <int BITS, int TMW, typename Map>
+__device__ __forceinline__ void hl_load_x(const QmmArgs &a, const Map &map, __amdgpu_buffer_rsrc_t xr, int grp,
+                                          uint8_t *buf) {
+    using H = Hl<BITS, TMW>;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int k = 0; k < H::BM / 32; ++k) {
+        const int c = wave + 4 * k;
+        const int row = 8 * c + (lane >> 3);
+        const int word = (lane & 7) ^ (lane >> 3);
+        const int64_t xrow = map.xrow(row);
+        const uint32_t off = xrow >= 0 ? (uint32_t)(xrow * a.K + grp * 64 + word * 8) * 2u : a.xbytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xr, (__attribute__((address_space(3))) void *)(buf + c * 1024), 16, off, 0, 0, 0);
+    }
+}
+
+template <int BITS, int TMW>
+__device__ __forceinline__ void hl_load(HlStage<BITS, TMW> &st, const QmmArgs &a, __amdgpu_buffer_rsrc_t wr,
+                                        __amdgpu_buffer_rsrc_t sr, __amdgpu_buffer_rsrc_t br, int grp) {
+    const int t = threadIdx.x;
+    // Weight row t / 2, columns 32 * (t % 2) .. +32 of the group.
+    const uint32_t r = (uint32_t)t >> 1, h = (uint32_t)t & 1u;
+#pragma unroll
+    for (int c = 0; c < BITS / 4; ++c) {
+        const uint32_t off = r * (uint32_t)a.rowbytes + (uint32_t)grp * (uint32_t)(8 * BITS) + h * (uint32_t)(4 * BITS) +
+                             (uint32_t)c * 16u;
+        st.w[c] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);
+    }
+    const uint32_t soff = (r * (uint32_t)a.G + (uint32_t)grp) * 2u;
+    st.s = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
+    st.b = __builtin_amdgcn_raw_buffer_load_b16(br, soff, 0, 0);
+}
+
+// (hi, lo) bfloat16 pairs of the fp32 pair (v0, v1): hi = bf16(v), lo = bf16(v - hi).
+__device__ __forceinline__ void hl_split(float v0, float v1, uint32_t &hp, uint32_t &lp) {
+    const f32x2 v = {v0, v1};
+    hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    const f32x2 l = {v0 - __uint_as_float(hp << 16), v1 - __uint_as_float(hp & 0xFFFF0000u)};
+    lp = __builtin_bit_cast(uint32_t, __builtin_convertvector(l, bf16x2));
+}
+
+template <int BITS, int TMW>
+__device__ __forceinline__ void hl_store(const HlStage<BITS, TMW> &st, uint8_t *buf) {
+    using H = Hl<BITS, TMW>;
+    u32x4 *bh = reinterpret_cast<u32x4 *>(buf + H::LDS_X);
+    u32x4 *bl = reinterpret_cast<u32x4 *>(buf + H::LDS_X + H::LDS_B);
+    const int t = threadIdx.x;
+    const float sf = bf16_lo(st.s), bfv = bf16_lo(st.b);
+    const int r = t >> 1, h = t & 1;
+    const uint32_t d[8] = {st.w[0].x, st.w[0].y, st.w[0].z, st.w[0].w,
+                           BITS == 8 ? st.w[BITS / 4 - 1].x : 0u, BITS == 8 ? st.w[BITS / 4 - 1].y : 0u,
+                           BITS == 8 ? st.w[BITS / 4 - 1].z : 0u, BITS == 8 ? st.w[BITS / 4 - 1].w : 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // B word 4h + j: columns 8j .. 8j + 7 of the thread's 32
+        float v[8];
+        if constexpr (BITS == 4) {
+            // codes low-first: byte i of the word holds columns 2i (low nibble) and 2i + 1
+            const uint32_t lo = d[j] & 0x0F0F0F0Fu, hi = (d[j] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = fmaf(sf, (float)((lo >> (8 * i)) & 0xFFu), bfv);
+                v[2 * i + 1] = fmaf(sf, (float)((hi >> (8 * i)) & 0xFFu), bfv);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] = fmaf(sf, (float)((d[2 * j] >> (8 * i)) & 0xFFu), bfv);
+                v[4 + i] = fmaf(sf, (float)((d[2 * j + 1] >> (8 * i)) & 0xFFu), bfv);
+            }
+        }
+        uint32_t hp[4], lp[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) hl_split(v[2 * p], v[2 * p + 1], hp[p], lp[p]);
+        const int word = 4 * h + j;
+        bh[r * 8 + (word ^ (r & 7))] = u32x4{hp[0], hp[1], hp[2], hp[3]};
+        bl[r * 8 + (word ^ (r & 7))] = u32x4{lp[0], lp[1], lp[2], lp[3]};
+    }
+}
+
+// One group's products: for each of the two 32-column steps, the wave's TMW x 4
+// sub-tiles take the hi and then the lo part into their accumulators.
+template <int BITS, int TMW>
+__device__ __forceinline__ void hl_compute(const uint8_t *buf, int wm, int wn, f32x4 (&acc)[TMW][4]) {
+    using H = Hl<BITS, TMW>;
+    const u32x4 *xs = reinterpret_cast<const u32x4 *>(buf);
+    const u32x4 *bh = reinterpret_cast<const u32x4 *>(buf + H::LDS_X);
+    const u32x4 *bl = reinterpret_cast<const u32x4 *>(buf + H::LDS_X + H::LDS_B);
+    const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+        const int word = 4 * step + g;
+        u32x4 av[TMW], hv[4], lv[4];
+#pragma unroll
+        for (int m = 0; m < TMW; ++m) {
+            const int row = wm * 16 * TMW + 16 * m + i;
+            av[m] = xs[row * 8 + (word ^ (row & 7))];
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int row = wn * 64 + 16 * n + i;
+            hv[n] = bh[row * 8 + (word ^ (row & 7))];
+            lv[n] = bl[row * 8 + (word ^ (row & 7))];
+        }
+        // All hi products, then all lo products: each accumulator's second product
+        // issues TMW*4 instructions after its first.
+#pragma unroll
+        for (int m = 0; m < TMW; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[m][n] = mma(av[m], hv[n], acc[m][n]);
+#pragma unroll
+        for (int m = 0; m < TMW; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[m][n] = mma(av[m], lv[n], acc[m][n]);
+    }
+}
+
+template <int BITS, int TMW, typename Map>
+__device__ __forceinline__ void hl_tile(const QmmArgs &a, const Map &map, const uint32_t *w, const uint16_t *s,
+                                        const uint16_t *b, int64_t n0, uint8_t *lds) {
+    using H = Hl<BITS, TMW>;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
+    const int64_t nrows = a.N - n0 < H::BN ? a.N - n0 : H::BN;
+    const __amdgpu_buffer_rsrc_t xr = span(a.x, a.xbytes);
+    const __amdgpu_buffer_rsrc_t wr = span(w + n0 * (a.rowbytes / 4), (uint32_t)(nrows * a.rowbytes));
+    const __amdgpu_buffer_rsrc_t sr = span(s + n0 * a.G, (uint32_t)(nrows * a.G * 2));
+    const __amdgpu_buffer_rsrc_t br = span(b + n0 * a.G, (uint32_t)(nrows * a.G * 2));
+
+    f32x4 acc[TMW][4];
+#pragma unroll
+    for (int m = 0; m < TMW; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // LDS buffer p holds the groups of parity p. One register stage of codes: it
+    // holds the group after the one being computed, is dequantized into the other
+    // buffer, and is at once reloaded with the group two ahead, so each load has a
+    // whole group's products to arrive. The x tile of the next group goes straight
+    // to LDS at the start of the group, once the buffer's last readers have passed
+    // the barrier; the wait before the next barrier leaves the code loads issued
+    // after it in flight. The loop body is branch-free: stores and loads past the
+    // last group repeat the last one into a buffer nothing reads again.
+    HlStage<BITS, TMW> st;
+    const int last = a.G - 1;
+    hl_load_x<BITS, TMW>(a, map, xr, 0, lds);
+    hl_load<BITS, TMW>(st, a, wr, sr, br, 0);
+    hl_store<BITS, TMW>(st, lds);
+    hl_load<BITS, TMW>(st, a, wr, sr, br, last < 1 ? last : 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kHlLoads<BITS>);  // vmcnt(loads of st): x has landed
+    __syncthreads();
+    auto step = [&](auto pc, int nxt) {
+        constexpr int P = decltype(pc)::value;
+        hl_load_x<BITS, TMW>(a, map, xr, nxt - 1 < last ? nxt - 1 : last, lds + (P ^ 1) * H::LDS_BUF);
+        hl_compute<BITS, TMW>(lds + P * H::LDS_BUF, wm, wn, acc);
+        hl_store<BITS, TMW>(st, lds + (P ^ 1) * H::LDS_BUF);
+        hl_load<BITS, TMW>(st, a, wr, sr, br, nxt < last ? nxt : last);
+        // Interleave the dequantization with the matrix-core products.
+#pragma unroll
+        for (int k = 0; k < 8 * TMW; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kHlLoads<BITS>);  // the next x tile has landed
+        __syncthreads();
+    };
+    int grp0 = 0;
+    for (; grp0 + 2 <= a.G; grp0 += 2) {
+        step(std::integral_constant<int, 0>{}, grp0 + 2);
+        step(std::integral_constant<int, 1>{}, grp0 + 3);
+    }
+    if (grp0 < a.G) hl_compute<BITS, TMW>(lds, wm, wn, acc);  // odd G: the last group, in buffer 0
+
+    // Store: lane holds rows 4g + r of sub-tile m, weight row i of sub-tile n.
+#pragma unroll
+    for (int m = 0; m < TMW; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t yr = map.yrow(wm * 16 * TMW + 16 * m + 4 * g + r);
+            if (yr < 0) continue;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int64_t col = wn * 64 + 16 * n + i;
+                if (col < nrows) a.y[yr * a.N + n0 + col] = f32_to_bf16(acc[m][n][r]);
+            }
+        }
+}
+
 }  // namespace
 
 // Dense: blockIdx.x = weight-row tile, blockIdx.y = activation-row tile.
@@ -357,21 +591,25 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
     qmm_tile<BITS, TM, TN, DEPTH, TT::PIPE>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * TT::BN, qmm_lds);
 }
 
-// Gather: blockIdx.x = weight-row tile, blockIdx.y = expert plane e. The
-// block lists the pairs routed to e (ascending p) and walks them BM at a
-// time. Blocks of plane 0 also write NaN rows for pairs whose indices are out
-// of range. LDS after the tile buffers: pair list (uint16) and x rows (uint32).
-template <int BITS, int TM, int TN, int DEPTH>
-__global__ __launch_bounds__(256) void gather_qmm_kernel(QmmArgs a) {
+// Large tiles, dense: blockIdx.x = 128-row weight tile, blockIdx.y = activation-row tile.
+template <int BITS, int TMW>
+__global__ __launch_bounds__(256) void qmm_hl_kernel(QmmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
-    using TT = Tile<BITS, TM, TN>;
-    uint16_t *plist = reinterpret_cast<uint16_t *>(qmm_lds + 2 * TT::LDS_BUF);
-    uint32_t *xlist = reinterpret_cast<uint32_t *>(qmm_lds + 2 * TT::LDS_BUF + ((a.M * 2 + 15) / 16) * 16);
-    __shared__ int wave_counts[4];
+    const DenseMap map{(int64_t)blockIdx.y * Hl<BITS, TMW>::BM, a.M};
+    hl_tile<BITS, TMW>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * Hl<BITS, TMW>::BN, qmm_lds);
+}
+
+namespace {
+
+// The gather's pair lists for plane blockIdx.y, in ascending p: plist holds the
+// pairs routed to the plane with an in-range x row, xlist their x rows; the
+// return value is their count. Blocks of plane 0 first write NaN over columns
+// [n0, n0 + bn) of the rows of pairs whose indices are out of range.
+__device__ __forceinline__ int gather_pairs(const QmmArgs &a, uint16_t *plist, uint32_t *xlist, int *wave_counts,
+                                            int64_t n0, int bn) {
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const uint32_t e = blockIdx.y;
-    const int64_t n0 = (int64_t)blockIdx.x * TT::BN;
     const uint32_t nx = (uint32_t)a.R_x, ne = (uint32_t)a.E;
 
     // Block-wide ordered compaction of the pairs p < P that satisfy pred into plist.
@@ -398,7 +636,7 @@ __global__ __launch_bounds__(256) void gather_qmm_kernel(QmmArgs a) {
             return xr >= nx || ex >= ne;
         });
         for (int k = 0; k < nbad; ++k)
-            for (int c = t; c < TT::BN; c += 256)
+            for (int c = t; c < bn; c += 256)
                 if (n0 + c < a.N) a.y[(int64_t)plist[k] * a.N + n0 + c] = 0x7FC0u;
         __syncthreads();
     }
@@ -409,13 +647,52 @@ __global__ __launch_bounds__(256) void gather_qmm_kernel(QmmArgs a) {
     });
     for (int k = t; k < count; k += 256) xlist[k] = a.lhs ? a.lhs[plist[k]] : (uint32_t)plist[k];
     __syncthreads();
+    return count;
+}
+
+}  // namespace
+
+// Gather: blockIdx.x = weight-row tile, blockIdx.y = expert plane e. The
+// block lists the pairs routed to e (ascending p) and walks them BM at a
+// time. Blocks of plane 0 also write NaN rows for pairs whose indices are out
+// of range. LDS after the tile buffers: pair list (uint16) and x rows (uint32).
+template <int BITS, int TM, int TN, int DEPTH>
+__global__ __launch_bounds__(256) void gather_qmm_kernel(QmmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
+    using TT = Tile<BITS, TM, TN>;
+    uint16_t *plist = reinterpret_cast<uint16_t *>(qmm_lds + 2 * TT::LDS_BUF);
+    uint32_t *xlist = reinterpret_cast<uint32_t *>(qmm_lds + 2 * TT::LDS_BUF + ((a.M * 2 + 15) / 16) * 16);
+    __shared__ int wave_counts[4];
+    const int64_t n0 = (int64_t)blockIdx.x * TT::BN;
+    const int count = gather_pairs(a, plist, xlist, wave_counts, n0, TT::BN);
     if (count == 0) return;
-    const int64_t plane = (int64_t)e * a.N;
+    const int64_t plane = (int64_t)blockIdx.y * a.N;
     const uint32_t *w = a.w + plane * (a.rowbytes / 4);
     const uint16_t *s = a.s + plane * a.G, *b = a.b + plane * a.G;
     for (int base = 0; base < count; base += TT::BM) {
         const GatherMap map{plist + base, xlist + base, count - base < TT::BM ? count - base : TT::BM};
         qmm_tile<BITS, TM, TN, DEPTH, TT::PIPE>(a, map, w, s, b, n0, qmm_lds);
+        __syncthreads();  // the LDS tiles are refilled by the next pass
+    }
+}
+
+// Large tiles, gathered (as gather_qmm_kernel).
+template <int BITS, int TMW>
+__global__ __launch_bounds__(256) void gather_qmm_hl_kernel(QmmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
+    using H = Hl<BITS, TMW>;
+    uint16_t *plist = reinterpret_cast<uint16_t *>(qmm_lds + 2 * H::LDS_BUF);
+    uint32_t *xlist = reinterpret_cast<uint32_t *>(qmm_lds + 2 * H::LDS_BUF + ((a.M * 2 + 15) / 16) * 16);
+    __shared__ int wave_counts[4];
+    const int64_t n0 = (int64_t)blockIdx.x * H::BN;
+    const int count = gather_pairs(a, plist, xlist, wave_counts, n0, H::BN);
+    if (count == 0) return;
+    const int64_t plane = (int64_t)blockIdx.y * a.N;
+    const uint32_t *w = a.w + plane * (a.rowbytes / 4);
+    const uint16_t *s = a.s + plane * a.G, *b = a.b + plane * a.G;
+    for (int base = 0; base < count; base += H::BM) {
+        const GatherMap map{plist + base, xlist + base, count - base < H::BM ? count - base : H::BM};
+        hl_tile<BITS, TMW>(a, map, w, s, b, n0, qmm_lds);
         __syncthreads();  // the LDS tiles are refilled by the next pass
     }
 }
@@ -434,9 +711,26 @@ static QmmKernel qmm_pick(bool gather) {
     return k;
 }
 
+template <int BITS, int TMW>
+static QmmKernel hl_pick(bool gather) {
+    QmmKernel k;
+    k.sym = gather ? reinterpret_cast<const void *>(&gather_qmm_hl_kernel<BITS, TMW>)
+                   : reinterpret_cast<const void *>(&qmm_hl_kernel<BITS, TMW>);
+    k.bm = Hl<BITS, TMW>::BM;
+    k.bn = Hl<BITS, TMW>::BN;
+    k.lds = 2 * Hl<BITS, TMW>::LDS_BUF;
+    return k;
+}
+
 QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t planes, int cus) {
     static_assert(Tile<4, 2, 2>::BN == kQmmTileN && Tile<4, 4, 2>::BN == kQmmTileN && Tile<4, 2, 2>::BM == kQmmTileMinM,
                   "the host checks assume these tile sizes");
+    static_assert(Hl<4, 8>::BN == kQmmHlTileN && Hl<4, 8>::BM >= kQmmTileMinM, "the host checks assume these tile sizes");
+    // Split-weight tiles where the rows fill them and their grid gives every
+    // compute unit a block.
+    constexpr int HBM = Hl<4, 8>::BM;
+    if (rows >= kQmmHlMinRows && planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN) * ((rows + HBM - 1) / HBM) >= cus)
+        return bits == 4 ? hl_pick<4, 8>(gather) : hl_pick<8, 8>(gather);
     constexpr int LBM = Tile<4, 4, 2>::BM;
     const int64_t large_blocks = planes * ((rows + LBM - 1) / LBM) * ((N + kQmmTileN - 1) / kQmmTileN);
     const bool small = rows <= (gather ? kQmmSmallPairs : kQmmSmallM) ||

@@ -43,6 +43,10 @@ def dev_weight(d):
     (4, 17, 129, 512, False), (4, 100, 333, 2048, False), (4, 128, 1000, 14336, True), (4, 300, 200, 4096, False),
     # enough 128x64 tiles for two blocks per compute unit: the large tile
     (4, 1024, 4100, 512, True), (8, 1000, 4096, 576, True),
+    # grids of 128-row weight tiles that fill the device: the split-weight tiles
+    # (256 x 128 and 128 x 128), with ragged activation rows and weight rows
+    (4, 2048, 4096, 1024, True), (4, 1100, 33000, 256, True), (8, 2048, 4096, 512, True),
+    (8, 700, 9000, 320, True), (4, 260, 16400, 2048, True),
 ])
 def test_qmm_shapes(bits, M, N, K, sample):
     """Shapes on both tile sizes: the 128x64 tile where it gives at least two blocks per
@@ -113,6 +117,25 @@ def test_qmm_one_hot_columns_are_bitwise_weights(bits):
     assert np.array_equal(got, want.T)
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_qmm_split_weight_tiles_one_hot_bitwise(bits):
+    """On the split-weight tiles (a grid that fills the device), x = e_k gives
+    y[n] = bf16(w_hat[n, k]) bit for bit: the weights of the quantizer's recipe need at
+    most 16 significant bits, so their bfloat16 parts hi + lo hold them exactly."""
+    N, K = 8192, 1024
+    d = si.draw_quantized_weight(33, bits, N, K, bits)
+    w, s, b = dev_weight(d)
+    ref, bad = oracle.dequantize(d["w"], d["scales"], d["biases"], K, bits)
+    assert bad == 0
+    want = si.bf16_bits(ref.astype(np.float32))
+    cols = np.arange(K)
+    x = np.zeros((K, K), np.uint16)
+    x[cols, cols] = 0x3F80
+    progress(f"qmm split-weight one-hot bits={bits}")
+    got = bf16_bits_host(agq.qmm(bf16_dev(x), w, s, b, bits=bits))
+    assert np.array_equal(got, want.T)
+
+
 @pytest.fixture(scope="module")
 def moe_w1():
     progress("generating the Mixtral-shaped W1 planes")
@@ -168,6 +191,32 @@ def test_gather_qmm_edges(bits):
                           lhs_indices=u32_dev(np.arange(E, dtype=np.uint32)), bits=bits)
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits_host(y_id), bf16_bits_host(y_ex))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gather_qmm_split_weight_tiles(bits):
+    """About 512 pairs per plane on planes of 8192 rows: the split-weight tiles (256 x 128),
+    with ragged pair counts per plane, an empty plane, repeated x rows and one
+    out-of-range pair of each kind (NaN rows). Checked on tile-seam weight rows."""
+    E, N, K, R, P = 5, 8192, 256, 300, 2048
+    planes = [si.draw_quantized_weight(36, 10 * bits + e, N, K, bits) for e in range(E)]
+    st = {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+    x = si.draw_activations(36, bits, R, K)
+    rng = np.random.default_rng([36, bits])
+    rhs = rng.integers(0, E - 1, P).astype(np.uint32)  # plane E - 1 stays empty
+    lhs = rng.integers(0, R, P).astype(np.uint32)
+    lhs[5], rhs[9] = R + 1, E + 2
+    progress(f"gather_qmm split-weight tiles bits={bits}")
+    y = agq.gather_qmm(bf16_dev(x), u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"]),
+                       rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs), bits=bits)
+    torch.cuda.synchronize()
+    yh = bf16_host(y)
+    assert np.all(np.isnan(yh[5])) and np.all(np.isnan(yh[9]))
+    ok = np.array([p for p in range(P) if p not in (5, 9)])
+    rows = seam_rows(N)
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs[ok], rhs[ok], K, bits, rows=rows)
+    yg = y[torch.as_tensor(ok, device=y.device)][:, torch.as_tensor(rows, device=y.device)]
+    check_close(yg, y_ref, A, f"gather_qmm split-weight bits={bits}")
 
 
 def test_gather_qmm_at_the_pair_limit():
