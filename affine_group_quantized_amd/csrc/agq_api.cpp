@@ -562,7 +562,7 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
     a.xbytes = (uint32_t)(M * K * 2);
     st = allow_lds(k.sym, (size_t)k.lds, dev);
     if (st != AGQ_OK) return st;
-    return launch(k.sym, dim3((unsigned)nt, (unsigned)mt), dim3(256), (size_t)k.lds, &a, stream);
+    return launch(k.sym, dim3((unsigned)nt, (unsigned)mt), dim3(k.threads), (size_t)k.lds, &a, stream);
 }
 
 agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases,
@@ -608,7 +608,7 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
     const size_t lds = (size_t)k.lds + (size_t)((P * 2 + 15) / 16 * 16 + P * 4);
     st = allow_lds(k.sym, lds, dev);
     if (st != AGQ_OK) return st;
-    return launch(k.sym, dim3((unsigned)nt, (unsigned)E), dim3(256), lds, &a, stream);
+    return launch(k.sym, dim3((unsigned)nt, (unsigned)E), dim3(k.threads), lds, &a, stream);
 }
 
 int64_t agq_moe_decode_workspace(int64_t T, int64_t k, int64_t H, int64_t F) {

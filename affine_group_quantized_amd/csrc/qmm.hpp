@@ -54,6 +54,7 @@ struct QmmKernel {
     const void *sym = nullptr;
     int bm = 0, bn = 0;  // tile rows of x and of W
     int lds = 0;         // dynamic LDS bytes of the tile buffers
+    int threads = 256;   // block size
 };
 
 // The kernel for `rows` activation rows (dense M, or the gather's pairs per

@@ -392,10 +392,9 @@ constexpr int kHlLoads = BITS / 4 + 2;
 // (L % 8) ^ (L / 8). Rows past the tile (or the pass) read zero.
 template <int BITS, int TMW, typename Map>
 __device__ __forceinline__ void hl_load_x(const QmmArgs &a, const Map &map, __amdgpu_buffer_rsrc_t xr, int grp,
-                                          uint8_t *buf) {
+                                          uint8_t *buf, int wave) {
     using H = Hl<BITS, TMW>;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int k = 0; k < H::BM / 32; ++k) {
         const int c = wave + 4 * k;
@@ -410,8 +409,7 @@ __device__ __forceinline__ void hl_load_x(const QmmArgs &a, const Map &map, __am
 
 template <int BITS, int TMW>
 __device__ __forceinline__ void hl_load(HlStage<BITS, TMW> &st, const QmmArgs &a, __amdgpu_buffer_rsrc_t wr,
-                                        __amdgpu_buffer_rsrc_t sr, __amdgpu_buffer_rsrc_t br, int grp) {
-    const int t = threadIdx.x;
+                                        __amdgpu_buffer_rsrc_t sr, __amdgpu_buffer_rsrc_t br, int grp, int t) {
     // Weight row t / 2, columns 32 * (t % 2) .. +32 of the group.
     const uint32_t r = (uint32_t)t >> 1, h = (uint32_t)t & 1u;
 #pragma unroll
@@ -434,11 +432,10 @@ __device__ __forceinline__ void hl_split(float v0, float v1, uint32_t &hp, uint3
 }
 
 template <int BITS, int TMW>
-__device__ __forceinline__ void hl_store(const HlStage<BITS, TMW> &st, uint8_t *buf) {
+__device__ __forceinline__ void hl_store(const HlStage<BITS, TMW> &st, uint8_t *buf, int t) {
     using H = Hl<BITS, TMW>;
     u32x4 *bh = reinterpret_cast<u32x4 *>(buf + H::LDS_X);
     u32x4 *bl = reinterpret_cast<u32x4 *>(buf + H::LDS_X + H::LDS_B);
-    const int t = threadIdx.x;
     const float sf = bf16_lo(st.s), bfv = bf16_lo(st.b);
     const int r = t >> 1, h = t & 1;
     const uint32_t d[8] = {st.w[0].x, st.w[0].y, st.w[0].z, st.w[0].w,
@@ -513,58 +510,51 @@ __device__ __forceinline__ void hl_tile(const QmmArgs &a, const Map &map, const 
                                         const uint16_t *b, int64_t n0, uint8_t *lds) {
     using H = Hl<BITS, TMW>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
     const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
     const int64_t nrows = a.N - n0 < H::BN ? a.N - n0 : H::BN;
-    const __amdgpu_buffer_rsrc_t xr = span(a.x, a.xbytes);
-    const __amdgpu_buffer_rsrc_t wr = span(w + n0 * (a.rowbytes / 4), (uint32_t)(nrows * a.rowbytes));
-    const __amdgpu_buffer_rsrc_t sr = span(s + n0 * a.G, (uint32_t)(nrows * a.G * 2));
-    const __amdgpu_buffer_rsrc_t br = span(b + n0 * a.G, (uint32_t)(nrows * a.G * 2));
-
+    const int last = a.G - 1;
+    // Two roles, one wave of each per SIMD: waves 4-7 stage group grp + 1 into LDS
+    // buffer (grp + 1) % 2 (x with direct-to-LDS loads, the weights dequantized and
+    // split) while waves 0-3 take group grp's products out of buffer grp % 2. One
+    // block barrier per group; both roles meet it the same number of times.
+    if (wave >= 4) {
+        const int pw = wave - 4, t = threadIdx.x - 256;
+        const __amdgpu_buffer_rsrc_t xr = span(a.x, a.xbytes);
+        const __amdgpu_buffer_rsrc_t wr = span(w + n0 * (a.rowbytes / 4), (uint32_t)(nrows * a.rowbytes));
+        const __amdgpu_buffer_rsrc_t sr = span(s + n0 * a.G, (uint32_t)(nrows * a.G * 2));
+        const __amdgpu_buffer_rsrc_t br = span(b + n0 * a.G, (uint32_t)(nrows * a.G * 2));
+        // The register stage holds the codes of the next group to stage; its
+        // reload goes out right after, so each load has a group's products to arrive.
+        HlStage<BITS, TMW> st;
+        hl_load_x<BITS, TMW>(a, map, xr, 0, lds, pw);
+        hl_load<BITS, TMW>(st, a, wr, sr, br, 0, t);
+        hl_store<BITS, TMW>(st, lds, t);
+        hl_load<BITS, TMW>(st, a, wr, sr, br, last < 1 ? last : 1, t);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kHlLoads<BITS>);  // vmcnt(loads of st): x has landed
+        __syncthreads();
+        for (int grp = 0; grp < a.G; ++grp) {
+            if (grp + 1 < a.G) {  // uniform
+                uint8_t *nb = lds + ((grp + 1) & 1) * H::LDS_BUF;
+                hl_load_x<BITS, TMW>(a, map, xr, grp + 1, nb, pw);
+                hl_store<BITS, TMW>(st, nb, t);
+                hl_load<BITS, TMW>(st, a, wr, sr, br, grp + 2 < last ? grp + 2 : last, t);
+                __builtin_amdgcn_s_waitcnt(0x0F70 | kHlLoads<BITS>);  // the staged x has landed
+            }
+            __syncthreads();
+        }
+        return;
+    }
+    const int wm = wave >> 1, wn = wave & 1;
     f32x4 acc[TMW][4];
 #pragma unroll
     for (int m = 0; m < TMW; ++m)
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // LDS buffer p holds the groups of parity p. One register stage of codes: it
-    // holds the group after the one being computed, is dequantized into the other
-    // buffer, and is at once reloaded with the group two ahead, so each load has a
-    // whole group's products to arrive. The x tile of the next group goes straight
-    // to LDS at the start of the group, once the buffer's last readers have passed
-    // the barrier; the wait before the next barrier leaves the code loads issued
-    // after it in flight. The loop body is branch-free: stores and loads past the
-    // last group repeat the last one into a buffer nothing reads again.
-    HlStage<BITS, TMW> st;
-    const int last = a.G - 1;
-    hl_load_x<BITS, TMW>(a, map, xr, 0, lds);
-    hl_load<BITS, TMW>(st, a, wr, sr, br, 0);
-    hl_store<BITS, TMW>(st, lds);
-    hl_load<BITS, TMW>(st, a, wr, sr, br, last < 1 ? last : 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | kHlLoads<BITS>);  // vmcnt(loads of st): x has landed
     __syncthreads();
-    auto step = [&](auto pc, int nxt) {
-        constexpr int P = decltype(pc)::value;
-        hl_load_x<BITS, TMW>(a, map, xr, nxt - 1 < last ? nxt - 1 : last, lds + (P ^ 1) * H::LDS_BUF);
-        hl_compute<BITS, TMW>(lds + P * H::LDS_BUF, wm, wn, acc);
-        hl_store<BITS, TMW>(st, lds + (P ^ 1) * H::LDS_BUF);
-        hl_load<BITS, TMW>(st, a, wr, sr, br, nxt < last ? nxt : last);
-        // Interleave the dequantization with the matrix-core products.
-#pragma unroll
-        for (int k = 0; k < 8 * TMW; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // 3 VALU
-        }
-        __builtin_amdgcn_s_waitcnt(0x0F70 | kHlLoads<BITS>);  // the next x tile has landed
+    for (int grp = 0; grp < a.G; ++grp) {
+        hl_compute<BITS, TMW>(lds + (grp & 1) * H::LDS_BUF, wm, wn, acc);
         __syncthreads();
-    };
-    int grp0 = 0;
-    for (; grp0 + 2 <= a.G; grp0 += 2) {
-        step(std::integral_constant<int, 0>{}, grp0 + 2);
-        step(std::integral_constant<int, 1>{}, grp0 + 3);
     }
-    if (grp0 < a.G) hl_compute<BITS, TMW>(lds, wm, wn, acc);  // odd G: the last group, in buffer 0
-
     // Store: lane holds rows 4g + r of sub-tile m, weight row i of sub-tile n.
 #pragma unroll
     for (int m = 0; m < TMW; ++m)
@@ -593,7 +583,7 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
 
 // Large tiles, dense: blockIdx.x = 128-row weight tile, blockIdx.y = activation-row tile.
 template <int BITS, int TMW>
-__global__ __launch_bounds__(256) void qmm_hl_kernel(QmmArgs a) {
+__global__ __launch_bounds__(512) void qmm_hl_kernel(QmmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
     const DenseMap map{(int64_t)blockIdx.y * Hl<BITS, TMW>::BM, a.M};
     hl_tile<BITS, TMW>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * Hl<BITS, TMW>::BN, qmm_lds);
@@ -604,7 +594,9 @@ namespace {
 // The gather's pair lists for plane blockIdx.y, in ascending p: plist holds the
 // pairs routed to the plane with an in-range x row, xlist their x rows; the
 // return value is their count. Blocks of plane 0 first write NaN over columns
-// [n0, n0 + bn) of the rows of pairs whose indices are out of range.
+// [n0, n0 + bn) of the rows of pairs whose indices are out of range. NT: threads
+// of the block (wave_counts holds NT / 64 counts).
+template <int NT>
 __device__ __forceinline__ int gather_pairs(const QmmArgs &a, uint16_t *plist, uint32_t *xlist, int *wave_counts,
                                             int64_t n0, int bn) {
     const int t = threadIdx.x, lane = t & 63;
@@ -615,7 +607,7 @@ __device__ __forceinline__ int gather_pairs(const QmmArgs &a, uint16_t *plist, u
     // Block-wide ordered compaction of the pairs p < P that satisfy pred into plist.
     auto compact = [&](auto pred) {
         int total = 0;
-        for (int base = 0; base < a.M; base += 256) {
+        for (int base = 0; base < a.M; base += NT) {
             const int p = base + t;
             const bool take = p < a.M && pred(p);
             const uint64_t mask = __ballot(take);
@@ -624,7 +616,8 @@ __device__ __forceinline__ int gather_pairs(const QmmArgs &a, uint16_t *plist, u
             int before = total;
             for (int v = 0; v < wave; ++v) before += wave_counts[v];
             if (take) plist[before + __popcll(mask & ((1ull << lane) - 1ull))] = (uint16_t)p;
-            total += wave_counts[0] + wave_counts[1] + wave_counts[2] + wave_counts[3];
+#pragma unroll
+            for (int v = 0; v < NT / 64; ++v) total += wave_counts[v];
             __syncthreads();
         }
         return total;
@@ -636,7 +629,7 @@ __device__ __forceinline__ int gather_pairs(const QmmArgs &a, uint16_t *plist, u
             return xr >= nx || ex >= ne;
         });
         for (int k = 0; k < nbad; ++k)
-            for (int c = t; c < bn; c += 256)
+            for (int c = t; c < bn; c += NT)
                 if (n0 + c < a.N) a.y[(int64_t)plist[k] * a.N + n0 + c] = 0x7FC0u;
         __syncthreads();
     }
@@ -645,7 +638,7 @@ __device__ __forceinline__ int gather_pairs(const QmmArgs &a, uint16_t *plist, u
         const uint32_t ex = a.rhs ? a.rhs[p] : (uint32_t)p;
         return ex == e && xr < nx;
     });
-    for (int k = t; k < count; k += 256) xlist[k] = a.lhs ? a.lhs[plist[k]] : (uint32_t)plist[k];
+    for (int k = t; k < count; k += NT) xlist[k] = a.lhs ? a.lhs[plist[k]] : (uint32_t)plist[k];
     __syncthreads();
     return count;
 }
@@ -664,7 +657,7 @@ __global__ __launch_bounds__(256) void gather_qmm_kernel(QmmArgs a) {
     uint32_t *xlist = reinterpret_cast<uint32_t *>(qmm_lds + 2 * TT::LDS_BUF + ((a.M * 2 + 15) / 16) * 16);
     __shared__ int wave_counts[4];
     const int64_t n0 = (int64_t)blockIdx.x * TT::BN;
-    const int count = gather_pairs(a, plist, xlist, wave_counts, n0, TT::BN);
+    const int count = gather_pairs<256>(a, plist, xlist, wave_counts, n0, TT::BN);
     if (count == 0) return;
     const int64_t plane = (int64_t)blockIdx.y * a.N;
     const uint32_t *w = a.w + plane * (a.rowbytes / 4);
@@ -678,14 +671,14 @@ __global__ __launch_bounds__(256) void gather_qmm_kernel(QmmArgs a) {
 
 // Large tiles, gathered (as gather_qmm_kernel).
 template <int BITS, int TMW>
-__global__ __launch_bounds__(256) void gather_qmm_hl_kernel(QmmArgs a) {
+__global__ __launch_bounds__(512) void gather_qmm_hl_kernel(QmmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
     using H = Hl<BITS, TMW>;
     uint16_t *plist = reinterpret_cast<uint16_t *>(qmm_lds + 2 * H::LDS_BUF);
     uint32_t *xlist = reinterpret_cast<uint32_t *>(qmm_lds + 2 * H::LDS_BUF + ((a.M * 2 + 15) / 16) * 16);
-    __shared__ int wave_counts[4];
+    __shared__ int wave_counts[8];
     const int64_t n0 = (int64_t)blockIdx.x * H::BN;
-    const int count = gather_pairs(a, plist, xlist, wave_counts, n0, H::BN);
+    const int count = gather_pairs<512>(a, plist, xlist, wave_counts, n0, H::BN);
     if (count == 0) return;
     const int64_t plane = (int64_t)blockIdx.y * a.N;
     const uint32_t *w = a.w + plane * (a.rowbytes / 4);
@@ -719,6 +712,7 @@ static QmmKernel hl_pick(bool gather) {
     k.bm = Hl<BITS, TMW>::BM;
     k.bn = Hl<BITS, TMW>::BN;
     k.lds = 2 * Hl<BITS, TMW>::LDS_BUF;
+    k.threads = 512;
     return k;
 }
 
