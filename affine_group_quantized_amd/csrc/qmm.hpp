@@ -24,9 +24,9 @@ constexpr int kQmmSmallPairs = 64;
 constexpr int kQmmLargeBlocksPerCu = 2;
 // Split-weight tiles (256 x 128, qmm_hl_kernel) from this many rows, where
 // their grid gives every compute unit a block (4-bit, us: 4096x4096 at M =
-// 2048: 157 -> 136; 28672x4096 at M = 512 / 2048: 326 / 1221 -> 279 / 994;
-// 4096x14336 at M = 2048: 554 -> 446). With 128-row tiles they lost at M =
-// 256 (28672x4096: 167 -> 221) and on the Mixtral prefill gather (430 -> 665).
+// 2048: 157 -> 107; 28672x4096 at M = 512 / 2048: 326 / 1221 -> 218 / 796;
+// 4096x14336 at M = 2048: 554 -> 341). Tiles of 128 rows lost at M = 256
+// (28672x4096: 166 -> 174) and on the Mixtral prefill gather.
 constexpr int kQmmHlMinRows = 256;
 constexpr int kQmmPassRows = 128;  // 4-bit products of up to this many rows run on the matvec kernel in passes of 16
 

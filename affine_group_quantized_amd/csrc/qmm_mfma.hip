@@ -33,6 +33,8 @@
 // read 16 rows of one word, and the XOR spreads them over all 64 banks.
 // Global loads run DEPTH groups ahead in registers; the LDS tiles are double
 // buffered, so each group costs one block barrier.
+// (Grids of 256-row tiles that fill the device take the split-weight kernels
+// below instead.)
 //
 // Lanes and MFMA operands (16x16x32, bf16): lane l, g = l / 16, i = l % 16.
 // A: row i of the 16-row sub-tile, words 4*step + g; B: weight row i of the
@@ -363,16 +365,19 @@ __device__ __forceinline__ void qmm_tile(const QmmArgs &a, const Map &map, const
 // recipe needs at most 12 at 4 bits and 16 at 8 bits); otherwise the weight
 // is off by at most 2^-17 of itself. Infinite weights give NaN (lo = inf - inf).
 //
-// A block of 4 waves (2 x 2) computes BM = 32*TMW activation rows by 128
-// weight rows; wave (wm, wn) owns 16*TMW x 64. K advances one 64-column group
-// at a time: per group the block stages x (BM rows x 8 words of 8 columns,
-// natural order) and the weights' hi and lo parts (128 rows x 8 words each)
-// into LDS, word w of a row at slot w ^ (row & 7). Each thread dequantizes 32
-// columns of one weight row. Global loads run two groups ahead in registers;
-// the LDS buffers are double buffered (one block barrier per group).
+// A block of 8 waves computes BM = 32*TMW activation rows by 128 weight rows,
+// one 64-column group at a time, through two LDS buffers (x: BM rows x 8
+// words of 8 columns in natural order; the weights' hi and lo parts: 128 rows
+// x 8 words each; word w of a row at slot w ^ (row & 7)). Waves 0-3 (2 x 2,
+// 16*TMW x 64 each) only take products out of one buffer; waves 4-7 stage the
+// next group into the other: x with direct-to-LDS buffer loads, and the codes
+// (loaded two groups ahead) dequantized and split, 32 columns of one weight row
+// per thread. One block barrier per group; one wave of each role per SIMD, so
+// staging overlaps the matrix-core work (4096x4096 at M = 2048: 136 us with all
+// four waves doing both in turn, 107 us with the roles split).
 template <int BITS, int TMW>
 struct Hl {
-    static constexpr int BM = 32 * TMW, BN = 128, THREADS = 256;
+    static constexpr int BM = 32 * TMW, BN = 128;
     static constexpr int LDS_X = BM * 128, LDS_B = BN * 128;
     static constexpr int LDS_BUF = LDS_X + 2 * LDS_B;
 };
