@@ -18,7 +18,7 @@ import os
 
 import torch
 
-__all__ = ["qmv", "qmv_wide", "qmv_fused", "qmv_nvfp4", "ACT_NONE", "ACT_SWIGLU", "ACT_GEGLU", "gather_qmv", "qmm", "gather_qmm", "moe_decode", "moe_decode_workspace", "quantize",
+__all__ = ["qmv", "qmv_wide", "qmv_fused", "qmv_nvfp4", "qmm_nvfp4", "ACT_NONE", "ACT_SWIGLU", "ACT_GEGLU", "gather_qmv", "qmm", "gather_qmm", "moe_decode", "moe_decode_workspace", "quantize",
            "dequantize", "plan", "launch_plan", "prepare_qmv", "AgqError",
            "LIB_PATH", "lib"]
 
@@ -62,6 +62,7 @@ def _load(path: str = LIB_PATH):
     lib.agq_qmv_wide.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
     lib.agq_qmv_fused.argtypes = [P, P, ctypes.c_float, P, P, P, P, I, P, I64, I64, I, I, P]
     lib.agq_qmv_nvfp4.argtypes = [P, P, P, ctypes.c_float, P, I64, I64, I64, P]
+    lib.agq_qmm_nvfp4.argtypes = [P, P, P, ctypes.c_float, P, I64, I64, I64, P]
     lib.agq_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.agq_qmm.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
     lib.agq_gather_qmm.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
@@ -74,7 +75,7 @@ def _load(path: str = LIB_PATH):
     lib.agq_dequantize.argtypes = [P, P, P, P, I64, I64, I, I, P]
     lib.agq_plan_product.argtypes = [I64, I64, I64, I, I, I, I, I64, ctypes.POINTER(Plan)]
     lib.agq_plan_launch.argtypes = [I64, I64, I64, I, I, I64, ctypes.POINTER(Plan)]
-    for f in (lib.agq_qmv, lib.agq_qmv_wide, lib.agq_qmv_fused, lib.agq_qmv_nvfp4, lib.agq_gather_qmv, lib.agq_qmm, lib.agq_gather_qmm, lib.agq_dequantize,
+    for f in (lib.agq_qmv, lib.agq_qmv_wide, lib.agq_qmv_fused, lib.agq_qmv_nvfp4, lib.agq_qmm_nvfp4, lib.agq_gather_qmv, lib.agq_qmm, lib.agq_gather_qmm, lib.agq_dequantize,
               lib.agq_plan_product, lib.agq_plan_launch):
         f.restype = I
     return lib
@@ -186,9 +187,7 @@ def qmv_fused(x, w, scales, biases, bits: int = 4, group_size: int = 64, norm_we
     return out
 
 
-def qmv_nvfp4(x, w, scales, tensor_scale: float = 1.0, out=None):
-    """NVFP4 product: ``x`` [K] or [M, K] bf16 (M <= 4), ``w`` [N, K/8] int32/uint32 E2M1 codes,
-    ``scales`` [N, K/16] uint8 E4M3 block scales -> ``y`` [N] or [M, N] bf16."""
+def _nvfp4(fn, x, w, scales, tensor_scale, out):
     device = x.device
     _need(x, "x", _BF16, device)
     _need(w, "w", _U32, device)
@@ -208,9 +207,20 @@ def qmv_nvfp4(x, w, scales, tensor_scale: float = 1.0, out=None):
         if out.numel() != M * N:
             raise ValueError("out has the wrong size")
     with torch.cuda.device(device):
-        _check(lib.agq_qmv_nvfp4(_ptr(x), _ptr(w), _ptr(scales), float(tensor_scale), _ptr(out), M, N, K,
-                                 _stream(device)))
+        _check(fn(_ptr(x), _ptr(w), _ptr(scales), float(tensor_scale), _ptr(out), M, N, K, _stream(device)))
     return out
+
+
+def qmv_nvfp4(x, w, scales, tensor_scale: float = 1.0, out=None):
+    """NVFP4 product: ``x`` [K] or [M, K] bf16 (M <= 4), ``w`` [N, K/8] int32/uint32 E2M1 codes,
+    ``scales`` [N, K/16] uint8 E4M3 block scales -> ``y`` [N] or [M, N] bf16."""
+    return _nvfp4(lib.agq_qmv_nvfp4, x, w, scales, tensor_scale, out)
+
+
+def qmm_nvfp4(x, w, scales, tensor_scale: float = 1.0, out=None):
+    """NVFP4 product for any number of rows ``x`` [M, K] (agq_qmm_nvfp4: up to 4 rows the
+    matvec kernel, beyond it the matrix-core GEMM, which needs K % 64 == 0)."""
+    return _nvfp4(lib.agq_qmm_nvfp4, x, w, scales, tensor_scale, out)
 
 
 def prepare_qmv(x, w, scales, biases, out, bits: int = 4, group_size: int = 64, stream=None):

@@ -474,6 +474,69 @@ agq_status agq_qmv_nvfp4(const void *x, const uint32_t *w, const void *scales, f
     return launch(sym, dim3((unsigned)plan.blocks), dim3(plan.threads), 0, &a, stream);
 }
 
+// Whether M > 4 rows of an NVFP4 product run faster as passes of 4 rows of the
+// matvec kernel (each pass streams the weights once) than on the GEMM, whose
+// blocks walk K one 64-column group at a time (about 0.6 us per group, latency-
+// bound, when the grid is small). A pass costs about its weight bytes at 4.5 TB/s
+// plus 3 us. Measured (us, GEMM / passes): 4096x4096 at M = 16 / 32: 37.9 / 22.3,
+// 39.1 / 44.4; 28672x4096 at M = 8 / 16: 53.8 / 39.8, 52.8 / 77.3; 4096x14336 at
+// M = 32 / 64: 138.5 / 99.5, 142.1 / 196.1.
+bool nvfp4_passes_win(int64_t M, int64_t N, int64_t K, int cus) {
+    const double pass_us = (double)N * (double)K * 0.5625 / 4.5e6 + 3.0;
+    const double passes_us = (double)((M + 3) / 4) * pass_us;
+    const agq::QmmKernel k = agq::qmm_nvfp4_kernel_for(M, N, cus);
+    const int64_t blocks = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn);
+    const double gemm_us = (double)(K / 64) * 0.6 * (double)((blocks + cus - 1) / cus);
+    return passes_us < gemm_us;
+}
+
+agq_status agq_qmm_nvfp4(const void *x, const uint32_t *w, const void *scales, float tensor_scale, void *y, int64_t M,
+                         int64_t N, int64_t K, void *stream) {
+    if (M <= 4) return agq_qmv_nvfp4(x, w, scales, tensor_scale, y, M, N, K, stream);
+    if (!x || !w || !scales || !y) return fail(AGQ_EINVAL, "null tensor pointer");
+    if (N <= 0 || K <= 0) return fail(AGQ_EINVAL, "N and K must be positive (N=%lld, K=%lld)", (long long)N, (long long)K);
+    if (N > kMaxN || K > kMaxK) return fail(AGQ_EINVAL, "N or K too large (N=%lld, K=%lld)", (long long)N, (long long)K);
+    if (K % 16 != 0) return fail(AGQ_EINVAL, "K=%lld is not a multiple of the NVFP4 block of 16", (long long)K);
+    if (K % 32 != 0) return fail(AGQ_ENOTSUP, "K=%lld: the NVFP4 kernels read 32-code chunks", (long long)K);
+    if (!(tensor_scale == tensor_scale) || tensor_scale > 3.0e38f || tensor_scale < -3.0e38f)
+        return fail(AGQ_EINVAL, "tensor_scale must be finite");
+    if (misaligned(x, 16) || misaligned(w, 16)) return fail(AGQ_EINVAL, "x and w must be 16-byte aligned");
+    if (misaligned(scales, 2) || misaligned(y, 2)) return fail(AGQ_EINVAL, "scales and y must be 2-byte aligned");
+    if (M * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (M*K*2 bytes)");
+    if ((int64_t)agq::kQmmHlTileN * (K / 2) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
+    if ((M + agq::kQmmTileMinM - 1) / agq::kQmmTileMinM > 65535 || (N + agq::kQmmHlTileN - 1) / agq::kQmmHlTileN > INT32_MAX)
+        return fail(AGQ_ENOTSUP, "grid too large (M=%lld, N=%lld)", (long long)M, (long long)N);
+    int cus = 0, dev = 0;
+    agq_status st = current_device(&cus, &dev);
+    if (st != AGQ_OK) return st;
+    if (K % 64 != 0 || nvfp4_passes_win(M, N, K, cus)) {
+        // Passes of up to 4 rows through the matvec kernel.
+        for (int64_t r0 = 0; r0 < M; r0 += 4) {
+            st = agq_qmv_nvfp4(static_cast<const uint16_t *>(x) + r0 * K, w, scales, tensor_scale,
+                               static_cast<uint16_t *>(y) + r0 * N, M - r0 < 4 ? M - r0 : 4, N, K, stream);
+            if (st != AGQ_OK) return st;
+        }
+        return AGQ_OK;
+    }
+    const agq::QmmKernel k = agq::qmm_nvfp4_kernel_for(M, N, cus);
+    const int64_t mt = (M + k.bm - 1) / k.bm, nt = (N + k.bn - 1) / k.bn;
+    agq::QmmArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = w;
+    a.s = static_cast<const uint16_t *>(scales);  // scale bytes, addressed bytewise by the kernel
+    a.y = static_cast<uint16_t *>(y);
+    a.N = N;
+    a.M = (int32_t)M;
+    a.K = (int32_t)K;
+    a.G = (int32_t)(K / 64);
+    a.rowbytes = (int32_t)(K / 2);
+    a.xbytes = (uint32_t)(M * K * 2);
+    a.ts = tensor_scale;
+    st = allow_lds(k.sym, (size_t)k.lds, dev);
+    if (st != AGQ_OK) return st;
+    return launch(k.sym, dim3((unsigned)nt, (unsigned)mt), dim3(k.threads), (size_t)k.lds, &a, stream);
+}
+
 agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y, int64_t P, int64_t R,
                           int64_t E, int64_t N, int64_t K, int bits, int group_size, void *stream) {

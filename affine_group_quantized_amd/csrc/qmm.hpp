@@ -47,7 +47,7 @@ struct QmmArgs {
     uint32_t xbytes;      // bytes of x (the range of its buffer descriptor)
     int32_t R_x;          // gather: rows of x
     int32_t E;            // gather: expert planes
-    int32_t pad_;
+    float ts;             // NVFP4: the tensor scale applied to each result (unused by the affine kernels)
 };
 
 struct QmmKernel {
@@ -60,6 +60,8 @@ struct QmmKernel {
 // The kernel for `rows` activation rows (dense M, or the gather's pairs per
 // expert plane) against N weight rows in `planes` planes on `cus` compute units.
 QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t planes, int cus);
+// The NVFP4 GEMM (E2M1 codes, E4M3 scales per 16 columns) for M > 4 activation rows.
+QmmKernel qmm_nvfp4_kernel_for(int64_t M, int64_t N, int cus);
 // Tile geometry shared by both shapes (the host checks use it before any HIP call).
 constexpr int kQmmTileN = 64;
 constexpr int kQmmTileMinM = 64;

@@ -375,33 +375,152 @@ __device__ __forceinline__ void qmm_tile(const QmmArgs &a, const Map &map, const
 // per thread. One block barrier per group; one wave of each role per SIMD, so
 // staging overlaps the matrix-core work (4096x4096 at M = 2048: 136 us with all
 // four waves doing both in turn, 107 us with the roles split).
-template <int BITS, int TMW>
+// (hi, lo) bfloat16 pairs of the fp32 pair (v0, v1): hi = bf16(v), lo = bf16(v - hi).
+__device__ __forceinline__ void hl_split(float v0, float v1, uint32_t &hp, uint32_t &lp) {
+    const f32x2 v = {v0, v1};
+    hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    const f32x2 l = {v0 - __uint_as_float(hp << 16), v1 - __uint_as_float(hp & 0xFFFF0000u)};
+    lp = __builtin_bit_cast(uint32_t, __builtin_convertvector(l, bf16x2));
+}
+
+// Weight formats of the split-weight tiles: what one producer thread loads per
+// group (32 columns of one weight row, two groups ahead) and the B parts it
+// writes for them.
+//  - Affine codes (4- or 8-bit, BF16 scale and bias per 64 columns): two
+//    parts, hi = bf16(w) and lo = bf16(w - hi) of w = fma(s, q, b).
+//  - NVFP4 (E2M1 codes, one E4M3 scale byte per 16 columns): one part,
+//    bf16(e2m1(q) * e4m3(s)), exact (at most 6 significant bits); the fp32
+//    tensor scale multiplies each result once, before its bf16 rounding.
+template <int BITS>
+struct AffineFmt {
+    static constexpr int kParts = 2;
+    static constexpr int kLoads = BITS / 4 + 2;  // vector-memory instructions of one load
+    static constexpr bool kScaled = false;
+    struct Stage {
+        u32x4 w[BITS / 4];  // the thread's 32 codes (4-bit: 16 bytes; 8-bit: 32 bytes)
+        uint16_t s, b;
+    };
+    __device__ static __amdgpu_buffer_rsrc_t srange(const QmmArgs &a, const uint16_t *s, int64_t n0, int64_t nrows) {
+        return span(s + n0 * a.G, (uint32_t)(nrows * a.G * 2));
+    }
+    __device__ static __amdgpu_buffer_rsrc_t brange(const QmmArgs &a, const uint16_t *b, int64_t n0, int64_t nrows) {
+        return span(b + n0 * a.G, (uint32_t)(nrows * a.G * 2));
+    }
+    // Weight row t / 2, columns 32 * (t % 2) .. +32 of group grp.
+    __device__ static void load(Stage &st, const QmmArgs &a, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                __amdgpu_buffer_rsrc_t br, int grp, int t) {
+        const uint32_t r = (uint32_t)t >> 1, h = (uint32_t)t & 1u;
+#pragma unroll
+        for (int c = 0; c < BITS / 4; ++c) {
+            const uint32_t off = r * (uint32_t)a.rowbytes + (uint32_t)grp * (uint32_t)(8 * BITS) +
+                                 h * (uint32_t)(4 * BITS) + (uint32_t)c * 16u;
+            st.w[c] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);
+        }
+        const uint32_t soff = (r * (uint32_t)a.G + (uint32_t)grp) * 2u;
+        st.s = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
+        st.b = __builtin_amdgcn_raw_buffer_load_b16(br, soff, 0, 0);
+    }
+    // The thread's four B words (8 columns each) of both parts.
+    __device__ static void store(const Stage &st, u32x4 *p0, u32x4 *p1, int t) {
+        const float sf = bf16_lo(st.s), bfv = bf16_lo(st.b);
+        const int r = t >> 1, h = t & 1;
+        const uint32_t d[8] = {st.w[0].x, st.w[0].y, st.w[0].z, st.w[0].w,
+                               BITS == 8 ? st.w[BITS / 4 - 1].x : 0u, BITS == 8 ? st.w[BITS / 4 - 1].y : 0u,
+                               BITS == 8 ? st.w[BITS / 4 - 1].z : 0u, BITS == 8 ? st.w[BITS / 4 - 1].w : 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // B word 4h + j: columns 8j .. 8j + 7 of the thread's 32
+            float v[8];
+            if constexpr (BITS == 4) {
+                // codes low-first: byte i of the word holds columns 2i (low nibble) and 2i + 1
+                const uint32_t lo = d[j] & 0x0F0F0F0Fu, hi = (d[j] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = fmaf(sf, (float)((lo >> (8 * i)) & 0xFFu), bfv);
+                    v[2 * i + 1] = fmaf(sf, (float)((hi >> (8 * i)) & 0xFFu), bfv);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[i] = fmaf(sf, (float)((d[2 * j] >> (8 * i)) & 0xFFu), bfv);
+                    v[4 + i] = fmaf(sf, (float)((d[2 * j + 1] >> (8 * i)) & 0xFFu), bfv);
+                }
+            }
+            uint32_t hp[4], lp[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hl_split(v[2 * q], v[2 * q + 1], hp[q], lp[q]);
+            const int word = 4 * h + j;
+            p0[r * 8 + (word ^ (r & 7))] = u32x4{hp[0], hp[1], hp[2], hp[3]};
+            p1[r * 8 + (word ^ (r & 7))] = u32x4{lp[0], lp[1], lp[2], lp[3]};
+        }
+    }
+};
+
+struct Nvfp4Fmt {
+    static constexpr int kParts = 1;
+    static constexpr int kLoads = 2;
+    static constexpr bool kScaled = true;
+    struct Stage {
+        u32x4 w;     // the thread's 32 codes
+        uint16_t s;  // their two E4M3 scale bytes
+    };
+    // (a.s points at the scale bytes, [N, K/16] uint8; there is no bias.)
+    __device__ static __amdgpu_buffer_rsrc_t srange(const QmmArgs &a, const uint16_t *s, int64_t n0, int64_t nrows) {
+        return span(reinterpret_cast<const uint8_t *>(s) + n0 * (a.K / 16), (uint32_t)(nrows * (a.K / 16)));
+    }
+    __device__ static __amdgpu_buffer_rsrc_t brange(const QmmArgs &, const uint16_t *, int64_t, int64_t) {
+        return span(nullptr, 0u);
+    }
+    __device__ static void load(Stage &st, const QmmArgs &a, __amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr,
+                                __amdgpu_buffer_rsrc_t, int grp, int t) {
+        const uint32_t r = (uint32_t)t >> 1, h = (uint32_t)t & 1u;
+        st.w = __builtin_amdgcn_raw_buffer_load_b128(wr, r * (uint32_t)a.rowbytes + (uint32_t)grp * 32u + h * 16u, 0, 2);
+        st.s = __builtin_amdgcn_raw_buffer_load_b16(sr, r * (uint32_t)(a.K / 16) + (uint32_t)grp * 4u + h * 2u, 0, 0);
+    }
+    // Words 0-1 of the thread's 32 codes take scale byte 0, words 2-3 byte 1.
+    // The FP4 convert turns byte p of a word into the bf16 pair (column 2p,
+    // column 2p + 1), exactly (scale operand 1: it applies only an exponent).
+    __device__ static void store(const Stage &st, u32x4 *p0, u32x4 *, int t) {
+        const int r = t >> 1, h = t & 1;
+        const float sc[2] = {__builtin_amdgcn_cvt_f32_fp8((uint32_t)st.s, 0),
+                             __builtin_amdgcn_cvt_f32_fp8((uint32_t)st.s, 1)};
+        const uint32_t d[4] = {st.w.x, st.w.y, st.w.z, st.w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t pr[4] = {
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], 1.0f, 0)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], 1.0f, 1)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], 1.0f, 2)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[j], 1.0f, 3))};
+            const float f = sc[j >> 1];
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x2 v = {__uint_as_float(pr[q] << 16) * f, __uint_as_float(pr[q] & 0xFFFF0000u) * f};
+                o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+            }
+            const int word = 4 * h + j;
+            p0[r * 8 + (word ^ (r & 7))] = u32x4{o[0], o[1], o[2], o[3]};
+        }
+    }
+};
+
+template <typename F, int TMW>
 struct Hl {
     static constexpr int BM = 32 * TMW, BN = 128;
     static constexpr int LDS_X = BM * 128, LDS_B = BN * 128;
-    static constexpr int LDS_BUF = LDS_X + 2 * LDS_B;
+    static constexpr int LDS_BUF = LDS_X + F::kParts * LDS_B;
 };
-
-template <int BITS, int TMW>
-struct HlStage {
-    u32x4 w[BITS / 4];  // the thread's 32 codes (4-bit: 16 bytes; 8-bit: 32 bytes)
-    uint16_t s, b;
-};
-// Vector-memory instructions of one hl_load (codes, scale, bias).
-template <int BITS>
-constexpr int kHlLoads = BITS / 4 + 2;
 
 // x of group grp into the LDS buffer's x tile with direct-to-LDS loads: wave w
 // writes 1 KB chunks c = w, w + 4, ... (rows 8c .. 8c + 7); lane L of a chunk
 // fills slot L % 8 of row 8c + L / 8, so it fetches that row's word
 // (L % 8) ^ (L / 8). Rows past the tile (or the pass) read zero.
-template <int BITS, int TMW, typename Map>
+template <int BM, typename Map>
 __device__ __forceinline__ void hl_load_x(const QmmArgs &a, const Map &map, __amdgpu_buffer_rsrc_t xr, int grp,
                                           uint8_t *buf, int wave) {
-    using H = Hl<BITS, TMW>;
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int k = 0; k < H::BM / 32; ++k) {
+    for (int k = 0; k < BM / 32; ++k) {
         const int c = wave + 4 * k;
         const int row = 8 * c + (lane >> 3);
         const int word = (lane & 7) ^ (lane >> 3);
@@ -412,138 +531,77 @@ __device__ __forceinline__ void hl_load_x(const QmmArgs &a, const Map &map, __am
     }
 }
 
-template <int BITS, int TMW>
-__device__ __forceinline__ void hl_load(HlStage<BITS, TMW> &st, const QmmArgs &a, __amdgpu_buffer_rsrc_t wr,
-                                        __amdgpu_buffer_rsrc_t sr, __amdgpu_buffer_rsrc_t br, int grp, int t) {
-    // Weight row t / 2, columns 32 * (t % 2) .. +32 of the group.
-    const uint32_t r = (uint32_t)t >> 1, h = (uint32_t)t & 1u;
-#pragma unroll
-    for (int c = 0; c < BITS / 4; ++c) {
-        const uint32_t off = r * (uint32_t)a.rowbytes + (uint32_t)grp * (uint32_t)(8 * BITS) + h * (uint32_t)(4 * BITS) +
-                             (uint32_t)c * 16u;
-        st.w[c] = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);
-    }
-    const uint32_t soff = (r * (uint32_t)a.G + (uint32_t)grp) * 2u;
-    st.s = __builtin_amdgcn_raw_buffer_load_b16(sr, soff, 0, 0);
-    st.b = __builtin_amdgcn_raw_buffer_load_b16(br, soff, 0, 0);
-}
-
-// (hi, lo) bfloat16 pairs of the fp32 pair (v0, v1): hi = bf16(v), lo = bf16(v - hi).
-__device__ __forceinline__ void hl_split(float v0, float v1, uint32_t &hp, uint32_t &lp) {
-    const f32x2 v = {v0, v1};
-    hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-    const f32x2 l = {v0 - __uint_as_float(hp << 16), v1 - __uint_as_float(hp & 0xFFFF0000u)};
-    lp = __builtin_bit_cast(uint32_t, __builtin_convertvector(l, bf16x2));
-}
-
-template <int BITS, int TMW>
-__device__ __forceinline__ void hl_store(const HlStage<BITS, TMW> &st, uint8_t *buf, int t) {
-    using H = Hl<BITS, TMW>;
-    u32x4 *bh = reinterpret_cast<u32x4 *>(buf + H::LDS_X);
-    u32x4 *bl = reinterpret_cast<u32x4 *>(buf + H::LDS_X + H::LDS_B);
-    const float sf = bf16_lo(st.s), bfv = bf16_lo(st.b);
-    const int r = t >> 1, h = t & 1;
-    const uint32_t d[8] = {st.w[0].x, st.w[0].y, st.w[0].z, st.w[0].w,
-                           BITS == 8 ? st.w[BITS / 4 - 1].x : 0u, BITS == 8 ? st.w[BITS / 4 - 1].y : 0u,
-                           BITS == 8 ? st.w[BITS / 4 - 1].z : 0u, BITS == 8 ? st.w[BITS / 4 - 1].w : 0u};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {  // B word 4h + j: columns 8j .. 8j + 7 of the thread's 32
-        float v[8];
-        if constexpr (BITS == 4) {
-            // codes low-first: byte i of the word holds columns 2i (low nibble) and 2i + 1
-            const uint32_t lo = d[j] & 0x0F0F0F0Fu, hi = (d[j] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = fmaf(sf, (float)((lo >> (8 * i)) & 0xFFu), bfv);
-                v[2 * i + 1] = fmaf(sf, (float)((hi >> (8 * i)) & 0xFFu), bfv);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[i] = fmaf(sf, (float)((d[2 * j] >> (8 * i)) & 0xFFu), bfv);
-                v[4 + i] = fmaf(sf, (float)((d[2 * j + 1] >> (8 * i)) & 0xFFu), bfv);
-            }
-        }
-        uint32_t hp[4], lp[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) hl_split(v[2 * p], v[2 * p + 1], hp[p], lp[p]);
-        const int word = 4 * h + j;
-        bh[r * 8 + (word ^ (r & 7))] = u32x4{hp[0], hp[1], hp[2], hp[3]};
-        bl[r * 8 + (word ^ (r & 7))] = u32x4{lp[0], lp[1], lp[2], lp[3]};
-    }
-}
-
 // One group's products: for each of the two 32-column steps, the wave's TMW x 4
-// sub-tiles take the hi and then the lo part into their accumulators.
-template <int BITS, int TMW>
+// sub-tiles take each part of the weights (hi, then lo) into their accumulators.
+template <typename F, int TMW>
 __device__ __forceinline__ void hl_compute(const uint8_t *buf, int wm, int wn, f32x4 (&acc)[TMW][4]) {
-    using H = Hl<BITS, TMW>;
+    using H = Hl<F, TMW>;
     const u32x4 *xs = reinterpret_cast<const u32x4 *>(buf);
-    const u32x4 *bh = reinterpret_cast<const u32x4 *>(buf + H::LDS_X);
-    const u32x4 *bl = reinterpret_cast<const u32x4 *>(buf + H::LDS_X + H::LDS_B);
     const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
 #pragma unroll
     for (int step = 0; step < 2; ++step) {
         const int word = 4 * step + g;
-        u32x4 av[TMW], hv[4], lv[4];
+        u32x4 av[TMW], bv[F::kParts][4];
 #pragma unroll
         for (int m = 0; m < TMW; ++m) {
             const int row = wm * 16 * TMW + 16 * m + i;
             av[m] = xs[row * 8 + (word ^ (row & 7))];
         }
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int row = wn * 64 + 16 * n + i;
-            hv[n] = bh[row * 8 + (word ^ (row & 7))];
-            lv[n] = bl[row * 8 + (word ^ (row & 7))];
+        for (int q = 0; q < F::kParts; ++q) {
+            const u32x4 *bs = reinterpret_cast<const u32x4 *>(buf + H::LDS_X + q * H::LDS_B);
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int row = wn * 64 + 16 * n + i;
+                bv[q][n] = bs[row * 8 + (word ^ (row & 7))];
+            }
         }
-        // All hi products, then all lo products: each accumulator's second product
-        // issues TMW*4 instructions after its first.
+        // Part by part: each accumulator's next product issues TMW*4 instructions later.
 #pragma unroll
-        for (int m = 0; m < TMW; ++m)
+        for (int q = 0; q < F::kParts; ++q)
 #pragma unroll
-            for (int n = 0; n < 4; ++n) acc[m][n] = mma(av[m], hv[n], acc[m][n]);
+            for (int m = 0; m < TMW; ++m)
 #pragma unroll
-        for (int m = 0; m < TMW; ++m)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) acc[m][n] = mma(av[m], lv[n], acc[m][n]);
+                for (int n = 0; n < 4; ++n) acc[m][n] = mma(av[m], bv[q][n], acc[m][n]);
     }
 }
 
-template <int BITS, int TMW, typename Map>
+template <typename F, int TMW, typename Map>
 __device__ __forceinline__ void hl_tile(const QmmArgs &a, const Map &map, const uint32_t *w, const uint16_t *s,
                                         const uint16_t *b, int64_t n0, uint8_t *lds) {
-    using H = Hl<BITS, TMW>;
+    using H = Hl<F, TMW>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
     const int64_t nrows = a.N - n0 < H::BN ? a.N - n0 : H::BN;
     const int last = a.G - 1;
     // Two roles, one wave of each per SIMD: waves 4-7 stage group grp + 1 into LDS
-    // buffer (grp + 1) % 2 (x with direct-to-LDS loads, the weights dequantized and
-    // split) while waves 0-3 take group grp's products out of buffer grp % 2. One
-    // block barrier per group; both roles meet it the same number of times.
+    // buffer (grp + 1) % 2 (x with direct-to-LDS loads, the weights dequantized
+    // into their B parts) while waves 0-3 take group grp's products out of buffer
+    // grp % 2. One block barrier per group; both roles meet it the same number of times.
     if (wave >= 4) {
         const int pw = wave - 4, t = threadIdx.x - 256;
         const __amdgpu_buffer_rsrc_t xr = span(a.x, a.xbytes);
         const __amdgpu_buffer_rsrc_t wr = span(w + n0 * (a.rowbytes / 4), (uint32_t)(nrows * a.rowbytes));
-        const __amdgpu_buffer_rsrc_t sr = span(s + n0 * a.G, (uint32_t)(nrows * a.G * 2));
-        const __amdgpu_buffer_rsrc_t br = span(b + n0 * a.G, (uint32_t)(nrows * a.G * 2));
+        const __amdgpu_buffer_rsrc_t sr = F::srange(a, s, n0, nrows);
+        const __amdgpu_buffer_rsrc_t br = F::brange(a, b, n0, nrows);
+        // The B parts of an LDS buffer follow its x tile.
+        auto part = [&](uint8_t *buf, int q) { return reinterpret_cast<u32x4 *>(buf + H::LDS_X + q * H::LDS_B); };
         // The register stage holds the codes of the next group to stage; its
         // reload goes out right after, so each load has a group's products to arrive.
-        HlStage<BITS, TMW> st;
-        hl_load_x<BITS, TMW>(a, map, xr, 0, lds, pw);
-        hl_load<BITS, TMW>(st, a, wr, sr, br, 0, t);
-        hl_store<BITS, TMW>(st, lds, t);
-        hl_load<BITS, TMW>(st, a, wr, sr, br, last < 1 ? last : 1, t);
-        __builtin_amdgcn_s_waitcnt(0x0F70 | kHlLoads<BITS>);  // vmcnt(loads of st): x has landed
+        typename F::Stage st;
+        hl_load_x<H::BM>(a, map, xr, 0, lds, pw);
+        F::load(st, a, wr, sr, br, 0, t);
+        F::store(st, part(lds, 0), part(lds, F::kParts - 1), t);
+        F::load(st, a, wr, sr, br, last < 1 ? last : 1, t);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | F::kLoads);  // vmcnt(loads of st): x has landed
         __syncthreads();
         for (int grp = 0; grp < a.G; ++grp) {
             if (grp + 1 < a.G) {  // uniform
                 uint8_t *nb = lds + ((grp + 1) & 1) * H::LDS_BUF;
-                hl_load_x<BITS, TMW>(a, map, xr, grp + 1, nb, pw);
-                hl_store<BITS, TMW>(st, nb, t);
-                hl_load<BITS, TMW>(st, a, wr, sr, br, grp + 2 < last ? grp + 2 : last, t);
-                __builtin_amdgcn_s_waitcnt(0x0F70 | kHlLoads<BITS>);  // the staged x has landed
+                hl_load_x<H::BM>(a, map, xr, grp + 1, nb, pw);
+                F::store(st, part(nb, 0), part(nb, F::kParts - 1), t);
+                F::load(st, a, wr, sr, br, grp + 2 < last ? grp + 2 : last, t);
+                __builtin_amdgcn_s_waitcnt(0x0F70 | F::kLoads);  // the staged x has landed
             }
             __syncthreads();
         }
@@ -557,7 +615,7 @@ __device__ __forceinline__ void hl_tile(const QmmArgs &a, const Map &map, const 
         for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
     for (int grp = 0; grp < a.G; ++grp) {
-        hl_compute<BITS, TMW>(lds + (grp & 1) * H::LDS_BUF, wm, wn, acc);
+        hl_compute<F, TMW>(lds + (grp & 1) * H::LDS_BUF, wm, wn, acc);
         __syncthreads();
     }
     // Store: lane holds rows 4g + r of sub-tile m, weight row i of sub-tile n.
@@ -570,7 +628,8 @@ __device__ __forceinline__ void hl_tile(const QmmArgs &a, const Map &map, const 
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
                 const int64_t col = wn * 64 + 16 * n + i;
-                if (col < nrows) a.y[yr * a.N + n0 + col] = f32_to_bf16(acc[m][n][r]);
+                const float v = F::kScaled ? acc[m][n][r] * a.ts : acc[m][n][r];
+                if (col < nrows) a.y[yr * a.N + n0 + col] = f32_to_bf16(v);
             }
         }
 }
@@ -586,12 +645,13 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
     qmm_tile<BITS, TM, TN, DEPTH, TT::PIPE>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * TT::BN, qmm_lds);
 }
 
-// Large tiles, dense: blockIdx.x = 128-row weight tile, blockIdx.y = activation-row tile.
-template <int BITS, int TMW>
+// Split-weight tiles, dense: blockIdx.x = 128-row weight tile, blockIdx.y =
+// activation-row tile; F: the weight format.
+template <typename F, int TMW>
 __global__ __launch_bounds__(512) void qmm_hl_kernel(QmmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
-    const DenseMap map{(int64_t)blockIdx.y * Hl<BITS, TMW>::BM, a.M};
-    hl_tile<BITS, TMW>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * Hl<BITS, TMW>::BN, qmm_lds);
+    const DenseMap map{(int64_t)blockIdx.y * Hl<F, TMW>::BM, a.M};
+    hl_tile<F, TMW>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * Hl<F, TMW>::BN, qmm_lds);
 }
 
 namespace {
@@ -678,7 +738,7 @@ __global__ __launch_bounds__(256) void gather_qmm_kernel(QmmArgs a) {
 template <int BITS, int TMW>
 __global__ __launch_bounds__(512) void gather_qmm_hl_kernel(QmmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
-    using H = Hl<BITS, TMW>;
+    using H = Hl<AffineFmt<BITS>, TMW>;
     uint16_t *plist = reinterpret_cast<uint16_t *>(qmm_lds + 2 * H::LDS_BUF);
     uint32_t *xlist = reinterpret_cast<uint32_t *>(qmm_lds + 2 * H::LDS_BUF + ((a.M * 2 + 15) / 16) * 16);
     __shared__ int wave_counts[8];
@@ -690,7 +750,7 @@ __global__ __launch_bounds__(512) void gather_qmm_hl_kernel(QmmArgs a) {
     const uint16_t *s = a.s + plane * a.G, *b = a.b + plane * a.G;
     for (int base = 0; base < count; base += H::BM) {
         const GatherMap map{plist + base, xlist + base, count - base < H::BM ? count - base : H::BM};
-        hl_tile<BITS, TMW>(a, map, w, s, b, n0, qmm_lds);
+        hl_tile<AffineFmt<BITS>, TMW>(a, map, w, s, b, n0, qmm_lds);
         __syncthreads();  // the LDS tiles are refilled by the next pass
     }
 }
@@ -712,11 +772,12 @@ static QmmKernel qmm_pick(bool gather) {
 template <int BITS, int TMW>
 static QmmKernel hl_pick(bool gather) {
     QmmKernel k;
+    using H = Hl<AffineFmt<BITS>, TMW>;
     k.sym = gather ? reinterpret_cast<const void *>(&gather_qmm_hl_kernel<BITS, TMW>)
-                   : reinterpret_cast<const void *>(&qmm_hl_kernel<BITS, TMW>);
-    k.bm = Hl<BITS, TMW>::BM;
-    k.bn = Hl<BITS, TMW>::BN;
-    k.lds = 2 * Hl<BITS, TMW>::LDS_BUF;
+                   : reinterpret_cast<const void *>(&qmm_hl_kernel<AffineFmt<BITS>, TMW>);
+    k.bm = H::BM;
+    k.bn = H::BN;
+    k.lds = 2 * H::LDS_BUF;
     k.threads = 512;
     return k;
 }
@@ -724,10 +785,11 @@ static QmmKernel hl_pick(bool gather) {
 QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t planes, int cus) {
     static_assert(Tile<4, 2, 2>::BN == kQmmTileN && Tile<4, 4, 2>::BN == kQmmTileN && Tile<4, 2, 2>::BM == kQmmTileMinM,
                   "the host checks assume these tile sizes");
-    static_assert(Hl<4, 8>::BN == kQmmHlTileN && Hl<4, 8>::BM >= kQmmTileMinM, "the host checks assume these tile sizes");
+    static_assert(Hl<AffineFmt<4>, 8>::BN == kQmmHlTileN && Hl<AffineFmt<4>, 8>::BM >= kQmmTileMinM,
+                  "the host checks assume these tile sizes");
     // Split-weight tiles where the rows fill them and their grid gives every
     // compute unit a block.
-    constexpr int HBM = Hl<4, 8>::BM;
+    constexpr int HBM = Hl<AffineFmt<4>, 8>::BM;
     if (rows >= kQmmHlMinRows && planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN) * ((rows + HBM - 1) / HBM) >= cus)
         return bits == 4 ? hl_pick<4, 8>(gather) : hl_pick<8, 8>(gather);
     constexpr int LBM = Tile<4, 4, 2>::BM;
@@ -736,6 +798,24 @@ QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t
                        large_blocks < (int64_t)kQmmLargeBlocksPerCu * cus;
     if (bits == 4) return small ? qmm_pick<4, 2, 2, 4>(gather) : qmm_pick<4, 4, 2, 2>(gather);
     return small ? qmm_pick<8, 2, 2, 4>(gather) : qmm_pick<8, 4, 2, 2>(gather);
+}
+
+// The NVFP4 GEMM for M activation rows: 256-row tiles where their grid gives
+// every compute unit a block, 64-row tiles otherwise.
+QmmKernel qmm_nvfp4_kernel_for(int64_t M, int64_t N, int cus) {
+    using HL = Hl<Nvfp4Fmt, 8>;
+    using HS = Hl<Nvfp4Fmt, 2>;
+    static_assert(HL::BN == kQmmHlTileN && HS::BN == kQmmHlTileN && HS::BM >= kQmmTileMinM,
+                  "the host checks assume these tile sizes");
+    const bool large = M >= kQmmHlMinRows && ((N + HL::BN - 1) / HL::BN) * ((M + HL::BM - 1) / HL::BM) >= cus;
+    QmmKernel k;
+    k.sym = large ? reinterpret_cast<const void *>(&qmm_hl_kernel<Nvfp4Fmt, 8>)
+                  : reinterpret_cast<const void *>(&qmm_hl_kernel<Nvfp4Fmt, 2>);
+    k.bm = large ? HL::BM : HS::BM;
+    k.bn = HL::BN;
+    k.lds = 2 * (large ? HL::LDS_BUF : HS::LDS_BUF);
+    k.threads = 512;
+    return k;
 }
 
 }  // namespace agq

@@ -320,8 +320,8 @@ TITLES = {"llama": "Llama-3-8B-shaped decode GEMV set, batch 1, 4-bit gs64",
           "layer": "Llama-shaped decode layer projections through the fused batch-1 kernel (norm + qkv, "
                    "o + residual, norm + gate/up + SwiGLU, down + residual, final norm + lm_head), against the "
                    "bare products and the unfused sequence (4-bit gs64)",
-          "nvfp4": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, NVFP4 weights (E2M1 codes, E4M3 scale per "
-                   "16 columns), against the affine 4-bit gs64 product on the same shapes"}
+          "nvfp4": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, and GEMMs at M = 16, 256, 2048, NVFP4 weights "
+                   "(E2M1 codes, E4M3 scale per 16 columns), against the affine 4-bit gs64 products on the same shapes"}
 
 
 def write_profiles(workload, dirs):
@@ -739,7 +739,8 @@ def layer_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
 
 def nvfp4_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
     """Workload 1's five products with NVFP4 weights at M = 1 and 4, each against the affine
-    4-bit gs64 product (agq_qmv / agq_qmv_wide) on the same shape and activations. Both
+    4-bit gs64 product (agq_qmv / agq_qmv_wide) on the same shape and activations, and the
+    matrix-core GEMMs (agq_qmm_nvfp4, agq_qmm) at M = 16, 256 and 2048 on all but lm_head. Both
     formats carry N*K/2 code bytes and N*K/16 scale bytes, so the algorithmic bytes match.
     The NVFP4 weights are nvfp4_weight rows (stream cfg 12) drawn for at most 4096 rows and
     repeated down to N: every code word costs the kernel the same fixed-latency converts and
@@ -767,13 +768,25 @@ def nvfp4_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
         aff = rotation(u32, bf16, m, weight_bytes(N, K, 4))
         aptr = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr()) for c in aff]
         arot = len(aff)
-        xall = bf16(si.draw_activations(12, 100 + t, 4, K))
-        for M in (1, 4):
+        gemm_ms = (16, 256, 2048) if name != "lm_head" else ()
+        xall = bf16(si.draw_activations(12, 100 + t, max(gemm_ms + (4,)), K))
+        for M in (1, 4) + gemm_ms:
             x = xall[:M].contiguous()
             y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-            agq.qmv_nvfp4(x, *fp4[0], ts, out=y)  # validates the operands once
+            agq.qmm_nvfp4(x, *fp4[0], ts, out=y)  # validates the operands once
             xp, yp = x.data_ptr(), y.data_ptr()
             nb = algo_bytes(N, K, 4, M)
+            if M > 4:
+                # the GEMM lines: both formats, against the bf16 matrix-core peak
+                flops = 2 * M * N * K
+                calls = max(2, args.calls // (4 if M >= 2048 else 1))
+                us, us_min = time_shape(torch, lambda i: agq.lib.agq_qmm_nvfp4(xp, *fptr[i % rot], ts, yp, M, N, K,
+                                                                                 st), calls, 5, stream)
+                emit(qmm_line(f"nvfp4 qmm: {name} {N}x{K} M={M}", us, us_min, flops, nb))
+                ua, ua_min = time_shape(torch, lambda i: agq.lib.agq_qmm(xp, *aptr[i % arot], yp, M, N, K, 4, 64, st),
+                                        calls, 5, stream)
+                emit(qmm_line(f"affine qmm: {name} {N}x{K} M={M}", ua, ua_min, flops, nb))
+                continue
             ceil = calib.ceiling(nb) if calib else None
             us, us_min = time_shape(torch, lambda i: agq.lib.agq_qmv_nvfp4(xp, *fptr[i % rot], ts, yp, M, N, K, st),
                                     args.calls, 5, stream)

@@ -200,6 +200,20 @@ agq_status agq_qmv_nvfp4(const void *x, const uint32_t *w, const void *scales, f
                          int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * NVFP4 product for any number of activation rows (prefill as well as decode):
+ * the same operands and result as agq_qmv_nvfp4, with M >= 1. Up to 4 rows it
+ * is agq_qmv_nvfp4. Beyond, either passes of up to 4 rows through that kernel
+ * (few rows, or K not a multiple of 64) or a matrix-core GEMM: each weight's
+ * value e2m1(q) * e4m3(s) has at most 6 significant bits, so it goes to the
+ * matrix cores as an exact bfloat16, with fp32 accumulation over K and the
+ * tensor scale applied to each result once before its bfloat16 rounding. The
+ * choice is made on the host from the shape. M*K*2 must stay below 2^31.
+ * Same argument checks and errors as agq_qmv_nvfp4 otherwise.
+ */
+agq_status agq_qmm_nvfp4(const void *x, const uint32_t *w, const void *scales, float tensor_scale, void *y,
+                         int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * Expert-gathered matrix-matrix product (MoE prefill, the gather_qmm of the
  * same epic: its Diagnosis (baseline) MoE prefill row is the largest measured
  * gap on those pages, and Phase 3 (#629) targets it). Same arguments and

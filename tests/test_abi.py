@@ -83,6 +83,10 @@ def nvfp4(M=1, N=16, K=64, ts=1.0, x=A, w=A, s=A, y=A):
     return lib.agq_qmv_nvfp4(x, w, s, ts, y, M, N, K, None)
 
 
+def nvfp4mm(M=64, N=16, K=64, ts=1.0, x=A, w=A, s=A, y=A):
+    return lib.agq_qmm_nvfp4(x, w, s, ts, y, M, N, K, None)
+
+
 def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     return lib.agq_gather_qmm(x, A, A, A, lhs, rhs, A, P, R, E, N, K, bits, gs, None)
 
@@ -167,6 +171,17 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: nvfp4(x=A2), EINVAL),
     (lambda: nvfp4(K=114688 + 32), ENOTSUP),
     (lambda: nvfp4(M=4, K=32768 + 32), ENOTSUP),
+    (lambda: nvfp4mm(x=NUL), EINVAL),
+    (lambda: nvfp4mm(s=NUL), EINVAL),
+    (lambda: nvfp4mm(M=0), EINVAL),
+    (lambda: nvfp4mm(M=3, K=48), ENOTSUP),
+    (lambda: nvfp4mm(K=24), EINVAL),
+    (lambda: nvfp4mm(K=48), ENOTSUP),
+    (lambda: nvfp4mm(N=0), EINVAL),
+    (lambda: nvfp4mm(ts=float("nan")), EINVAL),
+    (lambda: nvfp4mm(s=ctypes.c_void_p(0x10001)), EINVAL),
+    (lambda: nvfp4mm(x=A2), EINVAL),
+    (lambda: nvfp4mm(M=1 << 20, K=1024), ENOTSUP),
     (lambda: gqmm(P=0), EINVAL),
     (lambda: gqmm(lhs=NUL, R=3), EINVAL),
     (lambda: gqmm(rhs=NUL, E=3), EINVAL),

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import seeded_inputs as si
-from gpu_util import bf16_bits_host, bf16_dev, check_close, progress, u32_dev
+from gpu_util import bf16_bits_host, bf16_dev, bf16_host, check_close, progress, u32_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -121,3 +121,81 @@ def test_nvfp4_is_deterministic():
     b = agq.qmv_nvfp4(x, w, s, d["tensor_scale"])
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------- any M (agq_qmm_nvfp4)
+
+def seam_rows(N):
+    n = np.arange(N)
+    keep = np.isin(n % 128, [0, 15, 16, 31, 32, 63, 64, 127]) | (n % 13 == 0) | (n == N - 1)
+    return n[keep]
+
+
+@pytest.mark.parametrize("M,N,K,sample", [
+    (5, 300, 64, False), (8, 1000, 512, False), (17, 129, 1024, False), (64, 4096, 4096, True),
+    (100, 333, 2048, False), (300, 2000, 4096, True), (255, 128, 192, False),
+    # passes of 4 rows through the matvec kernel: few rows on a large matrix, K % 64 != 0
+    (16, 4096, 4096, True), (6, 500, 96, False), (13, 200, 2080, False),
+    # grids of 256-row tiles that fill the device
+    (1024, 8192, 512, True), (2048, 4096, 1024, True), (1100, 33000, 256, True),
+])
+def test_qmm_nvfp4_shapes(M, N, K, sample):
+    """The matrix-core NVFP4 GEMM (64- and 256-row tiles) against the oracle, with ragged
+    activation and weight rows; seam rows and every 13th where the oracle would be slow."""
+    d = si.nvfp4_weight(13, M + N, N, K)
+    x = si.draw_activations(13, 100 + M, M, K)
+    progress(f"qmm_nvfp4 M={M} N={N} K={K}")
+    y = agq.qmm_nvfp4(bf16_dev(x), u32_dev(d["w"]), u8_dev(d["scales"]), d["tensor_scale"])
+    torch.cuda.synchronize()
+    rows = seam_rows(N) if sample else None
+    y_ref, a = oracle.qmv_nvfp4(x, d["w"], d["scales"], d["tensor_scale"], K, rows=rows)
+    yg = y if rows is None else y[:, torch.as_tensor(rows, device=y.device)]
+    worst = check_close(yg, y_ref, a, f"qmm_nvfp4 M={M} N={N} K={K}", extra_half_ulp=K <= 128)
+    progress(f"qmm_nvfp4: ok, worst |err|/A = {worst:.3e}")
+
+
+@pytest.mark.parametrize("M,N", [(256, 300), (1024, 8192)])
+def test_qmm_nvfp4_one_hot_columns_are_bitwise_weights(M, N):
+    """x = e_k gives y[n] = bf16(e2m1(q[n, k]) * e4m3(s[n, k/16])) bit for bit on both tile
+    sizes: the weight goes to the matrix cores exactly (code 8, -0, compared as +0)."""
+    K = M
+    g = np.random.default_rng([14, N])
+    codes = g.integers(0, 16, size=(N, K), dtype=np.uint8)
+    scales = g.integers(0x01, 0x7F, size=(N, K // 16), dtype=np.uint8)
+    e2m1 = np.array([oracle.load().agqo_e2m1(c) for c in range(16)])
+    e4m3 = np.array([oracle.load().agqo_e4m3(b) for b in range(256)])
+    want = si.bf16_bits((e2m1[codes] * e4m3[np.repeat(scales, 16, axis=1)]).astype(np.float32) + np.float32(0))
+    cols = np.arange(K)
+    x = np.zeros((K, K), np.uint16)
+    x[cols, cols] = 0x3F80
+    progress(f"qmm_nvfp4 one-hot M={M} N={N}")
+    got = bf16_bits_host(agq.qmm_nvfp4(bf16_dev(x), u32_dev(si.pack_codes(codes, 4)), u8_dev(scales), 1.0))
+    bad = np.argwhere(got != want.T)
+    assert bad.size == 0, (bad[:8], got[tuple(bad[:8].T)], want.T[tuple(bad[:8].T)])
+
+
+def test_qmm_nvfp4_nan_scale_and_small_m_route():
+    """A NaN scale byte makes NaN exactly the outputs of its weight row, in every activation
+    row; up to 4 rows the call is the matvec product, bit for bit."""
+    M, N, K = 64, 200, 512
+    d = si.nvfp4_weight(15, 0, N, K)
+    sc = d["scales"].copy()
+    sc[7, 3] = 0xFF
+    x = si.draw_activations(15, 1, M, K)
+    w, s = u32_dev(d["w"]), u8_dev(sc)
+    progress("qmm_nvfp4 NaN scale, small-M route")
+    y = bf16_host(agq.qmm_nvfp4(bf16_dev(x), w, s, d["tensor_scale"]))
+    nan = np.isnan(y)
+    assert np.array_equal(np.flatnonzero(nan.any(axis=0)), [7]) and nan[:, 7].all()
+    for m in (1, 3, 4):
+        a = agq.qmm_nvfp4(bf16_dev(x[:m]), w, s, d["tensor_scale"])
+        b = agq.qmv_nvfp4(bf16_dev(x[:m]), w, s, d["tensor_scale"])
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # K % 64 != 0: passes of 4 rows for any M, bit for bit the matvec kernel's rows
+    d2 = si.nvfp4_weight(15, 1, N, 96)
+    x2 = si.draw_activations(15, 2, 11, 96)
+    w2, s2 = u32_dev(d2["w"]), u8_dev(d2["scales"])
+    a = bf16_bits_host(agq.qmm_nvfp4(bf16_dev(x2), w2, s2, 0.5))
+    b = np.concatenate([bf16_bits_host(agq.qmv_nvfp4(bf16_dev(x2[r:r + 4]), w2, s2, 0.5)) for r in (0, 4, 8)])
+    assert np.array_equal(a, b)
