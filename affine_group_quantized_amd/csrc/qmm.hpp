@@ -23,10 +23,11 @@ constexpr int kQmmSmallM = 128;
 constexpr int kQmmSmallPairs = 64;
 constexpr int kQmmLargeBlocksPerCu = 2;
 // Split-weight tiles (256 x 128, qmm_hl_kernel) from this many rows, where
-// their grid gives every compute unit a block (4-bit, us: 4096x4096 at M =
-// 2048: 157 -> 107; 28672x4096 at M = 512 / 2048: 326 / 1221 -> 218 / 796;
-// 4096x14336 at M = 2048: 554 -> 341). Tiles of 128 rows lost at M = 256
-// (28672x4096: 166 -> 174) and on the Mixtral prefill gather.
+// their grid gives at least 3/4 of the compute units a block (a partial round
+// costs a full one) (4-bit, us: 4096x4096 at M = 2048: 157 -> 107; 28672x4096
+// at M = 256 / 512 / 2048: 166 / 326 / 1221 -> 110 / 218 / 796; 4096x14336 at
+// M = 2048: 554 -> 341). Tiles of 128 rows lost at M = 256 (28672x4096: 166 ->
+// 174) and on the Mixtral prefill gather.
 constexpr int kQmmHlMinRows = 256;
 constexpr int kQmmPassRows = 128;  // 4-bit products of up to this many rows run on the matvec kernel in passes of 16
 

@@ -790,7 +790,7 @@ QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t
     // Split-weight tiles where the rows fill them and their grid gives every
     // compute unit a block.
     constexpr int HBM = Hl<AffineFmt<4>, 8>::BM;
-    if (rows >= kQmmHlMinRows && planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN) * ((rows + HBM - 1) / HBM) >= cus)
+    if (rows >= kQmmHlMinRows && 4 * planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN) * ((rows + HBM - 1) / HBM) >= 3 * cus)
         return bits == 4 ? hl_pick<4, 8>(gather) : hl_pick<8, 8>(gather);
     constexpr int LBM = Tile<4, 4, 2>::BM;
     const int64_t large_blocks = planes * ((rows + LBM - 1) / LBM) * ((N + kQmmTileN - 1) / kQmmTileN);
@@ -807,7 +807,7 @@ QmmKernel qmm_nvfp4_kernel_for(int64_t M, int64_t N, int cus) {
     using HS = Hl<Nvfp4Fmt, 2>;
     static_assert(HL::BN == kQmmHlTileN && HS::BN == kQmmHlTileN && HS::BM >= kQmmTileMinM,
                   "the host checks assume these tile sizes");
-    const bool large = M >= kQmmHlMinRows && ((N + HL::BN - 1) / HL::BN) * ((M + HL::BM - 1) / HL::BM) >= cus;
+    const bool large = M >= kQmmHlMinRows && 4 * ((N + HL::BN - 1) / HL::BN) * ((M + HL::BM - 1) / HL::BM) >= 3 * cus;
     QmmKernel k;
     k.sym = large ? reinterpret_cast<const void *>(&qmm_hl_kernel<Nvfp4Fmt, 8>)
                   : reinterpret_cast<const void *>(&qmm_hl_kernel<Nvfp4Fmt, 2>);
