@@ -62,9 +62,13 @@ def _load(path: str = LIB_PATH):
     lib.agq_qmv_wide.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
     lib.agq_qmv_fused.argtypes = [P, P, ctypes.c_float, P, P, P, P, I, P, I64, I64, I, I, P]
     lib.agq_qmv_nvfp4.argtypes = [P, P, P, ctypes.c_float, P, I64, I64, I64, P]
-    lib.agq_qmm_nvfp4.argtypes = [P, P, P, ctypes.c_float, P, I64, I64, I64, P]
+    lib.agq_qmm_nvfp4.argtypes = [P, P, P, ctypes.c_float, P, I64, I64, I64, P, I64, P]
+    lib.agq_qmm_nvfp4_workspace.argtypes = [I64, I64, I64]
+    lib.agq_qmm_nvfp4_workspace.restype = I64
     lib.agq_gather_qmv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
-    lib.agq_qmm.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P]
+    lib.agq_qmm.argtypes = [P, P, P, P, P, I64, I64, I64, I, I, P, I64, P]
+    lib.agq_qmm_workspace.argtypes = [I64, I64, I64, I, I]
+    lib.agq_qmm_workspace.restype = I64
     lib.agq_gather_qmm.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, I, P]
     lib.agq_moe_decode_workspace.argtypes = [I64, I64, I64, I64]
     lib.agq_moe_decode_workspace.restype = I64
@@ -187,7 +191,18 @@ def qmv_fused(x, w, scales, biases, bits: int = 4, group_size: int = 64, norm_we
     return out
 
 
-def _nvfp4(fn, x, w, scales, tensor_scale, out):
+def _workspace(nbytes, workspace, device):
+    """(pointer, bytes) of the GEMM workspace: ``workspace`` if given (a device uint8
+    tensor), else a fresh one of ``nbytes`` when the call can use one, else none."""
+    if workspace is False or (workspace is None and nbytes <= 0):
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", (torch.uint8,), device)
+    return workspace, workspace.numel()
+
+
+def _nvfp4(fn, x, w, scales, tensor_scale, out, workspace=False):
     device = x.device
     _need(x, "x", _BF16, device)
     _need(w, "w", _U32, device)
@@ -207,7 +222,12 @@ def _nvfp4(fn, x, w, scales, tensor_scale, out):
         if out.numel() != M * N:
             raise ValueError("out has the wrong size")
     with torch.cuda.device(device):
-        _check(fn(_ptr(x), _ptr(w), _ptr(scales), float(tensor_scale), _ptr(out), M, N, K, _stream(device)))
+        if fn is lib.agq_qmm_nvfp4:
+            ws, nb = _workspace(lib.agq_qmm_nvfp4_workspace(M, N, K) if workspace is None else 0, workspace, device)
+            _check(fn(_ptr(x), _ptr(w), _ptr(scales), float(tensor_scale), _ptr(out), M, N, K, _ptr(ws), nb,
+                      _stream(device)))
+        else:
+            _check(fn(_ptr(x), _ptr(w), _ptr(scales), float(tensor_scale), _ptr(out), M, N, K, _stream(device)))
     return out
 
 
@@ -217,10 +237,12 @@ def qmv_nvfp4(x, w, scales, tensor_scale: float = 1.0, out=None):
     return _nvfp4(lib.agq_qmv_nvfp4, x, w, scales, tensor_scale, out)
 
 
-def qmm_nvfp4(x, w, scales, tensor_scale: float = 1.0, out=None):
+def qmm_nvfp4(x, w, scales, tensor_scale: float = 1.0, out=None, workspace=None):
     """NVFP4 product for any number of rows ``x`` [M, K] (agq_qmm_nvfp4: up to 4 rows the
-    matvec kernel, beyond it the matrix-core GEMM, which needs K % 64 == 0)."""
-    return _nvfp4(lib.agq_qmm_nvfp4, x, w, scales, tensor_scale, out)
+    matvec kernel, beyond it the matrix-core GEMM, which needs K % 64 == 0). ``workspace``:
+    None allocates the K split's scratch where the call can use one, a device uint8 tensor
+    is used as given, False runs without a split."""
+    return _nvfp4(lib.agq_qmm_nvfp4, x, w, scales, tensor_scale, out, workspace)
 
 
 def prepare_qmv(x, w, scales, biases, out, bits: int = 4, group_size: int = 64, stream=None):
@@ -271,8 +293,10 @@ def qmv_wide(x, w, scales, biases, bits: int = 4, group_size: int = 64, out=None
     return out
 
 
-def qmm(x, w, scales, biases, bits: int = 4, group_size: int = 64, out=None):
-    """Quantized matrix-matrix product: ``x`` [M, K] bf16 (any M) -> ``y`` [M, N] bf16."""
+def qmm(x, w, scales, biases, bits: int = 4, group_size: int = 64, out=None, workspace=None):
+    """Quantized matrix-matrix product: ``x`` [M, K] bf16 (any M) -> ``y`` [M, N] bf16.
+    ``workspace``: None allocates the K split's scratch where the call can use one, a device
+    uint8 tensor is used as given, False runs without a split."""
     device = x.device
     _need(x, "x", _BF16, device)
     if x.dim() != 2:
@@ -286,8 +310,10 @@ def qmm(x, w, scales, biases, bits: int = 4, group_size: int = 64, out=None):
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
     with torch.cuda.device(device):
+        need = lib.agq_qmm_workspace(M, N, K, bits, group_size) if workspace is None else 0
+        ws, nb = _workspace(need, workspace, device)
         _check(lib.agq_qmm(_ptr(x), _ptr(w), _ptr(scales), _ptr(biases), _ptr(out), M, N, K, bits, group_size,
-                           _stream(device)))
+                           _ptr(ws), nb, _stream(device)))
     return out
 
 

@@ -481,19 +481,77 @@ agq_status agq_qmv_nvfp4(const void *x, const uint32_t *w, const void *scales, f
 // plus 3 us. Measured (us, GEMM / passes): 4096x4096 at M = 16 / 32: 37.9 / 22.3,
 // 39.1 / 44.4; 28672x4096 at M = 8 / 16: 53.8 / 39.8, 52.8 / 77.3; 4096x14336 at
 // M = 32 / 64: 138.5 / 99.5, 142.1 / 196.1.
-bool nvfp4_passes_win(int64_t M, int64_t N, int64_t K, int cus) {
+// With a K split each block walks its split's groups, and the partials cost
+// their bytes twice at 4 TB/s plus a launch.
+bool nvfp4_passes_win(int64_t M, int64_t N, int64_t K, int cus, const agq::QmmKernel &k) {
     const double pass_us = (double)N * (double)K * 0.5625 / 4.5e6 + 3.0;
     const double passes_us = (double)((M + 3) / 4) * pass_us;
-    const agq::QmmKernel k = agq::qmm_nvfp4_kernel_for(M, N, cus);
-    const int64_t blocks = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn);
-    const double gemm_us = (double)(K / 64) * 0.6 * (double)((blocks + cus - 1) / cus);
+    const int64_t blocks = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) * k.splits;
+    const double groups = k.splits > 1 ? (double)k.gps : (double)(K / 64);
+    const double reduce_us = k.splits > 1 ? 2.0 * (double)agq::qmm_split_bytes(k, M, N) / 4.0e6 + 3.0 : 0.0;
+    const double gemm_us = groups * 0.6 * (double)((blocks + cus - 1) / cus) + reduce_us;
     return passes_us < gemm_us;
 }
 
+// Workspace checks of the GEMM entry points: NULL (no K split), or at least
+// `need` bytes, 16-byte aligned.
+agq_status check_workspace(const void *ws, int64_t ws_bytes, int64_t need) {
+    if (!ws) return AGQ_OK;
+    if (misaligned(ws, 16)) return fail(AGQ_EINVAL, "workspace must be 16-byte aligned");
+    if (ws_bytes < need)
+        return fail(AGQ_EINVAL, "workspace of %lld bytes is below the %lld this call needs", (long long)ws_bytes,
+                    (long long)need);
+    return AGQ_OK;
+}
+
+// The GEMM launch, then (with a K split) the reduction of the partials into y.
+agq_status launch_qmm(const agq::QmmKernel &k, agq::QmmArgs &a, int64_t M, int64_t N, void *ws, int dev,
+                      void *stream) {
+    const int64_t mt = (M + k.bm - 1) / k.bm, nt = (N + k.bn - 1) / k.bn;
+    agq_status st = allow_lds(k.sym, (size_t)k.lds, dev);
+    if (st != AGQ_OK) return st;
+    if (k.splits <= 1) {
+        a.gps = a.G;
+        return launch(k.sym, dim3((unsigned)nt, (unsigned)mt), dim3(k.threads), (size_t)k.lds, &a, stream);
+    }
+    a.part = static_cast<float *>(ws);
+    a.gps = k.gps;
+    st = launch(k.sym, dim3((unsigned)nt, (unsigned)mt, (unsigned)k.splits), dim3(k.threads), (size_t)k.lds, &a,
+                stream);
+    if (st != AGQ_OK) return st;
+    int64_t MN = M * N;
+    const float *part = a.part;
+    uint16_t *y = a.y;
+    int splits = k.splits;
+    float ts = a.ts;
+    void *args[] = {&part, &y, &MN, &splits, &ts};
+    hipError_t e = hipLaunchKernel(agq::qmm_reduce_kernel(), dim3((unsigned)((MN + 1023) / 1024)), dim3(256), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(AGQ_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return AGQ_OK;
+}
+
+// Whether an NVFP4 GEMM call takes the matrix-core kernels (else passes of the
+// matvec kernel), and which, on `cus` compute units.
+bool nvfp4_gemm_plan(int64_t M, int64_t N, int64_t K, int cus, bool split_ok, agq::QmmKernel *k) {
+    *k = agq::qmm_nvfp4_kernel_for(M, N, K, cus, split_ok);
+    return K % 64 == 0 && !nvfp4_passes_win(M, N, K, cus, *k);
+}
+
+int64_t agq_qmm_nvfp4_workspace(int64_t M, int64_t N, int64_t K) {
+    if (M <= 4 || N <= 0 || K <= 0 || K % 32 != 0 || N > kMaxN || K > kMaxK) return 0;
+    if (M * K * 2 >= (int64_t(1) << 31)) return 0;
+    int cus = 0, dev = 0;
+    if (current_device(&cus, &dev) != AGQ_OK) return 0;
+    agq::QmmKernel k;
+    return nvfp4_gemm_plan(M, N, K, cus, true, &k) ? agq::qmm_split_bytes(k, M, N) : 0;
+}
+
 agq_status agq_qmm_nvfp4(const void *x, const uint32_t *w, const void *scales, float tensor_scale, void *y, int64_t M,
-                         int64_t N, int64_t K, void *stream) {
+                         int64_t N, int64_t K, void *workspace, int64_t workspace_bytes, void *stream) {
     if (M <= 4) return agq_qmv_nvfp4(x, w, scales, tensor_scale, y, M, N, K, stream);
     if (!x || !w || !scales || !y) return fail(AGQ_EINVAL, "null tensor pointer");
+    if (workspace && misaligned(workspace, 16)) return fail(AGQ_EINVAL, "workspace must be 16-byte aligned");
     if (N <= 0 || K <= 0) return fail(AGQ_EINVAL, "N and K must be positive (N=%lld, K=%lld)", (long long)N, (long long)K);
     if (N > kMaxN || K > kMaxK) return fail(AGQ_EINVAL, "N or K too large (N=%lld, K=%lld)", (long long)N, (long long)K);
     if (K % 16 != 0) return fail(AGQ_EINVAL, "K=%lld is not a multiple of the NVFP4 block of 16", (long long)K);
@@ -509,7 +567,8 @@ agq_status agq_qmm_nvfp4(const void *x, const uint32_t *w, const void *scales, f
     int cus = 0, dev = 0;
     agq_status st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
-    if (K % 64 != 0 || nvfp4_passes_win(M, N, K, cus)) {
+    agq::QmmKernel k;
+    if (!nvfp4_gemm_plan(M, N, K, cus, workspace != nullptr, &k)) {
         // Passes of up to 4 rows through the matvec kernel.
         for (int64_t r0 = 0; r0 < M; r0 += 4) {
             st = agq_qmv_nvfp4(static_cast<const uint16_t *>(x) + r0 * K, w, scales, tensor_scale,
@@ -518,8 +577,8 @@ agq_status agq_qmm_nvfp4(const void *x, const uint32_t *w, const void *scales, f
         }
         return AGQ_OK;
     }
-    const agq::QmmKernel k = agq::qmm_nvfp4_kernel_for(M, N, cus);
-    const int64_t mt = (M + k.bm - 1) / k.bm, nt = (N + k.bn - 1) / k.bn;
+    st = check_workspace(workspace, workspace_bytes, agq::qmm_split_bytes(k, M, N));
+    if (st != AGQ_OK) return st;
     agq::QmmArgs a{};
     a.x = static_cast<const uint16_t *>(x);
     a.w = w;
@@ -532,9 +591,7 @@ agq_status agq_qmm_nvfp4(const void *x, const uint32_t *w, const void *scales, f
     a.rowbytes = (int32_t)(K / 2);
     a.xbytes = (uint32_t)(M * K * 2);
     a.ts = tensor_scale;
-    st = allow_lds(k.sym, (size_t)k.lds, dev);
-    if (st != AGQ_OK) return st;
-    return launch(k.sym, dim3((unsigned)nt, (unsigned)mt), dim3(k.threads), (size_t)k.lds, &a, stream);
+    return launch_qmm(k, a, M, N, workspace, dev, stream);
 }
 
 agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
@@ -581,10 +638,27 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
                   stream);
 }
 
+// The GEMM kernels of an agq_qmm call beyond the matvec forms (rows > 8, and
+// beyond kQmmPassRows or outside the matrix-core matvec's formats).
+bool qmm_uses_gemm(int64_t M, int64_t N, int64_t K, int bits) {
+    return M > 8 && !(M <= agq::kQmmPassRows && agq::mfma_eligible(M, K, bits, 0, M));
+}
+
+int64_t agq_qmm_workspace(int64_t M, int64_t N, int64_t K, int bits, int group_size) {
+    if (M <= 0 || N <= 0 || K <= 0 || N > kMaxN || K > kMaxK || (bits != 4 && bits != 8) || group_size != 64)
+        return 0;
+    if (K % 64 != 0 || M * K * 2 >= (int64_t(1) << 31) || !qmm_uses_gemm(M, N, K, bits)) return 0;
+    int cus = 0, dev = 0;
+    if (current_device(&cus, &dev) != AGQ_OK) return 0;
+    return agq::qmm_split_bytes(agq::qmm_kernel_for(bits, false, M, N, K, 1, cus, true), M, N);
+}
+
 agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases, void *y, int64_t M,
-                   int64_t N, int64_t K, int bits, int group_size, void *stream) {
+                   int64_t N, int64_t K, int bits, int group_size, void *workspace, int64_t workspace_bytes,
+                   void *stream) {
     agq_status st = check_operands(x, w, scales, biases, y, N, K, bits, group_size, true);
     if (st != AGQ_OK) return st;
+    if (workspace && misaligned(workspace, 16)) return fail(AGQ_EINVAL, "workspace must be 16-byte aligned");
     if (M <= 0) return fail(AGQ_EINVAL, "M must be positive (got %lld)", (long long)M);
     if (M * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (M*K*2 bytes)");
     // Up to 8 rows: the matvec kernels. Up to kQmmPassRows rows of 4-bit codes (K
@@ -609,8 +683,9 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
     int cus = 0, dev = 0;
     st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
-    const agq::QmmKernel k = agq::qmm_kernel_for(bits, false, M, N, 1, cus);
-    const int64_t mt = (M + k.bm - 1) / k.bm, nt = (N + k.bn - 1) / k.bn;
+    const agq::QmmKernel k = agq::qmm_kernel_for(bits, false, M, N, K, 1, cus, workspace != nullptr);
+    st = check_workspace(workspace, workspace_bytes, agq::qmm_split_bytes(k, M, N));
+    if (st != AGQ_OK) return st;
     agq::QmmArgs a{};
     a.x = static_cast<const uint16_t *>(x);
     a.w = w;
@@ -623,9 +698,8 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
     a.G = (int32_t)(K / 64);
     a.rowbytes = (int32_t)(K * bits / 8);
     a.xbytes = (uint32_t)(M * K * 2);
-    st = allow_lds(k.sym, (size_t)k.lds, dev);
-    if (st != AGQ_OK) return st;
-    return launch(k.sym, dim3((unsigned)nt, (unsigned)mt), dim3(k.threads), (size_t)k.lds, &a, stream);
+    a.ts = 1.0f;
+    return launch_qmm(k, a, M, N, workspace, dev, stream);
 }
 
 agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases,
@@ -650,7 +724,7 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
     int cus = 0, dev = 0;
     st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
-    const agq::QmmKernel k = agq::qmm_kernel_for(bits, true, (P + E - 1) / E, N, E, cus);
+    const agq::QmmKernel k = agq::qmm_kernel_for(bits, true, (P + E - 1) / E, N, K, E, cus, false);
     const int64_t nt = (N + k.bn - 1) / k.bn;
     agq::QmmArgs a{};
     a.x = static_cast<const uint16_t *>(x);
@@ -668,6 +742,7 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
     a.xbytes = (uint32_t)(R * K * 2);
     a.R_x = (int32_t)R;
     a.E = (int32_t)E;
+    a.gps = a.G;
     const size_t lds = (size_t)k.lds + (size_t)((P * 2 + 15) / 16 * 16 + P * 4);
     st = allow_lds(k.sym, lds, dev);
     if (st != AGQ_OK) return st;

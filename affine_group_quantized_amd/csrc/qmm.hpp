@@ -49,6 +49,9 @@ struct QmmArgs {
     int32_t R_x;          // gather: rows of x
     int32_t E;            // gather: expert planes
     float ts;             // NVFP4: the tensor scale applied to each result (unused by the affine kernels)
+    float *part;          // K split: fp32 partial products [splits, M, N] (NULL: results go to y)
+    int32_t gps;          // K split: 64-column groups per split (blockIdx.z = split)
+    int32_t pad_;
 };
 
 struct QmmKernel {
@@ -56,13 +59,28 @@ struct QmmKernel {
     int bm = 0, bn = 0;  // tile rows of x and of W
     int lds = 0;         // dynamic LDS bytes of the tile buffers
     int threads = 256;   // block size
+    int splits = 1;      // K splits (grid.z); above 1 the partials go to a workspace and qmm_reduce_kernel sums them
+    int gps = 0;         // 64-column groups per split
 };
 
+// K splits of the split-weight tiles: where a grid of them leaves compute
+// units idle, blockIdx.z takes a run of at least kQmmSplitMinGroups groups and
+// the splits' fp32 partials meet in a workspace.
+constexpr int kQmmSplitMinGroups = 4;
+
 // The kernel for `rows` activation rows (dense M, or the gather's pairs per
-// expert plane) against N weight rows in `planes` planes on `cus` compute units.
-QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t planes, int cus);
+// expert plane) against N weight rows of K columns in `planes` planes on
+// `cus` compute units; K splits only where split_ok (dense, with a workspace).
+QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t K, int64_t planes, int cus,
+                         bool split_ok);
 // The NVFP4 GEMM (E2M1 codes, E4M3 scales per 16 columns) for M > 4 activation rows.
-QmmKernel qmm_nvfp4_kernel_for(int64_t M, int64_t N, int cus);
+QmmKernel qmm_nvfp4_kernel_for(int64_t M, int64_t N, int64_t K, int cus, bool split_ok);
+// Workspace bytes of a kernel choice: splits * M * N fp32 partials (0 without a split).
+inline int64_t qmm_split_bytes(const QmmKernel &k, int64_t M, int64_t N) {
+    return k.splits > 1 ? (int64_t)k.splits * M * N * 4 : 0;
+}
+// y = bf16(ts * sum over splits of the partials), splits summed in order.
+const void *qmm_reduce_kernel();
 // Tile geometry shared by both shapes (the host checks use it before any HIP call).
 constexpr int kQmmTileN = 64;
 constexpr int kQmmTileMinM = 64;

@@ -566,14 +566,16 @@ __device__ __forceinline__ void hl_compute(const uint8_t *buf, int wm, int wn, f
     }
 }
 
+// Groups g0 .. g1 - 1 of the tile (all of K, or one K split); with a.part
+// the fp32 results go to split blockIdx.z's plane of the partials.
 template <typename F, int TMW, typename Map>
 __device__ __forceinline__ void hl_tile(const QmmArgs &a, const Map &map, const uint32_t *w, const uint16_t *s,
-                                        const uint16_t *b, int64_t n0, uint8_t *lds) {
+                                        const uint16_t *b, int64_t n0, uint8_t *lds, int g0, int g1) {
     using H = Hl<F, TMW>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15;
     const int64_t nrows = a.N - n0 < H::BN ? a.N - n0 : H::BN;
-    const int last = a.G - 1;
+    const int last = g1 - 1;
     // Two roles, one wave of each per SIMD: waves 4-7 stage group grp + 1 into LDS
     // buffer (grp + 1) % 2 (x with direct-to-LDS loads, the weights dequantized
     // into their B parts) while waves 0-3 take group grp's products out of buffer
@@ -589,15 +591,15 @@ __device__ __forceinline__ void hl_tile(const QmmArgs &a, const Map &map, const 
         // The register stage holds the codes of the next group to stage; its
         // reload goes out right after, so each load has a group's products to arrive.
         typename F::Stage st;
-        hl_load_x<H::BM>(a, map, xr, 0, lds, pw);
-        F::load(st, a, wr, sr, br, 0, t);
+        hl_load_x<H::BM>(a, map, xr, g0, lds, pw);
+        F::load(st, a, wr, sr, br, g0, t);
         F::store(st, part(lds, 0), part(lds, F::kParts - 1), t);
-        F::load(st, a, wr, sr, br, last < 1 ? last : 1, t);
+        F::load(st, a, wr, sr, br, last < g0 + 1 ? last : g0 + 1, t);
         __builtin_amdgcn_s_waitcnt(0x0F70 | F::kLoads);  // vmcnt(loads of st): x has landed
         __syncthreads();
-        for (int grp = 0; grp < a.G; ++grp) {
-            if (grp + 1 < a.G) {  // uniform
-                uint8_t *nb = lds + ((grp + 1) & 1) * H::LDS_BUF;
+        for (int grp = g0; grp < g1; ++grp) {
+            if (grp + 1 < g1) {  // uniform
+                uint8_t *nb = lds + ((grp + 1 - g0) & 1) * H::LDS_BUF;
                 hl_load_x<H::BM>(a, map, xr, grp + 1, nb, pw);
                 F::store(st, part(nb, 0), part(nb, F::kParts - 1), t);
                 F::load(st, a, wr, sr, br, grp + 2 < last ? grp + 2 : last, t);
@@ -614,11 +616,12 @@ __device__ __forceinline__ void hl_tile(const QmmArgs &a, const Map &map, const 
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
-    for (int grp = 0; grp < a.G; ++grp) {
-        hl_compute<F, TMW>(lds + (grp & 1) * H::LDS_BUF, wm, wn, acc);
+    for (int grp = g0; grp < g1; ++grp) {
+        hl_compute<F, TMW>(lds + ((grp - g0) & 1) * H::LDS_BUF, wm, wn, acc);
         __syncthreads();
     }
     // Store: lane holds rows 4g + r of sub-tile m, weight row i of sub-tile n.
+    float *pp = a.part ? a.part + (int64_t)blockIdx.z * a.M * a.N : nullptr;
 #pragma unroll
     for (int m = 0; m < TMW; ++m)
 #pragma unroll
@@ -628,8 +631,13 @@ __device__ __forceinline__ void hl_tile(const QmmArgs &a, const Map &map, const 
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
                 const int64_t col = wn * 64 + 16 * n + i;
-                const float v = F::kScaled ? acc[m][n][r] * a.ts : acc[m][n][r];
-                if (col < nrows) a.y[yr * a.N + n0 + col] = f32_to_bf16(v);
+                if (col >= nrows) continue;
+                if (pp) {
+                    pp[yr * a.N + n0 + col] = acc[m][n][r];
+                } else {
+                    const float v = F::kScaled ? acc[m][n][r] * a.ts : acc[m][n][r];
+                    a.y[yr * a.N + n0 + col] = f32_to_bf16(v);
+                }
             }
         }
 }
@@ -646,13 +654,37 @@ __global__ __launch_bounds__(256) void qmm_kernel(QmmArgs a) {
 }
 
 // Split-weight tiles, dense: blockIdx.x = 128-row weight tile, blockIdx.y =
-// activation-row tile; F: the weight format.
+// activation-row tile, blockIdx.z = K split (groups z*gps .. of it); F: the
+// weight format.
 template <typename F, int TMW>
 __global__ __launch_bounds__(512) void qmm_hl_kernel(QmmArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
     const DenseMap map{(int64_t)blockIdx.y * Hl<F, TMW>::BM, a.M};
-    hl_tile<F, TMW>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * Hl<F, TMW>::BN, qmm_lds);
+    const int g0 = (int)blockIdx.z * a.gps;
+    const int g1 = a.G - g0 < a.gps ? a.G : g0 + a.gps;
+    hl_tile<F, TMW>(a, map, a.w, a.s, a.b, (int64_t)blockIdx.x * Hl<F, TMW>::BN, qmm_lds, g0, g1);
 }
+
+// The K splits' partials [splits, M, N] (MN = M * N) summed in split order,
+// times ts, rounded to bf16 into y [M, N]; four outputs per thread.
+__global__ __launch_bounds__(256) void qmm_reduce(const float *part, uint16_t *y, int64_t MN, int splits, float ts) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= MN) return;
+    if (MN % 4 == 0) {  // uniform: every plane starts 16-byte aligned
+        f32x4 v = *reinterpret_cast<const f32x4 *>(part + i);
+        for (int z = 1; z < splits; ++z) v += *reinterpret_cast<const f32x4 *>(part + (int64_t)z * MN + i);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[i + k] = f32_to_bf16(v[k] * ts);
+        return;
+    }
+    for (int k = 0; k < 4 && i + k < MN; ++k) {
+        float v = part[i + k];
+        for (int z = 1; z < splits; ++z) v += part[(int64_t)z * MN + i + k];
+        y[i + k] = f32_to_bf16(v * ts);
+    }
+}
+
+const void *qmm_reduce_kernel() { return reinterpret_cast<const void *>(&qmm_reduce); }
 
 namespace {
 
@@ -750,7 +782,7 @@ __global__ __launch_bounds__(512) void gather_qmm_hl_kernel(QmmArgs a) {
     const uint16_t *s = a.s + plane * a.G, *b = a.b + plane * a.G;
     for (int base = 0; base < count; base += H::BM) {
         const GatherMap map{plist + base, xlist + base, count - base < H::BM ? count - base : H::BM};
-        hl_tile<AffineFmt<BITS>, TMW>(a, map, w, s, b, n0, qmm_lds);
+        hl_tile<AffineFmt<BITS>, TMW>(a, map, w, s, b, n0, qmm_lds, 0, a.G);
         __syncthreads();  // the LDS tiles are refilled by the next pass
     }
 }
@@ -782,16 +814,33 @@ static QmmKernel hl_pick(bool gather) {
     return k;
 }
 
-QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t planes, int cus) {
+// K splits for a grid of `tiles` split-weight tiles over G groups: as many as
+// fit one block per compute unit, each of at least kQmmSplitMinGroups groups;
+// none (k unchanged) unless the split grid gives 3/4 of the compute units a block.
+static bool split_k(QmmKernel &k, int64_t tiles, int64_t G, int cus) {
+    int64_t s = cus / tiles;
+    if (s > G / kQmmSplitMinGroups) s = G / kQmmSplitMinGroups;
+    if (s < 2 || 4 * tiles * s < 3 * (int64_t)cus) return false;
+    k.gps = (int)((G + s - 1) / s);
+    k.splits = (int)((G + k.gps - 1) / k.gps);
+    return true;
+}
+
+QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t K, int64_t planes, int cus,
+                         bool split_ok) {
     static_assert(Tile<4, 2, 2>::BN == kQmmTileN && Tile<4, 4, 2>::BN == kQmmTileN && Tile<4, 2, 2>::BM == kQmmTileMinM,
                   "the host checks assume these tile sizes");
     static_assert(Hl<AffineFmt<4>, 8>::BN == kQmmHlTileN && Hl<AffineFmt<4>, 8>::BM >= kQmmTileMinM,
                   "the host checks assume these tile sizes");
-    // Split-weight tiles where the rows fill them and their grid gives every
-    // compute unit a block.
+    // Split-weight tiles where the rows fill them and their grid, or (dense,
+    // with a workspace) their grid split along K, gives every compute unit a block.
     constexpr int HBM = Hl<AffineFmt<4>, 8>::BM;
-    if (rows >= kQmmHlMinRows && 4 * planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN) * ((rows + HBM - 1) / HBM) >= 3 * cus)
-        return bits == 4 ? hl_pick<4, 8>(gather) : hl_pick<8, 8>(gather);
+    if (rows >= kQmmHlMinRows) {
+        const int64_t tiles = planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN) * ((rows + HBM - 1) / HBM);
+        QmmKernel k = bits == 4 ? hl_pick<4, 8>(gather) : hl_pick<8, 8>(gather);
+        if (4 * tiles >= 3 * (int64_t)cus) return k;
+        if (!gather && split_ok && split_k(k, tiles, K / 64, cus)) return k;
+    }
     constexpr int LBM = Tile<4, 4, 2>::BM;
     const int64_t large_blocks = planes * ((rows + LBM - 1) / LBM) * ((N + kQmmTileN - 1) / kQmmTileN);
     const bool small = rows <= (gather ? kQmmSmallPairs : kQmmSmallM) ||
@@ -800,21 +849,32 @@ QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t
     return small ? qmm_pick<8, 2, 2, 4>(gather) : qmm_pick<8, 4, 2, 2>(gather);
 }
 
-// The NVFP4 GEMM for M activation rows: 256-row tiles where their grid gives
-// every compute unit a block, 64-row tiles otherwise.
-QmmKernel qmm_nvfp4_kernel_for(int64_t M, int64_t N, int cus) {
+// The NVFP4 GEMM for M activation rows: 256-row tiles where their grid, or
+// (with a workspace) their grid split along K, gives every compute unit a
+// block; 64-row tiles (split along K where that fills the device) otherwise.
+QmmKernel qmm_nvfp4_kernel_for(int64_t M, int64_t N, int64_t K, int cus, bool split_ok) {
     using HL = Hl<Nvfp4Fmt, 8>;
     using HS = Hl<Nvfp4Fmt, 2>;
     static_assert(HL::BN == kQmmHlTileN && HS::BN == kQmmHlTileN && HS::BM >= kQmmTileMinM,
                   "the host checks assume these tile sizes");
-    const bool large = M >= kQmmHlMinRows && 4 * ((N + HL::BN - 1) / HL::BN) * ((M + HL::BM - 1) / HL::BM) >= 3 * cus;
     QmmKernel k;
-    k.sym = large ? reinterpret_cast<const void *>(&qmm_hl_kernel<Nvfp4Fmt, 8>)
-                  : reinterpret_cast<const void *>(&qmm_hl_kernel<Nvfp4Fmt, 2>);
-    k.bm = large ? HL::BM : HS::BM;
     k.bn = HL::BN;
-    k.lds = 2 * (large ? HL::LDS_BUF : HS::LDS_BUF);
     k.threads = 512;
+    const int64_t nt = (N + HL::BN - 1) / HL::BN;
+    if (M >= kQmmHlMinRows) {
+        k.sym = reinterpret_cast<const void *>(&qmm_hl_kernel<Nvfp4Fmt, 8>);
+        k.bm = HL::BM;
+        k.lds = 2 * HL::LDS_BUF;
+        const int64_t tiles = nt * ((M + HL::BM - 1) / HL::BM);
+        if (4 * tiles >= 3 * (int64_t)cus || (split_ok && split_k(k, tiles, K / 64, cus))) return k;
+        k.splits = 1;
+        k.gps = 0;
+    }
+    k.sym = reinterpret_cast<const void *>(&qmm_hl_kernel<Nvfp4Fmt, 2>);
+    k.bm = HS::BM;
+    k.lds = 2 * HS::LDS_BUF;
+    const int64_t tiles = nt * ((M + HS::BM - 1) / HS::BM);
+    if (4 * tiles < 3 * (int64_t)cus && split_ok) split_k(k, tiles, K / 64, cus);
     return k;
 }
 

@@ -596,12 +596,15 @@ def qmm_workload(args, torch, si, agq, bf16, u32, stream, st, emit):
             x = bf16(si.draw_activations(6, M, M, K))
             y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
             agq.qmm(x, *cp[0], bits=4, out=y)
+            wsb = agq.lib.agq_qmm_workspace(M, N, K, 4, 64)
+            ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+            wsp = ws.data_ptr() if wsb > 0 else None
             calls = max(4, min(args.calls, int(2e6 / (2 * M * N * K / 1e9 + 1))))
             us, us_min = time_shape(torch, lambda i: agq.lib.agq_qmm(x.data_ptr(), *ptrs[i % rot], y.data_ptr(), M,
-                                                                     N, K, 4, 64, st), calls, 5, stream)
+                                                                     N, K, 4, 64, wsp, wsb, st), calls, 5, stream)
             emit(qmm_line(f"qmm {name} {N}x{K} M={M}", us, us_min, 2 * M * N * K,
                           weight_bytes(N, K, 4) + 2 * M * K + 2 * M * N))
-            del x, y
+            del x, y, ws
         del cp
         torch.cuda.empty_cache()
     moe = si.workload(4, only=("w1",))
@@ -780,11 +783,16 @@ def nvfp4_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
                 # the GEMM lines: both formats, against the bf16 matrix-core peak
                 flops = 2 * M * N * K
                 calls = max(2, args.calls // (4 if M >= 2048 else 1))
+                wsn = agq.lib.agq_qmm_nvfp4_workspace(M, N, K)
+                wsa = agq.lib.agq_qmm_workspace(M, N, K, 4, 64)
+                ws = torch.empty(max(wsn, wsa, 16), dtype=torch.uint8, device=dev)
+                wsp_n = ws.data_ptr() if wsn > 0 else None
+                wsp_a = ws.data_ptr() if wsa > 0 else None
                 us, us_min = time_shape(torch, lambda i: agq.lib.agq_qmm_nvfp4(xp, *fptr[i % rot], ts, yp, M, N, K,
-                                                                                 st), calls, 5, stream)
+                                                                                 wsp_n, wsn, st), calls, 5, stream)
                 emit(qmm_line(f"nvfp4 qmm: {name} {N}x{K} M={M}", us, us_min, flops, nb))
-                ua, ua_min = time_shape(torch, lambda i: agq.lib.agq_qmm(xp, *aptr[i % arot], yp, M, N, K, 4, 64, st),
-                                        calls, 5, stream)
+                ua, ua_min = time_shape(torch, lambda i: agq.lib.agq_qmm(xp, *aptr[i % arot], yp, M, N, K, 4, 64, wsp_a,
+                                                                         wsa, st), calls, 5, stream)
                 emit(qmm_line(f"affine qmm: {name} {N}x{K} M={M}", ua, ua_min, flops, nb))
                 continue
             ceil = calib.ceiling(nb) if calib else None

@@ -144,9 +144,22 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
  * forms. M*K*2 must stay below 2^31 (else AGQ_ENOTSUP). Beyond 8 rows it
  * takes group size 64 (else AGQ_ENOTSUP). Argument checks and errors as for
  * agq_qmv.
+ *
+ * workspace (optional, owned by the caller): device scratch for a K split.
+ * Where the output tiles alone leave compute units idle (a few hundred rows
+ * against a few thousand weight rows), the tiles split K and write fp32
+ * partial sums to the workspace, and a second launch on `stream` adds the
+ * splits in a fixed order and rounds once to bf16, so results stay bitwise
+ * deterministic (they differ from the unsplit kernels' only in fp32 rounding
+ * order). NULL runs without a split. A non-NULL workspace must be 16-byte
+ * aligned and hold at least agq_qmm_workspace(M, N, K, bits, group_size)
+ * bytes (else AGQ_EINVAL); its contents on return are unspecified, and two
+ * calls that overlap in time must not share one.
  */
+int64_t agq_qmm_workspace(int64_t M, int64_t N, int64_t K, int bits, int group_size);
 agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases, void *y,
-                   int64_t M, int64_t N, int64_t K, int bits, int group_size, void *stream);
+                   int64_t M, int64_t N, int64_t K, int bits, int group_size,
+                   void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Fused batch-1 projection: the decode layer's neighbouring stages that "MLX
@@ -208,10 +221,14 @@ agq_status agq_qmv_nvfp4(const void *x, const uint32_t *w, const void *scales, f
  * matrix cores as an exact bfloat16, with fp32 accumulation over K and the
  * tensor scale applied to each result once before its bfloat16 rounding. The
  * choice is made on the host from the shape. M*K*2 must stay below 2^31.
- * Same argument checks and errors as agq_qmv_nvfp4 otherwise.
+ * Same argument checks and errors as agq_qmv_nvfp4 otherwise. workspace and
+ * workspace_bytes as for agq_qmm, sized by agq_qmm_nvfp4_workspace; with a K
+ * split the tensor scale multiplies the sum of the splits.
  */
+int64_t agq_qmm_nvfp4_workspace(int64_t M, int64_t N, int64_t K);
 agq_status agq_qmm_nvfp4(const void *x, const uint32_t *w, const void *scales, float tensor_scale, void *y,
-                         int64_t M, int64_t N, int64_t K, void *stream);
+                         int64_t M, int64_t N, int64_t K, void *workspace, int64_t workspace_bytes,
+                         void *stream);
 
 /*
  * Expert-gathered matrix-matrix product (MoE prefill, the gather_qmm of the

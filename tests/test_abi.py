@@ -47,6 +47,17 @@ def test_moe_workspace_size():
     assert lib.agq_moe_decode_workspace(0, 2, 4096, 14336) == 0
 
 
+def test_gemm_workspace_sizes_of_calls_that_need_none():
+    """Calls that are not K-split GEMMs need no workspace (answered on the host)."""
+    assert lib.agq_qmm_workspace(0, 4096, 4096, 4, 64) == 0
+    assert lib.agq_qmm_workspace(256, 4096, 4096, 3, 64) == 0
+    assert lib.agq_qmm_workspace(256, 4096, 4096, 4, 32) == 0
+    assert lib.agq_qmm_workspace(8, 4096, 4096, 4, 64) == 0
+    assert lib.agq_qmm_workspace(100, 4096, 4096, 4, 64) == 0   # matrix-core matvec passes
+    assert lib.agq_qmm_nvfp4_workspace(4, 4096, 4096) == 0
+    assert lib.agq_qmm_nvfp4_workspace(64, 4096, 48) == 0
+
+
 def test_status_strings():
     assert lib.agq_status_str(0) == b"AGQ_OK"
     assert lib.agq_status_str(1) == b"AGQ_EINVAL"
@@ -67,8 +78,8 @@ def gather(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     return lib.agq_gather_qmv(x, A, A, A, lhs, rhs, A, P, R, E, N, K, bits, gs, None)
 
 
-def qmm(M=16, x=A, N=16, K=64, bits=4, gs=64, y=A):
-    return lib.agq_qmm(x, A, A, A, y, M, N, K, bits, gs, None)
+def qmm(M=16, x=A, N=16, K=64, bits=4, gs=64, y=A, ws=NUL, wsb=0):
+    return lib.agq_qmm(x, A, A, A, y, M, N, K, bits, gs, ws, wsb, None)
 
 
 def moe(T=4, k=2, E=4, H=512, F=1024, bits=4, gs=64, x=A, ws=A, wsb=1 << 30, ex=A):
@@ -83,8 +94,8 @@ def nvfp4(M=1, N=16, K=64, ts=1.0, x=A, w=A, s=A, y=A):
     return lib.agq_qmv_nvfp4(x, w, s, ts, y, M, N, K, None)
 
 
-def nvfp4mm(M=64, N=16, K=64, ts=1.0, x=A, w=A, s=A, y=A):
-    return lib.agq_qmm_nvfp4(x, w, s, ts, y, M, N, K, None)
+def nvfp4mm(M=64, N=16, K=64, ts=1.0, x=A, w=A, s=A, y=A, ws=NUL, wsb=0):
+    return lib.agq_qmm_nvfp4(x, w, s, ts, y, M, N, K, ws, wsb, None)
 
 
 def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
@@ -143,6 +154,7 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: lib.agq_quantize(A2, 0, A, A, A, 4, 64, 4, 64, None), EINVAL),
     (lambda: lib.agq_quantize(NUL, 0, A, A, A, 4, 64, 4, 64, None), EINVAL),
     (lambda: qmm(x=A2), EINVAL),
+    (lambda: qmm(ws=A2, wsb=1 << 20), EINVAL),
     (lambda: qmm(M=1 << 20, K=1024), ENOTSUP),
     (lambda: fused(act=3), EINVAL),
     (lambda: fused(act=-1), EINVAL),
@@ -172,6 +184,7 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: nvfp4(K=114688 + 32), ENOTSUP),
     (lambda: nvfp4(M=4, K=32768 + 32), ENOTSUP),
     (lambda: nvfp4mm(x=NUL), EINVAL),
+    (lambda: nvfp4mm(ws=A2, wsb=1 << 20), EINVAL),
     (lambda: nvfp4mm(s=NUL), EINVAL),
     (lambda: nvfp4mm(M=0), EINVAL),
     (lambda: nvfp4mm(M=3, K=48), ENOTSUP),

@@ -134,8 +134,10 @@ def seam_rows(N):
 @pytest.mark.parametrize("M,N,K,sample", [
     (5, 300, 64, False), (8, 1000, 512, False), (17, 129, 1024, False), (64, 4096, 4096, True),
     (100, 333, 2048, False), (300, 2000, 4096, True), (255, 128, 192, False),
-    # passes of 4 rows through the matvec kernel: few rows on a large matrix, K % 64 != 0
+    # few rows on a large matrix (a K split of the 64-row tiles), K % 64 != 0 (passes of 4 rows)
     (16, 4096, 4096, True), (6, 500, 96, False), (13, 200, 2080, False),
+    # K splits of the 256-row tiles
+    (256, 4096, 4096, True), (300, 1000, 14336, True),
     # grids of 256-row tiles that fill the device
     (1024, 8192, 512, True), (2048, 4096, 1024, True), (1100, 33000, 256, True),
 ])
@@ -199,3 +201,26 @@ def test_qmm_nvfp4_nan_scale_and_small_m_route():
     a = bf16_bits_host(agq.qmm_nvfp4(bf16_dev(x2), w2, s2, 0.5))
     b = np.concatenate([bf16_bits_host(agq.qmv_nvfp4(bf16_dev(x2[r:r + 4]), w2, s2, 0.5)) for r in (0, 4, 8)])
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (64, 1000, 8192), (256, 4096, 4096)])
+def test_qmm_nvfp4_k_split_matches_unsplit_and_is_deterministic(M, N, K):
+    """The K split (workspace from the binding) against the same call without one: within
+    the oracle bound of each other, and bitwise repeatable; the tensor scale multiplies the
+    sum of the splits."""
+    need = agq.lib.agq_qmm_nvfp4_workspace(M, N, K)
+    assert need > 0
+    d = si.nvfp4_weight(16, M + N, N, K)
+    x = si.draw_activations(16, 200 + M, M, K)
+    xd, w, s = bf16_dev(x), u32_dev(d["w"]), u8_dev(d["scales"])
+    progress(f"qmm_nvfp4 K split M={M} N={N} K={K}: {need // (4 * M * N)} splits")
+    a = agq.qmm_nvfp4(xd, w, s, d["tensor_scale"])
+    b = agq.qmm_nvfp4(xd, w, s, d["tensor_scale"])
+    c = agq.qmm_nvfp4(xd, w, s, d["tensor_scale"], workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    rows = seam_rows(N)
+    y_ref, A = oracle.qmv_nvfp4(x, d["w"], d["scales"], d["tensor_scale"], K, rows=rows)
+    ri = torch.as_tensor(rows, device=a.device)
+    check_close(a[:, ri], y_ref, A, "split")
+    check_close(c[:, ri], y_ref, A, "unsplit")

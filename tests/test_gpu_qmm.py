@@ -136,6 +136,81 @@ def test_qmm_split_weight_tiles_one_hot_bitwise(bits):
     assert np.array_equal(got, want.T)
 
 
+# --------------------------------------------------------------------------- K splits
+
+@pytest.mark.parametrize("bits,M,N,K", [
+    (4, 256, 4096, 4096),    # 32 split-weight tiles, 8 splits of 8 groups
+    (4, 256, 1000, 14336),   # 8 tiles, 32 splits of 7 groups
+    (8, 300, 2000, 2048),    # 8-bit, ragged rows, 8 splits of 4 groups
+    (4, 257, 3000, 2560),    # one row past a tile, ragged weight rows, 5 splits of 8 groups
+])
+def test_qmm_k_split_against_oracle_and_unsplit(bits, M, N, K):
+    """Where the split-weight tiles alone leave compute units idle, the call splits K
+    (workspace from the binding): parity with the oracle on seam rows, agreement with the
+    unsplit kernels within the same bound, and bitwise determinism of the split path."""
+    need = agq.lib.agq_qmm_workspace(M, N, K, bits, 64)
+    assert need > 0 and need % (4 * M * N) == 0, need
+    d = si.draw_quantized_weight(36, 100 * bits + M, N, K, bits)
+    x = si.draw_activations(36, 1000 + M, M, K)
+    w, s, b = dev_weight(d)
+    xd = bf16_dev(x)
+    progress(f"qmm K split bits={bits} M={M} N={N} K={K}: {need // (4 * M * N)} splits")
+    y = agq.qmm(xd, w, s, b, bits=bits)
+    y2 = agq.qmm(xd, w, s, b, bits=bits)
+    y0 = agq.qmm(xd, w, s, b, bits=bits, workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    rows = seam_rows(N)
+    y_ref, A = oracle.qmv(x, d["w"], d["scales"], d["biases"], K, bits, rows=rows)
+    ri = torch.as_tensor(rows, device=y.device)
+    worst = check_close(y[:, ri], y_ref, A, f"split M={M} N={N} K={K}")
+    check_close(y0[:, ri], y_ref, A, f"unsplit M={M} N={N} K={K}")
+    progress(f"qmm K split: ok, worst |err|/A = {worst:.3e}")
+
+
+def test_qmm_k_split_one_hot_bitwise():
+    """x = e_k through a K split: one split holds the exact weight, the others +0, so the
+    in-order sum and the one bf16 rounding give bf16(w_hat[n, k]) bit for bit."""
+    N, K = 4096, 1024
+    assert agq.lib.agq_qmm_workspace(K, N, K, 4, 64) > 0
+    d = si.draw_quantized_weight(37, 4, N, K, 4)
+    w, s, b = dev_weight(d)
+    ref, bad = oracle.dequantize(d["w"], d["scales"], d["biases"], K, 4)
+    assert bad == 0
+    want = si.bf16_bits(ref.astype(np.float32))
+    cols = np.arange(K)
+    x = np.zeros((K, K), np.uint16)
+    x[cols, cols] = 0x3F80
+    progress("qmm K split one-hot")
+    got = bf16_bits_host(agq.qmm(bf16_dev(x), w, s, b))
+    assert np.array_equal(got, want.T)
+
+
+def test_qmm_workspace_checks():
+    """A workspace below the queried size or off 16-byte alignment is AGQ_EINVAL before any
+    launch; a larger one, and none at all, run; calls that need none ignore it."""
+    M, N, K = 256, 4096, 4096
+    need = agq.lib.agq_qmm_workspace(M, N, K, 4, 64)
+    assert need > 0
+    assert agq.lib.agq_qmm_workspace(8, N, K, 4, 64) == 0          # matvec
+    assert agq.lib.agq_qmm_workspace(2048, N, K, 4, 64) == 0       # grid fills the device
+    assert agq.lib.agq_qmm_workspace(M, N, K, 4, 32) == 0          # not a GEMM format
+    d = si.draw_quantized_weight(38, 0, N, K, 4)
+    w, s, b = dev_weight(d)
+    xd = bf16_dev(si.draw_activations(38, 1, M, K))
+    ws = torch.empty(need + 64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(agq.AgqError) as e:
+        agq.qmm(xd, w, s, b, workspace=ws[:need - 16])
+    assert e.value.status == agq.AGQ_EINVAL
+    with pytest.raises(agq.AgqError) as e:
+        agq.qmm(xd, w, s, b, workspace=ws[8:8 + need])
+    assert e.value.status == agq.AGQ_EINVAL
+    a = agq.qmm(xd, w, s, b, workspace=ws)
+    c = agq.qmm(xd, w, s, b, workspace=ws[16:16 + need])
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
 @pytest.fixture(scope="module")
 def moe_w1():
     progress("generating the Mixtral-shaped W1 planes")
