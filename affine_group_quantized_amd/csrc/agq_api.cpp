@@ -638,19 +638,25 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
                   stream);
 }
 
-// The GEMM kernels of an agq_qmm call beyond the matvec forms (rows > 8, and
-// beyond kQmmPassRows or outside the matrix-core matvec's formats).
-bool qmm_uses_gemm(int64_t M, int64_t N, int64_t K, int bits) {
-    return M > 8 && !(M <= agq::kQmmPassRows && agq::mfma_eligible(M, K, bits, 0, M));
+// The GEMM of an agq_qmm call of M > 8 rows on `cus` compute units, or false
+// for passes of the matrix-core matvec kernel: up to kQmmPassRows rows of its
+// formats, unless more than kQmmHlSplitMinRows rows get split-weight tiles
+// that fill the device.
+bool qmm_gemm_plan(int64_t M, int64_t N, int64_t K, int bits, int cus, bool split_ok, agq::QmmKernel *k) {
+    *k = agq::qmm_kernel_for(bits, false, M, N, K, 1, cus, split_ok);
+    if (M <= agq::kQmmPassRows && agq::mfma_eligible(M, K, bits, 0, M))
+        return M > agq::kQmmHlSplitMinRows && k->split_weight;
+    return true;
 }
 
 int64_t agq_qmm_workspace(int64_t M, int64_t N, int64_t K, int bits, int group_size) {
-    if (M <= 0 || N <= 0 || K <= 0 || N > kMaxN || K > kMaxK || (bits != 4 && bits != 8) || group_size != 64)
+    if (M <= 8 || N <= 0 || K <= 0 || N > kMaxN || K > kMaxK || (bits != 4 && bits != 8) || group_size != 64)
         return 0;
-    if (K % 64 != 0 || M * K * 2 >= (int64_t(1) << 31) || !qmm_uses_gemm(M, N, K, bits)) return 0;
+    if (K % 64 != 0 || M * K * 2 >= (int64_t(1) << 31)) return 0;
     int cus = 0, dev = 0;
     if (current_device(&cus, &dev) != AGQ_OK) return 0;
-    return agq::qmm_split_bytes(agq::qmm_kernel_for(bits, false, M, N, K, 1, cus, true), M, N);
+    agq::QmmKernel k;
+    return qmm_gemm_plan(M, N, K, bits, cus, true, &k) ? agq::qmm_split_bytes(k, M, N) : 0;
 }
 
 agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases, void *y, int64_t M,
@@ -663,10 +669,23 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
     if (M * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (M*K*2 bytes)");
     // Up to 8 rows: the matvec kernels. Up to kQmmPassRows rows of 4-bit codes (K
     // a multiple of 512): the matrix-core matvec kernel, one grid row per pass of
-    // 16 rows. Beyond: the tiled GEMM.
+    // 16 rows, unless (beyond kQmmHlSplitMinRows rows) the split-weight tiles
+    // fill the device. Beyond: the tiled GEMM.
     if (M <= 8) return dense_product(x, w, scales, biases, y, M, N, K, bits, group_size, stream);
     if (group_size != 64) return fail(AGQ_ENOTSUP, "qmm beyond 8 rows takes group size 64");
-    if (M <= agq::kQmmPassRows && agq::mfma_eligible(M, K, bits, 0, M)) {
+    const bool pass_ok = M <= agq::kQmmPassRows && agq::mfma_eligible(M, K, bits, 0, M);
+    // (The GEMM: the weight range for the widest tile; the grid for the smallest.)
+    const bool k_ok = (int64_t)agq::kQmmHlTileN * (K * bits / 8) < (int64_t(1) << 31);
+    const bool grid_ok = (M + agq::kQmmTileMinM - 1) / agq::kQmmTileMinM <= 65535 &&
+                         (N + agq::kQmmTileN - 1) / agq::kQmmTileN <= INT32_MAX;
+    if (!pass_ok && !k_ok) return fail(AGQ_ENOTSUP, "K too large");
+    if (!pass_ok && !grid_ok)
+        return fail(AGQ_ENOTSUP, "grid too large (M=%lld, N=%lld)", (long long)M, (long long)N);
+    int cus = 0, dev = 0;
+    st = current_device(&cus, &dev);
+    if (st != AGQ_OK) return st;
+    agq::QmmKernel k;
+    if (!(k_ok && grid_ok && qmm_gemm_plan(M, N, K, bits, cus, workspace != nullptr, &k))) {
         agq::MfmaPlan mp;
         const void *sym = nullptr;
         const int passes = (int)((M + 15) / 16);
@@ -676,14 +695,6 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
         return launch(sym, dim3((unsigned)mp.groups, (unsigned)passes), dim3(mp.threads), (size_t)mp.lds_bytes, &a,
                       stream);
     }
-    // (The weight range for the widest tile; the grid for the smallest.)
-    if ((int64_t)agq::kQmmHlTileN * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
-    if ((M + agq::kQmmTileMinM - 1) / agq::kQmmTileMinM > 65535 || (N + agq::kQmmTileN - 1) / agq::kQmmTileN > INT32_MAX)
-        return fail(AGQ_ENOTSUP, "grid too large (M=%lld, N=%lld)", (long long)M, (long long)N);
-    int cus = 0, dev = 0;
-    st = current_device(&cus, &dev);
-    if (st != AGQ_OK) return st;
-    const agq::QmmKernel k = agq::qmm_kernel_for(bits, false, M, N, K, 1, cus, workspace != nullptr);
     st = check_workspace(workspace, workspace_bytes, agq::qmm_split_bytes(k, M, N));
     if (st != AGQ_OK) return st;
     agq::QmmArgs a{};

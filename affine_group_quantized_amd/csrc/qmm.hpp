@@ -29,6 +29,13 @@ constexpr int kQmmLargeBlocksPerCu = 2;
 // M = 2048: 554 -> 341). Tiles of 128 rows lost at M = 256 (28672x4096: 166 ->
 // 174) and on the Mixtral prefill gather.
 constexpr int kQmmHlMinRows = 256;
+// Dense products of more rows than this take the split-weight tiles (256-row
+// tiles, partly empty) wherever their grid, alone or split along K, fills the
+// device: against the matvec passes and the corrected tiles (4-bit, us):
+// 4096x14336 at M = 64 / 128 / 255: 63.6 / 121 / 154 -> 52.9 / 59.9 / 70.9;
+// 28672x4096 at M = 96 / 128: 130 / 155 -> 99.3 / 105; 4096x4096 at M = 64 /
+// 96: 21.0 / 37.4 against 24.8 / 28.8 (so not from 64 rows).
+constexpr int kQmmHlSplitMinRows = 64;
 constexpr int kQmmPassRows = 128;  // 4-bit products of up to this many rows run on the matvec kernel in passes of 16
 
 // Passed by value as the single kernel argument.
@@ -61,6 +68,7 @@ struct QmmKernel {
     int threads = 256;   // block size
     int splits = 1;      // K splits (grid.z); above 1 the partials go to a workspace and qmm_reduce_kernel sums them
     int gps = 0;         // 64-column groups per split
+    bool split_weight = false;  // the split-weight tiles (qmm_hl_kernel, gather_qmm_hl_kernel)
 };
 
 // K splits of the split-weight tiles: where a grid of them leaves compute

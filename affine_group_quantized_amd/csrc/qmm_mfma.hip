@@ -811,6 +811,7 @@ static QmmKernel hl_pick(bool gather) {
     k.bn = H::BN;
     k.lds = 2 * H::LDS_BUF;
     k.threads = 512;
+    k.split_weight = true;
     return k;
 }
 
@@ -832,10 +833,11 @@ QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t
                   "the host checks assume these tile sizes");
     static_assert(Hl<AffineFmt<4>, 8>::BN == kQmmHlTileN && Hl<AffineFmt<4>, 8>::BM >= kQmmTileMinM,
                   "the host checks assume these tile sizes");
-    // Split-weight tiles where the rows fill them and their grid, or (dense,
-    // with a workspace) their grid split along K, gives every compute unit a block.
+    // Split-weight tiles where the rows fill them (dense: more than
+    // kQmmHlSplitMinRows) and their grid, or (dense, with a workspace) their
+    // grid split along K, gives every compute unit a block.
     constexpr int HBM = Hl<AffineFmt<4>, 8>::BM;
-    if (rows >= kQmmHlMinRows) {
+    if (rows >= kQmmHlMinRows || (!gather && rows > kQmmHlSplitMinRows)) {
         const int64_t tiles = planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN) * ((rows + HBM - 1) / HBM);
         QmmKernel k = bits == 4 ? hl_pick<4, 8>(gather) : hl_pick<8, 8>(gather);
         if (4 * tiles >= 3 * (int64_t)cus) return k;

@@ -53,7 +53,7 @@ def test_gemm_workspace_sizes_of_calls_that_need_none():
     assert lib.agq_qmm_workspace(256, 4096, 4096, 3, 64) == 0
     assert lib.agq_qmm_workspace(256, 4096, 4096, 4, 32) == 0
     assert lib.agq_qmm_workspace(8, 4096, 4096, 4, 64) == 0
-    assert lib.agq_qmm_workspace(100, 4096, 4096, 4, 64) == 0   # matrix-core matvec passes
+    assert lib.agq_qmm_workspace(64, 4096, 4096, 4, 64) == 0    # matrix-core matvec passes
     assert lib.agq_qmm_nvfp4_workspace(4, 4096, 4096) == 0
     assert lib.agq_qmm_nvfp4_workspace(64, 4096, 48) == 0
 

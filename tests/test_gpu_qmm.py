@@ -47,6 +47,9 @@ def dev_weight(d):
     # (256 x 128 and 128 x 128), with ragged activation rows and weight rows
     (4, 2048, 4096, 1024, True), (4, 1100, 33000, 256, True), (8, 2048, 4096, 512, True),
     (8, 700, 9000, 320, True), (4, 260, 16400, 2048, True),
+    # 65-255 rows on the split-weight tiles (most rows of the 256-row tile empty): split
+    # along K (65, 200 rows), and a grid that fills the device unsplit (100 rows)
+    (4, 65, 4096, 4096, True), (8, 200, 4096, 2048, True), (4, 100, 28672, 1024, True),
 ])
 def test_qmm_shapes(bits, M, N, K, sample):
     """Shapes on both tile sizes: the 128x64 tile where it gives at least two blocks per
@@ -68,9 +71,10 @@ def test_qmm_shapes(bits, M, N, K, sample):
 
 @pytest.mark.parametrize("M", [9, 40, 128])
 def test_qmm_passes_agree_with_the_tiled_gemm(M):
-    """4-bit products of 9-128 rows run on the matrix-core matvec kernel, one grid row per
-    16-row pass; the same rows through agq_gather_qmm (identity routing onto one plane, the
-    tiled GEMM) meet the same tolerance against the oracle."""
+    """4-bit products of 9-64 rows (and up to 128 where split-weight tiles would leave the
+    device idle, as here: 5 weight tiles) run on the matrix-core matvec kernel, one grid row
+    per 16-row pass; the same rows through agq_gather_qmm (identity routing onto one plane,
+    the tiled GEMM) meet the same tolerance against the oracle."""
     N, K = 520, 2048
     d = si.draw_quantized_weight(35, M, N, K, 4)
     x = si.draw_activations(35, 100 + M, M, K)
@@ -139,6 +143,7 @@ def test_qmm_split_weight_tiles_one_hot_bitwise(bits):
 # --------------------------------------------------------------------------- K splits
 
 @pytest.mark.parametrize("bits,M,N,K", [
+    (4, 100, 4096, 4096),    # 100 rows: 8 splits of one 256-row tile row; unsplit, the matvec passes
     (4, 256, 4096, 4096),    # 32 split-weight tiles, 8 splits of 8 groups
     (4, 256, 1000, 14336),   # 8 tiles, 32 splits of 7 groups
     (8, 300, 2000, 2048),    # 8-bit, ragged rows, 8 splits of 4 groups
