@@ -640,12 +640,12 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
 
 // The GEMM of an agq_qmm call of M > 8 rows on `cus` compute units, or false
 // for passes of the matrix-core matvec kernel: up to kQmmPassRows rows of its
-// formats, unless more than kQmmHlSplitMinRows rows get split-weight tiles
+// formats, unless more than kQmmHlSmallMinRows rows get split-weight tiles
 // that fill the device.
 bool qmm_gemm_plan(int64_t M, int64_t N, int64_t K, int bits, int cus, bool split_ok, agq::QmmKernel *k) {
     *k = agq::qmm_kernel_for(bits, false, M, N, K, 1, cus, split_ok);
     if (M <= agq::kQmmPassRows && agq::mfma_eligible(M, K, bits, 0, M))
-        return M > agq::kQmmHlSplitMinRows && k->split_weight;
+        return M > agq::kQmmHlSmallMinRows && k->split_weight;
     return true;
 }
 

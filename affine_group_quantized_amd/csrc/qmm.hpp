@@ -36,6 +36,17 @@ constexpr int kQmmHlMinRows = 256;
 // 28672x4096 at M = 96 / 128: 130 / 155 -> 99.3 / 105; 4096x4096 at M = 64 /
 // 96: 21.0 / 37.4 against 24.8 / 28.8 (so not from 64 rows).
 constexpr int kQmmHlSplitMinRows = 64;
+// Dense products of more rows than this, up to kQmmHlSplitMinRows, take
+// 64-row split-weight tiles where their grid (alone or split along K) fills
+// the device, instead of 3-4 matvec passes; up to kQmmHlSmallNarrowRows rows
+// (three passes) only where K splits at least kQmmHlSmallMinSplits ways, i.e.
+// few weight rows (4-bit, us, passes -> tiles: 4096x14336 at M = 48 / 64:
+// 64.8 / 63.6 -> 41.0 / 42.0; 6144x4096: 30.5 / 30.4 -> 22.3 / 23.6;
+// 14336x4096 (2 splits) at M = 48 / 64: 38.6 / 49.0 -> 42.3 / 43.7; 28672x4096
+// (no split) 73.2 / 81.3 -> 75.2 / 75.2; at M = 24 / 32 the passes win).
+constexpr int kQmmHlSmallMinRows = 32;
+constexpr int kQmmHlSmallNarrowRows = 48;
+constexpr int kQmmHlSmallMinSplits = 4;
 constexpr int kQmmPassRows = 128;  // 4-bit products of up to this many rows run on the matvec kernel in passes of 16
 
 // Passed by value as the single kernel argument.

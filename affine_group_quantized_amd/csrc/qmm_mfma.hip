@@ -834,9 +834,21 @@ QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t
     static_assert(Hl<AffineFmt<4>, 8>::BN == kQmmHlTileN && Hl<AffineFmt<4>, 8>::BM >= kQmmTileMinM,
                   "the host checks assume these tile sizes");
     // Split-weight tiles where the rows fill them (dense: more than
-    // kQmmHlSplitMinRows) and their grid, or (dense, with a workspace) their
-    // grid split along K, gives every compute unit a block.
+    // kQmmHlSplitMinRows; 64-row tiles from kQmmHlSmallMinRows) and their
+    // grid, or (dense, with a workspace) their grid split along K, gives every
+    // compute unit a block.
     constexpr int HBM = Hl<AffineFmt<4>, 8>::BM;
+    if (!gather && rows > kQmmHlSmallMinRows && rows <= kQmmHlSplitMinRows) {
+        static_assert(Hl<AffineFmt<4>, 2>::BM == kQmmHlSplitMinRows, "one row of 64-row tiles");
+        const int64_t tiles = planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN);
+        QmmKernel k = bits == 4 ? hl_pick<4, 2>(false) : hl_pick<8, 2>(false);
+        const bool narrow = rows <= kQmmHlSmallNarrowRows;
+        if (4 * tiles >= 3 * (int64_t)cus) {
+            if (!narrow) return k;
+        } else if (split_ok && split_k(k, tiles, K / 64, cus) && (!narrow || k.splits >= kQmmHlSmallMinSplits)) {
+            return k;
+        }
+    }
     if (rows >= kQmmHlMinRows || (!gather && rows > kQmmHlSplitMinRows)) {
         const int64_t tiles = planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN) * ((rows + HBM - 1) / HBM);
         QmmKernel k = bits == 4 ? hl_pick<4, 8>(gather) : hl_pick<8, 8>(gather);

@@ -50,6 +50,9 @@ def dev_weight(d):
     # 65-255 rows on the split-weight tiles (most rows of the 256-row tile empty): split
     # along K (65, 200 rows), and a grid that fills the device unsplit (100 rows)
     (4, 65, 4096, 4096, True), (8, 200, 4096, 2048, True), (4, 100, 28672, 1024, True),
+    # 33-64 rows on 64-row split-weight tiles: split along K, and a full grid unsplit (49+ rows)
+    (4, 48, 4096, 14336, True), (8, 40, 4096, 2048, True), (4, 64, 28672, 512, True), (4, 33, 3000, 4096, True),
+    (4, 40, 28672, 512, True),
 ])
 def test_qmm_shapes(bits, M, N, K, sample):
     """Shapes on both tile sizes: the 128x64 tile where it gives at least two blocks per
@@ -189,6 +192,27 @@ def test_qmm_k_split_one_hot_bitwise():
     progress("qmm K split one-hot")
     got = bf16_bits_host(agq.qmm(bf16_dev(x), w, s, b))
     assert np.array_equal(got, want.T)
+
+
+def test_qmm_small_split_weight_tile_one_hot_bitwise():
+    """64 one-hot rows (x = e_c for 64 columns across chunk, group and K-split seams) on the
+    64-row split-weight tile split along K: y[m, n] = bf16(w_hat[n, c_m]) bit for bit."""
+    N, K, M = 8192, 1024, 64
+    assert agq.lib.agq_qmm_workspace(M, N, K, 4, 64) > 0
+    d = si.draw_quantized_weight(39, 4, N, K, 4)
+    w, s, b = dev_weight(d)
+    ref, bad = oracle.dequantize(d["w"], d["scales"], d["biases"], K, 4)
+    assert bad == 0
+    want = si.bf16_bits(ref.astype(np.float32))
+    cols = np.array(list(range(0, 34)) + [63, 64, 65, 127, 128, 255, 256, 257, 511, 512, 513, 639, 640, 767, 768,
+                                          895, 896, 1000, 1020, 1021, 1022, 1023, 300, 400, 700, 800, 900, 950, 960,
+                                          970][:M])
+    assert len(set(cols.tolist())) == M
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), cols] = 0x3F80
+    progress("qmm 64-row split-weight tile one-hot")
+    got = bf16_bits_host(agq.qmm(bf16_dev(x), w, s, b))
+    assert np.array_equal(got, want[:, cols].T)
 
 
 def test_qmm_workspace_checks():
