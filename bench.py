@@ -249,6 +249,13 @@ def cpu_baseline(shapes, xs, bits=4, calls=3):
 # ----------------------------------------------------------------------------- profiles
 
 
+def kernel_label(name):
+    """A kernel's demangled name without its argument list, "void " and anonymous-namespace
+    qualifiers (template arguments can hold parentheses of their own)."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.rsplit("(", 1)[0] if name.endswith(")") else name
+
+
 KERNEL_SOURCES = ["affine_group_quantized_amd/csrc/qmv_kernels.hip", "affine_group_quantized_amd/csrc/qmv_core.hpp",
                   "affine_group_quantized_amd/csrc/qmv_device.hpp", "affine_group_quantized_amd/csrc/qmv_kernels.hpp",
                   "affine_group_quantized_amd/csrc/plan.hpp", "affine_group_quantized_amd/csrc/agq_api.cpp"]
@@ -293,7 +300,7 @@ def _counter(d, cname, pred):
     out = {}
     for r in _read_csv(d, "counter_collection.csv"):
         if r["Counter_Name"] == cname and pred(r["Kernel_Name"]):
-            out.setdefault((r["Kernel_Name"].split("(")[0].replace("void ", ""), int(r["Grid_Size"])), []).append(
+            out.setdefault((kernel_label(r["Kernel_Name"]), int(r["Grid_Size"])), []).append(
                 float(r["Counter_Value"]))
     return out
 
@@ -350,13 +357,13 @@ def write_profiles(workload, dirs):
              "| kernel | calls | average us | min us | max us | share of time |", "|---|---|---|---|---|---|"]
     for r in stats:
         if "agq::" in r["Name"]:
-            lines.append(f"| `{r['Name'].split('(')[0].replace('void ', '')}` | {r['Calls']} | "
+            lines.append(f"| `{kernel_label(r['Name'])}` | {r['Calls']} | "
                          f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                          f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
     by_grid = {}
     for r in trace:
         if "agq::" in r["Kernel_Name"]:
-            by_grid.setdefault((r["Kernel_Name"].split("(")[0].replace("void ", ""), int(r["Grid_Size_X"])),
+            by_grid.setdefault((kernel_label(r["Kernel_Name"]), int(r["Grid_Size_X"])),
                                []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines += ["", "Per launch shape (grid size in threads; grids are sized by occupancy, not by N, so one kernel "
               "and grid can serve several shapes of a workload, and then its row pools their launches):", "",
