@@ -801,12 +801,15 @@ static QmmKernel qmm_pick(bool gather) {
     return k;
 }
 
-template <int BITS, int TMW>
-static QmmKernel hl_pick(bool gather) {
+// (GATHER a template argument: only the instantiations a call can reach are compiled.)
+template <int BITS, int TMW, bool GATHER>
+static QmmKernel hl_pick() {
     QmmKernel k;
     using H = Hl<AffineFmt<BITS>, TMW>;
-    k.sym = gather ? reinterpret_cast<const void *>(&gather_qmm_hl_kernel<BITS, TMW>)
-                   : reinterpret_cast<const void *>(&qmm_hl_kernel<AffineFmt<BITS>, TMW>);
+    if constexpr (GATHER)
+        k.sym = reinterpret_cast<const void *>(&gather_qmm_hl_kernel<BITS, TMW>);
+    else
+        k.sym = reinterpret_cast<const void *>(&qmm_hl_kernel<AffineFmt<BITS>, TMW>);
     k.bm = H::BM;
     k.bn = H::BN;
     k.lds = 2 * H::LDS_BUF;
@@ -841,7 +844,7 @@ QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t
     if (!gather && rows > kQmmHlSmallMinRows && rows <= kQmmHlSplitMinRows) {
         static_assert(Hl<AffineFmt<4>, 2>::BM == kQmmHlSplitMinRows, "one row of 64-row tiles");
         const int64_t tiles = planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN);
-        QmmKernel k = bits == 4 ? hl_pick<4, 2>(false) : hl_pick<8, 2>(false);
+        QmmKernel k = bits == 4 ? hl_pick<4, 2, false>() : hl_pick<8, 2, false>();
         const bool narrow = rows <= kQmmHlSmallNarrowRows;
         if (4 * tiles >= 3 * (int64_t)cus) {
             if (!narrow) return k;
@@ -851,7 +854,8 @@ QmmKernel qmm_kernel_for(int bits, bool gather, int64_t rows, int64_t N, int64_t
     }
     if (rows >= kQmmHlMinRows || (!gather && rows > kQmmHlSplitMinRows)) {
         const int64_t tiles = planes * ((N + kQmmHlTileN - 1) / kQmmHlTileN) * ((rows + HBM - 1) / HBM);
-        QmmKernel k = bits == 4 ? hl_pick<4, 8>(gather) : hl_pick<8, 8>(gather);
+        QmmKernel k = gather ? (bits == 4 ? hl_pick<4, 8, true>() : hl_pick<8, 8, true>())
+                             : (bits == 4 ? hl_pick<4, 8, false>() : hl_pick<8, 8, false>());
         if (4 * tiles >= 3 * (int64_t)cus) return k;
         if (!gather && split_ok && split_k(k, tiles, K / 64, cus)) return k;
     }
