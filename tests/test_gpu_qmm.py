@@ -215,6 +215,57 @@ def test_qmm_small_split_weight_tile_one_hot_bitwise():
     assert np.array_equal(got, want[:, cols].T)
 
 
+def test_qmm_k_splits_in_a_graph():
+    """The split GEMM and its reduction (affine and NVFP4) and an unsplit GEMM captured in one
+    HIP graph: every replay, with the workspaces overwritten with NaN bytes, the outputs
+    cleared and eager work in between, reproduces the eager outputs bit for bit (no part of
+    the split path depends on earlier workspace contents)."""
+    M, N, K = 256, 4096, 4096
+    d = si.draw_quantized_weight(40, 0, N, K, 4)
+    w, s, b = dev_weight(d)
+    nv = si.nvfp4_weight(40, 1, N, K)
+    wn = u32_dev(nv["w"])
+    sn = torch.from_numpy(np.ascontiguousarray(nv["scales"])).to("cuda")
+    xd = bf16_dev(si.draw_activations(40, 2, M, K))
+    need_a = agq.lib.agq_qmm_workspace(M, N, K, 4, 64)
+    need_n = agq.lib.agq_qmm_nvfp4_workspace(64, N, K)
+    assert need_a > 0 and need_n > 0
+    ws_a = torch.empty(need_a, dtype=torch.uint8, device="cuda")
+    ws_n = torch.empty(need_n, dtype=torch.uint8, device="cuda")
+    ya = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    yn = torch.empty((64, N), dtype=torch.bfloat16, device="cuda")
+    yu = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    outs = (ya, yn, yu)
+    x64 = xd[:64].contiguous()
+
+    def run():
+        agq.qmm(xd, w, s, b, out=ya, workspace=ws_a)
+        agq.qmm_nvfp4(x64, wn, sn, nv["tensor_scale"], out=yn, workspace=ws_n)
+        agq.qmm(xd, w, s, b, out=yu, workspace=False)
+
+    progress("graph capture of split and unsplit GEMMs")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.synchronize()
+    eager = [bf16_bits_host(t).copy() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.zero_()
+        ws_a.fill_(0xFF)
+        ws_n.fill_(0xFF)
+        agq.qmm(xd[:100].contiguous(), w, s, b)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, eager):
+            assert np.array_equal(bf16_bits_host(got), want), f"replay {rep}"
+
+
 def test_qmm_workspace_checks():
     """A workspace below the queried size or off 16-byte alignment is AGQ_EINVAL before any
     launch; a larger one, and none at all, run; calls that need none ignore it."""
