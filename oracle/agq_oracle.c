@@ -25,8 +25,13 @@
  * the bit order. Readings adopted:
  *  - a weight is w = scale * q + bias, one (scale, bias) per 64 consecutive
  *    input columns of a row;
- *  - element k of a row sits in word k / (32/bits) at bit offset
- *    bits * (k % (32/bits)), i.e. low-first;
+ *  - element k of a row occupies bits [bits*k, bits*k + bits) of the row's
+ *    little-endian bit stream, word i holding stream bits 32i .. 32i + 31
+ *    (low-first). For 4 and 8 bits, the widths the pages name, element k is
+ *    in word k / (32/bits) at bit offset bits * (k % (32/bits)); the other
+ *    widths of the affine family (2, 3, 5, 6) take the same stream, so a 3-,
+ *    5- or 6-bit code may straddle two words and a group of 64 columns is
+ *    exactly 2 * bits words;
  *  - W is [N out, K in] and y[m, n] = sum_k x[m, k] * w[n, k].
  *
  * The decode MoE layer (agqo_moe_swiglu) composes these steps the way the
@@ -78,22 +83,26 @@ static double bf16_value(uint16_t h)
     return (double)f;
 }
 
+static int bits_ok(int bits) { return bits >= 2 && bits <= 8 && bits != 7; }
+
 static int check_format(int64_t K, int bits, int group_size)
 {
-    if (bits != 4 && bits != 8) return AGQO_EARG;
+    if (!bits_ok(bits)) return AGQO_EARG;
     if (group_size <= 0 || K <= 0 || K % group_size != 0) return AGQO_EARG;
-    if (K % (32 / bits) != 0) return AGQO_EARG;
+    if ((K * bits) % 32 != 0) return AGQO_EARG;  /* whole words per row */
     return AGQO_OK;
 }
 
-/* Step 1, unpack: the integer code of element k of one packed row. */
+/* Step 1, unpack: the integer code of element k of one packed row, bits
+ * [bits*k, bits*k + bits) of its stream (the word after, where they run past
+ * a word's end). */
 static uint32_t code_at(const uint32_t *packed_row, int64_t k, int bits)
 {
-    int64_t per_word = 32 / bits;
-    uint32_t word = packed_row[k / per_word];
-    uint32_t shift = (uint32_t)(bits * (k % per_word));
+    int64_t first = (int64_t)bits * k;
+    uint64_t pair = packed_row[first / 32];
+    if (first % 32 + bits > 32) pair |= (uint64_t)packed_row[first / 32 + 1] << 32;
     uint32_t mask = (1u << bits) - 1u;
-    return (word >> shift) & mask;
+    return (uint32_t)(pair >> (first % 32)) & mask;
 }
 
 /* Step 2, dequantize: w = scale * q + bias, in double (exact for bf16 scale/bias). */
@@ -125,7 +134,7 @@ static void row_dot(const uint16_t *x_row, const uint32_t *packed_row,
 /* Unpacked integer codes, q[n*K + k]. */
 int agqo_unpack(const uint32_t *w, int64_t N, int64_t K, int bits, uint8_t *q)
 {
-    if (!w || !q || N <= 0 || (bits != 4 && bits != 8) || K <= 0 || K % (32 / bits))
+    if (!w || !q || N <= 0 || !bits_ok(bits) || K <= 0 || (K * bits) % 32)
         return AGQO_EARG;
     int64_t words = K * bits / 32;
     for (int64_t n = 0; n < N; ++n)
@@ -295,14 +304,14 @@ static uint16_t bf16_rne(float f)
  *   scale = bf16((max - min) / (2^bits - 1)),  bias = bf16(min),
  *   q = clamp(rint((w - bias) / scale), 0, 2^bits - 1)   (q = 0 where scale is 0)
  * with rint rounding half to even, using the rounded scale and bias. Codes are
- * packed low-first into uint32 words. w is [N, K] float; wq [N, K*bits/32];
+ * packed into the row's low-first bit stream. w is [N, K] float; wq [N, K*bits/32];
  * scales and biases [N, K/group_size] bf16. */
 int agqo_quantize(const float *w, int64_t N, int64_t K, int bits, int group_size,
                   uint32_t *wq, uint16_t *scales, uint16_t *biases)
 {
     if (!w || !wq || !scales || !biases || N <= 0) return AGQO_EARG;
     if (check_format(K, bits, group_size)) return AGQO_EARG;
-    const int64_t groups = K / group_size, per_word = 32 / bits, words = K / per_word;
+    const int64_t groups = K / group_size, words = K * bits / 32;
     const float levels = (float)((1 << bits) - 1);
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t i = 0; i < words; ++i) wq[n * words + i] = 0;
@@ -326,8 +335,9 @@ int agqo_quantize(const float *w, int64_t N, int64_t K, int bits, int group_size
                     const float r = rintf(num / s);
                     q = r <= 0.0f ? 0u : r >= levels ? (uint32_t)levels : (uint32_t)r;
                 }
-                const int64_t k = g * group_size + j;
-                wq[n * words + k / per_word] |= q << (uint32_t)(bits * (k % per_word));
+                const int64_t first = (int64_t)bits * (g * group_size + j);  /* stream bit */
+                wq[n * words + first / 32] |= q << (uint32_t)(first % 32);
+                if (first % 32 + bits > 32) wq[n * words + first / 32 + 1] |= q >> (uint32_t)(32 - first % 32);
             }
         }
     }

@@ -23,8 +23,10 @@ Recipe (every draw is reproducible from the integers below):
   rounded to bfloat16 (RNE). Then ``q = clip(rint((w - bias) / scale), 0,
   2**bits - 1)``, computed in float32 with the rounded scale and bias. A
   group with ``max == min`` gets ``scale = 0`` and ``q = 0``.
-* Packing: element ``k`` of a row occupies bits ``[bits*(k % per), +bits)``
-  of word ``k // per``, with ``per = 32 // bits`` (low-first).
+* Packing: element ``k`` of a row occupies bits ``[bits*k, bits*k + bits)`` of
+  the row's little-endian bit stream of uint32 words (low-first). For 2, 4 and
+  8 bits that is bits ``[bits*(k % per), +bits)`` of word ``k // per``, with
+  ``per = 32 // bits``; a 3-, 5- or 6-bit code may run into the next word.
 
 Shapes follow the decode workloads: Llama-3-8B-class projections at 4 bits,
 a 0.5B-class model at 8 bits, and a Mixtral-class 8-expert MoE layer.
@@ -75,15 +77,23 @@ def bf16_to_f32(h: np.ndarray) -> np.ndarray:
 
 
 def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
-    """Integer codes ``[..., K]`` (uint8) -> packed uint32 ``[..., K*bits/32]``, low-first."""
-    per = 32 // bits
-    q = np.asarray(q, dtype=np.uint32)
-    assert q.shape[-1] % per == 0
-    qs = q.reshape(q.shape[:-1] + (q.shape[-1] // per, per))
-    out = np.zeros(qs.shape[:-1], dtype=np.uint32)
-    for j in range(per):
-        out |= qs[..., j] << np.uint32(bits * j)
-    return out
+    """Integer codes ``[..., K]`` (uint8) -> packed uint32 ``[..., K*bits/32]``, low-first: code k
+    fills bits bits*k .. bits*k + bits - 1 of the row's little-endian bit stream (a 3-, 5- or
+    6-bit code can run into the next word). Every 32 codes fill exactly ``bits`` words."""
+    q = np.asarray(q, dtype=np.uint64)
+    K = q.shape[-1]
+    assert (K * bits) % 32 == 0 and 2 <= bits <= 8
+    if K % 32:  # a partial chunk of 32 codes: pad with zero codes, keep the row's own words
+        q = np.concatenate([q, np.zeros(q.shape[:-1] + (32 - K % 32,), np.uint64)], axis=-1)
+    qs = q.reshape(q.shape[:-1] + (q.shape[-1] // 32, 32))
+    out = np.zeros(qs.shape[:-1] + (bits,), dtype=np.uint64)
+    for j in range(32):
+        word, shift = divmod(bits * j, 32)
+        v = qs[..., j] << np.uint64(shift)                 # up to 39 bits
+        out[..., word] |= v & np.uint64(0xFFFFFFFF)
+        if shift + bits > 32:
+            out[..., word + 1] |= v >> np.uint64(32)
+    return out.astype(np.uint32).reshape(q.shape[:-1] + (q.shape[-1] * bits // 32,))[..., :K * bits // 32]
 
 
 def quantize_rows(w: np.ndarray, bits: int, group_size: int = GROUP_SIZE):
@@ -123,9 +133,8 @@ def draw_quantized_weight(cfg: int, t: int, n: int, k: int, bits: int,
     ``biases`` (bf16 bits ``[n, k/64]``). With ``keep_codes`` it also returns
     ``codes`` (uint8 ``[n, k]``).
     """
-    per = 32 // bits
     g = k // GROUP_SIZE
-    wq = np.empty((n, k // per), dtype=np.uint32)
+    wq = np.empty((n, k * bits // 32), dtype=np.uint32)
     s = np.empty((n, g), dtype=np.uint16)
     b = np.empty((n, g), dtype=np.uint16)
     codes = np.empty((n, k), dtype=np.uint8) if keep_codes else None

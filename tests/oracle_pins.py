@@ -77,10 +77,20 @@ def pin_unpack_known_words(lib):
              [255, 0, 0, 0] + [127, 128, 0, 127] + [1, 0, 0, 0] + [0, 0, 0, 1])
     got8 = oracle.unpack(words8, 32, 8, lib=lib)
     assert got8.tolist() == [want8], got8
+    # The other widths: codes c_k = (3k + 1) mod 2^bits, k < 32, placed by hand at stream bits
+    # bits*k .. bits*k + bits - 1 (word 0 of the 3-bit row: bits 0, 5-8, 10, 12, 14, 18, 19,
+    # 22-24, 29-31 set, the last two from code 10 = 7, which runs into word 1).
+    words = {2: [0xB1B1B1B1, 0xB1B1B1B1],
+             3: [0xE1CC55E1, 0x55E1CC55, 0xCC55E1CC],
+             5: [0xE0D51C81, 0x517F99B4, 0x5E9172D0, 0x8930C1DD, 0xF6F1593D],
+             6: [0x0D287101, 0xF7195934, 0xBABA2589, 0x3DEB7D31, 0xF3091830, 0x79B61548]}
+    for bits, ws in words.items():
+        got = oracle.unpack(np.array([ws], np.uint32), 32, bits, lib=lib)
+        assert got.tolist() == [[(3 * k + 1) % 2 ** bits for k in range(32)]], (bits, got)
 
 
 def pin_unpack_roundtrip(lib):
-    for bits in (4, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         q = np.random.default_rng(bits).integers(0, 2 ** bits, size=(5, 192), dtype=np.uint8)
         got = oracle.unpack(pack_codes(q, bits), 192, bits, lib=lib)
         assert np.array_equal(got, q)
@@ -100,7 +110,7 @@ def pin_golden_worked(lib):
 
 
 def pin_dequant_quantizer_roundtrip(lib):
-    for bits in (4, 8):
+    for bits in (3, 4, 5, 6, 8):
         d = draw_quantized_weight(99, bits, 64, 256, bits, keep_codes=True)
         what, not_f32 = oracle.dequantize(d["w"], d["scales"], d["biases"], 256, bits, lib=lib)
         assert not_f32 == 0
@@ -153,7 +163,7 @@ def pin_dequant_not_f32_count(lib):
 
 
 def pin_dot_exact_bruteforce(lib):
-    for bits in (4, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         for seed, (M, N, K) in enumerate([(2, 3, 64), (1, 2, 128), (3, 4, 192)]):
             x, q, s, b = _random_problem(100 + seed + bits, M, N, K, bits)
             y, a = oracle.qmv(x, pack_codes(q, bits), s, b, K, bits, lib=lib)
@@ -167,7 +177,7 @@ def pin_dot_exact_bruteforce(lib):
 
 def pin_other_group_sizes_bruteforce(lib):
     """Groups of 32 and 128 columns: exact rationals over codes from before packing."""
-    for bits in (4, 8):
+    for bits in (3, 4, 5, 8):
         for gs, K in ((32, 96), (128, 256)):
             g = np.random.default_rng([70, bits, gs])
             M, N = 2, 3
@@ -187,7 +197,7 @@ def pin_other_group_sizes_bruteforce(lib):
 
 
 def pin_numpy_blas(lib):
-    for bits in (4, 8):
+    for bits in (3, 4, 6, 8):
         x, q, s, b = _random_problem(7 + bits, 3, 96, 1024, bits)
         y, a = oracle.qmv(x, pack_codes(q, bits), s, b, 1024, bits, lib=lib)
         sf = np.repeat(bf16_to_f32(s).astype(np.float64), 64, axis=1)
@@ -374,7 +384,7 @@ def pin_quantize_known_groups(lib):
     """Hand-worked groups: a ramp 1 + 0.5*c over codes c spanning 0 .. 2^bits - 1 gives
     scale 0.5, bias 1 and codes c; a constant group gives scale 0, bias the constant, codes 0; ties round
     to even codes; values beyond the ramp clamp."""
-    for bits in (4, 8):
+    for bits in (3, 4, 5, 6, 8):
         lv = 2 ** bits - 1
         K = 64
         codes = np.concatenate([[0, lv], np.arange(1, K - 1) % (lv + 1)])  # spans 0 .. 2^bits - 1
@@ -399,7 +409,7 @@ def pin_quantize_properties(lib):
     half a scale (plus the float32 rounding of (w - b)/s) of their dequantized weight; the
     dequantized weights re-quantize to the same codes, scales and biases wherever the codes
     span the full range (then max and min are exactly representable on the grid)."""
-    for bits in (4, 8):
+    for bits in (2, 3, 4, 5, 6, 8):
         for gs in (32, 64, 128):
             g = np.random.default_rng([71, bits, gs])
             N, K = 6, 256
@@ -425,6 +435,18 @@ def pin_quantize_properties(lib):
             q2 = oracle.unpack(wq2, K, bits, lib=lib).reshape(N, K // gs, gs)
             assert np.array_equal(sc2[full], sc[full]) and np.array_equal(bi2[full], bi[full])
             assert np.array_equal(q2[full], qg[full].astype(np.uint8))
+
+
+def pin_quantize_packs_like_the_producer(lib):
+    """The oracle quantizer's packed words, scales and biases equal the producer's (quantize_rows,
+    then pack_codes: the same recipe and bit stream written independently), at every width."""
+    for bits in (2, 3, 4, 5, 6, 8):
+        g = np.random.default_rng([72, bits])
+        w = (0.02 * g.standard_normal((5, 320))).astype(np.float32)
+        wq, sc, bi = oracle.quantize(w, bits, lib=lib)
+        q, s2, b2 = quantize_rows(w, bits)
+        assert np.array_equal(sc, s2) and np.array_equal(bi, b2), bits
+        assert np.array_equal(wq, pack_codes(q, bits)), bits
 
 
 def pin_quantize_codes_are_nearest(lib):

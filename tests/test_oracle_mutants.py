@@ -13,10 +13,13 @@ import oracle
 from oracle_pins import PINS
 
 MUTANTS = {
-    "high_first_unpack": ("uint32_t shift = (uint32_t)(bits * (k % per_word));",
-                          "uint32_t shift = (uint32_t)(bits * (per_word - 1 - k % per_word));"),
-    "wrong_word_index": ("uint32_t word = packed_row[k / per_word];",
-                         "uint32_t word = packed_row[k % per_word];"),
+    "high_first_unpack": ("return (uint32_t)(pair >> (first % 32)) & mask;",
+                          "return (uint32_t)(pair >> ((32 - bits - first % 32) & 63)) & mask;"),
+    "wrong_word_index": ("uint64_t pair = packed_row[first / 32];", "uint64_t pair = packed_row[k / 32];"),
+    "straddle_dropped": ("if (first % 32 + bits > 32) pair |= (uint64_t)packed_row[first / 32 + 1] << 32;", ""),
+    "quant_straddle_dropped": ("if (first % 32 + bits > 32) wq[n * words + first / 32 + 1] |= q >> (uint32_t)(32 - first % 32);", ""),
+    "quant_stream_offset": ("const int64_t first = (int64_t)bits * (g * group_size + j);",
+                            "const int64_t first = (int64_t)bits * (g * group_size) + 4 * j;"),
     "short_mask": ("uint32_t mask = (1u << bits) - 1u;", "uint32_t mask = (1u << (bits - 1)) - 1u;"),
     "dropped_bias": ("return bf16_value(scale_row[g]) * q + bf16_value(bias_row[g]);",
                      "return bf16_value(scale_row[g]) * q;"),
