@@ -120,7 +120,7 @@ def _weights(w, scales, biases, K, bits, group_size, device, planes):
     _need(w, "w", _U32, device)
     _need(scales, "scales", _BF16, device)
     _need(biases, "biases", _BF16, device)
-    if bits not in (4, 8) or group_size <= 0 or K % group_size or (K * bits) % 32:
+    if bits not in (2, 3, 4, 5, 6, 8) or group_size <= 0 or K % group_size or (K * bits) % 32:
         raise ValueError(f"bad format: K={K} bits={bits} group_size={group_size}")
     lead = w.shape[:-1]
     if w.dim() != planes + 1 or w.shape[-1] != K * bits // 32:

@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libagq.so")
 CALIB_LIB = os.path.join(PKG, "libagq_calib.so")
 
-SOURCES = ["qmv_kernels.hip", "qmv_fused.hip", "qmv_nvfp4.hip", "qmv_mfma.hip", "qmm_mfma.hip", "moe_mfma.hip", "quant.hip", "agq_api.cpp"]
+SOURCES = ["qmv_kernels.hip", "qmv_fused.hip", "qmv_nvfp4.hip", "qmv_stream.hip", "qmv_mfma.hip", "qmm_mfma.hip", "moe_mfma.hip",
+           "quant.hip", "agq_api.cpp"]
 CALIB_SOURCES = ["calib_read.hip"]
 
 # Packed-FP32 instructions are disabled for all device code.

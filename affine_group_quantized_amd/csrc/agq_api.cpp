@@ -157,10 +157,19 @@ agq_status check_format(int64_t N, int64_t K, int bits, int group_size) {
     if (N > kMaxN || K > kMaxK)
         return fail(AGQ_EINVAL, "N or K too large (N=%lld, K=%lld)", (long long)N, (long long)K);
     if (group_size <= 0) return fail(AGQ_EINVAL, "group_size must be positive (got %d)", group_size);
-    if (bits != 4 && bits != 8) return fail(AGQ_ENOTSUP, "bits=%d not supported (4 or 8)", bits);
+    if (bits != 2 && bits != 3 && bits != 4 && bits != 5 && bits != 6 && bits != 8)
+        return fail(AGQ_ENOTSUP, "bits=%d not supported (2, 3, 4, 5, 6 or 8)", bits);
     if (group_size != 32 && group_size != 64 && group_size != 128)
         return fail(AGQ_ENOTSUP, "group_size=%d not supported (32, 64 or 128)", group_size);
     if (K % group_size != 0) return fail(AGQ_EINVAL, "K=%lld is not a multiple of group_size", (long long)K);
+    return AGQ_OK;
+}
+
+// The bit-stream widths (2, 3, 5, 6 bits): the matvec, quantize and dequantize
+// forms only.
+bool stream_bits(int bits) { return bits != 4 && bits != 8; }
+agq_status need_4_or_8(int bits, const char *what) {
+    if (stream_bits(bits)) return fail(AGQ_ENOTSUP, "bits=%d: %s takes 4- or 8-bit codes", bits, what);
     return AGQ_OK;
 }
 
@@ -323,6 +332,17 @@ agq_status dense_product(const void *x, const uint32_t *w, const void *s, const 
     if (st != AGQ_OK) return st;
     if (M <= 0) return fail(AGQ_EINVAL, "M must be positive (got %lld)", (long long)M);
     if (M > 8) return fail(AGQ_ENOTSUP, "M=%lld > 8 is a quantized GEMM, not a matvec", (long long)M);
+    if (stream_bits(bits)) {
+        if (group_size != 64) return fail(AGQ_ENOTSUP, "bits=%d takes group size 64", bits);
+        if (M * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (M*K*2 bytes)");
+        if ((N + agq::kStreamRowsPerBlock - 1) / agq::kStreamRowsPerBlock > INT32_MAX)
+            return fail(AGQ_ENOTSUP, "N=%lld too large", (long long)N);
+        agq::StreamArgs a{static_cast<const uint16_t *>(x), w, static_cast<const uint16_t *>(s),
+                          static_cast<const uint16_t *>(b), static_cast<uint16_t *>(y), N, (int32_t)K, (int32_t)M};
+        return launch(agq::stream_kernel(bits, (int)M),
+                      dim3((unsigned)((N + agq::kStreamRowsPerBlock - 1) / agq::kStreamRowsPerBlock)), dim3(256), 0, &a,
+                      stream);
+    }
     if (group_size == 64 && agq::mfma_eligible(M, K, bits, 0, M)) {
         agq::MfmaPlan mp;
         const void *sym = nullptr;
@@ -382,6 +402,8 @@ agq_status agq_qmv_fused(const void *x, const void *norm_weight, float eps, cons
                          const void *biases, const void *residual, int act, void *y, int64_t N, int64_t K, int bits,
                          int group_size, void *stream) {
     agq_status st = check_operands(x, w, scales, biases, y, N, K, bits, group_size, true);
+    if (st != AGQ_OK) return st;
+    st = need_4_or_8(bits, "the fused projection");
     if (st != AGQ_OK) return st;
     if (act < AGQ_ACT_NONE || act > AGQ_ACT_GEGLU) return fail(AGQ_EINVAL, "act=%d is not 0, 1 or 2", act);
     if (act != AGQ_ACT_NONE && (N % 2 != 0 || residual))
@@ -599,6 +621,8 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
                           int64_t E, int64_t N, int64_t K, int bits, int group_size, void *stream) {
     agq_status st = check_operands(x, w, scales, biases, y, N, K, bits, group_size, true);
     if (st != AGQ_OK) return st;
+    st = need_4_or_8(bits, "the expert gather");
+    if (st != AGQ_OK) return st;
     if (P <= 0 || R <= 0 || E <= 0)
         return fail(AGQ_EINVAL, "P, R and E must be positive (P=%lld, R=%lld, E=%lld)", (long long)P,
                     (long long)R, (long long)E);
@@ -672,6 +696,15 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
     // 16 rows, unless (beyond kQmmHlSplitMinRows rows) the split-weight tiles
     // fill the device. Beyond: the tiled GEMM.
     if (M <= 8) return dense_product(x, w, scales, biases, y, M, N, K, bits, group_size, stream);
+    if (stream_bits(bits)) {  // passes of up to 8 rows through the bit-stream matvec
+        for (int64_t r0 = 0; r0 < M; r0 += 8) {
+            st = dense_product(static_cast<const uint16_t *>(x) + r0 * K, w, scales, biases,
+                               static_cast<uint16_t *>(y) + r0 * N, M - r0 < 8 ? M - r0 : 8, N, K, bits, group_size,
+                               stream);
+            if (st != AGQ_OK) return st;
+        }
+        return AGQ_OK;
+    }
     if (group_size != 64) return fail(AGQ_ENOTSUP, "qmm beyond 8 rows takes group size 64");
     const bool pass_ok = M <= agq::kQmmPassRows && agq::mfma_eligible(M, K, bits, 0, M);
     // (The GEMM: the weight range for the widest tile; the grid for the smallest.)
@@ -717,6 +750,8 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y, int64_t P, int64_t R,
                           int64_t E, int64_t N, int64_t K, int bits, int group_size, void *stream) {
     agq_status st = check_operands(x, w, scales, biases, y, N, K, bits, group_size, true);
+    if (st != AGQ_OK) return st;
+    st = need_4_or_8(bits, "the expert gather");
     if (st != AGQ_OK) return st;
     if (P <= 0 || R <= 0 || E <= 0)
         return fail(AGQ_EINVAL, "P, R and E must be positive (P=%lld, R=%lld, E=%lld)", (long long)P,
@@ -935,14 +970,16 @@ agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *bia
     int cus = 0, dev = 0;
     st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
-    int64_t words_per_row = K * bits / 32;
-    int64_t words = rows * words_per_row;
-    int64_t blocks = (words + 255) / 256;
+    // One thread per packed word (4 and 8 bits) or per 32 codes (the bit-stream widths).
+    const bool streamed = stream_bits(bits);
+    int64_t per_row = streamed ? K / 32 : K * bits / 32;
+    int64_t units = rows * per_row;
+    int64_t blocks = (units + 255) / 256;
     int64_t cap = (int64_t)cus * 32;
     if (blocks > cap) blocks = cap;
-    const void *sym = agq::dequant_kernel_sym(bits);
+    const void *sym = streamed ? agq::stream_dequant_kernel(bits) : agq::dequant_kernel_sym(bits);
     int64_t gs = group_size;
-    void *args[] = {&w, &scales, &biases, &out, &words, &words_per_row, &K, &gs};
+    void *args[] = {&w, &scales, &biases, &out, &units, &per_row, &K, &gs};
     hipError_t e = hipLaunchKernel(sym, dim3((unsigned)blocks), dim3(256), args, 0, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(AGQ_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return AGQ_OK;
@@ -951,6 +988,7 @@ agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *bia
 agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group_size, int num_cus,
                             int waves_per_cu, int64_t experts, agq_plan *out) {
     if (!out) return fail(AGQ_EINVAL, "null plan pointer");
+    if (bits == 2 || bits == 3 || bits == 5 || bits == 6) return need_4_or_8(bits, "a launch plan");
     agq_status st = check_format(N, K, bits, group_size);
     if (st != AGQ_OK) return st;
     if (experts < 0) return fail(AGQ_EINVAL, "experts must be >= 0");
@@ -976,6 +1014,7 @@ agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group
 agq_status agq_plan_launch(int64_t M, int64_t N, int64_t K, int bits, int group_size, int64_t experts,
                            agq_plan *out) {
     if (!out) return fail(AGQ_EINVAL, "null plan pointer");
+    if (bits == 2 || bits == 3 || bits == 5 || bits == 6) return need_4_or_8(bits, "a launch plan");
     agq_status st = check_format(N, K, bits, group_size);
     if (st != AGQ_OK) return st;
     if (experts < 0) return fail(AGQ_EINVAL, "experts must be >= 0");

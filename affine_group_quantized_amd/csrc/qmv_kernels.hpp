@@ -87,7 +87,7 @@ struct MfmaArgs {
 // LDS copy of x (0: none)), or NULL.
 const void *product_kernel(int bits, int mw, int cpt, int R, int NB, int x_lds, bool gather);
 const void *dequant_kernel_sym(int bits);
-// Group quantizer kernel for 4- or 8-bit codes from fp32 or bf16 weights.
+// Group quantizer kernel for 2-, 3-, 4-, 5-, 6- or 8-bit codes from fp32 or bf16 weights (NULL otherwise).
 const void *quantize_kernel_for(int bits, bool bf16_in);
 // Matrix-core kernel with bands of 16*tiles rows (tiles 1 or 2). Dense
 // products choose the activation load form by their rows per pass: one
@@ -101,5 +101,22 @@ const void *mfma_kernel(int tiles, bool gather, int rows);
 const void *fused_kernel(int bits, int cpt, int R, int NB, int xs, int epi, bool norm);
 // NVFP4 product kernel for (activation rows 1-4, chunks per lane, rows per iteration, ring stages), or NULL.
 const void *nvfp4_kernel_for(int mw, int cpt, int R, int NB);
+
+// Bit-stream widths (2, 3, 5 and 6 bits, group size 64; qmv_stream.hip).
+struct StreamArgs {
+    const uint16_t *x;  // activation rows, bf16 [M, K]
+    const uint32_t *w;  // codes [N, K*bits/32], the row's low-first bit stream
+    const uint16_t *s;  // bf16 scales [N, K/64]
+    const uint16_t *b;  // bf16 biases [N, K/64]
+    uint16_t *y;        // bf16 outputs [M, N]
+    int64_t N;
+    int32_t K;          // a multiple of 64
+    int32_t M;          // activation rows, 1 .. 8
+};
+constexpr int kStreamRowsPerBlock = 16;  // 4 waves of 4 weight rows
+// The matvec kernel for `bits` and M activation rows (NULL outside 2, 3, 5, 6 and 1..8).
+const void *stream_kernel(int bits, int M);
+// Dequantize kernel of the bit-stream widths: one thread per 32 codes (`bits` words).
+const void *stream_dequant_kernel(int bits);
 
 }  // namespace agq

@@ -1,6 +1,7 @@
 // Affine group quantizer on the GPU: weights (fp32 or bf16) [N, K] to U32-packed
-// 4- or 8-bit codes with BF16 scale and bias per group of 32, 64 or 128 columns,
-// the format the products read. It moves the quantization step onto the device
+// 2-, 3-, 4-, 5-, 6- or 8-bit codes with BF16 scale and bias per group of 32,
+// 64 or 128 columns, the format the products read: each row's codes form one
+// low-first bit stream (code k at stream bits bits*k .. bits*k + bits - 1). It moves the quantization step onto the device
 // ("MLX CUDA Cleanup Plan", Phase 5: repeated host-side quantization is one of
 // the per-op overheads to remove; the epic's Phase 5 quantized KV cache, #635,
 // quantizes on the device too).
@@ -13,7 +14,9 @@
 // are bit-identical to any other correct implementation of the recipe.
 //
 // One thread per group: a first pass over the group's values finds max and
-// min, a second (from cache) forms the codes and stores each packed word.
+// min, a second (from cache) forms the codes and stores each packed word as
+// the stream fills it (a group is a whole number of words: 32 * bits bits per
+// 32 columns).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,7 +44,6 @@ template <int BITS, typename IN>
 __global__ __launch_bounds__(256) void quantize_kernel(const IN *__restrict__ w, int64_t groups, int64_t K,
                                                        int gs, uint32_t *__restrict__ wq,
                                                        uint16_t *__restrict__ sc, uint16_t *__restrict__ bi) {
-    constexpr int PER = 32 / BITS;
     constexpr float kLevels = (float)((1 << BITS) - 1);
     const int64_t gpr = K / gs;  // groups per row
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < groups;
@@ -59,28 +61,42 @@ __global__ __launch_bounds__(256) void quantize_kernel(const IN *__restrict__ w,
         sc[i] = s16;
         bi[i] = b16;
         const float s = bf16_lo(s16), b = bf16_lo(b16);
-        uint32_t *dst = wq + row * (K / PER) + g * (gs / PER);
-        for (int j0 = 0; j0 < gs; j0 += PER) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int t = 0; t < PER; ++t) {
-                uint32_t q = 0;
-                if (s != 0.f) {
-                    const float r = rintf(__fdiv_rn(load_w(src + j0 + t) - b, s));
-                    q = r <= 0.f ? 0u : r >= kLevels ? (uint32_t)kLevels : (uint32_t)r;
-                }
-                word |= q << (BITS * t);
+        uint32_t *dst = wq + row * (K / 32 * BITS) + g * (gs / 32 * BITS);
+        uint64_t bitbuf = 0;  // stream bits not yet stored, low-first
+        int nbits = 0;
+        for (int j = 0; j < gs; ++j) {
+            uint32_t q = 0;
+            if (s != 0.f) {
+                const float r = rintf(__fdiv_rn(load_w(src + j) - b, s));
+                q = r <= 0.f ? 0u : r >= kLevels ? (uint32_t)kLevels : (uint32_t)r;
             }
-            dst[j0 / PER] = word;
+            bitbuf |= (uint64_t)q << nbits;
+            nbits += BITS;
+            if (nbits >= 32) {
+                *dst++ = (uint32_t)bitbuf;
+                bitbuf >>= 32;
+                nbits -= 32;
+            }
         }
     }
 }
 
+template <int BITS>
+static const void *quantize_pick(bool bf16_in) {
+    return bf16_in ? reinterpret_cast<const void *>(&quantize_kernel<BITS, uint16_t>)
+                   : reinterpret_cast<const void *>(&quantize_kernel<BITS, float>);
+}
+
 const void *quantize_kernel_for(int bits, bool bf16_in) {
-    if (bits == 4) return bf16_in ? reinterpret_cast<const void *>(&quantize_kernel<4, uint16_t>)
-                                  : reinterpret_cast<const void *>(&quantize_kernel<4, float>);
-    return bf16_in ? reinterpret_cast<const void *>(&quantize_kernel<8, uint16_t>)
-                   : reinterpret_cast<const void *>(&quantize_kernel<8, float>);
+    switch (bits) {
+        case 2: return quantize_pick<2>(bf16_in);
+        case 3: return quantize_pick<3>(bf16_in);
+        case 4: return quantize_pick<4>(bf16_in);
+        case 5: return quantize_pick<5>(bf16_in);
+        case 6: return quantize_pick<6>(bf16_in);
+        case 8: return quantize_pick<8>(bf16_in);
+    }
+    return nullptr;
 }
 
 }  // namespace agq

@@ -90,7 +90,7 @@ def parse():
                     help="summarize rocprofv3 CSV output of this benchmark into profiles/ and exit: "
                          "TRACE_DIR [FETCH_DIR WRITE_DIR]")
     ap.add_argument("--workload", choices=["llama", "c0", "wide", "c3", "gather", "qmm", "moe", "layer", "nvfp4",
-                                                  "calib"],
+                                                  "bits", "calib"],
                     default="llama")
     ap.add_argument("--calls", type=int, default=200, help="calls per timed loop of one shape")
     return ap.parse_args()
@@ -309,11 +309,13 @@ WORKLOAD_FLAGS = {"llama": "--steps 20 --repeats 3 --no-cpu-baseline --no-calib 
                   "c0": "--workload c0 --calls 100", "wide": "--workload wide --calls 40",
                   "c3": "--workload c3 --calls 100", "gather": "--workload gather --calls 40",
                   "qmm": "--workload qmm --calls 20", "moe": "--workload moe",
-                  "layer": "--workload layer --calls 40 --no-calib", "nvfp4": "--workload nvfp4 --calls 40"}
+                  "layer": "--workload layer --calls 40 --no-calib", "nvfp4": "--workload nvfp4 --calls 40",
+                  "bits": "--workload bits --calls 40"}
 PMC_FLAGS = {"llama": "--steps 5 --repeats 1 --warmup 2 --warm-seconds 0 --no-cpu-baseline --no-calib --no-graph",
              "c0": "--workload c0 --calls 8", "wide": "--workload wide --calls 8", "c3": "--workload c3 --calls 8",
              "gather": "--workload gather --calls 8", "qmm": "--workload qmm --calls 4", "moe": "--workload moe",
-             "layer": "--workload layer --calls 8 --no-calib", "nvfp4": "--workload nvfp4 --calls 8 --no-calib"}
+             "layer": "--workload layer --calls 8 --no-calib", "nvfp4": "--workload nvfp4 --calls 8 --no-calib",
+             "bits": "--workload bits --calls 8 --no-calib"}
 TITLES = {"llama": "Llama-3-8B-shaped decode GEMV set, batch 1, 4-bit gs64",
           "c0": "single product 4096x4096, batch 1, 4-bit gs64",
           "wide": "small-batch products 14336x4096 and 4096x14336 at M = 2, 4, 6, 8 (4-bit gs64)",
@@ -328,7 +330,9 @@ TITLES = {"llama": "Llama-3-8B-shaped decode GEMV set, batch 1, 4-bit gs64",
                    "o + residual, norm + gate/up + SwiGLU, down + residual, final norm + lm_head), against the "
                    "bare products and the unfused sequence (4-bit gs64)",
           "nvfp4": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, and GEMMs at M = 16, 256, 2048, NVFP4 weights "
-                   "(E2M1 codes, E4M3 scale per 16 columns), against the affine 4-bit gs64 products on the same shapes"}
+                   "(E2M1 codes, E4M3 scale per 16 columns), against the affine 4-bit gs64 products on the same shapes",
+          "bits": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, at 2, 3, 5 and 6 bits (the bit-stream widths, "
+                  "gs64) and 4 bits for reference"}
 
 
 def write_profiles(workload, dirs):
@@ -340,7 +344,8 @@ def write_profiles(workload, dirs):
     other workloads reuse the factors recorded with the llama counters."""
     name = {"llama": "qmv_llama_decode_set", "c0": "qmv_c0_4096x4096", "wide": "qmv_wide", "c3": "qmv_c3_8bit",
             "gather": "qmv_gather", "qmm": "qmm_prefill", "moe": "moe_decode_layer",
-            "layer": "qmv_fused_decode_layer", "nvfp4": "qmv_nvfp4_llama_decode_set"}[workload]
+            "layer": "qmv_fused_decode_layer", "nvfp4": "qmv_nvfp4_llama_decode_set",
+            "bits": "qmv_bitstream_widths_llama_decode_set"}[workload]
     stats = _read_csv(dirs[0], "kernel_stats.csv")
     trace = _read_csv(dirs[0], "kernel_trace.csv")
     cmd = f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o bench -- python3 bench.py " \
@@ -502,6 +507,9 @@ def other_workload(args):
         return
     if args.workload == "nvfp4":
         nvfp4_workload(args, torch, si, agq, bf16, u32, stream, calib, emit)
+        return
+    if args.workload == "bits":
+        bits_workload(args, torch, si, agq, bf16, u32, stream, calib, emit)
         return
 
     if args.workload in ("c0", "c3"):
@@ -745,6 +753,43 @@ def layer_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
           **{f"{k}_us": round(v, 3) for k, v in tot.items()},
           "fused_over_bare": round(tot["fused"] / tot["bare"], 4),
           "unfused_over_fused": round(tot["unfused"] / tot["fused"], 3)})
+
+
+def bits_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
+    """Workload 1's five products with 2-, 3-, 5- and 6-bit codes (group size 64, the
+    bit-stream widths) and, for reference, 4-bit codes, at M = 1 and 4 (agq_qmv_wide): us/call,
+    GB/s of algorithmic bytes and % of the read ceiling per shape, and the set's sum per width.
+    The weights are draw_quantized_weight rows (stream cfg 14) drawn for at most 4096 rows and
+    repeated down to N: the kernels do the same work for every code value (nothing branches
+    on a value), and drawing all 128256 lm_head rows per width would cost the host minutes."""
+    import numpy as np
+    st = stream.cuda_stream
+    dev = stream.device
+    tot = {}
+    for t, name, N, K, _, xname in si.WORKLOADS[1]["w"]:
+        xall = bf16(si.draw_activations(14, 100 + t, 4, K))
+        for bits in (2, 3, 4, 5, 6):
+            base = si.draw_quantized_weight(14, 10 * t + bits, min(N, 4096), K, bits)
+            reps = -(-N // base["w"].shape[0])
+            m = {k: np.tile(base[k], (reps, 1))[:N] for k in ("w", "scales", "biases")}
+            cp = rotation(u32, bf16, m, weight_bytes(N, K, bits))
+            ptrs = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr()) for c in cp]
+            rot = len(cp)
+            for M in (1, 4):
+                x = xall[:M].contiguous()
+                y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+                agq.qmv_wide(x, *cp[0], bits=bits, out=y)  # validates the operands once
+                xp, yp = x.data_ptr(), y.data_ptr()
+                us, us_min = time_shape(torch, lambda i: agq.lib.agq_qmv_wide(xp, *ptrs[i % rot], yp, M, N, K, bits,
+                                                                              64, st), args.calls, 5, stream)
+                nb = algo_bytes(N, K, bits, M)
+                emit(shape_line(f"{bits}-bit: {name} {N}x{K} M={M}", us, us_min, nb, None,
+                                calib.ceiling(nb) if calib else None))
+                tot[(bits, M)] = tot.get((bits, M), 0.0) + us
+            del cp, m, base
+            torch.cuda.empty_cache()
+    emit({"set": "Llama-shaped decode products at each width (group size 64), us per set",
+          **{f"bits{b}_m{M}_us": round(v, 3) for (b, M), v in sorted(tot.items())}})
 
 
 def nvfp4_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):

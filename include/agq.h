@@ -11,9 +11,14 @@
  *
  *     y[m, n] = sum_k x[m, k] * (scale[n, k/64] * q[n, k] + bias[n, k/64])
  *
- * Code q[n, k] is stored low-first: it is bits [bits*(k % (32/bits)), +bits)
- * of word k / (32/bits) of packed row n. W is [N out, K in]. Arithmetic is in
- * fp32, and outputs are BF16, rounded to nearest even.
+ * Code q[n, k] is stored low-first: it is bits [bits*k, bits*k + bits) of
+ * packed row n's little-endian bit stream, word i holding stream bits
+ * 32i .. 32i + 31. For 4 and 8 bits (and 2) that is bits
+ * [bits*(k % (32/bits)), +bits) of word k / (32/bits). The other widths of the
+ * affine family, 2, 3, 5 and 6 bits, use the same stream (a 3-, 5- or 6-bit
+ * code may run into the next word; a 64-column group is 2*bits words); the
+ * pages name 4 and 8. W is [N out, K in]. Arithmetic is in fp32, and outputs
+ * are BF16, rounded to nearest even.
  *
  * The product entry points map to the kernels those pages discuss:
  *  - agq_qmv is the batch-1 matvec;
@@ -87,9 +92,12 @@ const char *agq_last_error(void);
  *   scales [N, K/group_size] BF16
  *   biases [N, K/group_size] BF16
  *   y      [N] BF16 (written)
- * bits must be 4 or 8 and group_size 32, 64 or 128 (else AGQ_ENOTSUP); K must
- * be a positive multiple of group_size, and N positive (else AGQ_EINVAL). K
- * above 114688 (4-bit) or 57344 (8-bit) is AGQ_ENOTSUP.
+ * bits must be 2, 3, 4, 5, 6 or 8 and group_size 32, 64 or 128 (else
+ * AGQ_ENOTSUP; the bit-stream widths 2, 3, 5 and 6 take group size 64 only);
+ * K must be a positive multiple of group_size, and N positive (else
+ * AGQ_EINVAL). K above 114688 (4-bit) or 57344 (8-bit) is AGQ_ENOTSUP; the
+ * bit-stream widths walk K in chunks of 4096 columns and take any K with
+ * M*K*2 < 2^31 bytes of x.
  */
 agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                    void *y, int64_t N, int64_t K, int bits, int group_size, void *stream);
@@ -102,7 +110,8 @@ agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const v
  * codes, group size 64, M >= 4 and K a multiple of 512 the product runs on
  * the matrix cores and K is limited only by M*K*2 < 2^31 bytes of x. Otherwise the K limit
  * shrinks with M: K <= 16384 * c for 4-bit and 8192 * c for 8-bit, with
- * c = min(7, floor(8/M)) (larger K is AGQ_ENOTSUP).
+ * c = min(7, floor(8/M)) (larger K is AGQ_ENOTSUP). The bit-stream widths as
+ * for agq_qmv.
  */
 agq_status agq_qmv_wide(const void *x, const uint32_t *w, const void *scales, const void *biases,
                         void *y, int64_t M, int64_t N, int64_t K, int bits, int group_size,
@@ -124,7 +133,8 @@ agq_status agq_qmv_wide(const void *x, const uint32_t *w, const void *scales, co
  * rhs >= E gets an all-NaN output row, and no memory outside the arrays is
  * read. With 4-bit codes, group size 64 and K a multiple of 512 the gather
  * runs on the matrix cores, 16 pairs per pass, and K is limited only by R*K*2 < 2^31
- * bytes of x; otherwise K limits are those of agq_qmv_wide at M = 8.
+ * bytes of x; otherwise K limits are those of agq_qmv_wide at M = 8. Takes
+ * 4- or 8-bit codes (the bit-stream widths are AGQ_ENOTSUP), as agq_gather_qmm.
  */
 agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y,
@@ -142,8 +152,9 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
  * hold the codes exactly (128 + q for 4-bit, q for 8-bit) and applies each
  * group's scale and bias in fp32, so its error bound is that of the matvec
  * forms. M*K*2 must stay below 2^31 (else AGQ_ENOTSUP). Beyond 8 rows it
- * takes group size 64 (else AGQ_ENOTSUP). Argument checks and errors as for
- * agq_qmv.
+ * takes group size 64 (else AGQ_ENOTSUP). The bit-stream widths (2, 3, 5, 6
+ * bits) run as passes of up to 8 rows of agq_qmv_wide's kernel. Argument
+ * checks and errors as for agq_qmv.
  *
  * workspace (optional, owned by the caller): device scratch for a K split.
  * Where the output tiles alone leave compute units idle (a few hundred rows
@@ -311,11 +322,11 @@ agq_status agq_moe_decode_noalloc(const void *x, const uint32_t *w_gate, const v
  *     scale = bf16((max - min) / (2^bits - 1)),  bias = bf16(min),
  *     q = clamp(rint((w - bias) / scale), 0, 2^bits - 1)   (q = 0 where scale is 0)
  * with correctly rounded division, rint to nearest even and the rounded scale
- * and bias; codes packed low-first.
+ * and bias; codes packed into each row's low-first bit stream.
  *   w       [rows, K] float (w_dtype AGQ_DTYPE_F32) or BF16 (AGQ_DTYPE_BF16)
  *   codes   [rows, K*bits/32] U32 (written); scales, biases [rows, K/group_size] BF16 (written)
- * bits 4 or 8; group_size 32, 64 or 128. Inputs must be finite. Errors as for
- * agq_dequantize.
+ * bits 2, 3, 4, 5, 6 or 8; group_size 32, 64 or 128. Inputs must be finite.
+ * Errors as for agq_dequantize.
  */
 #define AGQ_DTYPE_F32 0
 #define AGQ_DTYPE_BF16 1
@@ -332,7 +343,8 @@ agq_status agq_quantize(const void *w, int w_dtype, uint32_t *codes, void *scale
  * rounded once to binary32. The exact value is representable, and the result
  * therefore exact, unless the bias exceeds the scale by more than about 2^15
  * (BF16 scale and bias hold 8 significant bits each).
- * `rows` covers stacked planes: pass E*N for a [E, N, .] tensor.
+ * `rows` covers stacked planes: pass E*N for a [E, N, .] tensor. Every width
+ * (2, 3, 4, 5, 6, 8 bits) and group size (32, 64, 128).
  *   w [rows, K*bits/32] U32; scales/biases [rows, K/group_size] BF16; out [rows, K] fp32.
  */
 agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *biases, float *out,
@@ -348,7 +360,7 @@ agq_status agq_dequantize(const uint32_t *w, const void *scales, const void *bia
  * sizes for 8 rows per pass).
  */
 typedef struct agq_plan {
-    int32_t bits;            /* 4 or 8 */
+    int32_t bits;            /* 4 or 8 (the bit-stream widths have no launch plan: AGQ_ENOTSUP) */
     int32_t chunks_per_row;  /* 16-byte chunks of packed codes per weight row */
     int32_t cpt;             /* chunks per lane within a wave's K segment */
     int32_t mw;              /* activation rows handled per pass */

@@ -110,8 +110,14 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: qmv(K=0), EINVAL),
     (lambda: qmv(N=-3), EINVAL),
     (lambda: qmv(K=96), EINVAL),
-    (lambda: qmv(bits=3), ENOTSUP),
-    (lambda: qmv(bits=2), ENOTSUP),
+    (lambda: qmv(bits=7), ENOTSUP),
+    (lambda: qmv(bits=9), ENOTSUP),
+    (lambda: qmv(bits=1), ENOTSUP),
+    (lambda: qmv(bits=3, gs=32, K=128), ENOTSUP),   # the bit-stream widths take group size 64
+    (lambda: wide(M=9, bits=5), ENOTSUP),
+    (lambda: gather(bits=3), ENOTSUP),              # the gathers take 4- or 8-bit codes
+    (lambda: gqmm(bits=6), ENOTSUP),
+    (lambda: qmm(bits=5, gs=128, K=128), ENOTSUP),
     (lambda: qmv(gs=16), ENOTSUP),
     (lambda: qmv(gs=256, K=256), ENOTSUP),
     (lambda: qmv(gs=32, K=48), EINVAL),
@@ -142,14 +148,14 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: qmm(x=NUL), EINVAL),
     (lambda: qmm(y=NUL), EINVAL),
     (lambda: qmm(K=96), EINVAL),
-    (lambda: qmm(bits=2), ENOTSUP),
+    (lambda: qmm(bits=7), ENOTSUP),
     (lambda: qmm(gs=16, K=128), ENOTSUP),
     (lambda: qmm(gs=128, K=128), ENOTSUP),
     (lambda: qmm(gs=32, K=128), ENOTSUP),
     (lambda: gqmm(gs=32, K=128), ENOTSUP),
     (lambda: moe(gs=32), ENOTSUP),
     (lambda: lib.agq_quantize(A, 2, A, A, A, 4, 64, 4, 64, None), EINVAL),
-    (lambda: lib.agq_quantize(A, 0, A, A, A, 4, 64, 3, 64, None), ENOTSUP),
+    (lambda: lib.agq_quantize(A, 0, A, A, A, 4, 64, 7, 64, None), ENOTSUP),
     (lambda: lib.agq_quantize(A, 0, A, A, A, 4, 64, 4, 48, None), ENOTSUP),
     (lambda: lib.agq_quantize(A2, 0, A, A, A, 4, 64, 4, 64, None), EINVAL),
     (lambda: lib.agq_quantize(NUL, 0, A, A, A, 4, 64, 4, 64, None), EINVAL),
@@ -168,6 +174,7 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: fused(x=NUL), EINVAL),
     (lambda: fused(y=NUL), EINVAL),
     (lambda: fused(bits=2), ENOTSUP),
+    (lambda: fused(bits=3), ENOTSUP),
     (lambda: fused(K=65536 + 64), ENOTSUP),
     (lambda: fused(K=32768 + 64, bits=8), ENOTSUP),
     (lambda: fused(N=1 << 31), ENOTSUP),
@@ -215,7 +222,7 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: moe(ws=ctypes.c_void_p(0x10008)), EINVAL),
     (lambda: moe(ex=ctypes.c_void_p(0x10002)), EINVAL),
     (lambda: lib.agq_dequantize(A, A, A, ctypes.c_void_p(0x10004), 4, 64, 4, 64, None), EINVAL),
-    (lambda: lib.agq_dequantize(A, A, A, A, 4, 64, 5, 64, None), ENOTSUP),
+    (lambda: lib.agq_dequantize(A, A, A, A, 4, 64, 7, 64, None), ENOTSUP),
 ])
 def test_host_validation(call, status):
     assert call() == status

@@ -1,4 +1,4 @@
-"""GPU parity of the format breadth: the device quantizer and group sizes 32 and 128.
+"""GPU parity of the format breadth: the device quantizer (every width) and group sizes 32 and 128.
 
 The quantizer's codes, scales and biases must equal the oracle's bit for bit (every step
 is one IEEE binary32 operation on both sides, so each code is decided in the same
@@ -34,7 +34,7 @@ def weights(seed, N, K):
     return w
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("gs", [32, 64, 128])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_quantize_bit_exact(bits, gs, dtype):

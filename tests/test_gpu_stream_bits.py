@@ -1,0 +1,121 @@
+"""GPU parity of the bit-stream widths: 2-, 3-, 5- and 6-bit affine codes (group size 64),
+whose codes fill each row's low-first bit stream (a 3-, 5- or 6-bit code can run into the
+next word). The products (agq_qmv, agq_qmv_wide, and agq_qmm in passes of 8 rows) meet the
+usual tolerance against the oracle on every row, |y_gpu - y_ref| <= 2e-3 * sum_k |x_k w_k|
+(plus half a bf16 ulp where K <= 128); one-hot columns give bf16(w_hat) bit for bit (each
+weight fma(s, q, b) is exact in fp32 for the quantizer's recipe); dequantization is bitwise.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from gpu_util import bf16_bits_host, bf16_dev, check_close, progress, u32_dev
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import affine_group_quantized_amd as agq  # noqa: E402
+
+BITS = [2, 3, 5, 6]
+
+
+def dev_weight(d):
+    return u32_dev(d["w"]), bf16_dev(d["scales"]), bf16_dev(d["biases"])
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("M,N,K", [
+    (1, 4096, 4096), (1, 1000, 14336), (3, 777, 4160), (8, 300, 2048), (5, 17, 64), (2, 33, 128),
+    (4, 2048, 8192), (7, 130, 4096 + 64 * 3),
+])
+def test_stream_bits_products(bits, M, N, K):
+    """Several 64-group chunks of K, partial last chunks, weight rows past the last full
+    block, and every activation-row count form (1, 2, 4, 8 and between)."""
+    d = si.draw_quantized_weight(50, 10 * bits + M, N, K, bits)
+    x = si.draw_activations(50, 100 + M, M, K)
+    w, s, b = dev_weight(d)
+    progress(f"stream bits={bits} M={M} N={N} K={K}")
+    xd = bf16_dev(x)
+    y = agq.qmv(xd[0], w, s, b, bits=bits)[None] if M == 1 else agq.qmv_wide(xd, w, s, b, bits=bits)
+    torch.cuda.synchronize()
+    y_ref, A = oracle.qmv(x, d["w"], d["scales"], d["biases"], K, bits)
+    worst = check_close(y, y_ref, A, f"bits={bits} M={M} N={N} K={K}", extra_half_ulp=K <= 128)
+    progress(f"stream bits: ok, worst |err|/A = {worst:.3e}")
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_stream_bits_one_hot_columns_are_bitwise_weights(bits):
+    """x = e_k for every column of 5 groups (all 64 positions of a code in its group, so
+    every straddling position): y[n] = bf16(w_hat[n, k]) bit for bit, through qmm's passes
+    of 8 rows."""
+    N, K = 300, 320
+    d = si.draw_quantized_weight(51, bits, N, K, bits)
+    w, s, b = dev_weight(d)
+    ref, bad = oracle.dequantize(d["w"], d["scales"], d["biases"], K, bits)
+    assert bad == 0
+    want = si.bf16_bits(ref.astype(np.float32))
+    x = np.zeros((K, K), np.uint16)
+    x[np.arange(K), np.arange(K)] = 0x3F80
+    progress(f"stream bits one-hot bits={bits}")
+    got = bf16_bits_host(agq.qmm(bf16_dev(x), w, s, b, bits=bits))
+    assert np.array_equal(got, want.T)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("gs", [32, 64, 128])
+def test_stream_bits_dequantize_bit_exact(bits, gs):
+    N, K = 97, 1024
+    g = np.random.default_rng([52, bits, gs])
+    q = g.integers(0, 2 ** bits, size=(N, K), dtype=np.uint8)
+    sc = si.bf16_bits((0.01 + 0.02 * g.random((N, K // gs))).astype(np.float32))
+    bi = si.bf16_bits((-0.05 + 0.03 * g.standard_normal((N, K // gs))).astype(np.float32))
+    wq = si.pack_codes(q, bits)
+    progress(f"stream bits dequantize bits={bits} gs={gs}")
+    out = agq.dequantize(u32_dev(wq), bf16_dev(sc), bf16_dev(bi), bits=bits, group_size=gs)
+    torch.cuda.synchronize()
+    ref, bad = oracle.dequantize(wq, sc, bi, K, bits, gs)
+    assert bad == 0
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_stream_bits_qmm_passes_and_device_quantizer(bits):
+    """Weights quantized on the device (the oracle's codes bit for bit) feed a 20-row qmm
+    (passes of 8, 8 and 4 rows) that meets the oracle bound on every row."""
+    N, K, M = 500, 1024, 20
+    wf = (0.02 * np.random.default_rng([53, bits]).standard_normal((N, K))).astype(np.float32)
+    x = si.draw_activations(53, bits, M, K)
+    progress(f"stream bits quantize -> qmm bits={bits}")
+    codes, sc, bi = agq.quantize(torch.as_tensor(wf, device="cuda"), bits=bits)
+    y = agq.qmm(bf16_dev(x), codes, sc, bi, bits=bits)
+    torch.cuda.synchronize()
+    wq, s_ref, b_ref = oracle.quantize(wf, bits)
+    assert np.array_equal(codes.cpu().numpy().view(np.uint32), wq)
+    y_ref, A = oracle.qmv(x, wq, s_ref, b_ref, K, bits)
+    check_close(y, y_ref, A, f"quantize -> qmm bits={bits}")
+
+
+def test_stream_bits_refused_where_not_supported():
+    """The gathers and the fused projection take 4- or 8-bit codes; other group sizes
+    (32, 128) are refused for the bit-stream products; every refusal precedes any launch."""
+    N, K = 64, 256
+    d = si.draw_quantized_weight(54, 0, N, K, 3)
+    w, s, b = dev_weight(d)
+    x = bf16_dev(si.draw_activations(54, 1, 2, K))
+    rhs, lhs = u32_dev(np.zeros(2, np.uint32)), u32_dev(np.arange(2, dtype=np.uint32))
+    for call in (lambda: agq.gather_qmv(x, w[None], s[None], b[None], rhs_indices=rhs, lhs_indices=lhs, bits=3),
+                 lambda: agq.qmv_fused(x[0], w, s, b, bits=3)):
+        with pytest.raises(agq.AgqError) as e:
+            call()
+        assert e.value.status == agq.AGQ_ENOTSUP
+    d32 = si.pack_codes(np.zeros((N, K), np.uint8), 3)
+    with pytest.raises(agq.AgqError) as e:
+        agq.qmv(x[0], u32_dev(d32), bf16_dev(np.zeros((N, K // 32), np.uint16)),
+                bf16_dev(np.zeros((N, K // 32), np.uint16)), bits=3, group_size=32)
+    assert e.value.status == agq.AGQ_ENOTSUP
