@@ -7,17 +7,23 @@
 // 4- and 8-bit layouts; a 3-, 5- or 6-bit code may run into the next word).
 // A 64-column group is then exactly 2*bits words (16, 24, 40 or 48 bytes).
 //
-//     y[m, n] = sum_k x[m, k] * w[n, k],  w = fma(s[n, k/64], q[n, k], b[n, k/64])
+//     y[m, n] = sum_k x[m, k] * (s[n, g] * q[n, k] + b[n, g]),  g = k / 64
+//             = sum_g s[n, g] * D[m, n, g] + (b[n, g] - 128 s[n, g]) * X[m, g],
+//     D = sum_{k in g} x[m, k] * (128 + q[n, k]),  X = sum_{k in g} x[m, k]
+// (the regrouping of the 4-bit VALU products). Each pair of adjacent codes
+// becomes the bfloat16 pair (128 + q, 128 + q') exactly (a code below 128 in
+// the low mantissa bits of 0x4300), and one v_dot2c_f32_bf16 per activation
+// row takes it against the pair of activations in natural order: about two
+// VALU instructions per code (a shift or funnel shift, two and-ors and a
+// shift per pair) plus half a dot per code and row.
 //
 // Layout of the work: lane l of a wave takes group l of a 64-group chunk of K,
 // so a wave reads one weight row's chunk as one contiguous run; each wave
 // takes 4 weight rows, a block 4 waves. Per chunk the block stages x (up to 8
 // rows) in LDS as 16-byte pieces [row][piece][group], so the 64 lanes read 64
-// consecutive pieces (no bank conflicts). Per code: a shift or funnel shift
-// and a mask, the conversion, one fma to w, and one fma per activation row;
-// the wave sums come from the DPP / permlane tree of the VALU products. The
-// work per weight is 4-6 VALU instructions, so these forms are VALU-bound
-// rather than HBM-bound.
+// consecutive pieces (no bank conflicts), once for the wave's 4 rows, with
+// their sums X. The wave sums come from the DPP / permlane tree of the VALU
+// products.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -38,6 +44,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const void *p, uint32_t b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
 }
 
+// Block barrier over LDS only (a __syncthreads() fence would also wait for the
+// weight loads in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt: at most N vector memory operations outstanding (other counters free).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+    asm volatile("" ::: "memory");
+}
+
 // Code j of a run of NW words holding a bit stream of BITS-bit codes.
 template <int BITS, int NW>
 __device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[NW], int j) {
@@ -48,6 +66,21 @@ __device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[NW], int j) 
     else
         v = __builtin_amdgcn_alignbit(w[word + 1], w[word], (uint32_t)shift);
     return v & ((1u << BITS) - 1u);
+}
+
+// Codes 2i and 2i + 1 of a run of NW stream words as the bfloat16 pair
+// (128 + q_2i, 128 + q_2i+1): both codes sit in the 32 bits from stream bit
+// 2*BITS*i (one word, or a funnel shift across two).
+template <int BITS, int NW>
+__device__ __forceinline__ uint32_t code_pair_bf16(const uint32_t (&w)[NW], int i) {
+    const int first = 2 * BITS * i, word = first >> 5, shift = first & 31;
+    uint32_t t;
+    if (shift + 2 * BITS <= 32)
+        t = shift ? w[word] >> shift : w[word];
+    else
+        t = __builtin_amdgcn_alignbit(w[word + 1], w[word], (uint32_t)shift);
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+    return ((t << (16 - BITS)) & (mask << 16)) | (t & mask) | 0x43004300u;
 }
 
 // The 2*BITS words of group g of a row: 16-byte loads where groups are 16-byte
@@ -91,18 +124,21 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
         for (int m = 0; m < MW; ++m) acc[r][m] = 0.f;
 
     for (int c0 = 0; c0 < G; c0 += 64) {
-        __syncthreads();  // the previous chunk's pieces have been read
-        // x of the chunk; rows past M read zero (the descriptor's range), groups past G are zeroed.
-        for (int p = threadIdx.x; p < MW * 512; p += 256) {
-            const int m = p >> 9, g = (p >> 3) & 63, j8 = p & 7;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (c0 + g < G)
-                v = __builtin_amdgcn_raw_buffer_load_b128(
-                    xr, ((uint32_t)m * (uint32_t)a.K + (uint32_t)(c0 + g) * 64u + 8u * (uint32_t)j8) * 2u, 0, 0);
-            xs[(m * 8 + j8) * 64 + g] = v;
+        // x of the chunk with direct-to-LDS loads, issued first: instruction
+        // (m, j8) brings piece j8 of every group of row m, lane g landing at slot
+        // g of [m][j8][.]. Rows past M and columns past K read zero (each row's
+        // range is its own K columns). The 4 waves take every fourth (m, j8).
+        lds_barrier();  // the previous chunk's pieces have been read
+        for (int q = wave_id(); q < MW * 8; q += kWaves) {
+            const int m = q >> 3, j8 = q & 7;
+            const __amdgpu_buffer_rsrc_t xr = span(a.x + (int64_t)(m < a.M ? m : 0) * a.K, m < a.M ? (uint32_t)a.K * 2u : 0u);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (__attribute__((address_space(3))) void *)(xs + q * 64),
+                16, ((uint32_t)(c0 + lane) * 64u + 8u * (uint32_t)j8) * 2u, 0, 0, 0);
         }
         // The codes, scale and bias of group c0 + lane of each of the wave's rows
-        // (zeros past the row's groups and for rows past N).
+        // (zeros past the row's groups and for rows past N), issued behind x so
+        // that the two fetches overlap.
         uint32_t w[kRpw][2 * BITS];
         uint32_t sc[kRpw], bi[kRpw];
 #pragma unroll
@@ -116,27 +152,48 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
             sc[r] = __builtin_amdgcn_raw_buffer_load_b16(span(a.s + rr * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
             bi[r] = __builtin_amdgcn_raw_buffer_load_b16(span(a.b + rr * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
         }
-        __syncthreads();
+        // Both fetches are in flight together; wait for all of them (the compiler
+        // may merge the weight loads, so no count of them is assumed), then for
+        // every wave's pieces at the barrier.
+        wait_vm<0>();
+        lds_barrier();
+        // D per row and activation row, and X, over the lane's group.
+        float d[kRpw][MW], sx[MW];
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+            sx[m] = 0.f;
+#pragma unroll
+            for (int r = 0; r < kRpw; ++r) d[r][m] = 0.f;
+        }
 #pragma unroll
         for (int j8 = 0; j8 < 8; ++j8) {
             u32x4 xv[MW];
 #pragma unroll
-            for (int m = 0; m < MW; ++m) xv[m] = xs[(m * 8 + j8) * 64 + lane];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                float xf[MW];
-#pragma unroll
-                for (int m = 0; m < MW; ++m) {
-                    const uint32_t pair = t < 2 ? xv[m].x : t < 4 ? xv[m].y : t < 6 ? xv[m].z : xv[m].w;
-                    xf[m] = (t & 1) ? bf16_hi(pair) : bf16_lo(pair);
-                }
-#pragma unroll
-                for (int r = 0; r < kRpw; ++r) {
-                    const float wv = fmaf(bf16_lo(sc[r]), (float)stream_code<BITS>(w[r], 8 * j8 + t), bf16_lo(bi[r]));
-#pragma unroll
-                    for (int m = 0; m < MW; ++m) acc[r][m] = fmaf(xf[m], wv, acc[r][m]);
-                }
+            for (int m = 0; m < MW; ++m) {
+                xv[m] = xs[(m * 8 + j8) * 64 + lane];
+                sx[m] = dot2_bf16(xv[m].x, 0x3F803F80u, sx[m]);
+                sx[m] = dot2_bf16(xv[m].y, 0x3F803F80u, sx[m]);
+                sx[m] = dot2_bf16(xv[m].z, 0x3F803F80u, sx[m]);
+                sx[m] = dot2_bf16(xv[m].w, 0x3F803F80u, sx[m]);
             }
+#pragma unroll
+            for (int r = 0; r < kRpw; ++r)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t cp = code_pair_bf16<BITS>(w[r], 4 * j8 + p);
+#pragma unroll
+                    for (int m = 0; m < MW; ++m) {
+                        const uint32_t xp = p == 0 ? xv[m].x : p == 1 ? xv[m].y : p == 2 ? xv[m].z : xv[m].w;
+                        d[r][m] = dot2_bf16(xp, cp, d[r][m]);
+                    }
+                }
+        }
+#pragma unroll
+        for (int r = 0; r < kRpw; ++r) {
+            const float s = bf16_lo(sc[r]);
+            const float c = fmaf(-128.f, s, bf16_lo(bi[r]));
+#pragma unroll
+            for (int m = 0; m < MW; ++m) acc[r][m] = fmaf(c, sx[m], fmaf(s, d[r][m], acc[r][m]));
         }
     }
 
