@@ -10,23 +10,31 @@
 //     y[m, n] = sum_k x[m, k] * (s[n, g] * q[n, k] + b[n, g]),  g = k / 64
 //             = sum_g s[n, g] * D[m, n, g] + (b[n, g] - 128 s[n, g]) * X[m, g],
 //     D = sum_{k in g} x[m, k] * (128 + q[n, k]),  X = sum_{k in g} x[m, k]
-// (the regrouping of the 4-bit VALU products). Each pair of adjacent codes
-// becomes the bfloat16 pair (128 + q, 128 + q') exactly (a code below 128 in
-// the low mantissa bits of 0x4300), and one v_dot2c_f32_bf16 per activation
-// row takes it against the pair of activations in natural order: about two
-// VALU instructions per code (a shift or funnel shift, two and-ors and a
-// shift per pair) plus half a dot per code and row.
+// (the regrouping of the 4-bit VALU products), with the constant 128 replaced
+// by a per-code constant under the window decode below.
 //
 // Layout of the work: lane l of a wave takes group l of a 64-group chunk of K,
-// so a wave reads one weight row's chunk as one contiguous run; each wave
-// takes 4 weight rows, a block 4 waves. Per chunk the block stages x (up to 8
-// rows) in LDS as 16-byte pieces [row][piece][group], so the 64 lanes read 64
-// consecutive pieces (no bank conflicts), once for the wave's 4 rows, with
-// their sums X. The wave sums come from the DPP / permlane tree of the VALU
+// each wave 4 weight rows, a block 4 waves. Per chunk the block stages x (up
+// to 8 rows) in LDS as 16-byte pieces [row][piece][group] with direct-to-LDS
+// loads, so the 64 lanes read 64 consecutive pieces (no bank conflicts).
+// Codes become bf16 lanes exactly (a code below 128 in the low mantissa bits
+// of a bf16 with a fixed exponent), and v_dot2c_f32_bf16 takes each lane pair
+// against the matching pair of activations:
+//   - with one or two activation rows at 2, 3 and 5 bits, the window decode:
+//     codes k and k + d share a 32-bit window of the stream and one and-or
+//     makes the pair (plan below);
+//   - otherwise adjacent codes (2i, 2i + 1) are taken from one funnel-shifted
+//     word and moved into the two bf16 lanes.
+// At 3, 5 and 6 bits with one or two activation rows the wave's weight rows
+// also pass through LDS (loads of contiguous 16-byte pieces; a lane reading
+// its own 24- to 48-byte group directly spreads each load over 2-3 times the
+// cache lines). The wave sums come from the DPP / permlane tree of the VALU
 // products.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 #include "qmv_device.hpp"
 
@@ -83,6 +91,192 @@ __device__ __forceinline__ uint32_t code_pair_bf16(const uint32_t (&w)[NW], int 
     return ((t << (16 - BITS)) & (mask << 16)) | (t & mask) | 0x43004300u;
 }
 
+// ---- Window decode (2, 3 and 5 bits; one or two activation rows) ----
+//
+// A bfloat16 with exponent field 134 - e and a code q in mantissa bits
+// [e, e + bits) reads as the exact value 2^(7-e) + q (for e + bits <= 7). So a
+// code whose stream bits fall inside mantissa bits 0..6 of either half of a
+// 32-bit window of the stream becomes a bf16 lane with one v_and_or_b32:
+// (window & mask) | magic, the magic holding each half's exponent. Codes k and
+// k + d with d = 8, 5, 3 (2, 3, 5 bits) lie 16, 15 and 15 stream bits apart,
+// so both fit one window, one in each half, and at 2 and 3 bits successive
+// pairs share windows. The group's 64 codes become 32 such pairs; at 3 and 5
+// bits the last four codes (which have no partner d further on) are taken as
+// adjacent pairs by code_pair_bf16. Against each pair the activations go as
+// the matching pair (x[k], x[k + d]), built by one byte permute, and
+//     sum_k q_k x_k = D - C,  D = sum over pairs of dot(code pair, x pair),
+//                             C = sum over pairs of dot(magic pair, x pair),
+// with C shared by the wave's rows. At 6 bits a code fills all but one
+// mantissa bit and no two codes 15..17 bits apart exist, so 6 bits, and any
+// three or more activation rows (where the per-row C and pair permutes cost
+// what the window saves), keep the adjacent pairs.
+
+struct WinSlot {
+    int lo, hi;      // the two codes (group positions): low and high bf16 lane
+    int p;           // window start (stream bit; -1 means the word shifted left by one)
+    bool win;        // false: adjacent pair (lo, lo + 1) by code_pair_bf16
+    uint32_t mask;   // code bits of the window
+    uint32_t magic;  // the two lanes' exponents; as bf16 values 2^(7-e_lo), 2^(7-e_hi)
+    int mi;          // index of magic among the plan's distinct magics
+    uint32_t sel;    // byte permute building (x[lo], x[hi]) from the natural x pairs
+};
+
+constexpr int kMaxMagics = 4;
+
+template <int BITS>
+struct WinPlan {
+    WinSlot s[32];
+    uint32_t magics[kMaxMagics];
+    int n_magics;
+    bool even[kMaxMagics];  // both lanes of the magic hold the same value c
+    float c[kMaxMagics];    // that value, 2^(7-e)
+};
+
+template <int BITS>
+constexpr WinPlan<BITS> make_win_plan() {
+    WinPlan<BITS> pl{};
+    constexpr int d = BITS == 2 ? 8 : BITS == 3 ? 5 : 3;
+    constexpr int room = 7 - BITS;  // largest code offset inside a mantissa
+    constexpr uint32_t cm = (1u << BITS) - 1u;
+    int n = 0, b0 = 0;
+    for (; b0 + 2 * d <= 64; b0 += 2 * d) {
+        int p = 0;
+        bool have = false;
+        for (int i = 0; i < d; ++i) {
+            const int lo = b0 + i, hi = lo + d;
+            const int olo = BITS * lo, ohi = BITS * hi - 16;  // high code's offset from the window's bit 16
+            const int pmax = olo < ohi ? olo : ohi;
+            const int pmin = (olo > ohi ? olo : ohi) - room;
+            if (!have || p < pmin || p > pmax) p = pmax;  // reuse the previous window where it fits
+            have = true;
+            const int elo = olo - p, ehi = ohi - p;
+            WinSlot &s = pl.s[n++];
+            s.lo = lo;
+            s.hi = hi;
+            s.p = p;
+            s.win = true;
+            s.mask = (cm << elo) | (cm << (16 + ehi));
+            s.magic = (uint32_t(134 - ehi) << 23) | (uint32_t(134 - elo) << 7);
+            const uint32_t a = 2u * (uint32_t)(lo & 1), b = 4u + 2u * (uint32_t)(hi & 1);
+            s.sel = a | (a + 1u) << 8 | b << 16 | (b + 1u) << 24;
+        }
+    }
+    for (int k = b0; k < 64; k += 2) {
+        WinSlot &s = pl.s[n++];
+        s.lo = k;
+        s.hi = k + 1;
+        s.p = 0;
+        s.win = false;
+        s.mask = 0;
+        s.magic = 0x43004300u;
+        s.sel = 0;
+    }
+    for (int i = 0; i < 32; ++i) {
+        WinSlot &s = pl.s[i];
+        s.mi = -1;
+        for (int j = 0; j < pl.n_magics; ++j)
+            if (pl.magics[j] == s.magic) s.mi = j;
+        if (s.mi < 0 && pl.n_magics < kMaxMagics) {
+            s.mi = pl.n_magics;
+            pl.magics[pl.n_magics++] = s.magic;
+        }
+    }
+    for (int j = 0; j < pl.n_magics; ++j) {
+        const uint32_t lo = pl.magics[j] & 0xFFFFu, hi = pl.magics[j] >> 16;
+        pl.even[j] = lo == hi;
+        float c = 1.f;
+        for (int e = 127; e < (int)(lo >> 7); ++e) c *= 2.f;  // lo is exponent << 7, mantissa 0
+        pl.c[j] = c;
+    }
+    return pl;
+}
+
+// Every code of the group decoded exactly once, inside the window and inside
+// a mantissa.
+template <int BITS>
+constexpr bool win_plan_ok() {
+    constexpr WinPlan<BITS> pl = make_win_plan<BITS>();
+    int seen[64] = {};
+    for (int i = 0; i < 32; ++i) {
+        const WinSlot &s = pl.s[i];
+        if (s.lo < 0 || s.hi >= 64) return false;
+        ++seen[s.lo];
+        ++seen[s.hi];
+        if (!s.win) {
+            if (s.hi != s.lo + 1 || (s.lo & 1)) return false;
+            continue;
+        }
+        const int elo = BITS * s.lo - s.p, ehi = BITS * s.hi - 16 - s.p;
+        if (elo < 0 || ehi < 0 || elo + BITS > 7 || ehi + BITS > 7 || s.p < -1) return false;
+    }
+    for (int k = 0; k < 64; ++k)
+        if (seen[k] != 1) return false;
+    for (int i = 0; i < 32; ++i)
+        if (pl.s[i].mi < 0 || pl.magics[pl.s[i].mi] != pl.s[i].magic) return false;
+    for (int j = 0; j < pl.n_magics; ++j)
+        if ((pl.magics[j] & 0x807Fu) != 0 || (pl.even[j] && pl.c[j] * 2.f > 256.f)) return false;
+    return true;
+}
+static_assert(win_plan_ok<2>() && win_plan_ok<3>() && win_plan_ok<5>(), "window plans");
+
+template <int BITS>
+constexpr WinPlan<BITS> kWinPlan = make_win_plan<BITS>();
+
+// Stream bits [P, P + 32) of a group's NW words (zeros outside the group).
+template <int P, int NW>
+__device__ __forceinline__ uint32_t window(const uint32_t (&w)[NW]) {
+    if constexpr (P < 0) {
+        return w[0] << (-P);
+    } else {
+        constexpr int word = P >> 5, sh = P & 31;
+        if constexpr (sh == 0)
+            return w[word];
+        else if constexpr (word + 1 < NW)
+            return __builtin_amdgcn_alignbit(w[word + 1], w[word], (uint32_t)sh);
+        else
+            return w[word] >> sh;
+    }
+}
+
+// (a & mask) | magic with the magic held in a VGPR: a VOP3 operation takes no
+// literal here, and as two VOP2 operations it costs two instructions.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+    return r;
+}
+
+// A constant in a VGPR the compiler does not fold back into literals.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+    return r;
+}
+
+// s_waitcnt vmcnt(0) after two rows' accumulators are final: the operands keep
+// it below the arithmetic that produces them (a bare wait can be scheduled
+// above independent arithmetic, which would stall on loads meant to overlap it).
+template <int MW>
+__device__ __forceinline__ void wait_vm_after(const float (&a0)[MW], const float (&a1)[MW]) {
+    static_assert(MW == 1 || MW == 2, "one or two activation rows");
+    if constexpr (MW == 1)
+        asm volatile("s_waitcnt vmcnt(0)" ::"v"(a0[0]), "v"(a1[0]) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::"v"(a0[0]), "v"(a0[1]), "v"(a1[0]), "v"(a1[1]) : "memory");
+}
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int BITS, int MW>
+constexpr bool kWindowed = BITS != 6 && MW <= 2;
+
 // The 2*BITS words of group g of a row: 16-byte loads where groups are 16-byte
 // aligned (2 and 6 bits), 8-byte loads otherwise (3 and 5 bits). Past the
 // row's range (its end, or a row past N) the words read zero.
@@ -111,89 +305,245 @@ __device__ __forceinline__ void load_group(uint32_t (&w)[2 * BITS], __amdgpu_buf
 
 template <int BITS, int MW>
 __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
-    __shared__ u32x4 xs[MW * 8 * 64];  // [row][piece of 8 columns][group]
-    const int lane = threadIdx.x & 63;
-    const int64_t row0 = ((int64_t)blockIdx.x * kWaves + wave_id()) * kRpw;
+    // Weight rows of 3, 5 and 6 bits go through LDS: a lane's own group is a
+    // 24-, 40- or 48-byte run, and lanes reading their runs directly touch
+    // 2-3 times the cache lines of a contiguous read per load instruction (the
+    // address unit then bounds the kernel). Instead each wave brings its rows'
+    // chunk in with direct-to-LDS loads of 16 contiguous bytes per lane, two
+    // rows at a time, and each lane reads its group back from LDS; the second
+    // pair of rows arrives while the first is computed.
+    constexpr bool kStaged = (BITS == 3 || BITS == 5 || BITS == 6) && MW <= 2;
+    constexpr int kGroupBytes = 8 * BITS;
+    constexpr int kDmaPerRow = (64 * kGroupBytes + 1023) / 1024;
+    constexpr int kHalves = kStaged ? 2 : 1;
+    constexpr int kRows = kRpw / kHalves;  // weight rows resident at a time
+    static_assert(!kStaged || kRows == 2, "staged halves are row pairs");
+    __shared__ u32x4 xs[MW * 8 * 64];       // [row][piece of 8 columns][group]
+    __shared__ u32x4 wl[kStaged ? kWaves * kRows * kDmaPerRow * 64 : 1];  // [wave][row][1 KB piece]
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int64_t row0 = ((int64_t)blockIdx.x * kWaves + wave) * kRpw;
     const int G = a.K / 64;
     const uint32_t rowbytes = (uint32_t)a.K / 8u * BITS;
-    const __amdgpu_buffer_rsrc_t xr = span(a.x, (uint32_t)a.M * (uint32_t)a.K * 2u);
     float acc[kRpw][MW];
 #pragma unroll
     for (int r = 0; r < kRpw; ++r)
 #pragma unroll
         for (int m = 0; m < MW; ++m) acc[r][m] = 0.f;
+    uint32_t magic_v[kMaxMagics] = {};
+    if constexpr (kWindowed<BITS, MW>) {
+#pragma unroll
+        for (int j = 0; j < kWinPlan<BITS>.n_magics; ++j) magic_v[j] = vgpr_const(kWinPlan<BITS>.magics[j]);
+    }
 
     for (int c0 = 0; c0 < G; c0 += 64) {
         // x of the chunk with direct-to-LDS loads, issued first: instruction
         // (m, j8) brings piece j8 of every group of row m, lane g landing at slot
         // g of [m][j8][.]. Rows past M and columns past K read zero (each row's
         // range is its own K columns). The 4 waves take every fourth (m, j8).
-        lds_barrier();  // the previous chunk's pieces have been read
-        for (int q = wave_id(); q < MW * 8; q += kWaves) {
+        lds_barrier();  // the previous chunk's pieces (x and staged rows) have been read
+        for (int q = wave; q < MW * 8; q += kWaves) {
             const int m = q >> 3, j8 = q & 7;
             const __amdgpu_buffer_rsrc_t xr = span(a.x + (int64_t)(m < a.M ? m : 0) * a.K, m < a.M ? (uint32_t)a.K * 2u : 0u);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xr, (__attribute__((address_space(3))) void *)(xs + q * 64),
                 16, ((uint32_t)(c0 + lane) * 64u + 8u * (uint32_t)j8) * 2u, 0, 0, 0);
         }
-        // The codes, scale and bias of group c0 + lane of each of the wave's rows
+        // The codes, scale and bias of group c0 + lane of the rows of half h
         // (zeros past the row's groups and for rows past N), issued behind x so
-        // that the two fetches overlap.
-        uint32_t w[kRpw][2 * BITS];
+        // that the fetches overlap: into registers, or (staged) into the wave's
+        // LDS rows, piece i of row rr holding the row's chunk bytes
+        // [1024 i, 1024 i + 1024).
+        uint32_t w[kRows][2 * BITS];
         uint32_t sc[kRpw], bi[kRpw];
+        auto issue = [&](int h) {
 #pragma unroll
-        for (int r = 0; r < kRpw; ++r) {
-            const int64_t row = row0 + r;
-            const bool ok = row < a.N;
-            const int64_t rr = ok ? row : 0;
-            load_group<BITS>(w[r], span(a.w + rr * (rowbytes / 4u), ok ? rowbytes : 0u),
-                             (uint32_t)(c0 + lane) * 8u * BITS);
-            const uint32_t sb = ok ? (uint32_t)G * 2u : 0u;
-            sc[r] = __builtin_amdgcn_raw_buffer_load_b16(span(a.s + rr * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
-            bi[r] = __builtin_amdgcn_raw_buffer_load_b16(span(a.b + rr * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
-        }
-        // Both fetches are in flight together; wait for all of them (the compiler
-        // may merge the weight loads, so no count of them is assumed), then for
-        // every wave's pieces at the barrier.
-        wait_vm<0>();
-        lds_barrier();
-        // D per row and activation row, and X, over the lane's group.
-        float d[kRpw][MW], sx[MW];
+            for (int rr = 0; rr < kRows; ++rr) {
+                const int r = h * kRows + rr;
+                const int64_t row = row0 + r;
+                const bool ok = row < a.N;
+                const int64_t ro = ok ? row : 0;
+                const __amdgpu_buffer_rsrc_t wr = span(a.w + ro * (rowbytes / 4u), ok ? rowbytes : 0u);
+                if constexpr (kStaged) {
 #pragma unroll
-        for (int m = 0; m < MW; ++m) {
-            sx[m] = 0.f;
-#pragma unroll
-            for (int r = 0; r < kRpw; ++r) d[r][m] = 0.f;
-        }
-#pragma unroll
-        for (int j8 = 0; j8 < 8; ++j8) {
-            u32x4 xv[MW];
-#pragma unroll
-            for (int m = 0; m < MW; ++m) {
-                xv[m] = xs[(m * 8 + j8) * 64 + lane];
-                sx[m] = dot2_bf16(xv[m].x, 0x3F803F80u, sx[m]);
-                sx[m] = dot2_bf16(xv[m].y, 0x3F803F80u, sx[m]);
-                sx[m] = dot2_bf16(xv[m].z, 0x3F803F80u, sx[m]);
-                sx[m] = dot2_bf16(xv[m].w, 0x3F803F80u, sx[m]);
+                    for (int i = 0; i < kDmaPerRow; ++i)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            wr, (__attribute__((address_space(3))) void *)(wl + ((wave * kRows + rr) * kDmaPerRow + i) * 64),
+                            16, (uint32_t)c0 * kGroupBytes + (uint32_t)(i * 64 + lane) * 16u, 0, 0, 2);
+                } else {
+                    load_group<BITS>(w[rr], wr, (uint32_t)(c0 + lane) * kGroupBytes);
+                }
+                const uint32_t sb = ok ? (uint32_t)G * 2u : 0u;
+                sc[r] = __builtin_amdgcn_raw_buffer_load_b16(span(a.s + ro * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
+                bi[r] = __builtin_amdgcn_raw_buffer_load_b16(span(a.b + ro * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
             }
+        };
+        // A lane's group of each staged row, from the wave's LDS rows.
+        auto read_rows = [&]() {
 #pragma unroll
-            for (int r = 0; r < kRpw; ++r)
+            for (int rr = 0; rr < kRows; ++rr) {
+                const u32x4 *base = wl + (wave * kRows + rr) * kDmaPerRow * 64;
+                if constexpr (BITS % 2 == 0) {
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t cp = code_pair_bf16<BITS>(w[r], 4 * j8 + p);
+                    for (int i = 0; i < BITS / 2; ++i) {
+                        const u32x4 v = base[lane * (BITS / 2) + i];
+                        w[rr][4 * i] = v.x;
+                        w[rr][4 * i + 1] = v.y;
+                        w[rr][4 * i + 2] = v.z;
+                        w[rr][4 * i + 3] = v.w;
+                    }
+                } else {
+                    const u32x2 *b2 = reinterpret_cast<const u32x2 *>(base);
 #pragma unroll
-                    for (int m = 0; m < MW; ++m) {
-                        const uint32_t xp = p == 0 ? xv[m].x : p == 1 ? xv[m].y : p == 2 ? xv[m].z : xv[m].w;
-                        d[r][m] = dot2_bf16(xp, cp, d[r][m]);
+                    for (int i = 0; i < BITS; ++i) {
+                        const u32x2 v = b2[lane * BITS + i];
+                        w[rr][2 * i] = v.x;
+                        w[rr][2 * i + 1] = v.y;
                     }
                 }
+            }
+        };
+        issue(0);
+        // Every fetch of this wave so far has landed (no count of them is
+        // assumed: the compiler may merge loads), then every wave's x pieces.
+        wait_vm<0>();
+        lds_barrier();
+
+        float sx[MW];
+#pragma unroll
+        for (int m = 0; m < MW; ++m) sx[m] = 0.f;
+
+        if constexpr (kWindowed<BITS, MW>) {
+            // The plan's 32 activation pairs of the lane's group, per activation
+            // row, with C and X. Where a magic's two lanes are equal (c, c), its
+            // slots' x sums S_j give both: X += S_j, C += c S_j.
+            uint32_t xp[32][MW];
+            float cx[MW], sj[kMaxMagics][MW];
+#pragma unroll
+            for (int m = 0; m < MW; ++m) {
+                uint32_t xn[32];
+#pragma unroll
+                for (int j8 = 0; j8 < 8; ++j8) {
+                    const u32x4 v = xs[(m * 8 + j8) * 64 + lane];
+                    xn[4 * j8] = v.x;
+                    xn[4 * j8 + 1] = v.y;
+                    xn[4 * j8 + 2] = v.z;
+                    xn[4 * j8 + 3] = v.w;
+                }
+                cx[m] = 0.f;
+#pragma unroll
+                for (int j = 0; j < kMaxMagics; ++j) sj[j][m] = 0.f;
+                static_for<32>([&](auto I) {
+                    constexpr WinSlot sl = kWinPlan<BITS>.s[decltype(I)::value];
+                    uint32_t v;
+                    if constexpr (sl.win)
+                        v = __builtin_amdgcn_perm(xn[sl.hi >> 1], xn[sl.lo >> 1], sl.sel);
+                    else
+                        v = xn[sl.lo >> 1];
+                    xp[decltype(I)::value][m] = v;
+                    if constexpr (kWinPlan<BITS>.even[sl.mi]) {
+                        sj[sl.mi][m] = dot2_bf16(v, 0x3F803F80u, sj[sl.mi][m]);
+                    } else {
+                        sx[m] = dot2_bf16(v, 0x3F803F80u, sx[m]);
+                        cx[m] = dot2_bf16(v, sl.magic, cx[m]);
+                    }
+                });
+#pragma unroll
+                for (int j = 0; j < kWinPlan<BITS>.n_magics; ++j)
+                    if (kWinPlan<BITS>.even[j]) {
+                        sx[m] += sj[j][m];
+                        cx[m] = fmaf(kWinPlan<BITS>.c[j], sj[j][m], cx[m]);
+                    }
+            }
+#pragma unroll
+            for (int h = 0; h < kHalves; ++h) {
+                if constexpr (kStaged) {
+                    // The second pair of rows (and its scales, biases) after the first is done.
+                    if (h > 0) wait_vm_after<MW>(acc[h * kRows - 2], acc[h * kRows - 1]);
+                    read_rows();
+                    if (h + 1 < kHalves) {
+                        // The rows are in registers before the next pair overwrites them.
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        issue(h + 1);
+                    }
+                }
+                float d[kRows][MW];
+#pragma unroll
+                for (int rr = 0; rr < kRows; ++rr)
+#pragma unroll
+                    for (int m = 0; m < MW; ++m) d[rr][m] = 0.f;
+                static_for<32>([&](auto I) {
+                    constexpr WinSlot sl = kWinPlan<BITS>.s[decltype(I)::value];
+#pragma unroll
+                    for (int rr = 0; rr < kRows; ++rr) {
+                        uint32_t cp;
+                        if constexpr (sl.win)
+                            cp = and_or(window<sl.p>(w[rr]), sl.mask, magic_v[sl.mi]);
+                        else
+                            cp = code_pair_bf16<BITS>(w[rr], sl.lo >> 1);
+#pragma unroll
+                        for (int m = 0; m < MW; ++m) d[rr][m] = dot2_bf16(xp[decltype(I)::value][m], cp, d[rr][m]);
+                    }
+                });
+#pragma unroll
+                for (int rr = 0; rr < kRows; ++rr) {
+                    const int r = h * kRows + rr;
+                    const float s = bf16_lo(sc[r]), b = bf16_lo(bi[r]);
+#pragma unroll
+                    for (int m = 0; m < MW; ++m) acc[r][m] = fmaf(s, d[rr][m] - cx[m], fmaf(b, sx[m], acc[r][m]));
+                }
+            }
+            continue;
         }
+        // Adjacent pairs: D per row and activation row, and X, over the lane's
+        // group, x read from LDS piece by piece.
 #pragma unroll
-        for (int r = 0; r < kRpw; ++r) {
-            const float s = bf16_lo(sc[r]);
-            const float c = fmaf(-128.f, s, bf16_lo(bi[r]));
+        for (int h = 0; h < kHalves; ++h) {
+            if constexpr (kStaged) {
+                if (h > 0) wait_vm_after<MW>(acc[h * kRows - 2], acc[h * kRows - 1]);
+                read_rows();
+                if (h + 1 < kHalves) {
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    issue(h + 1);
+                }
+            }
+            float d[kRows][MW];
 #pragma unroll
-            for (int m = 0; m < MW; ++m) acc[r][m] = fmaf(c, sx[m], fmaf(s, d[r][m], acc[r][m]));
+            for (int m = 0; m < MW; ++m)
+#pragma unroll
+                for (int rr = 0; rr < kRows; ++rr) d[rr][m] = 0.f;
+#pragma unroll
+            for (int j8 = 0; j8 < 8; ++j8) {
+                u32x4 xv[MW];
+#pragma unroll
+                for (int m = 0; m < MW; ++m) {
+                    xv[m] = xs[(m * 8 + j8) * 64 + lane];
+                    if (h == 0) {
+                        sx[m] = dot2_bf16(xv[m].x, 0x3F803F80u, sx[m]);
+                        sx[m] = dot2_bf16(xv[m].y, 0x3F803F80u, sx[m]);
+                        sx[m] = dot2_bf16(xv[m].z, 0x3F803F80u, sx[m]);
+                        sx[m] = dot2_bf16(xv[m].w, 0x3F803F80u, sx[m]);
+                    }
+                }
+#pragma unroll
+                for (int rr = 0; rr < kRows; ++rr)
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const uint32_t cp = code_pair_bf16<BITS>(w[rr], 4 * j8 + p);
+#pragma unroll
+                        for (int m = 0; m < MW; ++m) {
+                            const uint32_t xq = p == 0 ? xv[m].x : p == 1 ? xv[m].y : p == 2 ? xv[m].z : xv[m].w;
+                            d[rr][m] = dot2_bf16(xq, cp, d[rr][m]);
+                        }
+                    }
+            }
+#pragma unroll
+            for (int rr = 0; rr < kRows; ++rr) {
+                const int r = h * kRows + rr;
+                const float s = bf16_lo(sc[r]);
+                const float c = fmaf(-128.f, s, bf16_lo(bi[r]));
+#pragma unroll
+                for (int m = 0; m < MW; ++m) acc[r][m] = fmaf(c, sx[m], fmaf(s, d[rr][m], acc[r][m]));
+            }
         }
     }
 

@@ -32,7 +32,7 @@ def dev_weight(d):
 @pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("M,N,K", [
     (1, 4096, 4096), (1, 1000, 14336), (3, 777, 4160), (8, 300, 2048), (5, 17, 64), (2, 33, 128),
-    (4, 2048, 8192), (7, 130, 4096 + 64 * 3),
+    (4, 2048, 8192), (7, 130, 4096 + 64 * 3), (2, 1000, 4160), (2, 4096, 14336),
 ])
 def test_stream_bits_products(bits, M, N, K):
     """Several 64-group chunks of K, partial last chunks, weight rows past the last full
@@ -65,6 +65,35 @@ def test_stream_bits_one_hot_columns_are_bitwise_weights(bits):
     progress(f"stream bits one-hot bits={bits}")
     got = bf16_bits_host(agq.qmm(bf16_dev(x), w, s, b, bits=bits))
     assert np.array_equal(got, want.T)
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_stream_bits_one_hot_columns_matvec(bits):
+    """The one- and two-row matvec forms: x = e_k (and 2 e_k as a second activation row) for
+    every column of five groups, so every position of a code in its group, including the
+    codes decoded as pairs k, k + d from one stream window and the adjacent pairs at the end
+    of a 3- or 5-bit group: y = bf16(w_hat[:, k]) and bf16(2 w_hat[:, k]) bit for bit."""
+    N, K = 300, 320
+    d = si.draw_quantized_weight(53, bits, N, K, bits)
+    w, s, b = dev_weight(d)
+    ref, bad = oracle.dequantize(d["w"], d["scales"], d["biases"], K, bits)
+    assert bad == 0
+    want1 = si.bf16_bits(ref.astype(np.float32))
+    want2 = si.bf16_bits((2 * ref).astype(np.float32))
+    eye = np.zeros((K, K), np.uint16)
+    eye[np.arange(K), np.arange(K)] = 0x3F80
+    pair = np.zeros((K, 2, K), np.uint16)
+    pair[np.arange(K), 0, np.arange(K)] = 0x3F80
+    pair[np.arange(K), 1, np.arange(K)] = 0x4000
+    xe, xp = bf16_dev(eye), bf16_dev(pair.reshape(2 * K, K))
+    progress(f"stream bits one-hot matvec bits={bits}")
+    y1 = torch.stack([agq.qmv(xe[k], w, s, b, bits=bits) for k in range(K)])
+    y2 = torch.stack([agq.qmv_wide(xp[2 * k:2 * k + 2], w, s, b, bits=bits) for k in range(K)])
+    torch.cuda.synchronize()
+    g1, g2 = bf16_bits_host(y1), bf16_bits_host(y2)
+    assert np.array_equal(g1, want1.T)
+    assert np.array_equal(g2[:, 0], want1.T)
+    assert np.array_equal(g2[:, 1], want2.T)
 
 
 @pytest.mark.parametrize("bits", BITS)
