@@ -91,7 +91,7 @@ __device__ __forceinline__ uint32_t code_pair_bf16(const uint32_t (&w)[NW], int 
     return ((t << (16 - BITS)) & (mask << 16)) | (t & mask) | 0x43004300u;
 }
 
-// ---- Window decode (2, 3 and 5 bits; one or two activation rows) ----
+// ---- Pair plans of the one- and two-row forms (window decode at 2, 3, 5 bits) ----
 //
 // A bfloat16 with exponent field 134 - e and a code q in mantissa bits
 // [e, e + bits) reads as the exact value 2^(7-e) + q (for e + bits <= 7). So a
@@ -107,9 +107,9 @@ __device__ __forceinline__ uint32_t code_pair_bf16(const uint32_t (&w)[NW], int 
 //     sum_k q_k x_k = D - C,  D = sum over pairs of dot(code pair, x pair),
 //                             C = sum over pairs of dot(magic pair, x pair),
 // with C shared by the wave's rows. At 6 bits a code fills all but one
-// mantissa bit and no two codes 15..17 bits apart exist, so 6 bits, and any
-// three or more activation rows (where the per-row C and pair permutes cost
-// what the window saves), keep the adjacent pairs.
+// mantissa bit and no two codes lie 15..17 bits apart, so the 6-bit plan is
+// 32 adjacent pairs. Three or more activation rows keep the adjacent pairs
+// (the per-row C and pair permutes would cost what the window saves).
 
 struct WinSlot {
     int lo, hi;      // the two codes (group positions): low and high bf16 lane
@@ -135,11 +135,11 @@ struct WinPlan {
 template <int BITS>
 constexpr WinPlan<BITS> make_win_plan() {
     WinPlan<BITS> pl{};
-    constexpr int d = BITS == 2 ? 8 : BITS == 3 ? 5 : 3;
+    constexpr int d = BITS == 2 ? 8 : BITS == 3 ? 5 : BITS == 5 ? 3 : 0;  // 0: adjacent pairs only
     constexpr int room = 7 - BITS;  // largest code offset inside a mantissa
     constexpr uint32_t cm = (1u << BITS) - 1u;
     int n = 0, b0 = 0;
-    for (; b0 + 2 * d <= 64; b0 += 2 * d) {
+    for (; d > 0 && b0 + 2 * d <= 64; b0 += 2 * d) {
         int p = 0;
         bool have = false;
         for (int i = 0; i < d; ++i) {
@@ -217,7 +217,7 @@ constexpr bool win_plan_ok() {
         if ((pl.magics[j] & 0x807Fu) != 0 || (pl.even[j] && pl.c[j] * 2.f > 256.f)) return false;
     return true;
 }
-static_assert(win_plan_ok<2>() && win_plan_ok<3>() && win_plan_ok<5>(), "window plans");
+static_assert(win_plan_ok<2>() && win_plan_ok<3>() && win_plan_ok<5>() && win_plan_ok<6>(), "window plans");
 
 template <int BITS>
 constexpr WinPlan<BITS> kWinPlan = make_win_plan<BITS>();
@@ -274,8 +274,6 @@ __device__ __forceinline__ void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int BITS, int MW>
-constexpr bool kWindowed = BITS != 6 && MW <= 2;
 
 // The 2*BITS words of group g of a row: 16-byte loads where groups are 16-byte
 // aligned (2 and 6 bits), 8-byte loads otherwise (3 and 5 bits). Past the
@@ -305,20 +303,21 @@ __device__ __forceinline__ void load_group(uint32_t (&w)[2 * BITS], __amdgpu_buf
 
 template <int BITS, int MW>
 __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
-    // Weight rows of 3, 5 and 6 bits go through LDS: a lane's own group is a
-    // 24-, 40- or 48-byte run, and lanes reading their runs directly touch
-    // 2-3 times the cache lines of a contiguous read per load instruction (the
-    // address unit then bounds the kernel). Instead each wave brings its rows'
-    // chunk in with direct-to-LDS loads of 16 contiguous bytes per lane, two
-    // rows at a time, and each lane reads its group back from LDS; the second
-    // pair of rows arrives while the first is computed.
-    constexpr bool kStaged = (BITS == 3 || BITS == 5 || BITS == 6) && MW <= 2;
+    // One or two activation rows (the decode forms): the weight rows go through
+    // LDS. A lane's own group is a 16- to 48-byte run, and lanes reading their
+    // runs directly touch up to 2-3 times the cache lines of a contiguous read
+    // per load instruction (the address unit then bounds the kernel). Instead
+    // each wave brings its rows' chunk in with direct-to-LDS loads of 16
+    // contiguous bytes per lane, two rows at a time, and each lane reads its
+    // group back from LDS. The fetches run one step ahead of the arithmetic:
+    // the second pair of rows arrives while the first is computed, and the
+    // next chunk's x and first pair while the second is.
+    constexpr bool kStaged = MW <= 2;
     constexpr int kGroupBytes = 8 * BITS;
     constexpr int kDmaPerRow = (64 * kGroupBytes + 1023) / 1024;
-    constexpr int kHalves = kStaged ? 2 : 1;
-    constexpr int kRows = kRpw / kHalves;  // weight rows resident at a time
-    static_assert(!kStaged || kRows == 2, "staged halves are row pairs");
-    __shared__ u32x4 xs[MW * 8 * 64];       // [row][piece of 8 columns][group]
+    constexpr int kRows = 2;  // staged weight rows resident at a time
+    static_assert(kRpw == 2 * kRows, "two pairs of rows per wave");
+    __shared__ u32x4 xs[MW * 8 * 64];  // [row][piece of 8 columns][group]
     __shared__ u32x4 wl[kStaged ? kWaves * kRows * kDmaPerRow * 64 : 1];  // [wave][row][1 KB piece]
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int64_t row0 = ((int64_t)blockIdx.x * kWaves + wave) * kRpw;
@@ -329,18 +328,12 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
     for (int r = 0; r < kRpw; ++r)
 #pragma unroll
         for (int m = 0; m < MW; ++m) acc[r][m] = 0.f;
-    uint32_t magic_v[kMaxMagics] = {};
-    if constexpr (kWindowed<BITS, MW>) {
-#pragma unroll
-        for (int j = 0; j < kWinPlan<BITS>.n_magics; ++j) magic_v[j] = vgpr_const(kWinPlan<BITS>.magics[j]);
-    }
 
-    for (int c0 = 0; c0 < G; c0 += 64) {
-        // x of the chunk with direct-to-LDS loads, issued first: instruction
-        // (m, j8) brings piece j8 of every group of row m, lane g landing at slot
-        // g of [m][j8][.]. Rows past M and columns past K read zero (each row's
-        // range is its own K columns). The 4 waves take every fourth (m, j8).
-        lds_barrier();  // the previous chunk's pieces (x and staged rows) have been read
+    // x of chunk c0 with direct-to-LDS loads: instruction (m, j8) brings piece
+    // j8 of every group of row m, lane g landing at slot g of [m][j8][.]. Rows
+    // past M and columns past K read zero (each row's range is its own K
+    // columns). The 4 waves take every fourth (m, j8).
+    auto x_dma = [&](int c0) {
         for (int q = wave; q < MW * 8; q += kWaves) {
             const int m = q >> 3, j8 = q & 7;
             const __amdgpu_buffer_rsrc_t xr = span(a.x + (int64_t)(m < a.M ? m : 0) * a.K, m < a.M ? (uint32_t)a.K * 2u : 0u);
@@ -348,36 +341,41 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
                 xr, (__attribute__((address_space(3))) void *)(xs + q * 64),
                 16, ((uint32_t)(c0 + lane) * 64u + 8u * (uint32_t)j8) * 2u, 0, 0, 0);
         }
-        // The codes, scale and bias of group c0 + lane of the rows of half h
-        // (zeros past the row's groups and for rows past N), issued behind x so
-        // that the fetches overlap: into registers, or (staged) into the wave's
-        // LDS rows, piece i of row rr holding the row's chunk bytes
-        // [1024 i, 1024 i + 1024).
-        uint32_t w[kRows][2 * BITS];
+    };
+    // Scale and bias of group c0 + lane of row r (zero past the row's groups and
+    // for rows past N), and the row's code buffer.
+    auto row_rsrc = [&](int r, int c0, uint32_t &s_out, uint32_t &b_out) {
+        const int64_t row = row0 + r;
+        const bool ok = row < a.N;
+        const int64_t ro = ok ? row : 0;
+        const uint32_t sb = ok ? (uint32_t)G * 2u : 0u;
+        s_out = __builtin_amdgcn_raw_buffer_load_b16(span(a.s + ro * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
+        b_out = __builtin_amdgcn_raw_buffer_load_b16(span(a.b + ro * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
+        return span(a.w + ro * (rowbytes / 4u), ok ? rowbytes : 0u);
+    };
+
+    if constexpr (kStaged) {
+        uint32_t magic_v[kMaxMagics];
+#pragma unroll
+        for (int j = 0; j < kWinPlan<BITS>.n_magics; ++j) magic_v[j] = vgpr_const(kWinPlan<BITS>.magics[j]);
         uint32_t sc[kRpw], bi[kRpw];
-        auto issue = [&](int h) {
+        // Rows 2h, 2h + 1 of chunk c0 into the wave's LDS rows (piece i of row rr
+        // holds the row's chunk bytes [1024 i, 1024 i + 1024); past the row's
+        // end, zeros), with their scales and biases.
+        auto issue = [&](int h, int c0) {
 #pragma unroll
             for (int rr = 0; rr < kRows; ++rr) {
-                const int r = h * kRows + rr;
-                const int64_t row = row0 + r;
-                const bool ok = row < a.N;
-                const int64_t ro = ok ? row : 0;
-                const __amdgpu_buffer_rsrc_t wr = span(a.w + ro * (rowbytes / 4u), ok ? rowbytes : 0u);
-                if constexpr (kStaged) {
+                const __amdgpu_buffer_rsrc_t wr = row_rsrc(h * kRows + rr, c0, sc[h * kRows + rr], bi[h * kRows + rr]);
 #pragma unroll
-                    for (int i = 0; i < kDmaPerRow; ++i)
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                            wr, (__attribute__((address_space(3))) void *)(wl + ((wave * kRows + rr) * kDmaPerRow + i) * 64),
-                            16, (uint32_t)c0 * kGroupBytes + (uint32_t)(i * 64 + lane) * 16u, 0, 0, 2);
-                } else {
-                    load_group<BITS>(w[rr], wr, (uint32_t)(c0 + lane) * kGroupBytes);
-                }
-                const uint32_t sb = ok ? (uint32_t)G * 2u : 0u;
-                sc[r] = __builtin_amdgcn_raw_buffer_load_b16(span(a.s + ro * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
-                bi[r] = __builtin_amdgcn_raw_buffer_load_b16(span(a.b + ro * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
+                for (int i = 0; i < kDmaPerRow; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        wr, (__attribute__((address_space(3))) void *)(wl + ((wave * kRows + rr) * kDmaPerRow + i) * 64),
+                        16, (uint32_t)c0 * kGroupBytes + (uint32_t)(i * 64 + lane) * 16u, 0, 0, 2);
             }
         };
-        // A lane's group of each staged row, from the wave's LDS rows.
+        uint32_t w[kRows][2 * BITS];
+        // A lane's group of each staged row, then the rows are free for the
+        // next loads.
         auto read_rows = [&]() {
 #pragma unroll
             for (int rr = 0; rr < kRows; ++rr) {
@@ -401,23 +399,22 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
                     }
                 }
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         };
-        issue(0);
-        // Every fetch of this wave so far has landed (no count of them is
-        // assumed: the compiler may merge loads), then every wave's x pieces.
-        wait_vm<0>();
-        lds_barrier();
 
-        float sx[MW];
-#pragma unroll
-        for (int m = 0; m < MW; ++m) sx[m] = 0.f;
-
-        if constexpr (kWindowed<BITS, MW>) {
-            // The plan's 32 activation pairs of the lane's group, per activation
-            // row, with C and X. Where a magic's two lanes are equal (c, c), its
+        x_dma(0);
+        issue(0, 0);
+        for (int c0 = 0; c0 < G; c0 += 64) {
+            // This chunk's x (every wave's pieces) and this wave's first pair of
+            // rows have landed. Tied to the last rows' sums so that no wait is
+            // hoisted above the previous chunk's arithmetic.
+            wait_vm_after<MW>(acc[2], acc[3]);
+            lds_barrier();
+            // The plan's 32 activation pairs of the lane's group per activation
+            // row, with X and C. Where a magic's two lanes are equal (c, c), its
             // slots' x sums S_j give both: X += S_j, C += c S_j.
             uint32_t xp[32][MW];
-            float cx[MW], sj[kMaxMagics][MW];
+            float sx[MW], cx[MW];
 #pragma unroll
             for (int m = 0; m < MW; ++m) {
                 uint32_t xn[32];
@@ -429,9 +426,11 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
                     xn[4 * j8 + 2] = v.z;
                     xn[4 * j8 + 3] = v.w;
                 }
+                float sj[kMaxMagics];
+                sx[m] = 0.f;
                 cx[m] = 0.f;
 #pragma unroll
-                for (int j = 0; j < kMaxMagics; ++j) sj[j][m] = 0.f;
+                for (int j = 0; j < kMaxMagics; ++j) sj[j] = 0.f;
                 static_for<32>([&](auto I) {
                     constexpr WinSlot sl = kWinPlan<BITS>.s[decltype(I)::value];
                     uint32_t v;
@@ -441,7 +440,7 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
                         v = xn[sl.lo >> 1];
                     xp[decltype(I)::value][m] = v;
                     if constexpr (kWinPlan<BITS>.even[sl.mi]) {
-                        sj[sl.mi][m] = dot2_bf16(v, 0x3F803F80u, sj[sl.mi][m]);
+                        sj[sl.mi] = dot2_bf16(v, 0x3F803F80u, sj[sl.mi]);
                     } else {
                         sx[m] = dot2_bf16(v, 0x3F803F80u, sx[m]);
                         cx[m] = dot2_bf16(v, sl.magic, cx[m]);
@@ -450,22 +449,24 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
 #pragma unroll
                 for (int j = 0; j < kWinPlan<BITS>.n_magics; ++j)
                     if (kWinPlan<BITS>.even[j]) {
-                        sx[m] += sj[j][m];
-                        cx[m] = fmaf(kWinPlan<BITS>.c[j], sj[j][m], cx[m]);
+                        sx[m] += sj[j];
+                        cx[m] = fmaf(kWinPlan<BITS>.c[j], sj[j], cx[m]);
                     }
             }
+            // Every wave holds the chunk's x: the next chunk's pieces may land.
+            lds_barrier();
+            const bool more = c0 + 64 < G;
+            if (more) x_dma(c0 + 64);
 #pragma unroll
-            for (int h = 0; h < kHalves; ++h) {
-                if constexpr (kStaged) {
-                    // The second pair of rows (and its scales, biases) after the first is done.
-                    if (h > 0) wait_vm_after<MW>(acc[h * kRows - 2], acc[h * kRows - 1]);
-                    read_rows();
-                    if (h + 1 < kHalves) {
-                        // The rows are in registers before the next pair overwrites them.
-                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                        issue(h + 1);
-                    }
-                }
+            for (int h = 0; h < 2; ++h) {
+                // The second pair (and the next chunk's x) after the first pair
+                // is done.
+                if (h == 1) wait_vm_after<MW>(acc[0], acc[1]);
+                read_rows();
+                if (h == 0)
+                    issue(1, c0);
+                else if (more)
+                    issue(0, c0 + 64);
                 float d[kRows][MW];
 #pragma unroll
                 for (int rr = 0; rr < kRows; ++rr)
@@ -492,57 +493,59 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
                     for (int m = 0; m < MW; ++m) acc[r][m] = fmaf(s, d[rr][m] - cx[m], fmaf(b, sx[m], acc[r][m]));
                 }
             }
-            continue;
         }
-        // Adjacent pairs: D per row and activation row, and X, over the lane's
-        // group, x read from LDS piece by piece.
+    } else {
+        // Three to eight activation rows: adjacent pairs, each code pair taken
+        // against every activation row, weights read directly into registers.
+        for (int c0 = 0; c0 < G; c0 += 64) {
+            lds_barrier();  // the previous chunk's pieces have been read
+            x_dma(c0);
+            // Issued behind x so that the two fetches overlap.
+            uint32_t w[kRpw][2 * BITS];
+            uint32_t sc[kRpw], bi[kRpw];
 #pragma unroll
-        for (int h = 0; h < kHalves; ++h) {
-            if constexpr (kStaged) {
-                if (h > 0) wait_vm_after<MW>(acc[h * kRows - 2], acc[h * kRows - 1]);
-                read_rows();
-                if (h + 1 < kHalves) {
-                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    issue(h + 1);
-                }
+            for (int r = 0; r < kRpw; ++r)
+                load_group<BITS>(w[r], row_rsrc(r, c0, sc[r], bi[r]), (uint32_t)(c0 + lane) * kGroupBytes);
+            // Every fetch so far has landed (no count of them is assumed: the
+            // compiler may merge loads), then every wave's x pieces.
+            wait_vm<0>();
+            lds_barrier();
+            float d[kRpw][MW], sx[MW];
+#pragma unroll
+            for (int m = 0; m < MW; ++m) {
+                sx[m] = 0.f;
+#pragma unroll
+                for (int r = 0; r < kRpw; ++r) d[r][m] = 0.f;
             }
-            float d[kRows][MW];
-#pragma unroll
-            for (int m = 0; m < MW; ++m)
-#pragma unroll
-                for (int rr = 0; rr < kRows; ++rr) d[rr][m] = 0.f;
 #pragma unroll
             for (int j8 = 0; j8 < 8; ++j8) {
                 u32x4 xv[MW];
 #pragma unroll
                 for (int m = 0; m < MW; ++m) {
                     xv[m] = xs[(m * 8 + j8) * 64 + lane];
-                    if (h == 0) {
-                        sx[m] = dot2_bf16(xv[m].x, 0x3F803F80u, sx[m]);
-                        sx[m] = dot2_bf16(xv[m].y, 0x3F803F80u, sx[m]);
-                        sx[m] = dot2_bf16(xv[m].z, 0x3F803F80u, sx[m]);
-                        sx[m] = dot2_bf16(xv[m].w, 0x3F803F80u, sx[m]);
-                    }
+                    sx[m] = dot2_bf16(xv[m].x, 0x3F803F80u, sx[m]);
+                    sx[m] = dot2_bf16(xv[m].y, 0x3F803F80u, sx[m]);
+                    sx[m] = dot2_bf16(xv[m].z, 0x3F803F80u, sx[m]);
+                    sx[m] = dot2_bf16(xv[m].w, 0x3F803F80u, sx[m]);
                 }
 #pragma unroll
-                for (int rr = 0; rr < kRows; ++rr)
+                for (int r = 0; r < kRpw; ++r)
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
-                        const uint32_t cp = code_pair_bf16<BITS>(w[rr], 4 * j8 + p);
+                        const uint32_t cp = code_pair_bf16<BITS>(w[r], 4 * j8 + p);
 #pragma unroll
                         for (int m = 0; m < MW; ++m) {
                             const uint32_t xq = p == 0 ? xv[m].x : p == 1 ? xv[m].y : p == 2 ? xv[m].z : xv[m].w;
-                            d[rr][m] = dot2_bf16(xq, cp, d[rr][m]);
+                            d[r][m] = dot2_bf16(xq, cp, d[r][m]);
                         }
                     }
             }
 #pragma unroll
-            for (int rr = 0; rr < kRows; ++rr) {
-                const int r = h * kRows + rr;
+            for (int r = 0; r < kRpw; ++r) {
                 const float s = bf16_lo(sc[r]);
                 const float c = fmaf(-128.f, s, bf16_lo(bi[r]));
 #pragma unroll
-                for (int m = 0; m < MW; ++m) acc[r][m] = fmaf(c, sx[m], fmaf(s, d[rr][m], acc[r][m]));
+                for (int m = 0; m < MW; ++m) acc[r][m] = fmaf(c, sx[m], fmaf(s, d[r][m], acc[r][m]));
             }
         }
     }
