@@ -277,13 +277,16 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 // The 2*BITS words of group g of a row: 16-byte loads where groups are 16-byte
 // aligned (2 and 6 bits), 8-byte loads otherwise (3 and 5 bits). Past the
-// row's range (its end, or a row past N) the words read zero.
+// row's range (its end, or a row past N) the words read zero. Only a 16-byte
+// group (2 bits) fills whole lines per load instruction; wider groups spread
+// every instruction over all lines of the wave's span, so those loads keep
+// the default cache policy (non-temporal lines were fetched again).
 template <int BITS>
 __device__ __forceinline__ void load_group(uint32_t (&w)[2 * BITS], __amdgpu_buffer_rsrc_t r, uint32_t off) {
     if constexpr (BITS % 2 == 0) {
 #pragma unroll
         for (int i = 0; i < BITS / 2; ++i) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * i, 0, 2);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * i, 0, BITS == 2 ? 2 : 0);
             w[4 * i] = v.x;
             w[4 * i + 1] = v.y;
             w[4 * i + 2] = v.z;
@@ -292,7 +295,7 @@ __device__ __forceinline__ void load_group(uint32_t (&w)[2 * BITS], __amdgpu_buf
     } else {
 #pragma unroll
         for (int i = 0; i < BITS; ++i) {
-            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 8u * i, 0, 2);
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 8u * i, 0, 0);
             w[2 * i] = v.x;
             w[2 * i + 1] = v.y;
         }
