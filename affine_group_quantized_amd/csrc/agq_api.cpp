@@ -616,12 +616,42 @@ agq_status agq_qmm_nvfp4(const void *x, const uint32_t *w, const void *scales, f
     return launch_qmm(k, a, M, N, workspace, dev, stream);
 }
 
+// The expert gather at the bit-stream widths (agq_gather_qmv and
+// agq_gather_qmm alike): one grid row per expert plane, whose pairs run as
+// the activation rows of the matvec kernel, up to mw per pass (mw from the
+// mean pairs per plane). Index arguments are checked by the callers.
+agq_status stream_gather(const void *x, const uint32_t *w, const void *scales, const void *biases,
+                         const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y, int64_t P, int64_t R,
+                         int64_t E, int64_t N, int64_t K, int bits, int group_size, void *stream) {
+    if (group_size != 64) return fail(AGQ_ENOTSUP, "bits=%d takes group size 64", bits);
+    if (K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");
+    if ((N + agq::kStreamRowsPerBlock - 1) / agq::kStreamRowsPerBlock > INT32_MAX)
+        return fail(AGQ_ENOTSUP, "N=%lld too large", (long long)N);
+    agq::StreamArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.w = w;
+    a.s = static_cast<const uint16_t *>(scales);
+    a.b = static_cast<const uint16_t *>(biases);
+    a.y = static_cast<uint16_t *>(y);
+    a.N = N;
+    a.K = (int32_t)K;
+    a.M = (int32_t)P;
+    a.lhs = lhs_indices;
+    a.rhs = rhs_indices;
+    a.R_x = (int32_t)R;
+    a.E = (int32_t)E;
+    static_assert(agq::kMaxGatherPairs >= agq::kMaxPairs, "pair list");
+    const int64_t per_plane = (P + E - 1) / E;
+    const int mw = per_plane <= 1 ? 1 : per_plane <= 2 ? 2 : per_plane <= 4 ? 4 : 8;
+    return launch(agq::stream_gather_kernel(bits, mw),
+                  dim3((unsigned)((N + agq::kStreamRowsPerBlock - 1) / agq::kStreamRowsPerBlock), (unsigned)E),
+                  dim3(256), 0, &a, stream);
+}
+
 agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y, int64_t P, int64_t R,
                           int64_t E, int64_t N, int64_t K, int bits, int group_size, void *stream) {
     agq_status st = check_operands(x, w, scales, biases, y, N, K, bits, group_size, true);
-    if (st != AGQ_OK) return st;
-    st = need_4_or_8(bits, "the expert gather");
     if (st != AGQ_OK) return st;
     if (P <= 0 || R <= 0 || E <= 0)
         return fail(AGQ_EINVAL, "P, R and E must be positive (P=%lld, R=%lld, E=%lld)", (long long)P,
@@ -634,6 +664,9 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
     if (R > INT32_MAX) return fail(AGQ_EINVAL, "R too large");
     if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
     if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
+    if (stream_bits(bits))
+        return stream_gather(x, w, scales, biases, lhs_indices, rhs_indices, y, P, R, E, N, K, bits, group_size,
+                             stream);
     if (group_size == 64 && agq::mfma_eligible(8, K, bits, E, R)) {
         agq::MfmaPlan mp;
         const void *sym = nullptr;
@@ -751,8 +784,6 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
                           int64_t E, int64_t N, int64_t K, int bits, int group_size, void *stream) {
     agq_status st = check_operands(x, w, scales, biases, y, N, K, bits, group_size, true);
     if (st != AGQ_OK) return st;
-    st = need_4_or_8(bits, "the expert gather");
-    if (st != AGQ_OK) return st;
     if (P <= 0 || R <= 0 || E <= 0)
         return fail(AGQ_EINVAL, "P, R and E must be positive (P=%lld, R=%lld, E=%lld)", (long long)P,
                     (long long)R, (long long)E);
@@ -763,6 +794,10 @@ agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, 
     if (P > agq::kMaxPairs) return fail(AGQ_ENOTSUP, "P=%lld pairs exceeds %d", (long long)P, agq::kMaxPairs);
     if (E > 65535) return fail(AGQ_ENOTSUP, "E=%lld expert planes exceeds 65535", (long long)E);
     if (E * N > kMaxN) return fail(AGQ_EINVAL, "E*N too large");
+    if (R > INT32_MAX) return fail(AGQ_EINVAL, "R too large");
+    if (stream_bits(bits))
+        return stream_gather(x, w, scales, biases, lhs_indices, rhs_indices, y, P, R, E, N, K, bits, group_size,
+                             stream);
     if (R * K * 2 >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "x must stay below 2 GiB (R*K*2 bytes)");
     if (group_size != 64) return fail(AGQ_ENOTSUP, "gather_qmm takes group size 64");
     if ((int64_t)agq::kQmmHlTileN * (K * bits / 8) >= (int64_t(1) << 31)) return fail(AGQ_ENOTSUP, "K too large");

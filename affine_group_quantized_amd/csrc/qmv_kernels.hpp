@@ -112,10 +112,21 @@ struct StreamArgs {
     int64_t N;
     int32_t K;          // a multiple of 64
     int32_t M;          // activation rows, 1 .. 8
+    // The expert gather (grid row y = expert plane; M holds the pair count P):
+    // x [R_x, K], planes w [E, N, K*bits/32], s and b [E, N, K/64], y [P, N];
+    // NULL index arrays are the identity.
+    const uint32_t *lhs;
+    const uint32_t *rhs;
+    int32_t R_x;
+    int32_t E;
 };
 constexpr int kStreamRowsPerBlock = 16;  // 4 waves of 4 weight rows
 // The matvec kernel for `bits` and M activation rows (NULL outside 2, 3, 5, 6 and 1..8).
 const void *stream_kernel(int bits, int M);
+constexpr int kMaxGatherPairs = 4096;
+// The expert gather kernel for `bits` taking up to `mw` pairs of a plane per
+// pass (grid: row blocks x planes; NULL outside 2, 3, 5, 6 and 1..8).
+const void *stream_gather_kernel(int bits, int mw);
 // Dequantize kernel of the bit-stream widths: one thread per 32 codes (`bits` words).
 const void *stream_dequant_kernel(int bits);
 

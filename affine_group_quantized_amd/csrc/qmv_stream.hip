@@ -304,7 +304,7 @@ __device__ __forceinline__ void load_group(uint32_t (&w)[2 * BITS], __amdgpu_buf
 
 }  // namespace
 
-template <int BITS, int MW>
+template <int BITS, int MW, bool GATHER = false>
 __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
     // One or two activation rows (the decode forms): the weight rows go through
     // LDS. A lane's own group is a 16- to 48-byte run, and lanes reading their
@@ -326,6 +326,69 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
     const int64_t row0 = ((int64_t)blockIdx.x * kWaves + wave) * kRpw;
     const int G = a.K / 64;
     const uint32_t rowbytes = (uint32_t)a.K / 8u * BITS;
+    // The expert gather: grid row y is expert plane e. The pairs routed to e
+    // (rhs[p] == e with lhs[p] < R) are listed in LDS and taken as the
+    // activation rows, up to MW per pass, so each used plane streams once per
+    // pass of MW pairs and an unused plane is never read. Pairs with an index
+    // out of range get NaN rows, written by the plane-0 blocks. a.M holds P.
+    __shared__ uint16_t plist[GATHER ? kMaxGatherPairs : 1];
+    __shared__ int pcount;
+    int count = a.M;
+    if constexpr (GATHER) {
+        const uint32_t e = blockIdx.y, nx = (uint32_t)a.R_x, ne = (uint32_t)a.E;
+        const int P = a.M;
+        if (e == 0)
+            for (int p = threadIdx.x; p < P; p += blockDim.x) {
+                const uint32_t xr = a.lhs ? a.lhs[p] : (uint32_t)p, ex = a.rhs ? a.rhs[p] : (uint32_t)p;
+                if (xr < nx && ex < ne) continue;
+                for (int r = 0; r < kStreamRowsPerBlock; ++r) {
+                    const int64_t n = (int64_t)blockIdx.x * kStreamRowsPerBlock + r;
+                    if (n < a.N) a.y[(int64_t)p * a.N + n] = 0x7FC0u;
+                }
+            }
+        if (wave == 0) {
+            int c = 0;
+            for (int b0 = 0; b0 < P; b0 += 64) {
+                const int p = b0 + lane;
+                bool take = false;
+                if (p < P) {
+                    const uint32_t xr = a.lhs ? a.lhs[p] : (uint32_t)p, ex = a.rhs ? a.rhs[p] : (uint32_t)p;
+                    take = ex == e && xr < nx;
+                }
+                const uint64_t bal = __ballot(take);
+                if (take) plist[c + __popcll(bal & ((uint64_t(1) << lane) - 1))] = (uint16_t)p;
+                c += __popcll(bal);
+            }
+            if (lane == 0) pcount = c;
+        }
+        __syncthreads();
+        count = pcount;
+        if (count == 0) return;  // the whole block: no barrier follows
+        a.w += (int64_t)e * a.N * (a.K / 32 * BITS);
+        a.s += (int64_t)e * a.N * (a.K / 64);
+        a.b += (int64_t)e * a.N * (a.K / 64);
+    }
+    // Pass over activation rows [base, base + MW): x row and output row of
+    // row m of the pass.
+    // (One pass outside the gather, known at compile time.)
+    const int passes = GATHER ? (count + MW - 1) / MW : 1;
+    for (int pass = 0; pass < passes; ++pass) {
+    const int base = pass * MW;
+    const int mrows = GATHER ? (count - base < MW ? count - base : MW) : a.M;
+    auto x_row = [&](int m) -> int64_t {
+        if constexpr (GATHER) {
+            const uint32_t p = __builtin_amdgcn_readfirstlane(plist[base + m]);
+            return a.lhs ? (int64_t)a.lhs[p] : (int64_t)p;
+        } else {
+            return m;
+        }
+    };
+    auto y_row = [&](int m) -> int64_t {
+        if constexpr (GATHER)
+            return plist[base + m];
+        else
+            return m;
+    };
     float acc[kRpw][MW];
 #pragma unroll
     for (int r = 0; r < kRpw; ++r)
@@ -339,7 +402,7 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
     auto x_dma = [&](int c0) {
         for (int q = wave; q < MW * 8; q += kWaves) {
             const int m = q >> 3, j8 = q & 7;
-            const __amdgpu_buffer_rsrc_t xr = span(a.x + (int64_t)(m < a.M ? m : 0) * a.K, m < a.M ? (uint32_t)a.K * 2u : 0u);
+            const __amdgpu_buffer_rsrc_t xr = span(a.x + (m < mrows ? x_row(m) : 0) * a.K, m < mrows ? (uint32_t)a.K * 2u : 0u);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xr, (__attribute__((address_space(3))) void *)(xs + q * 64),
                 16, ((uint32_t)(c0 + lane) * 64u + 8u * (uint32_t)j8) * 2u, 0, 0, 0);
@@ -571,9 +634,10 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
             if (i >= V) continue;
             const int r = i / MW, m = i % MW;
             const int64_t row = row0 + r;
-            if (row < a.N && m < a.M) a.y[(int64_t)m * a.N + row] = f32_to_bf16(t[q]);
+            if (row < a.N && m < mrows) a.y[y_row(m) * a.N + row] = f32_to_bf16(t[q]);
         }
     }
+    }  // pass
 }
 
 // One thread per 32 codes (BITS words): w = fma(s, q, b) written as fp32 [N, K].
@@ -618,6 +682,25 @@ const void *stream_kernel(int bits, int M) {
         case 3: return stream_kernel_mw<3>(M);
         case 5: return stream_kernel_mw<5>(M);
         case 6: return stream_kernel_mw<6>(M);
+    }
+    return nullptr;
+}
+
+template <int BITS>
+static const void *stream_gather_mw(int mw) {
+    if (mw <= 1) return reinterpret_cast<const void *>(&qmv_stream_kernel<BITS, 1, true>);
+    if (mw <= 2) return reinterpret_cast<const void *>(&qmv_stream_kernel<BITS, 2, true>);
+    if (mw <= 4) return reinterpret_cast<const void *>(&qmv_stream_kernel<BITS, 4, true>);
+    return reinterpret_cast<const void *>(&qmv_stream_kernel<BITS, 8, true>);
+}
+
+const void *stream_gather_kernel(int bits, int mw) {
+    if (mw < 1 || mw > 8) return nullptr;
+    switch (bits) {
+        case 2: return stream_gather_mw<2>(mw);
+        case 3: return stream_gather_mw<3>(mw);
+        case 5: return stream_gather_mw<5>(mw);
+        case 6: return stream_gather_mw<6>(mw);
     }
     return nullptr;
 }

@@ -341,8 +341,8 @@ TITLES = {"llama": "Llama-3-8B-shaped decode GEMV set, batch 1, 4-bit gs64",
                    "bare products and the unfused sequence (4-bit gs64)",
           "nvfp4": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, and GEMMs at M = 16, 256, 2048, NVFP4 weights "
                    "(E2M1 codes, E4M3 scale per 16 columns), against the affine 4-bit gs64 products on the same shapes",
-          "bits": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, at 2, 3, 5 and 6 bits (the bit-stream widths, "
-                  "gs64) and 4 bits for reference"}
+          "bits": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, and the Mixtral-shaped decode gather W1, at 2, "
+                  "3, 5 and 6 bits (the bit-stream widths, gs64) and 4 bits for reference"}
 
 
 def write_profiles(workload, dirs):
@@ -801,6 +801,33 @@ def bits_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
             torch.cuda.empty_cache()
     emit({"set": "Llama-shaped decode products at each width (group size 64), us per set",
           **{f"bits{b}_m{M}_us": round(v, 3) for (b, M), v in sorted(tot.items())}})
+    # The Mixtral-shaped decode gather W1 (8 planes of 14336x4096, 16 tokens top-2: the
+    # routing of the gather workload) at each width; planes tiled from 4096 drawn rows.
+    m = si.MOE
+    E, N, K, T = m["experts"], m["ffn"], m["hidden"], m["tokens"]
+    rhs = si.moe_expert_ids(4, 1, T, E, m["top_k"]).reshape(-1).astype(np.uint32)
+    lhs = np.repeat(np.arange(T, dtype=np.uint32), m["top_k"])
+    P, used = len(rhs), len(set(rhs.tolist()))
+    x = bf16(si.draw_activations(4, 0, T, K))
+    ri, li = u32(rhs), u32(lhs)
+    for bits in (2, 3, 4, 5, 6):
+        base = si.draw_quantized_weight(14, 90 + bits, 4096, K, bits)
+        reps = -(-E * N // 4096)
+        planes = {k: np.tile(base[k], (reps, 1))[:E * N].reshape(E, N, -1) for k in ("w", "scales", "biases")}
+        cp = rotation(u32, bf16, planes, E * weight_bytes(N, K, bits))
+        ptrs = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr()) for c in cp]
+        rot = len(cp)
+        y = torch.empty(P, N, dtype=torch.bfloat16, device=dev)
+        agq.gather_qmv(x, *cp[0], rhs_indices=ri, lhs_indices=li, bits=bits, out=y)
+        us, us_min = time_shape(torch, lambda i: agq.lib.agq_gather_qmv(x.data_ptr(), *ptrs[i % rot], li.data_ptr(),
+                                                                        ri.data_ptr(), y.data_ptr(), P, T, E, N, K,
+                                                                        bits, 64, st),
+                                max(1, args.calls // 4), 5, stream)
+        nb = used * weight_bytes(N, K, bits) + 2 * T * K + 2 * P * N + 8 * P
+        emit(shape_line(f"{bits}-bit: gather w1 {E}x{N}x{K} P={P} ({used} planes used)", us, us_min, nb, None,
+                        calib.ceiling(nb) if calib else None))
+        del cp, planes, base
+        torch.cuda.empty_cache()
 
 
 def nvfp4_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):

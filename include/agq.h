@@ -133,8 +133,10 @@ agq_status agq_qmv_wide(const void *x, const uint32_t *w, const void *scales, co
  * rhs >= E gets an all-NaN output row, and no memory outside the arrays is
  * read. With 4-bit codes, group size 64 and K a multiple of 512 the gather
  * runs on the matrix cores, 16 pairs per pass, and K is limited only by R*K*2 < 2^31
- * bytes of x; otherwise K limits are those of agq_qmv_wide at M = 8. Takes
- * 4- or 8-bit codes (the bit-stream widths are AGQ_ENOTSUP), as agq_gather_qmm.
+ * bytes of x; otherwise K limits are those of agq_qmv_wide at M = 8. At the
+ * bit-stream widths (2, 3, 5, 6 bits; group size 64, else AGQ_ENOTSUP) each
+ * pair runs as its own one-row product on its plane: a plane shared by several
+ * pairs is read once per pair. agq_gather_qmm takes the same forms.
  */
 agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y,
@@ -248,8 +250,9 @@ agq_status agq_qmm_nvfp4(const void *x, const uint32_t *w, const void *scales, f
  * result as agq_gather_qmv, for any number of pairs per expert: each plane
  * that some pair uses streams once per 64 of its pairs, with every tile of x
  * rows gathered through the pair's lhs index. P may be at most 4096; R*K*2
- * must stay below 2^31; group size 64. Out-of-range indices give NaN rows, as
- * in agq_gather_qmv.
+ * must stay below 2^31 (4 and 8 bits); group size 64. Out-of-range indices
+ * give NaN rows, as in agq_gather_qmv. At the bit-stream widths (2, 3, 5, 6
+ * bits) each pair is one row product on its plane, as in agq_gather_qmv.
  */
 agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y,

@@ -115,8 +115,8 @@ def gqmm(P=4, R=4, E=4, N=16, K=64, bits=4, gs=64, lhs=A, rhs=A, x=A):
     (lambda: qmv(bits=1), ENOTSUP),
     (lambda: qmv(bits=3, gs=32, K=128), ENOTSUP),   # the bit-stream widths take group size 64
     (lambda: wide(M=9, bits=5), ENOTSUP),
-    (lambda: gather(bits=3), ENOTSUP),              # the gathers take 4- or 8-bit codes
-    (lambda: gqmm(bits=6), ENOTSUP),
+    (lambda: gather(bits=3, gs=32, K=128), ENOTSUP),  # the bit-stream gathers take group size 64
+    (lambda: gqmm(bits=6, gs=128, K=128), ENOTSUP),
     (lambda: qmm(bits=5, gs=128, K=128), ENOTSUP),
     (lambda: qmv(gs=16), ENOTSUP),
     (lambda: qmv(gs=256, K=256), ENOTSUP),

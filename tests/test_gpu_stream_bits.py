@@ -131,15 +131,13 @@ def test_stream_bits_qmm_passes_and_device_quantizer(bits):
 
 
 def test_stream_bits_refused_where_not_supported():
-    """The gathers and the fused projection take 4- or 8-bit codes; other group sizes
-    (32, 128) are refused for the bit-stream products; every refusal precedes any launch."""
+    """The fused projection takes 4- or 8-bit codes; other group sizes (32, 128) are
+    refused for the bit-stream products; every refusal precedes any launch."""
     N, K = 64, 256
     d = si.draw_quantized_weight(54, 0, N, K, 3)
     w, s, b = dev_weight(d)
     x = bf16_dev(si.draw_activations(54, 1, 2, K))
-    rhs, lhs = u32_dev(np.zeros(2, np.uint32)), u32_dev(np.arange(2, dtype=np.uint32))
-    for call in (lambda: agq.gather_qmv(x, w[None], s[None], b[None], rhs_indices=rhs, lhs_indices=lhs, bits=3),
-                 lambda: agq.qmv_fused(x[0], w, s, b, bits=3)):
+    for call in (lambda: agq.qmv_fused(x[0], w, s, b, bits=3),):
         with pytest.raises(agq.AgqError) as e:
             call()
         assert e.value.status == agq.AGQ_ENOTSUP
@@ -148,3 +146,76 @@ def test_stream_bits_refused_where_not_supported():
         agq.qmv(x[0], u32_dev(d32), bf16_dev(np.zeros((N, K // 32), np.uint16)),
                 bf16_dev(np.zeros((N, K // 32), np.uint16)), bits=3, group_size=32)
     assert e.value.status == agq.AGQ_ENOTSUP
+
+
+def stacked_planes(cfg, E, N, K, bits):
+    planes = [si.draw_quantized_weight(cfg, 10 * bits + e, N, K, bits) for e in range(E)]
+    return {k: np.stack([p[k] for p in planes]) for k in ("w", "scales", "biases")}
+
+
+def dev_planes(st):
+    return u32_dev(st["w"]), bf16_dev(st["scales"]), bf16_dev(st["biases"])
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_stream_bits_gather(bits):
+    """Expert gather at the bit-stream widths: pairs with repeated and unused experts,
+    planes of a ragged number of rows, two chunks of K (the second partial), and the NULL
+    index forms (identity lhs with R == P, identity rhs with E == P)."""
+    E, N, K, R = 6, 300, 4160, 5
+    st = stacked_planes(55, E, N, K, bits)
+    w, s, b = dev_planes(st)
+    x = si.draw_activations(55, bits, R, K)
+    rng = np.random.default_rng([55, bits])
+    rhs = np.array([3, 0, 3, 5, 3, 1, 0, 5, 3], np.uint32)
+    lhs = rng.integers(0, R, len(rhs)).astype(np.uint32)
+    progress(f"stream gather bits={bits} P={len(rhs)}")
+    y = agq.gather_qmv(bf16_dev(x), w, s, b, rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs), bits=bits)
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, bits)
+    check_close(y, y_ref, A, f"stream gather bits={bits}")
+    # Identity lhs (R == P) and identity rhs (E == P).
+    xp = si.draw_activations(55, 20 + bits, E, K)
+    progress(f"stream gather bits={bits} NULL indices")
+    y1 = agq.gather_qmv(bf16_dev(xp[:len(rhs[:E])]), w, s, b, rhs_indices=u32_dev(rhs[:E]), bits=bits)
+    y2 = agq.gather_qmv(bf16_dev(x), w, s, b, lhs_indices=u32_dev(lhs[:E]), bits=bits)
+    torch.cuda.synchronize()
+    r1, A1 = oracle.gather_qmv(xp, st["w"], st["scales"], st["biases"], None, rhs[:E], K, bits)
+    r2, A2 = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs[:E], None, K, bits)
+    check_close(y1, r1, A1, "identity lhs")
+    check_close(y2, r2, A2, "identity rhs")
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_stream_bits_gather_out_of_range_indices_give_nan_rows(bits):
+    E, N, K, R = 3, 130, 1024, 4
+    st = stacked_planes(56, E, N, K, bits)
+    w, s, b = dev_planes(st)
+    x = si.draw_activations(56, 99, R, K)
+    lhs = np.array([0, 9, 2, 3], np.uint32)     # 9 >= R
+    rhs = np.array([1, 0, 7, 2], np.uint32)     # 7 >= E
+    progress(f"stream gather invalid indices bits={bits}")
+    y = agq.gather_qmv(bf16_dev(x), w, s, b, rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs), bits=bits)
+    torch.cuda.synchronize()
+    yh = bf16_bits_host(y)
+    assert np.all(yh[1] == 0x7FC0) and np.all(yh[2] == 0x7FC0)
+    ok = np.array([0, 3])
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs[ok], rhs[ok], K, bits)
+    check_close(y[torch.as_tensor(ok, device=y.device)], y_ref, A, "valid pairs")
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+def test_stream_bits_gather_qmm(bits):
+    """gather_qmm at the bit-stream widths: many pairs per expert (a prefill gather)."""
+    E, N, K, R = 4, 200, 2048, 48
+    st = stacked_planes(57, E, N, K, bits)
+    w, s, b = dev_planes(st)
+    x = si.draw_activations(57, bits, R, K)
+    rng = np.random.default_rng([57, bits])
+    rhs = rng.integers(0, E - 1, 96).astype(np.uint32)   # plane E - 1 unused
+    lhs = rng.integers(0, R, 96).astype(np.uint32)
+    progress(f"stream gather_qmm bits={bits} P={len(rhs)}")
+    y = agq.gather_qmm(bf16_dev(x), w, s, b, rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs), bits=bits)
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, bits)
+    check_close(y, y_ref, A, f"stream gather_qmm bits={bits}")
