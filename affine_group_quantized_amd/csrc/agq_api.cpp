@@ -706,7 +706,21 @@ bool qmm_gemm_plan(int64_t M, int64_t N, int64_t K, int bits, int cus, bool spli
     return true;
 }
 
+// qmm at the bit-stream widths from this many rows, given a workspace: the
+// codes widened to the 8-bit layout in the workspace, then the 8-bit GEMM.
+// (Fewer rows: passes of 8 rows through the stream matvec, which read the
+// stream codes once per pass, cost less than writing and reading N*K bytes.)
+constexpr int64_t kStreamGemmMinRows = 64;
+
+int64_t stream_codes_bytes(int64_t N, int64_t K) { return (N * K + 255) / 256 * 256; }
+
 int64_t agq_qmm_workspace(int64_t M, int64_t N, int64_t K, int bits, int group_size) {
+    if (stream_bits(bits)) {
+        if (M < kStreamGemmMinRows || group_size != 64 || N <= 0 || K <= 0 || N > kMaxN || K > kMaxK ||
+            K % 64 != 0 || M * K * 2 >= (int64_t(1) << 31) || (int64_t)agq::kQmmHlTileN * K >= (int64_t(1) << 31))
+            return 0;
+        return stream_codes_bytes(N, K) + agq_qmm_workspace(M, N, K, 8, 64);
+    }
     if (M <= 8 || N <= 0 || K <= 0 || N > kMaxN || K > kMaxK || (bits != 4 && bits != 8) || group_size != 64)
         return 0;
     if (K % 64 != 0 || M * K * 2 >= (int64_t(1) << 31)) return 0;
@@ -729,7 +743,26 @@ agq_status agq_qmm(const void *x, const uint32_t *w, const void *scales, const v
     // 16 rows, unless (beyond kQmmHlSplitMinRows rows) the split-weight tiles
     // fill the device. Beyond: the tiled GEMM.
     if (M <= 8) return dense_product(x, w, scales, biases, y, M, N, K, bits, group_size, stream);
-    if (stream_bits(bits)) {  // passes of up to 8 rows through the bit-stream matvec
+    if (stream_bits(bits)) {
+        // With a workspace, from kStreamGemmMinRows rows: the codes widened to
+        // 8 bits in the workspace, then the 8-bit GEMM (the rest of the
+        // workspace serves its K split). Else passes of up to 8 rows through the
+        // bit-stream matvec.
+        const int64_t need = workspace ? agq_qmm_workspace(M, N, K, bits, group_size) : 0;
+        if (need > 0) {
+            st = check_workspace(workspace, workspace_bytes, need);
+            if (st != AGQ_OK) return st;
+            const uint32_t *src = w;
+            uint32_t *codes8 = static_cast<uint32_t *>(workspace);
+            int64_t units = N * K / 32;  // the kernel's three parameters, in order
+            void *targs[] = {&src, &codes8, &units};
+            const hipError_t e = hipLaunchKernel(agq::stream_to_u8_kernel(bits), dim3((unsigned)((units + 255) / 256)),
+                                                 dim3(256), targs, 0, static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) return fail(AGQ_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+            const int64_t cb = stream_codes_bytes(N, K);
+            return agq_qmm(x, codes8, scales, biases, y, M, N, K, 8, 64, static_cast<char *>(workspace) + cb,
+                           workspace_bytes - cb, stream);
+        }
         for (int64_t r0 = 0; r0 < M; r0 += 8) {
             st = dense_product(static_cast<const uint16_t *>(x) + r0 * K, w, scales, biases,
                                static_cast<uint16_t *>(y) + r0 * N, M - r0 < 8 ? M - r0 : 8, N, K, bits, group_size,

@@ -127,6 +127,9 @@ constexpr int kMaxGatherPairs = 4096;
 // The expert gather kernel for `bits` taking up to `mw` pairs of a plane per
 // pass (grid: row blocks x planes; NULL outside 2, 3, 5, 6 and 1..8).
 const void *stream_gather_kernel(int bits, int mw);
+// The codes widened to the 8-bit layout, one thread per 32 codes (grid: units / 256
+// blocks of 256 threads, units = rows * K / 32).
+const void *stream_to_u8_kernel(int bits);
 // Dequantize kernel of the bit-stream widths: one thread per 32 codes (`bits` words).
 const void *stream_dequant_kernel(int bits);
 

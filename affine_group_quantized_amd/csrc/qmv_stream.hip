@@ -667,6 +667,28 @@ __global__ __launch_bounds__(256) void dequant_stream_kernel(const uint32_t *__r
     }
 }
 
+// Widening to 8-bit codes, one thread per 32 codes: `bits` stream words in,
+// eight words out holding the same codes one per byte, low first (the 8-bit
+// layout). Rows are whole multiples of 32 codes, so unit i is words
+// [bits*i, bits*i + bits) in and [8i, 8i + 8) out across all rows alike.
+template <int BITS>
+__global__ __launch_bounds__(256) void stream_to_u8_kernel(const uint32_t *__restrict__ w, uint32_t *__restrict__ out,
+                                                          int64_t units) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= units) return;
+    uint32_t wd[BITS];
+#pragma unroll
+    for (int j = 0; j < BITS; ++j) wd[j] = w[i * BITS + j];
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        o[j] = stream_code<BITS>(wd, 4 * j) | stream_code<BITS>(wd, 4 * j + 1) << 8 |
+               stream_code<BITS>(wd, 4 * j + 2) << 16 | stream_code<BITS>(wd, 4 * j + 3) << 24;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(out + i * 8);
+    dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+    dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 template <int BITS>
 static const void *stream_kernel_mw(int M) {
     if (M <= 1) return reinterpret_cast<const void *>(&qmv_stream_kernel<BITS, 1>);
@@ -701,6 +723,16 @@ const void *stream_gather_kernel(int bits, int mw) {
         case 3: return stream_gather_mw<3>(mw);
         case 5: return stream_gather_mw<5>(mw);
         case 6: return stream_gather_mw<6>(mw);
+    }
+    return nullptr;
+}
+
+const void *stream_to_u8_kernel(int bits) {
+    switch (bits) {
+        case 2: return reinterpret_cast<const void *>(&stream_to_u8_kernel<2>);
+        case 3: return reinterpret_cast<const void *>(&stream_to_u8_kernel<3>);
+        case 5: return reinterpret_cast<const void *>(&stream_to_u8_kernel<5>);
+        case 6: return reinterpret_cast<const void *>(&stream_to_u8_kernel<6>);
     }
     return nullptr;
 }

@@ -341,8 +341,9 @@ TITLES = {"llama": "Llama-3-8B-shaped decode GEMV set, batch 1, 4-bit gs64",
                    "bare products and the unfused sequence (4-bit gs64)",
           "nvfp4": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, and GEMMs at M = 16, 256, 2048, NVFP4 weights "
                    "(E2M1 codes, E4M3 scale per 16 columns), against the affine 4-bit gs64 products on the same shapes",
-          "bits": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, and the Mixtral-shaped decode gather W1, at 2, "
-                  "3, 5 and 6 bits (the bit-stream widths, gs64) and 4 bits for reference"}
+          "bits": "Llama-3-8B-shaped decode GEMV set, batch 1 and 4, the Mixtral-shaped decode gather W1 and qmm "
+                  "(prefill) on 4096x4096, at 2, 3, 5 and 6 bits (the bit-stream widths, gs64) and 4 bits for "
+                  "reference"}
 
 
 def write_profiles(workload, dirs):
@@ -770,6 +771,7 @@ def bits_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
     """Workload 1's five products with 2-, 3-, 5- and 6-bit codes (group size 64, the
     bit-stream widths) and, for reference, 4-bit codes, at M = 1 and 4 (agq_qmv_wide): us/call,
     GB/s of algorithmic bytes and % of the read ceiling per shape, and the set's sum per width.
+    Then the Mixtral-shaped decode gather W1 and qmm on 4096x4096 at M = 64 .. 2048 per width.
     The weights are draw_quantized_weight rows (stream cfg 14) drawn for at most 4096 rows and
     repeated down to N: the kernels do the same work for every code value (nothing branches
     on a value), and drawing all 128256 lm_head rows per width would cost the host minutes."""
@@ -827,6 +829,31 @@ def bits_workload(args, torch, si, agq, bf16, u32, stream, calib, emit):
         emit(shape_line(f"{bits}-bit: gather w1 {E}x{N}x{K} P={P} ({used} planes used)", us, us_min, nb, None,
                         calib.ceiling(nb) if calib else None))
         del cp, planes, base
+        torch.cuda.empty_cache()
+    # qmm (prefill) on o 4096x4096 at each width: from 64 rows the stream widths widen their
+    # codes to 8 bits in the workspace and run the 8-bit GEMM; at 64 rows also the passes of
+    # 8 rows without a workspace. Bytes as the qmm workload (codes, scales, biases, x, y).
+    N, K = 4096, 4096
+    for bits in (2, 3, 4, 5, 6):
+        m = si.draw_quantized_weight(14, 80 + bits, N, K, bits)
+        cp = rotation(u32, bf16, m, weight_bytes(N, K, bits))
+        rot = len(cp)
+        ptrs = [(c[0].data_ptr(), c[1].data_ptr(), c[2].data_ptr()) for c in cp]
+        for M, use_ws in ((64, False), (64, True), (256, True), (2048, True)):
+            x = bf16(si.draw_activations(6, M, M, K))
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            wsb = agq.lib.agq_qmm_workspace(M, N, K, bits, 64) if use_ws else 0
+            ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+            wsp = ws.data_ptr() if wsb > 0 else None
+            agq.qmm(x, *cp[0], bits=bits, out=y, workspace=ws if wsb > 0 else False)
+            calls = max(4, min(args.calls, int(2e6 / (2 * M * N * K / 1e9 + 1))))
+            us, us_min = time_shape(torch, lambda i: agq.lib.agq_qmm(x.data_ptr(), *ptrs[i % rot], y.data_ptr(), M,
+                                                                     N, K, bits, 64, wsp, wsb, st), calls, 5, stream)
+            route = "" if bits == 4 else (" (widened to 8 bits)" if wsb > 0 else " (passes of 8 rows)")
+            emit(qmm_line(f"{bits}-bit: qmm o {N}x{K} M={M}{route}", us, us_min, 2 * M * N * K,
+                          weight_bytes(N, K, bits) + 2 * M * K + 2 * M * N))
+            del x, y, ws
+        del cp, m
         torch.cuda.empty_cache()
 
 

@@ -134,9 +134,10 @@ agq_status agq_qmv_wide(const void *x, const uint32_t *w, const void *scales, co
  * read. With 4-bit codes, group size 64 and K a multiple of 512 the gather
  * runs on the matrix cores, 16 pairs per pass, and K is limited only by R*K*2 < 2^31
  * bytes of x; otherwise K limits are those of agq_qmv_wide at M = 8. At the
- * bit-stream widths (2, 3, 5, 6 bits; group size 64, else AGQ_ENOTSUP) each
- * pair runs as its own one-row product on its plane: a plane shared by several
- * pairs is read once per pair. agq_gather_qmm takes the same forms.
+ * bit-stream widths (2, 3, 5, 6 bits; group size 64, else AGQ_ENOTSUP) the
+ * pairs of each used plane run as the activation rows of the bit-stream
+ * matvec, up to 1, 2, 4 or 8 per pass (from the mean pairs per plane, P/E),
+ * so a plane streams once per pass. agq_gather_qmm takes the same forms.
  */
 agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y,
@@ -155,10 +156,13 @@ agq_status agq_gather_qmv(const void *x, const uint32_t *w, const void *scales, 
  * group's scale and bias in fp32, so its error bound is that of the matvec
  * forms. M*K*2 must stay below 2^31 (else AGQ_ENOTSUP). Beyond 8 rows it
  * takes group size 64 (else AGQ_ENOTSUP). The bit-stream widths (2, 3, 5, 6
- * bits) run as passes of up to 8 rows of agq_qmv_wide's kernel. Argument
- * checks and errors as for agq_qmv.
+ * bits) run as passes of up to 8 rows of agq_qmv_wide's kernel; from 64 rows,
+ * given a workspace, the codes are first widened to the 8-bit layout in the
+ * workspace (N*K bytes, every code value kept) and the 8-bit GEMM runs on them
+ * with the same scales and biases. Argument checks and errors as for agq_qmv.
  *
- * workspace (optional, owned by the caller): device scratch for a K split.
+ * workspace (optional, owned by the caller): device scratch for a K split,
+ * and at the bit-stream widths for the widened codes.
  * Where the output tiles alone leave compute units idle (a few hundred rows
  * against a few thousand weight rows), the tiles split K and write fp32
  * partial sums to the workspace, and a second launch on `stream` adds the
@@ -252,7 +256,7 @@ agq_status agq_qmm_nvfp4(const void *x, const uint32_t *w, const void *scales, f
  * rows gathered through the pair's lhs index. P may be at most 4096; R*K*2
  * must stay below 2^31 (4 and 8 bits); group size 64. Out-of-range indices
  * give NaN rows, as in agq_gather_qmv. At the bit-stream widths (2, 3, 5, 6
- * bits) each pair is one row product on its plane, as in agq_gather_qmv.
+ * bits) the pairs run through the bit-stream matvec as in agq_gather_qmv.
  */
 agq_status agq_gather_qmm(const void *x, const uint32_t *w, const void *scales, const void *biases,
                           const uint32_t *lhs_indices, const uint32_t *rhs_indices, void *y,

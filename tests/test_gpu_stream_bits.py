@@ -50,10 +50,11 @@ def test_stream_bits_products(bits, M, N, K):
 
 
 @pytest.mark.parametrize("bits", BITS)
-def test_stream_bits_one_hot_columns_are_bitwise_weights(bits):
+@pytest.mark.parametrize("route", ["passes", "widened"])
+def test_stream_bits_one_hot_columns_are_bitwise_weights(bits, route):
     """x = e_k for every column of 5 groups (all 64 positions of a code in its group, so
     every straddling position): y[n] = bf16(w_hat[n, k]) bit for bit, through qmm's passes
-    of 8 rows."""
+    of 8 rows (no workspace) and through the codes widened to 8 bits and the 8-bit GEMM."""
     N, K = 300, 320
     d = si.draw_quantized_weight(51, bits, N, K, bits)
     w, s, b = dev_weight(d)
@@ -62,8 +63,8 @@ def test_stream_bits_one_hot_columns_are_bitwise_weights(bits):
     want = si.bf16_bits(ref.astype(np.float32))
     x = np.zeros((K, K), np.uint16)
     x[np.arange(K), np.arange(K)] = 0x3F80
-    progress(f"stream bits one-hot bits={bits}")
-    got = bf16_bits_host(agq.qmm(bf16_dev(x), w, s, b, bits=bits))
+    progress(f"stream bits one-hot bits={bits} route={route}")
+    got = bf16_bits_host(agq.qmm(bf16_dev(x), w, s, b, bits=bits, workspace=False if route == "passes" else None))
     assert np.array_equal(got, want.T)
 
 
@@ -219,3 +220,27 @@ def test_stream_bits_gather_qmm(bits):
     torch.cuda.synchronize()
     y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, bits)
     check_close(y, y_ref, A, f"stream gather_qmm bits={bits}")
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("M", [64, 300])
+def test_stream_bits_qmm_widened_to_8_bits(bits, M):
+    """From 64 rows with a workspace, qmm widens the codes to the 8-bit layout and runs
+    the 8-bit GEMM: every row meets the oracle bound, the workspace query covers the
+    widened codes (N*K bytes), and a smaller workspace is refused before any launch."""
+    N, K = 200, 1024
+    d = si.draw_quantized_weight(58, bits, N, K, bits)
+    w, s, b = dev_weight(d)
+    x = si.draw_activations(58, M, M, K)
+    need = agq.lib.agq_qmm_workspace(M, N, K, bits, 64)
+    assert need >= N * K
+    assert agq.lib.agq_qmm_workspace(63, N, K, bits, 64) == 0   # passes below 64 rows
+    progress(f"stream qmm widened bits={bits} M={M}")
+    y = agq.qmm(bf16_dev(x), w, s, b, bits=bits)
+    torch.cuda.synchronize()
+    y_ref, A = oracle.qmv(x, d["w"], d["scales"], d["biases"], K, bits)
+    check_close(y, y_ref, A, f"widened qmm bits={bits} M={M}")
+    small = torch.empty(N * K - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(agq.AgqError) as e:
+        agq.qmm(bf16_dev(x), w, s, b, bits=bits, workspace=small)
+    assert e.value.status == agq.AGQ_EINVAL
