@@ -121,7 +121,8 @@ struct StreamArgs {
     int32_t E;
 };
 constexpr int kStreamRowsPerBlock = 16;  // 4 waves of 4 weight rows
-// The matvec kernel for `bits` and M activation rows (NULL outside 2, 3, 5, 6 and 1..8).
+// The matvec kernel for `bits` and M activation rows (NULL outside 2, 3, 5, 6 and
+// 1..8, and 4 bits at M = 1).
 const void *stream_kernel(int bits, int M);
 constexpr int kMaxGatherPairs = 4096;
 // The expert gather kernel for `bits` taking up to `mw` pairs of a plane per

@@ -1,5 +1,5 @@
 // Affine group-quantized products for the bit-stream widths: 2-, 3-, 5- and
-// 6-bit codes with group size 64, the other widths of the affine family that
+// 6-bit codes with group size 64 (and the large batch-1 4-bit products), the other widths of the affine family that
 // "MLX CUDA Cleanup Plan" (Target Architecture §1; Refactor Plan, Phase 3)
 // names at 4 and 8 bits. A row's codes form one low-first bit stream over its
 // uint32 words: code k occupies stream bits bits*k .. bits*k + bits - 1, word
@@ -98,7 +98,7 @@ __device__ __forceinline__ uint32_t code_pair_bf16(const uint32_t (&w)[NW], int 
 // code whose stream bits fall inside mantissa bits 0..6 of either half of a
 // 32-bit window of the stream becomes a bf16 lane with one v_and_or_b32:
 // (window & mask) | magic, the magic holding each half's exponent. Codes k and
-// k + d with d = 8, 5, 3 (2, 3, 5 bits) lie 16, 15 and 15 stream bits apart,
+// k + d with d = 8, 4, 5, 3 (2, 4, 3, 5 bits) lie 16, 16, 15 and 15 stream bits apart,
 // so both fit one window, one in each half, and at 2 and 3 bits successive
 // pairs share windows. The group's 64 codes become 32 such pairs; at 3 and 5
 // bits the last four codes (which have no partner d further on) are taken as
@@ -135,7 +135,7 @@ struct WinPlan {
 template <int BITS>
 constexpr WinPlan<BITS> make_win_plan() {
     WinPlan<BITS> pl{};
-    constexpr int d = BITS == 2 ? 8 : BITS == 3 ? 5 : BITS == 5 ? 3 : 0;  // 0: adjacent pairs only
+    constexpr int d = BITS == 2 ? 8 : BITS == 3 ? 5 : BITS == 4 ? 4 : BITS == 5 ? 3 : 0;  // 0: adjacent pairs only
     constexpr int room = 7 - BITS;  // largest code offset inside a mantissa
     constexpr uint32_t cm = (1u << BITS) - 1u;
     int n = 0, b0 = 0;
@@ -217,7 +217,8 @@ constexpr bool win_plan_ok() {
         if ((pl.magics[j] & 0x807Fu) != 0 || (pl.even[j] && pl.c[j] * 2.f > 256.f)) return false;
     return true;
 }
-static_assert(win_plan_ok<2>() && win_plan_ok<3>() && win_plan_ok<5>() && win_plan_ok<6>(), "window plans");
+static_assert(win_plan_ok<2>() && win_plan_ok<3>() && win_plan_ok<4>() && win_plan_ok<5>() && win_plan_ok<6>(),
+              "window plans");
 
 template <int BITS>
 constexpr WinPlan<BITS> kWinPlan = make_win_plan<BITS>();
@@ -699,6 +700,7 @@ static const void *stream_kernel_mw(int M) {
 
 const void *stream_kernel(int bits, int M) {
     if (M < 1 || M > 8) return nullptr;
+    if (bits == 4) return M == 1 ? reinterpret_cast<const void *>(&qmv_stream_kernel<4, 1>) : nullptr;
     switch (bits) {
         case 2: return stream_kernel_mw<2>(M);
         case 3: return stream_kernel_mw<3>(M);

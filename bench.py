@@ -26,10 +26,11 @@ the read ceiling: the fastest plain streaming read of the same byte count
 (libagq_calib.so: non-temporal 16-byte loads, several wave counts, loads in
 flight and piece layouts), timed the same way.
 
-roofline: the kernel instantiation with the most time per step (with the
-launch planner's choices, the one that runs lm_head and nothing else); achieved
-GB/s is its algorithmic bytes per launch over its average duration in its
-back-to-back loop, against the 8 TB/s HBM3E peak. traffic is the HBM bytes per
+roofline: the kernel launch with the most time per step (with the launch
+planner's choices, the bit-stream kernel on lm_head's grid: its instantiation
+also runs gate_up, on a grid of its own); achieved GB/s is its algorithmic
+bytes per launch over its average duration in its back-to-back loop, against
+the 8 TB/s HBM3E peak. traffic is the HBM bytes per
 launch from the committed rocprofv3 counter summary, or null when the kernel
 sources changed since it was taken.
 
@@ -268,7 +269,8 @@ def kernel_label(name):
 
 KERNEL_SOURCES = ["affine_group_quantized_amd/csrc/qmv_kernels.hip", "affine_group_quantized_amd/csrc/qmv_core.hpp",
                   "affine_group_quantized_amd/csrc/qmv_device.hpp", "affine_group_quantized_amd/csrc/qmv_kernels.hpp",
-                  "affine_group_quantized_amd/csrc/plan.hpp", "affine_group_quantized_amd/csrc/agq_api.cpp"]
+                  "affine_group_quantized_amd/csrc/plan.hpp", "affine_group_quantized_amd/csrc/agq_api.cpp",
+                  "affine_group_quantized_amd/csrc/qmv_stream.hip"]
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "qmv_llama_decode_set_hbm_traffic.md")
 
 
@@ -974,8 +976,10 @@ def main():
 
     # Kernel instantiation of each product, as the launch planner picks it on this device.
     plans = {n: agq.launch_plan(1, mats[n]["N"], mats[n]["K"], 4) for n in SHAPES}
-    kern = lambda p: (p["cpt"], p["mw"], p["rows_per_iter"], p["stages"],  # noqa: E731
-                      p["waves_per_group"] if p["x_lds_bytes"] else 0)
+    # (The bit-stream kernel, engine 2, is one instantiation for every shape it runs; its
+    # grid tells the shapes apart, as the counter summary's per-launch rows do.)
+    kern = lambda p: (("stream", p["blocks"]) if p["engine"] == 2 else  # noqa: E731
+                      (p["cpt"], p["mw"], p["rows_per_iter"], p["stages"], p["waves_per_group"] if p["x_lds_bytes"] else 0))
     by_kernel = {}
     for n in SHAPES:
         by_kernel.setdefault(kern(plans[n]), []).append(n)
@@ -983,7 +987,8 @@ def main():
     dom = by_kernel[dom_key]
     # Template arguments: bits, chunks per lane, activation rows, rows per iteration, ring
     # stages, K segments of the block's LDS copy of x (0: none).
-    dom_name = "qmv_kernel<4, %d, %d, %d, %d, %d>" % dom_key
+    dom_name = ("qmv_stream_kernel<4, 1, false>" if dom_key[0] == "stream" else
+                "qmv_kernel<4, %d, %d, %d, %d, %d>" % dom_key)
 
     stream = torch.cuda.Stream(dev)
     calls = {name: [agq.prepare_qmv(mats[name]["x"], *c, mats[name]["y"], bits=4, stream=stream)

@@ -97,7 +97,9 @@ const char *agq_last_error(void);
  * K must be a positive multiple of group_size, and N positive (else
  * AGQ_EINVAL). K above 114688 (4-bit) or 57344 (8-bit) is AGQ_ENOTSUP; the
  * bit-stream widths walk K in chunks of 4096 columns and take any K with
- * M*K*2 < 2^31 bytes of x.
+ * M*K*2 < 2^31 bytes of x. 4-bit products with group size 64 whose N gives
+ * at least two 16-row blocks per compute unit run on the bit-stream kernel
+ * (the plan's engine 2), under the same 4-bit K limit.
  */
 agq_status agq_qmv(const void *x, const uint32_t *w, const void *scales, const void *biases,
                    void *y, int64_t N, int64_t K, int bits, int group_size, void *stream);
@@ -390,7 +392,12 @@ typedef struct agq_plan {
                                 gather): bands of rows_per_iter = 16*tiles rows, waves_per_group waves
                                 splitting K per block, one band group per block (groups_per_block 1,
                                 blocks = row_groups), mw = 16 rows per pass, cpt = 0, stages = 128-column
-                                segments in flight per wave */
+                                segments in flight per wave;
+                                2: the bit-stream kernel (4-bit, group size 64, M = 1, at least two
+                                16-row blocks per compute unit): blocks of 4 waves (groups_per_block 4,
+                                threads_per_block 256), each wave 4 consecutive rows (rows_per_iter =
+                                rows_per_group = 4, row_order 1), its rows staged through LDS two at a
+                                time (stages 2), x in LDS per 4096-column chunk (x_lds_bytes), cpt = 0 */
 } agq_plan;
 
 agq_status agq_plan_product(int64_t M, int64_t N, int64_t K, int bits, int group_size,

@@ -50,12 +50,21 @@ def test_moe_workspace_size():
 def test_gemm_workspace_sizes_of_calls_that_need_none():
     """Calls that are not K-split GEMMs need no workspace (answered on the host)."""
     assert lib.agq_qmm_workspace(0, 4096, 4096, 4, 64) == 0
-    assert lib.agq_qmm_workspace(256, 4096, 4096, 3, 64) == 0
+    assert lib.agq_qmm_workspace(63, 4096, 4096, 3, 64) == 0    # bit-stream widths: passes below 64 rows
+    assert lib.agq_qmm_workspace(256, 4096, 4096, 3, 128) == 0
     assert lib.agq_qmm_workspace(256, 4096, 4096, 4, 32) == 0
     assert lib.agq_qmm_workspace(8, 4096, 4096, 4, 64) == 0
     assert lib.agq_qmm_workspace(64, 4096, 4096, 4, 64) == 0    # matrix-core matvec passes
     assert lib.agq_qmm_nvfp4_workspace(4, 4096, 4096) == 0
     assert lib.agq_qmm_nvfp4_workspace(64, 4096, 48) == 0
+
+
+def test_gemm_workspace_of_the_widened_bit_stream_codes():
+    """From 64 rows the bit-stream widths widen their codes to 8 bits in the workspace:
+    at least N*K bytes (plus the 8-bit GEMM's split partials where a device is present)."""
+    for bits in (2, 3, 5, 6):
+        assert lib.agq_qmm_workspace(64, 4096, 4096, bits, 64) >= 4096 * 4096
+        assert lib.agq_qmm_workspace(2048, 100, 1024, bits, 64) >= 100 * 1024
 
 
 def test_status_strings():
@@ -269,7 +278,15 @@ def test_plan_covers_the_problem(M, N, K, bits, experts, cus, wpc):
         rows = visited_rows(p, N)
         assert rows.size == N and np.array_equal(np.sort(rows), np.arange(N))   # each row exactly once
     mfma = bits == 4 and K % 512 == 0 and (M >= 4 or experts > 0)
-    assert p["engine"] == (1 if mfma else 0)
+    stream = bits == 4 and M == 1 and not experts and -(-N // 16) >= 2 * cus
+    assert p["engine"] == (2 if stream else 1 if mfma else 0)
+    if stream:
+        # The bit-stream kernel: blocks of 4 waves, each 4 consecutive rows staged two at a
+        # time, x per 4096-column chunk in LDS.
+        assert (R, RPG, p["groups_per_block"], p["threads_per_block"], p["row_order"]) == (4, 4, 4, 256, 1)
+        assert p["blocks"] == -(-N // 16) and p["mw"] == 1 and p["cpt"] == 0 and p["stages"] == 2
+        assert p["x_lds_bytes"] == 8192 and p["resident_waves"] == cus * wpc
+        return
     if mfma:
         # Matrix cores: bands of 16 or 32 rows, up to 4 waves (2 for the gather) splitting
         # K into equal slices of whole 4-segment (512-column) blocks, one band group per block.

@@ -80,6 +80,39 @@ def test_products_at_other_group_sizes(bits, gs, M, N, K):
     assert np.array_equal(deq.cpu().numpy(), ref.astype(np.float32))
 
 
+def test_large_batch1_4bit_products_take_the_stream_kernel():
+    """Batch-1 4-bit gs64 products whose 16-row blocks number at least two per compute
+    unit run on the bit-stream kernel (engine 2); short grids stay on the VALU plans."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for N, K in ((128256, 4096), (28672, 4096), (6144, 4096), (4096, 4096), (4096, 14336)):
+        want = 2 if -(-N // 16) >= 2 * cus else 0
+        assert agq.launch_plan(1, N, K, 4)["engine"] == want, (N, K)
+    assert agq.launch_plan(2, 128256, 4096, 4)["engine"] == 0        # one activation row only
+    assert agq.launch_plan(1, 128256, 4096, 4, group_size=128)["engine"] == 0
+
+
+@pytest.mark.parametrize("gs", [32, 128])
+def test_deep_plan_at_other_group_sizes(gs):
+    """Batch-1 4-bit products over 128256 rows at group sizes 32 and 128 take the VALU deep
+    plan (two rows per iteration, x from L2); sampled rows, the last 40 among them, meet the
+    oracle bound. (4096 drawn rows tiled down the matrix: every row's address is walked.)"""
+    N, K, base = 128256, 4096, 4096
+    w = (0.02 * np.random.default_rng([82, gs]).standard_normal((base, K))).astype(np.float32)
+    q, sc, bi = si.quantize_rows(w, 4, group_size=gs)
+    reps = -(-N // base)
+    wq = np.tile(si.pack_codes(q, 4), (reps, 1))[:N]
+    sc, bi = np.tile(sc, (reps, 1))[:N], np.tile(bi, (reps, 1))[:N]
+    x = si.draw_activations(82, gs, 1, K)
+    plan = agq.launch_plan(1, N, K, 4, group_size=gs)
+    assert plan["engine"] == 0 and plan["rows_per_iter"] == 2 and plan["x_lds_bytes"] == 0
+    progress(f"deep plan gs={gs}")
+    y = agq.qmv(bf16_dev(x)[0], u32_dev(wq), bf16_dev(sc), bf16_dev(bi), bits=4, group_size=gs)[None]
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, N, 997), np.arange(N - 40, N)]))
+    y_ref, A = oracle.qmv(x, wq, sc, bi, K, 4, group_size=gs, rows=rows)
+    check_close(y[:, torch.as_tensor(rows, device=y.device)], y_ref, A, f"deep plan gs={gs}")
+
+
 @pytest.mark.parametrize("gs", [32, 128])
 def test_one_hot_and_gather_at_other_group_sizes(gs):
     bits, N, K, E = 4, 300, 1024, 3

@@ -322,13 +322,14 @@ def test_one_hot_columns_bitwise_on_the_vector_path(bits, M, N, K):
 
 
 def test_one_hot_columns_bitwise_on_lm_head(wl):
-    """The deep-plan instantiation that runs lm_head (128256x4096, 4-bit) and nothing else
-    in the benchmark, one-hot bitwise on the real weights."""
+    """The launch that runs lm_head (128256x4096, 4-bit) in the benchmark, the bit-stream
+    kernel (engine 2), one-hot bitwise on the real weights: every column of the first group
+    (each position of the 4-bit pair plan) and the chunk and row ends."""
     m = wl(1)["lm_head"]
     plan = agq.launch_plan(1, m["N"], m["K"], 4)
-    assert plan["engine"] == 0 and plan["rows_per_iter"] == 2
+    assert plan["engine"] == 2
     cols = list(range(64)) + [2047, 2048, 4031, 4032, 4095]
-    one_hot_sweep(*dev_weight(m), m, m["K"], 4, 1, cols, "one-hot lm_head (deep plan)")
+    one_hot_sweep(*dev_weight(m), m, m["K"], 4, 1, cols, "one-hot lm_head (bit-stream kernel)")
 
 
 @pytest.mark.parametrize("bits", [4, 8])
