@@ -371,7 +371,7 @@ def write_profiles(workload, dirs):
              "ring stages, LDS-copy segments, epilogue (0 residual, 1 SwiGLU, 2 GeGLU, 3 none), norm>` (VALU); "
              "`qmv_mfma_kernel<tiles per band, activation load form (4: compact, 2: staged, 1: four loads)>` and "
              "`gather_mfma_kernel<tiles>` (matrix cores); `qmm_kernel` / `gather_qmm_kernel<bits, tile rows / 32, "
-             "tile columns / 32, ...>` and the MoE kernels (matrix cores).", "",
+             "tile columns / 32, ...>` and the MoE kernels (matrix cores); and `qmv_stream_kernel<bits, activation rows, expert gather>` (the bit-stream kernel: 2-6 bits, and large batch-1 4-bit products).", "",
              "| kernel | calls | average us | min us | max us | share of time |", "|---|---|---|---|---|---|"]
     for r in stats:
         if "agq::" in r["Name"]:
