@@ -91,6 +91,31 @@ def test_large_batch1_4bit_products_take_the_stream_kernel():
     assert agq.launch_plan(1, 128256, 4096, 4, group_size=128)["engine"] == 0
 
 
+def test_stream_route_ragged_rows_and_chunk():
+    """The batch-1 4-bit route to the bit-stream kernel on a ragged shape: N not a multiple
+    of 16 rows (a last block with 3 rows, waves without rows) and K with a partial last
+    4096-column chunk; every row against the oracle, and one-hot columns bit for bit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K = 2 * cus * 16 + 3, 4096 + 64 * 3
+    assert agq.launch_plan(1, N, K, 4)["engine"] == 2
+    d = si.draw_quantized_weight(83, 0, N, K, 4)
+    x = si.draw_activations(83, 1, 1, K)
+    w, s, b = u32_dev(d["w"]), bf16_dev(d["scales"]), bf16_dev(d["biases"])
+    progress(f"stream route ragged N={N} K={K}")
+    y = agq.qmv(bf16_dev(x)[0], w, s, b, bits=4)[None]
+    torch.cuda.synchronize()
+    y_ref, A = oracle.qmv(x, d["w"], d["scales"], d["biases"], K, 4)
+    check_close(y, y_ref, A, "stream route ragged")
+    ref, bad = oracle.dequantize(d["w"], d["scales"], d["biases"], K, 4)
+    assert bad == 0
+    want = si.bf16_bits(ref.astype(np.float32))
+    for c in (0, 1, 7, 8, 63, 4095, 4096, 4097, K - 1):
+        e = np.zeros((1, K), np.uint16)
+        e[0, c] = 0x3F80
+        got = bf16_bits_host(agq.qmv(bf16_dev(e)[0], w, s, b, bits=4))
+        assert np.array_equal(got, want[:, c]), c
+
+
 @pytest.mark.parametrize("gs", [32, 128])
 def test_deep_plan_at_other_group_sizes(gs):
     """Batch-1 4-bit products over 128256 rows at group sizes 32 and 128 take the VALU deep

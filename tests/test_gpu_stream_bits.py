@@ -244,3 +244,20 @@ def test_stream_bits_qmm_widened_to_8_bits(bits, M):
     with pytest.raises(agq.AgqError) as e:
         agq.qmm(bf16_dev(x), w, s, b, bits=bits, workspace=small)
     assert e.value.status == agq.AGQ_EINVAL
+
+
+def test_stream_bits_gather_at_the_pair_limit():
+    """4096 pairs (the pair list's capacity) over two small planes: passes of 8 pairs, about
+    256 per plane, every pair's row against the oracle."""
+    E, N, K, R, bits = 2, 24, 128, 64, 3
+    st = stacked_planes(59, E, N, K, bits)
+    w, s, b = dev_planes(st)
+    x = si.draw_activations(59, 0, R, K)
+    rng = np.random.default_rng(59)
+    rhs = rng.integers(0, E, 4096).astype(np.uint32)
+    lhs = rng.integers(0, R, 4096).astype(np.uint32)
+    progress("stream gather at the pair limit")
+    y = agq.gather_qmv(bf16_dev(x), w, s, b, rhs_indices=u32_dev(rhs), lhs_indices=u32_dev(lhs), bits=bits)
+    torch.cuda.synchronize()
+    y_ref, A = oracle.gather_qmv(x, st["w"], st["scales"], st["biases"], lhs, rhs, K, bits)
+    check_close(y, y_ref, A, "stream gather, 4096 pairs", extra_half_ulp=True)
