@@ -382,9 +382,18 @@ agq_status dense_product(const void *x, const uint32_t *w, const void *s, const 
             return fail(AGQ_ENOTSUP, "N=%lld too large", (long long)N);
         agq::StreamArgs a{static_cast<const uint16_t *>(x), w, static_cast<const uint16_t *>(s),
                           static_cast<const uint16_t *>(b), static_cast<uint16_t *>(y), N, (int32_t)K, (int32_t)M};
-        return launch(agq::stream_kernel(bits, (int)M),
-                      dim3((unsigned)((N + agq::kStreamRowsPerBlock - 1) / agq::kStreamRowsPerBlock)), dim3(256), 0, &a,
-                      stream);
+        const int64_t blocks = (N + agq::kStreamRowsPerBlock - 1) / agq::kStreamRowsPerBlock;
+        if (M <= 2 && K / 64 >= 128 && stream_bits(bits)) {
+            // Short grids over several chunks of K: the K-split form, 8 rows per
+            // block, two waves per row set alternating chunks.
+            int cus = 0, dev = 0;
+            st = current_device(&cus, &dev);
+            if (st != AGQ_OK) return st;
+            if (blocks < 2 * (int64_t)cus)
+                return launch(agq::stream_split_kernel(bits, (int)M), dim3((unsigned)((N + 7) / 8)), dim3(256), 0, &a,
+                              stream);
+        }
+        return launch(agq::stream_kernel(bits, (int)M), dim3((unsigned)blocks), dim3(256), 0, &a, stream);
     }
     if (group_size == 64 && agq::mfma_eligible(M, K, bits, 0, M)) {
         agq::MfmaPlan mp;

@@ -125,6 +125,9 @@ constexpr int kStreamRowsPerBlock = 16;  // 4 waves of 4 weight rows
 // 1..8, and 4 bits at M = 1).
 const void *stream_kernel(int bits, int M);
 constexpr int kMaxGatherPairs = 4096;
+// The K-split form (8 rows per block, two waves per row set alternating
+// chunks of K) for `bits` (2, 3, 5, 6) and M <= 2; NULL otherwise.
+const void *stream_split_kernel(int bits, int M);
 // The expert gather kernel for `bits` taking up to `mw` pairs of a plane per
 // pass (grid: row blocks x planes; NULL outside 2, 3, 5, 6 and 1..8).
 const void *stream_gather_kernel(int bits, int mw);

@@ -305,8 +305,10 @@ __device__ __forceinline__ void load_group(uint32_t (&w)[2 * BITS], __amdgpu_buf
 
 }  // namespace
 
-template <int BITS, int MW, bool GATHER = false>
-__global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
+// The kernel body; KS = 1 for qmv_stream_kernel (the products and the gather),
+// KS = 2 for qmv_stream_split_kernel.
+template <int BITS, int MW, bool GATHER, int KS>
+__device__ __forceinline__ void stream_body(StreamArgs a) {
     // One or two activation rows (the decode forms): the weight rows go through
     // LDS. A lane's own group is a 16- to 48-byte run, and lanes reading their
     // runs directly touch up to 2-3 times the cache lines of a contiguous read
@@ -321,10 +323,16 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
     constexpr int kDmaPerRow = (64 * kGroupBytes + 1023) / 1024;
     constexpr int kRows = 2;  // staged weight rows resident at a time
     static_assert(kRpw == 2 * kRows, "two pairs of rows per wave");
-    __shared__ u32x4 xs[MW * 8 * 64];  // [row][piece of 8 columns][group]
+    // KS = 2 (short grids with several chunks of K): waves 2i and 2i + 1 take
+    // the same 4 rows and alternate chunks of K (a block then covers 8 rows),
+    // and their sums meet in LDS at the end; so twice the blocks, and half the
+    // chunks in each wave's chain.
+    static_assert(KS == 1 || (KS == 2 && kStaged && !GATHER), "K split: the staged plain products");
+    __shared__ u32x4 xs[KS * MW * 8 * 64];  // [chunk of the step][row][piece of 8 columns][group]
     __shared__ u32x4 wl[kStaged ? kWaves * kRows * kDmaPerRow * 64 : 1];  // [wave][row][1 KB piece]
     const int lane = threadIdx.x & 63, wave = wave_id();
-    const int64_t row0 = ((int64_t)blockIdx.x * kWaves + wave) * kRpw;
+    const int kh = KS > 1 ? wave % KS : 0;  // the wave's chunk within each step of KS chunks
+    const int64_t row0 = ((int64_t)blockIdx.x * (kWaves / KS) + wave / KS) * kRpw;
     const int G = a.K / 64;
     const uint32_t rowbytes = (uint32_t)a.K / 8u * BITS;
     // The expert gather: grid row y is expert plane e. The pairs routed to e
@@ -401,12 +409,12 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
     // past M and columns past K read zero (each row's range is its own K
     // columns). The 4 waves take every fourth (m, j8).
     auto x_dma = [&](int c0) {
-        for (int q = wave; q < MW * 8; q += kWaves) {
-            const int m = q >> 3, j8 = q & 7;
+        for (int q = wave; q < KS * MW * 8; q += kWaves) {
+            const int kk = q / (MW * 8), m = (q % (MW * 8)) >> 3, j8 = q & 7;
             const __amdgpu_buffer_rsrc_t xr = span(a.x + (m < mrows ? x_row(m) : 0) * a.K, m < mrows ? (uint32_t)a.K * 2u : 0u);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xr, (__attribute__((address_space(3))) void *)(xs + q * 64),
-                16, ((uint32_t)(c0 + lane) * 64u + 8u * (uint32_t)j8) * 2u, 0, 0, 0);
+                16, ((uint32_t)(c0 + 64 * kk + lane) * 64u + 8u * (uint32_t)j8) * 2u, 0, 0, 0);
         }
     };
     // Scale and bias of group c0 + lane of row r (zero past the row's groups and
@@ -430,14 +438,15 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
         // holds the row's chunk bytes [1024 i, 1024 i + 1024); past the row's
         // end, zeros), with their scales and biases.
         auto issue = [&](int h, int c0) {
+            const int cw = c0 + 64 * kh;  // the wave's chunk of the step (past K: zeros)
 #pragma unroll
             for (int rr = 0; rr < kRows; ++rr) {
-                const __amdgpu_buffer_rsrc_t wr = row_rsrc(h * kRows + rr, c0, sc[h * kRows + rr], bi[h * kRows + rr]);
+                const __amdgpu_buffer_rsrc_t wr = row_rsrc(h * kRows + rr, cw, sc[h * kRows + rr], bi[h * kRows + rr]);
 #pragma unroll
                 for (int i = 0; i < kDmaPerRow; ++i)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
                         wr, (__attribute__((address_space(3))) void *)(wl + ((wave * kRows + rr) * kDmaPerRow + i) * 64),
-                        16, (uint32_t)c0 * kGroupBytes + (uint32_t)(i * 64 + lane) * 16u, 0, 0, 2);
+                        16, (uint32_t)cw * kGroupBytes + (uint32_t)(i * 64 + lane) * 16u, 0, 0, 2);
             }
         };
         uint32_t w[kRows][2 * BITS];
@@ -471,7 +480,7 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
 
         x_dma(0);
         issue(0, 0);
-        for (int c0 = 0; c0 < G; c0 += 64) {
+        for (int c0 = 0; c0 < G; c0 += 64 * KS) {
             // This chunk's x (every wave's pieces) and this wave's first pair of
             // rows have landed. Tied to the last rows' sums so that no wait is
             // hoisted above the previous chunk's arithmetic.
@@ -487,7 +496,7 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
                 uint32_t xn[32];
 #pragma unroll
                 for (int j8 = 0; j8 < 8; ++j8) {
-                    const u32x4 v = xs[(m * 8 + j8) * 64 + lane];
+                    const u32x4 v = xs[((kh * MW + m) * 8 + j8) * 64 + lane];
                     xn[4 * j8] = v.x;
                     xn[4 * j8 + 1] = v.y;
                     xn[4 * j8 + 2] = v.z;
@@ -522,8 +531,8 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
             }
             // Every wave holds the chunk's x: the next chunk's pieces may land.
             lds_barrier();
-            const bool more = c0 + 64 < G;
-            if (more) x_dma(c0 + 64);
+            const bool more = c0 + 64 * KS < G;
+            if (more) x_dma(c0 + 64 * KS);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 // The second pair (and the next chunk's x) after the first pair
@@ -533,7 +542,7 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
                 if (h == 0)
                     issue(1, c0);
                 else if (more)
-                    issue(0, c0 + 64);
+                    issue(0, c0 + 64 * KS);
                 float d[kRows][MW];
 #pragma unroll
                 for (int rr = 0; rr < kRows; ++rr)
@@ -617,6 +626,22 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
         }
     }
 
+    if constexpr (KS > 1) {
+        // The second wave of each pair hands its per-lane sums to the first
+        // (one block barrier; the sum's order is fixed).
+        __shared__ float kred[kWaves / KS][kRpw * MW][64];
+        if (kh == 1)
+#pragma unroll
+            for (int r = 0; r < kRpw; ++r)
+#pragma unroll
+                for (int m = 0; m < MW; ++m) kred[wave / KS][r * MW + m][lane] = acc[r][m];
+        lds_barrier();
+        if (kh == 1) return;
+#pragma unroll
+        for (int r = 0; r < kRpw; ++r)
+#pragma unroll
+            for (int m = 0; m < MW; ++m) acc[r][m] += kred[wave / KS][r * MW + m][lane];
+    }
     // Wave sums: value i = r*MW + m sits in every lane of row rho of t[i/4]
     // with i % 4 == sum_slot(rho); lane 16*rho stores those values.
     constexpr int V = kRpw * MW;
@@ -639,6 +664,17 @@ __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
         }
     }
     }  // pass
+}
+
+template <int BITS, int MW, bool GATHER = false>
+__global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
+    stream_body<BITS, MW, GATHER, 1>(a);
+}
+
+// The K-split form: 8 rows per block, waves 2i and 2i + 1 alternating chunks of K.
+template <int BITS, int MW>
+__global__ __launch_bounds__(256) void qmv_stream_split_kernel(StreamArgs a) {
+    stream_body<BITS, MW, false, 2>(a);
 }
 
 // One thread per 32 codes (BITS words): w = fma(s, q, b) written as fp32 [N, K].
@@ -716,6 +752,23 @@ static const void *stream_gather_mw(int mw) {
     if (mw <= 2) return reinterpret_cast<const void *>(&qmv_stream_kernel<BITS, 2, true>);
     if (mw <= 4) return reinterpret_cast<const void *>(&qmv_stream_kernel<BITS, 4, true>);
     return reinterpret_cast<const void *>(&qmv_stream_kernel<BITS, 8, true>);
+}
+
+template <int BITS>
+static const void *stream_split_mw(int M) {
+    if (M <= 1) return reinterpret_cast<const void *>(&qmv_stream_split_kernel<BITS, 1>);
+    if (M <= 2) return reinterpret_cast<const void *>(&qmv_stream_split_kernel<BITS, 2>);
+    return nullptr;
+}
+
+const void *stream_split_kernel(int bits, int M) {
+    switch (bits) {
+        case 2: return stream_split_mw<2>(M);
+        case 3: return stream_split_mw<3>(M);
+        case 5: return stream_split_mw<5>(M);
+        case 6: return stream_split_mw<6>(M);
+    }
+    return nullptr;
 }
 
 const void *stream_gather_kernel(int bits, int mw) {

@@ -33,6 +33,7 @@ def dev_weight(d):
 @pytest.mark.parametrize("M,N,K", [
     (1, 4096, 4096), (1, 1000, 14336), (3, 777, 4160), (8, 300, 2048), (5, 17, 64), (2, 33, 128),
     (4, 2048, 8192), (7, 130, 4096 + 64 * 3), (2, 1000, 4160), (2, 4096, 14336),
+    (1, 999, 12288), (2, 300, 8192 + 64),   # the K split: an odd chunk count, a chunk of one group
 ])
 def test_stream_bits_products(bits, M, N, K):
     """Several 64-group chunks of K, partial last chunks, weight rows past the last full
