@@ -1,11 +1,12 @@
 // Affine group-quantized products for the bit-stream widths: 2-, 3-, 5- and
-// 6-bit codes with group size 64 (and the large batch-1 4-bit products), the other widths of the affine family that
+// 6-bit codes with group size 64, the other widths of the affine family that
 // "MLX CUDA Cleanup Plan" (Target Architecture §1; Refactor Plan, Phase 3)
-// names at 4 and 8 bits. A row's codes form one low-first bit stream over its
-// uint32 words: code k occupies stream bits bits*k .. bits*k + bits - 1, word
-// i holding bits 32i .. 32i + 31 (for 2 bits, k / 16 and k % 16 exactly as the
-// 4- and 8-bit layouts; a 3-, 5- or 6-bit code may run into the next word).
-// A 64-column group is then exactly 2*bits words (16, 24, 40 or 48 bytes).
+// names at 4 and 8 bits; and the batch-1 4-bit products whose grid gives
+// every compute unit at least two blocks. A row's codes form one low-first
+// bit stream over its uint32 words: code k occupies stream bits
+// bits*k .. bits*k + bits - 1, word i holding bits 32i .. 32i + 31 (for 2 and
+// 4 bits exactly the packed layout; a 3-, 5- or 6-bit code may run into the
+// next word). A 64-column group is then exactly 2*bits words (16 to 48 bytes).
 //
 //     y[m, n] = sum_k x[m, k] * (s[n, g] * q[n, k] + b[n, g]),  g = k / 64
 //             = sum_g s[n, g] * D[m, n, g] + (b[n, g] - 128 s[n, g]) * X[m, g],
@@ -14,22 +15,24 @@
 // by a per-code constant under the window decode below.
 //
 // Layout of the work: lane l of a wave takes group l of a 64-group chunk of K,
-// each wave 4 weight rows, a block 4 waves. Per chunk the block stages x (up
+// each wave 4 weight rows, a block 4 waves (16 rows; the K-split form: 8 rows,
+// two waves per row set alternating chunks). Per chunk the block stages x (up
 // to 8 rows) in LDS as 16-byte pieces [row][piece][group] with direct-to-LDS
 // loads, so the 64 lanes read 64 consecutive pieces (no bank conflicts).
 // Codes become bf16 lanes exactly (a code below 128 in the low mantissa bits
 // of a bf16 with a fixed exponent), and v_dot2c_f32_bf16 takes each lane pair
 // against the matching pair of activations:
-//   - with one or two activation rows at 2, 3 and 5 bits, the window decode:
-//     codes k and k + d share a 32-bit window of the stream and one and-or
-//     makes the pair (plan below);
+//   - with one or two activation rows at 2, 3, 4 and 5 bits, the window
+//     decode: codes k and k + d share a 32-bit window of the stream and one
+//     and-or makes the pair (plan below);
 //   - otherwise adjacent codes (2i, 2i + 1) are taken from one funnel-shifted
 //     word and moved into the two bf16 lanes.
-// At 3, 5 and 6 bits with one or two activation rows the wave's weight rows
-// also pass through LDS (loads of contiguous 16-byte pieces; a lane reading
-// its own 24- to 48-byte group directly spreads each load over 2-3 times the
-// cache lines). The wave sums come from the DPP / permlane tree of the VALU
-// products.
+// With one or two activation rows the wave's weight rows also pass through
+// LDS (loads of contiguous 16-byte pieces; a lane reading its own 24- to
+// 48-byte group directly spreads each load over 2-3 times the cache lines),
+// and the fetches run a step ahead of the arithmetic. The expert gather runs
+// each plane's pairs as activation rows. The wave sums come from the DPP /
+// permlane tree of the VALU products.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -91,7 +94,7 @@ __device__ __forceinline__ uint32_t code_pair_bf16(const uint32_t (&w)[NW], int 
     return ((t << (16 - BITS)) & (mask << 16)) | (t & mask) | 0x43004300u;
 }
 
-// ---- Pair plans of the one- and two-row forms (window decode at 2, 3, 5 bits) ----
+// ---- Pair plans of the one- and two-row forms (window decode at 2, 3, 4, 5 bits) ----
 //
 // A bfloat16 with exponent field 134 - e and a code q in mantissa bits
 // [e, e + bits) reads as the exact value 2^(7-e) + q (for e + bits <= 7). So a
