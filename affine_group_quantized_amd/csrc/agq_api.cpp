@@ -519,6 +519,23 @@ agq_status agq_qmv_nvfp4(const void *x, const uint32_t *w, const void *scales, f
     int cus = 0, dev = 0;
     agq_status st = current_device(&cus, &dev);
     if (st != AGQ_OK) return st;
+    if (M == 1 && K % 64 == 0 && !misaligned(scales, 4) &&
+        (N + agq::kStreamRowsPerBlock - 1) / agq::kStreamRowsPerBlock >= 2 * (int64_t)cus) {
+        // Large batch-1 grids: the bit-stream kernel's NVFP4 form, as for the
+        // affine 4-bit products.
+        agq::StreamArgs a{};
+        a.x = static_cast<const uint16_t *>(x);
+        a.w = w;
+        a.s = static_cast<const uint16_t *>(scales);  // E4M3 bytes [N, K/16]
+        a.y = static_cast<uint16_t *>(y);
+        a.N = N;
+        a.K = (int32_t)K;
+        a.M = 1;
+        a.ts = tensor_scale;
+        return launch(agq::stream_nvfp4_kernel(),
+                      dim3((unsigned)((N + agq::kStreamRowsPerBlock - 1) / agq::kStreamRowsPerBlock)), dim3(256), 0, &a,
+                      stream);
+    }
     const void *sym = nullptr;
     for (int pass = 0; pass < 2; ++pass) {
         sym = agq::nvfp4_kernel_for(plan.mw, plan.cpt, plan.R, plan.NB);

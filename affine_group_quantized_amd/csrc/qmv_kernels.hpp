@@ -119,6 +119,8 @@ struct StreamArgs {
     const uint32_t *rhs;
     int32_t R_x;
     int32_t E;
+    float ts;  // NVFP4: the tensor scale (s then holds E4M3 bytes [N, K/16])
+    int32_t pad_;
 };
 constexpr int kStreamRowsPerBlock = 16;  // 4 waves of 4 weight rows
 // The matvec kernel for `bits` and M activation rows (NULL outside 2, 3, 5, 6 and
@@ -128,6 +130,8 @@ constexpr int kMaxGatherPairs = 4096;
 // The K-split form (8 rows per block, two waves per row set alternating
 // chunks of K) for `bits` (2, 3, 5, 6) and M <= 2; NULL otherwise.
 const void *stream_split_kernel(int bits, int M);
+// The NVFP4 batch-1 product on the bit-stream kernel (K a multiple of 64).
+const void *stream_nvfp4_kernel();
 // The expert gather kernel for `bits` taking up to `mw` pairs of a plane per
 // pass (grid: row blocks x planes; NULL outside 2, 3, 5, 6 and 1..8).
 const void *stream_gather_kernel(int bits, int mw);

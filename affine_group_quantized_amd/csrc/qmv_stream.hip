@@ -310,8 +310,12 @@ __device__ __forceinline__ void load_group(uint32_t (&w)[2 * BITS], __amdgpu_buf
 
 // The kernel body; KS = 1 for qmv_stream_kernel (the products and the gather),
 // KS = 2 for qmv_stream_split_kernel.
-template <int BITS, int MW, bool GATHER, int KS>
+template <int BITS, int MW, bool GATHER, int KS, bool FP4 = false>
 __device__ __forceinline__ void stream_body(StreamArgs a) {
+    // FP4: the NVFP4 product (E2M1 codes in the 4-bit layout; s holds one E4M3
+    // byte per 16 columns, four per 64-column group; no biases; y scaled by the
+    // tensor scale ts before its rounding).
+    static_assert(!FP4 || (BITS == 4 && MW == 1 && !GATHER && KS == 1), "NVFP4: one row, no gather or split");
     // One or two activation rows (the decode forms): the weight rows go through
     // LDS. A lane's own group is a 16- to 48-byte run, and lanes reading their
     // runs directly touch up to 2-3 times the cache lines of a contiguous read
@@ -426,9 +430,16 @@ __device__ __forceinline__ void stream_body(StreamArgs a) {
         const int64_t row = row0 + r;
         const bool ok = row < a.N;
         const int64_t ro = ok ? row : 0;
-        const uint32_t sb = ok ? (uint32_t)G * 2u : 0u;
-        s_out = __builtin_amdgcn_raw_buffer_load_b16(span(a.s + ro * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
-        b_out = __builtin_amdgcn_raw_buffer_load_b16(span(a.b + ro * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
+        if constexpr (FP4) {  // the group's four scale bytes
+            const uint8_t *s8 = reinterpret_cast<const uint8_t *>(a.s);
+            s_out = __builtin_amdgcn_raw_buffer_load_b32(span(s8 + ro * G * 4, ok ? (uint32_t)G * 4u : 0u),
+                                                         (uint32_t)(c0 + lane) * 4u, 0, 0);
+            b_out = 0u;
+        } else {
+            const uint32_t sb = ok ? (uint32_t)G * 2u : 0u;
+            s_out = __builtin_amdgcn_raw_buffer_load_b16(span(a.s + ro * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
+            b_out = __builtin_amdgcn_raw_buffer_load_b16(span(a.b + ro * G, sb), (uint32_t)(c0 + lane) * 2u, 0, 0);
+        }
         return span(a.w + ro * (rowbytes / 4u), ok ? rowbytes : 0u);
     };
 
@@ -505,9 +516,14 @@ __device__ __forceinline__ void stream_body(StreamArgs a) {
                     xn[4 * j8 + 2] = v.z;
                     xn[4 * j8 + 3] = v.w;
                 }
-                float sj[kMaxMagics];
                 sx[m] = 0.f;
                 cx[m] = 0.f;
+                if constexpr (FP4) {  // natural pairs: the FP4 convert gives codes (2i, 2i + 1)
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) xp[i][m] = xn[i];
+                    continue;
+                }
+                float sj[kMaxMagics];
 #pragma unroll
                 for (int j = 0; j < kMaxMagics; ++j) sj[j] = 0.f;
                 static_for<32>([&](auto I) {
@@ -546,6 +562,29 @@ __device__ __forceinline__ void stream_body(StreamArgs a) {
                     issue(1, c0);
                 else if (more)
                     issue(0, c0 + 64 * KS);
+                if constexpr (FP4) {
+                    // Per 16-column block j (words 2j, 2j + 1): the dot of its 8 code
+                    // pairs with x, scaled by the block's E4M3 byte.
+#pragma unroll
+                    for (int rr = 0; rr < kRows; ++rr) {
+                        const int r = h * kRows + rr;
+                        static_for<4>([&](auto J) {
+                            constexpr int j = decltype(J)::value;
+                            float dj = 0.f;
+#pragma unroll
+                            for (int u = 0; u < 2; ++u) {
+                                const uint32_t wd = w[rr][2 * j + u];
+                                const int i0 = 4 * (2 * j + u);
+                                dj = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, 1.0f, 0)), xp[i0][0], dj);
+                                dj = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, 1.0f, 1)), xp[i0 + 1][0], dj);
+                                dj = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, 1.0f, 2)), xp[i0 + 2][0], dj);
+                                dj = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, 1.0f, 3)), xp[i0 + 3][0], dj);
+                            }
+                            acc[r][0] = fmaf(__builtin_amdgcn_cvt_f32_fp8(sc[r], j), dj, acc[r][0]);
+                        });
+                    }
+                    continue;
+                }
                 float d[kRows][MW];
 #pragma unroll
                 for (int rr = 0; rr < kRows; ++rr)
@@ -663,7 +702,7 @@ __device__ __forceinline__ void stream_body(StreamArgs a) {
             if (i >= V) continue;
             const int r = i / MW, m = i % MW;
             const int64_t row = row0 + r;
-            if (row < a.N && m < mrows) a.y[y_row(m) * a.N + row] = f32_to_bf16(t[q]);
+            if (row < a.N && m < mrows) a.y[y_row(m) * a.N + row] = f32_to_bf16(FP4 ? t[q] * a.ts : t[q]);
         }
     }
     }  // pass
@@ -672,6 +711,11 @@ __device__ __forceinline__ void stream_body(StreamArgs a) {
 template <int BITS, int MW, bool GATHER = false>
 __global__ __launch_bounds__(256) void qmv_stream_kernel(StreamArgs a) {
     stream_body<BITS, MW, GATHER, 1>(a);
+}
+
+// The NVFP4 batch-1 product (large grids).
+__global__ __launch_bounds__(256) void qmv_stream_nvfp4_kernel(StreamArgs a) {
+    stream_body<4, 1, false, 1, true>(a);
 }
 
 // The K-split form: 8 rows per block, waves 2i and 2i + 1 alternating chunks of K.
@@ -773,6 +817,8 @@ const void *stream_split_kernel(int bits, int M) {
     }
     return nullptr;
 }
+
+const void *stream_nvfp4_kernel() { return reinterpret_cast<const void *>(&qmv_stream_nvfp4_kernel); }
 
 const void *stream_gather_kernel(int bits, int mw) {
     if (mw < 1 || mw > 8) return nullptr;

@@ -68,6 +68,31 @@ def test_nvfp4_ragged_and_limits(M, N, K):
     run(d, x, "ragged")
 
 
+def test_nvfp4_large_grid_batch1():
+    """Batch-1 products whose 16-row grid gives every compute unit two blocks run on the
+    bit-stream kernel's NVFP4 form: random codes and scale bytes (both signs, subnormal
+    scales) over a ragged row count and two 4096-column chunks, every row against the
+    oracle, and one-hot columns bit for bit (code 8, -0, gives +0)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K = 2 * cus * 16 + 5, 4096 + 64 * 5
+    g = np.random.default_rng([10, N, K])
+    codes = g.integers(0, 16, size=(N, K), dtype=np.uint8)
+    scales = g.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8)
+    scales |= (g.random((N, K // 16)) < 0.3).astype(np.uint8) << 7
+    d = {"w": si.pack_codes(codes, 4), "scales": scales, "tensor_scale": 0.75}
+    x = si.draw_activations(10, 1, 1, K)
+    run(d, x, "large grid")
+    w, s = u32_dev(d["w"]), u8_dev(scales)
+    e2m1 = np.array([oracle.load().agqo_e2m1(c) for c in range(16)])
+    e4m3 = np.array([oracle.load().agqo_e4m3(b) for b in range(256)])
+    for c in (0, 1, 15, 16, 17, 63, 4095, 4096, K - 1):
+        e = np.zeros((1, K), np.uint16)
+        e[0, c] = 0x3F80
+        got = bf16_bits_host(agq.qmv_nvfp4(bf16_dev(e)[0], w, s, 1.0))
+        prod = (e2m1[codes[:, c]] * e4m3[scales[:, c // 16]]).astype(np.float32) + np.float32(0)
+        assert np.array_equal(got, si.bf16_bits(prod)), c
+
+
 def test_nvfp4_one_hot_columns_are_bitwise_weights():
     N, K = 300, 256
     g = np.random.default_rng(9)
