@@ -128,6 +128,8 @@ def test_decode_layer_final_norm_and_logits(layer):
     (999, 4160, 4, 64, 0), (2050, 8192, 4, 64, 2), (513, 2048, 8, 64, 0), (1538, 4096, 8, 128, 1),
     (4864 * 2, 896, 8, 64, 2), (896, 4864, 8, 64, 0), (300, 14336, 8, 64, 1), (64, 65536, 4, 64, 0),
     (130, 32768, 8, 32, 2), (4096, 12288, 4, 64, 1),
+    # large 4-bit grids with one chunk of K (ragged rows, a partial chunk, one group)
+    (8194, 1088, 4, 64, 1), (8202, 64, 4, 64, 0), (16390, 4096, 4, 64, 2), (8210, 4096, 4, 64, 0),
 ])
 def test_fused_shapes(N, K, bits, gs, act):
     d = quantized(N * 7 + K + bits, N, K, bits, gs)
@@ -148,6 +150,15 @@ def test_fused_gated_deep_plan(act):
     x = si.draw_activations(93, 1, 1, K)
     res = si.draw_activations(94, 1, 1, N)[0] if act == 0 else None
     run_case(d, x, 4, 64, act, gamma=norm_weight(7, K), eps=1e-6, res=res, sample=2048, what="deep", seed=act)
+
+
+def test_fused_large_grid_inplace_residual():
+    """A large 4-bit grid with the residual buffer as y (the in-place residual add)."""
+    N, K = 8200, 4096
+    d = quantized(13, N, K, 4)
+    x = si.draw_activations(99, 0, 1, K)
+    res = si.draw_activations(100, 0, 1, N)[0]
+    run_case(d, x, 4, 64, 0, gamma=norm_weight(5, K), eps=1e-5, res=res, what="large grid in-place", inplace=True)
 
 
 def test_fused_eps_and_scale():
