@@ -18,8 +18,9 @@ MUTANTS = {
     "wrong_word_index": ("uint64_t pair = packed_row[first / 32];", "uint64_t pair = packed_row[k / 32];"),
     "straddle_dropped": ("if (first % 32 + bits > 32) pair |= (uint64_t)packed_row[first / 32 + 1] << 32;", ""),
     "quant_straddle_dropped": ("if (first % 32 + bits > 32) wq[n * words + first / 32 + 1] |= q >> (uint32_t)(32 - first % 32);", ""),
+    # (in bounds: a mutant that writes past a row can crash the test process)
     "quant_stream_offset": ("const int64_t first = (int64_t)bits * (g * group_size + j);",
-                            "const int64_t first = (int64_t)bits * (g * group_size) + 4 * j;"),
+                            "const int64_t first = (int64_t)bits * (g * group_size + (j ^ 1));"),
     "short_mask": ("uint32_t mask = (1u << bits) - 1u;", "uint32_t mask = (1u << (bits - 1)) - 1u;"),
     "dropped_bias": ("return bf16_value(scale_row[g]) * q + bf16_value(bias_row[g]);",
                      "return bf16_value(scale_row[g]) * q;"),
